@@ -1,0 +1,233 @@
+"""ctypes binding of the CPU oracle (oracle/moe_ref.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product package.  Everything here
+works on host numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+ACCUMULATE = 1
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("D", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float)]
+
+
+class QMat(ctypes.Structure):
+    _fields_ = [("q4", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class Expert(ctypes.Structure):
+    _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("experts", ctypes.c_void_p), ("shared", ctypes.c_void_p)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = os.path.join(HERE, "libmoe_ref.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run oracle/build.py (or __graft_entry__.build())")
+        L = ctypes.CDLL(path)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.moe_ref_pack_int4.argtypes = [vp, i32, i32, vp, vp]
+        L.moe_ref_unpack_int4.argtypes = [vp, i32, i32, vp]
+        L.moe_ref_quant_row_i8.argtypes = [vp, i32, vp]
+        L.moe_ref_quant_row_i8.restype = f32
+        L.moe_ref_quant_act_i8.argtypes = [vp, i32, i32, vp, vp]
+        L.moe_ref_quant_act_i8_bf16.argtypes = [vp, i32, i32, vp, vp]
+        L.moe_ref_dot_i4_i8.argtypes = [vp, vp, i32]
+        L.moe_ref_dot_i4_i8.restype = ctypes.c_int32
+        L.moe_ref_router_topk.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.moe_ref_expert_swiglu_i4.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.moe_ref_layer_forward.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint]
+        L.moe_ref_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, vp, vp]
+        L.moe_ref_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name} returned {rc}")
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def make_config(D, I, E, K, n_shared=1, routed_scale=2.5) -> Config:
+    return Config(D, I, E, K, n_shared, routed_scale)
+
+
+# ---- primitives -------------------------------------------------------------
+
+def pack_int4(w: np.ndarray):
+    w = _c(w, np.float32)
+    O, C = w.shape
+    q4 = np.empty((O, (C + 1) // 2), np.uint8)
+    s = np.empty(O, np.float32)
+    _check(lib().moe_ref_pack_int4(_p(w), O, C, _p(q4), _p(s)), "pack_int4")
+    return q4, s
+
+
+def unpack_int4(q4: np.ndarray, C: int) -> np.ndarray:
+    q4 = _c(q4, np.uint8)
+    O = q4.shape[0]
+    q = np.empty((O, C), np.int8)
+    _check(lib().moe_ref_unpack_int4(_p(q4), O, C, _p(q)), "unpack_int4")
+    return q
+
+
+def quant_act_i8(x: np.ndarray):
+    x = _c(x, np.float32)
+    S, D = x.shape
+    xq = np.empty((S, D), np.int8)
+    sx = np.empty(S, np.float32)
+    _check(lib().moe_ref_quant_act_i8(_p(x), S, D, _p(xq), _p(sx)), "quant_act_i8")
+    return xq, sx
+
+
+def quant_act_i8_bf16(xbits: np.ndarray):
+    xbits = _c(xbits, np.uint16)
+    S, D = xbits.shape
+    xq = np.empty((S, D), np.int8)
+    sx = np.empty(S, np.float32)
+    _check(lib().moe_ref_quant_act_i8_bf16(_p(xbits), S, D, _p(xq), _p(sx)), "quant_act_i8_bf16")
+    return xq, sx
+
+
+def dot_i4_i8(q4row: np.ndarray, x: np.ndarray) -> int:
+    q4row = _c(q4row, np.uint8)
+    x = _c(x, np.int8)
+    return int(lib().moe_ref_dot_i4_i8(_p(q4row), _p(x), x.shape[0]))
+
+
+def router_topk(cfg: Config, x: np.ndarray, wr: np.ndarray, b: np.ndarray):
+    x = _c(x, np.float32)
+    S = x.shape[0]
+    wr, b = _c(wr, np.float32), _c(b, np.float32)
+    idx = np.empty((S, cfg.K), np.int32)
+    w = np.empty((S, cfg.K), np.float32)
+    logits = np.empty((S, cfg.E), np.float32)
+    choice = np.empty((S, cfg.E), np.float32)
+    _check(lib().moe_ref_router_topk(ctypes.byref(cfg), _p(x), S, _p(wr), _p(b), _p(idx), _p(w),
+                                     _p(logits), _p(choice)), "router_topk")
+    return idx, w, logits, choice
+
+
+# ---- experts and layers -----------------------------------------------------
+
+@dataclass
+class HostExpert:
+    """Packed int4 expert on the host: gate/up [I][D/2], down [D][I/2]."""
+    gate_q4: np.ndarray
+    gate_s: np.ndarray
+    up_q4: np.ndarray
+    up_s: np.ndarray
+    down_q4: np.ndarray
+    down_s: np.ndarray
+
+    def cstruct(self) -> Expert:
+        return Expert(QMat(_p(self.gate_q4), _p(self.gate_s)), QMat(_p(self.up_q4), _p(self.up_s)),
+                      QMat(_p(self.down_q4), _p(self.down_s)))
+
+    @staticmethod
+    def from_f32(g, u, d) -> "HostExpert":
+        gq, gs = pack_int4(g)
+        uq, us = pack_int4(u)
+        dq, ds = pack_int4(d)
+        return HostExpert(gq, gs, uq, us, dq, ds)
+
+
+def expert_swiglu(cfg: Config, xq: np.ndarray, sx: np.ndarray, e: HostExpert):
+    xq = _c(xq, np.int8)
+    sx = _c(sx, np.float32)
+    S = xq.shape[0]
+    y = np.empty((S, cfg.D), np.float32)
+    acc_gu = np.empty((S, 2, cfg.I), np.int32)
+    hq = np.empty((S, cfg.I), np.int8)
+    sh = np.empty(S, np.float32)
+    acc_d = np.empty((S, cfg.D), np.int32)
+    es = e.cstruct()
+    _check(lib().moe_ref_expert_swiglu_i4(ctypes.byref(cfg), _p(xq), _p(sx), S, ctypes.byref(es),
+                                          _p(y), _p(acc_gu), _p(hq), _p(sh), _p(acc_d)),
+           "expert_swiglu_i4")
+    return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
+
+
+class HostLayer:
+    """Router weights plus a dict of packed experts (any subset may be present;
+    the oracle fails if routing selects an expert that is absent)."""
+
+    def __init__(self, cfg: Config, router_w, router_b, experts: dict, shared: HostExpert | None):
+        self.cfg = cfg
+        self.router_w = _c(router_w, np.float32)
+        self.router_b = _c(router_b, np.float32)
+        self.experts = experts
+        self.shared = shared
+
+    def cstruct(self):
+        arr = (Expert * self.cfg.E)()
+        for e, ex in self.experts.items():
+            arr[e] = ex.cstruct()
+        sh = self.shared.cstruct() if self.shared is not None else None
+        keep = (arr, sh)
+        L = Layer(_p(self.router_w), _p(self.router_b), ctypes.addressof(arr),
+                  ctypes.addressof(sh) if sh is not None else None)
+        return L, keep
+
+
+def layer_forward(layer: HostLayer, x: np.ndarray, out: np.ndarray | None = None, flags: int = 0):
+    x = _c(x, np.float32)
+    S = x.shape[0]
+    out = np.zeros((S, layer.cfg.D), np.float32) if out is None else out
+    L, keep = layer.cstruct()
+    _check(lib().moe_ref_layer_forward(ctypes.byref(layer.cfg), ctypes.byref(L), _p(x), S, _p(out),
+                                       flags), "layer_forward")
+    return out
+
+
+def layer_forward_batch(layer: HostLayer, x: np.ndarray, out: np.ndarray | None = None,
+                        flags: int = 0):
+    x = _c(x, np.float32)
+    S = x.shape[0]
+    cfg = layer.cfg
+    out = np.zeros((S, cfg.D), np.float32) if out is None else out
+    idx = np.empty((S, cfg.K), np.int32)
+    w = np.empty((S, cfg.K), np.float32)
+    uniq = np.empty(cfg.E, np.int32)
+    nu = ctypes.c_int32(0)
+    L, keep = layer.cstruct()
+    _check(lib().moe_ref_layer_forward_batch(ctypes.byref(cfg), ctypes.byref(L), _p(x), S, _p(out),
+                                             flags, _p(idx), _p(w), _p(uniq), ctypes.byref(nu)),
+           "layer_forward_batch")
+    return out, idx, w, uniq[: nu.value].copy()
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-5) -> np.ndarray:
+    x = _c(x, np.float32)
+    S, D = x.shape
+    gamma = _c(gamma, np.float32)
+    y = np.empty_like(x)
+    _check(lib().moe_ref_rmsnorm(_p(x), _p(gamma), S, D, eps, _p(y)), "rmsnorm")
+    return y

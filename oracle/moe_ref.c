@@ -1,0 +1,359 @@
+/*
+ * moe_ref.c -- CPU oracle for the routed-expert int4 MoE block.
+ *
+ * TEST INFRASTRUCTURE ONLY (see moe_ref.h).  Plain single-threaded C, built
+ * with -O2 -ffp-contract=off so that every float expression is evaluated as
+ * written: one rounding per operation, no fused multiply-add.
+ *
+ * Rounding of float to integer uses lrintf in the default rounding mode
+ * (round half to even), as the article's listings do in sections 05, 06
+ * and 12.
+ */
+#include "moe_ref.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int bad_cfg(const moe_ref_config *c) {
+  return !c || c->D < 1 || c->I < 1 || c->E < 1 || c->K < 1 || c->K > c->E || c->K > 64 ||
+         c->n_shared < 0 || c->n_shared > 1;
+}
+
+/* ---- section 06: int4 weight container ------------------------------------ */
+
+int moe_ref_pack_int4(const float *w, int O, int C, uint8_t *q4, float *scale) {
+  if (!w || !q4 || !scale || O < 1 || C < 1) return -1;
+  const int qmax = 7, rb = (C + 1) / 2;
+  for (int o = 0; o < O; o++) {
+    const float *wr = w + (int64_t)o * C;
+    float amax = 0.f;
+    for (int i = 0; i < C; i++) {
+      float a = fabsf(wr[i]);
+      if (a > amax) amax = a;
+    }
+    float s = amax / (float)qmax;
+    if (s < 1e-8f) s = 1e-8f;
+    scale[o] = s;
+    uint8_t *qr = q4 + (int64_t)o * rb;
+    for (int i = 0; i < C; i += 2) {
+      int v0 = (int)lrintf(wr[i] / s);
+      if (v0 > qmax) v0 = qmax;
+      if (v0 < -8) v0 = -8;
+      int v1 = 0;
+      if (i + 1 < C) {
+        v1 = (int)lrintf(wr[i + 1] / s);
+        if (v1 > qmax) v1 = qmax;
+        if (v1 < -8) v1 = -8;
+      }
+      qr[i >> 1] = (uint8_t)((v0 + 8) | ((v1 + 8) << 4));
+    }
+  }
+  return 0;
+}
+
+static inline int nibble_value(const uint8_t *row, int c) {
+  uint8_t b = row[c >> 1];
+  int n = (c & 1) ? (b >> 4) : (b & 0x0F);
+  return n - 8;
+}
+
+int moe_ref_unpack_int4(const uint8_t *q4, int O, int C, int8_t *q) {
+  if (!q4 || !q || O < 1 || C < 1) return -1;
+  const int rb = (C + 1) / 2;
+  for (int o = 0; o < O; o++)
+    for (int c = 0; c < C; c++) q[(int64_t)o * C + c] = (int8_t)nibble_value(q4 + (int64_t)o * rb, c);
+  return 0;
+}
+
+/* ---- section 12: activation quantization and integer dots ---------------- */
+
+float moe_ref_quant_row_i8(const float *x, int n, int8_t *q) {
+  float amax = 0.f;
+  for (int i = 0; i < n; i++) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  float s = amax / 127.f;
+  if (s < 1e-12f) s = 1e-12f;
+  float inv = 1.f / s;
+  for (int i = 0; i < n; i++) {
+    long v = lrintf(x[i] * inv);
+    /* |x * inv| <= 127 up to rounding, so this clamp never changes a value. */
+    if (v > 127) v = 127;
+    if (v < -127) v = -127;
+    q[i] = (int8_t)v;
+  }
+  return s;
+}
+
+int moe_ref_quant_act_i8(const float *x, int S, int D, int8_t *xq, float *sx) {
+  if (!x || !xq || !sx || S < 1 || D < 1) return -1;
+  for (int s = 0; s < S; s++)
+    sx[s] = moe_ref_quant_row_i8(x + (int64_t)s * D, D, xq + (int64_t)s * D);
+  return 0;
+}
+
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+int moe_ref_quant_act_i8_bf16(const uint16_t *x, int S, int D, int8_t *xq, float *sx) {
+  if (!x || !xq || !sx || S < 1 || D < 1) return -1;
+  float *row = (float *)malloc((size_t)D * sizeof(float));
+  if (!row) return -2;
+  for (int s = 0; s < S; s++) {
+    for (int i = 0; i < D; i++) row[i] = bf16_to_f32(x[(int64_t)s * D + i]);
+    sx[s] = moe_ref_quant_row_i8(row, D, xq + (int64_t)s * D);
+  }
+  free(row);
+  return 0;
+}
+
+int32_t moe_ref_dot_i4_i8(const uint8_t *q4row, const int8_t *x, int C) {
+  int32_t acc = 0;
+  for (int c = 0; c < C; c++) acc += (int32_t)nibble_value(q4row, c) * (int32_t)x[c];
+  return acc;
+}
+
+/* ---- section 11: router ---------------------------------------------------- */
+
+static float sigmoid_ref(float v) { return 1.f / (1.f + expf(-v)); }
+
+/* Top-K by repeated argmax over the experts not yet taken.  An expert is a
+ * candidate when choice > -1e30 (the article's initial best value; a NaN is
+ * never greater, so NaN choices are never picked).  If fewer than K experts are
+ * candidates, the remaining slots take the lowest-numbered experts not yet
+ * taken (the article leaves this case undefined). */
+static void topk_row(const float *choice, const float *sig, int E, int K, float scale,
+                     int32_t *idx, float *w) {
+  for (int kk = 0; kk < K; kk++) {
+    int best = -1;
+    float bv = -1e30f;
+    for (int e = 0; e < E; e++) {
+      int taken = 0;
+      for (int j = 0; j < kk; j++)
+        if (idx[j] == e) { taken = 1; break; }
+      if (!taken && choice[e] > bv) { bv = choice[e]; best = e; }
+    }
+    if (best < 0) {
+      for (int e = 0; e < E && best < 0; e++) {
+        int taken = 0;
+        for (int j = 0; j < kk; j++)
+          if (idx[j] == e) { taken = 1; break; }
+        if (!taken) best = e;
+      }
+    }
+    idx[kk] = best;
+    w[kk] = sig[best];
+  }
+  for (int kk = 0; kk < K; kk++) w[kk] *= scale;
+}
+
+int moe_ref_router_topk(const moe_ref_config *cfg, const float *x, int S, const float *router_w,
+                        const float *router_b, int32_t *idx, float *w, float *logits,
+                        float *choice) {
+  if (bad_cfg(cfg) || !x || !router_w || !router_b || !idx || !w || S < 1) return -1;
+  const int D = cfg->D, E = cfg->E, K = cfg->K;
+  float *sig = (float *)malloc((size_t)E * sizeof(float));
+  float *ch = (float *)malloc((size_t)E * sizeof(float));
+  if (!sig || !ch) { free(sig); free(ch); return -2; }
+  for (int s = 0; s < S; s++) {
+    const float *xs = x + (int64_t)s * D;
+    for (int e = 0; e < E; e++) {
+      const float *we = router_w + (int64_t)e * D;
+      double acc = 0.0;
+      for (int i = 0; i < D; i++) acc += (double)xs[i] * (double)we[i];
+      float lg = (float)acc;
+      if (logits) logits[(int64_t)s * E + e] = lg;
+      sig[e] = sigmoid_ref(lg);
+      ch[e] = sig[e] + router_b[e];
+      if (choice) choice[(int64_t)s * E + e] = ch[e];
+    }
+    topk_row(ch, sig, E, K, cfg->routed_scale, idx + (int64_t)s * K, w + (int64_t)s * K);
+  }
+  free(sig);
+  free(ch);
+  return 0;
+}
+
+/* ---- sections 11 and 12: one SwiGLU expert ---------------------------------- */
+
+static float silu_ref(float v) { return v / (1.f + expf(-v)); }
+
+static int qmat_ok(const moe_ref_qmat *m) { return m->q4 && m->scale; }
+
+int moe_ref_expert_swiglu_i4(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
+                             const moe_ref_expert *e, float *y, int32_t *acc_gu, int8_t *hq,
+                             float *sh, int32_t *acc_d) {
+  if (bad_cfg(cfg) || !xq || !sx || !e || !y || S < 1) return -1;
+  if (!qmat_ok(&e->gate) || !qmat_ok(&e->up) || !qmat_ok(&e->down)) return -1;
+  const int D = cfg->D, I = cfg->I;
+  const int rbD = (D + 1) / 2, rbI = (I + 1) / 2;
+  float *h = (float *)malloc((size_t)I * sizeof(float));
+  int8_t *hqr = (int8_t *)malloc((size_t)I);
+  if (!h || !hqr) { free(h); free(hqr); return -2; }
+  for (int s = 0; s < S; s++) {
+    const int8_t *xs = xq + (int64_t)s * D;
+    const float sxs = sx[s];
+    /* gate and up: integer dots, then (acc * row scale) * activation scale */
+    for (int o = 0; o < I; o++) {
+      int32_t ag = moe_ref_dot_i4_i8(e->gate.q4 + (int64_t)o * rbD, xs, D);
+      int32_t au = moe_ref_dot_i4_i8(e->up.q4 + (int64_t)o * rbD, xs, D);
+      if (acc_gu) {
+        acc_gu[((int64_t)s * 2 + 0) * I + o] = ag;
+        acc_gu[((int64_t)s * 2 + 1) * I + o] = au;
+      }
+      float g = ((float)ag * e->gate.scale[o]) * sxs;
+      float u = ((float)au * e->up.scale[o]) * sxs;
+      h[o] = silu_ref(g) * u;
+    }
+    /* the down projection is an integer matmul too, so its input is quantized */
+    float shs = moe_ref_quant_row_i8(h, I, hqr);
+    if (hq) memcpy(hq + (int64_t)s * I, hqr, (size_t)I);
+    if (sh) sh[s] = shs;
+    for (int d = 0; d < D; d++) {
+      int32_t ad = moe_ref_dot_i4_i8(e->down.q4 + (int64_t)d * rbI, hqr, I);
+      if (acc_d) acc_d[(int64_t)s * D + d] = ad;
+      y[(int64_t)s * D + d] = ((float)ad * e->down.scale[d]) * shs;
+    }
+  }
+  free(h);
+  free(hqr);
+  return 0;
+}
+
+/* ---- the block ------------------------------------------------------------ */
+
+static int layer_ok(const moe_ref_config *cfg, const moe_ref_layer *L) {
+  if (bad_cfg(cfg) || !L || !L->router_w || !L->router_b || !L->experts) return 0;
+  if (cfg->n_shared == 1 && !L->shared) return 0;
+  return 1;
+}
+
+static void combine_row(const moe_ref_config *cfg, const float *w, const float *stage, float *out,
+                        unsigned flags) {
+  /* stage holds K (+1 shared) rows of D floats for one token */
+  const int D = cfg->D, K = cfg->K;
+  for (int d = 0; d < D; d++) {
+    float acc = 0.f;
+    for (int k = 0; k < K; k++) acc += w[k] * stage[(int64_t)k * D + d];
+    if (cfg->n_shared == 1) acc += stage[(int64_t)K * D + d];
+    if (flags & MOE_REF_ACCUMULATE)
+      out[d] = out[d] + acc;
+    else
+      out[d] = acc;
+  }
+}
+
+int moe_ref_layer_forward(const moe_ref_config *cfg, const moe_ref_layer *layer, const float *x,
+                          int S, float *out, unsigned flags) {
+  if (!layer_ok(cfg, layer) || !x || !out || S < 1) return -1;
+  const int D = cfg->D, K = cfg->K, slots = cfg->K + cfg->n_shared;
+  int32_t idx[64];
+  float w[64];
+  int8_t *xq = (int8_t *)malloc((size_t)D);
+  float *stage = (float *)malloc((size_t)slots * D * sizeof(float));
+  if (!xq || !stage) { free(xq); free(stage); return -2; }
+  int rc = 0;
+  for (int s = 0; s < S && rc == 0; s++) {
+    const float *xs = x + (int64_t)s * D;
+    rc = moe_ref_router_topk(cfg, xs, 1, layer->router_w, layer->router_b, idx, w, NULL, NULL);
+    if (rc) break;
+    float sxs = moe_ref_quant_row_i8(xs, D, xq);
+    for (int k = 0; k < K && rc == 0; k++)
+      rc = moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, &layer->experts[idx[k]],
+                                    stage + (int64_t)k * D, NULL, NULL, NULL, NULL);
+    if (rc == 0 && cfg->n_shared == 1)
+      rc = moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, layer->shared, stage + (int64_t)K * D, NULL,
+                                    NULL, NULL, NULL);
+    if (rc == 0) combine_row(cfg, w, stage, out + (int64_t)s * D, flags);
+  }
+  free(xq);
+  free(stage);
+  return rc;
+}
+
+int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                const float *x, int S, float *out, unsigned flags, int32_t *idx_out,
+                                float *w_out, int32_t *uniq_out, int32_t *n_uniq_out) {
+  if (!layer_ok(cfg, layer) || !x || !out || S < 1) return -1;
+  const int D = cfg->D, E = cfg->E, K = cfg->K, slots = cfg->K + cfg->n_shared;
+  int32_t *idx = (int32_t *)malloc((size_t)S * K * sizeof(int32_t));
+  float *w = (float *)malloc((size_t)S * K * sizeof(float));
+  int8_t *xq = (int8_t *)malloc((size_t)S * D);
+  float *sx = (float *)malloc((size_t)S * sizeof(float));
+  float *stage = (float *)malloc((size_t)S * slots * D * sizeof(float));
+  int32_t *uniq = (int32_t *)malloc((size_t)E * sizeof(int32_t));
+  unsigned char *seen = (unsigned char *)calloc((size_t)E, 1);
+  int32_t *rows = (int32_t *)malloc((size_t)S * sizeof(int32_t));
+  int32_t *slot = (int32_t *)malloc((size_t)S * sizeof(int32_t));
+  int8_t *xg = (int8_t *)malloc((size_t)S * D);
+  float *sg = (float *)malloc((size_t)S * sizeof(float));
+  float *yg = (float *)malloc((size_t)S * D * sizeof(float));
+  int rc = -2;
+  if (!idx || !w || !xq || !sx || !stage || !uniq || !seen || !rows || !slot || !xg || !sg || !yg)
+    goto done;
+  rc = moe_ref_router_topk(cfg, x, S, layer->router_w, layer->router_b, idx, w, NULL, NULL);
+  if (rc) goto done;
+  moe_ref_quant_act_i8(x, S, D, xq, sx);
+  /* union of the selected experts, in order of first appearance */
+  int nu = 0;
+  for (int s = 0; s < S; s++)
+    for (int k = 0; k < K; k++) {
+      int e = idx[(int64_t)s * K + k];
+      if (!seen[e]) { seen[e] = 1; uniq[nu++] = e; }
+    }
+  for (int u = 0; u < nu && rc == 0; u++) {
+    int e = uniq[u], nr = 0;
+    for (int s = 0; s < S; s++)
+      for (int k = 0; k < K; k++)
+        if (idx[(int64_t)s * K + k] == e) { rows[nr] = s; slot[nr] = k; nr++; }
+    for (int r = 0; r < nr; r++) {
+      memcpy(xg + (int64_t)r * D, xq + (int64_t)rows[r] * D, (size_t)D);
+      sg[r] = sx[rows[r]];
+    }
+    rc = moe_ref_expert_swiglu_i4(cfg, xg, sg, nr, &layer->experts[e], yg, NULL, NULL, NULL, NULL);
+    for (int r = 0; r < nr && rc == 0; r++)
+      memcpy(stage + ((int64_t)rows[r] * slots + slot[r]) * D, yg + (int64_t)r * D,
+             (size_t)D * sizeof(float));
+  }
+  if (rc == 0 && cfg->n_shared == 1) {
+    /* the shared expert is read once and applied to every row */
+    rc = moe_ref_expert_swiglu_i4(cfg, xq, sx, S, layer->shared, yg, NULL, NULL, NULL, NULL);
+    for (int s = 0; s < S && rc == 0; s++)
+      memcpy(stage + ((int64_t)s * slots + K) * D, yg + (int64_t)s * D, (size_t)D * sizeof(float));
+  }
+  if (rc == 0)
+    for (int s = 0; s < S; s++)
+      combine_row(cfg, w + (int64_t)s * K, stage + (int64_t)s * slots * D, out + (int64_t)s * D,
+                  flags);
+  if (rc == 0) {
+    if (idx_out) memcpy(idx_out, idx, (size_t)S * K * sizeof(int32_t));
+    if (w_out) memcpy(w_out, w, (size_t)S * K * sizeof(float));
+    if (uniq_out) memcpy(uniq_out, uniq, (size_t)nu * sizeof(int32_t));
+    if (n_uniq_out) *n_uniq_out = nu;
+  }
+done:
+  free(idx); free(w); free(xq); free(sx); free(stage); free(uniq); free(seen);
+  free(rows); free(slot); free(xg); free(sg); free(yg);
+  return rc;
+}
+
+/* ---- section 04: RMSNorm ---------------------------------------------------- */
+
+int moe_ref_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y) {
+  if (!x || !gamma || !y || S < 1 || D < 1) return -1;
+  for (int s = 0; s < S; s++) {
+    const float *xs = x + (int64_t)s * D;
+    float *ys = y + (int64_t)s * D;
+    double ms = 0.0;
+    for (int i = 0; i < D; i++) ms += (double)xs[i] * xs[i];
+    float r = 1.f / sqrtf((float)(ms / D) + eps);
+    for (int i = 0; i < D; i++) ys[i] = xs[i] * r * gamma[i];
+  }
+  return 0;
+}

@@ -1,0 +1,127 @@
+/*
+ * moe_ref.h -- CPU oracle for the routed-expert int4 MoE block.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is a plain, slow, single-threaded C model of
+ * what the block computes, used to check the GPU library.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it; the product
+ * library never calls it and shares no code with it.
+ *
+ * Source: the reader.mx article "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型"
+ * (called "the article" below), whose listings define every step:
+ *   - section 04 (RMSNorm, SiLU, layer order),
+ *   - section 06 (per-row int4 quantization and nibble packing),
+ *   - section 11 (sigmoid router with correction bias, top-K, unique-expert
+ *     union, SwiGLU expert, weighted scatter),
+ *   - section 12 (per-row int8 activation quantization; integer dot products
+ *     scaled by the weight and activation scales; activations are quantized in
+ *     front of every integer matmul).
+ * Readings of points the article leaves open are stated next to the function
+ * that takes them.
+ *
+ * All pointers are host pointers.  Matrices are row-major.  A packed int4
+ * matrix with O rows and C columns is q4[O][(C+1)/2] bytes plus scale[O];
+ * byte j of a row holds column 2j in its low nibble and column 2j+1 in its high
+ * nibble, each stored as q + 8.
+ *
+ * Functions return 0 on success and a negative value on invalid arguments.
+ */
+#ifndef MOE_REF_H
+#define MOE_REF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t D;          /* hidden size */
+  int32_t I;          /* expert intermediate size */
+  int32_t E;          /* routed experts */
+  int32_t K;          /* experts per token */
+  int32_t n_shared;   /* 0 or 1 shared expert */
+  float routed_scale; /* routed scaling factor (2.5 for the GLM shape) */
+} moe_ref_config;
+
+typedef struct {
+  const uint8_t *q4;  /* [O][(C+1)/2] */
+  const float *scale; /* [O] */
+} moe_ref_qmat;
+
+typedef struct {
+  moe_ref_qmat gate; /* O = I, C = D */
+  moe_ref_qmat up;   /* O = I, C = D */
+  moe_ref_qmat down; /* O = D, C = I */
+} moe_ref_expert;
+
+typedef struct {
+  const float *router_w;         /* [E][D] */
+  const float *router_b;         /* [E] correction bias */
+  const moe_ref_expert *experts; /* [E]; an entry may hold NULLs if never selected */
+  const moe_ref_expert *shared;  /* used when n_shared == 1 */
+} moe_ref_layer;
+
+enum { MOE_REF_ACCUMULATE = 1 };
+
+/* Section 06: per-row symmetric int4 quantization, s = max(amax/7, 1e-8),
+ * q = clamp(lrint(w/s), -8, 7), two nibbles per byte as q+8, even column in
+ * the low nibble.  An odd last column is padded with nibble 8 (value 0). */
+int moe_ref_pack_int4(const float *w, int O, int C, uint8_t *q4, float *scale);
+
+/* Inverse of the nibble packing: q[o][c] = nibble - 8. */
+int moe_ref_unpack_int4(const uint8_t *q4, int O, int C, int8_t *q);
+
+/* Section 12: per-row int8 activation quantization of n floats,
+ * s = max(amax/127, 1e-12), q = lrint(x * (1/s)).  Returns s. */
+float moe_ref_quant_row_i8(const float *x, int n, int8_t *q);
+
+/* Row-wise quantization of x[S][D] (f32) or of bf16 bit patterns widened to
+ * f32 exactly (section 08 widens bf16 by a 16-bit shift). */
+int moe_ref_quant_act_i8(const float *x, int S, int D, int8_t *xq, float *sx);
+int moe_ref_quant_act_i8_bf16(const uint16_t *x, int S, int D, int8_t *xq, float *sx);
+
+/* Exact integer dot of one packed int4 row of C columns with C int8 values. */
+int32_t moe_ref_dot_i4_i8(const uint8_t *q4row, const int8_t *x, int C);
+
+/* Section 11 router for S tokens: logits[s][e] = x[s] . W[e] (accumulated in
+ * double, rounded once to float), sig = 1/(1+exp(-logit)), choice = sig + b;
+ * K passes pick the largest choice not yet taken (strict >, experts scanned in
+ * ascending order, so ties go to the lowest index); weight = sig * scale.
+ * Outputs: idx[S][K], w[S][K]; logits[S][E] and choice[S][E] are optional. */
+int moe_ref_router_topk(const moe_ref_config *cfg, const float *x, int S, const float *router_w,
+                        const float *router_b, int32_t *idx, float *w, float *logits,
+                        float *choice);
+
+/* One SwiGLU expert applied to S quantized rows (sections 11 and 12).
+ * y[S][D] is the unweighted expert output.  Optional outputs: acc_gu[S][2][I]
+ * (gate then up int32 accumulators), hq[S][I] and sh[S] (requantized SwiGLU
+ * output), acc_d[S][D] (down-projection int32 accumulators). */
+int moe_ref_expert_swiglu_i4(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
+                             const moe_ref_expert *e, float *y, int32_t *acc_gu, int8_t *hq,
+                             float *sh, int32_t *acc_d);
+
+/* The block for S tokens, one token at a time: route, quantize the token,
+ * run its K experts and the shared expert, and combine
+ * out = sum_k w_k * y_k (k ascending, from 0) + y_shared.
+ * With MOE_REF_ACCUMULATE the result is added to out (residual). */
+int moe_ref_layer_forward(const moe_ref_config *cfg, const moe_ref_layer *layer, const float *x,
+                          int S, float *out, unsigned flags);
+
+/* Same block through the section 11 unique-expert union: the experts selected
+ * by any token are visited once each in order of first appearance, each one
+ * applied to all its rows; per-(token, slot) results are staged and combined
+ * in the same order as layer_forward, so the two agree bit for bit.
+ * Optional outputs: idx[S][K], w[S][K], uniq[E] and n_uniq. */
+int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                const float *x, int S, float *out, unsigned flags, int32_t *idx,
+                                float *w, int32_t *uniq, int32_t *n_uniq);
+
+/* Section 04 RMSNorm: ms = mean of squares in double, r = 1/sqrtf(ms + eps),
+ * y = x * r * gamma. */
+int moe_ref_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_REF_H */
