@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the GLM-shape routed-expert int4 MoE layer on one MI355X.
+
+Workload (one "step" = one pass of the whole block for one token): a GLM-5.2
+MoE layer (hidden 6144, 256 routed experts with gate/up 2048x6144 and down
+6144x2048 in packed int4 with a float scale per row, one shared expert of the
+same shape, float32 sigmoid router 256x6144 plus correction bias, top-8,
+routed scaling 2.5) applied to one token: router, top-8, int8 activation
+quantization, 9 SwiGLU experts, weighted combine.  Weights and activations
+are seeded synthetic data already resident in HBM.
+
+Steps cycle over R independent layer replicas (different seeds) and 256
+distinct tokens, so that consecutive steps never find a layer's weights in
+the 256 MB last-level cache (a real decode visits every other layer in
+between).  The timed region is K back-to-back calls of moe_layer_forward on
+one stream, bracketed by device synchronization; HIP events recorded around
+the second and third launches of every step give their average durations.
+The second launch (routed gate/up + shared-expert down, 107 MB of weights)
+is the dominant kernel reported in "roofline".
+
+Prints one JSON line.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+D, I, E, K = 6144, 2048, 256, 8
+EXPERT_GATEUP_BYTES = 2 * I * (D // 2) + 2 * I * 4          # 12,599,296
+EXPERT_DOWN_BYTES = D * (I // 2) + D * 4                     # 6,316,032
+EXPERT_BYTES = EXPERT_GATEUP_BYTES + EXPERT_DOWN_BYTES       # 18,915,328
+ROUTER_BYTES = E * D * 4 + E * 4                             # 6,292,480
+LAYER_TOKEN_BYTES = 9 * EXPERT_BYTES + ROUTER_BYTES + 2 * D * 4  # 176,579,584
+# the three launches of one decode step (algorithmic weight bytes)
+PHASE_A_BYTES = ROUTER_BYTES + EXPERT_GATEUP_BYTES           # router + shared gate/up
+PHASE_B_BYTES = K * EXPERT_GATEUP_BYTES + EXPERT_DOWN_BYTES  # routed gate/up + shared down
+PHASE_C_BYTES = K * EXPERT_DOWN_BYTES                        # routed down
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(n_tokens: int, seed: int = 0):
+    """The CPU oracle (single-threaded C) on a bounded sample of the same
+    workload: n_tokens decode tokens through replica 0."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from oracle.layers import LazyLayer, bias_for
+
+    L = LazyLayer(seed, synth.GLM, 0, bias_for("uniform", seed, synth.GLM))
+    x = synth.activations(seed, n_tokens, D)
+    L.ensure_for(x)
+    t0 = time.perf_counter()
+    for s in range(n_tokens):
+        oracle.layer_forward(L, x[s:s + 1])
+    dt = time.perf_counter() - t0
+    return dict(value=round(dt / n_tokens * 1e6, 1), unit="us/token", cores=1, kind="oracle",
+                sample=f"{n_tokens} GLM-shape decode tokens (seed {seed}) through one layer, "
+                       f"oracle per-token path, single-threaded C",
+                seconds=round(dt, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int4_expert_gemv_moe_amd as moe
+    import synth
+    from synth.device_layers import build_device_layer
+
+    torch.cuda.set_device(0)
+    lib = moe.lib()
+    t0 = time.time()
+    layers = []
+    for r in range(args.replicas):
+        b = synth.router_b_uniform(r, synth.GLM, r)
+        layers.append(build_device_layer(r, synth.GLM, r, b))
+    torch.cuda.synchronize()
+    log(f"built {args.replicas} layer replicas in {time.time() - t0:.1f}s")
+    T = args.tokens
+    x = torch.from_numpy(synth.activations(7, T, D)).cuda()
+    out = torch.empty(T, D, dtype=torch.float32, device="cuda")
+    cfg = layers[0].cfg
+    ws = moe.Workspace(cfg, 1, moe.WS_FORWARD)
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    lstructs = [l.cstruct() for l in layers]
+    lrefs = [ctypes.byref(s) for s in lstructs]
+    cref = ctypes.byref(cfg)
+    xp = [ctypes.c_void_p(x[t].data_ptr()) for t in range(T)]
+    op = [ctypes.c_void_p(out[t].data_ptr()) for t in range(T)]
+    fn = lib.moe_layer_forward
+    R = args.replicas
+
+    def run(n, probes=None):
+        rc = 0
+        for i in range(n):
+            pr = probes[i] if probes is not None else None
+            rc |= fn(cref, lrefs[i % R], xp[i % T], 1, op[i % T], 0, pr, ws.ptr, ws.nbytes, st)
+        if rc:
+            raise moe.MoeError(f"moe_layer_forward failed ({rc})")
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    # events around the gate/up and down kernels of every timed step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e4 in evs:
+        for e in e4:
+            e.record(stream)
+    torch.cuda.synchronize()
+    probes = []
+    for e4 in evs:
+        p = moe.Probe()
+        p.ev_gateup[0], p.ev_gateup[1] = e4[0].cuda_event, e4[1].cuda_event
+        p.ev_down[0], p.ev_down[1] = e4[2].cuda_event, e4[3].cuda_event
+        probes.append(ctypes.byref(p))
+        e4.append(p)  # keep the struct alive
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    run(args.steps, probes)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    us_per_token = elapsed / args.steps * 1e6
+    gu = np.array([e4[0].elapsed_time(e4[1]) for e4 in evs]) * 1e3  # us
+    dn = np.array([e4[2].elapsed_time(e4[3]) for e4 in evs]) * 1e3
+    gu_avg, dn_avg = float(gu.mean()), float(dn.mean())
+    achieved = PHASE_B_BYTES / (gu_avg * 1e-6) / 1e9
+    log(f"step {us_per_token:.2f} us/token; phase B {gu_avg:.2f} us (p50 {np.median(gu):.2f}, "
+        f"{achieved:.0f} GB/s); phase C {dn_avg:.2f} us ({PHASE_C_BYTES / dn_avg / 1e3:.0f} GB/s); "
+        f"layer {LAYER_TOKEN_BYTES / us_per_token / 1e3:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(args.cpu_tokens)
+        log(f"oracle: {cpu['value']} us/token")
+
+    layer_gbps = LAYER_TOKEN_BYTES / (us_per_token * 1e-6) / 1e9
+    rec = {
+        "metric": "MoE layer decode us/token + achieved HBM GB/s (frac of peak); prefill TOPS",
+        "value": round(us_per_token, 3),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_token / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xint8->int32, f32 epilogue",
+        "data": "synthetic (seeded N(0,0.02) weights packed to int4, N(0,1) activations)",
+        "config": {"workload": "GLM-shape MoE layer decode, 1 token/step (hidden 6144, 256 "
+                               "experts top-8 + 1 shared, int4 experts 2048x6144)",
+                   "global_batch": 1, "layer_replicas": R, "distinct_tokens": T},
+        "tokens_per_s": round(1e6 / us_per_token, 1),
+        "layer_bytes_per_token": LAYER_TOKEN_BYTES,
+        "layer_GBps": round(layer_gbps, 1),
+        "layer_frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
+        "kernels_us": {"phase_b_routed_gateup_shared_down": round(gu_avg, 3),
+                       "phase_c_routed_down_combine": round(dn_avg, 3)},
+        "roofline": {"bound": "hbm", "kernel": "decode_b_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": PHASE_B_BYTES},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

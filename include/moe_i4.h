@@ -1,0 +1,174 @@
+/*
+ * moe_i4.h -- C ABI of the MI355X (gfx950) routed-expert int4 MoE block.
+ *
+ * The block is the one described by the reader.mx article "惊呆了！25GB 内存上
+ * 运行 GLM 5.2 744B 模型" (cited below as "the article"):
+ *   - section 02: the GLM-5.2 shape (hidden 6144, 256 routed experts, top-8,
+ *     one shared expert, expert intermediate size 2048, sigmoid scoring,
+ *     routed scaling factor 2.5);
+ *   - section 06: the int4 weight container (per-row symmetric scale
+ *     amax/7, values clamped to [-8, 7], two per byte as value+8, even column
+ *     in the low nibble, one float scale per row);
+ *   - section 11: the router (sigmoid of the logits plus a correction bias
+ *     picks the top K experts; the weight is the unbiased sigmoid times the
+ *     routed scaling factor), the SwiGLU expert, and the unique-expert union
+ *     used to run a batch of tokens with each selected expert read once;
+ *   - section 12: per-row int8 activation quantization (scale amax/127,
+ *     floored at 1e-12, round half to even) in front of every integer matmul,
+ *     integer dot products rescaled by the weight and activation scales.
+ *
+ * Conventions
+ *   - Every pointer is a DEVICE pointer unless its comment says "host".
+ *   - Matrices are row-major.  A packed int4 matrix with O rows and C columns
+ *     is q4[O][C/2] bytes plus scale[O] floats.
+ *   - All calls are asynchronous on the given HIP stream and return a
+ *     moe_status.  Arguments are validated on the host before anything is
+ *     enqueued; an invalid call enqueues nothing.  No call allocates, frees or
+ *     keeps device memory: scratch space comes from the caller's workspace.
+ *   - Calls that take a workspace need it zero-filled once by
+ *     moe_workspace_init; every call leaves its counters at zero again.  Calls
+ *     that share one workspace must not overlap (use one workspace per
+ *     concurrent stream).
+ *   - Shape limits: D and I multiples of 32, 1 <= K <= E <= 1024, K <= 64,
+ *     n_shared 0 or 1, S >= 1.  q4, scale and activation buffers must be
+ *     16-byte aligned.  The device must be a gfx950.
+ */
+#ifndef MOE_I4_H
+#define MOE_I4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,     /* null pointer or bad scalar argument */
+  MOE_ESHAPE = -2,     /* shape outside the supported limits */
+  MOE_EALIGN = -3,     /* a buffer is not 16-byte aligned */
+  MOE_EWORKSPACE = -4, /* workspace too small */
+  MOE_EHIP = -5,       /* a HIP launch or runtime call failed */
+  MOE_EDEVICE = -6     /* current device is not a gfx950 */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Flags of the layer calls. */
+#define MOE_F_ACCUMULATE 1u /* out += block(x) instead of out = block(x) */
+
+typedef struct {
+  int32_t D;          /* hidden size (6144 for the GLM shape) */
+  int32_t I;          /* expert intermediate size (2048) */
+  int32_t E;          /* routed experts (256) */
+  int32_t K;          /* experts per token (8) */
+  int32_t n_shared;   /* shared experts, 0 or 1 */
+  float routed_scale; /* routed scaling factor (2.5) */
+} moe_config;
+
+/* One packed int4 matrix per expert, stacked over experts.  Expert e's matrix
+ * starts at q4 + e*q4_stride bytes and its scales at scale + e*scale_stride
+ * floats.  A stride of 0 means densely stacked (O*C/2 bytes, O floats), so
+ * e.g. gate.q4 may point at a [E][I][D/2] array.  Non-zero strides allow the
+ * article's section 13 slab layout (gate, up and down of one expert adjacent). */
+typedef struct {
+  const uint8_t *q4;
+  const float *scale;
+  int64_t q4_stride;
+  int64_t scale_stride;
+} moe_qmat;
+
+typedef struct {
+  moe_qmat gate; /* O = I, C = D */
+  moe_qmat up;   /* O = I, C = D */
+  moe_qmat down; /* O = D, C = I */
+} moe_experts;
+
+typedef struct {
+  const float *router_w; /* [E][D] float32 */
+  const float *router_b; /* [E] float32 correction bias */
+  moe_experts routed;    /* E experts */
+  moe_experts shared;    /* one expert; read only when n_shared == 1 */
+} moe_layer;
+
+/* Optional outputs of the layer calls (host struct; any member may be NULL). */
+typedef struct {
+  int32_t *topk_idx;    /* [S][K] experts chosen for each token, in selection order */
+  float *topk_w;        /* [S][K] their weights */
+  hipEvent_t ev_gateup[2]; /* if both set: recorded around the gate/up kernel */
+  hipEvent_t ev_down[2];   /* if both set: recorded around the down kernel */
+} moe_probe;
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_str(int status);
+
+/* Workspace bytes needed by a call with S tokens.  which: 0 = moe_layer_forward,
+ * 1 = moe_layer_forward_batch, 2 = moe_expert_swiglu_i4, 3 = moe_router_topk.
+ * Returns 0 for invalid arguments. */
+size_t moe_workspace_bytes(const moe_config *cfg, int S, int which);
+
+/* Zero-fill a workspace (once, before its first use). */
+int moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Section 06 converter: quantize w[O][C] (float32) to the int4 container,
+ * q4[O][C/2] and scale[O].  C must be even.  Bit-exact with the article's
+ * packer (division by the scale, round half to even, clamp to [-8, 7]). */
+int moe_pack_int4(const float *w, int O, int C, uint8_t *q4, float *scale, hipStream_t stream);
+
+/* Section 12: per-row int8 quantization of x[S][D] (float32, or bf16 widened
+ * exactly).  Outputs xq[S][D] and sx[S].  D must be a multiple of 8. */
+int moe_quant_act_i8(const void *x, moe_dtype dtype, int S, int D, int8_t *xq, float *sx,
+                     hipStream_t stream);
+
+/* Section 11 router for S tokens x[S][D]: logits = x . router_w^T in float32,
+ * sig = 1/(1+exp(-logit)), choice = sig + router_b; K passes take the largest
+ * choice not yet taken (ties to the lowest expert index; NaN choices and
+ * choices <= -1e30 are never taken unless fewer than K candidates remain, in
+ * which case the lowest untaken indices fill the rest).  Outputs
+ * topk_idx[S][K] (selection order) and topk_w[S][K] = routed_scale * sig;
+ * logits[S][E] is optional (NULL to skip).  D must be a multiple of 256. */
+int moe_router_topk(const moe_config *cfg, const float *x, int S, const float *router_w,
+                    const float *router_b, int32_t *topk_idx, float *topk_w, float *logits,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* One SwiGLU expert (sections 11 and 12) on S already-quantized rows
+ * xq[S][D], sx[S]: g = (acc_g * s_g) * s_x, u likewise, h = silu(g) * u,
+ * h requantized per row to (hq, sh), y = (acc_d * s_d) * sh.  The expert is
+ * number `expert` of the stacked matrices in *w (host struct).  Outputs
+ * y[S][D] (unweighted); optional integer probes acc_gu[S][2][I] (gate then
+ * up), hq[S][I], sh[S], acc_d[S][D]. */
+int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *sx, int S,
+                         const moe_experts *w, int expert, float *y, int32_t *acc_gu, int8_t *hq,
+                         float *sh, int32_t *acc_d, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The block, one token at a time (each token reads its own K experts):
+ * route, quantize, run the K routed experts and the shared expert, and
+ * combine out[s] = sum_k w_k * y_k (k in selection order, from 0) + y_shared.
+ * With MOE_F_ACCUMULATE the result is added to out.  x and out must not
+ * overlap.  probe is optional (host struct). */
+int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                      float *out, unsigned flags, const moe_probe *probe, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* The same block through the unique-expert union (section 11): tokens are
+ * grouped by selected expert and every selected expert's weights are read
+ * once for all its tokens.  Per-(token, slot) results are staged and combined
+ * in the same order as moe_layer_forward, so the two calls return identical
+ * bits for the same inputs. */
+int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                            float *out, unsigned flags, const moe_probe *probe, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Section 04 RMSNorm: y = x * (1/sqrt(mean(x^2) + eps)) * gamma per row,
+ * with the mean of squares accumulated in double. */
+int moe_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y,
+                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_I4_H */

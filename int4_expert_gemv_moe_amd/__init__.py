@@ -1,0 +1,296 @@
+"""Python binding of libmoe_i4.so, the gfx950 routed-expert int4 MoE block.
+
+Argument marshalling only: every function here checks Python-side types,
+passes device pointers of torch tensors and the current HIP stream to the
+C ABI declared in include/moe_i4.h, and raises on a non-zero status.  All
+arithmetic runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or the device is not a gfx950 the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+# MOE_I4_LIB may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MOE_I4_LIB") or os.path.join(HERE, "libmoe_i4.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+F_ACCUMULATE = 1
+WS_FORWARD, WS_BATCH, WS_SWIGLU, WS_ROUTER = 0, 1, 2, 3
+
+_lib = None
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("D", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float)]
+
+
+class QMat(ctypes.Structure):
+    _fields_ = [("q4", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("q4_stride", ctypes.c_int64), ("scale_stride", ctypes.c_int64)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+class LayerC(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("routed", Experts), ("shared", Experts)]
+
+
+class Probe(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("ev_gateup", ctypes.c_void_p * 2), ("ev_down", ctypes.c_void_p * 2)]
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libmoe_i4.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"{LIB_PATH} is not built; run int4_expert_gemv_moe_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, f32, u32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float,
+                                 ctypes.c_uint)
+        L.moe_status_str.argtypes = [i32]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_workspace_bytes.argtypes = [vp, i32, i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_init.argtypes = [vp, sz, vp]
+        L.moe_pack_int4.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_quant_act_i8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.moe_router_topk.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_swiglu_i4.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
+        L.moe_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
+        L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp, vp]
+        for name in ("moe_workspace_init", "moe_pack_int4", "moe_quant_act_i8", "moe_router_topk",
+                     "moe_expert_swiglu_i4", "moe_layer_forward", "moe_layer_forward_batch",
+                     "moe_rmsnorm"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(rc: int) -> str:
+    return lib().moe_status_str(rc).decode()
+
+
+def _check(rc: int, name: str) -> None:
+    if rc != 0:
+        raise MoeError(f"{name}: {status_str(rc)} ({rc})")
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise MoeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    return t
+
+
+def config(D: int, I: int, E: int, K: int, n_shared: int = 1, routed_scale: float = 2.5) -> Config:
+    return Config(D, I, E, K, n_shared, routed_scale)
+
+
+# ---- device weights -----------------------------------------------------------
+
+@dataclass
+class DeviceExperts:
+    """Stacked int4 experts on the device: gate/up q4 [n][I][D/2], scales
+    [n][I]; down q4 [n][D][I/2], scales [n][D]."""
+    gate_q4: torch.Tensor
+    gate_s: torch.Tensor
+    up_q4: torch.Tensor
+    up_s: torch.Tensor
+    down_q4: torch.Tensor
+    down_s: torch.Tensor
+
+    @staticmethod
+    def empty(n: int, D: int, I: int, device="cuda") -> "DeviceExperts":
+        u8, f32 = torch.uint8, torch.float32
+        return DeviceExperts(torch.empty(n, I, D // 2, dtype=u8, device=device),
+                             torch.empty(n, I, dtype=f32, device=device),
+                             torch.empty(n, I, D // 2, dtype=u8, device=device),
+                             torch.empty(n, I, dtype=f32, device=device),
+                             torch.empty(n, D, I // 2, dtype=u8, device=device),
+                             torch.empty(n, D, dtype=f32, device=device))
+
+    def cstruct(self) -> Experts:
+        def q(a, b):
+            return QMat(a.data_ptr(), b.data_ptr(), 0, 0)
+        return Experts(q(self.gate_q4, self.gate_s), q(self.up_q4, self.up_s),
+                       q(self.down_q4, self.down_s))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.gate_q4, self.gate_s, self.up_q4, self.up_s, self.down_q4, self.down_s))
+
+
+@dataclass
+class DeviceLayer:
+    cfg: Config
+    router_w: torch.Tensor  # [E][D] float32
+    router_b: torch.Tensor  # [E] float32
+    routed: DeviceExperts   # E experts
+    shared: DeviceExperts | None  # 1 expert when cfg.n_shared == 1
+
+    def cstruct(self) -> LayerC:
+        sh = self.shared.cstruct() if self.shared is not None else Experts()
+        return LayerC(self.router_w.data_ptr(), self.router_b.data_ptr(), self.routed.cstruct(), sh)
+
+
+class Workspace:
+    """Device scratch for the calls; zero-filled once on creation."""
+
+    def __init__(self, cfg: Config, S: int, which: int, device="cuda"):
+        n = lib().moe_workspace_bytes(ctypes.byref(cfg), S, which)
+        if n == 0:
+            raise MoeError("moe_workspace_bytes rejected the configuration")
+        self.nbytes = int(n)
+        self.buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.buf.data_ptr()) % 256
+        self.view = self.buf[off: off + self.nbytes]
+        _check(lib().moe_workspace_init(ctypes.c_void_p(self.view.data_ptr()), self.nbytes,
+                                        ctypes.c_void_p(_stream())), "moe_workspace_init")
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.view.data_ptr())
+
+
+# ---- entry points ------------------------------------------------------------
+
+def moe_pack_int4(w: torch.Tensor, q4: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                  stream=None):
+    """Section 06 converter on the device: w [O][C] float32 -> (q4 [O][C/2], scale [O])."""
+    _dev(w, torch.float32, "w")
+    O, C = w.shape
+    q4 = torch.empty(O, C // 2, dtype=torch.uint8, device=w.device) if q4 is None else q4
+    scale = torch.empty(O, dtype=torch.float32, device=w.device) if scale is None else scale
+    _check(lib().moe_pack_int4(_ptr(w), O, C, _ptr(q4), _ptr(scale), ctypes.c_void_p(_stream(stream))),
+           "moe_pack_int4")
+    return q4, scale
+
+
+def moe_quant_act_i8(x: torch.Tensor, stream=None):
+    """Per-row int8 quantization of x [S][D] (float32 or bfloat16)."""
+    if x.dtype == torch.float32:
+        dt = MOE_F32
+    elif x.dtype == torch.bfloat16:
+        dt = MOE_BF16
+    else:
+        raise MoeError("x must be float32 or bfloat16")
+    _dev(x, x.dtype, "x")
+    S, D = x.shape
+    xq = torch.empty(S, D, dtype=torch.int8, device=x.device)
+    sx = torch.empty(S, dtype=torch.float32, device=x.device)
+    _check(lib().moe_quant_act_i8(_ptr(x), dt, S, D, _ptr(xq), _ptr(sx),
+                                  ctypes.c_void_p(_stream(stream))), "moe_quant_act_i8")
+    return xq, sx
+
+
+def moe_router_topk(cfg: Config, x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Tensor,
+                    ws: Workspace, want_logits: bool = False, stream=None):
+    _dev(x, torch.float32, "x")
+    S = x.shape[0]
+    idx = torch.empty(S, cfg.K, dtype=torch.int32, device=x.device)
+    w = torch.empty(S, cfg.K, dtype=torch.float32, device=x.device)
+    logits = torch.empty(S, cfg.E, dtype=torch.float32, device=x.device) if want_logits else None
+    _check(lib().moe_router_topk(ctypes.byref(cfg), _ptr(x), S, _ptr(router_w), _ptr(router_b),
+                                 _ptr(idx), _ptr(w), _ptr(logits), ws.ptr, ws.nbytes,
+                                 ctypes.c_void_p(_stream(stream))), "moe_router_topk")
+    return idx, w, logits
+
+
+def moe_expert_swiglu_i4(cfg: Config, xq: torch.Tensor, sx: torch.Tensor, experts: DeviceExperts,
+                         expert: int, ws: Workspace, probes: bool = False, stream=None):
+    _dev(xq, torch.int8, "xq")
+    _dev(sx, torch.float32, "sx")
+    S = xq.shape[0]
+    dev = xq.device
+    y = torch.empty(S, cfg.D, dtype=torch.float32, device=dev)
+    acc_gu = hq = sh = acc_d = None
+    if probes:
+        acc_gu = torch.empty(S, 2, cfg.I, dtype=torch.int32, device=dev)
+        hq = torch.empty(S, cfg.I, dtype=torch.int8, device=dev)
+        sh = torch.empty(S, dtype=torch.float32, device=dev)
+        acc_d = torch.empty(S, cfg.D, dtype=torch.int32, device=dev)
+    es = experts.cstruct()
+    _check(lib().moe_expert_swiglu_i4(ctypes.byref(cfg), _ptr(xq), _ptr(sx), S, ctypes.byref(es),
+                                      expert, _ptr(y), _ptr(acc_gu), _ptr(hq), _ptr(sh), _ptr(acc_d),
+                                      ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
+           "moe_expert_swiglu_i4")
+    return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
+
+
+def _probe(topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None):
+    p = Probe()
+    p.topk_idx = None if topk_idx is None else topk_idx.data_ptr()
+    p.topk_w = None if topk_w is None else topk_w.data_ptr()
+    if ev_gateup is not None:
+        p.ev_gateup[0], p.ev_gateup[1] = ev_gateup
+    if ev_down is not None:
+        p.ev_down[0], p.ev_down[1] = ev_down
+    return p
+
+
+def _layer_call(fn_name, layer: DeviceLayer, x, out, flags, ws, topk_idx, topk_w, ev_gateup,
+                ev_down, stream):
+    _dev(x, torch.float32, "x")
+    S = x.shape[0]
+    if out is None:
+        out = torch.empty(S, layer.cfg.D, dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    L = layer.cstruct()
+    probe = _probe(topk_idx, topk_w, ev_gateup, ev_down)
+    fn = getattr(lib(), fn_name)
+    _check(fn(ctypes.byref(layer.cfg), ctypes.byref(L), _ptr(x), S, _ptr(out), flags,
+              ctypes.byref(probe), ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))), fn_name)
+    return out
+
+
+def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None, flags: int = 0,
+                      topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None, stream=None):
+    """Per-token path: each token reads its own K experts and the shared one."""
+    return _layer_call("moe_layer_forward", layer, x, out, flags, ws, topk_idx, topk_w, ev_gateup,
+                       ev_down, stream)
+
+
+def moe_layer_forward_batch(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None,
+                            flags: int = 0, topk_idx=None, topk_w=None, ev_gateup=None,
+                            ev_down=None, stream=None):
+    """Unique-expert union path: each selected expert is read once per call."""
+    return _layer_call("moe_layer_forward_batch", layer, x, out, flags, ws, topk_idx, topk_w,
+                       ev_gateup, ev_down, stream)
+
+
+def moe_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out=None, stream=None):
+    _dev(x, torch.float32, "x")
+    S, D = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _check(lib().moe_rmsnorm(_ptr(x), _ptr(gamma), S, D, eps, _ptr(out),
+                             ctypes.c_void_p(_stream(stream))), "moe_rmsnorm")
+    return out

@@ -1,0 +1,808 @@
+// decode.hip -- the per-token ("decode") MoE block in three launches
+// (sections 11 and 12 of the reader.mx article "惊呆了！25GB 内存上运行
+// GLM 5.2 744B 模型"):
+//
+//   phase A  router logits, token quantization    | shared-expert gate/up
+//   phase B  routed gate/up (each block selects   | shared-expert down
+//            its expert from the logits)          |   -> y_shared
+//   phase C  routed down + weighted combine (+ y_shared) -> out
+//
+// The shared expert does not depend on the routing, so its gate/up runs
+// beside the router and its down beside the routed gate/up.  No workgroup
+// waits for another inside a launch (no fences, no shared-address atomics):
+// on this chip a device-scope fence writes back and invalidates the issuing
+// XCD's L2 and a same-address atomic serializes at about 13 ns, so every
+// cross-workgroup hand-off goes through a launch boundary.  The max |h| of a
+// hidden row, needed for its requantization, is kept as one partial maximum
+// per gate/up workgroup and reduced by the consumer.
+//
+// Weight rows stream with 16-byte nontemporal loads: lane l reads bytes
+// 16l + 1024c of a row (c = 1 KB chunk), so one wave instruction covers 1 KB
+// of contiguous HBM.  Each wave walks its rows ROWS at a time and keeps the
+// next step's loads in flight while it computes the current one.
+#include "moe_kernels.h"
+#include "quant.h"
+#include "topk.h"
+
+namespace moe {
+
+// Every kernel here runs 256-thread workgroups (4 waves).
+constexpr int kWaves = 4;
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Unconditional 16-byte nontemporal load of p, or of `safe` when ok is false
+// (the result is then replaced by zeros).  Keeping every load unconditional
+// leaves the wave's code straight-line, so the compiler can wait for exactly
+// the loads a step needs instead of draining all of them at a branch.
+__device__ __forceinline__ uint4 ldnt16(const void *p, bool ok, const void *safe) {
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(ok ? p : safe));
+  return ok ? make_uint4(t.x, t.y, t.z, t.w) : make_uint4(0u, 0u, 0u, 0u);
+}
+
+__device__ __forceinline__ uint4 ld16(const void *p, bool ok, const void *safe) {
+  const uint4 t = *reinterpret_cast<const uint4 *>(ok ? p : safe);
+  return ok ? t : make_uint4(0u, 0u, 0u, 0u);
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+         ((uint32_t)(d & 0xFF) << 24);
+}
+
+// Rows [r0, r1) of block b when n rows are split over nb blocks.
+__device__ __forceinline__ void split_rows(int n, int nb, int b, int &r0, int &r1) {
+  r0 = (int)(((int64_t)n * b) / nb);
+  r1 = (int)(((int64_t)n * (b + 1)) / nb);
+}
+
+// ---- router: one wave computes one logit ----------------------------------------
+//
+// Same arithmetic as router_kernel (router.hip): lane p accumulates
+// fmaf(x[k], W[e][k], acc) for k = 4p + 256j + q, j then q ascending, and the
+// lanes are summed by wave_sum_f32.
+__device__ void router_logit(const DecodeArgs &a, int s, int e) {
+  if (e >= a.E) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int JB = 24;
+  const float4 *wr = reinterpret_cast<const float4 *>(a.W + (int64_t)e * a.D);
+  const float4 *xr = reinterpret_cast<const float4 *>(a.x + (int64_t)s * a.D);
+  const int nj = a.D >> 8;
+  float acc = 0.f;
+  for (int j0 = 0; j0 < nj; j0 += JB) {
+    float4 wv[JB], xv[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; jj++) {
+      wv[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+      xv[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + jj < nj) {
+        const uint4 t = ldnt16(wr + lane + 64 * (j0 + jj), true, wr);
+        wv[jj] = make_float4(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z),
+                             __uint_as_float(t.w));
+        xv[jj] = xr[lane + 64 * (j0 + jj)];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; jj++) {
+      if (j0 + jj < nj) {
+        acc = fmaf(xv[jj].x, wv[jj].x, acc);
+        acc = fmaf(xv[jj].y, wv[jj].y, acc);
+        acc = fmaf(xv[jj].z, wv[jj].z, acc);
+        acc = fmaf(xv[jj].w, wv[jj].w, acc);
+      }
+    }
+  }
+  const float v = wave_sum_f32(acc);
+  if (lane == 0) a.logits[(int64_t)s * a.E + e] = v;
+}
+
+// ---- token activations in the gate/up lanes ---------------------------------------
+
+// Lane l holds x[2048c + 32l .. +32) for chunk c < NCH.
+template <int NCH, bool MASKED>
+__device__ __forceinline__ void load_x_f32(const float *x, int D, float4 (&xf)[NCH][8]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    const int col = 2048 * c + 32 * lane;
+    const bool ok = !MASKED || col < D;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      xf[c][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok) xf[c][i] = reinterpret_cast<const float4 *>(x + col)[i];
+    }
+  }
+}
+
+// The matching 32 permuted codes per chunk from an already quantized row.
+template <int NCH, bool MASKED>
+__device__ __forceinline__ void load_x_codes(const int8_t *xq, int D, uint4 (&xv)[NCH][2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    const int col = 2048 * c + 32 * lane;
+    const bool ok = !MASKED || col < D;
+    xv[c][0] = ld16(xq + col, ok, xq);
+    xv[c][1] = ld16(xq + col + 16, ok, xq);
+  }
+}
+
+// Section 12 quantization of the whole row by one wave (its lanes cover the
+// row, so the maximum is a wave reduction).  Gives the permuted codes of the
+// lane, the scale and the row's code sum; the same bits as quant_row_block.
+template <int NCH>
+__device__ __forceinline__ int quant_x_wave(const float4 (&xf)[NCH][8], uint4 (&xv)[NCH][2],
+                                            float *sx) {
+  float m = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; c++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      m = fmax_nan_skip(m, fabsf(xf[c][i].x));
+      m = fmax_nan_skip(m, fabsf(xf[c][i].y));
+      m = fmax_nan_skip(m, fabsf(xf[c][i].z));
+      m = fmax_nan_skip(m, fabsf(xf[c][i].w));
+    }
+  m = wave_max_f32(m);
+  const float s = quant_scale(m);
+  const float inv = 1.f / s;
+  int sum = 0;
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    uint32_t w[8];
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const float4 p = xf[c][2 * g], q = xf[c][2 * g + 1];
+      const int q0 = quant_code(p.x, inv), q1 = quant_code(p.y, inv), q2 = quant_code(p.z, inv),
+                q3 = quant_code(p.w, inv), q4 = quant_code(q.x, inv), q5 = quant_code(q.y, inv),
+                q6 = quant_code(q.z, inv), q7 = quant_code(q.w, inv);
+      sum += ((q0 + q1) + (q2 + q3)) + ((q4 + q5) + (q6 + q7));
+      w[2 * g] = pack4(q0, q2, q4, q6);
+      w[2 * g + 1] = pack4(q1, q3, q5, q7);
+    }
+    xv[c][0] = make_uint4(w[0], w[1], w[2], w[3]);
+    xv[c][1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+  *sx = s;
+  return wave_sum_i32(sum);
+}
+
+// ---- gate/up rows -----------------------------------------------------------------
+//
+// A block works through a contiguous range of "items" of a concatenated list
+// of (slot, row) pairs: item i is row i % I of slot i / I.  Wave w takes
+// items lo + w*ROWS + k*4*ROWS, ROWS at a time, with the loads of the next
+// step in flight while it computes the current one.
+//
+// The loop body is free of branches around memory instructions: every stage
+// load is issued (past the end of the range it reads a row of the token's
+// own codes, which sit in L2, and the result is unused), and results go to
+// LDS and reach global memory once, after the loop.  Stores count in the same
+// counter as loads here and vector loads complete in issue order, so this is
+// what lets the compiler wait for exactly one stage at a time.
+
+// Most rows a gate/up block may own (its row scales and outputs sit in LDS).
+#define MOE_GU_MAX_ROWS 512
+
+struct GuMats {
+  RowPtr G, U;
+  float *h;  // hidden row of the slot
+};
+
+template <int NCH, int ROWS>
+struct GuStage {
+  uint4 g[ROWS][NCH], u[ROWS][NCH];
+};
+
+template <int NCH, bool MASKED, int ROWS, class Res>
+__device__ __forceinline__ void gu_load(Res res, int I, int rowbytes, int item, int hi,
+                                        const uint8_t *dummy, GuStage<NCH, ROWS> &st) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    const int it = item + r;
+    const bool live = it < hi;  // uniform across the wave
+    const int itc = min(it, hi - 1);
+    const int slot = itc / I;
+    const int row = itc - slot * I;
+    const GuMats m = res(slot);
+    const uint8_t *gr = live ? m.G.q + (int64_t)row * rowbytes : dummy;
+    const uint8_t *ur = live ? m.U.q + (int64_t)row * rowbytes : dummy;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+      const int off = c * 1024 + lane * 16;
+      const bool ok = !MASKED || off < rowbytes;
+      st.g[r][c] = ldnt16(gr + off, ok, gr);
+      st.u[r][c] = ldnt16(ur + off, ok, ur);
+    }
+  }
+}
+
+// Row scales of the block's items [lo, hi) into LDS (one round of loads).
+template <class Res>
+__device__ __forceinline__ void gu_scales(Res res, int I, int lo, int hi, float *gsc, float *usc) {
+  for (int t0 = 0; t0 < hi - lo; t0 += 64 * kWaves) {
+    const int t = t0 + threadIdx.x;
+    const int it = lo + min(t, hi - lo - 1);
+    const int slot = it / I;
+    const int row = it - slot * I;
+    const GuMats m = res(slot);
+    const float g = m.G.s[row], u = m.U.s[row];
+    if (t < hi - lo) {
+      gsc[t] = g;
+      usc[t] = u;
+    }
+  }
+}
+
+template <int NCH, int ROWS>
+__device__ __forceinline__ void gu_step(const GuStage<NCH, ROWS> &st, const uint4 (&xv)[NCH][2],
+                                        int corr, float sxs, int item, int lo, int hi,
+                                        const float *gsc, const float *usc, float *hout,
+                                        int *acco) {
+  const int lane = threadIdx.x & 63;
+  int ag[ROWS], au[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) {
+    ag[r] = 0;
+    au[r] = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+      ag[r] = dot32_i4(st.g[r][c], xv[c][0], xv[c][1], ag[r]);
+      au[r] = dot32_i4(st.u[r][c], xv[c][0], xv[c][1], au[r]);
+    }
+    ag[r] = wave_sum_i32(ag[r]);
+    au[r] = wave_sum_i32(au[r]);
+  }
+  int myg = ag[0], myu = au[0];
+#pragma unroll
+  for (int r = 1; r < ROWS; r++)
+    if (lane == r) {
+      myg = ag[r];
+      myu = au[r];
+    }
+  const int it = item + lane;
+  if (lane < ROWS && it < hi) {
+    const int t = it - lo;
+    const int accg = myg - corr, accu = myu - corr;
+    const float g = ((float)accg * gsc[t]) * sxs;
+    const float u = ((float)accu * usc[t]) * sxs;
+    hout[t] = silu(g) * u;
+    if (acco) {
+      acco[2 * t] = accg;
+      acco[2 * t + 1] = accu;
+    }
+  }
+}
+
+// Shared-memory buffers of a gate/up block.
+struct GuLds {
+  float gsc[MOE_GU_MAX_ROWS], usc[MOE_GU_MAX_ROWS], h[MOE_GU_MAX_ROWS];
+};
+
+// Walks this wave's items with a two-stage pipeline (the caller issued the
+// first stage into sa and staged the row scales), then writes the block's
+// hidden values (and accumulators when acc_gu is set) to global memory.
+template <int NCH, bool MASKED, int ROWS, class Res>
+__device__ __forceinline__ void gu_items(Res res, int I, int rowbytes, int lo, int hi,
+                                         const uint4 (&xv)[NCH][2], int corr, float sxs,
+                                         GuLds &L, int *acco, int32_t *acc_gu,
+                                         const uint8_t *dummy, GuStage<NCH, ROWS> &sa) {
+  const int wave = threadIdx.x >> 6;
+  const int stride = kWaves * ROWS;
+  const int first = lo + wave * ROWS;
+  const int nsteps = (first < hi) ? (hi - first + stride - 1) / stride : 0;
+  GuStage<NCH, ROWS> sb;
+  for (int i = 0; i < nsteps; i += 2) {
+    const int ra = first + i * stride, rb = ra + stride;
+    gu_load<NCH, MASKED, ROWS>(res, I, rowbytes, rb, hi, dummy, sb);
+    gu_step<NCH, ROWS>(sa, xv, corr, sxs, ra, lo, hi, L.gsc, L.usc, L.h, acco);
+    gu_load<NCH, MASKED, ROWS>(res, I, rowbytes, rb + stride, hi, dummy, sa);
+    if (i + 1 < nsteps) gu_step<NCH, ROWS>(sb, xv, corr, sxs, rb, lo, hi, L.gsc, L.usc, L.h, acco);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < hi - lo; t += 64 * kWaves) {
+    const int it = lo + t;
+    const int slot = it / I;
+    const int row = it - slot * I;
+    res(slot).h[row] = L.h[t];
+    if (acc_gu) {
+      acc_gu[row] = acco[2 * t];
+      acc_gu[I + row] = acco[2 * t + 1];
+    }
+  }
+}
+
+// Fixed expert (the shared one, or the single expert of a one-expert call) for
+// token s, rows of block gb.  LOCALQ: quantize the float token row in the
+// wave; otherwise read its codes.
+template <int NCH, bool MASKED, int ROWS, bool LOCALQ>
+__device__ void gateup_fixed(const DecodeArgs &a, int s, int gb) {
+  __shared__ GuLds L;
+  __shared__ int acco[2 * MOE_GU_MAX_ROWS];
+  const int wave = threadIdx.x >> 6;
+  const int rowbytes = a.D >> 1;
+  const int pair = s * a.P + a.fx_slot;
+  GuMats m;
+  m.G = pick(a.fx.gate, a.fx.gate, false, a.fx_index);
+  m.U = pick(a.fx.up, a.fx.up, false, a.fx_index);
+  m.h = a.h + (int64_t)pair * a.I;
+  auto res = [m](int) { return m; };
+  int lo, hi;
+  split_rows(a.I, a.n_gu_fx, gb, lo, hi);
+  const int first = lo + wave * ROWS;
+  const uint8_t *dummy = reinterpret_cast<const uint8_t *>(a.xq + (int64_t)s * a.D);
+  uint4 xv[NCH][2];
+  GuStage<NCH, ROWS> sa;
+  float sxs;
+  int sumx;
+  int32_t *acc_gu = a.acc_gu ? a.acc_gu + (int64_t)s * 2 * a.I : nullptr;
+  if (LOCALQ) {
+    float4 xf[NCH][8];
+    load_x_f32<NCH, MASKED>(a.x + (int64_t)s * a.D, a.D, xf);
+    gu_scales(res, a.I, lo, hi, L.gsc, L.usc);
+    gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
+    sumx = quant_x_wave<NCH>(xf, xv, &sxs);
+  } else {
+    load_x_codes<NCH, MASKED>(a.xq + (int64_t)s * a.D, a.D, xv);
+    sxs = a.sx[s];
+    sumx = a.sumx[s];
+    gu_scales(res, a.I, lo, hi, L.gsc, L.usc);
+    gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
+  }
+  __syncthreads();
+  gu_items<NCH, MASKED, ROWS>(res, a.I, rowbytes, lo, hi, xv, 8 * sumx, sxs, L,
+                              acc_gu ? acco : nullptr, acc_gu, dummy, sa);
+}
+
+// Routed experts of token s: the block runs the token's K selection rounds
+// once (block 0 publishes them), then works through its share of the
+// concatenated rows of the K selected experts.
+template <int NCH, bool MASKED, int ROWS>
+__device__ void gateup_routed(const DecodeArgs &a, int s, int gb) {
+  __shared__ int sel[64];
+  __shared__ GuLds L;
+  const int wave = threadIdx.x >> 6;
+  const int rowbytes = a.D >> 1;
+  uint4 xv[NCH][2];
+  load_x_codes<NCH, MASKED>(a.xq + (int64_t)s * a.D, a.D, xv);
+  const int corr = 8 * a.sumx[s];
+  const float sxs = a.sx[s];
+  if (wave == 0) {
+    const bool pub = (gb == 0);
+    topk_rounds(a.logits + (int64_t)s * a.E, a.bias, a.E, a.K, a.scale,
+                pub ? a.idx + (int64_t)s * a.K : nullptr, pub ? a.w + (int64_t)s * a.K : nullptr,
+                sel);
+  }
+  __syncthreads();
+  const ExpertSet &rt = a.rt;
+  float *hbase = a.h + (int64_t)s * a.P * a.I;
+  const int I = a.I;
+  auto res = [&](int slot) {
+    GuMats m;
+    const int e = sel[slot];
+    m.G = pick(rt.gate, rt.gate, false, e);
+    m.U = pick(rt.up, rt.up, false, e);
+    m.h = hbase + (int64_t)slot * I;
+    return m;
+  };
+  int lo, hi;
+  split_rows(a.K * a.I, a.n_gu_rt, gb, lo, hi);
+  const int first = lo + wave * ROWS;
+  const uint8_t *dummy = reinterpret_cast<const uint8_t *>(a.xq + (int64_t)s * a.D);
+  gu_scales(res, I, lo, hi, L.gsc, L.usc);
+  GuStage<NCH, ROWS> sa;
+  gu_load<NCH, MASKED, ROWS>(res, I, rowbytes, first, hi, dummy, sa);
+  __syncthreads();
+  gu_items<NCH, MASKED, ROWS>(res, I, rowbytes, lo, hi, xv, corr, sxs, L, nullptr, nullptr, dummy,
+                              sa);
+}
+
+// ---- down rows ----------------------------------------------------------------------
+
+#define MOE_DOWN_MAXP 8
+// Most rows a down block may own (its scales, combine inputs and outputs sit
+// in LDS).
+#define MOE_DN_MAX_ROWS 256
+
+struct DownTask {
+  int np;                         // slots (<= PMAX of the kernel)
+  RowPtr M[MOE_DOWN_MAXP];        // down matrices (all valid, also past np)
+  float wgt[MOE_DOWN_MAXP];       // combine weights
+  bool weighted[MOE_DOWN_MAXP];   // false: added with weight 1
+  const float *h[MOE_DOWN_MAXP];  // hidden rows (I floats; all valid)
+  int d0, d1;                     // rows of this block
+  const float *init;              // optional running combine to continue (D floats)
+  const float *extra;             // optional row added after the slots (D floats)
+  float *out;                     // D floats
+  bool accumulate;                // out = out + result
+  int32_t *acc_d;                 // optional (single slot)
+  int8_t *hq_nat;                 // optional (single slot), first block only
+  float *sh_out;                  // optional (single slot), first block only
+  bool first_block;
+};
+
+// Requantize the slots' hidden rows (section 12 rule) into LDS codes in the
+// permuted layout: one round of loads for all slots, the row maxima reduced
+// across the block, then the codes.  Scales go to sh[], code sums to sums[].
+// NCH bounds the groups of 8 per thread: I <= 2048*NCH with 256 threads.
+template <int PMAX, int NCH>
+__device__ void requant_to_lds(const DownTask &t, int I, int8_t *lds, float *sh, int *sums) {
+  __shared__ float redm[PMAX][kWaves];
+  __shared__ int reds[PMAX][kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ngroups = I >> 3;
+  float4 hv[PMAX][NCH][2];
+#pragma unroll
+  for (int p = 0; p < PMAX; p++)
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      // unconditional loads (index clamped; every t.h[p] is a valid row)
+      const int g = tid + k * 64 * kWaves;
+      const bool ok = (p < t.np) && (g < ngroups);
+      const int gc = min(g, ngroups - 1);
+      const float4 v0 = reinterpret_cast<const float4 *>(t.h[p])[2 * gc];
+      const float4 v1 = reinterpret_cast<const float4 *>(t.h[p])[2 * gc + 1];
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      hv[p][k][0] = ok ? v0 : z;
+      hv[p][k][1] = ok ? v1 : z;
+    }
+#pragma unroll
+  for (int p = 0; p < PMAX; p++) {
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; k++)
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        m = fmax_nan_skip(m, fabsf(hv[p][k][j].x));
+        m = fmax_nan_skip(m, fabsf(hv[p][k][j].y));
+        m = fmax_nan_skip(m, fabsf(hv[p][k][j].z));
+        m = fmax_nan_skip(m, fabsf(hv[p][k][j].w));
+      }
+    m = wave_max_f32(m);
+    if (lane == 0) redm[p][wave] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PMAX; p++) {
+    const float m = fmax_nan_skip(fmax_nan_skip(redm[p][0], redm[p][1]),
+                                  fmax_nan_skip(redm[p][2], redm[p][3]));
+    const float sc = quant_scale(m);
+    const float inv = 1.f / sc;
+    uint2 *dst = reinterpret_cast<uint2 *>(lds + p * I);
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      const int g = tid + k * 64 * kWaves;
+      const float4 x0 = hv[p][k][0], x1 = hv[p][k][1];
+      const int q0 = quant_code(x0.x, inv), q1 = quant_code(x0.y, inv), q2 = quant_code(x0.z, inv),
+                q3 = quant_code(x0.w, inv), q4 = quant_code(x1.x, inv), q5 = quant_code(x1.y, inv),
+                q6 = quant_code(x1.z, inv), q7 = quant_code(x1.w, inv);
+      sum += ((q0 + q1) + (q2 + q3)) + ((q4 + q5) + (q6 + q7));
+      if (g < ngroups) {
+        dst[g] = make_uint2(pack4(q0, q2, q4, q6), pack4(q1, q3, q5, q7));
+        if (t.hq_nat && t.first_block)
+          reinterpret_cast<uint2 *>(t.hq_nat)[g] =
+              make_uint2(pack4(q0, q1, q2, q3), pack4(q4, q5, q6, q7));
+      }
+    }
+    sum = wave_sum_i32(sum);
+    if (lane == 0) reds[p][wave] = sum;
+    if (tid == 0) {
+      sh[p] = sc;
+      if (t.sh_out && t.first_block) *t.sh_out = sc;
+    }
+  }
+  __syncthreads();
+  if (tid < PMAX) sums[tid] = (reds[tid][0] + reds[tid][1]) + (reds[tid][2] + reds[tid][3]);
+  __syncthreads();
+}
+
+// One pipeline stage of the down projection: ROWS rows of every slot's
+// weights (the only global loads of the loop body, see the gate/up notes).
+template <int NCH, int ROWS, int PMAX>
+struct DnStage {
+  uint4 w[PMAX][ROWS][NCH];
+};
+
+template <int NCH, bool MASKED, int ROWS, int PMAX>
+__device__ __forceinline__ void dn_load(const DownTask &t, int rowbytes, int row,
+                                        const uint8_t *dummy, DnStage<NCH, ROWS, PMAX> &st) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int p = 0; p < PMAX; p++) {
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) {
+      const int d = row + r;
+      const bool live = (d < t.d1) && (p < t.np);  // uniform across the wave
+      const uint8_t *wr = live ? t.M[p].q + (int64_t)d * rowbytes : dummy;
+#pragma unroll
+      for (int c = 0; c < NCH; c++) {
+        const int off = c * 1024 + lane * 16;
+        const bool ok = !MASKED || off < rowbytes;
+        st.w[p][r][c] = ldnt16(wr + off, ok, wr);
+      }
+    }
+  }
+}
+
+// Row scales of every slot for the block's rows, and the combine's running
+// value and final addend, into LDS (one round of loads).
+template <int PMAX>
+__device__ __forceinline__ void dn_scales(const DownTask &t, float (*dsc)[MOE_DN_MAX_ROWS],
+                                          float *init, float *extra) {
+  const int n = t.d1 - t.d0;
+  for (int i0 = 0; i0 < n; i0 += 64 * kWaves) {
+    const int i = i0 + threadIdx.x;
+    const int d = t.d0 + min(i, n - 1);
+    float v[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; p++) v[p] = t.M[p].s[d];
+    const float vi = t.init ? t.init[d] : 0.f;
+    const float ve = t.extra ? t.extra[d] : 0.f;
+    if (i < n) {
+#pragma unroll
+      for (int p = 0; p < PMAX; p++) dsc[p][i] = v[p];
+      init[i] = vi;
+      extra[i] = ve;
+    }
+  }
+}
+
+struct DnLds {
+  float sh[MOE_DOWN_MAXP];
+  int sums[MOE_DOWN_MAXP];
+  float dsc[MOE_DOWN_MAXP][MOE_DN_MAX_ROWS];
+  float init[MOE_DN_MAX_ROWS], extra[MOE_DN_MAX_ROWS], out[MOE_DN_MAX_ROWS];
+  int accd[MOE_DN_MAX_ROWS];
+};
+
+template <int NCH, bool MASKED, int ROWS, int PMAX>
+__device__ __forceinline__ void dn_step(const DownTask &t, const DnStage<NCH, ROWS, PMAX> &st,
+                                        const int8_t *codes, DnLds &L, int I, int row) {
+  const int lane = threadIdx.x & 63;
+  const int rowbytes = I >> 1;
+  const int i0 = row - t.d0;
+  const int n = t.d1 - t.d0;
+  float comb[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; r++) comb[r] = L.init[min(i0 + r, n - 1)];
+#pragma unroll
+  for (int p = 0; p < PMAX; p++) {
+    uint4 hv[NCH][2];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+      const int off = c * 1024 + lane * 16;
+      const int offc = (!MASKED || off < rowbytes) ? off : 0;
+      hv[c][0] = *reinterpret_cast<const uint4 *>(codes + p * I + 2 * offc);
+      hv[c][1] = *reinterpret_cast<const uint4 *>(codes + p * I + 2 * offc + 16);
+      if (MASKED && off >= rowbytes) {
+        hv[c][0] = make_uint4(0u, 0u, 0u, 0u);
+        hv[c][1] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    const int corr = 8 * L.sums[p];
+    const float shs = L.sh[p];
+    const bool use = p < t.np;
+#pragma unroll
+    for (int r = 0; r < ROWS; r++) {
+      int acc = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; c++) acc = dot32_i4(st.w[p][r][c], hv[c][0], hv[c][1], acc);
+      acc = wave_sum_i32(acc) - corr;
+      const float y = ((float)acc * L.dsc[p][min(i0 + r, n - 1)]) * shs;
+      const float nc = t.weighted[p] ? comb[r] + t.wgt[p] * y : comb[r] + y;
+      comb[r] = use ? nc : comb[r];
+      if (lane == r && i0 + r < n) L.accd[i0 + r] = acc;  // meaningful for single-slot calls
+    }
+  }
+  float mine = comb[0];
+#pragma unroll
+  for (int r = 1; r < ROWS; r++)
+    if (lane == r) mine = comb[r];
+  if (lane < ROWS && i0 + lane < n) L.out[i0 + lane] = mine;
+}
+
+template <int NCH, bool MASKED, int ROWS, int PMAX>
+__device__ void down_block(const DownTask &t, int I) {
+  extern __shared__ __align__(16) int8_t codes[];
+  __shared__ DnLds L;
+  const int wave = threadIdx.x >> 6;
+  const int rowbytes = I >> 1;
+  const int stride = kWaves * ROWS;
+  const int first = t.d0 + wave * ROWS;
+  const int nsteps = (first < t.d1) ? (t.d1 - first + stride - 1) / stride : 0;
+  const uint8_t *dummy = reinterpret_cast<const uint8_t *>(t.h[0]);
+  DnStage<NCH, ROWS, PMAX> sa, sb;
+  dn_scales<PMAX>(t, L.dsc, L.init, L.extra);
+  // the first step's weights do not depend on the hidden rows: issue them early
+  dn_load<NCH, MASKED, ROWS, PMAX>(t, rowbytes, first, dummy, sa);
+  requant_to_lds<PMAX, NCH>(t, I, codes, L.sh, L.sums);  // ends with a barrier
+  for (int i = 0; i < nsteps; i += 2) {
+    const int ra = first + i * stride, rb = ra + stride;
+    dn_load<NCH, MASKED, ROWS, PMAX>(t, rowbytes, rb, dummy, sb);
+    dn_step<NCH, MASKED, ROWS, PMAX>(t, sa, codes, L, I, ra);
+    dn_load<NCH, MASKED, ROWS, PMAX>(t, rowbytes, rb + stride, dummy, sa);
+    if (i + 1 < nsteps) dn_step<NCH, MASKED, ROWS, PMAX>(t, sb, codes, L, I, rb);
+  }
+  __syncthreads();
+  const int n = t.d1 - t.d0;
+  for (int i = threadIdx.x; i < n; i += 64 * kWaves) {
+    const int d = t.d0 + i;
+    float v = L.out[i];
+    if (t.extra) v = v + L.extra[i];
+    t.out[d] = t.accumulate ? (t.out[d] + v) : v;
+    if (t.acc_d) t.acc_d[d] = L.accd[i];
+  }
+}
+
+// Down projection of the fixed expert for token s, rows of block db.
+template <int NCH, bool MASKED, int ROWS>
+__device__ void down_fixed(const DecodeArgs &a, int s, int db) {
+  DownTask t;
+  const int pair = s * a.P + a.fx_slot;
+  t.np = 1;
+#pragma unroll
+  for (int j = 0; j < MOE_DOWN_MAXP; j++) {
+    t.M[j] = pick(a.fx.down, a.fx.down, false, a.fx_index);
+    t.wgt[j] = 1.f;
+    t.weighted[j] = false;
+    t.h[j] = a.h + (int64_t)pair * a.I;
+  }
+  split_rows(a.D, a.n_dn_fx, db, t.d0, t.d1);
+  t.init = nullptr;
+  t.extra = nullptr;
+  t.out = a.ysh + (int64_t)s * a.D;
+  t.accumulate = false;
+  t.acc_d = a.acc_d ? a.acc_d + (int64_t)s * a.D : nullptr;
+  t.hq_nat = a.hq_nat ? a.hq_nat + (int64_t)s * a.I : nullptr;
+  t.sh_out = a.sh_out ? a.sh_out + s : nullptr;
+  t.first_block = (db == 0);
+  down_block<NCH, MASKED, ROWS, 1>(t, a.I);
+}
+
+#ifndef MOE_DNFX_ROWS
+#define MOE_DNFX_ROWS 4
+#endif
+
+// ---- the three launches ----------------------------------------------------------------
+
+#ifndef MOE_GU_ROWS
+#define MOE_GU_ROWS 2
+#endif
+
+template <int NCHD, bool MD, bool LOCALQ>
+__global__ __launch_bounds__(256) void decode_a_kernel(DecodeArgs a) {
+  const int s = blockIdx.y, b = blockIdx.x;
+  if (b < a.n_router) {
+    router_logit(a, s, b * 4 + (threadIdx.x >> 6));
+    return;
+  }
+  if (b < a.n_router + a.n_quant) {
+    quant_row_block(a.x + (int64_t)s * a.D, nullptr, a.D, const_cast<int8_t *>(a.xq) + (int64_t)s * a.D,
+                    nullptr, const_cast<float *>(a.sx) + s, const_cast<int32_t *>(a.sumx) + s);
+    return;
+  }
+  gateup_fixed<NCHD, MD, MOE_GU_ROWS, LOCALQ>(a, s, b - a.n_router - a.n_quant);
+}
+
+template <int NCHD, bool MD, int NCHI, bool MI>
+__global__ __launch_bounds__(256) void decode_b_kernel(DecodeArgs a) {
+  const int s = blockIdx.y, b = blockIdx.x;
+  if (b < a.n_gu_rt) {
+    gateup_routed<NCHD, MD, MOE_GU_ROWS>(a, s, b);
+    return;
+  }
+  down_fixed<NCHI, MI, MOE_DNFX_ROWS>(a, s, b - a.n_gu_rt);
+}
+
+template <int NCHI, bool MI, int PMAX>
+__global__ __launch_bounds__(256) void decode_c_kernel(DecodeArgs a) {
+  const int s = blockIdx.y, db = blockIdx.x;
+  DownTask t;
+  t.np = a.p_hi - a.p_lo;
+#pragma unroll
+  for (int j = 0; j < MOE_DOWN_MAXP; j++) {
+    const int p = a.p_lo + j;
+    const bool ok = j < t.np;
+    const int e = ok ? a.idx[s * a.K + p] : 0;
+    t.M[j] = pick(a.rt.down, a.rt.down, false, e);
+    t.wgt[j] = ok ? a.w[s * a.K + p] : 0.f;
+    t.weighted[j] = true;
+    t.h[j] = a.h + ((int64_t)s * a.P + (ok ? p : 0)) * a.I;
+  }
+  split_rows(a.D, a.n_dn, db, t.d0, t.d1);
+  t.init = a.c_first ? nullptr : a.tmp + (int64_t)s * a.D;
+  const bool last = a.c_last;
+  t.extra = (last && a.P > a.K) ? a.ysh + (int64_t)s * a.D : nullptr;
+  t.out = last ? a.out + (int64_t)s * a.D : a.tmp + (int64_t)s * a.D;
+  t.accumulate = last && (a.flags & MOE_F_ACCUMULATE);
+  t.acc_d = nullptr;
+  t.hq_nat = nullptr;
+  t.sh_out = nullptr;
+  t.first_block = (db == 0);
+  down_block<NCHI, MI, 2, PMAX>(t, a.I);
+}
+
+// ---- launchers -----------------------------------------------------------------------
+
+// Column dispatch: NCH 1 KB chunks per row, masked when the row is not a whole
+// number of chunks.
+#define MOE_COLS(RB, F)                                         \
+  do {                                                          \
+    const int nch_ = ((RB) + 1023) / 1024;                      \
+    const bool msk_ = ((RB) % 1024) != 0;                       \
+    if (msk_) {                                                 \
+      if (nch_ == 1) F(1, true); else if (nch_ == 2) F(2, true); \
+      else if (nch_ == 3) F(3, true); else F(4, true);          \
+    } else {                                                    \
+      if (nch_ == 1) F(1, false); else if (nch_ == 2) F(2, false); \
+      else if (nch_ == 3) F(3, false); else F(4, false);        \
+    }                                                           \
+  } while (0)
+
+int decode_c_slots(int I) {
+  const int nch = (I / 2 + 1023) / 1024;
+  return nch == 1 ? 8 : (nch == 2 ? 4 : 2);
+}
+
+hipError_t launch_decode_a(const DecodeArgs &a, bool local_quant, hipStream_t st) {
+  const dim3 grid(a.n_router + a.n_quant + a.n_gu_fx, a.S);
+  const int rb = a.D / 2;
+#define MOE_FA(N, M)                                                                   \
+  do {                                                                                 \
+    if (local_quant)                                                                   \
+      hipLaunchKernelGGL((decode_a_kernel<N, M, true>), grid, dim3(256), 0, st, a);    \
+    else                                                                               \
+      hipLaunchKernelGGL((decode_a_kernel<N, M, false>), grid, dim3(256), 0, st, a);   \
+  } while (0)
+  MOE_COLS(rb, MOE_FA);
+#undef MOE_FA
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st) {
+  const dim3 grid(a.n_gu_rt + a.n_dn_fx, a.S);
+  const size_t lds = (size_t)a.I;  // one hidden row of codes
+  const int rbd = a.D / 2, rbi = a.I / 2;
+#define MOE_FBI(NI, MI, ND, MD) \
+  hipLaunchKernelGGL((decode_b_kernel<ND, MD, NI, MI>), grid, dim3(256), lds, st, a)
+#define MOE_FBD(ND, MD)                                          \
+  do {                                                           \
+    const int nchi_ = (rbi + 1023) / 1024;                       \
+    const bool mski_ = (rbi % 1024) != 0;                        \
+    if (mski_) {                                                 \
+      if (nchi_ == 1) MOE_FBI(1, true, ND, MD);                  \
+      else if (nchi_ == 2) MOE_FBI(2, true, ND, MD);             \
+      else if (nchi_ == 3) MOE_FBI(3, true, ND, MD);             \
+      else MOE_FBI(4, true, ND, MD);                             \
+    } else {                                                     \
+      if (nchi_ == 1) MOE_FBI(1, false, ND, MD);                 \
+      else if (nchi_ == 2) MOE_FBI(2, false, ND, MD);            \
+      else if (nchi_ == 3) MOE_FBI(3, false, ND, MD);            \
+      else MOE_FBI(4, false, ND, MD);                            \
+    }                                                            \
+  } while (0)
+  MOE_COLS(rbd, MOE_FBD);
+#undef MOE_FBD
+#undef MOE_FBI
+  return hipGetLastError();
+}
+
+template <int N, bool M>
+static void launch_c(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr int PMAX = N == 1 ? 8 : (N == 2 ? 4 : 2);
+  hipLaunchKernelGGL((decode_c_kernel<N, M, PMAX>), grid, dim3(256), lds, st, a);
+}
+
+hipError_t launch_decode_c(const DecodeArgs &a, hipStream_t st) {
+  const dim3 grid(a.n_dn, a.S);
+  const int rb = a.I / 2;
+  const size_t lds = (size_t)decode_c_slots(a.I) * a.I;
+#define MOE_FC(N, M) launch_c<N, M>(a, grid, lds, st)
+  MOE_COLS(rb, MOE_FC);
+#undef MOE_FC
+  return hipGetLastError();
+}
+
+}  // namespace moe

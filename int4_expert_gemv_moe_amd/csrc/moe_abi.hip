@@ -1,0 +1,480 @@
+// moe_abi.hip -- the extern "C" entry points declared in include/moe_i4.h:
+// host-side validation, workspace carving and the launch sequence of each
+// call.  No call allocates device memory.
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "moe_kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Per-device memo of "is this a gfx950" (read-only device property).
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= 64) return MOE_EDEVICE;
+  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_EHIP;
+    v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? MOE_OK : MOE_EDEVICE;
+}
+
+int check_cfg(const moe_config *c) {
+  if (!c) return MOE_EINVAL;
+  if (c->D < 256 || c->I < 32 || c->D % 256 || c->I % 32) return MOE_ESHAPE;
+  if (!gemv_cols_ok(c->D) || !gemv_cols_ok(c->I)) return MOE_ESHAPE;
+  if (c->E < 1 || c->E > 1024 || c->K < 1 || c->K > c->E || c->K > 64) return MOE_ESHAPE;
+  if (c->n_shared < 0 || c->n_shared > 1) return MOE_ESHAPE;
+  if (!(c->routed_scale == c->routed_scale)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+enum Which { W_FWD = 0, W_BATCH = 1, W_SWIGLU = 2, W_ROUTER = 3 };
+
+// Workgroup counts of the per-token path (rows of a phase are split evenly
+// over its workgroups).  MOE_DECODE_BLOCKS="a,b,c,d" overrides them for
+// tuning: shared gate/up (phase A), routed gate/up per slot and shared down
+// (phase B), routed down (phase C).
+struct DecodeShape {
+  int gu_fx, gu_rt, dn_fx, dn;
+};
+
+DecodeShape decode_shape(const moe_config &c) {
+  static const DecodeShape env = [] {
+    DecodeShape d{0, 0, 0, 0};
+    if (const char *v = std::getenv("MOE_DECODE_BLOCKS"))
+      std::sscanf(v, "%d,%d,%d,%d", &d.gu_fx, &d.gu_rt, &d.dn_fx, &d.dn);
+    return d;
+  }();
+  DecodeShape d;
+  d.gu_fx = env.gu_fx > 0 ? env.gu_fx : 64;
+  d.gu_rt = env.gu_rt > 0 ? env.gu_rt : 256;
+  d.dn_fx = env.dn_fx > 0 ? env.dn_fx : 96;
+  d.dn = env.dn > 0 ? env.dn : 256;
+  // at least 8 rows per workgroup, at most the rows whose scales fit in LDS
+  // (512 for gate/up, 256 for down)
+  auto clampn = [](int n, int rows, int maxrows) {
+    const int lo = (rows + maxrows - 1) / maxrows, hi = std::max(1, rows / 8);
+    return std::max(lo, std::min(n, hi));
+  };
+  d.gu_fx = clampn(d.gu_fx, c.I, 512);
+  d.gu_rt = clampn(d.gu_rt, c.I * c.K, 512);
+  d.dn_fx = clampn(d.dn_fx, c.D, 256);
+  d.dn = clampn(d.dn, c.D, 256);
+  return d;
+}
+
+// Workspace carving.  With base == nullptr only the size is computed.
+size_t carve(const moe_config &c, int S, int which, char *base, Work *w) {
+  const int P = (which == W_SWIGLU) ? 1 : c.K + c.n_shared;
+  const size_t s = (size_t)S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char * {
+    char *p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  Work t{};
+  if (which != W_SWIGLU) {
+    t.logits = (float *)take(s * c.E * 4);
+    t.idx = (int32_t *)take(s * c.K * 4);
+    t.w = (float *)take(s * c.K * 4);
+  }
+  if (which != W_ROUTER) {
+    t.xq = (int8_t *)take(s * c.D);
+    t.sx = (float *)take(s * 4);
+    t.sumx = (int32_t *)take(s * 4);
+    t.h = (float *)take(s * P * c.I * 4);
+  }
+  if (which == W_FWD || which == W_SWIGLU) {
+    t.ysh = (float *)take(s * c.D * 4);
+    t.tmp = (float *)take(s * c.D * 4);
+  }
+  if (which == W_BATCH) {
+    t.hq = (int8_t *)take(s * P * c.I);
+    t.sh = (float *)take(s * P * 4);
+    t.sumh = (int32_t *)take(s * P * 4);
+    t.gcount = (int32_t *)take((size_t)(c.E + 1) * 4);
+    t.goff = (int32_t *)take((size_t)(c.E + 2) * 4);
+    t.pairs = (int32_t *)take(s * P * 4);
+    t.stage = (float *)take(s * P * c.D * 4);
+  }
+  if (w) *w = t;
+  return off;
+}
+
+QMat to_qmat(const moe_qmat &m, int O, int C) {
+  QMat q;
+  q.q4 = m.q4;
+  q.scale = m.scale;
+  q.q4_stride = m.q4_stride ? m.q4_stride : (int64_t)O * (C / 2);
+  q.s_stride = m.scale_stride ? m.scale_stride : (int64_t)O;
+  return q;
+}
+
+ExpertSet to_set(const moe_experts &e, const moe_config &c) {
+  ExpertSet s;
+  s.gate = to_qmat(e.gate, c.I, c.D);
+  s.up = to_qmat(e.up, c.I, c.D);
+  s.down = to_qmat(e.down, c.D, c.I);
+  return s;
+}
+
+int check_qmat(const moe_qmat &m) {
+  if (!m.q4 || !m.scale) return MOE_EINVAL;
+  if (!aligned16(m.q4) || ((uintptr_t)m.scale & 3u)) return MOE_EALIGN;
+  if (m.q4_stride < 0 || m.scale_stride < 0 || (m.q4_stride & 15)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+int check_experts(const moe_experts &e) {
+  int rc;
+  if ((rc = check_qmat(e.gate)) || (rc = check_qmat(e.up)) || (rc = check_qmat(e.down))) return rc;
+  return MOE_OK;
+}
+
+int check_layer(const moe_config &c, const moe_layer *L) {
+  if (!L || !L->router_w || !L->router_b) return MOE_EINVAL;
+  if (!aligned16(L->router_w) || ((uintptr_t)L->router_b & 3u)) return MOE_EALIGN;
+  int rc = check_experts(L->routed);
+  if (rc) return rc;
+  if (c.n_shared) return check_experts(L->shared);
+  return MOE_OK;
+}
+
+__global__ void moe_zero_kernel(uint4 *p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+#define MOE_TRY(expr)             \
+  do {                            \
+    int rc_ = (expr);             \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
+#define MOE_TRY_HIP(expr) MOE_TRY(hip_rc(expr))
+
+// Router logits (+ activation quantization); the top-K runs in a kernel of
+// its own when with_topk, otherwise inside the per-token gate/up kernel.
+int run_router(const moe_config &c, const float *x, int S, const float *W, const float *b,
+               const Work &w, bool with_quant, bool with_topk, float *logits_out, hipStream_t st) {
+  RouterArgs r{};
+  r.x = x;
+  r.W = W;
+  r.S = S;
+  r.D = c.D;
+  r.E = c.E;
+  r.logits = w.logits;
+  r.logits_out = logits_out;
+  r.xq_perm = w.xq;
+  r.sx = w.sx;
+  r.sumx = w.sumx;
+  r.amax = nullptr;
+  r.P = c.K + c.n_shared;
+  MOE_TRY_HIP(launch_router(r, with_quant, st));
+  if (with_topk) {
+    TopkArgs t{w.logits, b, S, c.E, c.K, c.routed_scale, w.idx, w.w};
+    MOE_TRY_HIP(launch_topk(t, st));
+  }
+  return MOE_OK;
+}
+
+int copy_probe(const moe_config &c, int S, const moe_probe *probe, const Work &w,
+               hipStream_t st) {
+  if (!probe) return MOE_OK;
+  const size_t n = (size_t)S * c.K;
+  if (probe->topk_idx)
+    MOE_TRY_HIP(hipMemcpyAsync(probe->topk_idx, w.idx, n * 4, hipMemcpyDeviceToDevice, st));
+  if (probe->topk_w)
+    MOE_TRY_HIP(hipMemcpyAsync(probe->topk_w, w.w, n * 4, hipMemcpyDeviceToDevice, st));
+  return MOE_OK;
+}
+
+int record(const moe_probe *probe, int which, int side, hipStream_t st) {
+  if (!probe) return MOE_OK;
+  const hipEvent_t *ev = which == 0 ? probe->ev_gateup : probe->ev_down;
+  if (!ev[0] || !ev[1]) return MOE_OK;
+  return hip_rc(hipEventRecord(ev[side], st));
+}
+
+int layer_common_checks(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                        float *out, void *ws, size_t ws_bytes, int which) {
+  MOE_TRY(check_cfg(cfg));
+  if (S < 1 || !x || !out || !ws) return MOE_EINVAL;
+  MOE_TRY(check_layer(*cfg, layer));
+  if (!aligned16(x) || ((uintptr_t)out & 3u) || ((uintptr_t)ws & 255u)) return MOE_EALIGN;
+  const size_t xb = (size_t)S * cfg->D * 4;
+  if ((const char *)out < (const char *)x + xb && (const char *)x < (const char *)out + xb)
+    return MOE_EINVAL;
+  if (ws_bytes < carve(*cfg, S, which, nullptr, nullptr)) return MOE_EWORKSPACE;
+  return check_device();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ESHAPE: return "unsupported shape";
+    case MOE_EALIGN: return "misaligned buffer";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP error";
+    case MOE_EDEVICE: return "device is not a gfx950";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_config *cfg, int S, int which) {
+  if (check_cfg(cfg) != MOE_OK || S < 1 || which < 0 || which > 3) return 0;
+  return carve(*cfg, S, which, nullptr, nullptr);
+}
+
+int moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws) return MOE_EINVAL;
+  if (((uintptr_t)ws & 255u) || (ws_bytes & 15u)) return MOE_EALIGN;
+  MOE_TRY(check_device());
+  const size_t n16 = ws_bytes / 16;
+  if (n16 == 0) return MOE_OK;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(moe_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint4 *)ws, n16);
+  return hip_rc(hipGetLastError());
+}
+
+int moe_pack_int4(const float *w, int O, int C, uint8_t *q4, float *scale, hipStream_t stream) {
+  if (!w || !q4 || !scale) return MOE_EINVAL;
+  if (O < 1 || C < 2 || (C & 1)) return MOE_ESHAPE;
+  if (((uintptr_t)w & 7u) || ((uintptr_t)scale & 3u)) return MOE_EALIGN;
+  MOE_TRY(check_device());
+  PackArgs a{w, O, C, q4, scale};
+  return hip_rc(launch_pack(a, stream));
+}
+
+int moe_quant_act_i8(const void *x, moe_dtype dtype, int S, int D, int8_t *xq, float *sx,
+                     hipStream_t stream) {
+  if (!x || !xq || !sx) return MOE_EINVAL;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EINVAL;
+  if (S < 1 || D < 8 || (D & 7)) return MOE_ESHAPE;
+  if (!aligned16(x) || ((uintptr_t)xq & 7u) || ((uintptr_t)sx & 3u)) return MOE_EALIGN;
+  MOE_TRY(check_device());
+  QuantArgs a{};
+  a.xf = dtype == MOE_F32 ? (const float *)x : nullptr;
+  a.xb = dtype == MOE_BF16 ? (const uint16_t *)x : nullptr;
+  a.D = D;
+  a.xq_nat = xq;
+  a.sx = sx;
+  return hip_rc(launch_quant(a, S, stream));
+}
+
+int moe_router_topk(const moe_config *cfg, const float *x, int S, const float *router_w,
+                    const float *router_b, int32_t *topk_idx, float *topk_w, float *logits,
+                    void *ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (S < 1 || !x || !router_w || !router_b || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(router_w) || ((uintptr_t)ws & 255u)) return MOE_EALIGN;
+  if (ws_bytes < carve(*cfg, S, W_ROUTER, nullptr, nullptr)) return MOE_EWORKSPACE;
+  MOE_TRY(check_device());
+  Work w;
+  carve(*cfg, S, W_ROUTER, (char *)ws, &w);
+  MOE_TRY(run_router(*cfg, x, S, router_w, router_b, w, false, true, logits, stream));
+  const size_t n = (size_t)S * cfg->K * 4;
+  MOE_TRY_HIP(hipMemcpyAsync(topk_idx, w.idx, n, hipMemcpyDeviceToDevice, stream));
+  MOE_TRY_HIP(hipMemcpyAsync(topk_w, w.w, n, hipMemcpyDeviceToDevice, stream));
+  return MOE_OK;
+}
+
+int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *sx, int S,
+                         const moe_experts *wts, int expert, float *y, int32_t *acc_gu,
+                         int8_t *hq, float *sh, int32_t *acc_d, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (S < 1 || !xq || !sx || !wts || !y || !ws) return MOE_EINVAL;
+  if (expert < 0 || expert >= cfg->E) return MOE_EINVAL;
+  MOE_TRY(check_experts(*wts));
+  if (((uintptr_t)xq & 7u) || ((uintptr_t)ws & 255u)) return MOE_EALIGN;
+  if (hq && ((uintptr_t)hq & 7u)) return MOE_EALIGN;
+  if (ws_bytes < carve(*cfg, S, W_SWIGLU, nullptr, nullptr)) return MOE_EWORKSPACE;
+  MOE_TRY(check_device());
+  Work w;
+  carve(*cfg, S, W_SWIGLU, (char *)ws, &w);
+  PrepArgs pa{xq, cfg->D, w.xq, w.sumx, nullptr, 1};
+  MOE_TRY_HIP(launch_prep_xq(pa, S, stream));
+  const DecodeShape ds = decode_shape(*cfg);
+  DecodeArgs d{};
+  d.S = S;
+  d.D = cfg->D;
+  d.I = cfg->I;
+  d.E = cfg->E;
+  d.K = 0;
+  d.P = 1;
+  d.scale = cfg->routed_scale;
+  d.rt = to_set(*wts, *cfg);
+  d.fx = d.rt;
+  d.fx_index = expert;
+  d.fx_slot = 0;
+  d.xq = w.xq;
+  d.sx = sx;
+  d.sumx = w.sumx;
+  d.h = w.h;
+  d.ysh = y;
+  d.n_router = 0;
+  d.n_quant = 0;
+  d.n_gu_fx = ds.gu_fx;
+  d.n_gu_rt = 0;
+  d.n_dn_fx = ds.dn_fx;
+  d.acc_gu = acc_gu;
+  d.acc_d = acc_d;
+  d.hq_nat = hq;
+  d.sh_out = sh;
+  MOE_TRY_HIP(launch_decode_a(d, false, stream));
+  MOE_TRY_HIP(launch_decode_b(d, stream));
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                      float *out, unsigned flags, const moe_probe *probe, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, ws, ws_bytes, W_FWD));
+  const moe_config &c = *cfg;
+  Work w;
+  carve(c, S, W_FWD, (char *)ws, &w);
+  const DecodeShape ds = decode_shape(c);
+  DecodeArgs d{};
+  d.S = S;
+  d.D = c.D;
+  d.I = c.I;
+  d.E = c.E;
+  d.K = c.K;
+  d.P = c.K + c.n_shared;
+  d.scale = c.routed_scale;
+  d.x = x;
+  d.W = layer->router_w;
+  d.bias = layer->router_b;
+  d.rt = to_set(layer->routed, c);
+  d.fx = c.n_shared ? to_set(layer->shared, c) : d.rt;
+  d.fx_index = 0;
+  d.fx_slot = c.K;
+  d.xq = w.xq;
+  d.sx = w.sx;
+  d.sumx = w.sumx;
+  d.logits = w.logits;
+  d.idx = w.idx;
+  d.w = w.w;
+  d.h = w.h;
+  d.ysh = w.ysh;
+  d.tmp = w.tmp;
+  d.n_router = (c.E + 3) / 4;
+  d.n_quant = 1;
+  d.n_gu_fx = c.n_shared ? ds.gu_fx : 0;
+  d.n_gu_rt = ds.gu_rt;
+  d.n_dn_fx = c.n_shared ? ds.dn_fx : 0;
+  d.n_dn = ds.dn;
+  d.out = out;
+  d.flags = flags;
+  MOE_TRY_HIP(launch_decode_a(d, true, stream));
+  MOE_TRY(record(probe, 0, 0, stream));
+  MOE_TRY_HIP(launch_decode_b(d, stream));
+  MOE_TRY(record(probe, 0, 1, stream));
+  MOE_TRY(copy_probe(c, S, probe, w, stream));
+  const int batch = decode_c_slots(c.I);
+  MOE_TRY(record(probe, 1, 0, stream));
+  for (int p0 = 0; p0 < c.K; p0 += batch) {
+    d.p_lo = p0;
+    d.p_hi = std::min(c.K, p0 + batch);
+    d.c_first = (p0 == 0);
+    d.c_last = (d.p_hi == c.K);
+    MOE_TRY_HIP(launch_decode_c(d, stream));
+  }
+  MOE_TRY(record(probe, 1, 1, stream));
+  return MOE_OK;
+}
+
+int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                            float *out, unsigned flags, const moe_probe *probe, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, ws, ws_bytes, W_BATCH));
+  const moe_config &c = *cfg;
+  const int P = c.K + c.n_shared;
+  Work w;
+  carve(c, S, W_BATCH, (char *)ws, &w);
+  MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, true, nullptr, stream));
+  MOE_TRY(copy_probe(c, S, probe, w, stream));
+  GroupArgs ga{w.idx, S, c.E, c.K, P, c.n_shared, w.gcount, w.goff, w.pairs};
+  MOE_TRY_HIP(launch_group(ga, stream));
+  const ExpertSet rt = to_set(layer->routed, c);
+  const ExpertSet sh = c.n_shared ? to_set(layer->shared, c) : rt;
+  GroupedGateUpArgs g{};
+  g.rt = rt;
+  g.sh = sh;
+  g.D = c.D;
+  g.I = c.I;
+  g.E = c.E;
+  g.P = P;
+  g.gcount = w.gcount;
+  g.goff = w.goff;
+  g.pairs = w.pairs;
+  g.xq = w.xq;
+  g.sx = w.sx;
+  g.sumx = w.sumx;
+  g.h = w.h;
+  MOE_TRY(record(probe, 0, 0, stream));
+  MOE_TRY_HIP(launch_grouped_gateup(g, stream));
+  MOE_TRY(record(probe, 0, 1, stream));
+  RequantArgs rq{w.h, c.I, w.hq, w.sh, w.sumh};
+  MOE_TRY_HIP(launch_requant(rq, S * P, stream));
+  GroupedDownArgs d{};
+  d.rt = rt;
+  d.sh = sh;
+  d.D = c.D;
+  d.I = c.I;
+  d.E = c.E;
+  d.P = P;
+  d.gcount = w.gcount;
+  d.goff = w.goff;
+  d.pairs = w.pairs;
+  d.hq = w.hq;
+  d.sh_scale = w.sh;
+  d.sumh = w.sumh;
+  d.stage = w.stage;
+  MOE_TRY(record(probe, 1, 0, stream));
+  MOE_TRY_HIP(launch_grouped_down(d, stream));
+  MOE_TRY(record(probe, 1, 1, stream));
+  CombineArgs cb{w.stage, w.w, S, c.D, c.K, P, c.n_shared, out, flags};
+  MOE_TRY_HIP(launch_combine(cb, stream));
+  return MOE_OK;
+}
+
+int moe_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y,
+                hipStream_t stream) {
+  if (!x || !gamma || !y) return MOE_EINVAL;
+  if (S < 1 || D < 1) return MOE_ESHAPE;
+  if (((uintptr_t)x & 3u) || ((uintptr_t)gamma & 3u) || ((uintptr_t)y & 3u)) return MOE_EALIGN;
+  MOE_TRY(check_device());
+  RmsArgs a{x, gamma, D, eps, y};
+  return hip_rc(launch_rmsnorm(a, S, stream));
+}
+
+}  // extern "C"

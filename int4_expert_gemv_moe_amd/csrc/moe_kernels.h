@@ -1,0 +1,166 @@
+// moe_kernels.h -- kernel argument structs and kernel declarations.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+struct QuantArgs {
+  const float *xf;     // [S][D] float32, or null
+  const uint16_t *xb;  // [S][D] bf16 bits, or null
+  int D;
+  int8_t *xq_perm;     // optional permuted output
+  int8_t *xq_nat;      // optional natural-order output
+  float *sx;
+  int32_t *sumx;
+};
+
+struct RouterArgs {
+  const float *x;      // [S][D]
+  const float *W;      // [E][D]
+  int S, D, E;
+  float *logits;       // [S][E] scratch (always written)
+  float *logits_out;   // optional caller copy
+  int8_t *xq_perm;     // quantization blocks write these
+  float *sx;
+  int32_t *sumx;
+  uint32_t *amax;      // optional [S][P]: cleared by the quantization blocks
+  int P;
+};
+
+struct PrepArgs {
+  const int8_t *xq;    // [S][D] natural order
+  int D;
+  int8_t *xq_perm;
+  int32_t *sumx;
+  uint32_t *amax;      // optional [S][P]: cleared
+  int P;
+};
+
+struct TopkArgs {
+  const float *logits;
+  const float *bias;
+  int S, E, K;
+  float scale;
+  int32_t *idx;
+  float *w;
+};
+
+// Per-token ("decode") path: three launches, see decode.hip.
+struct DecodeArgs {
+  int S, D, I, E, K, P;     // P = K + n_shared slots per token
+  float scale;              // routed scaling factor
+  const float *x;           // [S][D] float32 tokens (phase A)
+  const float *W;           // [E][D] router
+  const float *bias;        // [E]
+  ExpertSet rt;             // routed stack
+  ExpertSet fx;             // stack holding the fixed expert (shared, or the single expert)
+  int fx_index;             // its index in fx
+  int fx_slot;              // its slot number (K for the shared expert)
+  const int8_t *xq;         // [S][D] permuted codes (phase B; also phase A single-expert calls)
+  const float *sx;          // [S]
+  const int32_t *sumx;      // [S]
+  float *logits;            // [S][E]
+  int32_t *idx;             // [S][K]
+  float *w;                 // [S][K]
+  float *h;                 // [S][P][I]
+  float *ysh;               // [S][D] output of the fixed expert's down projection
+  float *tmp;               // [S][D] running combine between slot batches
+  int n_router;             // phase A: router blocks per token
+  int n_quant;              // phase A: quantization blocks (one per token, column 0)
+  int n_gu_fx;              // phase A: fixed-expert gate/up blocks per token
+  int n_gu_rt;              // phase B: routed gate/up blocks per token
+  int n_dn_fx;              // phase B: fixed-expert down blocks per token
+  int n_dn;                 // phase C: down blocks per token
+  int p_lo, p_hi;           // phase C: routed slots of this launch
+  int c_first, c_last;      // phase C: first / last slot batch of the combine
+  float *out;               // [S][D]
+  unsigned flags;
+  int32_t *acc_gu;          // optional [S][2][I] (single-expert calls)
+  int32_t *acc_d;           // optional [S][D]
+  int8_t *hq_nat;           // optional [S][I]
+  float *sh_out;            // optional [S]
+};
+
+// Grouped (unique-expert union) kernels.
+struct GroupArgs {
+  const int32_t *idx;
+  int S, E, K, P, n_shared;
+  int32_t *gcount, *goff, *pairs;
+};
+
+struct GroupedGateUpArgs {
+  ExpertSet rt, sh;
+  int D, I, E, P;
+  const int32_t *gcount, *goff, *pairs;
+  const int8_t *xq;
+  const float *sx;
+  const int32_t *sumx;
+  float *h;               // [S][P][I]
+};
+
+struct RequantArgs {
+  const float *h;         // [rows][I]
+  int I;
+  int8_t *hq;             // [rows][I] permuted
+  float *sh_scale;
+  int32_t *sumh;
+};
+
+struct GroupedDownArgs {
+  ExpertSet rt, sh;
+  int D, I, E, P;
+  const int32_t *gcount, *goff, *pairs;
+  const int8_t *hq;
+  const float *sh_scale;
+  const int32_t *sumh;
+  float *stage;           // [S][P][D]
+};
+
+struct CombineArgs {
+  const float *stage;
+  const float *w;
+  int S, D, K, P, n_shared;
+  float *out;
+  unsigned flags;
+};
+
+struct PackArgs {
+  const float *w;
+  int O, C;
+  uint8_t *q4;
+  float *scale;
+};
+
+struct RmsArgs {
+  const float *x, *gamma;
+  int D;
+  float eps;
+  float *y;
+};
+
+// Host launchers, each defined next to its kernels.  They return the launch
+// status (hipGetLastError after the launch).
+hipError_t launch_quant(const QuantArgs &a, int S, hipStream_t st);
+hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t st);
+hipError_t launch_prep_xq(const PrepArgs &a, int S, hipStream_t st);
+// Phase launchers of the per-token path (decode.hip).
+hipError_t launch_decode_a(const DecodeArgs &a, bool local_quant, hipStream_t st);
+hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_decode_c(const DecodeArgs &a, hipStream_t st);
+// Slots per phase-C launch for rows of I columns.
+int decode_c_slots(int I);
+hipError_t launch_requant(const RequantArgs &a, int rows, hipStream_t st);
+hipError_t launch_group(const GroupArgs &a, hipStream_t st);
+hipError_t launch_grouped_gateup(const GroupedGateUpArgs &a, hipStream_t st);
+hipError_t launch_grouped_down(const GroupedDownArgs &a, hipStream_t st);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+hipError_t launch_pack(const PackArgs &a, hipStream_t st);
+hipError_t launch_rmsnorm(const RmsArgs &a, int S, hipStream_t st);
+
+// Row length C (int4 columns) supported by the GEMV kernels: C % 32 == 0 and
+// C/2 bytes either below 1024 or up to 4096.
+inline bool gemv_cols_ok(int C) { return C > 0 && C % 32 == 0 && C / 2 <= 4096; }
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+// quant.h -- per-row int8 activation quantization by one block of 256
+// threads (section 12 of the reader.mx article "惊呆了！25GB 内存上运行 GLM 5.2
+// 744B 模型"): s = max(amax/127, 1e-12), q = rint(x * (1/s)).  Shared by the
+// quantization kernel and the per-token path so both produce the same codes.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+// ---- activation quantization (one block of 256 threads per row) -----------
+
+__device__ inline void quant_row_block(const float *xf, const uint16_t *xb, int D, int8_t *xq_perm,
+                                int8_t *xq_nat, float *sx_out, int32_t *sumx_out) {
+  __shared__ float red_f[4];
+  __shared__ int red_i[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ngroups = D >> 3;
+  float m = 0.f;
+  for (int g = tid; g < ngroups; g += blockDim.x) {
+    float v[8];
+    if (xf) {
+      float4 a = reinterpret_cast<const float4 *>(xf)[2 * g];
+      float4 b = reinterpret_cast<const float4 *>(xf)[2 * g + 1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      uint4 r = reinterpret_cast<const uint4 *>(xb)[g];
+      uint32_t wds[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[2 * i] = __uint_as_float(wds[i] << 16);
+        v[2 * i + 1] = __uint_as_float(wds[i] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      float a = fabsf(v[i]);
+      m = (a > m) ? a : m;
+    }
+  }
+  m = wave_max_f32(m);
+  if (lane == 0) red_f[wave] = m;
+  __syncthreads();
+  float amax = red_f[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); i++) amax = (red_f[i] > amax) ? red_f[i] : amax;
+  const float s = quant_scale(amax);
+  const float inv = 1.f / s;
+  int sum = 0;
+  for (int g = tid; g < ngroups; g += blockDim.x) {
+    float v[8];
+    if (xf) {
+      float4 a = reinterpret_cast<const float4 *>(xf)[2 * g];
+      float4 b = reinterpret_cast<const float4 *>(xf)[2 * g + 1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      uint4 r = reinterpret_cast<const uint4 *>(xb)[g];
+      uint32_t wds[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[2 * i] = __uint_as_float(wds[i] << 16);
+        v[2 * i + 1] = __uint_as_float(wds[i] & 0xFFFF0000u);
+      }
+    }
+    int q[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      q[i] = quant_code(v[i], inv);
+      sum += q[i];
+    }
+    uint32_t pe = (q[0] & 0xFF) | ((q[2] & 0xFF) << 8) | ((q[4] & 0xFF) << 16) | ((uint32_t)(q[6] & 0xFF) << 24);
+    uint32_t po = (q[1] & 0xFF) | ((q[3] & 0xFF) << 8) | ((q[5] & 0xFF) << 16) | ((uint32_t)(q[7] & 0xFF) << 24);
+    if (xq_perm) reinterpret_cast<uint2 *>(xq_perm)[g] = make_uint2(pe, po);
+    if (xq_nat) {
+      uint32_t n0 = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | ((uint32_t)(q[3] & 0xFF) << 24);
+      uint32_t n1 = (q[4] & 0xFF) | ((q[5] & 0xFF) << 8) | ((q[6] & 0xFF) << 16) | ((uint32_t)(q[7] & 0xFF) << 24);
+      reinterpret_cast<uint2 *>(xq_nat)[g] = make_uint2(n0, n1);
+    }
+  }
+  sum = wave_sum_i32(sum);
+  if (lane == 0) red_i[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); i++) t += red_i[i];
+    if (sx_out) *sx_out = s;
+    if (sumx_out) *sumx_out = t;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,165 @@
+// router.hip -- sigmoid router, correction-bias top-K and per-row int8
+// activation quantization (sections 11 and 12 of the reader.mx article
+// "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型").
+//
+// Logit arithmetic is fixed independently of the launch shape, so a token
+// gets the same bits whether it is routed alone or inside a batch: lane p of
+// a wave accumulates, with fused multiply-adds in ascending order, the
+// products x[k]*W[e][k] for k = 4p + 256j + q (j ascending, q = 0..3); the 64
+// lane partials are then summed by the fixed DPP tree of wave_sum_f32.  This
+// needs D to be a multiple of 256.
+//
+// No kernel here communicates between workgroups inside a launch: on this
+// chip a device-scope fence writes back and invalidates the issuing XCD's L2,
+// which costs about a microsecond per workgroup, so every cross-workgroup
+// dependency goes through a kernel boundary instead.
+#include "moe_kernels.h"
+#include "topk.h"
+#include "quant.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
+  const int s = blockIdx.x;
+  quant_row_block(a.xf ? a.xf + (int64_t)s * a.D : nullptr,
+                  a.xb ? a.xb + (int64_t)s * a.D : nullptr, a.D,
+                  a.xq_perm ? a.xq_perm + (int64_t)s * a.D : nullptr,
+                  a.xq_nat ? a.xq_nat + (int64_t)s * a.D : nullptr, a.sx ? a.sx + s : nullptr,
+                  a.sumx ? a.sumx + s : nullptr);
+}
+
+// Natural-order int8 rows -> permuted layout plus the row's code sum.
+__global__ __launch_bounds__(256) void prep_xq_kernel(PrepArgs a) {
+  __shared__ int red[4];
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const uint2 *src = reinterpret_cast<const uint2 *>(a.xq + (int64_t)s * a.D);
+  uint2 *dst = reinterpret_cast<uint2 *>(a.xq_perm + (int64_t)s * a.D);
+  int sum = 0;
+  for (int g = tid; g < (a.D >> 3); g += blockDim.x) {
+    uint2 v = src[g];
+    int q[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      q[i] = (int)(int8_t)((v.x >> (8 * i)) & 0xFF);
+      q[4 + i] = (int)(int8_t)((v.y >> (8 * i)) & 0xFF);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) sum += q[i];
+    uint32_t pe = (q[0] & 0xFF) | ((q[2] & 0xFF) << 8) | ((q[4] & 0xFF) << 16) | ((uint32_t)(q[6] & 0xFF) << 24);
+    uint32_t po = (q[1] & 0xFF) | ((q[3] & 0xFF) << 8) | ((q[5] & 0xFF) << 16) | ((uint32_t)(q[7] & 0xFF) << 24);
+    dst[g] = make_uint2(pe, po);
+  }
+  sum = wave_sum_i32(sum);
+  if ((tid & 63) == 0) red[tid >> 6] = sum;
+  if (a.amax && tid < a.P) a.amax[(int64_t)s * a.P + tid] = 0u;
+  __syncthreads();
+  if (tid == 0) a.sumx[s] = red[0] + red[1] + red[2] + red[3];
+}
+
+// ---- top-K over one token's logits by one wave -----------------------------
+
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= a.S) return;
+  topk_rounds(a.logits + (int64_t)s * a.E, a.bias, a.E, a.K, a.scale, a.idx + (int64_t)s * a.K,
+              a.w + (int64_t)s * a.K);
+}
+
+// ---- router logits (+ quantization blocks) -----------------------------------
+
+// Block = 4 waves = 4 experts; TS tokens per block; JB 16-byte loads of the
+// expert row per lane issued together.  Blocks with index >= n_router
+// quantize token (index - n_router) and clear its amax slots.
+template <int TS, int JB>
+__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ne4 = (a.E + 3) >> 2;
+  const int n_router = ne4 * ((a.S + TS - 1) / TS);
+  if ((int)blockIdx.x >= n_router) {
+    const int s = blockIdx.x - n_router;
+    if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
+    quant_row_block(a.x + (int64_t)s * a.D, nullptr, a.D, a.xq_perm + (int64_t)s * a.D, nullptr,
+                    a.sx + s, a.sumx + s);
+    return;
+  }
+  const int e = (blockIdx.x % ne4) * 4 + wave;
+  const int s0 = (blockIdx.x / ne4) * TS;
+  if (e >= a.E) return;
+  float acc[TS];
+#pragma unroll
+  for (int t = 0; t < TS; t++) acc[t] = 0.f;
+  const float4 *wr = reinterpret_cast<const float4 *>(a.W + (int64_t)e * a.D);
+  const int nj = a.D >> 8;
+  for (int j0 = 0; j0 < nj; j0 += JB) {
+    float4 wv[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; jj++) {
+      wv[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + jj < nj) wv[jj] = wr[lane + 64 * (j0 + jj)];
+    }
+#pragma unroll
+    for (int t = 0; t < TS; t++) {
+      if (s0 + t < a.S) {
+        const float4 *xr = reinterpret_cast<const float4 *>(a.x + (int64_t)(s0 + t) * a.D);
+        float4 xv[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; jj++) {
+          xv[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (j0 + jj < nj) xv[jj] = xr[lane + 64 * (j0 + jj)];
+        }
+#pragma unroll
+        for (int jj = 0; jj < JB; jj++) {
+          if (j0 + jj < nj) {
+            acc[t] = fmaf(xv[jj].x, wv[jj].x, acc[t]);
+            acc[t] = fmaf(xv[jj].y, wv[jj].y, acc[t]);
+            acc[t] = fmaf(xv[jj].z, wv[jj].z, acc[t]);
+            acc[t] = fmaf(xv[jj].w, wv[jj].w, acc[t]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TS; t++) {
+    const float v = wave_sum_f32(acc[t]);
+    if (lane == 0 && s0 + t < a.S) {
+      a.logits[(int64_t)(s0 + t) * a.E + e] = v;
+      if (a.logits_out) a.logits_out[(int64_t)(s0 + t) * a.E + e] = v;
+    }
+  }
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_quant(const QuantArgs &a, int S, hipStream_t st) {
+  hipLaunchKernelGGL(quant_kernel, dim3(S), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
+  const int ne4 = (a.E + 3) / 4;
+  const int ts = a.S == 1 ? 1 : (a.S <= 4 ? 4 : 8);
+  const int n_router = ne4 * ((a.S + ts - 1) / ts);
+  const dim3 grid(n_router + (with_quant ? a.S : 0));
+  if (ts == 1)
+    hipLaunchKernelGGL((router_kernel<1, 24>), grid, dim3(256), 0, st, a);
+  else if (ts == 4)
+    hipLaunchKernelGGL((router_kernel<4, 6>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((router_kernel<8, 4>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_xq(const PrepArgs &a, int S, hipStream_t st) {
+  hipLaunchKernelGGL(prep_xq_kernel, dim3(S), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(topk_kernel, dim3((a.S + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,79 @@
+"""The C ABI library loads on a machine without a GPU, exports every function
+include/moe_i4.h declares, and rejects bad arguments on the host before it
+touches a device.  CPU only (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_i4.h")
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import int4_expert_gemv_moe_amd as moe
+    return moe.lib()
+
+
+def test_header_declares_the_five_block_calls():
+    names = _declared()
+    for n in ("moe_router_topk", "moe_quant_act_i8", "moe_expert_swiglu_i4", "moe_layer_forward",
+              "moe_layer_forward_batch"):
+        assert n in names
+    assert len(names) >= 10
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_str(0) == b"ok"
+    assert lib.moe_status_str(-4) == b"workspace too small"
+    assert lib.moe_status_str(-99) == b"unknown status"
+
+
+def test_workspace_bytes_host_logic():
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    cfg = moe.config(6144, 2048, 256, 8)
+    sizes = [L.moe_workspace_bytes(ctypes.byref(cfg), s, 1) for s in (1, 2, 64, 2048)]
+    assert all(a < b for a, b in zip(sizes, sizes[1:]))
+    # the union path stages (K+1) f32 rows of D per token
+    assert sizes[-1] >= 2048 * 9 * 6144 * 4
+    assert L.moe_workspace_bytes(ctypes.byref(cfg), 0, 0) == 0
+    assert L.moe_workspace_bytes(ctypes.byref(cfg), 1, 7) == 0
+    for bad in (moe.config(6000, 2048, 256, 8), moe.config(6144, 2048, 4, 8),
+                moe.config(6144, 2048, 256, 65), moe.config(6144, 2048, 2000, 8),
+                moe.config(6144, 2048, 256, 8, n_shared=2), moe.config(6144, 30, 256, 8)):
+        assert L.moe_workspace_bytes(ctypes.byref(bad), 1, 0) == 0
+
+
+def test_host_validation_before_device():
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    cfg = moe.config(256, 128, 8, 2)
+    layer = moe.LayerC()
+    # null layer / x / out -> invalid argument, decided on the host
+    assert L.moe_layer_forward(ctypes.byref(cfg), None, None, 1, None, 0, None, None, 0, None) == -1
+    assert L.moe_layer_forward_batch(ctypes.byref(cfg), ctypes.byref(layer), None, 1, None, 0, None,
+                                     None, 0, None) == -1
+    bad = moe.config(250, 128, 8, 2)
+    assert L.moe_layer_forward(ctypes.byref(bad), ctypes.byref(layer), None, 1, None, 0, None,
+                               None, 0, None) == -2
+    assert L.moe_pack_int4(None, 4, 8, None, None, None) == -1
+    buf = ctypes.create_string_buffer(64)
+    assert L.moe_pack_int4(buf, 4, 7, buf, buf, None) == -2  # odd C
+    assert L.moe_quant_act_i8(buf, 5, 1, 8, buf, buf, None) == -1  # unknown dtype
+    assert L.moe_quant_act_i8(buf, 0, 1, 12, buf, buf, None) == -2  # D % 8
+    assert L.moe_rmsnorm(None, None, 1, 8, 1e-5, None, None) == -1

@@ -1,0 +1,143 @@
+"""GPU parity of the library's building blocks against the CPU oracle:
+int4 packer, activation quantization, router/top-K, and one SwiGLU expert."""
+import numpy as np
+import pytest
+import torch
+
+import int4_expert_gemv_moe_amd as moe
+import oracle
+import synth
+from gpu_util import (assert_close_rows, check_routing, config_of, say, to_np)
+from oracle.layers import host_expert
+from ref64 import unpack64
+
+pytestmark = pytest.mark.gpu
+
+TINY, GLM = synth.TINY, synth.GLM
+
+
+def _dev_normal(seed, strm, n, sigma):
+    t = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.dev_fill_normal(t.data_ptr(), seed, strm, n, sigma, torch.cuda.current_stream().cuda_stream)
+    return t
+
+
+def test_device_generator_matches_host():
+    strm = synth.stream(synth.K_GATE, 2, 5)
+    d = to_np(_dev_normal(3, strm, 1 << 20, 0.02))
+    h = synth.host_normal(3, strm, 1 << 20, 0.02)
+    assert np.array_equal(d.view(np.uint32), h.view(np.uint32))
+
+
+@pytest.mark.parametrize("O,C", [(7, 256), (64, 6144), (2048, 6144), (6144, 2048), (3, 34)])
+def test_pack_bit_exact(O, C):
+    say(f"pack O={O} C={C}")
+    strm = synth.stream(synth.K_UP, 1, 9)
+    w = _dev_normal(0, strm, O * C, 0.02).view(O, C)
+    q4, s = moe.moe_pack_int4(w)
+    rq4, rs = oracle.pack_int4(synth.host_normal(0, strm, O * C, 0.02).reshape(O, C))
+    assert np.array_equal(to_np(q4), rq4)
+    assert np.array_equal(to_np(s).view(np.uint32), rs.view(np.uint32))
+
+
+def test_pack_edge_rows():
+    w = np.zeros((4, 64), np.float32)
+    w[1, 3] = 7.0
+    w[1, 4] = 3.5  # a tie: rounds to even
+    w[2] = np.linspace(-1, 1, 64, dtype=np.float32)
+    w[3, :] = 1e-9  # scale floor
+    q4, s = moe.moe_pack_int4(torch.from_numpy(w).cuda())
+    rq4, rs = oracle.pack_int4(w)
+    assert np.array_equal(to_np(q4), rq4) and np.array_equal(to_np(s), rs)
+
+
+@pytest.mark.parametrize("S,D", [(1, 6144), (4, 256), (64, 6144), (33, 1024)])
+def test_quant_bit_exact(S, D):
+    x = synth.activations(5, S, D)
+    x[0, 3] = 0.0
+    xq, sx = moe.moe_quant_act_i8(torch.from_numpy(x).cuda())
+    rxq, rsx = oracle.quant_act_i8(x)
+    assert np.array_equal(to_np(xq), rxq)
+    assert np.array_equal(to_np(sx).view(np.uint32), rsx.view(np.uint32))
+
+
+def test_quant_bf16_and_degenerate_rows():
+    x = synth.activations(6, 16, 512)
+    x[1] = 0.0
+    x[2] = 1e-11
+    x[3, ::2] = 127.5  # half-way codes after scaling
+    bits = synth.bf16_bits(x)
+    xb = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    xq, sx = moe.moe_quant_act_i8(xb)
+    rxq, rsx = oracle.quant_act_i8_bf16(bits)
+    assert np.array_equal(to_np(xq), rxq) and np.array_equal(to_np(sx), rsx)
+    xq2, sx2 = moe.moe_quant_act_i8(torch.from_numpy(x).cuda())
+    rxq2, rsx2 = oracle.quant_act_i8(x)
+    assert np.array_equal(to_np(xq2), rxq2) and np.array_equal(to_np(sx2), rsx2)
+
+
+@pytest.mark.parametrize("shape,S,bias", [(TINY, 4, "uniform"), (GLM, 1, "uniform"),
+                                          (GLM, 64, "uniform"), (GLM, 200, "zero")])
+def test_router_topk(shape, S, bias):
+    say(f"router D={shape.D} E={shape.E} S={S}")
+    cfg_o = config_of(shape)
+    cfg = moe.config(shape.D, shape.I, shape.E, shape.K, shape.n_shared, shape.routed_scale)
+    wr = synth.router_w(1, shape)
+    b = synth.router_b_uniform(1, shape) if bias == "uniform" else np.zeros(shape.E, np.float32)
+    x = synth.activations(7, S, shape.D)
+    ws = moe.Workspace(cfg, S, moe.WS_ROUTER)
+    idx, w, logits = moe.moe_router_topk(cfg, torch.from_numpy(x).cuda(), torch.from_numpy(wr).cuda(),
+                                         torch.from_numpy(b).cuda(), ws, want_logits=True)
+    ridx, rw, rlogits, rchoice = oracle.router_topk(cfg_o, x, wr, b)
+    lg = to_np(logits)
+    assert np.abs(lg - rlogits).max() <= 2e-6 * max(1.0, np.abs(rlogits).max())
+    uniq = check_routing(to_np(idx), rchoice, shape.K)
+    wg = to_np(w)
+    assert np.allclose(wg[uniq], rw[uniq], rtol=1e-5, atol=0)
+    say(f"  unique routing for {uniq.sum()}/{S} tokens")
+
+
+def test_router_batch_invariance():
+    # a token's routing does not depend on the batch it is in
+    shape = GLM
+    cfg = moe.config(shape.D, shape.I, shape.E, shape.K)
+    wr = torch.from_numpy(synth.router_w(2, shape)).cuda()
+    b = torch.from_numpy(synth.router_b_uniform(2, shape)).cuda()
+    x = torch.from_numpy(synth.activations(8, 37, shape.D)).cuda()
+    ws = moe.Workspace(cfg, 37, moe.WS_ROUTER)
+    _, _, lg_all = moe.moe_router_topk(cfg, x, wr, b, ws, want_logits=True)
+    for s in (0, 5, 36):
+        _, _, lg1 = moe.moe_router_topk(cfg, x[s:s + 1].contiguous(), wr, b, ws, want_logits=True)
+        assert torch.equal(lg1[0], lg_all[s])
+
+
+@pytest.mark.parametrize("shape,S", [(TINY, 4), (GLM, 1), (GLM, 3)])
+def test_expert_swiglu_parity(shape, S):
+    say(f"swiglu D={shape.D} I={shape.I} S={S}")
+    cfg = moe.config(shape.D, shape.I, shape.E, shape.K)
+    e_id = 3
+    he = host_expert(4, shape, 0, e_id)
+    dev = moe.DeviceExperts.empty(shape.E, shape.D, shape.I)
+    for name in ("gate_q4", "gate_s", "up_q4", "up_s", "down_q4", "down_s"):
+        getattr(dev, name)[e_id].copy_(torch.from_numpy(getattr(he, name)))
+    x = synth.activations(9, S, shape.D)
+    xq, sx = oracle.quant_act_i8(x)
+    ws = moe.Workspace(cfg, S, moe.WS_SWIGLU)
+    r = moe.moe_expert_swiglu_i4(cfg, torch.from_numpy(xq).cuda(), torch.from_numpy(sx).cuda(), dev,
+                                 e_id, ws, probes=True)
+    ref = oracle.expert_swiglu(config_of(shape), xq, sx, he)
+    assert np.array_equal(to_np(r["acc_gu"]), ref["acc_gu"])
+    hq = to_np(r["hq"])
+    mism = (hq != ref["hq"])
+    say(f"  hq mismatches: {int(mism.sum())} of {hq.size}")
+    assert mism.mean() < 1e-3 and np.abs(hq.astype(int) - ref["hq"]).max() <= 1
+    assert np.allclose(to_np(r["sh"]), ref["sh"], rtol=1e-6, atol=0)
+    acc_d = to_np(r["acc_d"])
+    same = ~mism.any(axis=1)
+    assert np.array_equal(acc_d[same], ref["acc_d"][same])
+    # rows whose codes moved by one step: the GPU's down accumulators are the
+    # exact integer products of its own codes
+    if (~same).any():
+        qd = unpack64(he.down_q4, shape.I).astype(np.int64)
+        assert np.array_equal(acc_d[~same], hq[~same].astype(np.int64) @ qd.T)
+    assert_close_rows(to_np(r["y"]), ref["y"], what="expert y")

@@ -1,0 +1,151 @@
+"""GPU parity of the whole block, per-token path and unique-expert union path,
+against the CPU oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import int4_expert_gemv_moe_amd as moe
+import oracle
+import synth
+from gpu_util import (assert_close_rows, bias_for, check_routing, device_layer, oracle_layer, say,
+                      to_np)
+
+pytestmark = pytest.mark.gpu
+
+TINY, GLM = synth.TINY, synth.GLM
+MID = synth.Shape(D=512, I=256, E=64, K=8)
+
+
+def _run(layer, x_np, path, flags=0, out=None):
+    S = x_np.shape[0]
+    ws = moe.Workspace(layer.cfg, S, moe.WS_FORWARD if path == "fwd" else moe.WS_BATCH)
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).cuda()
+    idx = torch.empty(S, layer.cfg.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(S, layer.cfg.K, dtype=torch.float32, device="cuda")
+    fn = moe.moe_layer_forward if path == "fwd" else moe.moe_layer_forward_batch
+    o = fn(layer, x, ws, out=out, flags=flags, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(idx), to_np(w)
+
+
+def _oracle_tokens(L, x_np, rows):
+    """Oracle outputs and choice values for the given token rows."""
+    xs = x_np[rows]
+    L.ensure_for(xs)
+    out = oracle.layer_forward(L, xs)
+    _, _, _, choice = oracle.router_topk(L.cfg, xs, L.router_w, L.router_b)
+    return out, choice
+
+
+@pytest.mark.parametrize("path", ["fwd", "batch"])
+def test_tiny_block(path):
+    b = bias_for("uniform", 0, TINY)
+    dl = device_layer(0, TINY, 0, b)
+    ol = oracle_layer(0, TINY, 0, b)
+    x = synth.activations(0, 4, TINY.D)
+    out, idx, _ = _run(dl, x, path)
+    ref, choice = _oracle_tokens(ol, x, np.arange(4))
+    uniq = check_routing(idx, choice, TINY.K)
+    assert_close_rows(out, ref, uniq, what=f"tiny {path}")
+
+
+@pytest.mark.parametrize("shape,S,bias", [(TINY, 4, "uniform"), (TINY, 1, "uniform"),
+                                          (MID, 5, "uniform"), (MID, 64, "zero"),
+                                          (synth.Shape(D=512, I=256, E=8, K=8), 7, "uniform"),
+                                          (synth.Shape(D=256, I=128, E=8, K=2, n_shared=0), 9,
+                                           "uniform")])
+def test_batch_union_equals_per_token_bit_exact(shape, S, bias):
+    b = bias_for(bias, 1, shape)
+    dl = device_layer(1, shape, 0, b)
+    x = synth.activations(1, S, shape.D)
+    a, ia, _ = _run(dl, x, "fwd")
+    c, ic, _ = _run(dl, x, "batch")
+    assert np.array_equal(ia, ic)
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+    ol = oracle_layer(1, shape, 0, b)
+    ref, choice = _oracle_tokens(ol, x, np.arange(S))
+    uniq = check_routing(ia, choice, shape.K)
+    assert_close_rows(a, ref, uniq, what=f"D={shape.D} E={shape.E} K={shape.K} S={S}")
+
+
+def test_accumulate_flag_and_residual():
+    b = bias_for("uniform", 2, MID)
+    dl = device_layer(2, MID, 0, b)
+    x = synth.activations(2, 6, MID.D)
+    base = synth.activations(3, 6, MID.D)
+    plain, _, _ = _run(dl, x, "fwd")
+    for path in ("fwd", "batch"):
+        acc = torch.from_numpy(base.copy()).cuda()
+        got, _, _ = _run(dl, x, path, flags=moe.F_ACCUMULATE, out=acc)
+        assert np.array_equal(got, base + plain)
+
+
+def test_glm_decode_tokens():
+    """GLM shape, one token per call (the decode step), several tokens."""
+    b = bias_for("uniform", 0, GLM)
+    dl = device_layer(0, GLM, 0, b)
+    ol = oracle_layer(0, GLM, 0, b)
+    x = synth.activations(11, 4, GLM.D)
+    outs, idxs = [], []
+    for s in range(4):
+        say(f"glm decode token {s}")
+        o, i, _ = _run(dl, x[s:s + 1], "fwd")
+        outs.append(o[0])
+        idxs.append(i[0])
+    ref, choice = _oracle_tokens(ol, x, np.arange(4))
+    uniq = check_routing(np.stack(idxs), choice, GLM.K)
+    assert_close_rows(np.stack(outs), ref, uniq, what="glm decode")
+
+
+def test_glm_batched_verify_zipf():
+    """GLM shape, 64 tokens with Zipf(1.1)-skewed routing through the union
+    path; sampled tokens against the oracle; batch == per-token on the GPU."""
+    wr = synth.router_w(0, GLM)
+    b = np.zeros(GLM.E, np.float32)
+    x, _, _ = synth.zipf_activations(0, GLM, 64, wr)
+    dl = device_layer(0, GLM, 0, b, router_w=wr)
+    out_b, idx_b, _ = _run(dl, x, "batch")
+    out_f, idx_f, _ = _run(dl, x, "fwd")
+    assert np.array_equal(idx_b, idx_f)
+    assert np.array_equal(out_b.view(np.uint32), out_f.view(np.uint32))
+    counts = np.bincount(idx_b.ravel(), minlength=GLM.E)
+    say(f"  union size {int((counts > 0).sum())}, hottest expert {int(counts.max())} tokens")
+    rows = np.array([0, 21, 42, 63])
+    ol = oracle_layer(0, GLM, 0, b, router_w=wr)
+    ref, choice = _oracle_tokens(ol, x, rows)
+    uniq = check_routing(idx_b[rows], choice, GLM.K)
+    assert_close_rows(out_b[rows], ref, uniq, what="glm zipf verify")
+
+
+@pytest.mark.slow
+def test_glm_prefill_2048_bf16():
+    """GLM shape, 2048 tokens whose activations are bf16 values, uniform
+    routing (b = 0): sampled tokens against the oracle."""
+    b = np.zeros(GLM.E, np.float32)
+    x = synth.bf16_to_f32(synth.bf16_bits(synth.activations(12, 2048, GLM.D)))
+    dl = device_layer(1, GLM, 0, b)
+    out_b, idx_b, _ = _run(dl, x, "batch")
+    counts = np.bincount(idx_b.ravel(), minlength=GLM.E)
+    say(f"  tokens per expert: min {counts.min()} max {counts.max()}")
+    rows = np.array([0, 1000, 2047])
+    ol = oracle_layer(1, GLM, 0, b)
+    ref, choice = _oracle_tokens(ol, x, rows)
+    uniq = check_routing(idx_b[rows], choice, GLM.K)
+    assert_close_rows(out_b[rows], ref, uniq, what="glm prefill")
+
+
+def test_error_codes():
+    cfg = moe.config(256, 128, 8, 2)
+    b = bias_for("uniform", 0, TINY)
+    dl = device_layer(0, TINY, 0, b)
+    x = torch.from_numpy(synth.activations(0, 4, 256)).cuda()
+    small = moe.Workspace(cfg, 1, moe.WS_FORWARD)
+    with pytest.raises(moe.MoeError, match="workspace"):
+        moe.moe_layer_forward(dl, x, small)
+    ws = moe.Workspace(cfg, 4, moe.WS_FORWARD)
+    xbig = torch.zeros(4 * 256 + 1, dtype=torch.float32, device="cuda")
+    with pytest.raises(moe.MoeError, match="misaligned"):
+        moe.moe_layer_forward(dl, xbig[1:].view(4, 256), ws)
+    bad = moe.config(250, 128, 8, 2)
+    with pytest.raises(moe.MoeError):
+        moe.Workspace(bad, 1, moe.WS_FORWARD)
