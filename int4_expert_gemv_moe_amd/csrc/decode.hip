@@ -696,32 +696,103 @@ __global__ __launch_bounds__(256) void decode_b_kernel(DecodeArgs a) {
   down_fixed<NCHI, MI, MOE_DNFX_ROWS>(a, s, b - a.n_gu_rt);
 }
 
-template <int NCHI, bool MI, int PMAX>
-__global__ __launch_bounds__(256) void decode_c_kernel(DecodeArgs a) {
+// ---- phase C: routed down + combine ---------------------------------------------
+//
+// A phase C workgroup has 8 waves, one per routed slot of the launch, and
+// owns RB consecutive output rows per pass.  Wave p holds slot p's whole
+// hidden row across its lanes (lane l: columns 2048c + 32l .. +32), so it
+// requantizes the row by itself (section 12 rule, the same bits as any other
+// quantization of that row) and keeps the codes in registers: no workgroup
+// barrier until the combine.  The hidden row is loaded first and all of the
+// pass's weight rows right after it, so the requantization runs while the
+// weights stream in.  Each wave leaves its RB partial outputs y_p in LDS;
+// then lane r of the workgroup forms row r's combine: running value, slots
+// in ascending order (weight * y_p), then the extra row.
+constexpr int kCWaves = 8;
+
+int decode_c_slots(int) { return kCWaves; }
+
+// rows per pass for NCH 1 KB chunks of a weight row (96 registers of weights)
+template <int NCH>
+struct CRows {
+  static constexpr int value = NCH == 1 ? 24 : (NCH == 2 ? 12 : (NCH == 3 ? 6 : 4));
+};
+
+int decode_c_rows_per_pass(int I) {
+  const int nch = (I / 2 + 1023) / 1024;
+  return nch == 1 ? 24 : (nch == 2 ? 12 : (nch == 3 ? 6 : 4));
+}
+
+template <int NCH, bool MASKED>
+__global__ __launch_bounds__(64 * kCWaves) void decode_c_kernel(DecodeArgs a) {
+  constexpr int RB = CRows<NCH>::value;
+  __shared__ float ys[kCWaves][RB];
   const int s = blockIdx.y, db = blockIdx.x;
-  DownTask t;
-  t.np = a.p_hi - a.p_lo;
+  const int lane = threadIdx.x & 63, p = threadIdx.x >> 6;
+  const int np = a.p_hi - a.p_lo;
+  const bool live = p < np;  // uniform across the wave
+  const int slot = a.p_lo + (live ? p : 0);
+  const int e = a.idx[s * a.K + slot];
+  const RowPtr M = pick(a.rt.down, a.rt.down, false, e);
+  const float *hrow = a.h + ((int64_t)s * a.P + slot) * a.I;
+  const int rowbytes = a.I >> 1;
+  int d0, d1;
+  split_rows(a.D, a.n_dn, db, d0, d1);
+
+  float4 xf[NCH][8];
+  load_x_f32<NCH, MASKED>(hrow, a.I, xf);
+  uint4 w[RB][NCH];
+  float dsc;
+  auto load_pass = [&](int base) {
 #pragma unroll
-  for (int j = 0; j < MOE_DOWN_MAXP; j++) {
-    const int p = a.p_lo + j;
-    const bool ok = j < t.np;
-    const int e = ok ? a.idx[s * a.K + p] : 0;
-    t.M[j] = pick(a.rt.down, a.rt.down, false, e);
-    t.wgt[j] = ok ? a.w[s * a.K + p] : 0.f;
-    t.weighted[j] = true;
-    t.h[j] = a.h + ((int64_t)s * a.P + (ok ? p : 0)) * a.I;
-  }
-  split_rows(a.D, a.n_dn, db, t.d0, t.d1);
-  t.init = a.c_first ? nullptr : a.tmp + (int64_t)s * a.D;
+    for (int r = 0; r < RB; r++) {
+      const int d = base + r;
+      const uint8_t *wr = (live && d < d1) ? M.q + (int64_t)d * rowbytes
+                                           : reinterpret_cast<const uint8_t *>(hrow);
+#pragma unroll
+      for (int c = 0; c < NCH; c++) {
+        const int off = c * 1024 + lane * 16;
+        const bool ok = !MASKED || off < rowbytes;
+        w[r][c] = ldnt16(wr + off, ok, wr);
+      }
+    }
+    dsc = M.s[min(base + min(lane, RB - 1), d1 - 1)];
+  };
+  int base = d0;
+  load_pass(base);
+  uint4 xv[NCH][2];
+  float sh;
+  const int corr = 8 * quant_x_wave<NCH>(xf, xv, &sh);
+  const float *init = a.c_first ? nullptr : a.tmp + (int64_t)s * a.D;
   const bool last = a.c_last;
-  t.extra = (last && a.P > a.K) ? a.ysh + (int64_t)s * a.D : nullptr;
-  t.out = last ? a.out + (int64_t)s * a.D : a.tmp + (int64_t)s * a.D;
-  t.accumulate = last && (a.flags & MOE_F_ACCUMULATE);
-  t.acc_d = nullptr;
-  t.hq_nat = nullptr;
-  t.sh_out = nullptr;
-  t.first_block = (db == 0);
-  down_block<NCHI, MI, 2, PMAX>(t, a.I);
+  const float *extra = (last && a.P > a.K) ? a.ysh + (int64_t)s * a.D : nullptr;
+  float *out = last ? a.out + (int64_t)s * a.D : a.tmp + (int64_t)s * a.D;
+  const bool accumulate = last && (a.flags & MOE_F_ACCUMULATE);
+  for (;;) {
+    int mine = 0;
+#pragma unroll
+    for (int r = 0; r < RB; r++) {
+      int acc = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; c++) acc = dot32_i4(w[r][c], xv[c][0], xv[c][1], acc);
+      acc = wave_sum_i32(acc);
+      mine = (lane == r) ? acc : mine;
+    }
+    if (lane < RB) ys[p][lane] = ((float)(mine - corr) * dsc) * sh;
+    __syncthreads();
+    const int d = base + threadIdx.x;
+    if (threadIdx.x < RB && d < d1) {
+      float comb = init ? init[d] : 0.f;
+      for (int q = 0; q < np; q++) comb = comb + a.w[s * a.K + a.p_lo + q] * ys[q][threadIdx.x];
+      float v = comb;
+      if (extra) v = v + extra[d];
+      out[d] = accumulate ? (out[d] + v) : v;
+    }
+    base += RB;
+    if (base >= d1) break;
+    __syncthreads();  // ys is rewritten by the next pass
+    load_pass(base);
+  }
 }
 
 // ---- launchers -----------------------------------------------------------------------
@@ -741,10 +812,6 @@ __global__ __launch_bounds__(256) void decode_c_kernel(DecodeArgs a) {
     }                                                           \
   } while (0)
 
-int decode_c_slots(int I) {
-  const int nch = (I / 2 + 1023) / 1024;
-  return nch == 1 ? 8 : (nch == 2 ? 4 : 2);
-}
 
 hipError_t launch_decode_a(const DecodeArgs &a, bool local_quant, hipStream_t st) {
   const dim3 grid(a.n_router + a.n_quant + a.n_gu_fx, a.S);
@@ -790,16 +857,14 @@ hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st) {
 }
 
 template <int N, bool M>
-static void launch_c(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  constexpr int PMAX = N == 1 ? 8 : (N == 2 ? 4 : 2);
-  hipLaunchKernelGGL((decode_c_kernel<N, M, PMAX>), grid, dim3(256), lds, st, a);
+static void launch_c(const DecodeArgs &a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((decode_c_kernel<N, M>), grid, dim3(64 * kCWaves), 0, st, a);
 }
 
 hipError_t launch_decode_c(const DecodeArgs &a, hipStream_t st) {
   const dim3 grid(a.n_dn, a.S);
   const int rb = a.I / 2;
-  const size_t lds = (size_t)decode_c_slots(a.I) * a.I;
-#define MOE_FC(N, M) launch_c<N, M>(a, grid, lds, st)
+#define MOE_FC(N, M) launch_c<N, M>(a, grid, st)
   MOE_COLS(rb, MOE_FC);
 #undef MOE_FC
   return hipGetLastError();

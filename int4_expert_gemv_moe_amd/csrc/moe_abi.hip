@@ -63,10 +63,12 @@ DecodeShape decode_shape(const moe_config &c) {
     return d;
   }();
   DecodeShape d;
-  d.gu_fx = env.gu_fx > 0 ? env.gu_fx : 64;
+  d.gu_fx = env.gu_fx > 0 ? env.gu_fx : 128;
   d.gu_rt = env.gu_rt > 0 ? env.gu_rt : 256;
-  d.dn_fx = env.dn_fx > 0 ? env.dn_fx : 96;
-  d.dn = env.dn > 0 ? env.dn : 256;
+  d.dn_fx = env.dn_fx > 0 ? env.dn_fx : 128;
+  // phase C: one pass of rows per workgroup
+  const int cr = decode_c_rows_per_pass(c.I);
+  d.dn = env.dn > 0 ? env.dn : (c.D + cr - 1) / cr;
   // at least 8 rows per workgroup, at most the rows whose scales fit in LDS
   // (512 for gate/up, 256 for down)
   auto clampn = [](int n, int rows, int maxrows) {

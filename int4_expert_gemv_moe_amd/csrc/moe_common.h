@@ -99,6 +99,30 @@ __device__ __forceinline__ float wave_max_f32(float v) {
                        fmax_nan_skip(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// Wave-wide maximum of an int32 through DPP only: the row steps above, then
+// the two GFX9 row broadcasts (lane 15 of each row into the next row, lane 31
+// into rows 2 and 3), after which lane 63 holds the maximum.
+#define MOE_DPP_ROW_BCAST15 0x142
+#define MOE_DPP_ROW_BCAST31 0x143
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, dpp_i<MOE_DPP_QUAD_X1>(v));
+  v = max(v, dpp_i<MOE_DPP_QUAD_X2>(v));
+  v = max(v, dpp_i<MOE_DPP_HALF_MIRROR>(v));
+  v = max(v, dpp_i<MOE_DPP_ROW_MIRROR>(v));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, MOE_DPP_ROW_BCAST15, 0xA, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, MOE_DPP_ROW_BCAST31, 0xC, 0xF, false));
+  return lane_i(v, 63);
+}
+
+// Minimum over the wave, same on every lane.
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, dpp_i<MOE_DPP_QUAD_X1>(v));
+  v = min(v, dpp_i<MOE_DPP_QUAD_X2>(v));
+  v = min(v, dpp_i<MOE_DPP_HALF_MIRROR>(v));
+  v = min(v, dpp_i<MOE_DPP_ROW_MIRROR>(v));
+  return min(min(lane_i(v, 0), lane_i(v, 16)), min(lane_i(v, 32), lane_i(v, 48)));
+}
+
 // Position of value j (0 <= j < 8) of an 8-group in the permuted layout.
 __device__ __host__ __forceinline__ int perm8(int j) { return (j & 1) ? 4 + (j >> 1) : (j >> 1); }
 

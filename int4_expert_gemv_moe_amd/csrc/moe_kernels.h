@@ -151,6 +151,8 @@ hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_c(const DecodeArgs &a, hipStream_t st);
 // Slots per phase-C launch for rows of I columns.
 int decode_c_slots(int I);
+// Output rows a phase C workgroup computes per pass.
+int decode_c_rows_per_pass(int I);
 hipError_t launch_requant(const RequantArgs &a, int rows, hipStream_t st);
 hipError_t launch_group(const GroupArgs &a, hipStream_t st);
 hipError_t launch_grouped_gateup(const GroupedGateUpArgs &a, hipStream_t st);

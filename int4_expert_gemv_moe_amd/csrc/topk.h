@@ -3,96 +3,106 @@
 // by the per-token gate/up kernel, so both select identically.
 #pragma once
 
+#include <climits>
+
 #include "moe_common.h"
 
 namespace moe {
+
+// Integer key with the order of a non-NaN float (-0 taken as +0 first, so
+// that equal choices give equal keys).
+__device__ __forceinline__ int topk_key(float c) {
+  const int b = __float_as_int(c == 0.f ? 0.f : c);
+  return b >= 0 ? b : (b ^ 0x7FFFFFFF);
+}
 
 // Runs `rounds` selection rounds of the section 11 rule over E experts held
 // MAXM per lane (expert e in lane e % 64, slot e / 64; E <= 64*MAXM).
 // Round k picks the largest choice not taken yet, ties to the lowest index;
 // candidates need choice > -1e30 (a NaN never qualifies); with no candidate
-// left, the lowest untaken index.  Each round is one wave-wide float maximum
-// (DPP) followed by ballots that find the lowest index holding that maximum,
-// so the whole selection is branch-free except for the uniform fallback.
-// If idx_out is given, lane 0 writes every round's expert and weight;
-// sel_out (e.g. shared memory) receives every round's expert.  Returns the
-// expert of the last round on every lane.
-template <int MAXM, bool CACHE>
+// left, the lowest untaken index.  Choices become order-preserving integer
+// keys (non-candidates the key of -inf; padding past E the lowest key of all,
+// index INT_MAX) and each lane sorts its own entries by (key descending,
+// index ascending), so a round only compares the 64 list heads: one DPP
+// maximum, a ballot of the lanes holding it (a tie between lanes takes an
+// integer minimum over their indices), and the winning lane pops its head.
+// Lanes 0..rounds-1 then write their round's expert to idx_out / sel_out and
+// weight sigmoid(logit) * scale to w_out (each pointer optional; sel_out may
+// be shared memory).  Returns the expert of the last round on every lane.
+template <int MAXM>
 __device__ inline int topk_rounds_m(const float *logits, const float *bias, int E, int rounds,
                                    float scale, int32_t *idx_out, float *w_out, int *sel_out) {
+  constexpr int kNone = static_cast<int>(0x807FFFFF);  // key of -inf
+  constexpr int kPad = INT_MIN;
   const int lane = threadIdx.x & 63;
-  const int nm = (E + 63) >> 6;
-  // choice values (-inf when not a candidate); held in registers when CACHE,
-  // else recomputed each round from the same expression (same bits)
-  float c[CACHE ? MAXM : 1];
-  if (CACHE) {
-    float lg[CACHE ? MAXM : 1], bs[CACHE ? MAXM : 1];
+  int v[MAXM], ix[MAXM];
+  {
+    float lg[MAXM], bs[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; m++) {
       const int e = min(lane + 64 * m, E - 1);
-      lg[CACHE ? m : 0] = logits[e];
-      bs[CACHE ? m : 0] = bias[e];
+      lg[m] = logits[e];
+      bs[m] = bias[e];
     }
 #pragma unroll
     for (int m = 0; m < MAXM; m++) {
       const int e = lane + 64 * m;
-      const float v = sigmoid(lg[CACHE ? m : 0]) + bs[CACHE ? m : 0];
-      c[CACHE ? m : 0] = (m < nm && e < E && v > -1e30f) ? v : -INFINITY;
+      const float c = sigmoid(lg[m]) + bs[m];
+      v[m] = e < E ? (c > -1e30f ? topk_key(c) : kNone) : kPad;
+      ix[m] = e < E ? e : INT_MAX;
     }
   }
-  uint32_t taken = 0;
-  int sel = 0;
+  // odd-even transposition sort of the lane's list (indices ascend with m,
+  // so keeping equal keys in place keeps them in index order)
+#pragma unroll
+  for (int r = 0; r < MAXM; r++) {
+#pragma unroll
+    for (int m = r & 1; m + 1 < MAXM; m += 2) {
+      const bool sw = v[m + 1] > v[m];
+      const int tv = v[m], ti = ix[m];
+      v[m] = sw ? v[m + 1] : tv;
+      ix[m] = sw ? ix[m + 1] : ti;
+      v[m + 1] = sw ? tv : v[m + 1];
+      ix[m + 1] = sw ? ti : ix[m + 1];
+    }
+  }
+  int mine = 0, sel = 0;
   for (int k = 0; k < rounds; k++) {
-    float cv[MAXM];
-#pragma unroll
-    for (int m = 0; m < MAXM; m++) {
-      const int e = lane + 64 * m;
-      float v;
-      if (CACHE) {
-        v = c[CACHE ? m : 0];
-      } else {
-        const int ec = min(e, E - 1);
-        const float t = sigmoid(logits[ec]) + bias[ec];
-        v = (m < nm && e < E && t > -1e30f) ? t : -INFINITY;
-      }
-      cv[m] = ((taken >> m) & 1u) ? -INFINITY : v;
-    }
-    float mx = cv[0];
-#pragma unroll
-    for (int m = 1; m < MAXM; m++) mx = fmax_nan_skip(mx, cv[m]);
-    mx = wave_max_f32(mx);
-    sel = -1;
-    if (mx > -INFINITY) {
-#pragma unroll
-      for (int m = 0; m < MAXM; m++) {
-        const unsigned long long b = __ballot(cv[m] == mx);
-        if (sel < 0 && b) sel = 64 * m + __builtin_ctzll(b);
-      }
+    const int mx = wave_max_i32(v[0]);
+    const unsigned long long ties = __ballot(v[0] == mx);
+    if (__popcll(ties) == 1) {
+      sel = lane_i(ix[0], __builtin_ctzll(ties));
     } else {
+      // several heads hold the maximum: the lowest index among them
+      sel = wave_min_i32(v[0] == mx ? ix[0] : INT_MAX);
+    }
+    if (lane == k) mine = sel;
+    const bool pop = (ix[0] == sel);
 #pragma unroll
-      for (int m = 0; m < MAXM; m++) {
-        const int e = lane + 64 * m;
-        const unsigned long long b = __ballot(m < nm && e < E && !((taken >> m) & 1u));
-        if (sel < 0 && b) sel = 64 * m + __builtin_ctzll(b);
-      }
+    for (int m = 0; m + 1 < MAXM; m++) {
+      v[m] = pop ? v[m + 1] : v[m];
+      ix[m] = pop ? ix[m + 1] : ix[m];
     }
-    if ((sel & 63) == lane) taken |= 1u << (sel >> 6);
-    if (idx_out && lane == 0) {
-      idx_out[k] = sel;
-      w_out[k] = sigmoid(logits[sel]) * scale;
+    v[MAXM - 1] = pop ? kPad : v[MAXM - 1];
+    ix[MAXM - 1] = pop ? INT_MAX : ix[MAXM - 1];
+  }
+  if (lane < rounds) {
+    if (sel_out) sel_out[lane] = mine;
+    if (idx_out) {
+      idx_out[lane] = mine;
+      w_out[lane] = sigmoid(logits[mine]) * scale;
     }
-    if (sel_out && lane == 0) sel_out[k] = sel;
   }
   return sel;
 }
 
-// sel_out (optional, e.g. shared memory) receives every round's expert.
+// sel_out (optional, e.g. shared memory) receives every round's expert; the
+// caller synchronizes before reading it.
 __device__ inline int topk_rounds(const float *logits, const float *bias, int E, int rounds,
                                   float scale, int32_t *idx_out, float *w_out,
                                   int *sel_out = nullptr) {
-  if (E <= 256)
-    return topk_rounds_m<4, true>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
-  return topk_rounds_m<16, false>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
+  if (E <= 256) return topk_rounds_m<4>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
+  return topk_rounds_m<16>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
 }
 
 }  // namespace moe
