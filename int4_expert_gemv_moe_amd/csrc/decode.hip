@@ -189,9 +189,13 @@ struct GuMats {
   float *h;  // hidden row of the slot
 };
 
+// One pipeline stage: ROWS gate and up rows of the wave, plus the row scales
+// of item (first + lane) for lanes < ROWS (they are only needed after the
+// stage's dot products, so they travel with its loads).
 template <int NCH, int ROWS>
 struct GuStage {
   uint4 g[ROWS][NCH], u[ROWS][NCH];
+  float gs, us;
 };
 
 template <int NCH, bool MASKED, int ROWS, class Res>
@@ -216,30 +220,18 @@ __device__ __forceinline__ void gu_load(Res res, int I, int rowbytes, int item, 
       st.u[r][c] = ldnt16(ur + off, ok, ur);
     }
   }
-}
-
-// Row scales of the block's items [lo, hi) into LDS (one round of loads).
-template <class Res>
-__device__ __forceinline__ void gu_scales(Res res, int I, int lo, int hi, float *gsc, float *usc) {
-  for (int t0 = 0; t0 < hi - lo; t0 += 64 * kWaves) {
-    const int t = t0 + threadIdx.x;
-    const int it = lo + min(t, hi - lo - 1);
-    const int slot = it / I;
-    const int row = it - slot * I;
-    const GuMats m = res(slot);
-    const float g = m.G.s[row], u = m.U.s[row];
-    if (t < hi - lo) {
-      gsc[t] = g;
-      usc[t] = u;
-    }
-  }
+  const int itc = min(item + min(lane, ROWS - 1), hi - 1);
+  const int slot = itc / I;
+  const int row = itc - slot * I;
+  const GuMats m = res(slot);
+  st.gs = m.G.s[row];
+  st.us = m.U.s[row];
 }
 
 template <int NCH, int ROWS>
 __device__ __forceinline__ void gu_step(const GuStage<NCH, ROWS> &st, const uint4 (&xv)[NCH][2],
                                         int corr, float sxs, int item, int lo, int hi,
-                                        const float *gsc, const float *usc, float *hout,
-                                        int *acco) {
+                                        float *hout, int *acco) {
   const int lane = threadIdx.x & 63;
   int ag[ROWS], au[ROWS];
 #pragma unroll
@@ -265,8 +257,8 @@ __device__ __forceinline__ void gu_step(const GuStage<NCH, ROWS> &st, const uint
   if (lane < ROWS && it < hi) {
     const int t = it - lo;
     const int accg = myg - corr, accu = myu - corr;
-    const float g = ((float)accg * gsc[t]) * sxs;
-    const float u = ((float)accu * usc[t]) * sxs;
+    const float g = ((float)accg * st.gs) * sxs;
+    const float u = ((float)accu * st.us) * sxs;
     hout[t] = silu(g) * u;
     if (acco) {
       acco[2 * t] = accg;
@@ -277,11 +269,11 @@ __device__ __forceinline__ void gu_step(const GuStage<NCH, ROWS> &st, const uint
 
 // Shared-memory buffers of a gate/up block.
 struct GuLds {
-  float gsc[MOE_GU_MAX_ROWS], usc[MOE_GU_MAX_ROWS], h[MOE_GU_MAX_ROWS];
+  float h[MOE_GU_MAX_ROWS];
 };
 
 // Walks this wave's items with a two-stage pipeline (the caller issued the
-// first stage into sa and staged the row scales), then writes the block's
+// first stage into sa), then writes the block's
 // hidden values (and accumulators when acc_gu is set) to global memory.
 template <int NCH, bool MASKED, int ROWS, class Res>
 __device__ __forceinline__ void gu_items(Res res, int I, int rowbytes, int lo, int hi,
@@ -296,9 +288,9 @@ __device__ __forceinline__ void gu_items(Res res, int I, int rowbytes, int lo, i
   for (int i = 0; i < nsteps; i += 2) {
     const int ra = first + i * stride, rb = ra + stride;
     gu_load<NCH, MASKED, ROWS>(res, I, rowbytes, rb, hi, dummy, sb);
-    gu_step<NCH, ROWS>(sa, xv, corr, sxs, ra, lo, hi, L.gsc, L.usc, L.h, acco);
+    gu_step<NCH, ROWS>(sa, xv, corr, sxs, ra, lo, hi, L.h, acco);
     gu_load<NCH, MASKED, ROWS>(res, I, rowbytes, rb + stride, hi, dummy, sa);
-    if (i + 1 < nsteps) gu_step<NCH, ROWS>(sb, xv, corr, sxs, rb, lo, hi, L.gsc, L.usc, L.h, acco);
+    if (i + 1 < nsteps) gu_step<NCH, ROWS>(sb, xv, corr, sxs, rb, lo, hi, L.h, acco);
   }
   __syncthreads();
   for (int t = threadIdx.x; t < hi - lo; t += 64 * kWaves) {
@@ -338,19 +330,31 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb) {
   int sumx;
   int32_t *acc_gu = a.acc_gu ? a.acc_gu + (int64_t)s * 2 * a.I : nullptr;
   if (LOCALQ) {
-    float4 xf[NCH][8];
-    load_x_f32<NCH, MASKED>(a.x + (int64_t)s * a.D, a.D, xf);
-    gu_scales(res, a.I, lo, hi, L.gsc, L.usc);
+    // the block quantizes the token row once into shared memory (each wave
+    // then reads its lanes' codes); the first weight stage is already in
+    // flight while it does
+    __shared__ __align__(16) int8_t xcodes[2048 * 4];
+    float4 xr[NCH][2];
+    quant_row_load<NCH>(a.x + (int64_t)s * a.D, a.D, xr);
     gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
-    sumx = quant_x_wave<NCH>(xf, xv, &sxs);
+    sumx = quant_row_block_lds<NCH>(xr, a.D, xcodes, &sxs);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+      const int col = 2048 * c + 32 * lane;
+      const bool ok = !MASKED || col < a.D;
+      const int cc = ok ? col : 0;
+      const uint4 v0 = *reinterpret_cast<const uint4 *>(xcodes + cc);
+      const uint4 v1 = *reinterpret_cast<const uint4 *>(xcodes + cc + 16);
+      xv[c][0] = ok ? v0 : make_uint4(0u, 0u, 0u, 0u);
+      xv[c][1] = ok ? v1 : make_uint4(0u, 0u, 0u, 0u);
+    }
   } else {
     load_x_codes<NCH, MASKED>(a.xq + (int64_t)s * a.D, a.D, xv);
     sxs = a.sx[s];
     sumx = a.sumx[s];
-    gu_scales(res, a.I, lo, hi, L.gsc, L.usc);
     gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
   }
-  __syncthreads();
   gu_items<NCH, MASKED, ROWS>(res, a.I, rowbytes, lo, hi, xv, 8 * sumx, sxs, L,
                               acc_gu ? acco : nullptr, acc_gu, dummy, sa);
 }
@@ -390,10 +394,8 @@ __device__ void gateup_routed(const DecodeArgs &a, int s, int gb) {
   split_rows(a.K * a.I, a.n_gu_rt, gb, lo, hi);
   const int first = lo + wave * ROWS;
   const uint8_t *dummy = reinterpret_cast<const uint8_t *>(a.xq + (int64_t)s * a.D);
-  gu_scales(res, I, lo, hi, L.gsc, L.usc);
   GuStage<NCH, ROWS> sa;
   gu_load<NCH, MASKED, ROWS>(res, I, rowbytes, first, hi, dummy, sa);
-  __syncthreads();
   gu_items<NCH, MASKED, ROWS>(res, I, rowbytes, lo, hi, xv, corr, sxs, L, nullptr, nullptr, dummy,
                               sa);
 }
