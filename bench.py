@@ -18,11 +18,11 @@ Timed regions (each bracketed by device synchronization):
   1. K steps replayed from HIP graphs of G consecutive steps (decode serving
      captures its step loop in graphs) -> "value";
   2. K steps launched directly on the stream -> "stream_us_per_token";
-  3. K steps on the stream with HIP events recorded around the second and
-     third launches of every step (events add gaps, so this pass gives only
-     the kernel durations) -> "kernels_us" and "roofline" (the second launch,
-     routed gate/up + shared-expert down, 107 MB of weights, is the dominant
-     kernel).
+  3. K steps on the stream with HIP events handed to the second and third
+     launches of every step (the library launches them with hipExtLaunchKernel,
+     so each event pair holds that kernel's own start and end timestamps)
+     -> "kernels_us" and "roofline" (the second launch, routed gate/up +
+     shared-expert down, 107 MB of weights, is the dominant kernel).
 
 Prints one JSON line.
 """
@@ -38,6 +38,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COPY_CAL_BYTES = 256 << 20
+# rocprofv3 counter summary of the dominant kernel (HBM bytes per launch, and
+# the hash of the kernel source it was taken on)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b_kernel_glm_decode_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "int4_expert_gemv_moe_amd", "csrc", f)
+                  for f in ("decode.hip", "moe_common.h", "quant.h", "topk.h", "moe_kernels.h",
+                            "moe_abi.hip")]
 D, I, E, K = 6144, 2048, 256, 8
 EXPERT_GATEUP_BYTES = 2 * I * (D // 2) + 2 * I * 4          # 12,599,296
 EXPERT_DOWN_BYTES = D * (I // 2) + D * 4                     # 6,316,032
@@ -52,6 +59,34 @@ PHASE_C_BYTES = K * EXPERT_DOWN_BYTES                        # routed down
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(n_tokens: int, seed: int = 0):
@@ -83,8 +118,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--tokens", type=int, default=256)
-    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay pass (value then comes from the stream pass); "
+                         "used for counter runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 8 times (the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -99,6 +140,17 @@ def main():
     from synth.device_layers import build_device_layer
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = COPY_CAL_BYTES // 4
+        src = torch.arange(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[-4:], src[-4:])
+        log(f"copied {COPY_CAL_BYTES} bytes 8 times")
+        return
     lib = moe.lib()
     t0 = time.time()
     layers = []
@@ -137,22 +189,26 @@ def main():
 
     # 1. graph replay: G steps per graph, G the largest divisor of K up to 64
     G = max(g for g in range(1, min(64, K) + 1) if K % g == 0)
-    n_graphs = max(1, min(K // G, (R * T) // G))
-    graphs = []
-    cap = torch.cuda.Stream()
-    for j in range(n_graphs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            run(G, stream_handle=ctypes.c_void_p(cap.cuda_stream), start=j * G)
-        graphs.append(g)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(K // G):
-        graphs[i % n_graphs].replay()
-    torch.cuda.synchronize()
-    graph_us = (time.perf_counter() - t_start) / K * 1e6
+    if args.no_graph:
+        G = 0
+    graph_us = None
+    if G:
+        n_graphs = max(1, min(K // G, (R * T) // G))
+        graphs = []
+        cap = torch.cuda.Stream()
+        for j in range(n_graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                run(G, stream_handle=ctypes.c_void_p(cap.cuda_stream), start=j * G)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(K // G):
+            graphs[i % n_graphs].replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - t_start) / K * 1e6
 
     # 2. plain stream launches
     torch.cuda.synchronize()
@@ -161,7 +217,7 @@ def main():
     torch.cuda.synchronize()
     stream_us = (time.perf_counter() - t_start) / K * 1e6
 
-    # 3. instrumented pass: events around the gate/up and down kernels
+    # 3. instrumented pass: kernel timestamps of the gate/up and down kernels
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for e4 in evs:
         for e in e4:
@@ -183,8 +239,8 @@ def main():
     dn = np.array([e4[2].elapsed_time(e4[3]) for e4 in evs]) * 1e3
     gu_avg, dn_avg = float(gu.mean()), float(dn.mean())
     achieved = PHASE_B_BYTES / (gu_avg * 1e-6) / 1e9
-    us_per_token = graph_us
-    log(f"graph {graph_us:.2f} us/token (G={G}); stream {stream_us:.2f}; with events "
+    us_per_token = graph_us if graph_us is not None else stream_us
+    log(f"graph {graph_us} us/token (G={G}); stream {stream_us:.2f}; with events "
         f"{evented_us:.2f}; phase B {gu_avg:.2f} us (p50 {np.median(gu):.2f}, {achieved:.0f} GB/s); "
         f"phase C {dn_avg:.2f} us ({PHASE_C_BYTES / dn_avg / 1e3:.0f} GB/s); "
         f"layer {LAYER_TOKEN_BYTES / us_per_token / 1e3:.0f} GB/s")
@@ -213,7 +269,7 @@ def main():
                                "experts top-8 + 1 shared, int4 experts 2048x6144)",
                    "global_batch": 1, "layer_replicas": R, "distinct_tokens": T},
         "tokens_per_s": round(1e6 / us_per_token, 1),
-        "timing": f"HIP graph replay, {G} steps per graph",
+        "timing": (f"HIP graph replay, {G} steps per graph" if G else "stream launches"),
         "stream_us_per_token": round(stream_us, 3),
         "layer_bytes_per_token": LAYER_TOKEN_BYTES,
         "layer_GBps": round(layer_gbps, 1),
@@ -222,7 +278,7 @@ def main():
                        "phase_c_routed_down_combine": round(dn_avg, 3)},
         "roofline": {"bound": "hbm", "kernel": "decode_b_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": PHASE_B_BYTES},
         "cpu_baseline": cpu,
     }

@@ -98,8 +98,13 @@ typedef struct {
 typedef struct {
   int32_t *topk_idx;    /* [S][K] experts chosen for each token, in selection order */
   float *topk_w;        /* [S][K] their weights */
-  hipEvent_t ev_gateup[2]; /* if both set: recorded around the gate/up kernel */
-  hipEvent_t ev_down[2];   /* if both set: recorded around the down kernel */
+  /* If both events of a pair are set they time that kernel.  moe_layer_forward
+   * launches its gate/up kernel (routed gate/up + shared down) and its down
+   * kernel(s) with hipExtLaunchKernel, so the events take the kernels' own
+   * start and end timestamps; moe_layer_forward_batch records them on the
+   * stream around its grouped gate/up and grouped down kernels. */
+  hipEvent_t ev_gateup[2];
+  hipEvent_t ev_down[2];
 } moe_probe;
 
 /* Human-readable name of a status code (static string). */

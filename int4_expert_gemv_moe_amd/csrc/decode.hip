@@ -20,6 +20,8 @@
 // 16l + 1024c of a row (c = 1 KB chunk), so one wave instruction covers 1 KB
 // of contiguous HBM.  Each wave walks its rows ROWS at a time and keeps the
 // next step's loads in flight while it computes the current one.
+#include <hip/hip_ext.h>
+
 #include "moe_kernels.h"
 #include "quant.h"
 #include "topk.h"
@@ -799,6 +801,17 @@ __global__ __launch_bounds__(64 * kCWaves) void decode_c_kernel(DecodeArgs a) {
 
 // ---- launchers -----------------------------------------------------------------------
 
+// Plain launch, or, when an event is given, a launch whose dispatch itself
+// records the kernel's start (e0) and end (e1) timestamps.
+template <class F>
+static void launch_timed(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, hipEvent_t e0,
+                         hipEvent_t e1, const DecodeArgs &a) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u, a);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, a);
+}
+
 // Column dispatch: NCH 1 KB chunks per row, masked when the row is not a whole
 // number of chunks.
 #define MOE_COLS(RB, F)                                         \
@@ -830,12 +843,12 @@ hipError_t launch_decode_a(const DecodeArgs &a, bool local_quant, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st) {
+hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(a.n_gu_rt + a.n_dn_fx, a.S);
   const size_t lds = (size_t)a.I;  // one hidden row of codes
   const int rbd = a.D / 2, rbi = a.I / 2;
 #define MOE_FBI(NI, MI, ND, MD) \
-  hipLaunchKernelGGL((decode_b_kernel<ND, MD, NI, MI>), grid, dim3(256), lds, st, a)
+  launch_timed((decode_b_kernel<ND, MD, NI, MI>), grid, dim3(256), lds, st, e0, e1, a)
 #define MOE_FBD(ND, MD)                                          \
   do {                                                           \
     const int nchi_ = (rbi + 1023) / 1024;                       \
@@ -859,14 +872,14 @@ hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st) {
 }
 
 template <int N, bool M>
-static void launch_c(const DecodeArgs &a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_c_kernel<N, M>), grid, dim3(64 * kCWaves), 0, st, a);
+static void launch_c(const DecodeArgs &a, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  launch_timed((decode_c_kernel<N, M>), grid, dim3(64 * kCWaves), 0, st, e0, e1, a);
 }
 
-hipError_t launch_decode_c(const DecodeArgs &a, hipStream_t st) {
+hipError_t launch_decode_c(const DecodeArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(a.n_dn, a.S);
   const int rb = a.I / 2;
-#define MOE_FC(N, M) launch_c<N, M>(a, grid, st)
+#define MOE_FC(N, M) launch_c<N, M>(a, grid, st, e0, e1)
   MOE_COLS(rb, MOE_FC);
 #undef MOE_FC
   return hipGetLastError();

@@ -397,20 +397,20 @@ int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float
   d.out = out;
   d.flags = flags;
   MOE_TRY_HIP(launch_decode_a(d, true, stream));
-  MOE_TRY(record(probe, 0, 0, stream));
-  MOE_TRY_HIP(launch_decode_b(d, stream));
-  MOE_TRY(record(probe, 0, 1, stream));
+  const bool tgu = probe && probe->ev_gateup[0] && probe->ev_gateup[1];
+  const bool tdn = probe && probe->ev_down[0] && probe->ev_down[1];
+  MOE_TRY_HIP(launch_decode_b(d, stream, tgu ? probe->ev_gateup[0] : nullptr,
+                              tgu ? probe->ev_gateup[1] : nullptr));
   MOE_TRY(copy_probe(c, S, probe, w, stream));
   const int batch = decode_c_slots(c.I);
-  MOE_TRY(record(probe, 1, 0, stream));
   for (int p0 = 0; p0 < c.K; p0 += batch) {
     d.p_lo = p0;
     d.p_hi = std::min(c.K, p0 + batch);
     d.c_first = (p0 == 0);
     d.c_last = (d.p_hi == c.K);
-    MOE_TRY_HIP(launch_decode_c(d, stream));
+    MOE_TRY_HIP(launch_decode_c(d, stream, (tdn && d.c_first) ? probe->ev_down[0] : nullptr,
+                                (tdn && d.c_last) ? probe->ev_down[1] : nullptr));
   }
-  MOE_TRY(record(probe, 1, 1, stream));
   return MOE_OK;
 }
 

@@ -147,8 +147,11 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st);
 hipError_t launch_prep_xq(const PrepArgs &a, int S, hipStream_t st);
 // Phase launchers of the per-token path (decode.hip).
 hipError_t launch_decode_a(const DecodeArgs &a, bool local_quant, hipStream_t st);
-hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st);
-hipError_t launch_decode_c(const DecodeArgs &a, hipStream_t st);
+// e0 / e1 (optional): events that take the kernel's own start / end timestamps
+hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st, hipEvent_t e0 = nullptr,
+                           hipEvent_t e1 = nullptr);
+hipError_t launch_decode_c(const DecodeArgs &a, hipStream_t st, hipEvent_t e0 = nullptr,
+                           hipEvent_t e1 = nullptr);
 // Slots per phase-C launch for rows of I columns.
 int decode_c_slots(int I);
 // Output rows a phase C workgroup computes per pass.
