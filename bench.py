@@ -41,10 +41,11 @@ HBM_PEAK_GBPS = 8000.0
 COPY_CAL_BYTES = 256 << 20
 # rocprofv3 counter summary of the dominant kernel (HBM bytes per launch, and
 # the hash of the kernel source it was taken on)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b_kernel_glm_decode_traffic.md")
+TRAFFIC_FILES = {k: os.path.join(ROOT, "profiles", f"{k}_glm_decode_traffic.md")
+                 for k in ("decode_b_kernel",)}
 KERNEL_SOURCES = [os.path.join(ROOT, "int4_expert_gemv_moe_amd", "csrc", f)
-                  for f in ("decode.hip", "moe_common.h", "quant.h", "topk.h", "moe_kernels.h",
-                            "moe_abi.hip")]
+                  for f in ("decode.hip", "rowops.h", "moe_common.h", "quant.h", "topk.h",
+                            "moe_kernels.h", "moe_abi.hip")]
 D, I, E, K = 6144, 2048, 256, 8
 EXPERT_GATEUP_BYTES = 2 * I * (D // 2) + 2 * I * 4          # 12,599,296
 EXPERT_DOWN_BYTES = D * (I // 2) + D * 4                     # 6,316,032
@@ -70,13 +71,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when it is missing or was taken on other kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of the kernel from the committed counter summary,
+    or None when it is missing or was taken on other kernel sources."""
+    path = TRAFFIC_FILES.get(kernel)
+    if path is None or not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if line.startswith("- ") and ":" in line:
                 k, v = line[2:].split(":", 1)
@@ -193,31 +195,43 @@ def main():
         G = 0
     graph_us = None
     if G:
-        n_graphs = max(1, min(K // G, (R * T) // G))
-        graphs = []
-        cap = torch.cuda.Stream()
-        for j in range(n_graphs):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                run(G, stream_handle=ctypes.c_void_p(cap.cuda_stream), start=j * G)
-            graphs.append(g)
-        for g in graphs:
-            g.replay()
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for i in range(K // G):
-            graphs[i % n_graphs].replay()
-        torch.cuda.synchronize()
-        graph_us = (time.perf_counter() - t_start) / K * 1e6
+        try:
+            n_graphs = max(1, min(K // G, (R * T) // G))
+            graphs = []
+            cap = torch.cuda.Stream()
+            for j in range(n_graphs):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    run(G, stream_handle=ctypes.c_void_p(cap.cuda_stream), start=j * G)
+                graphs.append(g)
+            for g in graphs:
+                g.replay()
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for i in range(K // G):
+                graphs[i % n_graphs].replay()
+            torch.cuda.synchronize()
+            graph_us = (time.perf_counter() - t_start) / K * 1e6
+        except Exception as exc:  # a launch the graph capture does not take
+            torch.cuda.synchronize()
+            log(f"graph capture unavailable ({type(exc).__name__}: {exc}); timing stream launches")
+            G = 0
+            graph_us = None
 
-    # 2. plain stream launches
+    # 2. plain stream launches, events bracketing the timed region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev0.record(stream)
     run(K)
+    ev1.record(stream)
     torch.cuda.synchronize()
     stream_us = (time.perf_counter() - t_start) / K * 1e6
+    region_us = ev0.elapsed_time(ev1) * 1e3 / K
+    us_per_token = graph_us if graph_us is not None else stream_us
 
     # 3. instrumented pass: kernel timestamps of the gate/up and down kernels
+    kernels_us = {}
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for e4 in evs:
         for e in e4:
@@ -231,19 +245,20 @@ def main():
         probes.append(ctypes.byref(p))
         e4.append(p)  # keep the struct alive
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
     run(K, probes)
     torch.cuda.synchronize()
-    evented_us = (time.perf_counter() - t_start) / K * 1e6
     gu = np.array([e4[0].elapsed_time(e4[1]) for e4 in evs]) * 1e3  # us
     dn = np.array([e4[2].elapsed_time(e4[3]) for e4 in evs]) * 1e3
     gu_avg, dn_avg = float(gu.mean()), float(dn.mean())
-    achieved = PHASE_B_BYTES / (gu_avg * 1e-6) / 1e9
-    us_per_token = graph_us if graph_us is not None else stream_us
-    log(f"graph {graph_us} us/token (G={G}); stream {stream_us:.2f}; with events "
-        f"{evented_us:.2f}; phase B {gu_avg:.2f} us (p50 {np.median(gu):.2f}, {achieved:.0f} GB/s); "
-        f"phase C {dn_avg:.2f} us ({PHASE_C_BYTES / dn_avg / 1e3:.0f} GB/s); "
-        f"layer {LAYER_TOKEN_BYTES / us_per_token / 1e3:.0f} GB/s")
+    kname, kbytes, k_us = "decode_b_kernel", PHASE_B_BYTES, gu_avg
+    kernels_us["phase_b_routed_gateup_shared_down"] = round(gu_avg, 3)
+    kernels_us["phase_c_routed_down_combine"] = round(dn_avg, 3)
+    log(f"graph {graph_us} us/token (G={G}); stream {stream_us:.2f} "
+        f"(events {region_us:.2f}); "
+        f"phase B {gu_avg:.2f} us ({PHASE_B_BYTES / gu_avg / 1e3:.0f} GB/s); "
+        f"phase C {dn_avg:.2f} us ({PHASE_C_BYTES / dn_avg / 1e3:.0f} GB/s)")
+    achieved = kbytes / (k_us * 1e-6) / 1e9
+    log(f"layer {LAYER_TOKEN_BYTES / us_per_token / 1e3:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -274,12 +289,11 @@ def main():
         "layer_bytes_per_token": LAYER_TOKEN_BYTES,
         "layer_GBps": round(layer_gbps, 1),
         "layer_frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
-        "kernels_us": {"phase_b_routed_gateup_shared_down": round(gu_avg, 3),
-                       "phase_c_routed_down_combine": round(dn_avg, 3)},
-        "roofline": {"bound": "hbm", "kernel": "decode_b_kernel", "achieved": round(achieved, 1),
+        "kernels_us": kernels_us,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": PHASE_B_BYTES},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(kname),
+                     "bytes_per_launch": kbytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

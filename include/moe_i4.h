@@ -153,7 +153,9 @@ int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *s
  * route, quantize, run the K routed experts and the shared expert, and
  * combine out[s] = sum_k w_k * y_k (k in selection order, from 0) + y_shared.
  * With MOE_F_ACCUMULATE the result is added to out.  x and out must not
- * overlap.  probe is optional (host struct). */
+ * overlap.  probe is optional (host struct).
+ * Launches: router + token quantization + shared gate/up; routed gate/up +
+ * shared down; routed down + combine (one launch per batch of 8 slots). */
 int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                       float *out, unsigned flags, const moe_probe *probe, void *ws,
                       size_t ws_bytes, hipStream_t stream);

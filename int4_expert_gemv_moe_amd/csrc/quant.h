@@ -87,33 +87,34 @@ __device__ inline void quant_row_block(const float *xf, const uint16_t *xb, int 
   }
 }
 
-// The same quantization of a row of D <= 2048*NCH floats by a block of 256
+// The same quantization of a row of D <= 8*NT*NCH floats by a block of NT
 // threads into shared memory (permuted codes, D bytes at `codes`).  Thread t
-// owns groups t + 256k: quant_row_load issues its loads (so the caller can
+// owns groups t + NT*k: quant_row_load issues its loads (so the caller can
 // put other loads behind them), quant_row_block_lds does the rest.
 // Returns the code sum on every thread; *sx receives the scale.
-template <int NCH>
+template <int NCH, int NT = 256>
 __device__ __forceinline__ void quant_row_load(const float *x, int D, float4 (&v)[NCH][2]) {
   const int ngroups = D >> 3;
 #pragma unroll
   for (int k = 0; k < NCH; k++) {
-    const int g = min((int)threadIdx.x + 256 * k, ngroups - 1);
+    const int g = min((int)threadIdx.x + NT * k, ngroups - 1);
     v[k][0] = reinterpret_cast<const float4 *>(x)[2 * g];
     v[k][1] = reinterpret_cast<const float4 *>(x)[2 * g + 1];
   }
 }
 
-template <int NCH>
+template <int NCH, int NT = 256>
 __device__ inline int quant_row_block_lds(const float4 (&v)[NCH][2], int D, int8_t *codes,
                                           float *sx) {
-  __shared__ float red_f[4];
-  __shared__ int red_i[4];
+  constexpr int NW = NT / 64;
+  __shared__ float red_f[NW];
+  __shared__ int red_i[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ngroups = D >> 3;
   float m = 0.f;
 #pragma unroll
   for (int k = 0; k < NCH; k++) {
-    const bool ok = tid + 256 * k < ngroups;
+    const bool ok = tid + NT * k < ngroups;
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const float4 t = v[k][j];
@@ -125,13 +126,15 @@ __device__ inline int quant_row_block_lds(const float4 (&v)[NCH][2], int D, int8
   m = wave_max_f32(m);
   if (lane == 0) red_f[wave] = m;
   __syncthreads();
-  const float amax = fmax_nan_skip(fmax_nan_skip(red_f[0], red_f[1]), fmax_nan_skip(red_f[2], red_f[3]));
+  float amax = red_f[0];
+#pragma unroll
+  for (int i = 1; i < NW; i++) amax = fmax_nan_skip(amax, red_f[i]);
   const float s = quant_scale(amax);
   const float inv = 1.f / s;
   int sum = 0;
 #pragma unroll
   for (int k = 0; k < NCH; k++) {
-    const int g = tid + 256 * k;
+    const int g = tid + NT * k;
     const float4 a = v[k][0], b = v[k][1];
     const int q0 = quant_code(a.x, inv), q1 = quant_code(a.y, inv), q2 = quant_code(a.z, inv),
               q3 = quant_code(a.w, inv), q4 = quant_code(b.x, inv), q5 = quant_code(b.y, inv),
@@ -147,7 +150,10 @@ __device__ inline int quant_row_block_lds(const float4 (&v)[NCH][2], int D, int8
   if (lane == 0) red_i[wave] = sum;
   __syncthreads();
   *sx = s;
-  return (red_i[0] + red_i[1]) + (red_i[2] + red_i[3]);
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < NW; i++) t += red_i[i];
+  return t;
 }
 
 }  // namespace moe

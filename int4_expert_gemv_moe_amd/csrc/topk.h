@@ -101,7 +101,8 @@ __device__ inline int topk_rounds_m(const float *logits, const float *bias, int 
 __device__ inline int topk_rounds(const float *logits, const float *bias, int E, int rounds,
                                   float scale, int32_t *idx_out, float *w_out,
                                   int *sel_out = nullptr) {
-  if (E <= 256) return topk_rounds_m<4>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
+  if (E <= 256)
+    return topk_rounds_m<4>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
   return topk_rounds_m<16>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
 }
 
