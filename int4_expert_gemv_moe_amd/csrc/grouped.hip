@@ -121,6 +121,34 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
     if (g < G) a.gcount[g] = cnt[g];
     a.goff[g] = off[g];
   }
+  if (!a.tiles) return;
+  // tiles of up to tile_rows pairs, groups in order: the same scan over the
+  // tile counts of the groups
+  __syncthreads();
+  int *toff = fill;  // reuse: the fill counters are no longer needed
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int g = base + lane;
+      int v = (g < G) ? (cnt[g] + a.tile_rows - 1) / a.tile_rows : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        int t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+      }
+      if (g < G) toff[g] = carry + incl - v;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) *a.ntiles = carry;
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const int nt = (cnt[g] + a.tile_rows - 1) / a.tile_rows;
+    for (int t = 0; t < nt; t++) a.tiles[toff[g] + t] = make_int2(g, t * a.tile_rows);
+  }
 }
 
 template <int NCH, bool MASKED, int ROWS>

@@ -116,6 +116,8 @@ size_t carve(const moe_config &c, int S, int which, char *base, Work *w) {
     t.goff = (int32_t *)take((size_t)(c.E + 2) * 4);
     t.pairs = (int32_t *)take(s * P * 4);
     t.stage = (float *)take(s * P * c.D * 4);
+    t.tiles = (int2 *)take((size_t)grouped_mfma_max_tiles(S, P, c.E) * 8);
+    t.ntiles = (int32_t *)take(4);
   }
   if (w) *w = t;
   return off;
@@ -424,10 +426,23 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
   carve(c, S, W_BATCH, (char *)ws, &w);
   MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, true, nullptr, stream));
   MOE_TRY(copy_probe(c, S, probe, w, stream));
-  GroupArgs ga{w.idx, S, c.E, c.K, P, c.n_shared, w.gcount, w.goff, w.pairs};
+  const bool mfma_gu = grouped_mfma_fits(c.D), mfma_dn = grouped_mfma_fits(c.I);
+  const int max_tiles = grouped_mfma_max_tiles(S, P, c.E);
+  GroupArgs ga{w.idx,    S,     c.E,     c.K,      P, c.n_shared, w.gcount, w.goff, w.pairs,
+               (mfma_gu || mfma_dn) ? w.tiles : nullptr, w.ntiles, kGroupedMfmaTile};
   MOE_TRY_HIP(launch_group(ga, stream));
   const ExpertSet rt = to_set(layer->routed, c);
   const ExpertSet sh = c.n_shared ? to_set(layer->shared, c) : rt;
+  GroupedMfmaArgs m{};
+  m.rt = rt;
+  m.sh = sh;
+  m.E = c.E;
+  m.P = P;
+  m.gcount = w.gcount;
+  m.goff = w.goff;
+  m.pairs = w.pairs;
+  m.tiles = w.tiles;
+  m.ntiles = w.ntiles;
   GroupedGateUpArgs g{};
   g.rt = rt;
   g.sh = sh;
@@ -443,7 +458,18 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
   g.sumx = w.sumx;
   g.h = w.h;
   MOE_TRY(record(probe, 0, 0, stream));
-  MOE_TRY_HIP(launch_grouped_gateup(g, stream));
+  if (mfma_gu) {
+    GroupedMfmaArgs mg = m;
+    mg.C = c.D;
+    mg.O = c.I;
+    mg.act = w.xq;
+    mg.ascale = w.sx;
+    mg.asum = w.sumx;
+    mg.out = w.h;
+    MOE_TRY_HIP(launch_grouped_mfma(mg, 0, max_tiles, stream));
+  } else {
+    MOE_TRY_HIP(launch_grouped_gateup(g, stream));
+  }
   MOE_TRY(record(probe, 0, 1, stream));
   RequantArgs rq{w.h, c.I, w.hq, w.sh, w.sumh};
   MOE_TRY_HIP(launch_requant(rq, S * P, stream));
@@ -462,7 +488,18 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
   d.sumh = w.sumh;
   d.stage = w.stage;
   MOE_TRY(record(probe, 1, 0, stream));
-  MOE_TRY_HIP(launch_grouped_down(d, stream));
+  if (mfma_dn) {
+    GroupedMfmaArgs md = m;
+    md.C = c.I;
+    md.O = c.D;
+    md.act = w.hq;
+    md.ascale = w.sh;
+    md.asum = w.sumh;
+    md.out = w.stage;
+    MOE_TRY_HIP(launch_grouped_mfma(md, 1, max_tiles, stream));
+  } else {
+    MOE_TRY_HIP(launch_grouped_down(d, stream));
+  }
   MOE_TRY(record(probe, 1, 1, stream));
   CombineArgs cb{w.stage, w.w, S, c.D, c.K, P, c.n_shared, out, flags};
   MOE_TRY_HIP(launch_combine(cb, stream));

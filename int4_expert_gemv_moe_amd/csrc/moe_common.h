@@ -191,6 +191,8 @@ struct Work {
   int32_t *goff;    // [E+2]
   int32_t *pairs;   // [S*P] (s*P + slot) grouped by expert
   float *stage;     // [S][P][D]
+  int2 *tiles;      // MFMA tiles of the grouped pairs
+  int32_t *ntiles;
 };
 
 }  // namespace moe

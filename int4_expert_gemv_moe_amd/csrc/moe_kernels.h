@@ -87,6 +87,24 @@ struct GroupArgs {
   const int32_t *idx;
   int S, E, K, P, n_shared;
   int32_t *gcount, *goff, *pairs;
+  int2 *tiles;            // optional: (group, first pair) of every tile of tile_rows pairs
+  int32_t *ntiles;        // number of tiles
+  int tile_rows;
+};
+
+// Grouped int8 MFMA GEMM of the union path (grouped_mfma.hip); mode 0 is
+// gate/up + SwiGLU, mode 1 is down.
+struct GroupedMfmaArgs {
+  ExpertSet rt, sh;
+  int E, P;
+  int C, O;               // contraction length and output rows of the matrix
+  const int32_t *gcount, *goff, *pairs;
+  const int2 *tiles;
+  const int32_t *ntiles;
+  const int8_t *act;      // mode 0: xq [S][D]; mode 1: hq [S*P][I] (permuted codes)
+  const float *ascale;    // sx [S] or sh [S*P]
+  const int32_t *asum;    // sumx [S] or sumh [S*P]
+  float *out;             // h [S*P][I] or stage [S*P][D]
 };
 
 struct GroupedGateUpArgs {
@@ -159,6 +177,11 @@ int decode_c_rows_per_pass(int I);
 hipError_t launch_requant(const RequantArgs &a, int rows, hipStream_t st);
 hipError_t launch_group(const GroupArgs &a, hipStream_t st);
 hipError_t launch_grouped_gateup(const GroupedGateUpArgs &a, hipStream_t st);
+// The MFMA form applies when the contraction length is a multiple of 256.
+bool grouped_mfma_fits(int C);
+constexpr int kGroupedMfmaTile = 64;  // pairs per tile
+int grouped_mfma_max_tiles(int S, int P, int E);
+hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, hipStream_t st);
 hipError_t launch_grouped_down(const GroupedDownArgs &a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_pack(const PackArgs &a, hipStream_t st);
