@@ -6,10 +6,12 @@
 // results are the same integers, and the same floats, as the GEMV kernels of
 // grouped.hip.
 //
-// Work unit: a tile of up to 64 (token, slot) pairs of one expert group (the
-// tile list is built by group_kernel) times 64 (gate/up) or 128 (down) output
-// rows.  A workgroup has 4 waves; wave w owns 16 gate rows and the 16 up rows
-// with the same indices (gate/up), or 32 down rows, for all 64 pairs.
+// Work unit: a tile of up to 128 (token, slot) pairs of one expert group (the
+// tile list is built by group_kernel; a routed expert of a 2048-token prefill
+// gets about 64 pairs, so its weights are read once) times 64 (gate/up) or
+// 128 (down) output rows.  A workgroup has 4 waves; wave w owns 16 gate rows
+// and the 16 up rows with the same indices (gate/up), or 32 down rows, for
+// all pairs of the tile.
 //
 // v_mfma_i32_16x16x64_i8 (layout checked on the device): lane l supplies row
 // l % 16 of A (a pair) and column l % 16 of B (an output row), each 16 int8
@@ -30,7 +32,7 @@ namespace moe {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kMT = 64;         // pairs per tile
+constexpr int kMT = kGroupedMfmaTile;  // pairs per tile (128)
 constexpr int kKS = 256;        // columns per pipeline step
 constexpr int kAStride = 272;   // LDS bytes per pair row (256 + 16: no bank conflicts)
 
@@ -47,89 +49,64 @@ __device__ __forceinline__ v4i unpack16(uint32_t w0, uint32_t w1) {
 
 // MODE 0: gate/up (A = token codes xq[s], B = gate and up rows, epilogue
 // h = silu(g) * u into h[pair]); MODE 1: down (A = hidden codes hq[pair],
-// B = down rows, epilogue y into stage[pair]).
-template <int MODE>
-__global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
-  constexpr int NS = 2;                    // B subtiles of 16 rows per wave
-  constexpr int ROWS_PER_BLOCK = MODE == 0 ? 64 : 128;
-  __shared__ __align__(16) int8_t As[2][kMT * kAStride];
-  __shared__ int pr_l[kMT];
-  const int tile = blockIdx.y;
-  if (tile >= *a.ntiles) return;
-  const int2 tg = a.tiles[tile];
-  const int g = tg.x, m0 = tg.y;
-  const int n = a.gcount[g];
-  const int rows = min(kMT, n - m0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool shared = (g == a.E);
-  const int e = shared ? 0 : g;
-  const int C = a.C;                       // contraction length
-  const int O = a.O;                       // output rows of the matrix
-  const int rowbytes = C >> 1;
-  const int o_blk = blockIdx.x * ROWS_PER_BLOCK;
+// B = down rows, epilogue y into stage[pair]).  MSV: 16-pair subtiles the
+// tile needs (2, 4 or 8); only those rows are loaded and multiplied.
+struct MfmaTile {
+  int rows;          // pairs of the tile
+  int j, lane, wave;
+  RowPtr Bm[2];
+  int ob[2];         // output rows of the lane's two B subtiles
+  const uint8_t *bp[2];
+};
 
-  // B rows of this lane: subtile ns covers 16 rows
-  RowPtr Bm[NS];
-  int ob[NS];
-  if (MODE == 0) {
-    Bm[0] = pick(a.rt.gate, a.sh.gate, shared, e);
-    Bm[1] = pick(a.rt.up, a.sh.up, shared, e);
-    ob[0] = ob[1] = o_blk + 16 * wave + (lane & 15);
-  } else {
-    Bm[0] = pick(a.rt.down, a.sh.down, shared, e);
-    Bm[1] = Bm[0];
-    ob[0] = o_blk + 32 * wave + (lane & 15);
-    ob[1] = ob[0] + 16;
-  }
-  const int j = lane >> 4;  // lane group: columns 64j .. 64j + 64 of a step
-  const uint8_t *bp[NS];
-#pragma unroll
-  for (int s = 0; s < NS; s++) {
-    const int oc = min(ob[s], O - 1);
-    bp[s] = Bm[s].q + (int64_t)oc * rowbytes + 32 * j;
-  }
-
-  // pair list of the tile
-  const int *plist = a.pairs + a.goff[g] + m0;
-  if (threadIdx.x < kMT) pr_l[threadIdx.x] = plist[min((int)threadIdx.x, rows - 1)];
-  __syncthreads();
-
-  // A loads: thread t copies 64 bytes (4 x 16) of pair row t / 4, piece t % 4
-  const int ar = threadIdx.x >> 2, aq = threadIdx.x & 3;
+template <int MODE, int MSV>
+__device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTile &t,
+                                          int8_t (*As)[kMT * kAStride], const int *pr_l,
+                                          const int *sum_l, const float *scl_l) {
+  constexpr int NS = 2;
+  constexpr int TPR = 16 / MSV;       // threads per pair row of a step
+  constexpr int PIECE = 16 * MSV;     // bytes per thread per step
+  const int C = a.C, O = a.O;
+  const int lane = t.lane, j = t.j, rows = t.rows;
+  // A loads: thread copies PIECE bytes of pair row tid / TPR
+  const int ar = threadIdx.x / TPR, aq = threadIdx.x % TPR;
   const int apr = pr_l[min(ar, rows - 1)];
   const int8_t *arow = (MODE == 0 ? a.act + (int64_t)(apr / a.P) * C : a.act + (int64_t)apr * C) +
-                       64 * aq;
+                       PIECE * aq;
   const bool alive = ar < rows;
-  uint4 av[4];
+  uint4 av[MSV];
   auto load_a = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) av[i] = *reinterpret_cast<const uint4 *>(arow + k0 + 16 * i);
+    for (int i = 0; i < MSV; i++) av[i] = *reinterpret_cast<const uint4 *>(arow + k0 + 16 * i);
   };
   auto store_a = [&](int buf) {
-    int8_t *dst = &As[buf][ar * kAStride + 64 * aq];
+    int8_t *dst = &As[buf][ar * kAStride + PIECE * aq];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < MSV; i++)
       *reinterpret_cast<uint4 *>(dst + 16 * i) = alive ? av[i] : make_uint4(0u, 0u, 0u, 0u);
   };
-  uint4 bcur[NS][2], bnext[NS][2];
+  uint4 bcur[NS][2], bnext[NS][2], bnext2[NS][2];
   auto load_b = [&](int k0, uint4 (&bv)[NS][2]) {
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-      bv[s][0] = ldnt16(bp[s] + k0 / 2, true, bp[s]);
-      bv[s][1] = ldnt16(bp[s] + k0 / 2 + 16, true, bp[s]);
+      bv[s][0] = ldnt16(t.bp[s] + k0 / 2, true, t.bp[s]);
+      bv[s][1] = ldnt16(t.bp[s] + k0 / 2 + 16, true, t.bp[s]);
     }
   };
-
-  v4i acc[4][NS];
+  v4i acc[MSV][NS];
 #pragma unroll
-  for (int ms = 0; ms < 4; ms++)
+  for (int ms = 0; ms < MSV; ms++)
 #pragma unroll
     for (int s = 0; s < NS; s++) acc[ms][s] = v4i{0, 0, 0, 0};
-  const int msa = (rows + 15) >> 4;  // active 16-pair subtiles (uniform)
+  float sc[NS];  // row scales of the lane's output rows
+#pragma unroll
+  for (int s = 0; s < NS; s++) sc[s] = t.Bm[s].s[min(t.ob[s], O - 1)];
   const int nsteps = C / kKS;
 
+  // weights run two steps ahead (HBM), activations one step (L2)
   load_a(0);
   load_b(0, bcur);
+  load_b(min(1, nsteps - 1) * kKS, bnext);
   store_a(0);
   __syncthreads();
   for (int step = 0; step < nsteps; step++) {
@@ -137,7 +114,9 @@ __global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
     const bool more = step + 1 < nsteps;
     const int kn = more ? (step + 1) * kKS : step * kKS;
     load_a(kn);
-    load_b(kn, bnext);
+    load_b(min(step + 2, nsteps - 1) * kKS, bnext2);
+    // per 64-column slice c: the operands first (one wait for shared
+    // memory), then the MFMAs
     const int8_t *abase = &As[buf][(lane & 15) * kAStride + 64 * j];
 #pragma unroll
     for (int c = 0; c < 4; c++) {
@@ -147,16 +126,17 @@ __global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
         const uint4 w = bcur[s][c >> 1];
         bb[s] = (c & 1) ? unpack16(w.z, w.w) : unpack16(w.x, w.y);
       }
+      v4i aa[MSV];
 #pragma unroll
-      for (int ms = 0; ms < 4; ms++) {
-        if (ms < msa) {
-          const uint4 av4 = *reinterpret_cast<const uint4 *>(abase + ms * 16 * kAStride + 16 * c);
-          const v4i aa = v4i{(int)av4.x, (int)av4.y, (int)av4.z, (int)av4.w};
-#pragma unroll
-          for (int s = 0; s < NS; s++)
-            acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa, bb[s], acc[ms][s], 0, 0, 0);
-        }
+      for (int ms = 0; ms < MSV; ms++) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(abase + ms * 16 * kAStride + 16 * c);
+        aa[ms] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
       }
+#pragma unroll
+      for (int ms = 0; ms < MSV; ms++)
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+          acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[s], acc[ms][s], 0, 0, 0);
     }
     if (more) store_a(buf ^ 1);
     __syncthreads();
@@ -164,42 +144,91 @@ __global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
     for (int s = 0; s < NS; s++) {
       bcur[s][0] = bnext[s][0];
       bcur[s][1] = bnext[s][1];
+      bnext[s][0] = bnext2[s][0];
+      bnext[s][1] = bnext2[s][1];
     }
   }
 
   // epilogue: lane holds output row ob[s] for pairs 16 ms + 4 j + i
-  float sc[NS];
 #pragma unroll
-  for (int s = 0; s < NS; s++) sc[s] = Bm[s].s[min(ob[s], O - 1)];
-#pragma unroll
-  for (int ms = 0; ms < 4; ms++) {
+  for (int ms = 0; ms < MSV; ms++) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int r = 16 * ms + 4 * j + i;
-      if (ms < msa && r < rows) {
+      if (r < rows) {
         const int pr = pr_l[r];
+        const int corr = 8 * sum_l[r];
+        const float as = scl_l[r];
         if (MODE == 0) {
-          const int s = pr / a.P;
-          const int o = ob[0];
+          const int o = t.ob[0];
           if (o < O) {
-            const int corr = 8 * a.asum[s];
-            const float sx = a.ascale[s];
-            const float gv = ((float)(acc[ms][0][i] - corr) * sc[0]) * sx;
-            const float uv = ((float)(acc[ms][1][i] - corr) * sc[1]) * sx;
+            const float gv = ((float)(acc[ms][0][i] - corr) * sc[0]) * as;
+            const float uv = ((float)(acc[ms][1][i] - corr) * sc[1]) * as;
             a.out[(int64_t)pr * O + o] = silu(gv) * uv;
           }
         } else {
-          const int corr = 8 * a.asum[pr];
-          const float shs = a.ascale[pr];
 #pragma unroll
           for (int s = 0; s < NS; s++) {
-            const int o = ob[s];
-            if (o < O) a.out[(int64_t)pr * O + o] = ((float)(acc[ms][s][i] - corr) * sc[s]) * shs;
+            const int o = t.ob[s];
+            if (o < O) a.out[(int64_t)pr * O + o] = ((float)(acc[ms][s][i] - corr) * sc[s]) * as;
           }
         }
       }
     }
   }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
+  constexpr int ROWS_PER_BLOCK = MODE == 0 ? 64 : 128;
+  __shared__ __align__(16) int8_t As[2][kMT * kAStride];
+  __shared__ int pr_l[kMT];
+  __shared__ int sum_l[kMT];    // code sum of each pair's activation row
+  __shared__ float scl_l[kMT];  // scale of each pair's activation row
+  const int tile = blockIdx.y;
+  if (tile >= *a.ntiles) return;
+  const int2 tg = a.tiles[tile];
+  const int g = tg.x, m0 = tg.y;
+  MfmaTile t;
+  t.rows = min(kMT, a.gcount[g] - m0);
+  t.lane = threadIdx.x & 63;
+  t.wave = threadIdx.x >> 6;
+  t.j = t.lane >> 4;  // lane group: columns 64j .. 64j + 64 of a step
+  const bool shared = (g == a.E);
+  const int e = shared ? 0 : g;
+  const int o_blk = blockIdx.x * ROWS_PER_BLOCK;
+  if (MODE == 0) {
+    t.Bm[0] = pick(a.rt.gate, a.sh.gate, shared, e);
+    t.Bm[1] = pick(a.rt.up, a.sh.up, shared, e);
+    t.ob[0] = t.ob[1] = o_blk + 16 * t.wave + (t.lane & 15);
+  } else {
+    t.Bm[0] = pick(a.rt.down, a.sh.down, shared, e);
+    t.Bm[1] = t.Bm[0];
+    t.ob[0] = o_blk + 32 * t.wave + (t.lane & 15);
+    t.ob[1] = t.ob[0] + 16;
+  }
+  const int rowbytes = a.C >> 1;
+#pragma unroll
+  for (int s = 0; s < 2; s++)
+    t.bp[s] = t.Bm[s].q + (int64_t)min(t.ob[s], a.O - 1) * rowbytes + 32 * t.j;
+
+  // pair list of the tile and the scale and code sum of each pair's row
+  const int *plist = a.pairs + a.goff[g] + m0;
+  if (threadIdx.x < kMT) {
+    const int pr = plist[min((int)threadIdx.x, t.rows - 1)];
+    const int ar = MODE == 0 ? pr / a.P : pr;  // activation row
+    pr_l[threadIdx.x] = pr;
+    sum_l[threadIdx.x] = a.asum[ar];
+    scl_l[threadIdx.x] = a.ascale[ar];
+  }
+  __syncthreads();
+  const int msa = (t.rows + 15) >> 4;  // uniform across the block
+  if (msa <= 2)
+    mfma_tile<MODE, 2>(a, t, As, pr_l, sum_l, scl_l);
+  else if (msa <= 4)
+    mfma_tile<MODE, 4>(a, t, As, pr_l, sum_l, scl_l);
+  else
+    mfma_tile<MODE, 8>(a, t, As, pr_l, sum_l, scl_l);
 }
 
 bool grouped_mfma_fits(int C) { return C % kKS == 0; }
