@@ -223,25 +223,3 @@ def fit_zipf_exponent(counts: np.ndarray) -> float:
     A = np.stack([np.log(r), np.ones_like(r)], axis=1)
     slope = np.linalg.lstsq(A, np.log(c), rcond=None)[0][0]
     return float(-slope)
-
-
-def calibrate_stack_beta(seed: int, E: int = 256, K: int = 8, s: float = 1.1,
-                         logit_sd: float = 0.02 * math.sqrt(6144), tokens: int = 4096) -> float:
-    """Pick the bias strength beta of the layer stack so that top-K selections
-    over c = sigmoid(l) + beta*(log p - mean), with l ~ N(0, logit_sd^2) drawn
-    independently per token, have a rank-frequency slope close to -s.
-    Generator-side calibration on synthetic logits; it does not use the code
-    under test."""
-    p = zipf_probs(seed, E, s, layer=0)
-    lp = np.log(p) - np.log(p).mean()
-    rng_l = host_normal(seed, stream(K_Z, 0xFFF0), tokens * E, logit_sd).reshape(tokens, E)
-    sig = 1.0 / (1.0 + np.exp(-rng_l.astype(np.float64)))
-    best, best_err = 0.0, float("inf")
-    for beta in np.linspace(0.0, 0.5, 101):
-        c = sig + beta * lp[None, :]
-        top = np.argpartition(-c, K - 1, axis=1)[:, :K]
-        counts = np.bincount(top.ravel(), minlength=E)
-        err = abs(fit_zipf_exponent(counts) - s)
-        if err < best_err:
-            best, best_err = float(beta), err
-    return best
