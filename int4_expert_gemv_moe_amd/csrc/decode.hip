@@ -519,6 +519,9 @@ template <int NCH, bool MASKED>
 __global__ __launch_bounds__(64 * kCWaves) void decode_c_kernel(DecodeArgs a) {
   constexpr int RB = CRows<NCH>::value;
   __shared__ float ys[kCWaves][RB];
+  // lane partial sums of the wave's rows, summed across lanes by lane r
+  // (one read of 64 values instead of a reduction tree per row)
+  __shared__ __align__(16) int part[kCWaves][RB][64];
   const int s = blockIdx.y, db = blockIdx.x;
   const int lane = threadIdx.x & 63, p = threadIdx.x >> 6;
   const int np = a.p_hi - a.p_lo;
@@ -561,16 +564,25 @@ __global__ __launch_bounds__(64 * kCWaves) void decode_c_kernel(DecodeArgs a) {
   float *out = last ? a.out + (int64_t)s * a.D : a.tmp + (int64_t)s * a.D;
   const bool accumulate = last && (a.flags & MOE_F_ACCUMULATE);
   for (;;) {
-    int mine = 0;
 #pragma unroll
     for (int r = 0; r < RB; r++) {
       int acc = 0;
 #pragma unroll
       for (int c = 0; c < NCH; c++) acc = dot32_i4(w[r][c], xv[c][0], xv[c][1], acc);
-      acc = wave_sum_i32(acc);
-      mine = (lane == r) ? acc : mine;
+      part[p][r][lane] = acc;
     }
-    if (lane < RB) ys[p][lane] = ((float)(mine - corr) * dsc) * sh;
+    // shared memory is in order within a wave: lane r reads its row's 64
+    // partial sums after the wave's writes
+    int mine = 0;
+    if (lane < RB) {
+      const int4 *pr = reinterpret_cast<const int4 *>(part[p][lane]);
+      int4 t[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) t[i] = pr[i];
+#pragma unroll
+      for (int i = 0; i < 16; i++) mine += (t[i].x + t[i].y) + (t[i].z + t[i].w);
+      ys[p][lane] = ((float)(mine - corr) * dsc) * sh;
+    }
     __syncthreads();
     const int d = base + threadIdx.x;
     if (threadIdx.x < RB && d < d1) {
