@@ -156,6 +156,47 @@ def bench_prefill(layer, iters: int = 5):
             "roofline_us": round(ideal_us, 1), "frac_of_roofline": round(ideal_us / us, 4)}
 
 
+def bench_verify(layer, iters: int = 20):
+    """Batched verify of 64 tokens through one GLM-shape layer on the
+    unique-expert union path, routing skewed so that expert popularity is
+    Zipf(1.1): the token rows are solved so that the router gives
+    log p_e + Gumbel noise (router bias 0)."""
+    import numpy as np
+    import torch
+
+    import int4_expert_gemv_moe_amd as moe
+    import synth
+
+    S = 64
+    wr = synth.router_w(0, synth.GLM)
+    x_np, _, _ = synth.zipf_activations(0, synth.GLM, S, wr)
+    zl = moe.DeviceLayer(layer.cfg, torch.from_numpy(wr).cuda(),
+                         torch.zeros(E, dtype=torch.float32, device="cuda"), layer.routed,
+                         layer.shared)
+    x = torch.from_numpy(x_np).cuda()
+    ws = moe.Workspace(zl.cfg, S, moe.WS_BATCH)
+    idx = torch.empty(S, K, dtype=torch.int32, device="cuda")
+    out = moe.moe_layer_forward_batch(zl, x, ws, topk_idx=idx)
+    torch.cuda.synchronize()
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
+    used = int((counts > 0).sum()) + 1  # + the shared expert
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        moe.moe_layer_forward_batch(zl, x, ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    nbytes = used * EXPERT_BYTES + ROUTER_BYTES + 2 * S * D * 4
+    log(f"verify 64 (Zipf): {us:.1f} us, union {used - 1} routed experts")
+    return {"workload": "GLM-shape layer, 64-token batched verify, Zipf(1.1) expert popularity, "
+                        "unique-expert union",
+            "us": round(us, 1), "us_per_token": round(us / S, 2),
+            "union_routed_experts": used - 1, "hottest_expert_tokens": int(counts.max()),
+            "hbm_bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+            "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+
+
 def bench_stack(steps: int = 64):
     """48 GLM-shape layers resident in HBM (per-layer Zipf-skewed routing,
     RMSNorm + residual between layers): decode steps of 1 token (per-token
@@ -368,10 +409,11 @@ def main():
     secondary = None
     if not args.no_secondary:
         secondary = {}
-        try:
-            secondary["prefill_2048"] = bench_prefill(layers[0])
-        except Exception as exc:  # reported, the headline line is still printed
-            secondary["prefill_2048"] = {"error": f"{type(exc).__name__}: {exc}"}
+        for key, fn in (("verify_64_zipf", bench_verify), ("prefill_2048", bench_prefill)):
+            try:
+                secondary[key] = fn(layers[0])
+            except Exception as exc:  # reported, the headline line is still printed
+                secondary[key] = {"error": f"{type(exc).__name__}: {exc}"}
         del layers, lstructs, lrefs, ws
         gc.collect()
         torch.cuda.synchronize()

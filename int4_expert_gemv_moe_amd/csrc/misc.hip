@@ -35,26 +35,57 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 }
 
 // One block per row: mean of squares in double, r = 1/sqrtf(ms + eps),
-// y = x * r * gamma.
+// y = x * r * gamma.  With a.vec (D <= 8192, D % 4 == 0, 16-byte aligned
+// rows) each row is read once, all of a thread's loads issued together (the
+// row is then in registers); otherwise the plain loop.
+__device__ __forceinline__ double block_sum_f64(double v, double *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(RmsArgs a) {
   __shared__ double red[4];
-  __shared__ float rshared;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const float *x = a.x + (int64_t)blockIdx.x * a.D;
   float *y = a.y + (int64_t)blockIdx.x * a.D;
+  if (a.vec) {
+    const int n4 = a.D / 4;
+    float4 xv[8], gv[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int i = min(tid + 256 * k, n4 - 1);
+      xv[k] = reinterpret_cast<const float4 *>(x)[i];
+      gv[k] = reinterpret_cast<const float4 *>(a.gamma)[i];
+    }
+    double ms = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      if (tid + 256 * k < n4) {
+        ms += (double)xv[k].x * (double)xv[k].x;
+        ms += (double)xv[k].y * (double)xv[k].y;
+        ms += (double)xv[k].z * (double)xv[k].z;
+        ms += (double)xv[k].w * (double)xv[k].w;
+      }
+    }
+    const double t = block_sum_f64(ms, red);
+    const float r = 1.f / sqrtf((float)(t / a.D) + a.eps);
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int i = tid + 256 * k;
+      if (i < n4)
+        reinterpret_cast<float4 *>(y)[i] = make_float4(xv[k].x * r * gv[k].x, xv[k].y * r * gv[k].y,
+                                                        xv[k].z * r * gv[k].z, xv[k].w * r * gv[k].w);
+    }
+    return;
+  }
   double ms = 0.0;
   for (int i = tid; i < a.D; i += blockDim.x) ms += (double)x[i] * (double)x[i];
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) ms += __shfl_xor(ms, d, 64);
-  if (lane == 0) red[wave] = ms;
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int i = 0; i < (int)(blockDim.x >> 6); i++) t += red[i];
-    rshared = 1.f / sqrtf((float)(t / a.D) + a.eps);
-  }
-  __syncthreads();
-  const float r = rshared;
+  const double t = block_sum_f64(ms, red);
+  const float r = 1.f / sqrtf((float)(t / a.D) + a.eps);
   for (int i = tid; i < a.D; i += blockDim.x) y[i] = x[i] * r * a.gamma[i];
 }
 

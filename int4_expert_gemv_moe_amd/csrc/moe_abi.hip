@@ -512,7 +512,8 @@ int moe_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, flo
   if (S < 1 || D < 1) return MOE_ESHAPE;
   if (((uintptr_t)x & 3u) || ((uintptr_t)gamma & 3u) || ((uintptr_t)y & 3u)) return MOE_EALIGN;
   MOE_TRY(check_device());
-  RmsArgs a{x, gamma, D, eps, y};
+  const int vec = (D % 4 == 0 && D <= 8192 && aligned16(x) && aligned16(gamma) && aligned16(y));
+  RmsArgs a{x, gamma, D, eps, y, vec};
   return hip_rc(launch_rmsnorm(a, S, stream));
 }
 

@@ -155,6 +155,7 @@ struct RmsArgs {
   int D;
   float eps;
   float *y;
+  int vec;  // float4 path: D <= 8192, D % 4 == 0, all three 16-byte aligned
 };
 
 // Host launchers, each defined next to its kernels.  They return the launch

@@ -140,13 +140,14 @@ hipError_t launch_quant(const QuantArgs &a, int S, hipStream_t st) {
 
 hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
   const int ne4 = (a.E + 3) / 4;
-  const int ts = a.S == 1 ? 1 : (a.S <= 4 ? 4 : 8);
+  // a few tokens: one token per wave, the whole weight row in one batch of
+  // loads (rows are re-read per token from L2); many tokens: 8 tokens share
+  // each weight load
+  const int ts = a.S <= 8 ? 1 : 8;
   const int n_router = ne4 * ((a.S + ts - 1) / ts);
   const dim3 grid(n_router + (with_quant ? a.S : 0));
   if (ts == 1)
     hipLaunchKernelGGL((router_kernel<1, 24>), grid, dim3(256), 0, st, a);
-  else if (ts == 4)
-    hipLaunchKernelGGL((router_kernel<4, 6>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((router_kernel<8, 4>), grid, dim3(256), 0, st, a);
   return hipGetLastError();

@@ -141,3 +141,23 @@ def test_expert_swiglu_parity(shape, S):
         qd = unpack64(he.down_q4, shape.I).astype(np.int64)
         assert np.array_equal(acc_d[~same], hq[~same].astype(np.int64) @ qd.T)
     assert_close_rows(to_np(r["y"]), ref["y"], what="expert y")
+
+
+@pytest.mark.parametrize("S,D,offset", [(1, 6144, 0), (4, 6144, 0), (3, 1000, 0), (2, 256, 1),
+                                        (1, 9000, 0)])
+def test_rmsnorm_matches_oracle(S, D, offset):
+    """Section 04 RMSNorm against the oracle's (mean of squares in double),
+    on the vector path (aligned rows) and the plain one (offset rows, odd D,
+    D > 8192), with a non-unit gain."""
+    x = synth.activations(30, S, D) * 3.0
+    g = (1.0 + 0.5 * synth.activations(31, 1, D)[0]).astype(np.float32)
+    ref = oracle.rmsnorm(x, g, 1e-5)
+    xb = torch.zeros(S * D + offset, dtype=torch.float32, device="cuda")
+    xb[offset:] = torch.from_numpy(x.ravel()).cuda()
+    xt = xb[offset:].view(S, D)
+    yb = torch.zeros(S * D + offset, dtype=torch.float32, device="cuda")
+    yt = yb[offset:].view(S, D)
+    gt = torch.from_numpy(g).cuda()
+    moe.moe_rmsnorm(xt, gt, 1e-5, out=yt)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(yt), ref, rtol=2e-6, atol=1e-6)
