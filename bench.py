@@ -261,7 +261,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the prefill (2048 tokens) and 48-layer stack measurements")
+                    help="skip the verify, prefill and 48-layer stack measurements")
+    ap.add_argument("--only", choices=["verify", "prefill", "stack"],
+                    help="run only that secondary measurement and print its record (for profiling)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay pass (value then comes from the stream pass); "
                          "used for counter runs")
@@ -294,6 +296,14 @@ def main():
         log(f"copied {COPY_CAL_BYTES} bytes 8 times")
         return
     lib = moe.lib()
+    if args.only:
+        if args.only == "stack":
+            rec = bench_stack()
+        else:
+            layer = build_device_layer(0, synth.GLM, 0, synth.router_b_uniform(0, synth.GLM, 0))
+            rec = (bench_verify if args.only == "verify" else bench_prefill)(layer)
+        print(json.dumps(rec), flush=True)
+        return
     t0 = time.time()
     layers = []
     for r in range(args.replicas):
