@@ -50,7 +50,7 @@ __device__ __forceinline__ v4i unpack16(uint32_t w0, uint32_t w1) {
 // MODE 0: gate/up (A = token codes xq[s], B = gate and up rows, epilogue
 // h = silu(g) * u into h[pair]); MODE 1: down (A = hidden codes hq[pair],
 // B = down rows, epilogue y into stage[pair]).  MSV: 16-pair subtiles the
-// tile needs (2, 4 or 8); only those rows are loaded and multiplied.
+// tile needs (1 to 8); only those rows are loaded and multiplied.
 struct MfmaTile {
   int rows;          // pairs of the tile
   int j, lane, wave;
@@ -64,26 +64,27 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
                                           int8_t (*As)[kMT * kAStride], const int *pr_l,
                                           const int *sum_l, const float *scl_l) {
   constexpr int NS = 2;
-  constexpr int TPR = 16 / MSV;       // threads per pair row of a step
-  constexpr int PIECE = 16 * MSV;     // bytes per thread per step
   const int C = a.C, O = a.O;
   const int lane = t.lane, j = t.j, rows = t.rows;
-  // A loads: thread copies PIECE bytes of pair row tid / TPR
-  const int ar = threadIdx.x / TPR, aq = threadIdx.x % TPR;
-  const int apr = pr_l[min(ar, rows - 1)];
-  const int8_t *arow = (MODE == 0 ? a.act + (int64_t)(apr / a.P) * C : a.act + (int64_t)apr * C) +
-                       PIECE * aq;
-  const bool alive = ar < rows;
-  uint4 av[MSV];
-  auto load_a = [&](int k0) {
+  // A loads: per step, load i of a thread copies 16 bytes (column piece
+  // tid % 16) of pair row 16 i + tid / 16; rows past the tile are zero
+  const int ar = threadIdx.x >> 4, aq = threadIdx.x & 15;
+  const int8_t *arow[MSV];
 #pragma unroll
-    for (int i = 0; i < MSV; i++) av[i] = *reinterpret_cast<const uint4 *>(arow + k0 + 16 * i);
+  for (int i = 0; i < MSV; i++) {
+    const int apr = pr_l[min(16 * i + ar, rows - 1)];
+    arow[i] = (MODE == 0 ? a.act + (int64_t)(apr / a.P) * C : a.act + (int64_t)apr * C) + 16 * aq;
+  }
+  uint4 av[MSV], avn[MSV];
+  auto load_a = [&](int k0, uint4 (&v)[MSV]) {
+#pragma unroll
+    for (int i = 0; i < MSV; i++) v[i] = *reinterpret_cast<const uint4 *>(arow[i] + k0);
   };
-  auto store_a = [&](int buf) {
-    int8_t *dst = &As[buf][ar * kAStride + PIECE * aq];
+  auto store_a = [&](int buf, const uint4 (&v)[MSV]) {
 #pragma unroll
     for (int i = 0; i < MSV; i++)
-      *reinterpret_cast<uint4 *>(dst + 16 * i) = alive ? av[i] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(&As[buf][(16 * i + ar) * kAStride + 16 * aq]) =
+          (16 * i + ar < rows) ? v[i] : make_uint4(0u, 0u, 0u, 0u);
   };
   uint4 bcur[NS][2], bnext[NS][2], bnext2[NS][2];
   auto load_b = [&](int k0, uint4 (&bv)[NS][2]) {
@@ -103,17 +104,19 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   for (int s = 0; s < NS; s++) sc[s] = t.Bm[s].s[min(t.ob[s], O - 1)];
   const int nsteps = C / kKS;
 
-  // weights run two steps ahead (HBM), activations one step (L2)
-  load_a(0);
+  // weights and activations both run two steps ahead: the activation rows
+  // of step s + 1 wait in registers during step s and go to shared memory at
+  // its end
+  load_a(0, avn);
   load_b(0, bcur);
+  load_a(min(1, nsteps - 1) * kKS, av);
   load_b(min(1, nsteps - 1) * kKS, bnext);
-  store_a(0);
+  store_a(0, avn);
   __syncthreads();
   for (int step = 0; step < nsteps; step++) {
     const int buf = step & 1;
     const bool more = step + 1 < nsteps;
-    const int kn = more ? (step + 1) * kKS : step * kKS;
-    load_a(kn);
+    load_a(min(step + 2, nsteps - 1) * kKS, avn);
     load_b(min(step + 2, nsteps - 1) * kKS, bnext2);
     // per 64-column slice c: the operands first (one wait for shared
     // memory), then the MFMAs
@@ -138,8 +141,10 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
         for (int s = 0; s < NS; s++)
           acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[s], acc[ms][s], 0, 0, 0);
     }
-    if (more) store_a(buf ^ 1);
+    if (more) store_a(buf ^ 1, av);
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MSV; i++) av[i] = avn[i];
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       bcur[s][0] = bnext[s][0];
@@ -222,13 +227,16 @@ __global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
     scl_l[threadIdx.x] = a.ascale[ar];
   }
   __syncthreads();
-  const int msa = (t.rows + 15) >> 4;  // uniform across the block
-  if (msa <= 2)
-    mfma_tile<MODE, 2>(a, t, As, pr_l, sum_l, scl_l);
-  else if (msa <= 4)
-    mfma_tile<MODE, 4>(a, t, As, pr_l, sum_l, scl_l);
-  else
-    mfma_tile<MODE, 8>(a, t, As, pr_l, sum_l, scl_l);
+  switch ((t.rows + 15) >> 4) {  // 16-pair subtiles in use, uniform across the block
+    case 1: mfma_tile<MODE, 1>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 2: mfma_tile<MODE, 2>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 3: mfma_tile<MODE, 3>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 4: mfma_tile<MODE, 4>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 5: mfma_tile<MODE, 5>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 6: mfma_tile<MODE, 6>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 7: mfma_tile<MODE, 7>(a, t, As, pr_l, sum_l, scl_l); break;
+    default: mfma_tile<MODE, 8>(a, t, As, pr_l, sum_l, scl_l); break;
+  }
 }
 
 bool grouped_mfma_fits(int C) { return C % kKS == 0; }

@@ -129,6 +129,80 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   }
 }
 
+// Many tokens: a register tile per wave, TT tokens x EE experts, so each
+// loaded x vector serves EE experts and each weight vector TT tokens.  Block
+// = 4 waves over 4 * EE consecutive experts of one token tile.  Every logit
+// is still lane p's ascending FMA chain over k = 4p + 256j + q followed by
+// wave_sum_f32, i.e. the same bits as router_kernel.  The operands of step
+// j + 1 are loaded while step j is multiplied.
+template <int TT, int EE>
+__global__ __launch_bounds__(256) void router_tile_kernel(RouterArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int neb = (a.E + 4 * EE - 1) / (4 * EE);
+  const int n_router = neb * ((a.S + TT - 1) / TT);
+  if ((int)blockIdx.x >= n_router) {
+    const int s = blockIdx.x - n_router;
+    if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
+    quant_row_block(a.x + (int64_t)s * a.D, nullptr, a.D, a.xq_perm + (int64_t)s * a.D, nullptr,
+                    a.sx + s, a.sumx + s);
+    return;
+  }
+  const int e0 = (blockIdx.x % neb) * 4 * EE + wave * EE;
+  const int s0 = (blockIdx.x / neb) * TT;
+  if (e0 >= a.E) return;
+  const float4 *xr[TT], *wr[EE];
+#pragma unroll
+  for (int t = 0; t < TT; t++)
+    xr[t] = reinterpret_cast<const float4 *>(a.x + (int64_t)min(s0 + t, a.S - 1) * a.D) + lane;
+#pragma unroll
+  for (int e = 0; e < EE; e++)
+    wr[e] = reinterpret_cast<const float4 *>(a.W + (int64_t)min(e0 + e, a.E - 1) * a.D) + lane;
+  float acc[TT][EE];
+#pragma unroll
+  for (int t = 0; t < TT; t++)
+#pragma unroll
+    for (int e = 0; e < EE; e++) acc[t][e] = 0.f;
+  const int nj = a.D >> 8;
+  float4 xv[TT], wv[EE];
+#pragma unroll
+  for (int t = 0; t < TT; t++) xv[t] = xr[t][0];
+#pragma unroll
+  for (int e = 0; e < EE; e++) wv[e] = wr[e][0];
+  for (int j = 0; j < nj; j++) {
+    const int jn = min(j + 1, nj - 1) * 64;
+    float4 xn[TT], wn[EE];
+#pragma unroll
+    for (int t = 0; t < TT; t++) xn[t] = xr[t][jn];
+#pragma unroll
+    for (int e = 0; e < EE; e++) wn[e] = wr[e][jn];
+#pragma unroll
+    for (int t = 0; t < TT; t++)
+#pragma unroll
+      for (int e = 0; e < EE; e++) {
+        float c = acc[t][e];
+        c = fmaf(xv[t].x, wv[e].x, c);
+        c = fmaf(xv[t].y, wv[e].y, c);
+        c = fmaf(xv[t].z, wv[e].z, c);
+        c = fmaf(xv[t].w, wv[e].w, c);
+        acc[t][e] = c;
+      }
+#pragma unroll
+    for (int t = 0; t < TT; t++) xv[t] = xn[t];
+#pragma unroll
+    for (int e = 0; e < EE; e++) wv[e] = wn[e];
+  }
+#pragma unroll
+  for (int t = 0; t < TT; t++)
+#pragma unroll
+    for (int e = 0; e < EE; e++) {
+      const float v = wave_sum_f32(acc[t][e]);
+      if (lane == 0 && s0 + t < a.S && e0 + e < a.E) {
+        a.logits[(int64_t)(s0 + t) * a.E + e0 + e] = v;
+        if (a.logits_out) a.logits_out[(int64_t)(s0 + t) * a.E + e0 + e] = v;
+      }
+    }
+}
+
 }  // namespace moe
 
 namespace moe {
@@ -140,16 +214,19 @@ hipError_t launch_quant(const QuantArgs &a, int S, hipStream_t st) {
 
 hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
   const int ne4 = (a.E + 3) / 4;
+  const int nq = with_quant ? a.S : 0;
   // a few tokens: one token per wave, the whole weight row in one batch of
-  // loads (rows are re-read per token from L2); many tokens: 8 tokens share
-  // each weight load
-  const int ts = a.S <= 8 ? 1 : 8;
-  const int n_router = ne4 * ((a.S + ts - 1) / ts);
-  const dim3 grid(n_router + (with_quant ? a.S : 0));
-  if (ts == 1)
-    hipLaunchKernelGGL((router_kernel<1, 24>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((router_kernel<8, 4>), grid, dim3(256), 0, st, a);
+  // loads (rows are re-read per token from L2); a few dozen: 8 tokens share
+  // each weight load; hundreds: 8 x 8 register tiles
+  if (a.S <= 8) {
+    hipLaunchKernelGGL((router_kernel<1, 24>), dim3(ne4 * a.S + nq), dim3(256), 0, st, a);
+  } else if (a.S < kRouterTileMinTokens) {
+    hipLaunchKernelGGL((router_kernel<8, 4>), dim3(ne4 * ((a.S + 7) / 8) + nq), dim3(256), 0, st, a);
+  } else {
+    const int neb = (a.E + 31) / 32;
+    hipLaunchKernelGGL((router_tile_kernel<8, 8>), dim3(neb * ((a.S + 7) / 8) + nq), dim3(256), 0,
+                       st, a);
+  }
   return hipGetLastError();
 }
 

@@ -77,7 +77,8 @@ def test_quant_bf16_and_degenerate_rows():
 
 
 @pytest.mark.parametrize("shape,S,bias", [(TINY, 4, "uniform"), (GLM, 1, "uniform"),
-                                          (GLM, 64, "uniform"), (GLM, 200, "zero")])
+                                          (GLM, 64, "uniform"), (GLM, 200, "zero"),
+                                          (GLM, 300, "uniform")])
 def test_router_topk(shape, S, bias):
     say(f"router D={shape.D} E={shape.E} S={S}")
     cfg_o = config_of(shape)
@@ -97,16 +98,18 @@ def test_router_topk(shape, S, bias):
     say(f"  unique routing for {uniq.sum()}/{S} tokens")
 
 
-def test_router_batch_invariance():
-    # a token's routing does not depend on the batch it is in
+@pytest.mark.parametrize("S", [37, 301])
+def test_router_batch_invariance(S):
+    # a token's routing does not depend on the batch it is in (37 tokens: the
+    # 8-token kernel; 301: the 8x8 register tiles with a ragged last tile)
     shape = GLM
     cfg = moe.config(shape.D, shape.I, shape.E, shape.K)
     wr = torch.from_numpy(synth.router_w(2, shape)).cuda()
     b = torch.from_numpy(synth.router_b_uniform(2, shape)).cuda()
-    x = torch.from_numpy(synth.activations(8, 37, shape.D)).cuda()
-    ws = moe.Workspace(cfg, 37, moe.WS_ROUTER)
+    x = torch.from_numpy(synth.activations(8, S, shape.D)).cuda()
+    ws = moe.Workspace(cfg, S, moe.WS_ROUTER)
     _, _, lg_all = moe.moe_router_topk(cfg, x, wr, b, ws, want_logits=True)
-    for s in (0, 5, 36):
+    for s in (0, 5, 36, S - 1):
         _, _, lg1 = moe.moe_router_topk(cfg, x[s:s + 1].contiguous(), wr, b, ws, want_logits=True)
         assert torch.equal(lg1[0], lg_all[s])
 
