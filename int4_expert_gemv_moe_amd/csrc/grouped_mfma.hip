@@ -25,12 +25,15 @@
 // the permuted activation codes [x0 x2 x4 x6 x1 x3 x5 x7] of each group of 8
 // (the low nibbles of a word are the even columns): acc - 8 * sum(x) is the
 // exact signed product.
+#include <type_traits>
+
 #include "moe_kernels.h"
 #include "rowops.h"
 
 namespace moe {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));  // 16 staged bytes
 
 constexpr int kMT = kGroupedMfmaTile;  // pairs per tile (128)
 constexpr int kKS = 256;        // columns per pipeline step
@@ -49,50 +52,73 @@ __device__ __forceinline__ v4i unpack16(uint32_t w0, uint32_t w1) {
 
 // MODE 0: gate/up (A = token codes xq[s], B = gate and up rows, epilogue
 // h = silu(g) * u into h[pair]); MODE 1: down (A = hidden codes hq[pair],
-// B = down rows, epilogue y into stage[pair]).  MSV: 16-pair subtiles the
-// tile needs (1 to 8); only those rows are loaded and multiplied.
+// B = down rows, epilogue y into stage[pair]).  NW waves per workgroup; MSV:
+// 16-pair subtiles the tile needs (1 to 8); only those rows are loaded and
+// multiplied.
 struct MfmaTile {
   int rows;          // pairs of the tile
   int j, lane, wave;
   RowPtr Bm[2];
   int ob[2];         // output rows of the lane's two B subtiles
-  const uint8_t *bp[2];
+  const uint8_t *bp[4];  // the lane's 16-byte piece of each coalesced weight load
+  int8_t *bs;        // the wave's weight transpose buffer in shared memory
 };
 
-template <int MODE, int MSV>
-__device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTile &t,
-                                          int8_t (*As)[kMT * kAStride], const int *pr_l,
-                                          const int *sum_l, const float *scl_l) {
+constexpr int kBStride = 144;  // shared bytes per weight row of a step (128 + 16)
+
+// As: two activation buffers of ABUF bytes each.
+template <int MODE, int NW, int MSV, int ABUF>
+__device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTile &t, int8_t *As,
+                                          const int *pr_l, const int *sum_l, const float *scl_l) {
   constexpr int NS = 2;
+  constexpr int RPL = NW * 4;                  // pair rows staged per load round
+  constexpr int NA = (MSV * 16 + RPL - 1) / RPL;  // 16-byte activation loads per thread per step
   const int C = a.C, O = a.O;
   const int lane = t.lane, j = t.j, rows = t.rows;
-  // A loads: per step, load i of a thread copies 16 bytes (column piece
-  // tid % 16) of pair row 16 i + tid / 16; rows past the tile are zero
+  // activation staging: load i of a thread copies 16 bytes (column piece
+  // tid % 16) of pair row RPL * i + tid / 16.  Rows from `rows` up to
+  // 16 * MSV repeat the tile's last pair: their products land only in
+  // output rows that the epilogue skips.
   const int ar = threadIdx.x >> 4, aq = threadIdx.x & 15;
-  const int8_t *arow[MSV];
+  const int8_t *arow[NA];
 #pragma unroll
-  for (int i = 0; i < MSV; i++) {
-    const int apr = pr_l[min(16 * i + ar, rows - 1)];
+  for (int i = 0; i < NA; i++) {
+    const int apr = pr_l[min(RPL * i + ar, rows - 1)];
     arow[i] = (MODE == 0 ? a.act + (int64_t)(apr / a.P) * C : a.act + (int64_t)apr * C) + 16 * aq;
   }
-  uint4 av[MSV], avn[MSV];
-  auto load_a = [&](int k0, uint4 (&v)[MSV]) {
+  auto load_a = [&](int k0, u4v (&v)[NA]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < MSV; i++) v[i] = *reinterpret_cast<const uint4 *>(arow[i] + k0);
+    for (int i = 0; i < NA; i++) v[i] = *reinterpret_cast<const u4v *>(arow[i] + k0);
   };
-  auto store_a = [&](int buf, const uint4 (&v)[MSV]) {
+  auto store_a = [&](int buf, const u4v (&v)[NA]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < MSV; i++)
-      *reinterpret_cast<uint4 *>(&As[buf][(16 * i + ar) * kAStride + 16 * aq]) =
-          (16 * i + ar < rows) ? v[i] : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < NA; i++)
+      if (RPL * (i + 1) <= MSV * 16 || RPL * i + ar < MSV * 16)
+        *reinterpret_cast<u4v *>(As + buf * ABUF + (RPL * i + ar) * kAStride + 16 * aq) = v[i];
   };
-  uint4 bcur[NS][2], bnext[NS][2], bnext2[NS][2];
-  auto load_b = [&](int k0, uint4 (&bv)[NS][2]) {
+  // Weights: the wave's 32 rows of a step (128 bytes each) arrive in four
+  // coalesced loads, load i holding rows 8 i .. 8 i + 7 with 8 lanes per
+  // row, and pass through the wave's own shared-memory buffer to reach the
+  // MFMA operand layout (lane: one row, 32 bytes).
+  auto load_b = [&](int k0, uint4 (&bv)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < NS; s++) {
-      bv[s][0] = ldnt16(t.bp[s] + k0 / 2, true, t.bp[s]);
-      bv[s][1] = ldnt16(t.bp[s] + k0 / 2 + 16, true, t.bp[s]);
-    }
+    for (int i = 0; i < 4; i++) bv[i] = ldnt16(t.bp[i] + k0 / 2, true, t.bp[i]);
+  };
+  auto transpose_b = [&](const uint4 (&bv)[4], uint4 (&bm)[NS][2]) __attribute__((always_inline)) {
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      *reinterpret_cast<uint4 *>(t.bs + (8 * i + (lane >> 3)) * kBStride + 16 * (lane & 7)) = bv[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+        bm[s][h] = *reinterpret_cast<const uint4 *>(t.bs + (16 * s + (lane & 15)) * kBStride + 32 * j +
+                                                    16 * h);
+    __builtin_amdgcn_wave_barrier();
   };
   v4i acc[MSV][NS];
 #pragma unroll
@@ -104,31 +130,64 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   for (int s = 0; s < NS; s++) sc[s] = t.Bm[s].s[min(t.ob[s], O - 1)];
   const int nsteps = C / kKS;
 
-  // weights and activations both run two steps ahead: the activation rows
-  // of step s + 1 wait in registers during step s and go to shared memory at
-  // its end
-  load_a(0, avn);
-  load_b(0, bcur);
-  load_a(min(1, nsteps - 1) * kKS, av);
-  load_b(min(1, nsteps - 1) * kKS, bnext);
-  store_a(0, avn);
+  // Two register sets each for weights (bw0, bw1) and activations (ra0,
+  // ra1), named statically by unrolling the step loop twice, so that no
+  // load is waited for before the step that uses it.  At the start of step
+  // s: bw[s % 2] holds the weights of step s, ra[(s + 1) % 2] the
+  // activations of step s + 1 and ra[s % 2] those of step s + 2; shared
+  // buffer s % 2 holds the activations of step s.  Step s unpacks its
+  // weights and refills their set with step s + 2, moves the activations of
+  // step s + 1 to shared memory and refills their set with step s + 3, and
+  // only then multiplies.
+  uint4 bw0[4], bw1[4];
+  u4v ra0[NA], ra1[NA];
+  // Loads past the last step repeat the last step's addresses: every load
+  // is issued unconditionally, so the compiler's count of loads in flight
+  // is exact and its waits name only the data a step needs.
+  const int last = (nsteps - 1) * kKS;
+  load_b(0, bw0);
+  load_a(0, ra0);
+  load_b(min(kKS, last), bw1);
+  load_a(min(kKS, last), ra1);
+  store_a(0, ra0);
+  load_a(min(2 * kKS, last), ra0);
   __syncthreads();
-  for (int step = 0; step < nsteps; step++) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    load_a(min(step + 2, nsteps - 1) * kKS, avn);
-    load_b(min(step + 2, nsteps - 1) * kKS, bnext2);
-    // per 64-column slice c: the operands first (one wait for shared
-    // memory), then the MFMAs
-    const int8_t *abase = &As[buf][(lane & 15) * kAStride + 64 * j];
+  // one step; H = st % 2 is a template constant, so every register set is
+  // named statically
+  auto step = [&](int st, auto hc) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
+    // the step's weights, unpacked at once so that their registers take
+    // the loads of step s + 2 before the multiplications start
+    uint4 bm[NS][2];
+    if constexpr (H == 0)
+      transpose_b(bw0, bm);
+    else
+      transpose_b(bw1, bm);
+    v4i bb[4][NS];
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      v4i bb[NS];
+    for (int c = 0; c < 4; c++)
 #pragma unroll
       for (int s = 0; s < NS; s++) {
-        const uint4 w = bcur[s][c >> 1];
-        bb[s] = (c & 1) ? unpack16(w.z, w.w) : unpack16(w.x, w.y);
+        const uint4 w = bm[s][c >> 1];
+        bb[c][s] = (c & 1) ? unpack16(w.z, w.w) : unpack16(w.x, w.y);
       }
+    const int kb = min((st + 2) * kKS, last), ka = min((st + 3) * kKS, last);
+    // shared buffer (s + 1) % 2 was last read in step s - 1, which ended
+    // with a barrier
+    if constexpr (H == 0) {
+      load_b(kb, bw0);
+      if (st + 1 < nsteps) store_a(1, ra1);
+      load_a(ka, ra1);
+    } else {
+      load_b(kb, bw1);
+      if (st + 1 < nsteps) store_a(0, ra0);
+      load_a(ka, ra0);
+    }
+    // keep the compiler from sinking those loads below the multiplications
+    __builtin_amdgcn_sched_barrier(0);
+    const int8_t *abase = As + H * ABUF + (lane & 15) * kAStride + 64 * j;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
       v4i aa[MSV];
 #pragma unroll
       for (int ms = 0; ms < MSV; ms++) {
@@ -139,20 +198,16 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
       for (int ms = 0; ms < MSV; ms++)
 #pragma unroll
         for (int s = 0; s < NS; s++)
-          acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[s], acc[ms][s], 0, 0, 0);
+          acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[c][s], acc[ms][s], 0, 0, 0);
     }
-    if (more) store_a(buf ^ 1, av);
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < MSV; i++) av[i] = avn[i];
-#pragma unroll
-    for (int s = 0; s < NS; s++) {
-      bcur[s][0] = bnext[s][0];
-      bcur[s][1] = bnext[s][1];
-      bnext[s][0] = bnext2[s][0];
-      bnext[s][1] = bnext2[s][1];
-    }
+  };
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(st, std::integral_constant<int, 0>{});
+    step(st + 1, std::integral_constant<int, 1>{});
   }
+  if (st < nsteps) step(st, std::integral_constant<int, 0>{});
 
   // epilogue: lane holds output row ob[s] for pairs 16 ms + 4 j + i
 #pragma unroll
@@ -183,10 +238,21 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
-  constexpr int ROWS_PER_BLOCK = MODE == 0 ? 64 : 128;
-  __shared__ __align__(16) int8_t As[2][kMT * kAStride];
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
+
+// Rows of B per workgroup: NW waves of 16 gate + 16 up rows (MODE 0) or
+// 32 down rows (MODE 1).
+template <int MODE, int NW>
+constexpr int mfma_block_rows() { return MODE == 0 ? 16 * NW : 32 * NW; }
+
+// MSVMAX: the largest subtile count the launch can meet (tiles never hold
+// more pairs than the batch has tokens); it bounds the registers the
+// compiler reserves.
+template <int MODE, int NW, int MSVMAX>
+__global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a) {
+  constexpr int ABUF = 16 * MSVMAX * kAStride;
+  __shared__ __align__(16) int8_t As[2 * ABUF];
+  __shared__ __align__(16) int8_t Bs[NW][32 * kBStride];
   __shared__ int pr_l[kMT];
   __shared__ int sum_l[kMT];    // code sum of each pair's activation row
   __shared__ float scl_l[kMT];  // scale of each pair's activation row
@@ -195,13 +261,13 @@ __global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
   const int2 tg = a.tiles[tile];
   const int g = tg.x, m0 = tg.y;
   MfmaTile t;
-  t.rows = min(kMT, a.gcount[g] - m0);
+  t.rows = min(16 * MSVMAX, a.gcount[g] - m0);
   t.lane = threadIdx.x & 63;
   t.wave = threadIdx.x >> 6;
   t.j = t.lane >> 4;  // lane group: columns 64j .. 64j + 64 of a step
   const bool shared = (g == a.E);
   const int e = shared ? 0 : g;
-  const int o_blk = blockIdx.x * ROWS_PER_BLOCK;
+  const int o_blk = blockIdx.x * mfma_block_rows<MODE, NW>();
   if (MODE == 0) {
     t.Bm[0] = pick(a.rt.gate, a.sh.gate, shared, e);
     t.Bm[1] = pick(a.rt.up, a.sh.up, shared, e);
@@ -213,9 +279,16 @@ __global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
     t.ob[1] = t.ob[0] + 16;
   }
   const int rowbytes = a.C >> 1;
+  // coalesced load i: wave row r = 8 i + lane / 8 (rows 0..15 are subtile
+  // 0, 16..31 subtile 1), bytes 16 (lane % 8) of the step's 128
 #pragma unroll
-  for (int s = 0; s < 2; s++)
-    t.bp[s] = t.Bm[s].q + (int64_t)min(t.ob[s], a.O - 1) * rowbytes + 32 * t.j;
+  for (int i = 0; i < 4; i++) {
+    const int r = 8 * i + (t.lane >> 3);
+    const int s = r >> 4;
+    const int o = (MODE == 0 ? o_blk + 16 * t.wave : o_blk + 32 * t.wave + 16 * s) + (r & 15);
+    t.bp[i] = t.Bm[s].q + (int64_t)min(o, a.O - 1) * rowbytes + 16 * (t.lane & 7);
+  }
+  t.bs = &Bs[t.wave][0];
 
   // pair list of the tile and the scale and code sum of each pair's row
   const int *plist = a.pairs + a.goff[g] + m0;
@@ -228,14 +301,14 @@ __global__ __launch_bounds__(256) void grouped_mfma_kernel(GroupedMfmaArgs a) {
   }
   __syncthreads();
   switch ((t.rows + 15) >> 4) {  // 16-pair subtiles in use, uniform across the block
-    case 1: mfma_tile<MODE, 1>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 2: mfma_tile<MODE, 2>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 3: mfma_tile<MODE, 3>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 4: mfma_tile<MODE, 4>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 5: mfma_tile<MODE, 5>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 6: mfma_tile<MODE, 6>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 7: mfma_tile<MODE, 7>(a, t, As, pr_l, sum_l, scl_l); break;
-    default: mfma_tile<MODE, 8>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 1: mfma_tile<MODE, NW, 1, ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 2: mfma_tile<MODE, NW, cmin(2, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 3: mfma_tile<MODE, NW, cmin(3, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 4: mfma_tile<MODE, NW, cmin(4, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 5: mfma_tile<MODE, NW, cmin(5, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 6: mfma_tile<MODE, NW, cmin(6, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 7: mfma_tile<MODE, NW, cmin(7, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    default: mfma_tile<MODE, NW, MSVMAX, ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
   }
 }
 
@@ -243,13 +316,29 @@ bool grouped_mfma_fits(int C) { return C % kKS == 0; }
 
 int grouped_mfma_max_tiles(int S, int P, int E) { return (S * P + kMT - 1) / kMT + E + 1; }
 
-hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, hipStream_t st) {
-  if (mode == 0) {
-    const dim3 grid((a.O + 63) / 64, max_tiles);
-    hipLaunchKernelGGL(grouped_mfma_kernel<0>, grid, dim3(256), 0, st, a);
+// Batches of up to 64 tokens (at most 4 subtiles per tile): 4-wave
+// workgroups, so that a few experts still spread over many workgroups;
+// larger batches: 8-wave workgroups, which stage each activation tile for
+// twice as many weight rows.
+hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, int S,
+                               hipStream_t st) {
+  if (S <= 64) {
+    const dim3 grid((a.O + mfma_block_rows<0, 4>() - 1) / mfma_block_rows<0, 4>(), max_tiles);
+    if (mode == 0)
+      hipLaunchKernelGGL((grouped_mfma_kernel<0, 4, 4>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((grouped_mfma_kernel<1, 4, 4>),
+                         dim3((a.O + mfma_block_rows<1, 4>() - 1) / mfma_block_rows<1, 4>(), max_tiles),
+                         dim3(256), 0, st, a);
   } else {
-    const dim3 grid((a.O + 127) / 128, max_tiles);
-    hipLaunchKernelGGL(grouped_mfma_kernel<1>, grid, dim3(256), 0, st, a);
+    if (mode == 0)
+      hipLaunchKernelGGL((grouped_mfma_kernel<0, 8, 8>),
+                         dim3((a.O + mfma_block_rows<0, 8>() - 1) / mfma_block_rows<0, 8>(), max_tiles),
+                         dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((grouped_mfma_kernel<1, 8, 8>),
+                         dim3((a.O + mfma_block_rows<1, 8>() - 1) / mfma_block_rows<1, 8>(), max_tiles),
+                         dim3(512), 0, st, a);
   }
   return hipGetLastError();
 }

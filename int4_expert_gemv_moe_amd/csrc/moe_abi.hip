@@ -466,7 +466,7 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
     mg.ascale = w.sx;
     mg.asum = w.sumx;
     mg.out = w.h;
-    MOE_TRY_HIP(launch_grouped_mfma(mg, 0, max_tiles, stream));
+    MOE_TRY_HIP(launch_grouped_mfma(mg, 0, max_tiles, S, stream));
   } else {
     MOE_TRY_HIP(launch_grouped_gateup(g, stream));
   }
@@ -496,7 +496,7 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
     md.ascale = w.sh;
     md.asum = w.sumh;
     md.out = w.stage;
-    MOE_TRY_HIP(launch_grouped_mfma(md, 1, max_tiles, stream));
+    MOE_TRY_HIP(launch_grouped_mfma(md, 1, max_tiles, S, stream));
   } else {
     MOE_TRY_HIP(launch_grouped_down(d, stream));
   }

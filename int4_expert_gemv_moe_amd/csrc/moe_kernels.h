@@ -183,7 +183,7 @@ bool grouped_mfma_fits(int C);
 constexpr int kGroupedMfmaTile = 128;  // pairs per tile
 constexpr int kRouterTileMinTokens = 256;  // batches from this size use the 8x8 router tiles
 int grouped_mfma_max_tiles(int S, int P, int E);
-hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, hipStream_t st);
+hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, int S, hipStream_t st);
 hipError_t launch_grouped_down(const GroupedDownArgs &a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_pack(const PackArgs &a, hipStream_t st);
