@@ -282,16 +282,62 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedDownArgs a) {
 }
 
 // out[s] = sum_k w[s][k] * stage[s][k] (k ascending, from 0) + stage[s][K]
+// VEC: 4 consecutive columns per thread (D % 4 == 0); the stage rows of a
+// column group are loaded 4 slots at a time before they are summed, in the
+// same order and with the same roundings as the scalar form.
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int s = blockIdx.y;
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  const float *wts = a.w + s * a.K;
+  if (!VEC) {
+    const int d = blockIdx.x * blockDim.x + threadIdx.x;
+    if (d >= a.D) return;
+    const float *st = a.stage + (int64_t)s * a.P * a.D + d;
+    float acc = 0.f;
+    for (int k = 0; k < a.K; k++) acc = acc + wts[k] * st[(int64_t)k * a.D];
+    if (a.n_shared) acc = acc + st[(int64_t)a.K * a.D];
+    float *o = a.out + (int64_t)s * a.D + d;
+    *o = (a.flags & MOE_F_ACCUMULATE) ? (*o + acc) : acc;
+    return;
+  }
+  const int d = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
   if (d >= a.D) return;
-  const float *st = a.stage + (int64_t)s * a.P * a.D + d;
-  float acc = 0.f;
-  for (int k = 0; k < a.K; k++) acc = acc + a.w[s * a.K + k] * st[(int64_t)k * a.D];
-  if (a.n_shared) acc = acc + st[(int64_t)a.K * a.D];
-  float *o = a.out + (int64_t)s * a.D + d;
-  *o = (a.flags & MOE_F_ACCUMULATE) ? (*o + acc) : acc;
+  const f4v *st = reinterpret_cast<const f4v *>(a.stage + (int64_t)s * a.P * a.D + d);
+  const int64_t step = a.D / 4;
+  f4v acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.K; k0 += 4) {
+    f4v v[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (k0 + i < a.K) v[i] = __builtin_nontemporal_load(st + (int64_t)(k0 + i) * step);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (k0 + i < a.K) {
+        const float w = wts[k0 + i];
+        acc.x = acc.x + w * v[i].x;
+        acc.y = acc.y + w * v[i].y;
+        acc.z = acc.z + w * v[i].z;
+        acc.w = acc.w + w * v[i].w;
+      }
+  }
+  if (a.n_shared) {
+    const f4v v = __builtin_nontemporal_load(st + (int64_t)a.K * step);
+    acc.x = acc.x + v.x;
+    acc.y = acc.y + v.y;
+    acc.z = acc.z + v.z;
+    acc.w = acc.w + v.w;
+  }
+  f4v *o = reinterpret_cast<f4v *>(a.out + (int64_t)s * a.D + d);
+  if (a.flags & MOE_F_ACCUMULATE) {
+    const f4v p = *o;
+    acc.x = p.x + acc.x;
+    acc.y = p.y + acc.y;
+    acc.z = p.z + acc.z;
+    acc.w = p.w + acc.w;
+  }
+  *o = acc;
 }
 
 #define MOE_DISPATCH_COLS(RB, LAUNCH)                         \
@@ -345,7 +391,12 @@ hipError_t launch_grouped_down(const GroupedDownArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel, dim3((a.D + 255) / 256, a.S), dim3(256), 0, st, a);
+  // the vector form needs 16-byte aligned rows of stage and out
+  const bool vec = a.D % 4 == 0 && ((uintptr_t)a.stage % 16) == 0 && ((uintptr_t)a.out % 16) == 0;
+  if (vec)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3((a.D / 4 + 255) / 256, a.S), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3((a.D + 255) / 256, a.S), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -8,12 +8,12 @@
 
 namespace moe {
 
-// ---- activation quantization (one block of 256 threads per row) -----------
+// ---- activation quantization (one block per row) ---------------------------
 
 __device__ inline void quant_row_block(const float *xf, const uint16_t *xb, int D, int8_t *xq_perm,
                                 int8_t *xq_nat, float *sx_out, int32_t *sumx_out) {
-  __shared__ float red_f[4];
-  __shared__ int red_i[4];
+  __shared__ float red_f[16];  // one slot per wave, blocks of up to 1024 threads
+  __shared__ int red_i[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ngroups = D >> 3;
   float m = 0.f;

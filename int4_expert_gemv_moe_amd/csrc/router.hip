@@ -131,15 +131,15 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 
 // Many tokens: a register tile per wave, TT tokens x EE experts, so each
 // loaded x vector serves EE experts and each weight vector TT tokens.  Block
-// = 4 waves over 4 * EE consecutive experts of one token tile.  Every logit
+// = TG x 4 waves over TG * TT tokens and 4 * EE consecutive experts.  Every logit
 // is still lane p's ascending FMA chain over k = 4p + 256j + q followed by
 // wave_sum_f32, i.e. the same bits as router_kernel.  The operands of step
 // j + 1 are loaded while step j is multiplied.
-template <int TT, int EE>
-__global__ __launch_bounds__(256) void router_tile_kernel(RouterArgs a) {
+template <int TT, int EE, int TG>
+__global__ __launch_bounds__(256 * TG) void router_tile_kernel(RouterArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int neb = (a.E + 4 * EE - 1) / (4 * EE);
-  const int n_router = neb * ((a.S + TT - 1) / TT);
+  const int n_router = neb * ((a.S + TG * TT - 1) / (TG * TT));
   if ((int)blockIdx.x >= n_router) {
     const int s = blockIdx.x - n_router;
     if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
@@ -147,9 +147,12 @@ __global__ __launch_bounds__(256) void router_tile_kernel(RouterArgs a) {
                     a.sx + s, a.sumx + s);
     return;
   }
-  const int e0 = (blockIdx.x % neb) * 4 * EE + wave * EE;
-  const int s0 = (blockIdx.x / neb) * TT;
-  if (e0 >= a.E) return;
+  // TG groups of 4 waves: group g takes tokens s0 + TT g .. +TT, wave w % 4
+  // of a group takes experts e0 + EE (w % 4) .. +EE; the groups share each
+  // weight vector through the cache
+  const int e0 = (blockIdx.x % neb) * 4 * EE + (wave & 3) * EE;
+  const int s0 = (blockIdx.x / neb) * TG * TT + (wave >> 2) * TT;
+  if (e0 >= a.E || s0 >= a.S) return;
   const float4 *xr[TT], *wr[EE];
 #pragma unroll
   for (int t = 0; t < TT; t++)
@@ -224,8 +227,8 @@ hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
     hipLaunchKernelGGL((router_kernel<8, 4>), dim3(ne4 * ((a.S + 7) / 8) + nq), dim3(256), 0, st, a);
   } else {
     const int neb = (a.E + 31) / 32;
-    hipLaunchKernelGGL((router_tile_kernel<8, 8>), dim3(neb * ((a.S + 7) / 8) + nq), dim3(256), 0,
-                       st, a);
+    hipLaunchKernelGGL((router_tile_kernel<8, 8, 2>), dim3(neb * ((a.S + 15) / 16) + nq), dim3(512),
+                       0, st, a);
   }
   return hipGetLastError();
 }
