@@ -199,8 +199,9 @@ def bench_verify(layer, iters: int = 20):
 
 def bench_stack(steps: int = 64):
     """48 GLM-shape layers resident in HBM (per-layer Zipf-skewed routing,
-    RMSNorm + residual between layers): decode steps of 1 token (per-token
-    path) and of 4 tokens (union path), each step one HIP graph replay."""
+    RMSNorm + residual, one MOE_F_PRENORM call per layer): decode steps of
+    1 token (per-token path) and of 4 tokens (union path), each step one HIP
+    graph replay."""
     import json as _json
 
     import torch
@@ -219,7 +220,8 @@ def bench_stack(steps: int = 64):
     log(f"built 48 layers in {time.time() - t0:.1f}s, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB resident")
     stack = Stack(layers, torch.ones(D, dtype=torch.float32, device="cuda"))
-    res = {"workload": "48 GLM-shape MoE layers resident in HBM, RMSNorm(eps 1e-5) + residual, "
+    res = {"workload": "48 GLM-shape MoE layers resident in HBM, one call per layer: "
+                       "x <- x + block(RMSNorm(x)) in place (RMSNorm eps 1e-5 inside the call), "
                        f"per-layer Zipf(1.1)-skewed routing (bias strength {beta})",
            "layers": 48}
     for S, union in ((1, False), (4, True)):

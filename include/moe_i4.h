@@ -59,6 +59,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Flags of the layer calls. */
 #define MOE_F_ACCUMULATE 1u /* out += block(x) instead of out = block(x) */
+/* The block's input is RMSNorm(x) with layer->norm_gamma and norm_eps
+ * (section 04 RMSNorm, the same bits as moe_rmsnorm) instead of x.  With
+ * MOE_F_ACCUMULATE and out == x this is one decoder-layer update
+ * x <- x + block(rmsnorm(x)) in place.  Needs D % 4 == 0, D <= 8192 and
+ * 16-byte aligned x and gamma (MOE_EALIGN otherwise). */
+#define MOE_F_PRENORM 2u
 
 typedef struct {
   int32_t D;          /* hidden size (6144 for the GLM shape) */
@@ -92,6 +98,8 @@ typedef struct {
   const float *router_b; /* [E] float32 correction bias */
   moe_experts routed;    /* E experts */
   moe_experts shared;    /* one expert; read only when n_shared == 1 */
+  const float *norm_gamma; /* [D] RMSNorm gain; read only with MOE_F_PRENORM */
+  float norm_eps;          /* RMSNorm epsilon (> 0); read only with MOE_F_PRENORM */
 } moe_layer;
 
 /* Optional outputs of the layer calls (host struct; any member may be NULL). */
@@ -153,7 +161,9 @@ int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *s
  * route, quantize, run the K routed experts and the shared expert, and
  * combine out[s] = sum_k w_k * y_k (k in selection order, from 0) + y_shared.
  * With MOE_F_ACCUMULATE the result is added to out.  x and out must not
- * overlap.  probe is optional (host struct).
+ * overlap, except out == x with MOE_F_PRENORM (in-place residual update;
+ * the first launch then normalizes each token inside every workgroup).
+ * Unknown flag bits give MOE_EINVAL.  probe is optional (host struct).
  * Launches: router + token quantization + shared gate/up; routed gate/up +
  * shared down; routed down + combine (one launch per batch of 8 slots). */
 int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
@@ -164,7 +174,8 @@ int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float
  * grouped by selected expert and every selected expert's weights are read
  * once for all its tokens.  Per-(token, slot) results are staged and combined
  * in the same order as moe_layer_forward, so the two calls return identical
- * bits for the same inputs. */
+ * bits for the same inputs.  Flags and the x/out rule as moe_layer_forward
+ * (with MOE_F_PRENORM the normalized rows go to the workspace first). */
 int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                             float *out, unsigned flags, const moe_probe *probe, void *ws,
                             size_t ws_bytes, hipStream_t stream);

@@ -20,6 +20,7 @@ LIB_PATH = os.environ.get("MOE_I4_LIB") or os.path.join(HERE, "libmoe_i4.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 F_ACCUMULATE = 1
+F_PRENORM = 2
 WS_FORWARD, WS_BATCH, WS_SWIGLU, WS_ROUTER = 0, 1, 2, 3
 
 _lib = None
@@ -42,7 +43,8 @@ class Experts(ctypes.Structure):
 
 class LayerC(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
-                ("routed", Experts), ("shared", Experts)]
+                ("routed", Experts), ("shared", Experts),
+                ("norm_gamma", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
 
 
 class Probe(ctypes.Structure):
@@ -157,9 +159,12 @@ class DeviceLayer:
     routed: DeviceExperts   # E experts
     shared: DeviceExperts | None  # 1 expert when cfg.n_shared == 1
 
-    def cstruct(self) -> LayerC:
+    def cstruct(self, norm_gamma: torch.Tensor | None = None, norm_eps: float = 0.0) -> LayerC:
+        """The C struct; norm_gamma / norm_eps are read by calls with F_PRENORM."""
         sh = self.shared.cstruct() if self.shared is not None else Experts()
-        return LayerC(self.router_w.data_ptr(), self.router_b.data_ptr(), self.routed.cstruct(), sh)
+        g = None if norm_gamma is None else norm_gamma.data_ptr()
+        return LayerC(self.router_w.data_ptr(), self.router_b.data_ptr(), self.routed.cstruct(), sh,
+                      g, float(norm_eps))
 
 
 class Workspace:
@@ -258,13 +263,16 @@ def _probe(topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None):
 
 
 def _layer_call(fn_name, layer: DeviceLayer, x, out, flags, ws, topk_idx, topk_w, ev_gateup,
-                ev_down, stream):
+                ev_down, stream, norm_gamma=None, norm_eps=1e-5):
     _dev(x, torch.float32, "x")
     S = x.shape[0]
     if out is None:
         out = torch.empty(S, layer.cfg.D, dtype=torch.float32, device=x.device)
     _dev(out, torch.float32, "out")
-    L = layer.cstruct()
+    if norm_gamma is not None:
+        _dev(norm_gamma, torch.float32, "norm_gamma")
+        flags |= F_PRENORM
+    L = layer.cstruct(norm_gamma, norm_eps)
     probe = _probe(topk_idx, topk_w, ev_gateup, ev_down)
     fn = getattr(lib(), fn_name)
     _check(fn(ctypes.byref(layer.cfg), ctypes.byref(L), _ptr(x), S, _ptr(out), flags,
@@ -273,18 +281,20 @@ def _layer_call(fn_name, layer: DeviceLayer, x, out, flags, ws, topk_idx, topk_w
 
 
 def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None, flags: int = 0,
-                      topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None, stream=None):
-    """Per-token path: each token reads its own K experts and the shared one."""
+                      topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None, stream=None,
+                      norm_gamma=None, norm_eps: float = 1e-5):
+    """Per-token path: each token reads its own K experts and the shared one.
+    norm_gamma: run the block on RMSNorm(x) (flag F_PRENORM); out may then be x."""
     return _layer_call("moe_layer_forward", layer, x, out, flags, ws, topk_idx, topk_w, ev_gateup,
-                       ev_down, stream)
+                       ev_down, stream, norm_gamma, norm_eps)
 
 
 def moe_layer_forward_batch(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None,
                             flags: int = 0, topk_idx=None, topk_w=None, ev_gateup=None,
-                            ev_down=None, stream=None):
+                            ev_down=None, stream=None, norm_gamma=None, norm_eps: float = 1e-5):
     """Unique-expert union path: each selected expert is read once per call."""
     return _layer_call("moe_layer_forward_batch", layer, x, out, flags, ws, topk_idx, topk_w,
-                       ev_gateup, ev_down, stream)
+                       ev_gateup, ev_down, stream, norm_gamma, norm_eps)
 
 
 def moe_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out=None, stream=None):

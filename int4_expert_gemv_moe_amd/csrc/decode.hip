@@ -24,6 +24,7 @@
 
 #include "moe_kernels.h"
 #include "quant.h"
+#include "norm.h"
 #include "rowops.h"
 #include "topk.h"
 
@@ -34,9 +35,9 @@ constexpr int kWaves = 4;
 
 // ---- router: one wave computes one logit ----------------------------------------
 
-__device__ void router_logit(const DecodeArgs &a, int s, int e) {
+__device__ void router_logit(const DecodeArgs &a, const float *xrow, int s, int e) {
   if (e >= a.E) return;
-  const float v = router_dot(a.x + (int64_t)s * a.D, a.W + (int64_t)e * a.D, a.D);
+  const float v = router_dot(xrow, a.W + (int64_t)e * a.D, a.D);
   if ((threadIdx.x & 63) == 0) a.logits[(int64_t)s * a.E + e] = v;
 }
 
@@ -99,7 +100,7 @@ __device__ __forceinline__ void gu_items(Res res, int I, int rowbytes, int lo, i
 // token s, rows of block gb.  LOCALQ: quantize the float token row in the
 // wave; otherwise read its codes.
 template <int NCH, bool MASKED, int ROWS, bool LOCALQ>
-__device__ void gateup_fixed(const DecodeArgs &a, int s, int gb) {
+__device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
   __shared__ GuLds L;
   __shared__ int acco[2 * MOE_GU_MAX_ROWS];
   const int wave = threadIdx.x >> 6;
@@ -125,8 +126,15 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb) {
     // flight while it does
     __shared__ __align__(16) int8_t xcodes[2048 * 4];
     float4 xr[NCH][2];
-    quant_row_load<NCH>(a.x + (int64_t)s * a.D, a.D, xr);
-    gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
+    if (a.gamma) {
+      // the first weight stage goes out before the normalization
+      gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
+      prenorm_to_lds(a.x + (int64_t)s * a.D, a.gamma, a.D, a.eps, xn);
+      quant_row_load<NCH>(xn, a.D, xr);
+    } else {
+      quant_row_load<NCH>(a.x + (int64_t)s * a.D, a.D, xr);
+      gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
+    }
     sumx = quant_row_block_lds<NCH>(xr, a.D, xcodes, &sxs);
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -463,19 +471,27 @@ __device__ void down_fixed(const DecodeArgs &a, int s, int db) {
 #define MOE_GU_ROWS 2
 #endif
 
+// With a.gamma set every workgroup of phase A first forms the token's RMSNorm
+// row in dynamic shared memory (D floats) and works on that.
 template <int NCHD, bool MD, bool LOCALQ>
 __global__ __launch_bounds__(256) void decode_a_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) float xn_dyn[];
   const int s = blockIdx.y, b = blockIdx.x;
+  const float *xrow = a.x + (int64_t)s * a.D;
+  if (b < a.n_router + a.n_quant && a.gamma) {
+    prenorm_to_lds(xrow, a.gamma, a.D, a.eps, xn_dyn);
+    xrow = xn_dyn;
+  }
   if (b < a.n_router) {
-    router_logit(a, s, b * 4 + (threadIdx.x >> 6));
+    router_logit(a, xrow, s, b * 4 + (threadIdx.x >> 6));
     return;
   }
   if (b < a.n_router + a.n_quant) {
-    quant_row_block(a.x + (int64_t)s * a.D, nullptr, a.D, const_cast<int8_t *>(a.xq) + (int64_t)s * a.D,
-                    nullptr, const_cast<float *>(a.sx) + s, const_cast<int32_t *>(a.sumx) + s);
+    quant_row_block(xrow, nullptr, a.D, const_cast<int8_t *>(a.xq) + (int64_t)s * a.D, nullptr,
+                    const_cast<float *>(a.sx) + s, const_cast<int32_t *>(a.sumx) + s);
     return;
   }
-  gateup_fixed<NCHD, MD, MOE_GU_ROWS, LOCALQ>(a, s, b - a.n_router - a.n_quant);
+  gateup_fixed<NCHD, MD, MOE_GU_ROWS, LOCALQ>(a, s, b - a.n_router - a.n_quant, xn_dyn);
 }
 
 template <int NCHD, bool MD, int NCHI, bool MI>
@@ -631,12 +647,13 @@ static void launch_timed(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_
 hipError_t launch_decode_a(const DecodeArgs &a, bool local_quant, hipStream_t st) {
   const dim3 grid(a.n_router + a.n_quant + a.n_gu_fx, a.S);
   const int rb = a.D / 2;
-#define MOE_FA(N, M)                                                                   \
-  do {                                                                                 \
-    if (local_quant)                                                                   \
-      hipLaunchKernelGGL((decode_a_kernel<N, M, true>), grid, dim3(256), 0, st, a);    \
-    else                                                                               \
-      hipLaunchKernelGGL((decode_a_kernel<N, M, false>), grid, dim3(256), 0, st, a);   \
+  const size_t lds = a.gamma ? (size_t)a.D * 4 : 0;  // the normalized row
+#define MOE_FA(N, M)                                                                     \
+  do {                                                                                   \
+    if (local_quant)                                                                     \
+      hipLaunchKernelGGL((decode_a_kernel<N, M, true>), grid, dim3(256), lds, st, a);    \
+    else                                                                                 \
+      hipLaunchKernelGGL((decode_a_kernel<N, M, false>), grid, dim3(256), lds, st, a);   \
   } while (0)
   MOE_COLS(rb, MOE_FA);
 #undef MOE_FA

@@ -5,6 +5,7 @@
 // group, and the per-pair outputs are staged and combined per token in
 // selection order.
 #include "moe_kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -72,8 +73,9 @@ __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a) {
                     a.sumh + r);
 }
 
-// One block of 1024 threads: counting sort of the S*K routed pairs by expert,
-// plus the shared expert as group E holding every token.  The order of pairs
+// One block of 1024 threads: (optionally the top-K of every token, then) a
+// counting sort of the S*K routed pairs by expert, plus the shared expert as
+// group E holding every token.  The order of pairs
 // inside a group is whatever the shared-memory atomics produce; it does not
 // affect any result, because each pair is computed on its own.
 __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
@@ -81,6 +83,13 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
   __shared__ int fill[1025];
   __shared__ int off[1026];
   const int G = a.E + 1;  // group E is the shared expert (empty without one)
+  if (a.with_topk) {
+    // the tokens' selections (E <= 256), one wave per token; the writes are
+    // visible to the whole workgroup after the barrier below
+    for (int s = threadIdx.x >> 6; s < a.S; s += blockDim.x >> 6)
+      topk_rounds_m<4>(a.logits + (int64_t)s * a.E, a.bias, a.E, a.K, a.scale,
+                       a.idx + (int64_t)s * a.K, a.wts + (int64_t)s * a.K, nullptr);
+  }
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     cnt[g] = 0;
     fill[g] = 0;

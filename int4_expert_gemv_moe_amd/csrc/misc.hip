@@ -1,6 +1,7 @@
 // misc.hip -- the int4 weight packer (section 06 of the reader.mx article
 // "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型") and RMSNorm (section 04).
 #include "moe_kernels.h"
+#include "norm.h"
 
 namespace moe {
 
@@ -38,47 +39,20 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 // y = x * r * gamma.  With a.vec (D <= 8192, D % 4 == 0, 16-byte aligned
 // rows) each row is read once, all of a thread's loads issued together (the
 // row is then in registers); otherwise the plain loop.
-__device__ __forceinline__ double block_sum_f64(double v, double *red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
 __global__ __launch_bounds__(256) void rmsnorm_kernel(RmsArgs a) {
   __shared__ double red[4];
   const int tid = threadIdx.x;
   const float *x = a.x + (int64_t)blockIdx.x * a.D;
   float *y = a.y + (int64_t)blockIdx.x * a.D;
   if (a.vec) {
+    const float r = rms_factor_256(x, a.D, a.eps, red);
     const int n4 = a.D / 4;
-    float4 xv[8], gv[8];
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const int i = min(tid + 256 * k, n4 - 1);
-      xv[k] = reinterpret_cast<const float4 *>(x)[i];
-      gv[k] = reinterpret_cast<const float4 *>(a.gamma)[i];
-    }
-    double ms = 0.0;
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      if (tid + 256 * k < n4) {
-        ms += (double)xv[k].x * (double)xv[k].x;
-        ms += (double)xv[k].y * (double)xv[k].y;
-        ms += (double)xv[k].z * (double)xv[k].z;
-        ms += (double)xv[k].w * (double)xv[k].w;
-      }
-    }
-    const double t = block_sum_f64(ms, red);
-    const float r = 1.f / sqrtf((float)(t / a.D) + a.eps);
 #pragma unroll
     for (int k = 0; k < 8; k++) {
       const int i = tid + 256 * k;
       if (i < n4)
-        reinterpret_cast<float4 *>(y)[i] = make_float4(xv[k].x * r * gv[k].x, xv[k].y * r * gv[k].y,
-                                                        xv[k].z * r * gv[k].z, xv[k].w * r * gv[k].w);
+        reinterpret_cast<float4 *>(y)[i] = norm4(reinterpret_cast<const float4 *>(x)[i],
+                                                 reinterpret_cast<const float4 *>(a.gamma)[i], r);
     }
     return;
   }

@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "moe_kernels.h"
+#include "norm.h"
 
 using namespace moe;
 
@@ -118,6 +119,7 @@ size_t carve(const moe_config &c, int S, int which, char *base, Work *w) {
     t.stage = (float *)take(s * P * c.D * 4);
     t.tiles = (int2 *)take((size_t)grouped_mfma_max_tiles(S, P, c.E) * 8);
     t.ntiles = (int32_t *)take(4);
+    t.xn = (float *)take(s * c.D * 4);
   }
   if (w) *w = t;
   return off;
@@ -222,13 +224,24 @@ int record(const moe_probe *probe, int which, int side, hipStream_t st) {
 }
 
 int layer_common_checks(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
-                        float *out, void *ws, size_t ws_bytes, int which) {
+                        float *out, unsigned flags, void *ws, size_t ws_bytes, int which) {
   MOE_TRY(check_cfg(cfg));
   if (S < 1 || !x || !out || !ws) return MOE_EINVAL;
+  if (flags & ~(MOE_F_ACCUMULATE | MOE_F_PRENORM)) return MOE_EINVAL;
   MOE_TRY(check_layer(*cfg, layer));
   if (!aligned16(x) || ((uintptr_t)out & 3u) || ((uintptr_t)ws & 255u)) return MOE_EALIGN;
+  const bool prenorm = (flags & MOE_F_PRENORM) != 0;
+  if (prenorm) {
+    const float eps = layer->norm_eps;
+    if (!layer->norm_gamma || !(eps > 0.f) || !(eps < INFINITY)) return MOE_EINVAL;
+    if (!rms_vec_ok(cfg->D, x, layer->norm_gamma)) return MOE_EALIGN;
+  }
+  // out may be x itself only for the in-place residual update of PRENORM:
+  // every read of x then precedes the first write of out
   const size_t xb = (size_t)S * cfg->D * 4;
-  if ((const char *)out < (const char *)x + xb && (const char *)x < (const char *)out + xb)
+  const bool same = (const void *)out == (const void *)x;
+  if ((const char *)out < (const char *)x + xb && (const char *)x < (const char *)out + xb &&
+      !(prenorm && same))
     return MOE_EINVAL;
   if (ws_bytes < carve(*cfg, S, which, nullptr, nullptr)) return MOE_EWORKSPACE;
   return check_device();
@@ -361,7 +374,7 @@ int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *s
 int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                       float *out, unsigned flags, const moe_probe *probe, void *ws,
                       size_t ws_bytes, hipStream_t stream) {
-  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, ws, ws_bytes, W_FWD));
+  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_FWD));
   const moe_config &c = *cfg;
   Work w;
   carve(c, S, W_FWD, (char *)ws, &w);
@@ -397,7 +410,11 @@ int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float
   d.n_dn_fx = c.n_shared ? ds.dn_fx : 0;
   d.n_dn = ds.dn;
   d.out = out;
-  d.flags = flags;
+  d.flags = flags & MOE_F_ACCUMULATE;
+  if (flags & MOE_F_PRENORM) {
+    d.gamma = layer->norm_gamma;
+    d.eps = layer->norm_eps;
+  }
   MOE_TRY_HIP(launch_decode_a(d, true, stream));
   const bool tgu = probe && probe->ev_gateup[0] && probe->ev_gateup[1];
   const bool tdn = probe && probe->ev_down[0] && probe->ev_down[1];
@@ -419,18 +436,34 @@ int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float
 int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                             float *out, unsigned flags, const moe_probe *probe, void *ws,
                             size_t ws_bytes, hipStream_t stream) {
-  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, ws, ws_bytes, W_BATCH));
+  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_BATCH));
   const moe_config &c = *cfg;
   const int P = c.K + c.n_shared;
   Work w;
   carve(c, S, W_BATCH, (char *)ws, &w);
-  MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, true, nullptr, stream));
-  MOE_TRY(copy_probe(c, S, probe, w, stream));
+  if (flags & MOE_F_PRENORM) {
+    // the normalized rows go to the workspace; x (maybe out itself) is read
+    // here and nowhere else
+    RmsArgs ra{x, layer->norm_gamma, c.D, layer->norm_eps, w.xn, 1};
+    MOE_TRY_HIP(launch_rmsnorm(ra, S, stream));
+    x = w.xn;
+    flags &= ~MOE_F_PRENORM;
+  }
+  // small batches select inside the grouping kernel (one launch fewer)
+  const bool topk_in_group = S <= kGroupTopkMaxTokens && c.E <= 256;
+  MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, !topk_in_group, nullptr,
+                     stream));
   const bool mfma_gu = grouped_mfma_fits(c.D), mfma_dn = grouped_mfma_fits(c.I);
   const int max_tiles = grouped_mfma_max_tiles(S, P, c.E);
   GroupArgs ga{w.idx,    S,     c.E,     c.K,      P, c.n_shared, w.gcount, w.goff, w.pairs,
                (mfma_gu || mfma_dn) ? w.tiles : nullptr, w.ntiles, kGroupedMfmaTile};
+  ga.with_topk = topk_in_group ? 1 : 0;
+  ga.logits = w.logits;
+  ga.bias = layer->router_b;
+  ga.scale = c.routed_scale;
+  ga.wts = w.w;
   MOE_TRY_HIP(launch_group(ga, stream));
+  MOE_TRY(copy_probe(c, S, probe, w, stream));
   const ExpertSet rt = to_set(layer->routed, c);
   const ExpertSet sh = c.n_shared ? to_set(layer->shared, c) : rt;
   GroupedMfmaArgs m{};

@@ -193,6 +193,7 @@ struct Work {
   float *stage;     // [S][P][D]
   int2 *tiles;      // MFMA tiles of the grouped pairs
   int32_t *ntiles;
+  float *xn;        // [S][D] normalized rows (batch path with MOE_F_PRENORM)
 };
 
 }  // namespace moe

@@ -80,16 +80,24 @@ struct DecodeArgs {
   int32_t *acc_d;           // optional [S][D]
   int8_t *hq_nat;           // optional [S][I]
   float *sh_out;            // optional [S]
+  const float *gamma;       // optional [D]: phase A works on RMSNorm(x) with gamma, eps
+  float eps;
 };
 
 // Grouped (unique-expert union) kernels.
 struct GroupArgs {
-  const int32_t *idx;
+  int32_t *idx;           // [S][K]: read, or written when with_topk
   int S, E, K, P, n_shared;
   int32_t *gcount, *goff, *pairs;
   int2 *tiles;            // optional: (group, first pair) of every tile of tile_rows pairs
   int32_t *ntiles;        // number of tiles
   int tile_rows;
+  // with_topk: the kernel first runs each token's top-K rounds itself (one
+  // wave per token) from logits and bias into idx and wts
+  int with_topk;
+  const float *logits, *bias;
+  float scale;
+  float *wts;
 };
 
 // Grouped int8 MFMA GEMM of the union path (grouped_mfma.hip); mode 0 is
@@ -181,7 +189,8 @@ hipError_t launch_grouped_gateup(const GroupedGateUpArgs &a, hipStream_t st);
 // The MFMA form applies when the contraction length is a multiple of 256.
 bool grouped_mfma_fits(int C);
 constexpr int kGroupedMfmaTile = 128;  // pairs per tile
-constexpr int kRouterTileMinTokens = 256;  // batches from this size use the 8x8 router tiles
+constexpr int kRouterTileMinTokens = 256;
+constexpr int kGroupTopkMaxTokens = 64;  // batches up to this size select inside group_kernel  // batches from this size use the 8x8 router tiles
 int grouped_mfma_max_tiles(int S, int P, int E);
 hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, int S, hipStream_t st);
 hipError_t launch_grouped_down(const GroupedDownArgs &a, hipStream_t st);

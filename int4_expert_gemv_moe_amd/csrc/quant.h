@@ -5,13 +5,16 @@
 #pragma once
 
 #include "moe_common.h"
+#include "norm.h"
 
 namespace moe {
 
 // ---- activation quantization (one block per row) ---------------------------
 
+// gamma (optional, with xf): quantize the RMSNorm (x * r) * gamma of the row.
 __device__ inline void quant_row_block(const float *xf, const uint16_t *xb, int D, int8_t *xq_perm,
-                                int8_t *xq_nat, float *sx_out, int32_t *sumx_out) {
+                                int8_t *xq_nat, float *sx_out, int32_t *sumx_out,
+                                const float *gamma = nullptr, float r = 0.f) {
   __shared__ float red_f[16];  // one slot per wave, blocks of up to 1024 threads
   __shared__ int red_i[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -22,6 +25,10 @@ __device__ inline void quant_row_block(const float *xf, const uint16_t *xb, int 
     if (xf) {
       float4 a = reinterpret_cast<const float4 *>(xf)[2 * g];
       float4 b = reinterpret_cast<const float4 *>(xf)[2 * g + 1];
+      if (gamma) {
+        a = norm4(a, reinterpret_cast<const float4 *>(gamma)[2 * g], r);
+        b = norm4(b, reinterpret_cast<const float4 *>(gamma)[2 * g + 1], r);
+      }
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
       uint4 r = reinterpret_cast<const uint4 *>(xb)[g];
@@ -51,6 +58,10 @@ __device__ inline void quant_row_block(const float *xf, const uint16_t *xb, int 
     if (xf) {
       float4 a = reinterpret_cast<const float4 *>(xf)[2 * g];
       float4 b = reinterpret_cast<const float4 *>(xf)[2 * g + 1];
+      if (gamma) {
+        a = norm4(a, reinterpret_cast<const float4 *>(gamma)[2 * g], r);
+        b = norm4(b, reinterpret_cast<const float4 *>(gamma)[2 * g + 1], r);
+      }
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
       uint4 r = reinterpret_cast<const uint4 *>(xb)[g];
@@ -92,14 +103,20 @@ __device__ inline void quant_row_block(const float *xf, const uint16_t *xb, int 
 // owns groups t + NT*k: quant_row_load issues its loads (so the caller can
 // put other loads behind them), quant_row_block_lds does the rest.
 // Returns the code sum on every thread; *sx receives the scale.
-template <int NCH, int NT = 256>
-__device__ __forceinline__ void quant_row_load(const float *x, int D, float4 (&v)[NCH][2]) {
+// NORM: the row is x's RMSNorm (x * r) * gamma.
+template <int NCH, int NT = 256, bool NORM = false>
+__device__ __forceinline__ void quant_row_load(const float *x, int D, float4 (&v)[NCH][2],
+                                               const float *gamma = nullptr, float r = 0.f) {
   const int ngroups = D >> 3;
 #pragma unroll
   for (int k = 0; k < NCH; k++) {
     const int g = min((int)threadIdx.x + NT * k, ngroups - 1);
     v[k][0] = reinterpret_cast<const float4 *>(x)[2 * g];
     v[k][1] = reinterpret_cast<const float4 *>(x)[2 * g + 1];
+    if (NORM) {
+      v[k][0] = norm4(v[k][0], reinterpret_cast<const float4 *>(gamma)[2 * g], r);
+      v[k][1] = norm4(v[k][1], reinterpret_cast<const float4 *>(gamma)[2 * g + 1], r);
+    }
   }
 }
 

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "moe_common.h"
+#include "norm.h"
 
 namespace moe {
 
@@ -41,11 +42,15 @@ __device__ __forceinline__ void split_rows(int n, int nb, int b, int &r0, int &r
 // fmaf(x[k], W[e][k], acc) for k = 4p + 256j + q, j then q ascending, and the
 // lanes are summed by wave_sum_f32.  D % 256 == 0.  Every lane returns the
 // logit.
-__device__ inline float router_dot(const float *x, const float *w, int D) {
+// NORM: x is the raw row and the dot uses its RMSNorm (x * r) * gamma.
+template <bool NORM = false>
+__device__ inline float router_dot(const float *x, const float *w, int D,
+                                   const float *gamma = nullptr, float r = 0.f) {
   const int lane = threadIdx.x & 63;
   constexpr int JB = 24;
   const float4 *wr = reinterpret_cast<const float4 *>(w);
   const float4 *xr = reinterpret_cast<const float4 *>(x);
+  const float4 *gr = reinterpret_cast<const float4 *>(gamma);
   const int nj = D >> 8;
   float acc = 0.f;
   for (int j0 = 0; j0 < nj; j0 += JB) {
@@ -59,6 +64,7 @@ __device__ inline float router_dot(const float *x, const float *w, int D) {
         wv[jj] = make_float4(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z),
                              __uint_as_float(t.w));
         xv[jj] = xr[lane + 64 * (j0 + jj)];
+        if (NORM) xv[jj] = norm4(xv[jj], gr[lane + 64 * (j0 + jj)], r);
       }
     }
 #pragma unroll

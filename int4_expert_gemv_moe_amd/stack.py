@@ -2,9 +2,11 @@
 section 04 of the reader.mx article "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型":
 for every layer, x <- x + block(rmsnorm(x)).
 
-Each layer is two library calls on the caller's stream: moe_rmsnorm into a
-scratch row block, then moe_layer_forward (or moe_layer_forward_batch, the
-unique-expert union) with MOE_F_ACCUMULATE into x.  The calls take prebuilt
+Each layer is one library call on the caller's stream: moe_layer_forward (or
+moe_layer_forward_batch, the unique-expert union) with MOE_F_PRENORM and
+MOE_F_ACCUMULATE on x in place; the per-token path normalizes inside its
+first launch.  With fused=False the normalization is a moe_rmsnorm call
+into a scratch row block first (the same bits).  The calls take prebuilt
 argument structs, so a step is cheap to issue and can be captured in a HIP
 graph as it is.
 """
@@ -14,7 +16,7 @@ import ctypes
 
 import torch
 
-from . import F_ACCUMULATE, DeviceLayer, MoeError, Probe, Workspace, _check, _dev, lib
+from . import F_ACCUMULATE, F_PRENORM, DeviceLayer, MoeError, Probe, Workspace, _check, _dev, lib
 
 
 class Stack:
@@ -32,39 +34,45 @@ class Stack:
         self.cfg = cfg
         self.gamma = gamma
         self.eps = float(eps)
-        self._lc = [l.cstruct() for l in layers]  # kept alive for the calls
+        self._lc = [l.cstruct(gamma, self.eps) for l in layers]  # kept alive for the calls
 
     def forward(self, x: torch.Tensor, ws: Workspace, xn: torch.Tensor | None = None,
                 union: bool = False, stream=None, taps: list | None = None,
-                topk_idx: list | None = None) -> torch.Tensor:
+                topk_idx: list | None = None, fused: bool = True) -> torch.Tensor:
         """Runs every layer on x [S][D] (float32, updated in place).
 
-        xn: scratch of x's shape (allocated if omitted).  union: use the
-        unique-expert union path.  taps[l] (optional tensors of x's shape)
-        receive x before layer l, topk_idx[l] (int32 [S][K]) its selection;
-        both are written on the given stream."""
+        union: use the unique-expert union path.  fused: normalize inside the
+        layer call (else a separate moe_rmsnorm into xn, allocated if
+        omitted).  taps[l] (optional tensors of x's shape) receive x before
+        layer l, topk_idx[l] (int32 [S][K]) its selection; both are written
+        on the given stream."""
         _dev(x, torch.float32, "x")
         S, D = x.shape
         if D != self.cfg.D:
             raise MoeError("x has the wrong width")
-        xn = torch.empty_like(x) if xn is None else xn
+        if not fused:
+            xn = torch.empty_like(x) if xn is None else xn
         L = lib()
         fn = L.moe_layer_forward_batch if union else L.moe_layer_forward
         s = torch.cuda.current_stream() if stream is None else stream
         st = ctypes.c_void_p(s.cuda_stream)
-        xp, xnp, gp = ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(xn.data_ptr()), \
-            ctypes.c_void_p(self.gamma.data_ptr())
+        xp, gp = ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(self.gamma.data_ptr())
+        xnp = None if fused else ctypes.c_void_p(xn.data_ptr())
         cref = ctypes.byref(self.cfg)
         for i, lc in enumerate(self._lc):
             if taps is not None:
                 with torch.cuda.stream(s):
                     taps[i].copy_(x)
-            _check(L.moe_rmsnorm(xp, gp, S, D, self.eps, xnp, st), "moe_rmsnorm")
             probe = None
             if topk_idx is not None:
                 p = Probe()
                 p.topk_idx = topk_idx[i].data_ptr()
                 probe = ctypes.byref(p)
-            _check(fn(cref, ctypes.byref(lc), xnp, S, xp, F_ACCUMULATE, probe, ws.ptr, ws.nbytes,
-                      st), "moe_layer_forward")
+            if fused:
+                _check(fn(cref, ctypes.byref(lc), xp, S, xp, F_ACCUMULATE | F_PRENORM, probe, ws.ptr,
+                          ws.nbytes, st), "moe_layer_forward")
+            else:
+                _check(L.moe_rmsnorm(xp, gp, S, D, self.eps, xnp, st), "moe_rmsnorm")
+                _check(fn(cref, ctypes.byref(lc), xnp, S, xp, F_ACCUMULATE, probe, ws.ptr, ws.nbytes,
+                          st), "moe_layer_forward")
         return x

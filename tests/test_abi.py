@@ -77,3 +77,33 @@ def test_host_validation_before_device():
     assert L.moe_quant_act_i8(buf, 5, 1, 8, buf, buf, None) == -1  # unknown dtype
     assert L.moe_quant_act_i8(buf, 0, 1, 12, buf, buf, None) == -2  # D % 8
     assert L.moe_rmsnorm(None, None, 1, 8, 1e-5, None, None) == -1
+
+
+def test_prenorm_flag_host_checks():
+    """MOE_F_PRENORM: gamma and eps are checked on the host, unknown flag bits
+    are refused, and out == x is accepted only with the flag (the calls stop
+    at the workspace check here, before any device work)."""
+    import numpy as np
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    cfg = moe.config(256, 128, 8, 2)
+    host = np.zeros(1 << 16, np.uint8)
+    base = host.ctypes.data + (-host.ctypes.data) % 256  # 256-byte aligned host address
+    q = moe.QMat(base, base, 0, 0)
+    ex = moe.Experts(q, q, q)
+    layer = moe.LayerC(base, base, ex, ex, base, 1e-5)
+    x = ctypes.c_void_p(base)
+    ws = ctypes.c_void_p(base)
+    for fn in (L.moe_layer_forward, L.moe_layer_forward_batch):
+        def call(flags, out=x, lay=layer):
+            return fn(ctypes.byref(cfg), ctypes.byref(lay), x, 1, out, flags, None, ws, 256, None)
+        assert call(4) == -1                                   # unknown flag bit
+        assert call(moe.F_ACCUMULATE) == -1                    # out overlaps x without the flag
+        assert call(moe.F_ACCUMULATE | moe.F_PRENORM) == -4    # in place: only the workspace is short
+        no_gamma = moe.LayerC(base, base, ex, ex, None, 1e-5)
+        assert call(moe.F_PRENORM, lay=no_gamma) == -1
+        for eps in (0.0, -1.0, float("inf"), float("nan")):
+            assert call(moe.F_PRENORM, lay=moe.LayerC(base, base, ex, ex, base, eps)) == -1
+        assert call(moe.F_PRENORM, lay=moe.LayerC(base, base, ex, ex, base + 4, 1e-5)) == -3
+        # out inside x but not equal to it stays refused
+        assert call(moe.F_ACCUMULATE | moe.F_PRENORM, out=ctypes.c_void_p(base + 16)) == -1

@@ -80,6 +80,32 @@ def test_accumulate_flag_and_residual():
         assert np.array_equal(got, base + plain)
 
 
+@pytest.mark.parametrize("shape,S,path", [(MID, 3, "fwd"), (MID, 6, "batch"), (GLM, 1, "fwd"),
+                                          (GLM, 4, "batch")])
+def test_prenorm_in_place_matches_separate_rmsnorm(shape, S, path):
+    """MOE_F_PRENORM with out == x (one in-place decoder-layer update) gives
+    the same bits as moe_rmsnorm into a scratch block followed by the plain
+    call with MOE_F_ACCUMULATE; without accumulation, the same bits as the
+    plain call on the normalized rows."""
+    say(f"prenorm {path} D={shape.D} S={S}")
+    b = bias_for("uniform", 4, shape)
+    dl = device_layer(4, shape, 0, b)
+    x0 = torch.from_numpy(synth.activations(12, S, shape.D)).cuda()
+    gamma = torch.from_numpy((1.0 + 0.1 * synth.activations(13, 1, shape.D)[0]).astype(np.float32)).cuda()
+    ws = moe.Workspace(dl.cfg, S, moe.WS_FORWARD if path == "fwd" else moe.WS_BATCH)
+    fn = moe.moe_layer_forward if path == "fwd" else moe.moe_layer_forward_batch
+    xn = moe.moe_rmsnorm(x0, gamma, 1e-5)
+    ref = x0.clone()
+    fn(dl, xn, ws, out=ref, flags=moe.F_ACCUMULATE)
+    y = x0.clone()
+    fn(dl, y, ws, out=y, flags=moe.F_ACCUMULATE, norm_gamma=gamma, norm_eps=1e-5)
+    plain = fn(dl, xn, ws)
+    fused = fn(dl, x0, ws, norm_gamma=gamma, norm_eps=1e-5)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(y).view(np.uint32), to_np(ref).view(np.uint32))
+    assert np.array_equal(to_np(fused).view(np.uint32), to_np(plain).view(np.uint32))
+
+
 def test_glm_decode_tokens():
     """GLM shape, one token per call (the decode step), several tokens."""
     b = bias_for("uniform", 0, GLM)
