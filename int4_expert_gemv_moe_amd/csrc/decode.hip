@@ -127,9 +127,12 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
     __shared__ __align__(16) int8_t xcodes[2048 * 4];
     float4 xr[NCH][2];
     if (a.gamma) {
-      // the first weight stage goes out before the normalization
+      // the token row and gain, then the first weight stage, are in flight
+      // together; the normalization waits only for the former
+      NormRow nr;
+      norm_row_load(a.x + (int64_t)s * a.D, a.gamma, a.D, nr);
       gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
-      prenorm_to_lds(a.x + (int64_t)s * a.D, a.gamma, a.D, a.eps, xn);
+      prenorm_finish_lds(nr, a.D, a.eps, xn);
       quant_row_load<NCH>(xn, a.D, xr);
     } else {
       quant_row_load<NCH>(a.x + (int64_t)s * a.D, a.D, xr);
@@ -479,7 +482,9 @@ __global__ __launch_bounds__(256) void decode_a_kernel(DecodeArgs a) {
   const int s = blockIdx.y, b = blockIdx.x;
   const float *xrow = a.x + (int64_t)s * a.D;
   if (b < a.n_router + a.n_quant && a.gamma) {
-    prenorm_to_lds(xrow, a.gamma, a.D, a.eps, xn_dyn);
+    NormRow nr;
+    norm_row_load(xrow, a.gamma, a.D, nr);
+    prenorm_finish_lds(nr, a.D, a.eps, xn_dyn);
     xrow = xn_dyn;
   }
   if (b < a.n_router) {

@@ -45,15 +45,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(RmsArgs a) {
   const float *x = a.x + (int64_t)blockIdx.x * a.D;
   float *y = a.y + (int64_t)blockIdx.x * a.D;
   if (a.vec) {
-    const float r = rms_factor_256(x, a.D, a.eps, red);
-    const int n4 = a.D / 4;
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const int i = tid + 256 * k;
-      if (i < n4)
-        reinterpret_cast<float4 *>(y)[i] = norm4(reinterpret_cast<const float4 *>(x)[i],
-                                                 reinterpret_cast<const float4 *>(a.gamma)[i], r);
-    }
+    NormRow nr;
+    norm_row_load(x, a.gamma, a.D, nr);
+    norm_row_store(nr, a.D, norm_row_factor(nr, a.D, a.eps, red), y);
     return;
   }
   double ms = 0.0;

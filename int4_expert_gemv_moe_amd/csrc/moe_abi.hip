@@ -183,8 +183,11 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 // Router logits (+ activation quantization); the top-K runs in a kernel of
 // its own when with_topk, otherwise inside the per-token gate/up kernel.
 int run_router(const moe_config &c, const float *x, int S, const float *W, const float *b,
-               const Work &w, bool with_quant, bool with_topk, float *logits_out, hipStream_t st) {
+               const Work &w, bool with_quant, bool with_topk, float *logits_out, hipStream_t st,
+               const float *gamma = nullptr, float eps = 0.f) {
   RouterArgs r{};
+  r.gamma = gamma;
+  r.eps = eps;
   r.x = x;
   r.W = W;
   r.S = S;
@@ -441,18 +444,25 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
   const int P = c.K + c.n_shared;
   Work w;
   carve(c, S, W_BATCH, (char *)ws, &w);
+  // x (maybe out itself) is read by the router launch and nowhere else.
+  // With MOE_F_PRENORM, batches of up to 8 tokens normalize inside the
+  // router's workgroups; larger ones get the normalized rows in the
+  // workspace first.
+  const float *gamma = nullptr;
   if (flags & MOE_F_PRENORM) {
-    // the normalized rows go to the workspace; x (maybe out itself) is read
-    // here and nowhere else
-    RmsArgs ra{x, layer->norm_gamma, c.D, layer->norm_eps, w.xn, 1};
-    MOE_TRY_HIP(launch_rmsnorm(ra, S, stream));
-    x = w.xn;
+    if (S <= 8) {
+      gamma = layer->norm_gamma;
+    } else {
+      RmsArgs ra{x, layer->norm_gamma, c.D, layer->norm_eps, w.xn, 1};
+      MOE_TRY_HIP(launch_rmsnorm(ra, S, stream));
+      x = w.xn;
+    }
     flags &= ~MOE_F_PRENORM;
   }
   // small batches select inside the grouping kernel (one launch fewer)
   const bool topk_in_group = S <= kGroupTopkMaxTokens && c.E <= 256;
   MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, !topk_in_group, nullptr,
-                     stream));
+                     stream, gamma, layer->norm_eps));
   const bool mfma_gu = grouped_mfma_fits(c.D), mfma_dn = grouped_mfma_fits(c.I);
   const int max_tiles = grouped_mfma_max_tiles(S, P, c.E);
   GroupArgs ga{w.idx,    S,     c.E,     c.K,      P, c.n_shared, w.gcount, w.goff, w.pairs,

@@ -26,6 +26,8 @@ struct RouterArgs {
   int32_t *sumx;
   uint32_t *amax;      // optional [S][P]: cleared by the quantization blocks
   int P;
+  const float *gamma;  // optional [D] (one-token-per-block launches only): work on RMSNorm(x)
+  float eps;
 };
 
 struct PrepArgs {

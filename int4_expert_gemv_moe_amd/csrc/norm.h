@@ -29,22 +29,37 @@ inline bool rms_vec_ok(int D, const void *x, const void *gamma) {
   return D % 4 == 0 && D <= 8192 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)gamma % 16) == 0;
 }
 
-// The factor r of row x by a whole 256-thread block (every thread gets it).
-// Thread t sums the squares of float4s t, t + 256, ... in that order, each
-// float4's components x, y, z, w in order.
-__device__ inline float rms_factor_256(const float *x, int D, float eps, double *red) {
-  const int tid = threadIdx.x, n4 = D / 4;
-  float4 xv[8];
+// One row in the registers of a 256-thread block: thread t holds float4s
+// t, t + 256, ... (up to 8) of x and of gamma.  norm_row_load only issues
+// the loads, so that a caller can put other loads behind them.
+struct NormRow {
+  float4 xv[8], gv[8];
+};
+
+__device__ __forceinline__ void norm_row_load(const float *x, const float *gamma, int D,
+                                              NormRow &nr) {
+  const int n4 = D / 4;
 #pragma unroll
-  for (int k = 0; k < 8; k++) xv[k] = reinterpret_cast<const float4 *>(x)[min(tid + 256 * k, n4 - 1)];
+  for (int k = 0; k < 8; k++) {
+    const int i = min((int)threadIdx.x + 256 * k, n4 - 1);
+    nr.xv[k] = reinterpret_cast<const float4 *>(x)[i];
+    nr.gv[k] = reinterpret_cast<const float4 *>(gamma)[i];
+  }
+}
+
+// The factor r = 1 / sqrt(mean(x^2) + eps) of the loaded row, on every
+// thread.  Thread t sums the squares of its float4s in order (components
+// x, y, z, w), then block_sum_f64.
+__device__ inline float norm_row_factor(const NormRow &nr, int D, float eps, double *red) {
+  const int n4 = D / 4;
   double ms = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; k++) {
-    if (tid + 256 * k < n4) {
-      ms += (double)xv[k].x * (double)xv[k].x;
-      ms += (double)xv[k].y * (double)xv[k].y;
-      ms += (double)xv[k].z * (double)xv[k].z;
-      ms += (double)xv[k].w * (double)xv[k].w;
+    if ((int)threadIdx.x + 256 * k < n4) {
+      ms += (double)nr.xv[k].x * (double)nr.xv[k].x;
+      ms += (double)nr.xv[k].y * (double)nr.xv[k].y;
+      ms += (double)nr.xv[k].z * (double)nr.xv[k].z;
+      ms += (double)nr.xv[k].w * (double)nr.xv[k].w;
     }
   }
   const double t = block_sum_f64(ms, red);
@@ -55,20 +70,21 @@ __device__ __forceinline__ float4 norm4(float4 x, float4 g, float r) {
   return make_float4(x.x * r * g.x, x.y * r * g.y, x.z * r * g.z, x.w * r * g.w);
 }
 
-// RMSNorm of row x into shared memory dst (D floats, 16-byte aligned) by a
-// whole 256-thread block; dst is complete for every thread on return.
-__device__ inline void prenorm_to_lds(const float *x, const float *gamma, int D, float eps,
-                                      float *dst) {
-  __shared__ double red[4];
-  const float r = rms_factor_256(x, D, eps, red);
+// The normalized row (x * r) * gamma to dst (global or shared memory).
+__device__ __forceinline__ void norm_row_store(const NormRow &nr, int D, float r, float *dst) {
   const int n4 = D / 4;
 #pragma unroll
   for (int k = 0; k < 8; k++) {
     const int i = threadIdx.x + 256 * k;
-    if (i < n4)
-      reinterpret_cast<float4 *>(dst)[i] = norm4(reinterpret_cast<const float4 *>(x)[i],
-                                                 reinterpret_cast<const float4 *>(gamma)[i], r);
+    if (i < n4) reinterpret_cast<float4 *>(dst)[i] = norm4(nr.xv[k], nr.gv[k], r);
   }
+}
+
+// Loaded row -> RMSNorm row in shared memory dst (D floats, 16-byte
+// aligned), complete for every thread on return.
+__device__ inline void prenorm_finish_lds(const NormRow &nr, int D, float eps, float *dst) {
+  __shared__ double red[4];
+  norm_row_store(nr, D, norm_row_factor(nr, D, eps, red), dst);
   __syncthreads();
 }
 

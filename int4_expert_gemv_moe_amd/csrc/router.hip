@@ -16,6 +16,7 @@
 #include "moe_kernels.h"
 #include "topk.h"
 #include "quant.h"
+#include "norm.h"
 
 namespace moe {
 
@@ -70,20 +71,32 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 // Block = 4 waves = 4 experts; TS tokens per block; JB 16-byte loads of the
 // expert row per lane issued together.  Blocks with index >= n_router
 // quantize token (index - n_router) and clear its amax slots.
+// With a.gamma (TS == 1 launches) every workgroup first forms its token's
+// RMSNorm row in dynamic shared memory and works on that.
 template <int TS, int JB>
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
+  extern __shared__ __align__(16) float xn_dyn[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ne4 = (a.E + 3) >> 2;
   const int n_router = ne4 * ((a.S + TS - 1) / TS);
-  if ((int)blockIdx.x >= n_router) {
-    const int s = blockIdx.x - n_router;
+  const bool quant = (int)blockIdx.x >= n_router;
+  const int e = (blockIdx.x % ne4) * 4 + wave;
+  const int s0 = quant ? blockIdx.x - n_router : (blockIdx.x / ne4) * TS;
+  const bool normed = TS == 1 && a.gamma;
+  if (normed) {
+    NormRow nr;
+    norm_row_load(a.x + (int64_t)s0 * a.D, a.gamma, a.D, nr);
+    prenorm_finish_lds(nr, a.D, a.eps, xn_dyn);
+  }
+  // token row s as the block sees it (the normalized row of token s0 when normed)
+  auto xrow = [&](int s) { return normed ? (const float *)xn_dyn : a.x + (int64_t)s * a.D; };
+  if (quant) {
+    const int s = s0;
     if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
-    quant_row_block(a.x + (int64_t)s * a.D, nullptr, a.D, a.xq_perm + (int64_t)s * a.D, nullptr,
-                    a.sx + s, a.sumx + s);
+    quant_row_block(xrow(s), nullptr, a.D, a.xq_perm + (int64_t)s * a.D, nullptr, a.sx + s,
+                    a.sumx + s);
     return;
   }
-  const int e = (blockIdx.x % ne4) * 4 + wave;
-  const int s0 = (blockIdx.x / ne4) * TS;
   if (e >= a.E) return;
   float acc[TS];
 #pragma unroll
@@ -100,7 +113,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 #pragma unroll
     for (int t = 0; t < TS; t++) {
       if (s0 + t < a.S) {
-        const float4 *xr = reinterpret_cast<const float4 *>(a.x + (int64_t)(s0 + t) * a.D);
+        const float4 *xr = reinterpret_cast<const float4 *>(xrow(s0 + t));
         float4 xv[JB];
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) {
@@ -222,7 +235,8 @@ hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
   // loads (rows are re-read per token from L2); a few dozen: 8 tokens share
   // each weight load; hundreds: 8 x 8 register tiles
   if (a.S <= 8) {
-    hipLaunchKernelGGL((router_kernel<1, 24>), dim3(ne4 * a.S + nq), dim3(256), 0, st, a);
+    const size_t lds = a.gamma ? (size_t)a.D * 4 : 0;  // the normalized row
+    hipLaunchKernelGGL((router_kernel<1, 24>), dim3(ne4 * a.S + nq), dim3(256), lds, st, a);
   } else if (a.S < kRouterTileMinTokens) {
     hipLaunchKernelGGL((router_kernel<8, 4>), dim3(ne4 * ((a.S + 7) / 8) + nq), dim3(256), 0, st, a);
   } else {

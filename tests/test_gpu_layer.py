@@ -80,8 +80,8 @@ def test_accumulate_flag_and_residual():
         assert np.array_equal(got, base + plain)
 
 
-@pytest.mark.parametrize("shape,S,path", [(MID, 3, "fwd"), (MID, 6, "batch"), (GLM, 1, "fwd"),
-                                          (GLM, 4, "batch")])
+@pytest.mark.parametrize("shape,S,path", [(MID, 3, "fwd"), (MID, 6, "batch"), (MID, 20, "batch"),
+                                          (GLM, 1, "fwd"), (GLM, 4, "batch")])
 def test_prenorm_in_place_matches_separate_rmsnorm(shape, S, path):
     """MOE_F_PRENORM with out == x (one in-place decoder-layer update) gives
     the same bits as moe_rmsnorm into a scratch block followed by the plain
