@@ -45,9 +45,11 @@ COPY_CAL_BYTES = 256 << 20
 # the hash of the kernel source it was taken on)
 TRAFFIC_FILES = {k: os.path.join(ROOT, "profiles", f"{k}_glm_decode_traffic.md")
                  for k in ("decode_b_kernel",)}
+# device code of the decode kernels (the counter summaries are valid while
+# these files are unchanged)
 KERNEL_SOURCES = [os.path.join(ROOT, "int4_expert_gemv_moe_amd", "csrc", f)
                   for f in ("decode.hip", "rowops.h", "moe_common.h", "quant.h", "topk.h",
-                            "moe_kernels.h", "moe_abi.hip")]
+                            "norm.h")]
 D, I, E, K = 6144, 2048, 256, 8
 EXPERT_GATEUP_BYTES = 2 * I * (D // 2) + 2 * I * 4          # 12,599,296
 EXPERT_DOWN_BYTES = D * (I // 2) + D * 4                     # 6,316,032

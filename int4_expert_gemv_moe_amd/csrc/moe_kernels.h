@@ -191,8 +191,9 @@ hipError_t launch_grouped_gateup(const GroupedGateUpArgs &a, hipStream_t st);
 // The MFMA form applies when the contraction length is a multiple of 256.
 bool grouped_mfma_fits(int C);
 constexpr int kGroupedMfmaTile = 128;  // pairs per tile
-constexpr int kRouterTileMinTokens = 256;
-constexpr int kGroupTopkMaxTokens = 64;  // batches up to this size select inside group_kernel  // batches from this size use the 8x8 router tiles
+constexpr int kRouterTileMinTokens = 256;  // batches from this size use the 8x8 router tiles
+// batches up to this size select inside group_kernel (one wave per token)
+constexpr int kGroupTopkMaxTokens = 16;
 int grouped_mfma_max_tiles(int S, int P, int E);
 hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, int S, hipStream_t st);
 hipError_t launch_grouped_down(const GroupedDownArgs &a, hipStream_t st);
