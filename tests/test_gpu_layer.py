@@ -53,7 +53,13 @@ def test_tiny_block(path):
                                           (MID, 5, "uniform"), (MID, 64, "zero"),
                                           (synth.Shape(D=512, I=256, E=8, K=8), 7, "uniform"),
                                           (synth.Shape(D=256, I=128, E=8, K=2, n_shared=0), 9,
-                                           "uniform")])
+                                           "uniform"),
+                                          # K > 8: two routed-down launches per token
+                                          (synth.Shape(D=256, I=128, E=64, K=16), 5, "uniform"),
+                                          # E > 256: the 16-entry lists of the selection
+                                          (synth.Shape(D=256, I=128, E=512, K=8), 6, "uniform"),
+                                          # I % 256 != 0: GEMV down, masked row tails
+                                          (synth.Shape(D=256, I=384, E=16, K=4), 3, "uniform")])
 def test_batch_union_equals_per_token_bit_exact(shape, S, bias):
     b = bias_for(bias, 1, shape)
     dl = device_layer(1, shape, 0, b)
