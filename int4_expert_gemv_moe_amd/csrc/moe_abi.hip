@@ -66,7 +66,7 @@ DecodeShape decode_shape(const moe_config &c) {
   DecodeShape d;
   d.gu_fx = env.gu_fx > 0 ? env.gu_fx : 128;
   d.gu_rt = env.gu_rt > 0 ? env.gu_rt : 256;
-  d.dn_fx = env.dn_fx > 0 ? env.dn_fx : 128;
+  d.dn_fx = env.dn_fx > 0 ? env.dn_fx : 192;
   // phase C: one pass of rows per workgroup
   const int cr = decode_c_rows_per_pass(c.I);
   d.dn = env.dn > 0 ? env.dn : (c.D + cr - 1) / cr;
