@@ -29,9 +29,11 @@
  *     moe_workspace_init; every call leaves its counters at zero again.  Calls
  *     that share one workspace must not overlap (use one workspace per
  *     concurrent stream).
- *   - Shape limits: D and I multiples of 32, 1 <= K <= E <= 1024, K <= 64,
- *     n_shared 0 or 1, S >= 1.  q4, scale and activation buffers must be
- *     16-byte aligned.  The device must be a gfx950.
+ *   - Shape limits: D a multiple of 256 (the router's lane order), I a
+ *     multiple of 32, D/2 and I/2 at most 4096 bytes per packed row,
+ *     1 <= K <= E <= 1024, K <= 64, n_shared 0 or 1, S >= 1 (MOE_ESHAPE
+ *     otherwise).  q4, scale and activation buffers must be 16-byte aligned.
+ *     The device must be a gfx950.
  */
 #ifndef MOE_I4_H
 #define MOE_I4_H
