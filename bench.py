@@ -195,6 +195,10 @@ def bench_verify(layer, iters: int = 20):
                         "unique-expert union",
             "us": round(us, 1), "us_per_token": round(us / S, 2),
             "union_routed_experts": used - 1, "hottest_expert_tokens": int(counts.max()),
+            "popularity_top8": [int(c) for c in np.sort(counts)[::-1][:8]],
+            "experts_by_tokens": {"1": int((counts == 1).sum()), "2-3": int(((counts >= 2) & (counts <= 3)).sum()),
+                                  "4-15": int(((counts >= 4) & (counts <= 15)).sum()),
+                                  "16+": int((counts >= 16).sum())},
             "hbm_bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
             "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
 
@@ -214,7 +218,8 @@ def bench_stack(steps: int = 64):
     from synth.device_layers import build_device_layer
 
     with open(os.path.join(ROOT, "tests", "golden", "stack_beta.json")) as f:
-        beta = _json.load(f)["beta"]
+        cal = _json.load(f)
+    beta = cal["beta"]
     t0 = time.time()
     layers = [build_device_layer(0, synth.GLM, l, synth.zipf_bias(0, E, l, beta))
               for l in range(48)]
@@ -225,7 +230,8 @@ def bench_stack(steps: int = 64):
     res = {"workload": "48 GLM-shape MoE layers resident in HBM, one call per layer: "
                        "x <- x + block(RMSNorm(x)) in place (RMSNorm eps 1e-5 inside the call), "
                        f"per-layer Zipf(1.1)-skewed routing (bias strength {beta})",
-           "layers": 48}
+           "layers": 48, "bias_strength": beta, "target_zipf_exponent": cal["target_exponent"],
+           "calibrated_zipf_exponent": cal["fitted_exponent"]}
     for S, union in ((1, False), (4, True)):
         x0 = torch.from_numpy(synth.activations(0, S, D, item=70 + S)).cuda()
         x = x0.clone()
@@ -253,6 +259,32 @@ def bench_stack(steps: int = 64):
     res["batch1"]["frac_of_hbm_peak"] = round(res["batch1"]["hbm_GBps"] / HBM_PEAK_GBPS, 4)
     del g, stack, layers
     return res
+
+
+def hbm_read_probe(nbytes: int = 4 << 30, reps: int = 5):
+    """Same-box reference for the HBM rates: the library's read-only stream
+    (moe_stream_read, the decode kernels' load pattern) over 4 GiB, far
+    beyond the 256 MB MALL; best of reps."""
+    import torch
+
+    import int4_expert_gemv_moe_amd as moe
+
+    big = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    moe.moe_stream_read(big)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        moe.moe_stream_read(big)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3
+        best = us if best is None else min(best, us)
+    del big
+    torch.cuda.empty_cache()
+    return {"GBps": round(nbytes / best / 1e3, 1), "kernel": "moe_stream_read over 4 GiB",
+            "bytes": nbytes}
 
 
 def main():
@@ -348,6 +380,7 @@ def main():
     if args.no_graph:
         G = 0
     graph_us = None
+    graph_spread = None
     if G:
         try:
             n_graphs = max(1, min(K // G, (R * T) // G))
@@ -366,6 +399,20 @@ def main():
                 graphs[i % n_graphs].replay()
             torch.cuda.synchronize()
             graph_us = (time.perf_counter() - t_start) / K * 1e6
+            # spread over replays (each one graph of G steps, events around it)
+            reps = min(K // G, 64)
+            evr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            for i, (a, b) in enumerate(evr):
+                a.record(stream)
+                graphs[i % n_graphs].replay()
+                b.record(stream)
+            torch.cuda.synchronize()
+            per = np.array([a.elapsed_time(b) for a, b in evr]) * 1e3 / G
+            graph_spread = {"replays": reps, "steps_per_replay": G,
+                            "p10": round(float(np.percentile(per, 10)), 3),
+                            "p50": round(float(np.percentile(per, 50)), 3),
+                            "p90": round(float(np.percentile(per, 90)), 3)}
         except Exception as exc:  # a launch the graph capture does not take
             torch.cuda.synchronize()
             log(f"graph capture unavailable ({type(exc).__name__}: {exc}); timing stream launches")
@@ -414,6 +461,9 @@ def main():
     achieved = kbytes / (k_us * 1e-6) / 1e9
     log(f"layer {LAYER_TOKEN_BYTES / us_per_token / 1e3:.0f} GB/s")
 
+    probe = hbm_read_probe()
+    log(f"read probe {probe['GBps']} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
@@ -456,10 +506,13 @@ def main():
                    "global_batch": 1, "layer_replicas": R, "distinct_tokens": T},
         "tokens_per_s": round(1e6 / us_per_token, 1),
         "timing": (f"HIP graph replay, {G} steps per graph" if G else "stream launches"),
+        "us_per_token_spread": graph_spread,
         "stream_us_per_token": round(stream_us, 3),
         "layer_bytes_per_token": LAYER_TOKEN_BYTES,
         "layer_GBps": round(layer_gbps, 1),
         "layer_frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
+        "hbm_read_probe": probe,
+        "layer_frac_of_read_probe": round(layer_gbps / probe["GBps"], 4),
         "kernels_us": kernels_us,
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -187,6 +187,16 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
 int moe_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y,
                 hipStream_t stream);
 
+/* Measurement reference, not part of the block: reads buf[bytes] once with
+ * the library's streaming load pattern (16-byte nontemporal loads, 8 lanes
+ * per 128-byte segment) and leaves one xor word per workgroup in
+ * sink[moe_stream_read_sink_words()].  bytes must be a non-zero multiple of
+ * 16 and buf 16-byte aligned.  Timing it on a buffer far larger than the
+ * 256 MB MALL gives the device's read rate to compare the block's rates
+ * with. */
+int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+int moe_stream_read_sink_words(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -77,9 +77,11 @@ def lib():
         L.moe_layer_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp, vp]
+        L.moe_stream_read.argtypes = [vp, sz, vp, vp]
+        L.moe_stream_read_sink_words.argtypes = []
         for name in ("moe_workspace_init", "moe_pack_int4", "moe_quant_act_i8", "moe_router_topk",
                      "moe_expert_swiglu_i4", "moe_layer_forward", "moe_layer_forward_batch",
-                     "moe_rmsnorm"):
+                     "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -295,6 +297,15 @@ def moe_layer_forward_batch(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, 
     """Unique-expert union path: each selected expert is read once per call."""
     return _layer_call("moe_layer_forward_batch", layer, x, out, flags, ws, topk_idx, topk_w,
                        ev_gateup, ev_down, stream, norm_gamma, norm_eps)
+
+
+def moe_stream_read(buf: torch.Tensor, stream=None) -> torch.Tensor:
+    """Measurement reference: read buf once; returns the sink words."""
+    n = lib().moe_stream_read_sink_words()
+    sink = torch.empty(n, dtype=torch.int32, device=buf.device)
+    _check(lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 ctypes.c_void_p(_stream(stream))), "moe_stream_read")
+    return sink
 
 
 def moe_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out=None, stream=None):

@@ -57,6 +57,43 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(RmsArgs a) {
   for (int i = tid; i < a.D; i += blockDim.x) y[i] = x[i] * r * a.gamma[i];
 }
 
+// Read-only streaming reference: every byte of buf read once with 16-byte
+// nontemporal loads, 8 lanes per 128-byte segment, four loads in flight per
+// thread; one xor word per workgroup keeps the loads live.
+constexpr int kStreamBlocks = 4096;
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *buf, size_t n16,
+                                                          uint32_t *sink) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const u4v *p = reinterpret_cast<const u4v *>(buf);
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u4v a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + stride),
+              c = __builtin_nontemporal_load(p + i + 2 * stride),
+              d = __builtin_nontemporal_load(p + i + 3 * stride);
+    acc ^= (a.x ^ b.y) + (c.z ^ d.w) + (a.w ^ b.x) + (c.y ^ d.z);
+  }
+  for (; i < n16; i += stride) {
+    const u4v a = __builtin_nontemporal_load(p + i);
+    acc ^= a.x + a.y + a.z + a.w;
+  }
+  __shared__ uint32_t red[4];
+  for (int d = 32; d >= 1; d >>= 1) acc ^= __shfl_xor(acc, d, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamBlocks), dim3(256), 0, st,
+                     reinterpret_cast<const uint4 *>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+int stream_read_sink_words() { return kStreamBlocks; }
+
 hipError_t launch_pack(const PackArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(pack_kernel, dim3((a.O + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();

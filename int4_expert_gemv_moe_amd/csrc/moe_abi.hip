@@ -560,4 +560,14 @@ int moe_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, flo
   return hip_rc(launch_rmsnorm(a, S, stream));
 }
 
+int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  if (!buf || !sink) return MOE_EINVAL;
+  if (bytes == 0 || bytes % 16) return MOE_ESHAPE;
+  if (!aligned16(buf) || ((uintptr_t)sink & 3u)) return MOE_EALIGN;
+  MOE_TRY(check_device());
+  return hip_rc(launch_stream_read(buf, bytes, sink, stream));
+}
+
+int moe_stream_read_sink_words(void) { return stream_read_sink_words(); }
+
 }  // extern "C"

@@ -200,6 +200,8 @@ hipError_t launch_grouped_down(const GroupedDownArgs &a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_pack(const PackArgs &a, hipStream_t st);
 hipError_t launch_rmsnorm(const RmsArgs &a, int S, hipStream_t st);
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
+int stream_read_sink_words();
 
 // Row length C (int4 columns) supported by the GEMV kernels: C % 32 == 0 and
 // C/2 bytes either below 1024 or up to 4096.

@@ -164,3 +164,19 @@ def test_rmsnorm_matches_oracle(S, D, offset):
     moe.moe_rmsnorm(xt, gt, 1e-5, out=yt)
     torch.cuda.synchronize()
     np.testing.assert_allclose(to_np(yt), ref, rtol=2e-6, atol=1e-6)
+
+
+def test_stream_read_reference():
+    """The measurement reference reads the buffer (deterministic sink words,
+    sensitive to the data) and rejects misaligned or ragged buffers."""
+    buf = torch.arange(1 << 22, dtype=torch.int32, device="cuda")  # 16 MiB
+    s1 = moe.moe_stream_read(buf)
+    s2 = moe.moe_stream_read(buf)
+    buf[12345] += 1
+    s3 = moe.moe_stream_read(buf)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and not torch.equal(s1, s3)
+    with pytest.raises(moe.MoeError, match="misaligned"):
+        moe.moe_stream_read(buf[1:5])
+    with pytest.raises(moe.MoeError, match="shape"):
+        moe.moe_stream_read(buf[:3])
