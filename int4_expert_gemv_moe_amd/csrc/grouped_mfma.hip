@@ -58,19 +58,22 @@ __device__ __forceinline__ v4i unpack16(uint32_t w0, uint32_t w1) {
 struct MfmaTile {
   int rows;          // pairs of the tile
   int j, lane, wave;
-  RowPtr Bm[2];
-  int ob[2];         // output rows of the lane's two B subtiles
-  const uint8_t *bp[4];  // the lane's 16-byte piece of each coalesced weight load
+  RowPtr Bm[4];      // matrix of each of the wave's 16-row B subtiles
+  int ob[4];         // output row of the lane in each B subtile
+  const uint8_t *bbase[4];  // matrix base of each subtile (uniform)
+  int boff[8];       // byte offset of the lane's piece of each coalesced weight load
   int8_t *bs;        // the wave's weight transpose buffer in shared memory
 };
 
 constexpr int kBStride = 144;  // shared bytes per weight row of a step (128 + 16)
 
-// As: two activation buffers of ABUF bytes each.
-template <int MODE, int NW, int MSV, int ABUF>
+// As: two activation buffers of ABUF bytes each.  NS: 16-row B subtiles
+// per wave (2: 16 gate + 16 up rows, or 32 down rows; 4: twice that, so each
+// activation fragment read from shared memory feeds four MFMAs).
+template <int MODE, int NW, int NS, int MSV, int ABUF>
 __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTile &t, int8_t *As,
                                           const int *pr_l, const int *sum_l, const float *scl_l) {
-  constexpr int NS = 2;
+  constexpr int NI = 2 * NS;  // coalesced weight loads per step (8 rows each)
   constexpr int RPL = NW * 4;                  // pair rows staged per load round
   constexpr int NA = (MSV * 16 + RPL - 1) / RPL;  // 16-byte activation loads per thread per step
   const int C = a.C, O = a.O;
@@ -80,15 +83,15 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   // 16 * MSV repeat the tile's last pair: their products land only in
   // output rows that the epilogue skips.
   const int ar = threadIdx.x >> 4, aq = threadIdx.x & 15;
-  const int8_t *arow[NA];
+  int aoff[NA];  // byte offsets into a.act (rows * C < 2^31, checked on the host)
 #pragma unroll
   for (int i = 0; i < NA; i++) {
     const int apr = pr_l[min(RPL * i + ar, rows - 1)];
-    arow[i] = (MODE == 0 ? a.act + (int64_t)(apr / a.P) * C : a.act + (int64_t)apr * C) + 16 * aq;
+    aoff[i] = (MODE == 0 ? apr / a.P : apr) * C + 16 * aq;
   }
   auto load_a = [&](int k0, u4v (&v)[NA]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NA; i++) v[i] = *reinterpret_cast<const u4v *>(arow[i] + k0);
+    for (int i = 0; i < NA; i++) v[i] = *reinterpret_cast<const u4v *>(a.act + aoff[i] + k0);
   };
   auto store_a = [&](int buf, const u4v (&v)[NA]) __attribute__((always_inline)) {
 #pragma unroll
@@ -96,29 +99,32 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
       if (RPL * (i + 1) <= MSV * 16 || RPL * i + ar < MSV * 16)
         *reinterpret_cast<u4v *>(As + buf * ABUF + (RPL * i + ar) * kAStride + 16 * aq) = v[i];
   };
-  // Weights: the wave's 32 rows of a step (128 bytes each) arrive in four
+  // Weights: the wave's 16 NS rows of a step (128 bytes each) arrive in NI
   // coalesced loads, load i holding rows 8 i .. 8 i + 7 with 8 lanes per
   // row, and pass through the wave's own shared-memory buffer to reach the
   // MFMA operand layout (lane: one row, 32 bytes).
-  auto load_b = [&](int k0, uint4 (&bv)[4]) __attribute__((always_inline)) {
+  auto load_b = [&](int k0, uint4 (&bv)[NI]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) bv[i] = ldnt16(t.bp[i] + k0 / 2, true, t.bp[i]);
+    for (int i = 0; i < NI; i++) {
+      const uint8_t *p = t.bbase[i >> 1] + t.boff[i] + k0 / 2;  // load i is subtile i / 2
+      bv[i] = ldnt16(p, true, p);
+    }
   };
-  auto transpose_b = [&](const uint4 (&bv)[4], uint4 (&bm)[NS][2]) __attribute__((always_inline)) {
+  auto write_b = [&](const uint4 (&bv)[NI]) __attribute__((always_inline)) {
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < NI; i++)
       *reinterpret_cast<uint4 *>(t.bs + (8 * i + (lane >> 3)) * kBStride + 16 * (lane & 7)) = bv[i];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // half h of the step's weights in the MFMA layout: lane holds 16 bytes of
+  // row 16 s + lane % 16 of each subtile s
+  auto read_b = [&](int h, uint4 (&bm)[NS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < NS; s++)
-#pragma unroll
-      for (int h = 0; h < 2; h++)
-        bm[s][h] = *reinterpret_cast<const uint4 *>(t.bs + (16 * s + (lane & 15)) * kBStride + 32 * j +
-                                                    16 * h);
-    __builtin_amdgcn_wave_barrier();
+      bm[s] = *reinterpret_cast<const uint4 *>(t.bs + (16 * s + (lane & 15)) * kBStride + 32 * j + 16 * h);
   };
   v4i acc[MSV][NS];
 #pragma unroll
@@ -139,7 +145,12 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   // weights and refills their set with step s + 2, moves the activations of
   // step s + 1 to shared memory and refills their set with step s + 3, and
   // only then multiplies.
-  uint4 bw0[4], bw1[4];
+  // B1 (NS == 4, where registers are scarce): one register set of weights;
+  // the step's weights wait in the wave's shared buffer instead.  At the
+  // start of step s the buffer holds step s and bw step s + 1; after its
+  // multiplications the step moves bw to the buffer and loads step s + 2.
+  constexpr bool B1 = NS == 4;
+  uint4 bw0[NI], bw1[B1 ? 1 : NI];
   u4v ra0[NA], ra1[NA];
   // Loads past the last step repeat the last step's addresses: every load
   // is issued unconditionally, so the compiler's count of loads in flight
@@ -147,7 +158,12 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   const int last = (nsteps - 1) * kKS;
   load_b(0, bw0);
   load_a(0, ra0);
-  load_b(min(kKS, last), bw1);
+  if constexpr (B1) {
+    write_b(bw0);
+    load_b(min(kKS, last), bw0);
+  } else {
+    load_b(min(kKS, last), bw1);
+  }
   load_a(min(kKS, last), ra1);
   store_a(0, ra0);
   load_a(min(2 * kKS, last), ra0);
@@ -156,38 +172,39 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   // named statically
   auto step = [&](int st, auto hc) __attribute__((always_inline)) {
     constexpr int H = decltype(hc)::value;
-    // the step's weights, unpacked at once so that their registers take
-    // the loads of step s + 2 before the multiplications start
-    uint4 bm[NS][2];
-    if constexpr (H == 0)
-      transpose_b(bw0, bm);
-    else
-      transpose_b(bw1, bm);
-    v4i bb[4][NS];
-#pragma unroll
-    for (int c = 0; c < 4; c++)
-#pragma unroll
-      for (int s = 0; s < NS; s++) {
-        const uint4 w = bm[s][c >> 1];
-        bb[c][s] = (c & 1) ? unpack16(w.z, w.w) : unpack16(w.x, w.y);
-      }
+    // the step's weights in the MFMA layout (bm); without B1 this frees
+    // their load registers for step s + 2 before the multiplications start
+    if constexpr (!B1) {
+      if constexpr (H == 0)
+        write_b(bw0);
+      else
+        write_b(bw1);
+    }
     const int kb = min((st + 2) * kKS, last), ka = min((st + 3) * kKS, last);
     // shared buffer (s + 1) % 2 was last read in step s - 1, which ended
     // with a barrier
     if constexpr (H == 0) {
-      load_b(kb, bw0);
+      if constexpr (!B1) load_b(kb, bw0);
       if (st + 1 < nsteps) store_a(1, ra1);
       load_a(ka, ra1);
     } else {
-      load_b(kb, bw1);
+      if constexpr (!B1) load_b(kb, bw1);
       if (st + 1 < nsteps) store_a(0, ra0);
       load_a(ka, ra0);
     }
     // keep the compiler from sinking those loads below the multiplications
     __builtin_amdgcn_sched_barrier(0);
     const int8_t *abase = As + H * ABUF + (lane & 15) * kAStride + 64 * j;
+    uint4 bm[NS];
 #pragma unroll
     for (int c = 0; c < 4; c++) {
+      if ((c & 1) == 0) read_b(c >> 1, bm);
+      v4i bb[NS];
+#pragma unroll
+      for (int s = 0; s < NS; s++) {
+        const uint4 w = bm[s];
+        bb[s] = (c & 1) ? unpack16(w.z, w.w) : unpack16(w.x, w.y);
+      }
       v4i aa[MSV];
 #pragma unroll
       for (int ms = 0; ms < MSV; ms++) {
@@ -198,7 +215,13 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
       for (int ms = 0; ms < MSV; ms++)
 #pragma unroll
         for (int s = 0; s < NS; s++)
-          acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[c][s], acc[ms][s], 0, 0, 0);
+          acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[s], acc[ms][s], 0, 0, 0);
+    }
+    if constexpr (B1) {
+      // after this wave's reads of its buffer (shared-memory operations of a
+      // wave complete in order): step s + 1 into it, step s + 2 into bw
+      write_b(bw0);
+      load_b(kb, bw0);
     }
     __syncthreads();
   };
@@ -220,11 +243,15 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
         const int corr = 8 * sum_l[r];
         const float as = scl_l[r];
         if (MODE == 0) {
-          const int o = t.ob[0];
-          if (o < O) {
-            const float gv = ((float)(acc[ms][0][i] - corr) * sc[0]) * as;
-            const float uv = ((float)(acc[ms][1][i] - corr) * sc[1]) * as;
-            a.out[(int64_t)pr * O + o] = silu(gv) * uv;
+          // subtile s holds gate rows, s + NS / 2 the up rows of the same outputs
+#pragma unroll
+          for (int s = 0; s < NS / 2; s++) {
+            const int o = t.ob[s];
+            if (o < O) {
+              const float gv = ((float)(acc[ms][s][i] - corr) * sc[s]) * as;
+              const float uv = ((float)(acc[ms][s + NS / 2][i] - corr) * sc[s + NS / 2]) * as;
+              a.out[(int64_t)pr * O + o] = silu(gv) * uv;
+            }
           }
         } else {
 #pragma unroll
@@ -240,19 +267,18 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
 
 constexpr int cmin(int x, int y) { return x < y ? x : y; }
 
-// Rows of B per workgroup: NW waves of 16 gate + 16 up rows (MODE 0) or
-// 32 down rows (MODE 1).
-template <int MODE, int NW>
-constexpr int mfma_block_rows() { return MODE == 0 ? 16 * NW : 32 * NW; }
+// Rows of B per workgroup: NW waves of 8 NS gate + 8 NS up rows (MODE 0) or
+// 16 NS down rows (MODE 1).
+template <int MODE, int NW, int NS>
+constexpr int mfma_block_rows() { return MODE == 0 ? 8 * NS * NW : 16 * NS * NW; }
 
-// MSVMAX: the largest subtile count the launch can meet (tiles never hold
-// more pairs than the batch has tokens); it bounds the registers the
-// compiler reserves.
-template <int MODE, int NW, int MSVMAX>
+// MSVMAX: the largest subtile count of the launch's tiles; it bounds the
+// registers the compiler reserves.
+template <int MODE, int NW, int NS, int MSVMAX>
 __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a) {
   constexpr int ABUF = 16 * MSVMAX * kAStride;
   __shared__ __align__(16) int8_t As[2 * ABUF];
-  __shared__ __align__(16) int8_t Bs[NW][32 * kBStride];
+  __shared__ __align__(16) int8_t Bs[NW][16 * NS * kBStride];
   __shared__ int pr_l[kMT];
   __shared__ int sum_l[kMT];    // code sum of each pair's activation row
   __shared__ float scl_l[kMT];  // scale of each pair's activation row
@@ -267,26 +293,30 @@ __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a
   t.j = t.lane >> 4;  // lane group: columns 64j .. 64j + 64 of a step
   const bool shared = (g == a.E);
   const int e = shared ? 0 : g;
-  const int o_blk = blockIdx.x * mfma_block_rows<MODE, NW>();
-  if (MODE == 0) {
-    t.Bm[0] = pick(a.rt.gate, a.sh.gate, shared, e);
-    t.Bm[1] = pick(a.rt.up, a.sh.up, shared, e);
-    t.ob[0] = t.ob[1] = o_blk + 16 * t.wave + (t.lane & 15);
-  } else {
-    t.Bm[0] = pick(a.rt.down, a.sh.down, shared, e);
-    t.Bm[1] = t.Bm[0];
-    t.ob[0] = o_blk + 32 * t.wave + (t.lane & 15);
-    t.ob[1] = t.ob[0] + 16;
+  const int o_blk = blockIdx.x * mfma_block_rows<MODE, NW, NS>();
+  // B subtile s of the wave: MODE 0: gate rows (s < NS / 2) or up rows,
+  // 16 (s mod NS / 2) .. +16 of the wave's 8 NS outputs; MODE 1: down rows
+  // 16 s .. +16 of the wave's 16 NS.
+  const RowPtr G = MODE == 0 ? pick(a.rt.gate, a.sh.gate, shared, e) : pick(a.rt.down, a.sh.down, shared, e);
+  const RowPtr U = MODE == 0 ? pick(a.rt.up, a.sh.up, shared, e) : G;
+  auto sub_row = [&](int s, int r) {  // output row of row r (0..15) of subtile s
+    return MODE == 0 ? o_blk + 8 * NS * t.wave + 16 * (s % (NS / 2)) + r
+                     : o_blk + 16 * NS * t.wave + 16 * s + r;
+  };
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    t.Bm[s] = (MODE == 0 && s >= NS / 2) ? U : G;
+    t.ob[s] = sub_row(s, t.lane & 15);
   }
   const int rowbytes = a.C >> 1;
-  // coalesced load i: wave row r = 8 i + lane / 8 (rows 0..15 are subtile
-  // 0, 16..31 subtile 1), bytes 16 (lane % 8) of the step's 128
+  // coalesced load i: wave row r = 8 i + lane / 8 (subtile r / 16), bytes
+  // 16 (lane % 8) of the step's 128
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int r = 8 * i + (t.lane >> 3);
-    const int s = r >> 4;
-    const int o = (MODE == 0 ? o_blk + 16 * t.wave : o_blk + 32 * t.wave + 16 * s) + (r & 15);
-    t.bp[i] = t.Bm[s].q + (int64_t)min(o, a.O - 1) * rowbytes + 16 * (t.lane & 7);
+  for (int s = 0; s < NS; s++) t.bbase[s] = t.Bm[s].q;
+#pragma unroll
+  for (int i = 0; i < 2 * NS; i++) {
+    const int r = 8 * i + (t.lane >> 3);  // subtile r / 16 == i / 2
+    t.boff[i] = min(sub_row(i >> 1, r & 15), a.O - 1) * rowbytes + 16 * (t.lane & 7);
   }
   t.bs = &Bs[t.wave][0];
 
@@ -301,44 +331,52 @@ __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a
   }
   __syncthreads();
   switch ((t.rows + 15) >> 4) {  // 16-pair subtiles in use, uniform across the block
-    case 1: mfma_tile<MODE, NW, 1, ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 2: mfma_tile<MODE, NW, cmin(2, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 3: mfma_tile<MODE, NW, cmin(3, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 4: mfma_tile<MODE, NW, cmin(4, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 5: mfma_tile<MODE, NW, cmin(5, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 6: mfma_tile<MODE, NW, cmin(6, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
-    case 7: mfma_tile<MODE, NW, cmin(7, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
-    default: mfma_tile<MODE, NW, MSVMAX, ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 1: mfma_tile<MODE, NW, NS, 1, ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 2: mfma_tile<MODE, NW, NS, cmin(2, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 3: mfma_tile<MODE, NW, NS, cmin(3, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 4: mfma_tile<MODE, NW, NS, cmin(4, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 5: mfma_tile<MODE, NW, NS, cmin(5, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 6: mfma_tile<MODE, NW, NS, cmin(6, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    case 7: mfma_tile<MODE, NW, NS, cmin(7, MSVMAX), ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
+    default: mfma_tile<MODE, NW, NS, MSVMAX, ABUF>(a, t, As, pr_l, sum_l, scl_l); break;
   }
 }
 
 bool grouped_mfma_fits(int C) { return C % kKS == 0; }
 
-int grouped_mfma_max_tiles(int S, int P, int E) { return (S * P + kMT - 1) / kMT + E + 1; }
+// Pairs per tile: batches above 64 tokens use tiles of 80 pairs (the 8-wave
+// kernel holds at most 5 subtiles); smaller batches never have more than 64
+// pairs per group, so their tiles are whole groups.
+int grouped_mfma_tile_rows(int S) { return S > 64 ? 80 : kMT; }
+
+int grouped_mfma_max_tiles(int S, int P, int E) {
+  const int tr = grouped_mfma_tile_rows(S);
+  return (S * P + tr - 1) / tr + E + 1;
+}
+
+template <int MODE, int NW, int NS, int MSVMAX>
+static void launch_mode(const GroupedMfmaArgs &a, int max_tiles, hipStream_t st) {
+  constexpr int RPB = mfma_block_rows<MODE, NW, NS>();
+  const dim3 grid((a.O + RPB - 1) / RPB, max_tiles);
+  hipLaunchKernelGGL((grouped_mfma_kernel<MODE, NW, NS, MSVMAX>), grid, dim3(NW * 64), 0, st, a);
+}
 
 // Batches of up to 64 tokens (at most 4 subtiles per tile): 4-wave
-// workgroups, so that a few experts still spread over many workgroups;
-// larger batches: 8-wave workgroups, which stage each activation tile for
-// twice as many weight rows.
+// workgroups of 32 B rows per wave, so that a few experts still spread over
+// many workgroups; larger batches: 8-wave workgroups of 64 B rows per wave,
+// which halves the shared-memory reads of activations per weight byte.
 hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, int S,
                                hipStream_t st) {
   if (S <= 64) {
-    const dim3 grid((a.O + mfma_block_rows<0, 4>() - 1) / mfma_block_rows<0, 4>(), max_tiles);
     if (mode == 0)
-      hipLaunchKernelGGL((grouped_mfma_kernel<0, 4, 4>), grid, dim3(256), 0, st, a);
+      launch_mode<0, 4, 2, 4>(a, max_tiles, st);
     else
-      hipLaunchKernelGGL((grouped_mfma_kernel<1, 4, 4>),
-                         dim3((a.O + mfma_block_rows<1, 4>() - 1) / mfma_block_rows<1, 4>(), max_tiles),
-                         dim3(256), 0, st, a);
+      launch_mode<1, 4, 2, 4>(a, max_tiles, st);
   } else {
     if (mode == 0)
-      hipLaunchKernelGGL((grouped_mfma_kernel<0, 8, 8>),
-                         dim3((a.O + mfma_block_rows<0, 8>() - 1) / mfma_block_rows<0, 8>(), max_tiles),
-                         dim3(512), 0, st, a);
+      launch_mode<0, 8, 4, 5>(a, max_tiles, st);
     else
-      hipLaunchKernelGGL((grouped_mfma_kernel<1, 8, 8>),
-                         dim3((a.O + mfma_block_rows<1, 8>() - 1) / mfma_block_rows<1, 8>(), max_tiles),
-                         dim3(512), 0, st, a);
+      launch_mode<1, 8, 4, 5>(a, max_tiles, st);
   }
   return hipGetLastError();
 }

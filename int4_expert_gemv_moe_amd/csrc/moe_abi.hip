@@ -463,10 +463,12 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
   const bool topk_in_group = S <= kGroupTopkMaxTokens && c.E <= 256;
   MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, !topk_in_group, nullptr,
                      stream, gamma, layer->norm_eps));
-  const bool mfma_gu = grouped_mfma_fits(c.D), mfma_dn = grouped_mfma_fits(c.I);
+  // the MFMA kernels address activation rows with 32-bit byte offsets
+  const bool offs_ok = (int64_t)S * P * std::max(c.D, c.I) < INT32_MAX;
+  const bool mfma_gu = grouped_mfma_fits(c.D) && offs_ok, mfma_dn = grouped_mfma_fits(c.I) && offs_ok;
   const int max_tiles = grouped_mfma_max_tiles(S, P, c.E);
   GroupArgs ga{w.idx,    S,     c.E,     c.K,      P, c.n_shared, w.gcount, w.goff, w.pairs,
-               (mfma_gu || mfma_dn) ? w.tiles : nullptr, w.ntiles, kGroupedMfmaTile};
+               (mfma_gu || mfma_dn) ? w.tiles : nullptr, w.ntiles, grouped_mfma_tile_rows(S)};
   ga.with_topk = topk_in_group ? 1 : 0;
   ga.logits = w.logits;
   ga.bias = layer->router_b;

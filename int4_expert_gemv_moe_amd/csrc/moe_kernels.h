@@ -194,6 +194,7 @@ constexpr int kGroupedMfmaTile = 128;  // pairs per tile
 constexpr int kRouterTileMinTokens = 256;  // batches from this size use the 8x8 router tiles
 // batches up to this size select inside group_kernel (one wave per token)
 constexpr int kGroupTopkMaxTokens = 16;
+int grouped_mfma_tile_rows(int S);
 int grouped_mfma_max_tiles(int S, int P, int E);
 hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, int S, hipStream_t st);
 hipError_t launch_grouped_down(const GroupedDownArgs &a, hipStream_t st);
