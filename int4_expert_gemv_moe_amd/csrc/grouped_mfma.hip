@@ -67,7 +67,7 @@ struct MfmaTile {
 
 constexpr int kBStride = 144;  // shared bytes per weight row of a step (128 + 16)
 
-// As: two activation buffers of ABUF bytes each.  NS: 16-row B subtiles
+// As: three activation buffers of ABUF bytes each.  NS: 16-row B subtiles
 // per wave (2: 16 gate + 16 up rows, or 32 down rows; 4: twice that, so each
 // activation fragment read from shared memory feeds four MFMAs).
 template <int MODE, int NW, int NS, int MSV, int ABUF>
@@ -151,7 +151,7 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   // multiplications the step moves bw to the buffer and loads step s + 2.
   constexpr bool B1 = NS == 4;
   uint4 bw0[NI], bw1[B1 ? 1 : NI];
-  u4v ra0[NA], ra1[NA];
+  u4v ra0[NA], ra1[B1 ? 1 : NA];
   // Loads past the last step repeat the last step's addresses: every load
   // is issued unconditionally, so the compiler's count of loads in flight
   // is exact and its waits name only the data a step needs.
@@ -164,52 +164,77 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
   } else {
     load_b(min(kKS, last), bw1);
   }
-  load_a(min(kKS, last), ra1);
-  store_a(0, ra0);
-  load_a(min(2 * kKS, last), ra0);
+  if constexpr (B1) {
+    // one activation register set: step s + 1 waits in it during step s
+    store_a(0, ra0);
+    load_a(min(kKS, last), ra0);
+  } else {
+    load_a(min(kKS, last), ra1);
+    store_a(0, ra0);
+    load_a(min(2 * kKS, last), ra0);
+  }
   __syncthreads();
   // one step; H = st % 2 is a template constant, so every register set is
-  // named statically
+  // named statically.  The activations sit in a ring of three shared
+  // buffers (step s in buffer s % 3): step s reads its first operands,
+  // stores step s + 1, then passes the workgroup barrier and multiplies.
+  // Buffer (s + 1) % 3 was last read in step s - 2, which every wave
+  // finished before the barrier of step s - 1; step s's operands were
+  // stored before the barrier of step s - 1.  One barrier per step, and
+  // the first reads of a step wait out the barrier instead of following it.
   auto step = [&](int st, auto hc) __attribute__((always_inline)) {
     constexpr int H = decltype(hc)::value;
-    // the step's weights in the MFMA layout (bm); without B1 this frees
-    // their load registers for step s + 2 before the multiplications start
+    // the step's weights in the MFMA layout; without B1 this frees their
+    // load registers for step s + 2 before the multiplications start
     if constexpr (!B1) {
       if constexpr (H == 0)
         write_b(bw0);
       else
         write_b(bw1);
     }
+    const int8_t *abase = As + (st % 3) * ABUF + (lane & 15) * kAStride + 64 * j;
+    auto read_a = [&](int c, v4i (&aa)[MSV]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ms = 0; ms < MSV; ms++) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(abase + ms * 16 * kAStride + 16 * c);
+        aa[ms] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+      }
+    };
+    // the first operands before the barrier, where registers allow (not B1)
+    constexpr bool EARLY = !B1;
+    uint4 bm[NS];
+    v4i aa[MSV];
+    if constexpr (EARLY) {
+      read_b(0, bm);
+      read_a(0, aa);
+    }
     const int kb = min((st + 2) * kKS, last), ka = min((st + 3) * kKS, last);
-    // shared buffer (s + 1) % 2 was last read in step s - 1, which ended
-    // with a barrier
-    if constexpr (H == 0) {
-      if constexpr (!B1) load_b(kb, bw0);
-      if (st + 1 < nsteps) store_a(1, ra1);
+    if constexpr (B1) {
+      if (st + 1 < nsteps) store_a((st + 1) % 3, ra0);
+      load_a(min((st + 2) * kKS, last), ra0);
+    } else if constexpr (H == 0) {
+      load_b(kb, bw0);
+      if (st + 1 < nsteps) store_a((st + 1) % 3, ra1);
       load_a(ka, ra1);
     } else {
-      if constexpr (!B1) load_b(kb, bw1);
-      if (st + 1 < nsteps) store_a(0, ra0);
+      load_b(kb, bw1);
+      if (st + 1 < nsteps) store_a((st + 1) % 3, ra0);
       load_a(ka, ra0);
     }
     // keep the compiler from sinking those loads below the multiplications
     __builtin_amdgcn_sched_barrier(0);
-    const int8_t *abase = As + H * ABUF + (lane & 15) * kAStride + 64 * j;
-    uint4 bm[NS];
+    __syncthreads();
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      if ((c & 1) == 0) read_b(c >> 1, bm);
+      if (c > 0 || !EARLY) {
+        if ((c & 1) == 0) read_b(c >> 1, bm);
+        read_a(c, aa);
+      }
       v4i bb[NS];
 #pragma unroll
       for (int s = 0; s < NS; s++) {
         const uint4 w = bm[s];
         bb[s] = (c & 1) ? unpack16(w.z, w.w) : unpack16(w.x, w.y);
-      }
-      v4i aa[MSV];
-#pragma unroll
-      for (int ms = 0; ms < MSV; ms++) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(abase + ms * 16 * kAStride + 16 * c);
-        aa[ms] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
       }
 #pragma unroll
       for (int ms = 0; ms < MSV; ms++)
@@ -223,7 +248,6 @@ __device__ __forceinline__ void mfma_tile(const GroupedMfmaArgs &a, const MfmaTi
       write_b(bw0);
       load_b(kb, bw0);
     }
-    __syncthreads();
   };
   int st = 0;
   for (; st + 1 < nsteps; st += 2) {
@@ -277,7 +301,7 @@ constexpr int mfma_block_rows() { return MODE == 0 ? 8 * NS * NW : 16 * NS * NW;
 template <int MODE, int NW, int NS, int MSVMAX>
 __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a) {
   constexpr int ABUF = 16 * MSVMAX * kAStride;
-  __shared__ __align__(16) int8_t As[2 * ABUF];
+  __shared__ __align__(16) int8_t As[3 * ABUF];
   __shared__ __align__(16) int8_t Bs[NW][16 * NS * kBStride];
   __shared__ int pr_l[kMT];
   __shared__ int sum_l[kMT];    // code sum of each pair's activation row
