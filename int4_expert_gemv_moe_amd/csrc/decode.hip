@@ -465,13 +465,13 @@ __device__ void down_fixed(const DecodeArgs &a, int s, int db) {
 }
 
 #ifndef MOE_DNFX_ROWS
-#define MOE_DNFX_ROWS 4
+#define MOE_DNFX_ROWS 2
 #endif
 
 // ---- the three launches ----------------------------------------------------------------
 
 #ifndef MOE_GU_ROWS
-#define MOE_GU_ROWS 2
+#define MOE_GU_ROWS 1
 #endif
 
 // With a.gamma set every workgroup of phase A first forms the token's RMSNorm
@@ -488,7 +488,8 @@ __global__ __launch_bounds__(256) void decode_a_kernel(DecodeArgs a) {
     xrow = xn_dyn;
   }
   if (b < a.n_router) {
-    router_logit(a, xrow, s, b * 4 + (threadIdx.x >> 6));
+    const int wave = threadIdx.x >> 6;
+    if (wave < kARouterWaves) router_logit(a, xrow, s, b * kARouterWaves + wave);
     return;
   }
   if (b < a.n_router + a.n_quant) {
@@ -525,15 +526,19 @@ constexpr int kCWaves = 8;
 
 int decode_c_slots(int) { return kCWaves; }
 
-// rows per pass for NCH 1 KB chunks of a weight row (96 registers of weights)
+#ifndef MOE_C_RB1
+#define MOE_C_RB1 24
+#endif
+// rows per pass for NCH 1 KB chunks of a weight row (at most 96 registers of
+// weights)
 template <int NCH>
 struct CRows {
-  static constexpr int value = NCH == 1 ? 24 : (NCH == 2 ? 12 : (NCH == 3 ? 6 : 4));
+  static constexpr int value = NCH == 1 ? MOE_C_RB1 : (NCH == 2 ? 12 : (NCH == 3 ? 6 : 4));
 };
 
 int decode_c_rows_per_pass(int I) {
   const int nch = (I / 2 + 1023) / 1024;
-  return nch == 1 ? 24 : (nch == 2 ? 12 : (nch == 3 ? 6 : 4));
+  return nch == 1 ? MOE_C_RB1 : (nch == 2 ? 12 : (nch == 3 ? 6 : 4));
 }
 
 template <int NCH, bool MASKED>

@@ -406,7 +406,7 @@ int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float
   d.h = w.h;
   d.ysh = w.ysh;
   d.tmp = w.tmp;
-  d.n_router = (c.E + 3) / 4;
+  d.n_router = (c.E + kARouterWaves - 1) / kARouterWaves;
   d.n_quant = 1;
   d.n_gu_fx = c.n_shared ? ds.gu_fx : 0;
   d.n_gu_rt = ds.gu_rt;

@@ -191,6 +191,8 @@ hipError_t launch_grouped_gateup(const GroupedGateUpArgs &a, hipStream_t st);
 // The MFMA form applies when the contraction length is a multiple of 256.
 bool grouped_mfma_fits(int C);
 constexpr int kGroupedMfmaTile = 128;  // pairs per tile
+// logits per phase-A router workgroup (one per wave)
+constexpr int kARouterWaves = 4;
 constexpr int kRouterTileMinTokens = 256;  // batches from this size use the 8x8 router tiles
 // batches up to this size select inside group_kernel (one wave per token)
 constexpr int kGroupTopkMaxTokens = 16;
