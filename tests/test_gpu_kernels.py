@@ -98,10 +98,11 @@ def test_router_topk(shape, S, bias):
     say(f"  unique routing for {uniq.sum()}/{S} tokens")
 
 
-@pytest.mark.parametrize("S", [37, 301])
+@pytest.mark.parametrize("S", [37, 301, 2048])
 def test_router_batch_invariance(S):
     # a token's routing does not depend on the batch it is in (37 tokens: the
-    # 8-token kernel; 301: the 8x8 register tiles with a ragged last tile)
+    # 8-token kernel; 301: the 8x8 register tiles with a ragged
+    # last tile; 2048: the prefill batch)
     shape = GLM
     cfg = moe.config(shape.D, shape.I, shape.E, shape.K)
     wr = torch.from_numpy(synth.router_w(2, shape)).cuda()

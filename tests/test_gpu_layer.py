@@ -59,7 +59,15 @@ def test_tiny_block(path):
                                           # E > 256: the 16-entry lists of the selection
                                           (synth.Shape(D=256, I=128, E=512, K=8), 6, "uniform"),
                                           # I % 256 != 0: GEMV down, masked row tails
-                                          (synth.Shape(D=256, I=384, E=16, K=4), 3, "uniform")])
+                                          (synth.Shape(D=256, I=384, E=16, K=4), 3, "uniform"),
+                                          # the documented limits: E = 1024 and K = 64
+                                          # (eight routed-down launches per token)
+                                          (synth.Shape(D=256, I=128, E=1024, K=64), 3, "uniform"),
+                                          # smallest I (16-byte down rows) and a single
+                                          # expert (E = K = 1)
+                                          (synth.Shape(D=256, I=32, E=1, K=1), 2, "uniform"),
+                                          # widest rows: 4 KB packed gate/up rows
+                                          (synth.Shape(D=8192, I=4096, E=8, K=2), 2, "uniform")])
 def test_batch_union_equals_per_token_bit_exact(shape, S, bias):
     b = bias_for(bias, 1, shape)
     dl = device_layer(1, shape, 0, b)
