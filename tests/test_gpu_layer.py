@@ -189,3 +189,28 @@ def test_error_codes():
     bad = moe.config(250, 128, 8, 2)
     with pytest.raises(moe.MoeError):
         moe.Workspace(bad, 1, moe.WS_FORWARD)
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_per_token_selection_repeated_calls(S):
+    """The per-token path selects inside its gate/up launch (every routed
+    gate/up workgroup runs the token's selection rounds; the first one
+    publishes them).  Many consecutive calls on one workspace must select
+    exactly what the separate router and top-K kernels select for the same
+    tokens (same logit bits, same rule), with the same weights."""
+    shape = GLM
+    b = bias_for("uniform", 3, shape)
+    dl = device_layer(3, shape, 0, b)
+    cfg = dl.cfg
+    n_calls = 48
+    x = torch.from_numpy(synth.activations(21, n_calls * S, shape.D)).cuda()
+    ws = moe.Workspace(cfg, S, moe.WS_FORWARD)
+    idx = torch.empty(n_calls, S, cfg.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(n_calls, S, cfg.K, dtype=torch.float32, device="cuda")
+    for c in range(n_calls):
+        moe.moe_layer_forward(dl, x[c * S:(c + 1) * S], ws, topk_idx=idx[c], topk_w=w[c])
+    wsr = moe.Workspace(cfg, n_calls * S, moe.WS_ROUTER)
+    ridx, rw, _ = moe.moe_router_topk(cfg, x, dl.router_w, dl.router_b, wsr)
+    torch.cuda.synchronize()
+    assert torch.equal(idx.view(-1, cfg.K), ridx)
+    assert torch.equal(w.view(-1, cfg.K).view(torch.int32), rw.view(torch.int32))
