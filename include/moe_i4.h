@@ -182,6 +182,84 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
                             float *out, unsigned flags, const moe_probe *probe, void *ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/* The per-token block with the routing given by the caller instead of the
+ * router (section 11 computes the routing first and the experts after it;
+ * section 13 fetches the selected experts between the two).  topk_idx[S][K]
+ * (int32) are expert indices into layer->routed and topk_w[S][K] (float32)
+ * their combine weights, both device arrays read by the call; indices outside
+ * [0, E) are clamped into it, so no access leaves the expert stack.
+ * layer->router_w and router_b are not read and may be NULL.  Everything else
+ * (flags, x/out rule, workspace of moe_workspace_bytes(cfg, S, 0)) is as in
+ * moe_layer_forward; with the routing that moe_layer_forward selects, the two
+ * calls return identical bits. */
+int moe_layer_forward_routed(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                             const int32_t *topk_idx, const float *topk_w, float *out,
+                             unsigned flags, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- Expert residency tiers (section 05 expert cache, section 13 tiers) ----
+ * Every expert of a layer is kept as one slab, the three packed matrices
+ * followed by the three scale vectors (section 13 reads an expert with a
+ * single ~19 MB read for this reason); moe_slab_layout_of gives the byte
+ * offsets.  A layer's routed stack in moe_experts form over such slabs uses
+ * q4 = base + offset, scale = base + offset, q4_stride = bytes and
+ * scale_stride = bytes / 4.  All experts live in pinned host memory
+ * (hipHostMalloc); each layer has n_slots HBM slab slots.  A call's experts
+ * are mapped to slots by moe_tier_map, the missing slabs are copied in by
+ * moe_tier_fetch, and moe_layer_forward_routed then runs on the slot stack
+ * with the routing rewritten to slot numbers. */
+typedef struct {
+  int64_t gate_q4, up_q4, down_q4; /* byte offsets of the packed matrices */
+  int64_t gate_s, up_s, down_s;    /* byte offsets of the float32 scales */
+  int64_t bytes;                   /* slab size (a multiple of 16) */
+} moe_slab_layout;
+
+/* Offsets of one expert slab for cfg's D and I (host; MOE_ESHAPE unless both
+ * are multiples of 32). */
+int moe_slab_layout_of(const moe_config *cfg, moe_slab_layout *out);
+
+/* Host bookkeeping of the HBM slots of n_layers layers of n_experts experts,
+ * n_slots per layer, all empty.  Returns NULL on invalid sizes or when host
+ * memory runs out.  The object holds no device memory. */
+typedef struct moe_tier moe_tier;
+moe_tier *moe_tier_create(int n_layers, int n_experts, int n_slots);
+void moe_tier_destroy(moe_tier *t);
+
+/* Section 05 expert_get for each of eids[0..n) of one call, in order (host
+ * arrays): a resident expert is a hit and its slot's use clock is refreshed;
+ * a missing one takes the next unused slot, else the least recently used slot
+ * (ties: the lowest slot), and loads[i] = 1 says its slab must be copied in
+ * before the call.  slots[i] receives the slot.  With n <= n_slots (checked,
+ * MOE_ESHAPE otherwise) no slot of the call is evicted by the same call.
+ * Returns the number of misses, or a negative status (eids outside [0,
+ * n_experts) or a bad layer: MOE_EINVAL, nothing changed). */
+int moe_tier_map(moe_tier *t, int layer, const int32_t *eids, int n, int32_t *slots,
+                 int32_t *loads);
+
+/* Hits and misses of every moe_tier_map so far (either pointer may be NULL). */
+int moe_tier_stats(const moe_tier *t, uint64_t *hits, uint64_t *misses);
+
+/* Enqueue one host-to-device copy of slab_bytes per i with loads[i] != 0:
+ * host_slabs + eids[i]*slab_bytes (pinned host memory) to hbm_slots +
+ * slots[i]*slab_bytes (device).  eids, slots and loads are host arrays.  The
+ * copies are ordered on stream before the work queued after them. */
+int moe_tier_fetch(const void *host_slabs, void *hbm_slots, size_t slab_bytes,
+                   const int32_t *eids, const int32_t *slots, const int32_t *loads, int n,
+                   hipStream_t stream);
+
+/* Section 13 swap rule for a frequency-managed tier holding pinned[0..n_pinned)
+ * (host arrays, expert ids): take the coldest held expert by heat (first of
+ * equals) and the hottest expert not held (first of equals, heat > 0); swap
+ * only if the newcomer's heat exceeds the coldest's by more than a quarter of
+ * it plus 4.  Returns 1 and the held position, the newcomer and the heat gain,
+ * or 0 (no swap, or invalid arguments). */
+int moe_tier_pick_swap(const uint32_t *heat, int n_experts, const int32_t *pinned, int n_pinned,
+                       int32_t *slot, int32_t *eid, int64_t *gain);
+
+/* Section 13 frequency-first score: heat in the high bits, then recency
+ * (255 - age for ages below 255, else 0) so that recency only orders experts
+ * of equal heat. */
+uint64_t moe_tier_lfru_score(uint32_t heat, uint32_t last, uint32_t clock);
+
 /* Section 04 RMSNorm: y = x * (1/sqrt(mean(x^2) + eps)) * gamma per row,
  * with the mean of squares accumulated in double. */
 int moe_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y,

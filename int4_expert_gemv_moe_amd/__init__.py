@@ -78,10 +78,24 @@ def lib():
         L.moe_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp, vp]
         L.moe_stream_read.argtypes = [vp, sz, vp, vp]
+        L.moe_layer_forward_routed.argtypes = [vp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
+        L.moe_slab_layout_of.argtypes = [vp, vp]
+        L.moe_tier_create.argtypes = [i32, i32, i32]
+        L.moe_tier_create.restype = vp
+        L.moe_tier_destroy.argtypes = [vp]
+        L.moe_tier_destroy.restype = None
+        L.moe_tier_map.argtypes = [vp, i32, vp, i32, vp, vp]
+        L.moe_tier_stats.argtypes = [vp, vp, vp]
+        L.moe_tier_fetch.argtypes = [vp, vp, sz, vp, vp, vp, i32, vp]
+        L.moe_tier_pick_swap.argtypes = [vp, i32, vp, i32, vp, vp, vp]
+        L.moe_tier_lfru_score.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
+        L.moe_tier_lfru_score.restype = ctypes.c_uint64
         L.moe_stream_read_sink_words.argtypes = []
         for name in ("moe_workspace_init", "moe_pack_int4", "moe_quant_act_i8", "moe_router_topk",
                      "moe_expert_swiglu_i4", "moe_layer_forward", "moe_layer_forward_batch",
-                     "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words"):
+                     "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
+                     "moe_layer_forward_routed", "moe_slab_layout_of", "moe_tier_map",
+                     "moe_tier_stats", "moe_tier_fetch", "moe_tier_pick_swap"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -315,3 +329,182 @@ def moe_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out=Non
     _check(lib().moe_rmsnorm(_ptr(x), _ptr(gamma), S, D, eps, _ptr(out),
                              ctypes.c_void_p(_stream(stream))), "moe_rmsnorm")
     return out
+
+
+# ---- given routing and expert residency tiers ---------------------------------
+
+def moe_layer_forward_routed(layer, x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                             ws: Workspace, out=None, flags: int = 0, stream=None,
+                             norm_gamma=None, norm_eps: float = 1e-5):
+    """Per-token path with the routing given: topk_idx [S][K] int32 indices
+    into layer's routed stack, topk_w [S][K] float32 weights (device)."""
+    _dev(x, torch.float32, "x")
+    _dev(topk_idx, torch.int32, "topk_idx")
+    _dev(topk_w, torch.float32, "topk_w")
+    S = x.shape[0]
+    if out is None:
+        out = torch.empty(S, layer.cfg.D, dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    if norm_gamma is not None:
+        _dev(norm_gamma, torch.float32, "norm_gamma")
+        flags |= F_PRENORM
+    L = layer.cstruct(norm_gamma, norm_eps)
+    _check(lib().moe_layer_forward_routed(ctypes.byref(layer.cfg), ctypes.byref(L), _ptr(x), S,
+                                          _ptr(topk_idx), _ptr(topk_w), _ptr(out), flags, ws.ptr,
+                                          ws.nbytes, ctypes.c_void_p(_stream(stream))),
+           "moe_layer_forward_routed")
+    return out
+
+
+class SlabLayout(ctypes.Structure):
+    _fields_ = [("gate_q4", ctypes.c_int64), ("up_q4", ctypes.c_int64), ("down_q4", ctypes.c_int64),
+                ("gate_s", ctypes.c_int64), ("up_s", ctypes.c_int64), ("down_s", ctypes.c_int64),
+                ("bytes", ctypes.c_int64)]
+
+
+def slab_layout(cfg: Config) -> SlabLayout:
+    lay = SlabLayout()
+    _check(lib().moe_slab_layout_of(ctypes.byref(cfg), ctypes.byref(lay)), "moe_slab_layout_of")
+    return lay
+
+
+class SlabExperts:
+    """A stack of expert slabs (one slab per expert or slot) in the
+    moe_experts form: base + offset, stride = slab bytes."""
+
+    def __init__(self, buf: torch.Tensor, lay: SlabLayout):
+        self.buf, self.lay = buf, lay
+
+    def cstruct(self) -> Experts:
+        b, L = self.buf.data_ptr(), self.lay
+
+        def q(oq, os_):
+            return QMat(b + oq, b + os_, L.bytes, L.bytes // 4)
+        return Experts(q(L.gate_q4, L.gate_s), q(L.up_q4, L.up_s), q(L.down_q4, L.down_s))
+
+
+def pack_slabs(experts: DeviceExperts, lay: SlabLayout, out: torch.Tensor) -> torch.Tensor:
+    """Copy a stacked expert set into slab form (out: uint8 [n][lay.bytes],
+    device or pinned host)."""
+    n = experts.gate_q4.shape[0]
+    parts = ((lay.gate_q4, experts.gate_q4), (lay.up_q4, experts.up_q4),
+             (lay.down_q4, experts.down_q4), (lay.gate_s, experts.gate_s),
+             (lay.up_s, experts.up_s), (lay.down_s, experts.down_s))
+    for off, t in parts:
+        flat = t.reshape(n, -1).view(torch.uint8)
+        out[:, off:off + flat.shape[1]].copy_(flat)
+    return out
+
+
+class Tier:
+    """Host bookkeeping of the HBM expert slots (moe_tier_*)."""
+
+    def __init__(self, n_layers: int, n_experts: int, n_slots: int):
+        h = lib().moe_tier_create(n_layers, n_experts, n_slots)
+        if not h:
+            raise MoeError("moe_tier_create failed")
+        self.h, self.n_slots = h, n_slots
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            lib().moe_tier_destroy(self.h)
+            self.h = None
+
+    def map(self, layer: int, eids):
+        """(slots, loads, misses) for the experts of one call (host arrays)."""
+        import numpy as np
+        e = np.ascontiguousarray(eids, np.int32)
+        slots = np.empty(e.size, np.int32)
+        loads = np.empty(e.size, np.int32)
+        r = lib().moe_tier_map(self.h, layer, e.ctypes.data, e.size, slots.ctypes.data,
+                               loads.ctypes.data)
+        if r < 0:
+            raise MoeError(f"moe_tier_map: {status_str(r)}")
+        return slots, loads, r
+
+    def stats(self):
+        h, m = ctypes.c_uint64(0), ctypes.c_uint64(0)
+        _check(lib().moe_tier_stats(self.h, ctypes.byref(h), ctypes.byref(m)), "moe_tier_stats")
+        return h.value, m.value
+
+    @staticmethod
+    def fetch(host_slabs: torch.Tensor, hbm_slots: torch.Tensor, slab_bytes: int, eids, slots,
+              loads, stream=None):
+        import numpy as np
+        e = np.ascontiguousarray(eids, np.int32)
+        sl = np.ascontiguousarray(slots, np.int32)
+        ld = np.ascontiguousarray(loads, np.int32)
+        _check(lib().moe_tier_fetch(_ptr(host_slabs), _ptr(hbm_slots), slab_bytes, e.ctypes.data,
+                                    sl.ctypes.data, ld.ctypes.data, e.size,
+                                    ctypes.c_void_p(_stream(stream))), "moe_tier_fetch")
+
+
+def tier_pick_swap(heat, pinned):
+    """(swap?, pinned position, expert, gain) by the section 13 rule."""
+    import numpy as np
+    h = np.ascontiguousarray(heat, np.uint32)
+    p = np.ascontiguousarray(pinned, np.int32)
+    slot, eid, gain = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int64(0)
+    r = lib().moe_tier_pick_swap(h.ctypes.data, h.size, p.ctypes.data, p.size, ctypes.byref(slot),
+                                 ctypes.byref(eid), ctypes.byref(gain))
+    return bool(r), slot.value, eid.value, gain.value
+
+
+def tier_lfru_score(heat: int, last: int, clock: int) -> int:
+    return int(lib().moe_tier_lfru_score(heat, last, clock))
+
+
+@dataclass
+class TieredLayer:
+    """One layer whose routed experts live in pinned host memory (all of them)
+    and in n_slots HBM slots (those in use); router and shared expert in HBM.
+    forward() routes on the device, maps the selected experts to slots on the
+    host, copies the missing slabs in and runs the per-token block on the slot
+    stack with the routing rewritten to slot numbers."""
+    cfg: Config
+    router_w: torch.Tensor
+    router_b: torch.Tensor
+    routed: SlabExperts        # the HBM slot stack
+    shared: DeviceExperts | None
+    host_slabs: torch.Tensor   # pinned uint8 [E][slab]
+    tier: Tier
+    layer_index: int = 0
+
+    @staticmethod
+    def from_device_layer(dl: DeviceLayer, n_slots: int, tier: Tier | None = None,
+                          layer_index: int = 0) -> "TieredLayer":
+        lay = slab_layout(dl.cfg)
+        E = dl.cfg.E
+        staged = pack_slabs(dl.routed, lay, torch.empty(E, lay.bytes, dtype=torch.uint8,
+                                                         device=dl.router_w.device))
+        host = torch.empty(E, lay.bytes, dtype=torch.uint8, pin_memory=True)
+        host.copy_(staged)
+        del staged
+        slots = torch.empty(n_slots, lay.bytes, dtype=torch.uint8, device=dl.router_w.device)
+        tier = tier or Tier(1, E, n_slots)
+        return TieredLayer(dl.cfg, dl.router_w, dl.router_b, SlabExperts(slots, lay), dl.shared,
+                           host, tier, layer_index)
+
+    def cstruct(self, norm_gamma=None, norm_eps: float = 0.0) -> LayerC:
+        sh = self.shared.cstruct() if self.shared is not None else Experts()
+        g = None if norm_gamma is None else norm_gamma.data_ptr()
+        return LayerC(None, None, self.routed.cstruct(), sh, g, float(norm_eps))
+
+    def forward(self, x: torch.Tensor, ws_router: Workspace, ws: Workspace, out=None,
+                stream=None):
+        """Returns (out, misses of this call)."""
+        import numpy as np
+        idx, w, _ = moe_router_topk(self.cfg, x, self.router_w, self.router_b, ws_router,
+                                    stream=stream)
+        idx_h = idx.cpu().numpy()            # waits for the routing
+        uniq, inv = np.unique(idx_h.ravel(), return_inverse=True)
+        order = np.argsort(np.unique(idx_h.ravel(), return_index=True)[1])  # first appearance
+        eids = uniq[order]
+        slots, loads, misses = self.tier.map(self.layer_index, eids)
+        Tier.fetch(self.host_slabs, self.routed.buf, self.routed.lay.bytes, eids, slots, loads,
+                   stream)
+        slot_of = np.empty(uniq.size, np.int32)
+        slot_of[order] = slots
+        sidx = torch.from_numpy(slot_of[inv].reshape(idx_h.shape).astype(np.int32)).to(x.device)
+        o = moe_layer_forward_routed(self, x, sidx, w, ws, out=out, stream=stream)
+        return o, misses

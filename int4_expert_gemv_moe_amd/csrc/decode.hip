@@ -41,6 +41,12 @@ __device__ void router_logit(const DecodeArgs &a, const float *xrow, int s, int 
   if ((threadIdx.x & 63) == 0) a.logits[(int64_t)s * a.E + e] = v;
 }
 
+// An expert index read back from memory (the caller's, when the routing is
+// given), kept inside the stack.
+__device__ __forceinline__ int expert_at(const DecodeArgs &a, int64_t i) {
+  return min(max((int)a.idx[i], 0), a.E - 1);
+}
+
 // ---- gate/up rows -----------------------------------------------------------------
 //
 // A block works through a contiguous range of "items" of a concatenated list
@@ -161,8 +167,8 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
 }
 
 // Routed experts of token s: the block runs the token's K selection rounds
-// once (block 0 publishes them), then works through its share of the
-// concatenated rows of the K selected experts.
+// once (block 0 publishes them), or reads the caller's selection, then works
+// through its share of the concatenated rows of the K selected experts.
 template <int NCH, bool MASKED, int ROWS>
 __device__ void gateup_routed(const DecodeArgs &a, int s, int gb) {
   __shared__ int sel[64];
@@ -173,7 +179,9 @@ __device__ void gateup_routed(const DecodeArgs &a, int s, int gb) {
   load_x_codes<NCH, MASKED>(a.xq + (int64_t)s * a.D, a.D, xv);
   const int corr = 8 * a.sumx[s];
   const float sxs = a.sx[s];
-  if (wave == 0) {
+  if (a.given) {
+    if ((int)threadIdx.x < a.K) sel[threadIdx.x] = expert_at(a, (int64_t)s * a.K + threadIdx.x);
+  } else if (wave == 0) {
     const bool pub = (gb == 0);
     topk_rounds(a.logits + (int64_t)s * a.E, a.bias, a.E, a.K, a.scale,
                 pub ? a.idx + (int64_t)s * a.K : nullptr, pub ? a.w + (int64_t)s * a.K : nullptr,
@@ -553,7 +561,7 @@ __global__ __launch_bounds__(64 * kCWaves) void decode_c_kernel(DecodeArgs a) {
   const int np = a.p_hi - a.p_lo;
   const bool live = p < np;  // uniform across the wave
   const int slot = a.p_lo + (live ? p : 0);
-  const int e = a.idx[s * a.K + slot];
+  const int e = expert_at(a, (int64_t)s * a.K + slot);
   const RowPtr M = pick(a.rt.down, a.rt.down, false, e);
   const float *hrow = a.h + ((int64_t)s * a.P + slot) * a.I;
   const int rowbytes = a.I >> 1;

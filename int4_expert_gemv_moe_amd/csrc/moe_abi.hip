@@ -155,9 +155,12 @@ int check_experts(const moe_experts &e) {
   return MOE_OK;
 }
 
-int check_layer(const moe_config &c, const moe_layer *L) {
-  if (!L || !L->router_w || !L->router_b) return MOE_EINVAL;
-  if (!aligned16(L->router_w) || ((uintptr_t)L->router_b & 3u)) return MOE_EALIGN;
+int check_layer(const moe_config &c, const moe_layer *L, bool router = true) {
+  if (!L) return MOE_EINVAL;
+  if (router) {
+    if (!L->router_w || !L->router_b) return MOE_EINVAL;
+    if (!aligned16(L->router_w) || ((uintptr_t)L->router_b & 3u)) return MOE_EALIGN;
+  }
   int rc = check_experts(L->routed);
   if (rc) return rc;
   if (c.n_shared) return check_experts(L->shared);
@@ -227,11 +230,12 @@ int record(const moe_probe *probe, int which, int side, hipStream_t st) {
 }
 
 int layer_common_checks(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
-                        float *out, unsigned flags, void *ws, size_t ws_bytes, int which) {
+                        float *out, unsigned flags, void *ws, size_t ws_bytes, int which,
+                        bool router = true) {
   MOE_TRY(check_cfg(cfg));
   if (S < 1 || !x || !out || !ws) return MOE_EINVAL;
   if (flags & ~(MOE_F_ACCUMULATE | MOE_F_PRENORM)) return MOE_EINVAL;
-  MOE_TRY(check_layer(*cfg, layer));
+  MOE_TRY(check_layer(*cfg, layer, router));
   if (!aligned16(x) || ((uintptr_t)out & 3u) || ((uintptr_t)ws & 255u)) return MOE_EALIGN;
   const bool prenorm = (flags & MOE_F_PRENORM) != 0;
   if (prenorm) {
@@ -374,10 +378,20 @@ int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *s
   return MOE_OK;
 }
 
-int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
-                      float *out, unsigned flags, const moe_probe *probe, void *ws,
-                      size_t ws_bytes, hipStream_t stream) {
-  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_FWD));
+}  // extern "C"
+
+namespace {
+
+// The per-token path; with given_idx / given_w the caller's routing replaces
+// the router and the selection (phase A then has no router workgroups).
+int layer_forward_impl(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                       const int32_t *given_idx, const float *given_w, float *out,
+                       unsigned flags, const moe_probe *probe, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  const bool given = given_idx != nullptr;
+  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_FWD, !given));
+  if (given && (((uintptr_t)given_idx & 3u) || !given_w || ((uintptr_t)given_w & 3u)))
+    return given_w ? MOE_EALIGN : MOE_EINVAL;
   const moe_config &c = *cfg;
   Work w;
   carve(c, S, W_FWD, (char *)ws, &w);
@@ -401,12 +415,13 @@ int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float
   d.sx = w.sx;
   d.sumx = w.sumx;
   d.logits = w.logits;
-  d.idx = w.idx;
-  d.w = w.w;
+  d.idx = given ? const_cast<int32_t *>(given_idx) : w.idx;
+  d.w = given ? const_cast<float *>(given_w) : w.w;
+  d.given = given ? 1 : 0;
   d.h = w.h;
   d.ysh = w.ysh;
   d.tmp = w.tmp;
-  d.n_router = (c.E + kARouterWaves - 1) / kARouterWaves;
+  d.n_router = given ? 0 : (c.E + kARouterWaves - 1) / kARouterWaves;
   d.n_quant = 1;
   d.n_gu_fx = c.n_shared ? ds.gu_fx : 0;
   d.n_gu_rt = ds.gu_rt;
@@ -423,7 +438,7 @@ int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float
   const bool tdn = probe && probe->ev_down[0] && probe->ev_down[1];
   MOE_TRY_HIP(launch_decode_b(d, stream, tgu ? probe->ev_gateup[0] : nullptr,
                               tgu ? probe->ev_gateup[1] : nullptr));
-  MOE_TRY(copy_probe(c, S, probe, w, stream));
+  if (!given) MOE_TRY(copy_probe(c, S, probe, w, stream));
   const int batch = decode_c_slots(c.I);
   for (int p0 = 0; p0 < c.K; p0 += batch) {
     d.p_lo = p0;
@@ -434,6 +449,25 @@ int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float
                                 (tdn && d.c_last) ? probe->ev_down[1] : nullptr));
   }
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                      float *out, unsigned flags, const moe_probe *probe, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  return layer_forward_impl(cfg, layer, x, S, nullptr, nullptr, out, flags, probe, ws, ws_bytes,
+                            stream);
+}
+
+int moe_layer_forward_routed(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                             const int32_t *topk_idx, const float *topk_w, float *out,
+                             unsigned flags, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!topk_idx) return MOE_EINVAL;
+  return layer_forward_impl(cfg, layer, x, S, topk_idx, topk_w, out, flags, nullptr, ws,
+                            ws_bytes, stream);
 }
 
 int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const float *x, int S,

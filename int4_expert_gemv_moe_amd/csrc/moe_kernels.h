@@ -84,6 +84,7 @@ struct DecodeArgs {
   float *sh_out;            // optional [S]
   const float *gamma;       // optional [D]: phase A works on RMSNorm(x) with gamma, eps
   float eps;
+  int given;                // routing given by the caller: idx and w are inputs
 };
 
 // Grouped (unique-expert union) kernels.

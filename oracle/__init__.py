@@ -58,6 +58,10 @@ def lib():
         L.moe_ref_layer_forward.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint]
         L.moe_ref_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, vp, vp]
         L.moe_ref_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp]
+        L.moe_ref_expert_get.argtypes = [vp, vp, i32, vp, vp, vp, vp, ctypes.c_int32, vp]
+        L.moe_ref_tier_pick_swap.argtypes = [vp, i32, vp, i32, vp, vp, vp]
+        L.moe_ref_tier_lfru_score.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
+        L.moe_ref_tier_lfru_score.restype = ctypes.c_uint64
         _lib = L
     return _lib
 
@@ -231,3 +235,52 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-5) -> np.ndarray:
     y = np.empty_like(x)
     _check(lib().moe_ref_rmsnorm(_p(x), _p(gamma), S, D, eps, _p(y)), "rmsnorm")
     return y
+
+
+class ExpertCache:
+    """Section 05 per-layer expert caches (cap slots per layer) with the
+    article's shared clock and hit/miss counters, driven through the oracle's
+    moe_ref_expert_get."""
+
+    def __init__(self, n_layers: int, cap: int):
+        self.cap = cap
+        self.eid = np.full((n_layers, cap), -1, np.int32)
+        self.used = np.zeros((n_layers, cap), np.uint64)
+        self.n_used = np.zeros(n_layers, np.int32)
+        self.counters = np.zeros(3, np.uint64)  # clock, hits, misses
+
+    def get(self, layer: int, eid: int):
+        """(slot, loaded) for one lookup."""
+        loaded = ctypes.c_int(0)
+        n = ctypes.c_int(int(self.n_used[layer]))
+        c = self.counters
+        cp = c.ctypes.data
+        slot = lib().moe_ref_expert_get(self.eid[layer].ctypes.data, self.used[layer].ctypes.data,
+                                        self.cap, ctypes.byref(n), cp, cp + 8, cp + 16,
+                                        int(eid), ctypes.byref(loaded))
+        if slot < 0:
+            raise ValueError("moe_ref_expert_get rejected its arguments")
+        self.n_used[layer] = n.value
+        return slot, loaded.value
+
+    @property
+    def hits(self) -> int:
+        return int(self.counters[1])
+
+    @property
+    def misses(self) -> int:
+        return int(self.counters[2])
+
+
+def tier_pick_swap(heat, pinned):
+    """(swap?, pinned position, expert, gain) of the section 13 swap rule."""
+    heat = np.ascontiguousarray(heat, np.uint32)
+    pinned = np.ascontiguousarray(pinned, np.int32)
+    slot, eid, gain = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int64(0)
+    r = lib().moe_ref_tier_pick_swap(heat.ctypes.data, heat.size, pinned.ctypes.data, pinned.size,
+                                     ctypes.byref(slot), ctypes.byref(eid), ctypes.byref(gain))
+    return bool(r), slot.value, eid.value, gain.value
+
+
+def tier_lfru_score(heat: int, last: int, clock: int) -> int:
+    return int(lib().moe_ref_tier_lfru_score(heat, last, clock))

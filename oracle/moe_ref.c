@@ -357,3 +357,76 @@ int moe_ref_rmsnorm(const float *x, const float *gamma, int S, int D, float eps,
   }
   return 0;
 }
+
+/* ---- section 05 expert cache and section 13 tier policy ---------------- */
+
+int moe_ref_expert_get(int32_t *slot_eid, uint64_t *slot_used, int cap, int *n_used,
+                       uint64_t *clock, uint64_t *hits, uint64_t *misses, int32_t eid,
+                       int *loaded) {
+  int i, victim;
+  if (!slot_eid || !slot_used || !n_used || !clock || !hits || !misses || !loaded) return -1;
+  if (cap < 1 || *n_used < 0 || *n_used > cap) return -1;
+  /* lookup: a hit refreshes the slot's use */
+  for (i = 0; i < *n_used; i++) {
+    if (slot_eid[i] == eid) {
+      *hits += 1;
+      *clock += 1;
+      slot_used[i] = *clock;
+      *loaded = 0;
+      return i;
+    }
+  }
+  *misses += 1;
+  if (*n_used < cap) {
+    victim = *n_used;
+    *n_used += 1;
+  } else {
+    /* least recently used slot */
+    victim = 0;
+    for (i = 1; i < *n_used; i++)
+      if (slot_used[i] < slot_used[victim]) victim = i;
+  }
+  slot_eid[victim] = eid;
+  *clock += 1;
+  slot_used[victim] = *clock;
+  *loaded = 1;
+  return victim;
+}
+
+int moe_ref_tier_pick_swap(const uint32_t *heat, int nexpert, const int32_t *pinned, int npin,
+                           int32_t *slot, int32_t *eid, int64_t *gain) {
+  int z, e, cold = 0, hot = -1;
+  uint32_t fh = 0;
+  uint64_t fc;
+  if (!heat || !pinned || !slot || !eid || !gain || npin < 1 || nexpert < 1) return 0;
+  for (z = 0; z < npin; z++)
+    if (pinned[z] < 0 || pinned[z] >= nexpert) return 0;
+  for (z = 1; z < npin; z++)
+    if (heat[pinned[z]] < heat[pinned[cold]]) cold = z;
+  for (e = 0; e < nexpert; e++) {
+    int resident = 0;
+    for (z = 0; z < npin; z++) {
+      if (pinned[z] == e) {
+        resident = 1;
+        break;
+      }
+    }
+    if (!resident && heat[e] > fh) {
+      fh = heat[e];
+      hot = e;
+    }
+  }
+  if (hot < 0) return 0;
+  fc = heat[pinned[cold]];
+  if ((uint64_t)fh <= fc + fc / 4 + 4) return 0;
+  *slot = cold;
+  *eid = hot;
+  *gain = (int64_t)fh - (int64_t)fc;
+  return 1;
+}
+
+uint64_t moe_ref_tier_lfru_score(uint32_t heat, uint32_t last, uint32_t clock) {
+  uint32_t age = clock - last;
+  uint32_t recent = age < 255u ? 255u - age : 0u;
+  return ((uint64_t)heat << 8) | (uint64_t)recent;
+}

@@ -120,6 +120,33 @@ int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *
  * y = x * r * gamma. */
 int moe_ref_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y);
 
+/* Section 05 per-layer expert cache, one lookup (the article's expert_get):
+ * the layer's cache has cap slots, of which *n_used are filled; slot_eid[z]
+ * is the expert held by slot z and slot_used[z] the clock value of its last
+ * use.  A held expert is a hit: its slot gets the next clock value.  Else it
+ * is a miss: the next unused slot if any, otherwise the slot with the
+ * smallest use value found first scanning from slot 0, gets the expert and
+ * the next clock value.  *clock, *hits and *misses are the counters the
+ * article keeps in its model (shared by all layers).  Returns the slot and
+ * sets *loaded to 1 for a miss, 0 for a hit. */
+int moe_ref_expert_get(int32_t *slot_eid, uint64_t *slot_used, int cap, int *n_used,
+                       uint64_t *clock, uint64_t *hits, uint64_t *misses, int32_t eid,
+                       int *loaded);
+
+/* Section 13 swap decision for the pinned tier: the coldest pinned expert (by
+ * heat, first of equals) against the hottest expert not pinned (first of
+ * equals; heat must exceed 0).  Swap when the newcomer's heat exceeds
+ * fc + fc/4 + 4 (fc = the coldest one's heat, fc/4 rounded down).  Reading:
+ * that bound is evaluated without wrap-around (the article's listing adds in
+ * 32 bits; heats that large never occur in a run).  Returns 1 with the pinned
+ * position, the expert and the heat gain, else 0. */
+int moe_ref_tier_pick_swap(const uint32_t *heat, int nexpert, const int32_t *pinned, int npin,
+                           int32_t *slot, int32_t *eid, int64_t *gain);
+
+/* Section 13 frequency-first score: (heat << 8) | recent, recent = 255 - age
+ * for age = clock - last below 255, else 0 (unsigned 32-bit age). */
+uint64_t moe_ref_tier_lfru_score(uint32_t heat, uint32_t last, uint32_t clock);
+
 #ifdef __cplusplus
 }
 #endif

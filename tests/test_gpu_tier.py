@@ -1,0 +1,81 @@
+"""GPU checks of the given-routing call and of the expert residency tiers
+(article section 05 expert cache, section 13 tiers): a layer whose routed
+experts live in pinned host memory and a few HBM slots returns the same bits
+as the fully resident layer, and its hits and misses are the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import int4_expert_gemv_moe_amd as moe
+import oracle
+import synth
+from gpu_util import bias_for, device_layer, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+TINY, GLM = synth.TINY, synth.GLM
+MID = synth.Shape(D=512, I=256, E=64, K=8)
+
+
+def _resident(dl, x):
+    S, K = x.shape[0], dl.cfg.K
+    ws = moe.Workspace(dl.cfg, S, moe.WS_FORWARD)
+    idx = torch.empty(S, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(S, K, dtype=torch.float32, device="cuda")
+    o = moe.moe_layer_forward(dl, x, ws, topk_idx=idx, topk_w=w)
+    return o, idx, w
+
+
+def _bits(t):
+    return to_np(t).view(np.uint32)
+
+
+@pytest.mark.parametrize("shape,S", [(TINY, 4), (MID, 5), (GLM, 1), (GLM, 3)])
+def test_routed_call_equals_per_token_path(shape, S):
+    say(f"routed call D={shape.D} E={shape.E} S={S}")
+    dl = device_layer(5, shape, 0, bias_for("uniform", 5, shape))
+    x = torch.from_numpy(synth.activations(31, S, shape.D)).cuda()
+    ref, idx, w = _resident(dl, x)
+    out = moe.moe_layer_forward_routed(dl, x, idx, w, moe.Workspace(dl.cfg, S, moe.WS_FORWARD))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out), _bits(ref))
+
+
+def test_routed_call_clamps_indices():
+    shape = TINY
+    dl = device_layer(6, shape, 0, bias_for("uniform", 6, shape))
+    x = torch.from_numpy(synth.activations(32, 3, shape.D)).cuda()
+    w = torch.tensor([[0.7, 1.1], [2.0, 0.5], [1.0, 1.0]], dtype=torch.float32, device="cuda")
+    bad = torch.tensor([[-5, 3], [shape.E + 3, 1], [2, 2 ** 30]], dtype=torch.int32, device="cuda")
+    good = torch.tensor([[0, 3], [shape.E - 1, 1], [2, shape.E - 1]], dtype=torch.int32,
+                        device="cuda")
+    a = moe.moe_layer_forward_routed(dl, x, bad, w, moe.Workspace(dl.cfg, 3, moe.WS_FORWARD))
+    b = moe.moe_layer_forward_routed(dl, x, good, w, moe.Workspace(dl.cfg, 3, moe.WS_FORWARD))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(a), _bits(b))
+
+
+@pytest.mark.parametrize("shape,n_slots,S,calls", [(MID, 16, 1, 40), (MID, 24, 3, 20),
+                                                   (GLM, 24, 1, 12)])
+def test_tiered_layer_matches_resident_layer(shape, n_slots, S, calls):
+    say(f"tiered D={shape.D} E={shape.E} slots={n_slots} S={S}")
+    dl = device_layer(7, shape, 0, bias_for("zipf", 7, shape, 0, 0.05))
+    tl = moe.TieredLayer.from_device_layer(dl, n_slots)
+    cache = oracle.ExpertCache(1, n_slots)
+    wsr = moe.Workspace(dl.cfg, S, moe.WS_ROUTER)
+    ws = moe.Workspace(dl.cfg, S, moe.WS_FORWARD)
+    x_all = torch.from_numpy(synth.activations(33, S * calls, shape.D)).cuda()
+    hits = 0
+    for c in range(calls):
+        x = x_all[c * S:(c + 1) * S]
+        ref, idx, _ = _resident(dl, x)
+        out, misses = tl.forward(x, wsr, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(out), _bits(ref)), f"call {c}"
+        flat = to_np(idx).ravel().tolist()
+        eids = [e for i, e in enumerate(flat) if e not in flat[:i]]  # first appearance
+        expect = [cache.get(0, e)[1] for e in eids]
+        assert misses == sum(expect), f"call {c}"
+        hits += len(eids) - misses
+    assert tl.tier.stats() == (cache.hits, cache.misses)
+    say(f"  hits {cache.hits} misses {cache.misses}")
