@@ -203,6 +203,61 @@ def bench_verify(layer, iters: int = 20):
             "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
 
 
+def bench_tiered(layer, slot_counts=(192, 64), warm: int = 64, timed: int = 192):
+    """Decode through one GLM-shape layer whose routed experts live in pinned
+    host memory and only n_slots HBM slab slots (section 05 LRU expert cache,
+    section 13 slab reads), Zipf(1.1)-skewed routing, one token per call: the
+    router runs on the device, the host maps the selected experts to slots and
+    copies the missing 18.9 MB slabs in, then the block runs on the slot stack
+    with the given routing.  Wall time per token after `warm` tokens."""
+    import numpy as np
+    import torch
+
+    import int4_expert_gemv_moe_amd as moe
+    import synth
+
+    n = warm + timed
+    wr = synth.router_w(0, synth.GLM)
+    x_np, _, _ = synth.zipf_activations(1, synth.GLM, n, wr)
+    zl = moe.DeviceLayer(layer.cfg, torch.from_numpy(wr).cuda(),
+                         torch.zeros(E, dtype=torch.float32, device="cuda"), layer.routed,
+                         layer.shared)
+    x = torch.from_numpy(x_np).cuda()
+    wsr = moe.Workspace(zl.cfg, 1, moe.WS_ROUTER)
+    ws = moe.Workspace(zl.cfg, 1, moe.WS_FORWARD)
+    out = torch.empty(1, D, dtype=torch.float32, device="cuda")
+    res = {"workload": "GLM-shape layer decode, 1 token/call, Zipf(1.1) routing, routed experts in "
+                       "pinned host memory with n_slots HBM slab slots (LRU), shared expert and "
+                       "router resident",
+           "tokens_timed": timed, "slab_bytes": EXPERT_BYTES}
+    host = None
+    for n_slots in slot_counts:
+        tl = moe.TieredLayer.from_device_layer(zl, n_slots, host_slabs=host)
+        host = tl.host_slabs
+        for t in range(warm):
+            tl.forward(x[t:t + 1], wsr, ws, out=out)
+        torch.cuda.synchronize()
+        h0, m0 = tl.tier.stats()
+        t0 = time.perf_counter()
+        for t in range(warm, n):
+            tl.forward(x[t:t + 1], wsr, ws, out=out)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / timed
+        h1, m1 = tl.tier.stats()
+        hits, misses = h1 - h0, m1 - m0
+        key = f"slots_{n_slots}_of_{E}"
+        res[key] = {"us_per_token": round(us, 1), "tokens_per_s": round(1e6 / us, 1),
+                    "hit_rate": round(hits / max(1, hits + misses), 4),
+                    "misses_per_token": round(misses / timed, 3),
+                    "h2d_GB_per_token": round(misses * EXPERT_BYTES / timed / 1e9, 4),
+                    "h2d_GBps": round(misses * EXPERT_BYTES / (us * timed) / 1e3, 1)}
+        log(f"tiered {key}: {us:.1f} us/token, hit rate {res[key]['hit_rate']}")
+        del tl
+    del host
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_stack(steps: int = 64):
     """48 GLM-shape layers resident in HBM (per-layer Zipf-skewed routing,
     RMSNorm + residual, one MOE_F_PRENORM call per layer): decode steps of
@@ -298,7 +353,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the verify, prefill and 48-layer stack measurements")
-    ap.add_argument("--only", choices=["verify", "prefill", "stack"],
+    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered"],
                     help="run only that secondary measurement and print its record (for profiling)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay pass (value then comes from the stream pass); "
@@ -337,7 +392,8 @@ def main():
             rec = bench_stack()
         else:
             layer = build_device_layer(0, synth.GLM, 0, synth.router_b_uniform(0, synth.GLM, 0))
-            rec = (bench_verify if args.only == "verify" else bench_prefill)(layer)
+            rec = {"verify": bench_verify, "prefill": bench_prefill,
+                   "tiered": bench_tiered}[args.only](layer)
         print(json.dumps(rec), flush=True)
         return
     t0 = time.time()
@@ -473,7 +529,8 @@ def main():
     secondary = None
     if not args.no_secondary:
         secondary = {}
-        for key, fn in (("verify_64_zipf", bench_verify), ("prefill_2048", bench_prefill)):
+        for key, fn in (("verify_64_zipf", bench_verify), ("prefill_2048", bench_prefill),
+                        ("tiered_decode", bench_tiered)):
             try:
                 secondary[key] = fn(layers[0])
             except Exception as exc:  # reported, the headline line is still printed

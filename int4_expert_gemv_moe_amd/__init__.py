@@ -472,14 +472,24 @@ class TieredLayer:
 
     @staticmethod
     def from_device_layer(dl: DeviceLayer, n_slots: int, tier: Tier | None = None,
-                          layer_index: int = 0) -> "TieredLayer":
+                          layer_index: int = 0, host_slabs: torch.Tensor | None = None
+                          ) -> "TieredLayer":
+        """host_slabs: reuse the pinned slabs of an earlier TieredLayer of the
+        same layer instead of packing them again."""
         lay = slab_layout(dl.cfg)
         E = dl.cfg.E
-        staged = pack_slabs(dl.routed, lay, torch.empty(E, lay.bytes, dtype=torch.uint8,
-                                                         device=dl.router_w.device))
-        host = torch.empty(E, lay.bytes, dtype=torch.uint8, pin_memory=True)
-        host.copy_(staged)
-        del staged
+        host = host_slabs
+        if host is None:
+            host = torch.empty(E, lay.bytes, dtype=torch.uint8, pin_memory=True)
+            for e0 in range(0, E, 16):  # staged 16 experts at a time
+                e1 = min(E, e0 + 16)
+                part = DeviceExperts(*(t[e0:e1] for t in (
+                    dl.routed.gate_q4, dl.routed.gate_s, dl.routed.up_q4, dl.routed.up_s,
+                    dl.routed.down_q4, dl.routed.down_s)))
+                staged = pack_slabs(part, lay, torch.empty(e1 - e0, lay.bytes, dtype=torch.uint8,
+                                                           device=dl.router_w.device))
+                host[e0:e1].copy_(staged)
+            del staged
         slots = torch.empty(n_slots, lay.bytes, dtype=torch.uint8, device=dl.router_w.device)
         tier = tier or Tier(1, E, n_slots)
         return TieredLayer(dl.cfg, dl.router_w, dl.router_b, SlabExperts(slots, lay), dl.shared,
