@@ -21,7 +21,7 @@ ACCUMULATE = 1
 class Config(ctypes.Structure):
     _fields_ = [("D", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("n_shared", ctypes.c_int32),
-                ("routed_scale", ctypes.c_float)]
+                ("routed_scale", ctypes.c_float), ("expert_topp", ctypes.c_float)]
 
 
 class QMat(ctypes.Structure):
@@ -58,6 +58,7 @@ def lib():
         L.moe_ref_layer_forward.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint]
         L.moe_ref_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, vp, vp]
         L.moe_ref_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp]
+        L.moe_ref_expert_keff.argtypes = [vp, i32, f32]
         L.moe_ref_expert_get.argtypes = [vp, vp, i32, vp, vp, vp, vp, ctypes.c_int32, vp]
         L.moe_ref_tier_pick_swap.argtypes = [vp, i32, vp, i32, vp, vp, vp]
         L.moe_ref_tier_lfru_score.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
@@ -79,8 +80,8 @@ def _c(a, dt):
     return np.ascontiguousarray(a, dtype=dt)
 
 
-def make_config(D, I, E, K, n_shared=1, routed_scale=2.5) -> Config:
-    return Config(D, I, E, K, n_shared, routed_scale)
+def make_config(D, I, E, K, n_shared=1, routed_scale=2.5, expert_topp=0.0) -> Config:
+    return Config(D, I, E, K, n_shared, routed_scale, expert_topp)
 
 
 # ---- primitives -------------------------------------------------------------
@@ -284,3 +285,9 @@ def tier_pick_swap(heat, pinned):
 
 def tier_lfru_score(heat: int, last: int, clock: int) -> int:
     return int(lib().moe_ref_tier_lfru_score(heat, last, clock))
+
+
+def expert_keff(w, p: float) -> int:
+    """Adaptive expert top-p: experts kept for one token's weights w[K]."""
+    w = np.ascontiguousarray(w, np.float32)
+    return int(lib().moe_ref_expert_keff(w.ctypes.data, w.size, float(p)))

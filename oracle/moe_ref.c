@@ -17,7 +17,21 @@
 
 static int bad_cfg(const moe_ref_config *c) {
   return !c || c->D < 1 || c->I < 1 || c->E < 1 || c->K < 1 || c->K > c->E || c->K > 64 ||
-         c->n_shared < 0 || c->n_shared > 1;
+         c->n_shared < 0 || c->n_shared > 1 || !(c->expert_topp >= 0.f && c->expert_topp <= 1.f);
+}
+
+int moe_ref_expert_keff(const float *w, int K, float p) {
+  float total = 0.f, run = 0.f, thr;
+  int k;
+  if (!w || K < 1) return -1;
+  if (!(p > 0.f && p < 1.f)) return K;
+  for (k = 0; k < K; k++) total = total + w[k];
+  thr = p * total;
+  for (k = 0; k < K; k++) {
+    run = run + w[k];
+    if (run >= thr) return k + 1;
+  }
+  return K;
 }
 
 /* ---- section 06: int4 weight container ------------------------------------ */
@@ -234,13 +248,14 @@ static int layer_ok(const moe_ref_config *cfg, const moe_ref_layer *L) {
   return 1;
 }
 
-static void combine_row(const moe_ref_config *cfg, const float *w, const float *stage, float *out,
-                        unsigned flags) {
-  /* stage holds K (+1 shared) rows of D floats for one token */
+static void combine_row(const moe_ref_config *cfg, const float *w, int keff, const float *stage,
+                        float *out, unsigned flags) {
+  /* stage holds K (+1 shared) rows of D floats for one token; the first keff
+   * routed rows take part */
   const int D = cfg->D, K = cfg->K;
   for (int d = 0; d < D; d++) {
     float acc = 0.f;
-    for (int k = 0; k < K; k++) acc += w[k] * stage[(int64_t)k * D + d];
+    for (int k = 0; k < keff; k++) acc += w[k] * stage[(int64_t)k * D + d];
     if (cfg->n_shared == 1) acc += stage[(int64_t)K * D + d];
     if (flags & MOE_REF_ACCUMULATE)
       out[d] = out[d] + acc;
@@ -264,13 +279,14 @@ int moe_ref_layer_forward(const moe_ref_config *cfg, const moe_ref_layer *layer,
     rc = moe_ref_router_topk(cfg, xs, 1, layer->router_w, layer->router_b, idx, w, NULL, NULL);
     if (rc) break;
     float sxs = moe_ref_quant_row_i8(xs, D, xq);
-    for (int k = 0; k < K && rc == 0; k++)
+    const int keff = moe_ref_expert_keff(w, K, cfg->expert_topp);
+    for (int k = 0; k < keff && rc == 0; k++)
       rc = moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, &layer->experts[idx[k]],
                                     stage + (int64_t)k * D, NULL, NULL, NULL, NULL);
     if (rc == 0 && cfg->n_shared == 1)
       rc = moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, layer->shared, stage + (int64_t)K * D, NULL,
                                     NULL, NULL, NULL);
-    if (rc == 0) combine_row(cfg, w, stage, out + (int64_t)s * D, flags);
+    if (rc == 0) combine_row(cfg, w, keff, stage, out + (int64_t)s * D, flags);
   }
   free(xq);
   free(stage);
@@ -294,23 +310,27 @@ int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *
   int8_t *xg = (int8_t *)malloc((size_t)S * D);
   float *sg = (float *)malloc((size_t)S * sizeof(float));
   float *yg = (float *)malloc((size_t)S * D * sizeof(float));
+  int32_t *keff = (int32_t *)malloc((size_t)S * sizeof(int32_t));
   int rc = -2;
-  if (!idx || !w || !xq || !sx || !stage || !uniq || !seen || !rows || !slot || !xg || !sg || !yg)
+  if (!idx || !w || !xq || !sx || !stage || !uniq || !seen || !rows || !slot || !xg || !sg || !yg ||
+      !keff)
     goto done;
   rc = moe_ref_router_topk(cfg, x, S, layer->router_w, layer->router_b, idx, w, NULL, NULL);
   if (rc) goto done;
   moe_ref_quant_act_i8(x, S, D, xq, sx);
-  /* union of the selected experts, in order of first appearance */
+  /* keff[s] experts per token; the union of the kept experts, in order of
+   * first appearance */
+  for (int s = 0; s < S; s++) keff[s] = moe_ref_expert_keff(w + (int64_t)s * K, K, cfg->expert_topp);
   int nu = 0;
   for (int s = 0; s < S; s++)
-    for (int k = 0; k < K; k++) {
+    for (int k = 0; k < keff[s]; k++) {
       int e = idx[(int64_t)s * K + k];
       if (!seen[e]) { seen[e] = 1; uniq[nu++] = e; }
     }
   for (int u = 0; u < nu && rc == 0; u++) {
     int e = uniq[u], nr = 0;
     for (int s = 0; s < S; s++)
-      for (int k = 0; k < K; k++)
+      for (int k = 0; k < keff[s]; k++)
         if (idx[(int64_t)s * K + k] == e) { rows[nr] = s; slot[nr] = k; nr++; }
     for (int r = 0; r < nr; r++) {
       memcpy(xg + (int64_t)r * D, xq + (int64_t)rows[r] * D, (size_t)D);
@@ -329,8 +349,8 @@ int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *
   }
   if (rc == 0)
     for (int s = 0; s < S; s++)
-      combine_row(cfg, w + (int64_t)s * K, stage + (int64_t)s * slots * D, out + (int64_t)s * D,
-                  flags);
+      combine_row(cfg, w + (int64_t)s * K, keff[s], stage + (int64_t)s * slots * D,
+                  out + (int64_t)s * D, flags);
   if (rc == 0) {
     if (idx_out) memcpy(idx_out, idx, (size_t)S * K * sizeof(int32_t));
     if (w_out) memcpy(w_out, w, (size_t)S * K * sizeof(float));
@@ -339,7 +359,7 @@ int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *
   }
 done:
   free(idx); free(w); free(xq); free(sx); free(stage); free(uniq); free(seen);
-  free(rows); free(slot); free(xg); free(sg); free(yg);
+  free(rows); free(slot); free(xg); free(sg); free(yg); free(keff);
   return rc;
 }
 

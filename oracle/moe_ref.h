@@ -41,6 +41,7 @@ typedef struct {
   int32_t K;          /* experts per token */
   int32_t n_shared;   /* 0 or 1 shared expert */
   float routed_scale; /* routed scaling factor (2.5 for the GLM shape) */
+  float expert_topp;  /* adaptive expert top-p in (0, 1); 0 or 1 = all K experts */
 } moe_ref_config;
 
 typedef struct {
@@ -119,6 +120,15 @@ int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *
 /* Section 04 RMSNorm: ms = mean of squares in double, r = 1/sqrtf(ms + eps),
  * y = x * r * gamma. */
 int moe_ref_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y);
+
+/* Adaptive expert top-p (section 11 runs keff[s] experts per token; the
+ * article's --topp option, its reduced-reads figures in the summary pages).
+ * The article gives no formula; reading: keff is the smallest k in 1..K
+ * whose running sum w[0] + ... + w[k-1] (float32, in selection order) reaches
+ * p * (w[0] + ... + w[K-1]) (float32 total in the same order, one float32
+ * product); p <= 0 or p >= 1 keeps all K.  The kept experts keep their
+ * weights (no renormalization, as in the section 11 listing). */
+int moe_ref_expert_keff(const float *w, int K, float p);
 
 /* Section 05 per-layer expert cache, one lookup (the article's expert_get):
  * the layer's cache has cap slots, of which *n_used are filled; slot_eid[z]
