@@ -258,6 +258,64 @@ def bench_tiered(layer, slot_counts=(192, 64), warm: int = 64, timed: int = 192)
     return res
 
 
+def bench_topp(layers, x, steps: int = 512, ps=(0.7, 0.9, 1.0)):
+    """Per-token decode with the adaptive expert top-p: the same layer
+    replicas (cold in the MALL) and tokens as the headline decode, one token
+    per call, plain stream launches between events.  Reports the experts
+    kept per token and the weight bytes actually read."""
+    import numpy as np
+    import torch
+
+    import int4_expert_gemv_moe_amd as moe
+
+    T, R = x.shape[0], len(layers)
+    res = {"workload": "GLM-shape MoE layer decode, 1 token/step, adaptive expert top-p "
+                       "(keff of the top-8 per token), 8 cold layer replicas",
+           "steps": steps}
+    lib = moe.lib()
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    out = torch.empty(1, D, dtype=torch.float32, device="cuda")
+    xp = [ctypes.c_void_p(x[t].data_ptr()) for t in range(T)]
+    op = ctypes.c_void_p(out.data_ptr())
+    lstructs = [l.cstruct() for l in layers]
+    lrefs = [ctypes.byref(s_) for s_ in lstructs]
+    for p in ps:
+        c = layers[0].cfg
+        cfg = moe.config(c.D, c.I, c.E, c.K, c.n_shared, c.routed_scale, p)
+        tl = [moe.DeviceLayer(cfg, l.router_w, l.router_b, l.routed, l.shared) for l in layers]
+        ws = moe.Workspace(cfg, 1, moe.WS_FORWARD)
+        keff = torch.empty(T, dtype=torch.int32, device="cuda")
+        for t in range(T):  # kept experts per token (each token on its replica)
+            moe.moe_layer_forward(tl[t % R], x[t:t + 1], ws, out=out, keff=keff[t:t + 1])
+        torch.cuda.synchronize()
+        mean_keff = float(keff.float().mean())
+        cref = ctypes.byref(cfg)
+
+        def run(n):
+            rc = 0
+            for i in range(n):
+                rc |= lib.moe_layer_forward(cref, lrefs[i % R], xp[i % T], 1, op, 0, None, ws.ptr,
+                                            ws.nbytes, st)
+            if rc:
+                raise moe.MoeError(f"moe_layer_forward failed ({rc})")
+
+        run(64)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        nbytes = (mean_keff + 1) * EXPERT_BYTES + ROUTER_BYTES + 2 * D * 4
+        res[f"topp_{p}"] = {"us_per_token": round(us, 3), "mean_keff": round(mean_keff, 3),
+                            "bytes_per_token": int(nbytes),
+                            "GBps": round(nbytes / us / 1e3, 1),
+                            "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+        log(f"top-p {p}: {us:.2f} us/token, mean keff {mean_keff:.2f}")
+    return res
+
+
 def bench_stack(steps: int = 64):
     """48 GLM-shape layers resident in HBM (per-layer Zipf-skewed routing,
     RMSNorm + residual, one MOE_F_PRENORM call per layer): decode steps of
@@ -529,6 +587,10 @@ def main():
     secondary = None
     if not args.no_secondary:
         secondary = {}
+        try:
+            secondary["topp_decode"] = bench_topp(layers, x)
+        except Exception as exc:  # reported, the headline line is still printed
+            secondary["topp_decode"] = {"error": f"{type(exc).__name__}: {exc}"}
         for key, fn in (("verify_64_zipf", bench_verify), ("prefill_2048", bench_prefill),
                         ("tiered_decode", bench_tiered)):
             try:

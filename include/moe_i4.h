@@ -75,6 +75,13 @@ typedef struct {
   int32_t K;          /* experts per token (8) */
   int32_t n_shared;   /* shared experts, 0 or 1 */
   float routed_scale; /* routed scaling factor (2.5) */
+  /* Adaptive expert top-p (section 11 runs keff[s] experts per token).  In
+   * (0, 1): token s keeps its first keff selected experts, keff the smallest
+   * k in 1..K whose float32 running weight sum (selection order) reaches
+   * expert_topp * the float32 sum of its K weights; the kept experts keep
+   * their weights.  0 or 1: all K experts.  Other values: MOE_EINVAL.
+   * moe_layer_forward_routed always runs all K given experts. */
+  float expert_topp;
 } moe_config;
 
 /* One packed int4 matrix per expert, stacked over experts.  Expert e's matrix
@@ -115,6 +122,7 @@ typedef struct {
    * stream around its grouped gate/up and grouped down kernels. */
   hipEvent_t ev_gateup[2];
   hipEvent_t ev_down[2];
+  int32_t *keff;        /* [S] experts kept per token (K unless expert_topp is in (0, 1)) */
 } moe_probe;
 
 /* Human-readable name of a status code (static string). */

@@ -29,7 +29,7 @@ _lib = None
 class Config(ctypes.Structure):
     _fields_ = [("D", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("n_shared", ctypes.c_int32),
-                ("routed_scale", ctypes.c_float)]
+                ("routed_scale", ctypes.c_float), ("expert_topp", ctypes.c_float)]
 
 
 class QMat(ctypes.Structure):
@@ -49,7 +49,8 @@ class LayerC(ctypes.Structure):
 
 class Probe(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
-                ("ev_gateup", ctypes.c_void_p * 2), ("ev_down", ctypes.c_void_p * 2)]
+                ("ev_gateup", ctypes.c_void_p * 2), ("ev_down", ctypes.c_void_p * 2),
+                ("keff", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -129,8 +130,9 @@ def _dev(t: torch.Tensor, dtype, name: str):
     return t
 
 
-def config(D: int, I: int, E: int, K: int, n_shared: int = 1, routed_scale: float = 2.5) -> Config:
-    return Config(D, I, E, K, n_shared, routed_scale)
+def config(D: int, I: int, E: int, K: int, n_shared: int = 1, routed_scale: float = 2.5,
+           expert_topp: float = 0.0) -> Config:
+    return Config(D, I, E, K, n_shared, routed_scale, expert_topp)
 
 
 # ---- device weights -----------------------------------------------------------
@@ -267,10 +269,11 @@ def moe_expert_swiglu_i4(cfg: Config, xq: torch.Tensor, sx: torch.Tensor, expert
     return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
 
 
-def _probe(topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None):
+def _probe(topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None, keff=None):
     p = Probe()
     p.topk_idx = None if topk_idx is None else topk_idx.data_ptr()
     p.topk_w = None if topk_w is None else topk_w.data_ptr()
+    p.keff = None if keff is None else keff.data_ptr()
     if ev_gateup is not None:
         p.ev_gateup[0], p.ev_gateup[1] = ev_gateup
     if ev_down is not None:
@@ -279,7 +282,7 @@ def _probe(topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None):
 
 
 def _layer_call(fn_name, layer: DeviceLayer, x, out, flags, ws, topk_idx, topk_w, ev_gateup,
-                ev_down, stream, norm_gamma=None, norm_eps=1e-5):
+                ev_down, stream, norm_gamma=None, norm_eps=1e-5, keff=None):
     _dev(x, torch.float32, "x")
     S = x.shape[0]
     if out is None:
@@ -289,7 +292,7 @@ def _layer_call(fn_name, layer: DeviceLayer, x, out, flags, ws, topk_idx, topk_w
         _dev(norm_gamma, torch.float32, "norm_gamma")
         flags |= F_PRENORM
     L = layer.cstruct(norm_gamma, norm_eps)
-    probe = _probe(topk_idx, topk_w, ev_gateup, ev_down)
+    probe = _probe(topk_idx, topk_w, ev_gateup, ev_down, keff)
     fn = getattr(lib(), fn_name)
     _check(fn(ctypes.byref(layer.cfg), ctypes.byref(L), _ptr(x), S, _ptr(out), flags,
               ctypes.byref(probe), ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))), fn_name)
@@ -298,19 +301,21 @@ def _layer_call(fn_name, layer: DeviceLayer, x, out, flags, ws, topk_idx, topk_w
 
 def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None, flags: int = 0,
                       topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None, stream=None,
-                      norm_gamma=None, norm_eps: float = 1e-5):
-    """Per-token path: each token reads its own K experts and the shared one.
+                      norm_gamma=None, norm_eps: float = 1e-5, keff=None):
+    """Per-token path: each token reads its own K experts (keff with
+    cfg.expert_topp) and the shared one.
     norm_gamma: run the block on RMSNorm(x) (flag F_PRENORM); out may then be x."""
     return _layer_call("moe_layer_forward", layer, x, out, flags, ws, topk_idx, topk_w, ev_gateup,
-                       ev_down, stream, norm_gamma, norm_eps)
+                       ev_down, stream, norm_gamma, norm_eps, keff)
 
 
 def moe_layer_forward_batch(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None,
                             flags: int = 0, topk_idx=None, topk_w=None, ev_gateup=None,
-                            ev_down=None, stream=None, norm_gamma=None, norm_eps: float = 1e-5):
+                            ev_down=None, stream=None, norm_gamma=None, norm_eps: float = 1e-5,
+                            keff=None):
     """Unique-expert union path: each selected expert is read once per call."""
     return _layer_call("moe_layer_forward_batch", layer, x, out, flags, ws, topk_idx, topk_w,
-                       ev_gateup, ev_down, stream, norm_gamma, norm_eps)
+                       ev_gateup, ev_down, stream, norm_gamma, norm_eps, keff)
 
 
 def moe_stream_read(buf: torch.Tensor, stream=None) -> torch.Tensor:

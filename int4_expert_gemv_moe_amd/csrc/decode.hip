@@ -172,6 +172,7 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
 template <int NCH, bool MASKED, int ROWS>
 __device__ void gateup_routed(const DecodeArgs &a, int s, int gb) {
   __shared__ int sel[64];
+  __shared__ int keff;
   __shared__ GuLds L;
   const int wave = threadIdx.x >> 6;
   const int rowbytes = a.D >> 1;
@@ -181,13 +182,17 @@ __device__ void gateup_routed(const DecodeArgs &a, int s, int gb) {
   const float sxs = a.sx[s];
   if (a.given) {
     if ((int)threadIdx.x < a.K) sel[threadIdx.x] = expert_at(a, (int64_t)s * a.K + threadIdx.x);
+    if (threadIdx.x == 0) keff = a.K;
   } else if (wave == 0) {
     const bool pub = (gb == 0);
     topk_rounds(a.logits + (int64_t)s * a.E, a.bias, a.E, a.K, a.scale,
                 pub ? a.idx + (int64_t)s * a.K : nullptr, pub ? a.w + (int64_t)s * a.K : nullptr,
-                sel);
+                sel, a.topp, &keff);
   }
   __syncthreads();
+  // with top-p the block's share is taken from the kept slots only (every
+  // block computed the same keff); block 0 publishes it for phase C
+  if (gb == 0 && threadIdx.x == 0 && a.keff) a.keff[s] = keff;
   const ExpertSet &rt = a.rt;
   float *hbase = a.h + (int64_t)s * a.P * a.I;
   const int I = a.I;
@@ -200,7 +205,7 @@ __device__ void gateup_routed(const DecodeArgs &a, int s, int gb) {
     return m;
   };
   int lo, hi;
-  split_rows(a.K * a.I, a.n_gu_rt, gb, lo, hi);
+  split_rows(keff * a.I, a.n_gu_rt, gb, lo, hi);
   const int first = lo + wave * ROWS;
   const uint8_t *dummy = reinterpret_cast<const uint8_t *>(a.xq + (int64_t)s * a.D);
   GuStage<NCH, ROWS> sa;
@@ -558,9 +563,12 @@ __global__ __launch_bounds__(64 * kCWaves) void decode_c_kernel(DecodeArgs a) {
   __shared__ __align__(16) int part[kCWaves][RB][64];
   const int s = blockIdx.y, db = blockIdx.x;
   const int lane = threadIdx.x & 63, p = threadIdx.x >> 6;
-  const int np = a.p_hi - a.p_lo;
+  // routed slots of this launch that the token keeps (top-p); the wave's
+  // slot does not depend on it, so the index and keff loads go out together
+  const int keff = a.keff ? a.keff[s] : a.K;
+  const int np = max(0, min(a.p_hi, keff) - a.p_lo);
   const bool live = p < np;  // uniform across the wave
-  const int slot = a.p_lo + (live ? p : 0);
+  const int slot = a.p_lo + min(p, a.p_hi - a.p_lo - 1);
   const int e = expert_at(a, (int64_t)s * a.K + slot);
   const RowPtr M = pick(a.rt.down, a.rt.down, false, e);
   const float *hrow = a.h + ((int64_t)s * a.P + slot) * a.I;

@@ -88,7 +88,8 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
     // visible to the whole workgroup after the barrier below
     for (int s = threadIdx.x >> 6; s < a.S; s += blockDim.x >> 6)
       topk_rounds_m<4>(a.logits + (int64_t)s * a.E, a.bias, a.E, a.K, a.scale,
-                       a.idx + (int64_t)s * a.K, a.wts + (int64_t)s * a.K, nullptr);
+                       a.idx + (int64_t)s * a.K, a.wts + (int64_t)s * a.K, nullptr, a.topp,
+                       a.keff ? a.keff + s : nullptr);
   }
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     cnt[g] = 0;
@@ -96,7 +97,10 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
   }
   __syncthreads();
   const int np = a.S * a.K;
-  for (int p = threadIdx.x; p < np; p += blockDim.x) atomicAdd(&cnt[a.idx[p]], 1);
+  // pairs past a token's keff (adaptive top-p) are not grouped
+  auto kept = [&](int p) { return !a.keff || (p % a.K) < a.keff[p / a.K]; };
+  for (int p = threadIdx.x; p < np; p += blockDim.x)
+    if (kept(p)) atomicAdd(&cnt[a.idx[p]], 1);
   if (threadIdx.x == 0) cnt[a.E] = a.n_shared ? a.S : 0;
   __syncthreads();
   // exclusive scan over G <= 1025 counts: each wave scans a 64-wide slice in
@@ -120,6 +124,7 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
   }
   __syncthreads();
   for (int p = threadIdx.x; p < np; p += blockDim.x) {
+    if (!kept(p)) continue;
     const int e = a.idx[p];
     const int pos = off[e] + atomicAdd(&fill[e], 1);
     a.pairs[pos] = (p / a.K) * a.P + (p % a.K);
@@ -300,12 +305,13 @@ template <bool VEC>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int s = blockIdx.y;
   const float *wts = a.w + s * a.K;
+  const int K = a.keff ? a.keff[s] : a.K;  // routed slots kept (top-p)
   if (!VEC) {
     const int d = blockIdx.x * blockDim.x + threadIdx.x;
     if (d >= a.D) return;
     const float *st = a.stage + (int64_t)s * a.P * a.D + d;
     float acc = 0.f;
-    for (int k = 0; k < a.K; k++) acc = acc + wts[k] * st[(int64_t)k * a.D];
+    for (int k = 0; k < K; k++) acc = acc + wts[k] * st[(int64_t)k * a.D];
     if (a.n_shared) acc = acc + st[(int64_t)a.K * a.D];
     float *o = a.out + (int64_t)s * a.D + d;
     *o = (a.flags & MOE_F_ACCUMULATE) ? (*o + acc) : acc;
@@ -316,14 +322,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const f4v *st = reinterpret_cast<const f4v *>(a.stage + (int64_t)s * a.P * a.D + d);
   const int64_t step = a.D / 4;
   f4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.K; k0 += 4) {
+  for (int k0 = 0; k0 < K; k0 += 4) {
     f4v v[4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
-      if (k0 + i < a.K) v[i] = __builtin_nontemporal_load(st + (int64_t)(k0 + i) * step);
+      if (k0 + i < K) v[i] = __builtin_nontemporal_load(st + (int64_t)(k0 + i) * step);
 #pragma unroll
     for (int i = 0; i < 4; i++)
-      if (k0 + i < a.K) {
+      if (k0 + i < K) {
         const float w = wts[k0 + i];
         acc.x = acc.x + w * v[i].x;
         acc.y = acc.y + w * v[i].y;

@@ -43,6 +43,7 @@ int check_cfg(const moe_config *c) {
   if (c->E < 1 || c->E > 1024 || c->K < 1 || c->K > c->E || c->K > 64) return MOE_ESHAPE;
   if (c->n_shared < 0 || c->n_shared > 1) return MOE_ESHAPE;
   if (!(c->routed_scale == c->routed_scale)) return MOE_EINVAL;
+  if (!(c->expert_topp >= 0.f && c->expert_topp <= 1.f)) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -98,6 +99,7 @@ size_t carve(const moe_config &c, int S, int which, char *base, Work *w) {
     t.logits = (float *)take(s * c.E * 4);
     t.idx = (int32_t *)take(s * c.K * 4);
     t.w = (float *)take(s * c.K * 4);
+    t.keff = (int32_t *)take(s * 4);
   }
   if (which != W_ROUTER) {
     t.xq = (int8_t *)take(s * c.D);
@@ -205,7 +207,7 @@ int run_router(const moe_config &c, const float *x, int S, const float *W, const
   r.P = c.K + c.n_shared;
   MOE_TRY_HIP(launch_router(r, with_quant, st));
   if (with_topk) {
-    TopkArgs t{w.logits, b, S, c.E, c.K, c.routed_scale, w.idx, w.w};
+    TopkArgs t{w.logits, b, S, c.E, c.K, c.routed_scale, w.idx, w.w, c.expert_topp, w.keff};
     MOE_TRY_HIP(launch_topk(t, st));
   }
   return MOE_OK;
@@ -219,6 +221,8 @@ int copy_probe(const moe_config &c, int S, const moe_probe *probe, const Work &w
     MOE_TRY_HIP(hipMemcpyAsync(probe->topk_idx, w.idx, n * 4, hipMemcpyDeviceToDevice, st));
   if (probe->topk_w)
     MOE_TRY_HIP(hipMemcpyAsync(probe->topk_w, w.w, n * 4, hipMemcpyDeviceToDevice, st));
+  if (probe->keff)
+    MOE_TRY_HIP(hipMemcpyAsync(probe->keff, w.keff, (size_t)S * 4, hipMemcpyDeviceToDevice, st));
   return MOE_OK;
 }
 
@@ -418,6 +422,8 @@ int layer_forward_impl(const moe_config *cfg, const moe_layer *layer, const floa
   d.idx = given ? const_cast<int32_t *>(given_idx) : w.idx;
   d.w = given ? const_cast<float *>(given_w) : w.w;
   d.given = given ? 1 : 0;
+  d.topp = given ? 0.f : c.expert_topp;
+  d.keff = given ? nullptr : w.keff;
   d.h = w.h;
   d.ysh = w.ysh;
   d.tmp = w.tmp;
@@ -504,6 +510,8 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
   GroupArgs ga{w.idx,    S,     c.E,     c.K,      P, c.n_shared, w.gcount, w.goff, w.pairs,
                (mfma_gu || mfma_dn) ? w.tiles : nullptr, w.ntiles, grouped_mfma_tile_rows(S)};
   ga.with_topk = topk_in_group ? 1 : 0;
+  ga.topp = c.expert_topp;
+  ga.keff = w.keff;
   ga.logits = w.logits;
   ga.bias = layer->router_b;
   ga.scale = c.routed_scale;
@@ -580,7 +588,7 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
     MOE_TRY_HIP(launch_grouped_down(d, stream));
   }
   MOE_TRY(record(probe, 1, 1, stream));
-  CombineArgs cb{w.stage, w.w, S, c.D, c.K, P, c.n_shared, out, flags};
+  CombineArgs cb{w.stage, w.w, S, c.D, c.K, P, c.n_shared, out, flags, w.keff};
   MOE_TRY_HIP(launch_combine(cb, stream));
   return MOE_OK;
 }

@@ -180,6 +180,7 @@ struct Work {
   float *logits;    // [S][E]
   int32_t *idx;     // [S][K]
   float *w;         // [S][K]
+  int32_t *keff;    // [S] experts kept per token
   float *h;         // [S][P][I]
   int8_t *hq;       // [S][P][I] permuted
   float *sh;        // [S][P]

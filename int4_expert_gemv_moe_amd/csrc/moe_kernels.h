@@ -46,6 +46,8 @@ struct TopkArgs {
   float scale;
   int32_t *idx;
   float *w;
+  float topp;             // adaptive expert top-p (keff per token)
+  int32_t *keff;          // [S] out
 };
 
 // Per-token ("decode") path: three launches, see decode.hip.
@@ -85,6 +87,8 @@ struct DecodeArgs {
   const float *gamma;       // optional [D]: phase A works on RMSNorm(x) with gamma, eps
   float eps;
   int given;                // routing given by the caller: idx and w are inputs
+  float topp;               // adaptive expert top-p (0: all K)
+  int32_t *keff;            // [S] experts kept per token (phase B writes, C reads); null: K
 };
 
 // Grouped (unique-expert union) kernels.
@@ -101,6 +105,8 @@ struct GroupArgs {
   const float *logits, *bias;
   float scale;
   float *wts;
+  float topp;             // adaptive expert top-p
+  int32_t *keff;          // [S]: written with the selection (with_topk), else read
 };
 
 // Grouped int8 MFMA GEMM of the union path (grouped_mfma.hip); mode 0 is
@@ -152,6 +158,7 @@ struct CombineArgs {
   int S, D, K, P, n_shared;
   float *out;
   unsigned flags;
+  const int32_t *keff;  // [S] routed slots combined per token
 };
 
 struct PackArgs {

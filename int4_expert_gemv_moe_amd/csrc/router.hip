@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (s >= a.S) return;
   topk_rounds(a.logits + (int64_t)s * a.E, a.bias, a.E, a.K, a.scale, a.idx + (int64_t)s * a.K,
-              a.w + (int64_t)s * a.K);
+              a.w + (int64_t)s * a.K, nullptr, a.topp, a.keff ? a.keff + s : nullptr);
 }
 
 // ---- router logits (+ quantization blocks) -----------------------------------

@@ -29,9 +29,52 @@ __device__ __forceinline__ int topk_key(float c) {
 // Lanes 0..rounds-1 then write their round's expert to idx_out / sel_out and
 // weight sigmoid(logit) * scale to w_out (each pointer optional; sel_out may
 // be shared memory).  Returns the expert of the last round on every lane.
+// Adaptive expert top-p over the weights of one token's selection (lane k
+// holds the weight of round k, k < K): the smallest k whose running sum, in
+// round order, reaches p times the sum of all K (float32, one rounding per
+// addition and one product); K when p is not in (0, 1).  Same on every lane.
+// (k is uniform, so each weight is read with a lane read into a scalar
+// register, a few cycles, rather than a cross-lane permute through LDS.)
+__device__ inline int topk_keff(float wk, int K, float p) {
+  if (!(p > 0.f && p < 1.f)) return K;
+  const int wb = __float_as_int(wk);
+  if (K <= 8) {
+    // unrolled, constant lanes: the eight reads issue back to back; the sums
+    // are the same left-to-right additions over k < K
+    float w[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) w[k] = __int_as_float(__builtin_amdgcn_readlane(wb, k));
+    float total = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+      if (k < K) total = total + w[k];
+    const float thr = p * total;
+    float run = 0.f;
+    int keff = K;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      if (k < K) {
+        run = run + w[k];
+        if (run >= thr && keff == K) keff = k + 1;
+      }
+    }
+    return keff;
+  }
+  float total = 0.f;
+  for (int k = 0; k < K; k++) total = total + __int_as_float(__builtin_amdgcn_readlane(wb, k));
+  const float thr = p * total;
+  float run = 0.f;
+  for (int k = 0; k < K; k++) {
+    run = run + __int_as_float(__builtin_amdgcn_readlane(wb, k));
+    if (run >= thr) return k + 1;
+  }
+  return K;
+}
+
 template <int MAXM>
 __device__ inline int topk_rounds_m(const float *logits, const float *bias, int E, int rounds,
-                                   float scale, int32_t *idx_out, float *w_out, int *sel_out) {
+                                   float scale, int32_t *idx_out, float *w_out, int *sel_out,
+                                   float topp = 0.f, int *keff_out = nullptr) {
   constexpr int kNone = static_cast<int>(0x807FFFFF);  // key of -inf
   constexpr int kPad = INT_MIN;
   const int lane = threadIdx.x & 63;
@@ -86,12 +129,17 @@ __device__ inline int topk_rounds_m(const float *logits, const float *bias, int 
     v[MAXM - 1] = pop ? kPad : v[MAXM - 1];
     ix[MAXM - 1] = pop ? INT_MAX : ix[MAXM - 1];
   }
+  const float wk = lane < rounds ? sigmoid(logits[mine]) * scale : 0.f;
   if (lane < rounds) {
     if (sel_out) sel_out[lane] = mine;
     if (idx_out) {
       idx_out[lane] = mine;
-      w_out[lane] = sigmoid(logits[mine]) * scale;
+      w_out[lane] = wk;
     }
+  }
+  if (keff_out) {
+    const int ke = topk_keff(wk, rounds, topp);
+    if (lane == 0) *keff_out = ke;
   }
   return sel;
 }
@@ -100,10 +148,13 @@ __device__ inline int topk_rounds_m(const float *logits, const float *bias, int 
 // caller synchronizes before reading it.
 __device__ inline int topk_rounds(const float *logits, const float *bias, int E, int rounds,
                                   float scale, int32_t *idx_out, float *w_out,
-                                  int *sel_out = nullptr) {
+                                  int *sel_out = nullptr, float topp = 0.f,
+                                  int *keff_out = nullptr) {
   if (E <= 256)
-    return topk_rounds_m<4>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
-  return topk_rounds_m<16>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out);
+    return topk_rounds_m<4>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out, topp,
+                            keff_out);
+  return topk_rounds_m<16>(logits, bias, E, rounds, scale, idx_out, w_out, sel_out, topp,
+                           keff_out);
 }
 
 }  // namespace moe

@@ -55,7 +55,10 @@ def test_workspace_bytes_host_logic():
     assert L.moe_workspace_bytes(ctypes.byref(cfg), 1, 7) == 0
     for bad in (moe.config(6000, 2048, 256, 8), moe.config(6144, 2048, 4, 8),
                 moe.config(6144, 2048, 256, 65), moe.config(6144, 2048, 2000, 8),
-                moe.config(6144, 2048, 256, 8, n_shared=2), moe.config(6144, 30, 256, 8)):
+                moe.config(6144, 2048, 256, 8, n_shared=2), moe.config(6144, 30, 256, 8),
+                moe.config(6144, 2048, 256, 8, expert_topp=-0.1),
+                moe.config(6144, 2048, 256, 8, expert_topp=1.5),
+                moe.config(6144, 2048, 256, 8, expert_topp=float("nan"))):
         assert L.moe_workspace_bytes(ctypes.byref(bad), 1, 0) == 0
 
 
