@@ -411,7 +411,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the verify, prefill and 48-layer stack measurements")
-    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered"],
+    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered", "topp"],
                     help="run only that secondary measurement and print its record (for profiling)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay pass (value then comes from the stream pass); "
@@ -448,6 +448,10 @@ def main():
     if args.only:
         if args.only == "stack":
             rec = bench_stack()
+        elif args.only == "topp":
+            reps = [build_device_layer(r, synth.GLM, r, synth.router_b_uniform(r, synth.GLM, r))
+                    for r in range(args.replicas)]
+            rec = bench_topp(reps, torch.from_numpy(synth.activations(7, args.tokens, D)).cuda())
         else:
             layer = build_device_layer(0, synth.GLM, 0, synth.router_b_uniform(0, synth.GLM, 0))
             rec = {"verify": bench_verify, "prefill": bench_prefill,
