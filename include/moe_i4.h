@@ -204,6 +204,17 @@ int moe_layer_forward_routed(const moe_config *cfg, const moe_layer *layer, cons
                              const int32_t *topk_idx, const float *topk_w, float *out,
                              unsigned flags, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The unique-expert union with the routing given by the caller, as
+ * moe_layer_forward_routed is to moe_layer_forward: topk_idx[S][K] and
+ * topk_w[S][K] (device, read by the call; indices clamped into [0, E)), all
+ * K experts of every token; layer->router_w and router_b are not read.  With
+ * MOE_F_PRENORM the normalized rows go to the workspace first.  With the
+ * routing that moe_layer_forward_batch selects, the two calls return
+ * identical bits. */
+int moe_layer_forward_batch_routed(const moe_config *cfg, const moe_layer *layer, const float *x,
+                                   int S, const int32_t *topk_idx, const float *topk_w, float *out,
+                                   unsigned flags, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- Expert residency tiers (section 05 expert cache, section 13 tiers) ----
  * Every expert of a layer is kept as one slab, the three packed matrices
  * followed by the three scale vectors (section 13 reads an expert with a

@@ -80,6 +80,7 @@ def lib():
         L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp, vp]
         L.moe_stream_read.argtypes = [vp, sz, vp, vp]
         L.moe_layer_forward_routed.argtypes = [vp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
+        L.moe_layer_forward_batch_routed.argtypes = [vp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
         L.moe_slab_layout_of.argtypes = [vp, vp]
         L.moe_tier_create.argtypes = [i32, i32, i32]
         L.moe_tier_create.restype = vp
@@ -95,7 +96,8 @@ def lib():
         for name in ("moe_workspace_init", "moe_pack_int4", "moe_quant_act_i8", "moe_router_topk",
                      "moe_expert_swiglu_i4", "moe_layer_forward", "moe_layer_forward_batch",
                      "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
-                     "moe_layer_forward_routed", "moe_slab_layout_of", "moe_tier_map",
+                     "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
+                     "moe_slab_layout_of", "moe_tier_map",
                      "moe_tier_stats", "moe_tier_fetch", "moe_tier_pick_swap"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -340,9 +342,12 @@ def moe_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, out=Non
 
 def moe_layer_forward_routed(layer, x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
                              ws: Workspace, out=None, flags: int = 0, stream=None,
-                             norm_gamma=None, norm_eps: float = 1e-5):
+                             norm_gamma=None, norm_eps: float = 1e-5,
+                             fn_name: str = "moe_layer_forward_routed"):
     """Per-token path with the routing given: topk_idx [S][K] int32 indices
-    into layer's routed stack, topk_w [S][K] float32 weights (device)."""
+    into layer's routed stack, topk_w [S][K] float32 weights (device).
+    fn_name="moe_layer_forward_batch_routed": the union path instead (its
+    workspace is WS_BATCH)."""
     _dev(x, torch.float32, "x")
     _dev(topk_idx, torch.int32, "topk_idx")
     _dev(topk_w, torch.float32, "topk_w")
@@ -354,11 +359,18 @@ def moe_layer_forward_routed(layer, x: torch.Tensor, topk_idx: torch.Tensor, top
         _dev(norm_gamma, torch.float32, "norm_gamma")
         flags |= F_PRENORM
     L = layer.cstruct(norm_gamma, norm_eps)
-    _check(lib().moe_layer_forward_routed(ctypes.byref(layer.cfg), ctypes.byref(L), _ptr(x), S,
-                                          _ptr(topk_idx), _ptr(topk_w), _ptr(out), flags, ws.ptr,
-                                          ws.nbytes, ctypes.c_void_p(_stream(stream))),
-           "moe_layer_forward_routed")
+    _check(getattr(lib(), fn_name)(ctypes.byref(layer.cfg), ctypes.byref(L), _ptr(x), S,
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(out), flags, ws.ptr,
+                                   ws.nbytes, ctypes.c_void_p(_stream(stream))), fn_name)
     return out
+
+
+def moe_layer_forward_batch_routed(layer, x: torch.Tensor, topk_idx: torch.Tensor,
+                                   topk_w: torch.Tensor, ws: Workspace, out=None, flags: int = 0,
+                                   stream=None, norm_gamma=None, norm_eps: float = 1e-5):
+    """Unique-expert union path with the routing given (workspace WS_BATCH)."""
+    return moe_layer_forward_routed(layer, x, topk_idx, topk_w, ws, out, flags, stream,
+                                    norm_gamma, norm_eps, "moe_layer_forward_batch_routed")
 
 
 class SlabLayout(ctypes.Structure):
@@ -506,8 +518,10 @@ class TieredLayer:
         return LayerC(None, None, self.routed.cstruct(), sh, g, float(norm_eps))
 
     def forward(self, x: torch.Tensor, ws_router: Workspace, ws: Workspace, out=None,
-                stream=None):
-        """Returns (out, misses of this call)."""
+                stream=None, union: bool = False):
+        """Returns (out, misses of this call).  union: run the unique-expert
+        union path (ws must then be a WS_BATCH workspace); the union of the
+        tokens' experts must fit in the layer's slots."""
         import numpy as np
         idx, w, _ = moe_router_topk(self.cfg, x, self.router_w, self.router_b, ws_router,
                                     stream=stream)
@@ -521,5 +535,6 @@ class TieredLayer:
         slot_of = np.empty(uniq.size, np.int32)
         slot_of[order] = slots
         sidx = torch.from_numpy(slot_of[inv].reshape(idx_h.shape).astype(np.int32)).to(x.device)
-        o = moe_layer_forward_routed(self, x, sidx, w, ws, out=out, stream=stream)
+        fn = moe_layer_forward_batch_routed if union else moe_layer_forward_routed
+        o = fn(self, x, sidx, w, ws, out=out, stream=stream)
         return o, misses

@@ -99,8 +99,10 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
   const int np = a.S * a.K;
   // pairs past a token's keff (adaptive top-p) are not grouped
   auto kept = [&](int p) { return !a.keff || (p % a.K) < a.keff[p / a.K]; };
+  // expert ids (the caller's, when the routing is given) kept inside [0, E)
+  auto expert = [&](int p) { return min(max((int)a.idx[p], 0), a.E - 1); };
   for (int p = threadIdx.x; p < np; p += blockDim.x)
-    if (kept(p)) atomicAdd(&cnt[a.idx[p]], 1);
+    if (kept(p)) atomicAdd(&cnt[expert(p)], 1);
   if (threadIdx.x == 0) cnt[a.E] = a.n_shared ? a.S : 0;
   __syncthreads();
   // exclusive scan over G <= 1025 counts: each wave scans a 64-wide slice in
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
   __syncthreads();
   for (int p = threadIdx.x; p < np; p += blockDim.x) {
     if (!kept(p)) continue;
-    const int e = a.idx[p];
+    const int e = expert(p);
     const int pos = off[e] + atomicAdd(&fill[e], 1);
     a.pairs[pos] = (p / a.K) * a.P + (p % a.K);
   }

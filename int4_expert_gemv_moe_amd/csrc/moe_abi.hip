@@ -476,21 +476,31 @@ int moe_layer_forward_routed(const moe_config *cfg, const moe_layer *layer, cons
                             ws_bytes, stream);
 }
 
-int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
-                            float *out, unsigned flags, const moe_probe *probe, void *ws,
-                            size_t ws_bytes, hipStream_t stream) {
-  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_BATCH));
+}  // extern "C"
+
+namespace {
+
+// The union path; with given_idx / given_w the caller's routing replaces the
+// router and the selection (the tokens are only quantized).
+int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                             const int32_t *given_idx, const float *given_w, float *out,
+                             unsigned flags, const moe_probe *probe, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  const bool given = given_idx != nullptr;
+  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_BATCH, !given));
+  if (given && (((uintptr_t)given_idx & 3u) || !given_w || ((uintptr_t)given_w & 3u)))
+    return given_w ? MOE_EALIGN : MOE_EINVAL;
   const moe_config &c = *cfg;
   const int P = c.K + c.n_shared;
   Work w;
   carve(c, S, W_BATCH, (char *)ws, &w);
   // x (maybe out itself) is read by the router launch and nowhere else.
   // With MOE_F_PRENORM, batches of up to 8 tokens normalize inside the
-  // router's workgroups; larger ones get the normalized rows in the
-  // workspace first.
+  // router's workgroups; larger ones (and calls with given routing) get the
+  // normalized rows in the workspace first.
   const float *gamma = nullptr;
   if (flags & MOE_F_PRENORM) {
-    if (S <= 8) {
+    if (S <= 8 && !given) {
       gamma = layer->norm_gamma;
     } else {
       RmsArgs ra{x, layer->norm_gamma, c.D, layer->norm_eps, w.xn, 1};
@@ -500,24 +510,32 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
     flags &= ~MOE_F_PRENORM;
   }
   // small batches select inside the grouping kernel (one launch fewer)
-  const bool topk_in_group = S <= kGroupTopkMaxTokens && c.E <= 256;
-  MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, !topk_in_group, nullptr,
-                     stream, gamma, layer->norm_eps));
+  const bool topk_in_group = !given && S <= kGroupTopkMaxTokens && c.E <= 256;
+  if (given) {
+    QuantArgs q{x, nullptr, c.D, w.xq, nullptr, w.sx, w.sumx};
+    MOE_TRY_HIP(launch_quant(q, S, stream));
+  } else {
+    MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, !topk_in_group, nullptr,
+                       stream, gamma, layer->norm_eps));
+  }
+  int32_t *idx = given ? const_cast<int32_t *>(given_idx) : w.idx;
+  const float *wts = given ? given_w : w.w;
+  int32_t *keff = given ? nullptr : w.keff;
   // the MFMA kernels address activation rows with 32-bit byte offsets
   const bool offs_ok = (int64_t)S * P * std::max(c.D, c.I) < INT32_MAX;
   const bool mfma_gu = grouped_mfma_fits(c.D) && offs_ok, mfma_dn = grouped_mfma_fits(c.I) && offs_ok;
   const int max_tiles = grouped_mfma_max_tiles(S, P, c.E);
-  GroupArgs ga{w.idx,    S,     c.E,     c.K,      P, c.n_shared, w.gcount, w.goff, w.pairs,
+  GroupArgs ga{idx,      S,     c.E,     c.K,      P, c.n_shared, w.gcount, w.goff, w.pairs,
                (mfma_gu || mfma_dn) ? w.tiles : nullptr, w.ntiles, grouped_mfma_tile_rows(S)};
   ga.with_topk = topk_in_group ? 1 : 0;
   ga.topp = c.expert_topp;
-  ga.keff = w.keff;
+  ga.keff = keff;
   ga.logits = w.logits;
   ga.bias = layer->router_b;
   ga.scale = c.routed_scale;
   ga.wts = w.w;
   MOE_TRY_HIP(launch_group(ga, stream));
-  MOE_TRY(copy_probe(c, S, probe, w, stream));
+  if (!given) MOE_TRY(copy_probe(c, S, probe, w, stream));
   const ExpertSet rt = to_set(layer->routed, c);
   const ExpertSet sh = c.n_shared ? to_set(layer->shared, c) : rt;
   GroupedMfmaArgs m{};
@@ -588,9 +606,28 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
     MOE_TRY_HIP(launch_grouped_down(d, stream));
   }
   MOE_TRY(record(probe, 1, 1, stream));
-  CombineArgs cb{w.stage, w.w, S, c.D, c.K, P, c.n_shared, out, flags, w.keff};
+  CombineArgs cb{w.stage, wts, S, c.D, c.K, P, c.n_shared, out, flags, keff};
   MOE_TRY_HIP(launch_combine(cb, stream));
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
+                            float *out, unsigned flags, const moe_probe *probe, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  return layer_forward_batch_impl(cfg, layer, x, S, nullptr, nullptr, out, flags, probe, ws,
+                                  ws_bytes, stream);
+}
+
+int moe_layer_forward_batch_routed(const moe_config *cfg, const moe_layer *layer, const float *x,
+                                   int S, const int32_t *topk_idx, const float *topk_w, float *out,
+                                   unsigned flags, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!topk_idx) return MOE_EINVAL;
+  return layer_forward_batch_impl(cfg, layer, x, S, topk_idx, topk_w, out, flags, nullptr, ws,
+                                  ws_bytes, stream);
 }
 
 int moe_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y,

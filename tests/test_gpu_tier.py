@@ -79,3 +79,56 @@ def test_tiered_layer_matches_resident_layer(shape, n_slots, S, calls):
         hits += len(eids) - misses
     assert tl.tier.stats() == (cache.hits, cache.misses)
     say(f"  hits {cache.hits} misses {cache.misses}")
+
+
+@pytest.mark.parametrize("shape,S", [(MID, 37), (GLM, 64)])
+def test_batch_routed_call_equals_union_path(shape, S):
+    dl = device_layer(11, shape, 0, bias_for("uniform", 11, shape))
+    x = torch.from_numpy(synth.activations(34, S, shape.D)).cuda()
+    ws = moe.Workspace(dl.cfg, S, moe.WS_BATCH)
+    idx = torch.empty(S, shape.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(S, shape.K, dtype=torch.float32, device="cuda")
+    ref = moe.moe_layer_forward_batch(dl, x, ws, topk_idx=idx, topk_w=w)
+    out = moe.moe_layer_forward_batch_routed(dl, x, idx, w, moe.Workspace(dl.cfg, S, moe.WS_BATCH))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out), _bits(ref))
+
+
+def test_batch_routed_call_clamps_indices():
+    shape = MID
+    dl = device_layer(12, shape, 0, bias_for("uniform", 12, shape))
+    S = 3
+    x = torch.from_numpy(synth.activations(35, S, shape.D)).cuda()
+    w = torch.rand(S, shape.K, dtype=torch.float32, device="cuda")
+    good = torch.randint(0, shape.E, (S, shape.K), dtype=torch.int32, device="cuda")
+    bad = good.clone()
+    bad[0, 0], bad[1, 3], bad[2, 7] = -7, shape.E + 5, 2 ** 30
+    good[0, 0], good[1, 3], good[2, 7] = 0, shape.E - 1, shape.E - 1
+    a = moe.moe_layer_forward_batch_routed(dl, x, bad, w, moe.Workspace(dl.cfg, S, moe.WS_BATCH))
+    b = moe.moe_layer_forward_batch_routed(dl, x, good, w, moe.Workspace(dl.cfg, S, moe.WS_BATCH))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(a), _bits(b))
+
+
+@pytest.mark.parametrize("shape,n_slots,S,calls", [(MID, 48, 6, 12), (GLM, 192, 64, 3)])
+def test_tiered_union_matches_resident_union(shape, n_slots, S, calls):
+    say(f"tiered union D={shape.D} E={shape.E} slots={n_slots} S={S}")
+    dl = device_layer(13, shape, 0, bias_for("zipf", 13, shape, 0, 0.05))
+    tl = moe.TieredLayer.from_device_layer(dl, n_slots)
+    cache = oracle.ExpertCache(1, n_slots)
+    wsr = moe.Workspace(dl.cfg, S, moe.WS_ROUTER)
+    ws = moe.Workspace(dl.cfg, S, moe.WS_BATCH)
+    wsb = moe.Workspace(dl.cfg, S, moe.WS_BATCH)
+    x_all = torch.from_numpy(synth.activations(36, S * calls, shape.D)).cuda()
+    for c in range(calls):
+        x = x_all[c * S:(c + 1) * S]
+        idx = torch.empty(S, shape.K, dtype=torch.int32, device="cuda")
+        ref = moe.moe_layer_forward_batch(dl, x, wsb, topk_idx=idx)
+        out, misses = tl.forward(x, wsr, ws, union=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(out), _bits(ref)), f"call {c}"
+        flat = to_np(idx).ravel().tolist()
+        eids = [e for i, e in enumerate(flat) if e not in flat[:i]]
+        assert misses == sum(cache.get(0, e)[1] for e in eids), f"call {c}"
+    assert tl.tier.stats() == (cache.hits, cache.misses)
+    say(f"  hits {cache.hits} misses {cache.misses}")
