@@ -252,6 +252,31 @@ def bench_tiered(layer, slot_counts=(192, 64), warm: int = 64, timed: int = 192)
                     "h2d_GB_per_token": round(misses * EXPERT_BYTES / timed / 1e9, 4),
                     "h2d_GBps": round(misses * EXPERT_BYTES / (us * timed) / 1e3, 1)}
         log(f"tiered {key}: {us:.1f} us/token, hit rate {res[key]['hit_rate']}")
+        if n_slots >= 160:
+            # 64-token verify steps through the union path on the same slots
+            S, nb = 64, 12
+            xb_np, _, _ = synth.zipf_activations(2, synth.GLM, S * nb, wr)
+            xb = torch.from_numpy(xb_np).cuda()
+            wsrb = moe.Workspace(zl.cfg, S, moe.WS_ROUTER)
+            wsb = moe.Workspace(zl.cfg, S, moe.WS_BATCH)
+            outb = torch.empty(S, D, dtype=torch.float32, device="cuda")
+            for b in range(4):
+                tl.forward(xb[b * S:(b + 1) * S], wsrb, wsb, out=outb, union=True)
+            torch.cuda.synchronize()
+            h0, m0 = tl.tier.stats()
+            t0 = time.perf_counter()
+            for b in range(4, nb):
+                tl.forward(xb[b * S:(b + 1) * S], wsrb, wsb, out=outb, union=True)
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / (nb - 4)
+            h1, m1 = tl.tier.stats()
+            hits, misses = h1 - h0, m1 - m0
+            res[key]["verify_64_union"] = {
+                "us_per_step": round(us, 1), "us_per_token": round(us / S, 2),
+                "hit_rate": round(hits / max(1, hits + misses), 4),
+                "misses_per_step": round(misses / (nb - 4), 2),
+                "h2d_GBps": round(misses * EXPERT_BYTES / (us * (nb - 4)) / 1e3, 1)}
+            log(f"tiered {key} verify 64: {us:.1f} us/step")
         del tl
     del host
     torch.cuda.empty_cache()
