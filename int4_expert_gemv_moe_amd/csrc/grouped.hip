@@ -98,7 +98,7 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
   __syncthreads();
   const int np = a.S * a.K;
   // pairs past a token's keff (adaptive top-p) are not grouped
-  auto kept = [&](int p) { return !a.keff || (p % a.K) < a.keff[p / a.K]; };
+  auto kept = [&](int p) { return !a.use_keff || (p % a.K) < a.keff[p / a.K]; };
   // expert ids (the caller's, when the routing is given) kept inside [0, E)
   auto expert = [&](int p) { return min(max((int)a.idx[p], 0), a.E - 1); };
   for (int p = threadIdx.x; p < np; p += blockDim.x)

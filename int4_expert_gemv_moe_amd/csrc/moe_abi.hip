@@ -520,6 +520,9 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
   }
   int32_t *idx = given ? const_cast<int32_t *>(given_idx) : w.idx;
   const float *wts = given ? given_w : w.w;
+  // keff is always computed with the selection (the probe reports it); the
+  // grouping and the combine consult it only when top-p is on
+  const bool topp_on = !given && c.expert_topp > 0.f && c.expert_topp < 1.f;
   int32_t *keff = given ? nullptr : w.keff;
   // the MFMA kernels address activation rows with 32-bit byte offsets
   const bool offs_ok = (int64_t)S * P * std::max(c.D, c.I) < INT32_MAX;
@@ -530,6 +533,7 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
   ga.with_topk = topk_in_group ? 1 : 0;
   ga.topp = c.expert_topp;
   ga.keff = keff;
+  ga.use_keff = topp_on ? 1 : 0;
   ga.logits = w.logits;
   ga.bias = layer->router_b;
   ga.scale = c.routed_scale;
@@ -606,7 +610,7 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
     MOE_TRY_HIP(launch_grouped_down(d, stream));
   }
   MOE_TRY(record(probe, 1, 1, stream));
-  CombineArgs cb{w.stage, wts, S, c.D, c.K, P, c.n_shared, out, flags, keff};
+  CombineArgs cb{w.stage, wts, S, c.D, c.K, P, c.n_shared, out, flags, topp_on ? keff : nullptr};
   MOE_TRY_HIP(launch_combine(cb, stream));
   return MOE_OK;
 }

@@ -107,6 +107,7 @@ struct GroupArgs {
   float *wts;
   float topp;             // adaptive expert top-p
   int32_t *keff;          // [S]: written with the selection (with_topk), else read
+  int use_keff;           // drop pairs past keff (top-p on); else keep all K
 };
 
 // Grouped int8 MFMA GEMM of the union path (grouped_mfma.hip); mode 0 is
