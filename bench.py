@@ -203,7 +203,7 @@ def bench_verify(layer, iters: int = 20):
             "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
 
 
-def bench_tiered(layer, slot_counts=(192, 64), warm: int = 64, timed: int = 192):
+def bench_tiered(layer, slot_counts=(192, (128, 64), 64), warm: int = 64, timed: int = 192):
     """Decode through one GLM-shape layer whose routed experts live in pinned
     host memory and only n_slots HBM slab slots (section 05 LRU expert cache,
     section 13 slab reads), Zipf(1.1)-skewed routing, one token per call: the
@@ -232,7 +232,9 @@ def bench_tiered(layer, slot_counts=(192, 64), warm: int = 64, timed: int = 192)
            "tokens_timed": timed, "slab_bytes": EXPERT_BYTES}
     host = None
     for n_slots in slot_counts:
-        tl = moe.TieredLayer.from_device_layer(zl, n_slots, host_slabs=host)
+        # (lru, pinned): pinned slots kept by heat (section 13 swap rule)
+        n_slots, n_pin = n_slots if isinstance(n_slots, tuple) else (n_slots, 0)
+        tl = moe.TieredLayer.from_device_layer(zl, n_slots, host_slabs=host, n_pinned=n_pin)
         host = tl.host_slabs
         for t in range(warm):
             tl.forward(x[t:t + 1], wsr, ws, out=out)
@@ -245,14 +247,15 @@ def bench_tiered(layer, slot_counts=(192, 64), warm: int = 64, timed: int = 192)
         us = (time.perf_counter() - t0) * 1e6 / timed
         h1, m1 = tl.tier.stats()
         hits, misses = h1 - h0, m1 - m0
-        key = f"slots_{n_slots}_of_{E}"
+        key = (f"slots_{n_slots}_of_{E}" if not n_pin else
+               f"slots_{n_slots}_lru_{n_pin}_pinned_of_{E}")
         res[key] = {"us_per_token": round(us, 1), "tokens_per_s": round(1e6 / us, 1),
                     "hit_rate": round(hits / max(1, hits + misses), 4),
                     "misses_per_token": round(misses / timed, 3),
                     "h2d_GB_per_token": round(misses * EXPERT_BYTES / timed / 1e9, 4),
                     "h2d_GBps": round(misses * EXPERT_BYTES / (us * timed) / 1e3, 1)}
         log(f"tiered {key}: {us:.1f} us/token, hit rate {res[key]['hit_rate']}")
-        if n_slots >= 160:
+        if n_slots >= 160 and not n_pin:
             # 64-token verify steps through the union path on the same slots
             S, nb = 64, 12
             xb_np, _, _ = synth.zipf_activations(2, synth.GLM, S * nb, wr)

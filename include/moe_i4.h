@@ -243,6 +243,23 @@ typedef struct moe_tier moe_tier;
 moe_tier *moe_tier_create(int n_layers, int n_experts, int n_slots);
 void moe_tier_destroy(moe_tier *t);
 
+/* As moe_tier_create, plus n_pinned heat-managed slots per layer (0 <=
+ * n_pinned < n_experts; the section 13 pinned tier): slots 0 .. n_pinned-1 of
+ * a layer are pinned slots, its n_lru LRU slots follow.  Every lookup of
+ * moe_tier_map adds 1 to the expert's heat; a pinned expert is a hit in its
+ * pinned slot before the LRU slots are searched.  moe_tier_rebalance decides
+ * what the pinned slots hold. */
+moe_tier *moe_tier_create_pinned(int n_layers, int n_experts, int n_lru, int n_pinned);
+
+/* One pinned-slot change for a layer, after its calls: an empty pinned slot
+ * takes the hottest expert not pinned (heat > 0, first of equals); with all
+ * filled, moe_tier_pick_swap over the layer's heat and pinned experts.
+ * Returns 1 with the pinned slot, the new expert and the one it replaces (-1
+ * when the slot was empty) -- the caller copies the new expert's slab into the
+ * slot (moe_tier_fetch) before the layer's next call -- or 0 (no change), or a
+ * negative status. */
+int moe_tier_rebalance(moe_tier *t, int layer, int32_t *slot, int32_t *eid, int32_t *old_eid);
+
 /* Section 05 expert_get for each of eids[0..n) of one call, in order (host
  * arrays): a resident expert is a hit and its slot's use clock is refreshed;
  * a missing one takes the next unused slot, else the least recently used slot
@@ -253,6 +270,8 @@ void moe_tier_destroy(moe_tier *t);
  * n_experts) or a bad layer: MOE_EINVAL, nothing changed). */
 int moe_tier_map(moe_tier *t, int layer, const int32_t *eids, int n, int32_t *slots,
                  int32_t *loads);
+
+/* (With pinned slots, the LRU slot numbers start at n_pinned.) */
 
 /* Hits and misses of every moe_tier_map so far (either pointer may be NULL). */
 int moe_tier_stats(const moe_tier *t, uint64_t *hits, uint64_t *misses);

@@ -84,6 +84,9 @@ def lib():
         L.moe_slab_layout_of.argtypes = [vp, vp]
         L.moe_tier_create.argtypes = [i32, i32, i32]
         L.moe_tier_create.restype = vp
+        L.moe_tier_create_pinned.argtypes = [i32, i32, i32, i32]
+        L.moe_tier_create_pinned.restype = vp
+        L.moe_tier_rebalance.argtypes = [vp, i32, vp, vp, vp]
         L.moe_tier_destroy.argtypes = [vp]
         L.moe_tier_destroy.restype = None
         L.moe_tier_map.argtypes = [vp, i32, vp, i32, vp, vp]
@@ -98,7 +101,8 @@ def lib():
                      "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
                      "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
                      "moe_slab_layout_of", "moe_tier_map",
-                     "moe_tier_stats", "moe_tier_fetch", "moe_tier_pick_swap"):
+                     "moe_tier_stats", "moe_tier_fetch", "moe_tier_pick_swap",
+                     "moe_tier_rebalance"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -416,11 +420,22 @@ def pack_slabs(experts: DeviceExperts, lay: SlabLayout, out: torch.Tensor) -> to
 class Tier:
     """Host bookkeeping of the HBM expert slots (moe_tier_*)."""
 
-    def __init__(self, n_layers: int, n_experts: int, n_slots: int):
-        h = lib().moe_tier_create(n_layers, n_experts, n_slots)
+    def __init__(self, n_layers: int, n_experts: int, n_slots: int, n_pinned: int = 0):
+        """n_slots LRU slots per layer, after n_pinned heat-managed ones."""
+        h = (lib().moe_tier_create_pinned(n_layers, n_experts, n_slots, n_pinned) if n_pinned
+             else lib().moe_tier_create(n_layers, n_experts, n_slots))
         if not h:
             raise MoeError("moe_tier_create failed")
-        self.h, self.n_slots = h, n_slots
+        self.h, self.n_slots, self.n_pinned = h, n_slots, n_pinned
+
+    def rebalance(self, layer: int):
+        """(changed, pinned slot, new expert, replaced expert or -1)."""
+        z, e, o = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int32(-1)
+        r = lib().moe_tier_rebalance(self.h, layer, ctypes.byref(z), ctypes.byref(e),
+                                     ctypes.byref(o))
+        if r < 0:
+            raise MoeError(f"moe_tier_rebalance: {status_str(r)}")
+        return bool(r), z.value, e.value, o.value
 
     def __del__(self):
         if getattr(self, "h", None):
@@ -489,8 +504,8 @@ class TieredLayer:
 
     @staticmethod
     def from_device_layer(dl: DeviceLayer, n_slots: int, tier: Tier | None = None,
-                          layer_index: int = 0, host_slabs: torch.Tensor | None = None
-                          ) -> "TieredLayer":
+                          layer_index: int = 0, host_slabs: torch.Tensor | None = None,
+                          n_pinned: int = 0) -> "TieredLayer":
         """host_slabs: reuse the pinned slabs of an earlier TieredLayer of the
         same layer instead of packing them again."""
         lay = slab_layout(dl.cfg)
@@ -507,8 +522,9 @@ class TieredLayer:
                                                            device=dl.router_w.device))
                 host[e0:e1].copy_(staged)
             del staged
-        slots = torch.empty(n_slots, lay.bytes, dtype=torch.uint8, device=dl.router_w.device)
-        tier = tier or Tier(1, E, n_slots)
+        slots = torch.empty(n_pinned + n_slots, lay.bytes, dtype=torch.uint8,
+                            device=dl.router_w.device)
+        tier = tier or Tier(1, E, n_slots, n_pinned)
         return TieredLayer(dl.cfg, dl.router_w, dl.router_b, SlabExperts(slots, lay), dl.shared,
                            host, tier, layer_index)
 
@@ -537,4 +553,10 @@ class TieredLayer:
         sidx = torch.from_numpy(slot_of[inv].reshape(idx_h.shape).astype(np.int32)).to(x.device)
         fn = moe_layer_forward_batch_routed if union else moe_layer_forward_routed
         o = fn(self, x, sidx, w, ws, out=out, stream=stream)
+        if self.tier.n_pinned:
+            # one pinned-slot change by heat; its copy is ordered after the call
+            changed, z, e, _ = self.tier.rebalance(self.layer_index)
+            if changed:
+                Tier.fetch(self.host_slabs, self.routed.buf, self.routed.lay.bytes, [e], [z], [1],
+                           stream)
         return o, misses

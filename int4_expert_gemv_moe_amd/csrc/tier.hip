@@ -21,12 +21,17 @@
 #include "../../include/moe_i4.h"
 
 struct moe_tier {
-  int n_layers, n_experts, n_slots;
-  // per layer: slots in use, and per slot the expert it holds and the clock
-  // value of its last use
+  int n_layers, n_experts, n_slots;  // n_slots: the LRU slots of a layer
+  int n_pinned = 0;                  // heat-managed slots of a layer, numbered first
+  // per layer: LRU slots in use, and per LRU slot the expert it holds and the
+  // clock value of its last use
   std::vector<int> used_n;
   std::vector<int32_t> eid;
   std::vector<uint64_t> used;
+  // per layer: the expert of each pinned slot (-1: empty) and every expert's
+  // heat (lookups so far)
+  std::vector<int32_t> pinned;
+  std::vector<uint32_t> heat;
   uint64_t clock = 0, hits = 0, misses = 0;
 };
 
@@ -66,6 +71,21 @@ moe_tier *moe_tier_create(int n_layers, int n_experts, int n_slots) {
   return t;
 }
 
+moe_tier *moe_tier_create_pinned(int n_layers, int n_experts, int n_lru, int n_pinned) {
+  if (n_pinned < 0 || n_pinned >= n_experts) return nullptr;
+  moe_tier *t = moe_tier_create(n_layers, n_experts, n_lru);
+  if (!t) return nullptr;
+  t->n_pinned = n_pinned;
+  try {
+    t->pinned.assign((size_t)n_layers * n_pinned, -1);
+    t->heat.assign((size_t)n_layers * n_experts, 0u);
+  } catch (...) {
+    delete t;
+    return nullptr;
+  }
+  return t;
+}
+
 void moe_tier_destroy(moe_tier *t) { delete t; }
 
 int moe_tier_map(moe_tier *t, int layer, const int32_t *eids, int n, int32_t *slots,
@@ -81,9 +101,22 @@ int moe_tier_map(moe_tier *t, int layer, const int32_t *eids, int n, int32_t *sl
   int32_t *le = t->eid.data() + (size_t)layer * t->n_slots;
   uint64_t *lu = t->used.data() + (size_t)layer * t->n_slots;
   int &ln = t->used_n[layer];
+  const int np = t->n_pinned;
+  const int32_t *pin = np ? t->pinned.data() + (size_t)layer * np : nullptr;
+  uint32_t *heat = np ? t->heat.data() + (size_t)layer * t->n_experts : nullptr;
   int misses = 0;
   for (int i = 0; i < n; i++) {
     const int32_t e = eids[i];
+    if (heat) heat[e]++;
+    // a pinned expert is a hit in its pinned slot (slots 0 .. n_pinned-1)
+    int z = 0;
+    while (z < np && pin[z] != e) z++;
+    if (z < np) {
+      t->hits++;
+      slots[i] = z;
+      loads[i] = 0;
+      continue;
+    }
     int s = -1;
     for (int z = 0; z < ln; z++)
       if (le[z] == e) {
@@ -93,7 +126,7 @@ int moe_tier_map(moe_tier *t, int layer, const int32_t *eids, int n, int32_t *sl
     if (s >= 0) {
       t->hits++;
       lu[s] = ++t->clock;
-      slots[i] = s;
+      slots[i] = np + s;
       loads[i] = 0;
       continue;
     }
@@ -108,10 +141,48 @@ int moe_tier_map(moe_tier *t, int layer, const int32_t *eids, int n, int32_t *sl
     }
     le[s] = e;
     lu[s] = ++t->clock;
-    slots[i] = s;
+    slots[i] = np + s;
     loads[i] = 1;
   }
   return misses;
+}
+
+int moe_tier_rebalance(moe_tier *t, int layer, int32_t *slot, int32_t *eid, int32_t *old_eid) {
+  if (!t || !slot || !eid || !old_eid || layer < 0 || layer >= t->n_layers) return MOE_EINVAL;
+  const int np = t->n_pinned;
+  if (np == 0) return 0;
+  int32_t *pin = t->pinned.data() + (size_t)layer * np;
+  const uint32_t *heat = t->heat.data() + (size_t)layer * t->n_experts;
+  // an empty pinned slot takes the hottest expert not pinned (heat > 0,
+  // first of equals)
+  for (int z = 0; z < np; z++) {
+    if (pin[z] >= 0) continue;
+    int hot = -1;
+    uint32_t hh = 0;
+    for (int e = 0; e < t->n_experts; e++) {
+      bool held = false;
+      for (int y = 0; y < np; y++) held = held || pin[y] == e;
+      if (!held && heat[e] > hh) {
+        hh = heat[e];
+        hot = e;
+      }
+    }
+    if (hot < 0) return 0;
+    *slot = z;
+    *eid = hot;
+    *old_eid = -1;
+    pin[z] = hot;
+    return 1;
+  }
+  // all filled: the section 13 swap rule
+  int32_t z, e;
+  int64_t gain;
+  if (!moe_tier_pick_swap(heat, t->n_experts, pin, np, &z, &e, &gain)) return 0;
+  *slot = z;
+  *eid = e;
+  *old_eid = pin[z];
+  pin[z] = e;
+  return 1;
 }
 
 int moe_tier_stats(const moe_tier *t, uint64_t *hits, uint64_t *misses) {

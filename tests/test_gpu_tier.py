@@ -132,3 +132,23 @@ def test_tiered_union_matches_resident_union(shape, n_slots, S, calls):
         assert misses == sum(cache.get(0, e)[1] for e in eids), f"call {c}"
     assert tl.tier.stats() == (cache.hits, cache.misses)
     say(f"  hits {cache.hits} misses {cache.misses}")
+
+
+@pytest.mark.parametrize("shape,n_slots,n_pinned,calls", [(MID, 12, 8, 60), (GLM, 128, 64, 16)])
+def test_tiered_layer_with_pinned_slots_matches_resident(shape, n_slots, n_pinned, calls):
+    """Heat-managed pinned slots (section 13 swap rule) in front of the LRU
+    slots: the slab copies of a rebalance are ordered after the call that
+    decided them, and every call still returns the resident layer's bits."""
+    say(f"pinned tier D={shape.D} E={shape.E} lru={n_slots} pinned={n_pinned}")
+    dl = device_layer(14, shape, 0, bias_for("zipf", 14, shape, 0, 0.05))
+    tl = moe.TieredLayer.from_device_layer(dl, n_slots, n_pinned=n_pinned)
+    wsr = moe.Workspace(dl.cfg, 1, moe.WS_ROUTER)
+    ws = moe.Workspace(dl.cfg, 1, moe.WS_FORWARD)
+    x_all = torch.from_numpy(synth.activations(37, calls, shape.D)).cuda()
+    for c in range(calls):
+        x = x_all[c:c + 1]
+        ref, _, _ = _resident(dl, x)
+        out, _ = tl.forward(x, wsr, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(out), _bits(ref)), f"call {c}"
+    say(f"  hits/misses {tl.tier.stats()}")

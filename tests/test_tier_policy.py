@@ -74,3 +74,69 @@ def test_slab_layout_closed_form():
         assert all(v % 16 == 0 for v in (lay.up_q4, lay.down_q4, lay.gate_s, lay.up_s, lay.down_s,
                                          lay.bytes))
     assert moe.slab_layout(moe.config(6144, 2048, 256, 8)).bytes == 18_915_328
+
+
+class PinnedRef:
+    """The pinned tier composed from the oracle's parts: heat = lookups so far,
+    pinned slots checked first, the section 05 expert cache behind them
+    (slots numbered after the pinned ones), and per rebalance either the
+    hottest unpinned expert into an empty pinned slot or the section 13 swap."""
+
+    def __init__(self, E, n_lru, n_pin):
+        self.E, self.np = E, n_pin
+        self.pinned = [-1] * n_pin
+        self.heat = np.zeros(E, np.uint32)
+        self.cache = oracle.ExpertCache(1, n_lru)
+        self.pin_hits = 0
+
+    def map(self, eids):
+        slots, loads = [], []
+        for e in eids:
+            self.heat[e] += 1
+            if e in self.pinned:
+                slots.append(self.pinned.index(e))
+                loads.append(0)
+                self.pin_hits += 1
+            else:
+                s, l = self.cache.get(0, int(e))
+                slots.append(self.np + s)
+                loads.append(l)
+        return slots, loads
+
+    def rebalance(self):
+        if -1 in self.pinned:
+            z = self.pinned.index(-1)
+            free = [e for e in range(self.E) if e not in self.pinned and self.heat[e] > 0]
+            if not free:
+                return False, -1, -1, -1
+            hot = min(free, key=lambda e: (-int(self.heat[e]), e))
+            self.pinned[z] = hot
+            return True, z, hot, -1
+        ok, z, e, _ = oracle.tier_pick_swap(self.heat, self.pinned)
+        if not ok:
+            return False, -1, -1, -1
+        old = self.pinned[z]
+        self.pinned[z] = e
+        return True, z, e, old
+
+
+@pytest.mark.parametrize("E,n_lru,n_pin,calls,per_call,seed", [(16, 4, 2, 80, 2, 0),
+                                                                (256, 128, 64, 400, 8, 1),
+                                                                (64, 12, 8, 300, 8, 2)])
+def test_pinned_tier_matches_composed_oracle(E, n_lru, n_pin, calls, per_call, seed):
+    rng = np.random.default_rng(seed)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    t = moe.Tier(1, E, n_lru, n_pin)
+    ref = PinnedRef(E, n_lru, n_pin)
+    swaps = 0
+    for _ in range(calls):
+        eids = rng.choice(E, size=per_call, replace=False, p=p).astype(np.int32)
+        slots, loads, misses = t.map(0, eids)
+        rs, rl = ref.map(eids.tolist())
+        assert slots.tolist() == rs and loads.tolist() == rl and misses == sum(rl)
+        got = t.rebalance(0)
+        assert got == ref.rebalance()
+        swaps += got[0] and got[3] >= 0
+    assert t.stats() == (ref.cache.hits + ref.pin_hits, ref.cache.misses)
+    assert all(e >= 0 for e in ref.pinned) and len(set(ref.pinned)) == n_pin
