@@ -541,7 +541,9 @@ class TieredLayer:
         import numpy as np
         idx, w, _ = moe_router_topk(self.cfg, x, self.router_w, self.router_b, ws_router,
                                     stream=stream)
-        idx_h = idx.cpu().numpy()            # waits for the routing
+        # the routing is read on the host: wait for the stream the router ran on
+        (torch.cuda.current_stream() if stream is None else stream).synchronize()
+        idx_h = idx.cpu().numpy()
         uniq, inv = np.unique(idx_h.ravel(), return_inverse=True)
         order = np.argsort(np.unique(idx_h.ravel(), return_index=True)[1])  # first appearance
         eids = uniq[order]
