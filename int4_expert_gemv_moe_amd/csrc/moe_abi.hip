@@ -393,9 +393,9 @@ int layer_forward_impl(const moe_config *cfg, const moe_layer *layer, const floa
                        unsigned flags, const moe_probe *probe, void *ws, size_t ws_bytes,
                        hipStream_t stream) {
   const bool given = given_idx != nullptr;
+  if (given && !given_w) return MOE_EINVAL;
+  if (given && (((uintptr_t)given_idx & 3u) || ((uintptr_t)given_w & 3u))) return MOE_EALIGN;
   MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_FWD, !given));
-  if (given && (((uintptr_t)given_idx & 3u) || !given_w || ((uintptr_t)given_w & 3u)))
-    return given_w ? MOE_EALIGN : MOE_EINVAL;
   const moe_config &c = *cfg;
   Work w;
   carve(c, S, W_FWD, (char *)ws, &w);
@@ -487,9 +487,9 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
                              unsigned flags, const moe_probe *probe, void *ws, size_t ws_bytes,
                              hipStream_t stream) {
   const bool given = given_idx != nullptr;
+  if (given && !given_w) return MOE_EINVAL;
+  if (given && (((uintptr_t)given_idx & 3u) || ((uintptr_t)given_w & 3u))) return MOE_EALIGN;
   MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_BATCH, !given));
-  if (given && (((uintptr_t)given_idx & 3u) || !given_w || ((uintptr_t)given_w & 3u)))
-    return given_w ? MOE_EALIGN : MOE_EINVAL;
   const moe_config &c = *cfg;
   const int P = c.K + c.n_shared;
   Work w;

@@ -82,6 +82,36 @@ def test_host_validation_before_device():
     assert L.moe_rmsnorm(None, None, 1, 8, 1e-5, None, None) == -1
 
 
+def test_given_routing_and_tier_host_checks():
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    cfg = moe.config(256, 128, 8, 2)
+    layer = moe.LayerC()
+    buf = ctypes.create_string_buffer(256)
+    a16 = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    for fn in (L.moe_layer_forward_routed, L.moe_layer_forward_batch_routed):
+        # routing pointers: missing -> invalid argument, misaligned -> alignment
+        assert fn(ctypes.byref(cfg), ctypes.byref(layer), None, 1, None, None, None, 0, None, 0,
+                  None) == -1
+        assert fn(ctypes.byref(cfg), ctypes.byref(layer), None, 1, a16, None, None, 0, None, 0,
+                  None) == -1
+        assert fn(ctypes.byref(cfg), ctypes.byref(layer), None, 1, a16 + 2, a16, None, 0, None, 0,
+                  None) == -3
+        assert fn(ctypes.byref(cfg), ctypes.byref(layer), None, 1, a16, a16 + 1, None, 0, None, 0,
+                  None) == -3
+    # the tier's copies: slab size must be a non-zero multiple of 16
+    ids = (ctypes.c_int32 * 1)(0)
+    assert L.moe_tier_fetch(a16, a16, 0, ids, ids, ids, 1, None) == -3
+    assert L.moe_tier_fetch(a16, a16, 24, ids, ids, ids, 1, None) == -3
+    assert L.moe_tier_fetch(None, a16, 32, ids, ids, ids, 1, None) == -1
+    # a layout needs D and I multiples of 32
+    lay = moe.SlabLayout()
+    assert L.moe_slab_layout_of(ctypes.byref(moe.config(256, 48, 8, 2)), ctypes.byref(lay)) == -2
+    # tier objects: invalid sizes give no object
+    assert not L.moe_tier_create(0, 8, 4) and not L.moe_tier_create(1, 8, 0)
+    assert not L.moe_tier_create_pinned(1, 8, 4, 8)   # pinned slots < experts
+
+
 def test_prenorm_flag_host_checks():
     """MOE_F_PRENORM: gamma and eps are checked on the host, unknown flag bits
     are refused, and out == x is accepted only with the flag (the calls stop
