@@ -449,8 +449,9 @@ def main():
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(expert- or tensor-parallel sharding over RCCL is a design, not code).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
