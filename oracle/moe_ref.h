@@ -127,7 +127,9 @@ int moe_ref_rmsnorm(const float *x, const float *gamma, int S, int D, float eps,
  * whose running sum w[0] + ... + w[k-1] (float32, in selection order) reaches
  * p * (w[0] + ... + w[K-1]) (float32 total in the same order, one float32
  * product); p <= 0 or p >= 1 keeps all K.  The kept experts keep their
- * weights (no renormalization, as in the section 11 listing). */
+ * weights (no renormalization, as in the section 11 listing).  The tests pin
+ * this function to the rule as stated; the rule itself is a reading, so its
+ * parity with the article is unpinned. */
 int moe_ref_expert_keff(const float *w, int K, float p);
 
 /* Section 05 per-layer expert cache, one lookup (the article's expert_get):
