@@ -37,8 +37,13 @@ def _run(layer, x_np, path):
     return to_np(o), to_np(idx), to_np(w), to_np(keff)
 
 
+K16 = synth.Shape(D=256, I=128, E=64, K=16)   # two routed-down launches per token
+E512 = synth.Shape(D=256, I=128, E=512, K=8)  # 16-entry selection lists
+
+
 @pytest.mark.parametrize("shape,S,p", [(MID, 6, 0.5), (MID, 6, 0.7), (MID, 9, 0.9),
-                                       (GLM, 3, 0.7)])
+                                       (GLM, 3, 0.7), (K16, 5, 0.4), (K16, 4, 0.8),
+                                       (E512, 6, 0.6)])
 def test_topp_against_oracle(shape, S, p):
     say(f"top-p {p} D={shape.D} E={shape.E} S={S}")
     b = bias_for("uniform", 8, shape)
@@ -62,7 +67,8 @@ def test_topp_against_oracle(shape, S, p):
         say(f"  {path}: keff {keff.tolist()}")
 
 
-@pytest.mark.parametrize("shape,S,p", [(MID, 5, 0.6), (MID, 37, 0.8), (GLM, 4, 0.7)])
+@pytest.mark.parametrize("shape,S,p", [(MID, 5, 0.6), (MID, 37, 0.8), (GLM, 4, 0.7),
+                                       (K16, 7, 0.4), (E512, 5, 0.6)])
 def test_topp_union_equals_per_token_bit_exact(shape, S, p):
     dl = _with_topp(device_layer(9, shape, 0, bias_for("uniform", 9, shape)), p)
     x = synth.activations(41, S, shape.D)
