@@ -284,6 +284,25 @@ int moe_tier_fetch(const void *host_slabs, void *hbm_slots, size_t slab_bytes,
                    const int32_t *eids, const int32_t *slots, const int32_t *loads, int n,
                    hipStream_t stream);
 
+/* One call of a tiered layer, the steps above in native code: the router and
+ * the K selection rounds on the device (layer->router_w, router_b), one
+ * synchronization of stream to read the selection into host_idx (pinned host
+ * memory, S*K int32, owned by the caller and overwritten), moe_tier_map of the
+ * call's experts in order of first appearance, moe_tier_fetch of the missing
+ * slabs, the routing rewritten to slot numbers and copied back, then
+ * moe_layer_forward_routed (union_path = 0; ws of moe_workspace_bytes(cfg, S, 0))
+ * or moe_layer_forward_batch_routed (union_path = 1; which = 1) with
+ * layer->routed describing the slot stack over hbm_slots.  ws_router: a
+ * workspace of moe_workspace_bytes(cfg, S, 3).  Flags: MOE_F_ACCUMULATE only.
+ * *misses (optional) receives the call's misses.  The call returns after the
+ * selection has been read; the rest is queued on stream.  All K experts of
+ * every token are used (expert_topp does not apply). */
+int moe_tier_forward(moe_tier *t, int layer_index, const moe_config *cfg, const moe_layer *layer,
+                     const void *host_slabs, void *hbm_slots, size_t slab_bytes, const float *x,
+                     int S, float *out, unsigned flags, int union_path, int32_t *host_idx,
+                     int32_t *misses, void *ws_router, size_t ws_router_bytes, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+
 /* Section 13 swap rule for a frequency-managed tier holding pinned[0..n_pinned)
  * (host arrays, expert ids): take the coldest held expert by heat (first of
  * equals) and the hottest expert not held (first of equals, heat > 0); swap

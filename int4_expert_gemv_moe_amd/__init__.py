@@ -87,6 +87,8 @@ def lib():
         L.moe_tier_create_pinned.argtypes = [i32, i32, i32, i32]
         L.moe_tier_create_pinned.restype = vp
         L.moe_tier_rebalance.argtypes = [vp, i32, vp, vp, vp]
+        L.moe_tier_forward.argtypes = [vp, i32, vp, vp, vp, vp, sz, vp, i32, vp, u32, i32, vp, vp,
+                                       vp, sz, vp, sz, vp]
         L.moe_tier_destroy.argtypes = [vp]
         L.moe_tier_destroy.restype = None
         L.moe_tier_map.argtypes = [vp, i32, vp, i32, vp, vp]
@@ -102,7 +104,7 @@ def lib():
                      "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
                      "moe_slab_layout_of", "moe_tier_map",
                      "moe_tier_stats", "moe_tier_fetch", "moe_tier_pick_swap",
-                     "moe_tier_rebalance"):
+                     "moe_tier_rebalance", "moe_tier_forward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -529,36 +531,40 @@ class TieredLayer:
                            host, tier, layer_index)
 
     def cstruct(self, norm_gamma=None, norm_eps: float = 0.0) -> LayerC:
+        """Router and shared expert resident; routed experts = the slot stack."""
         sh = self.shared.cstruct() if self.shared is not None else Experts()
         g = None if norm_gamma is None else norm_gamma.data_ptr()
-        return LayerC(None, None, self.routed.cstruct(), sh, g, float(norm_eps))
+        return LayerC(self.router_w.data_ptr(), self.router_b.data_ptr(), self.routed.cstruct(), sh,
+                      g, float(norm_eps))
 
     def forward(self, x: torch.Tensor, ws_router: Workspace, ws: Workspace, out=None,
                 stream=None, union: bool = False):
-        """Returns (out, misses of this call).  union: run the unique-expert
-        union path (ws must then be a WS_BATCH workspace); the union of the
-        tokens' experts must fit in the layer's slots."""
-        import numpy as np
-        idx, w, _ = moe_router_topk(self.cfg, x, self.router_w, self.router_b, ws_router,
-                                    stream=stream)
-        # the routing is read on the host: wait for the stream the router ran on
-        (torch.cuda.current_stream() if stream is None else stream).synchronize()
-        idx_h = idx.cpu().numpy()
-        uniq, inv = np.unique(idx_h.ravel(), return_inverse=True)
-        order = np.argsort(np.unique(idx_h.ravel(), return_index=True)[1])  # first appearance
-        eids = uniq[order]
-        slots, loads, misses = self.tier.map(self.layer_index, eids)
-        Tier.fetch(self.host_slabs, self.routed.buf, self.routed.lay.bytes, eids, slots, loads,
-                   stream)
-        slot_of = np.empty(uniq.size, np.int32)
-        slot_of[order] = slots
-        sidx = torch.from_numpy(slot_of[inv].reshape(idx_h.shape).astype(np.int32)).to(x.device)
-        fn = moe_layer_forward_batch_routed if union else moe_layer_forward_routed
-        o = fn(self, x, sidx, w, ws, out=out, stream=stream)
+        """Returns (out, misses of this call), through moe_tier_forward: the
+        selection is read back once, the missing slabs are copied in and the
+        block runs on the slot stack.  union: the unique-expert union path (ws
+        must then be a WS_BATCH workspace); the union of the tokens' experts
+        must fit in the layer's slots."""
+        _dev(x, torch.float32, "x")
+        S = x.shape[0]
+        n = S * self.cfg.K
+        if getattr(self, "_host_idx", None) is None or self._host_idx.numel() < n:
+            self._host_idx = torch.empty(n, dtype=torch.int32, pin_memory=True)
+        if out is None:
+            out = torch.empty(S, self.cfg.D, dtype=torch.float32, device=x.device)
+        L = self.cstruct()
+        misses = ctypes.c_int32(0)
+        _check(lib().moe_tier_forward(self.tier.h, self.layer_index, ctypes.byref(self.cfg),
+                                      ctypes.byref(L), _ptr(self.host_slabs), _ptr(self.routed.buf),
+                                      self.routed.lay.bytes, _ptr(x), S, _ptr(out), 0,
+                                      1 if union else 0, _ptr(self._host_idx),
+                                      ctypes.byref(misses), ws_router.ptr, ws_router.nbytes,
+                                      ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
+               "moe_tier_forward")
+        o = out
         if self.tier.n_pinned:
             # one pinned-slot change by heat; its copy is ordered after the call
             changed, z, e, _ = self.tier.rebalance(self.layer_index)
             if changed:
                 Tier.fetch(self.host_slabs, self.routed.buf, self.routed.lay.bytes, [e], [z], [1],
                            stream)
-        return o, misses
+        return o, misses.value

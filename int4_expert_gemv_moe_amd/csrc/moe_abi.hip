@@ -2,6 +2,7 @@
 // host-side validation, workspace carving and the launch sequence of each
 // call.  No call allocates device memory.
 #include <algorithm>
+#include <vector>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -632,6 +633,57 @@ int moe_layer_forward_batch_routed(const moe_config *cfg, const moe_layer *layer
   if (!topk_idx) return MOE_EINVAL;
   return layer_forward_batch_impl(cfg, layer, x, S, topk_idx, topk_w, out, flags, nullptr, ws,
                                   ws_bytes, stream);
+}
+
+int moe_tier_forward(moe_tier *t, int layer_index, const moe_config *cfg, const moe_layer *layer,
+                     const void *host_slabs, void *hbm_slots, size_t slab_bytes, const float *x,
+                     int S, float *out, unsigned flags, int union_path, int32_t *host_idx,
+                     int32_t *misses, void *ws_router, size_t ws_router_bytes, void *ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config &c = *cfg;
+  if (!t || !layer || !host_slabs || !hbm_slots || !x || !out || !host_idx || !ws_router || !ws ||
+      S < 1)
+    return MOE_EINVAL;
+  if (flags & ~MOE_F_ACCUMULATE) return MOE_EINVAL;
+  if (!layer->router_w || !layer->router_b) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(layer->router_w) || ((uintptr_t)ws_router & 255u))
+    return MOE_EALIGN;
+  if (ws_router_bytes < carve(c, S, W_ROUTER, nullptr, nullptr)) return MOE_EWORKSPACE;
+  if (ws_bytes < carve(c, S, union_path ? W_BATCH : W_FWD, nullptr, nullptr)) return MOE_EWORKSPACE;
+  MOE_TRY(check_device());
+  // 1. selection on the device (all K experts; top-p does not apply here)
+  Work wr;
+  carve(c, S, W_ROUTER, (char *)ws_router, &wr);
+  MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, wr, false, true, nullptr, stream));
+  const size_t n = (size_t)S * c.K;
+  MOE_TRY_HIP(hipMemcpyAsync(host_idx, wr.idx, n * 4, hipMemcpyDeviceToHost, stream));
+  MOE_TRY_HIP(hipStreamSynchronize(stream));
+  // 2. the call's experts in order of first appearance, mapped to slots
+  std::vector<int32_t> eids, pos(n);
+  eids.reserve(n);
+  for (size_t i = 0; i < n; i++) {
+    const int32_t e = host_idx[i];
+    size_t u = 0;
+    while (u < eids.size() && eids[u] != e) u++;
+    if (u == eids.size()) eids.push_back(e);
+    pos[i] = (int32_t)u;
+  }
+  std::vector<int32_t> slots(eids.size()), loads(eids.size());
+  const int nm = moe_tier_map(t, layer_index, eids.data(), (int)eids.size(), slots.data(),
+                              loads.data());
+  if (nm < 0) return nm;
+  if (misses) *misses = nm;
+  // 3. the missing slabs, then the routing as slot numbers, both in stream order
+  MOE_TRY(moe_tier_fetch(host_slabs, hbm_slots, slab_bytes, eids.data(), slots.data(),
+                         loads.data(), (int)eids.size(), stream));
+  for (size_t i = 0; i < n; i++) host_idx[i] = slots[pos[i]];
+  MOE_TRY_HIP(hipMemcpyAsync(wr.idx, host_idx, n * 4, hipMemcpyHostToDevice, stream));
+  // 4. the block on the slot stack
+  return union_path ? layer_forward_batch_impl(cfg, layer, x, S, wr.idx, wr.w, out, flags, nullptr,
+                                               ws, ws_bytes, stream)
+                    : layer_forward_impl(cfg, layer, x, S, wr.idx, wr.w, out, flags, nullptr, ws,
+                                         ws_bytes, stream);
 }
 
 int moe_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y,
