@@ -107,6 +107,14 @@ def test_given_routing_and_tier_host_checks():
     # a layout needs D and I multiples of 32
     lay = moe.SlabLayout()
     assert L.moe_slab_layout_of(ctypes.byref(moe.config(256, 48, 8, 2)), ctypes.byref(lay)) == -2
+    # a tiered call: missing objects, or flags other than accumulate, are refused
+    t = L.moe_tier_create(1, 8, 4)
+    z = ctypes.c_size_t(0)
+    assert L.moe_tier_forward(None, 0, ctypes.byref(cfg), ctypes.byref(layer), a16, a16, 32, a16, 1,
+                              a16, 0, 0, a16, None, a16, 0, a16, 0, None) == -1
+    assert L.moe_tier_forward(t, 0, ctypes.byref(cfg), ctypes.byref(layer), a16, a16, 32, a16, 1,
+                              a16, 2, 0, a16, None, a16, 0, a16, 0, None) == -1
+    L.moe_tier_destroy(t)
     # tier objects: invalid sizes give no object
     assert not L.moe_tier_create(0, 8, 4) and not L.moe_tier_create(1, 8, 0)
     assert not L.moe_tier_create_pinned(1, 8, 4, 8)   # pinned slots < experts
