@@ -232,13 +232,17 @@ hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
   const int ne4 = (a.E + 3) / 4;
   const int nq = with_quant ? a.S : 0;
   // a few tokens: one token per wave, the whole weight row in one batch of
-  // loads (rows are re-read per token from L2); a few dozen: 8 tokens share
-  // each weight load; hundreds: 8 x 8 register tiles
+  // loads (rows are re-read per token from L2); up to 255: 4 x 4 register
+  // tiles; more: 8 x 8 register tiles
   if (a.S <= 8) {
     const size_t lds = a.gamma ? (size_t)a.D * 4 : 0;  // the normalized row
     hipLaunchKernelGGL((router_kernel<1, 24>), dim3(ne4 * a.S + nq), dim3(256), lds, st, a);
   } else if (a.S < kRouterTileMinTokens) {
-    hipLaunchKernelGGL((router_kernel<8, 4>), dim3(ne4 * ((a.S + 7) / 8) + nq), dim3(256), 0, st, a);
+    // 4 x 4 register tiles, 4 tokens x 16 experts per workgroup (swept against
+    // one expert x 8 tokens per wave: 19-20 against 21-24 us up to 64 tokens,
+    // 26-37 against 38-63 us from 128 to 255, router and selection together)
+    hipLaunchKernelGGL((router_tile_kernel<4, 4, 1>), dim3(((a.E + 15) / 16) * ((a.S + 3) / 4) + nq),
+                       dim3(256), 0, st, a);
   } else {
     // 4-wave workgroups of 8 tokens x 32 experts (swept against 8-wave
     // workgroups of 16 x 32 and other tiles: 188 against 209 us at 2048 tokens)
