@@ -55,6 +55,10 @@ def lib():
         L.moe_ref_dot_i4_i8.restype = ctypes.c_int32
         L.moe_ref_router_topk.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_ref_expert_swiglu_i4.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.moe_ref_quantize_rows.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.moe_ref_dot_i8_i8.argtypes = [vp, vp, i32]
+        L.moe_ref_dot_i8_i8.restype = ctypes.c_int32
+        L.moe_ref_expert_swiglu_i8.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_ref_layer_forward.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint]
         L.moe_ref_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, vp, vp]
         L.moe_ref_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp]
@@ -177,6 +181,68 @@ def expert_swiglu(cfg: Config, xq: np.ndarray, sx: np.ndarray, e: HostExpert):
     _check(lib().moe_ref_expert_swiglu_i4(ctypes.byref(cfg), _p(xq), _p(sx), S, ctypes.byref(es),
                                           _p(y), _p(acc_gu), _p(hq), _p(sh), _p(acc_d)),
            "expert_swiglu_i4")
+    return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
+
+
+def quantize_rows(w: np.ndarray, bits: int = 8):
+    """Section 05 per-row quantizer: (q [O][C] int8, scale [O] float32)."""
+    w = _c(w, np.float32)
+    O, C = w.shape
+    q = np.empty((O, C), np.int8)
+    s = np.empty(O, np.float32)
+    _check(lib().moe_ref_quantize_rows(_p(w), O, C, bits, _p(q), _p(s)), "quantize_rows")
+    return q, s
+
+
+def dot_i8_i8(w: np.ndarray, x: np.ndarray) -> int:
+    w = _c(w, np.int8)
+    x = _c(x, np.int8)
+    return int(lib().moe_ref_dot_i8_i8(_p(w), _p(x), w.size))
+
+
+class Q8Mat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class ExpertI8(ctypes.Structure):
+    _fields_ = [("gate", Q8Mat), ("up", Q8Mat), ("down", Q8Mat)]
+
+
+@dataclass
+class HostExpertI8:
+    """int8 expert on the host (section 05 format): gate/up [I][D], down [D][I]."""
+    gate_q: np.ndarray
+    gate_s: np.ndarray
+    up_q: np.ndarray
+    up_s: np.ndarray
+    down_q: np.ndarray
+    down_s: np.ndarray
+
+    def cstruct(self) -> ExpertI8:
+        return ExpertI8(Q8Mat(_p(self.gate_q), _p(self.gate_s)), Q8Mat(_p(self.up_q), _p(self.up_s)),
+                        Q8Mat(_p(self.down_q), _p(self.down_s)))
+
+    @staticmethod
+    def from_f32(g, u, d) -> "HostExpertI8":
+        gq, gs = quantize_rows(g, 8)
+        uq, us = quantize_rows(u, 8)
+        dq, ds = quantize_rows(d, 8)
+        return HostExpertI8(gq, gs, uq, us, dq, ds)
+
+
+def expert_swiglu_i8(cfg: Config, xq: np.ndarray, sx: np.ndarray, e: HostExpertI8):
+    xq = _c(xq, np.int8)
+    sx = _c(sx, np.float32)
+    S = xq.shape[0]
+    y = np.empty((S, cfg.D), np.float32)
+    acc_gu = np.empty((S, 2, cfg.I), np.int32)
+    hq = np.empty((S, cfg.I), np.int8)
+    sh = np.empty(S, np.float32)
+    acc_d = np.empty((S, cfg.D), np.int32)
+    es = e.cstruct()
+    _check(lib().moe_ref_expert_swiglu_i8(ctypes.byref(cfg), _p(xq), _p(sx), S, ctypes.byref(es),
+                                          _p(y), _p(acc_gu), _p(hq), _p(sh), _p(acc_d)),
+           "expert_swiglu_i8")
     return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
 
 

@@ -240,6 +240,77 @@ int moe_ref_expert_swiglu_i4(const moe_ref_config *cfg, const int8_t *xq, const 
   return 0;
 }
 
+/* ---- section 05: int8 weight rows; section 12: the int8 integer path ------ */
+
+int moe_ref_quantize_rows(const float *w, int O, int C, int bits, int8_t *q, float *scale) {
+  if (!w || !q || !scale || O < 1 || C < 1 || bits < 2 || bits > 8) return -1;
+  const int qmax = (1 << (bits - 1)) - 1;
+  for (int o = 0; o < O; o++) {
+    const float *wr = w + (int64_t)o * C;
+    float amax = 0.f;
+    for (int i = 0; i < C; i++) {
+      float a = fabsf(wr[i]);
+      if (a > amax) amax = a;
+    }
+    float s = amax / (float)qmax;
+    if (s < 1e-8f) s = 1e-8f;
+    scale[o] = s;
+    int8_t *qr = q + (int64_t)o * C;
+    for (int i = 0; i < C; i++) {
+      long v = lrintf(wr[i] / s);
+      if (v > qmax) v = qmax;
+      if (v < -qmax - 1) v = -qmax - 1;
+      qr[i] = (int8_t)v;
+    }
+  }
+  return 0;
+}
+
+int32_t moe_ref_dot_i8_i8(const int8_t *w, const int8_t *x, int C) {
+  int32_t acc = 0;
+  for (int c = 0; c < C; c++) acc += (int32_t)w[c] * (int32_t)x[c];
+  return acc;
+}
+
+static int q8mat_ok(const moe_ref_q8mat *m) { return m->q && m->scale; }
+
+int moe_ref_expert_swiglu_i8(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
+                             const moe_ref_expert_i8 *e, float *y, int32_t *acc_gu, int8_t *hq,
+                             float *sh, int32_t *acc_d) {
+  if (bad_cfg(cfg) || !xq || !sx || !e || !y || S < 1) return -1;
+  if (!q8mat_ok(&e->gate) || !q8mat_ok(&e->up) || !q8mat_ok(&e->down)) return -1;
+  const int D = cfg->D, I = cfg->I;
+  float *h = (float *)malloc((size_t)I * sizeof(float));
+  int8_t *hqr = (int8_t *)malloc((size_t)I);
+  if (!h || !hqr) { free(h); free(hqr); return -2; }
+  for (int s = 0; s < S; s++) {
+    const int8_t *xs = xq + (int64_t)s * D;
+    const float sxs = sx[s];
+    for (int o = 0; o < I; o++) {
+      int32_t ag = moe_ref_dot_i8_i8(e->gate.q + (int64_t)o * D, xs, D);
+      int32_t au = moe_ref_dot_i8_i8(e->up.q + (int64_t)o * D, xs, D);
+      if (acc_gu) {
+        acc_gu[((int64_t)s * 2 + 0) * I + o] = ag;
+        acc_gu[((int64_t)s * 2 + 1) * I + o] = au;
+      }
+      float g = ((float)ag * e->gate.scale[o]) * sxs;
+      float u = ((float)au * e->up.scale[o]) * sxs;
+      h[o] = silu_ref(g) * u;
+    }
+    float shs = moe_ref_quant_row_i8(h, I, hqr);
+    if (hq) memcpy(hq + (int64_t)s * I, hqr, (size_t)I);
+    if (sh) sh[s] = shs;
+    for (int d = 0; d < D; d++) {
+      int32_t ad = moe_ref_dot_i8_i8(e->down.q + (int64_t)d * I, hqr, I);
+      if (acc_d) acc_d[(int64_t)s * D + d] = ad;
+      y[(int64_t)s * D + d] = ((float)ad * e->down.scale[d]) * shs;
+    }
+  }
+  free(h);
+  free(hqr);
+  return 0;
+}
+
 /* ---- the block ------------------------------------------------------------ */
 
 static int layer_ok(const moe_ref_config *cfg, const moe_ref_layer *L) {

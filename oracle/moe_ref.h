@@ -9,6 +9,8 @@
  * Source: the reader.mx article "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型"
  * (called "the article" below), whose listings define every step:
  *   - section 04 (RMSNorm, SiLU, layer order),
+ *   - section 05 (per-row absmax quantization to int8, the expert cache's
+ *     int8 weight format),
  *   - section 06 (per-row int4 quantization and nibble packing),
  *   - section 11 (sigmoid router with correction bias, top-K, unique-expert
  *     union, SwiGLU expert, weighted scatter),
@@ -99,6 +101,36 @@ int moe_ref_router_topk(const moe_ref_config *cfg, const float *x, int S, const 
  * output), acc_d[S][D] (down-projection int32 accumulators). */
 int moe_ref_expert_swiglu_i4(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
                              const moe_ref_expert *e, float *y, int32_t *acc_gu, int8_t *hq,
+                             float *sh, int32_t *acc_d);
+
+/* Section 05 (the expert cache's per-row absmax quantizer, one int8 per
+ * value): qmax = 2^(bits-1) - 1 for bits in 2..8, s = max(amax/qmax, 1e-8),
+ * q = clamp(lrint(w/s), -qmax-1, qmax), w divided by s as in the article.
+ * bits = 8 gives the article's int8 expert format; bits = 4 gives the codes
+ * that moe_ref_pack_int4 packs. */
+int moe_ref_quantize_rows(const float *w, int O, int C, int bits, int8_t *q, float *scale);
+
+/* Exact integer dot of two int8 rows of C values (section 12 dot_i8i8: its
+ * sign folding is exact, so the result is the plain sum of products). */
+int32_t moe_ref_dot_i8_i8(const int8_t *w, const int8_t *x, int C);
+
+typedef struct {
+  const int8_t *q;    /* [O][C] */
+  const float *scale; /* [O] */
+} moe_ref_q8mat;
+
+typedef struct {
+  moe_ref_q8mat gate; /* O = I, C = D */
+  moe_ref_q8mat up;   /* O = I, C = D */
+  moe_ref_q8mat down; /* O = D, C = I */
+} moe_ref_expert_i8;
+
+/* moe_ref_expert_swiglu_i4 with int8 weight rows (section 12's integer path
+ * for the int8 format: int8 weights times int8 activation codes, the int32
+ * sum scaled by the weight row scale, then by the activation scale).  Same
+ * outputs and optional probes. */
+int moe_ref_expert_swiglu_i8(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
+                             const moe_ref_expert_i8 *e, float *y, int32_t *acc_gu, int8_t *hq,
                              float *sh, int32_t *acc_d);
 
 /* The block for S tokens, one token at a time: route, quantize the token,
