@@ -344,6 +344,62 @@ def bench_topp(layers, x, steps: int = 512, ps=(0.7, 0.9, 1.0)):
     return res
 
 
+EXPERT_I8_BYTES = 3 * I * D + (2 * I + D) * 4   # 37,789,696: int8 codes + row scales
+
+
+def bench_fmt8(layer, steps: int = 512, n8: int = 8, n4: int = 16):
+    """One GLM-shape SwiGLU expert on one token, int8 weight format against
+    the int4 one: each call reads one expert (cycling over 8 int8 or 16 int4
+    experts, about 302 MB either way, so the weights come from HBM rather
+    than the MALL); plain stream launches between events."""
+    import torch
+
+    import int4_expert_gemv_moe_amd as moe
+    import synth
+    from synth.device_layers import build_device_experts_i8
+
+    lib = moe.lib()
+    cfg = layer.cfg
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    e8 = build_device_experts_i8(0, synth.GLM, 0, n8)
+    xq, sx = moe.moe_quant_act_i8(torch.from_numpy(synth.activations(7, 1, D)).cuda())
+    y = torch.empty(1, D, dtype=torch.float32, device="cuda")
+    ws8 = moe.Workspace(cfg, 1, moe.WS_SWIGLU8)
+    ws4 = moe.Workspace(cfg, 1, moe.WS_SWIGLU)
+    s8, s4 = e8.cstruct(), layer.routed.cstruct()
+    cref = ctypes.byref(cfg)
+    args = (ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(sx.data_ptr()), 1)
+    yp = ctypes.c_void_p(y.data_ptr())
+    calls = {
+        "int8": (lib.moe_expert_swiglu_i8, ctypes.byref(s8), n8, ws8, EXPERT_I8_BYTES),
+        "int4": (lib.moe_expert_swiglu_i4, ctypes.byref(s4), n4, ws4, EXPERT_BYTES),
+    }
+    res = {"workload": "one GLM-shape SwiGLU expert (6144 -> 2048 -> 6144), 1 token per call, "
+                       "int8 weight format against int4, weights cycled over ~302 MB",
+           "steps": steps}
+    for name, (fn, eref, n, ws, nbytes) in calls.items():
+        def run(k):
+            rc = 0
+            for i in range(k):
+                rc |= fn(cref, *args, eref, i % n, yp, None, None, None, None, ws.ptr, ws.nbytes, st)
+            if rc:
+                raise moe.MoeError(f"{name} expert call failed ({rc})")
+
+        run(64)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        res[name] = {"us_per_call": round(us, 3), "weight_bytes": int(nbytes),
+                     "GBps": round(nbytes / us / 1e3, 1),
+                     "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+        log(f"expert {name}: {us:.2f} us/call ({nbytes / us / 1e3:.0f} GB/s)")
+    return res
+
+
 def bench_stack(steps: int = 64):
     """48 GLM-shape layers resident in HBM (per-layer Zipf-skewed routing,
     RMSNorm + residual, one MOE_F_PRENORM call per layer): decode steps of
@@ -439,7 +495,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the verify, prefill and 48-layer stack measurements")
-    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered", "topp"],
+    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered", "topp", "fmt8"],
                     help="run only that secondary measurement and print its record (for profiling)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay pass (value then comes from the stream pass); "
@@ -484,7 +540,7 @@ def main():
         else:
             layer = build_device_layer(0, synth.GLM, 0, synth.router_b_uniform(0, synth.GLM, 0))
             rec = {"verify": bench_verify, "prefill": bench_prefill,
-                   "tiered": bench_tiered}[args.only](layer)
+                   "tiered": bench_tiered, "fmt8": bench_fmt8}[args.only](layer)
         print(json.dumps(rec), flush=True)
         return
     t0 = time.time()
@@ -625,7 +681,7 @@ def main():
         except Exception as exc:  # reported, the headline line is still printed
             secondary["topp_decode"] = {"error": f"{type(exc).__name__}: {exc}"}
         for key, fn in (("verify_64_zipf", bench_verify), ("prefill_2048", bench_prefill),
-                        ("tiered_decode", bench_tiered)):
+                        ("tiered_decode", bench_tiered), ("expert_int8_format", bench_fmt8)):
             try:
                 secondary[key] = fn(layers[0])
             except Exception as exc:  # reported, the headline line is still printed

@@ -125,11 +125,31 @@ typedef struct {
   int32_t *keff;        /* [S] experts kept per token (K unless expert_topp is in (0, 1)) */
 } moe_probe;
 
+/* The article's int8 weight format (section 05: the expert cache holds each
+ * matrix as one int8 code per weight plus one float scale per row; section 12
+ * runs it on the integer path).  One int8 matrix per expert, stacked over
+ * experts: expert e's codes q[O][C] start at q + e*q_stride bytes and its
+ * scales at scale + e*scale_stride floats; a stride of 0 means densely
+ * stacked (O*C bytes, O floats).  q and q_stride must be 16-byte aligned. */
+typedef struct {
+  const int8_t *q;
+  const float *scale;
+  int64_t q_stride;
+  int64_t scale_stride;
+} moe_q8mat;
+
+typedef struct {
+  moe_q8mat gate; /* O = I, C = D */
+  moe_q8mat up;   /* O = I, C = D */
+  moe_q8mat down; /* O = D, C = I */
+} moe_experts_i8;
+
 /* Human-readable name of a status code (static string). */
 const char *moe_status_str(int status);
 
 /* Workspace bytes needed by a call with S tokens.  which: 0 = moe_layer_forward,
- * 1 = moe_layer_forward_batch, 2 = moe_expert_swiglu_i4, 3 = moe_router_topk.
+ * 1 = moe_layer_forward_batch, 2 = moe_expert_swiglu_i4, 3 = moe_router_topk,
+ * 4 = moe_expert_swiglu_i8.
  * Returns 0 for invalid arguments. */
 size_t moe_workspace_bytes(const moe_config *cfg, int S, int which);
 
@@ -140,6 +160,14 @@ int moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
  * q4[O][C/2] and scale[O].  C must be even.  Bit-exact with the article's
  * packer (division by the scale, round half to even, clamp to [-8, 7]). */
 int moe_pack_int4(const float *w, int O, int C, uint8_t *q4, float *scale, hipStream_t stream);
+
+/* Section 05 per-row weight quantization to int8 codes: for each row of
+ * w[O][C] (float32), s = max(amax/127, 1e-8), q = clamp(rint(w/s), -128, 127)
+ * (division by the scale, round half to even, as the article's quantizer
+ * does with bits = 8).  Outputs q[O][C] and scale[O].  Any C >= 1; w and
+ * scale 4-byte aligned.  Bit-exact with the article's quantizer. */
+int moe_quantize_rows_i8(const float *w, int O, int C, int8_t *q, float *scale,
+                         hipStream_t stream);
 
 /* Section 12: per-row int8 quantization of x[S][D] (float32, or bf16 widened
  * exactly).  Outputs xq[S][D] and sx[S].  D must be a multiple of 8. */
@@ -166,6 +194,17 @@ int moe_router_topk(const moe_config *cfg, const float *x, int S, const float *r
 int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *sx, int S,
                          const moe_experts *w, int expert, float *y, int32_t *acc_gu, int8_t *hq,
                          float *sh, int32_t *acc_d, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_expert_swiglu_i4 for an expert in the int8 format (*w, host struct):
+ * gate/up sums acc = sum_c q[o][c] * xq[s][c] over int8 weight codes, then
+ * g = (acc_g * s_g) * s_x, u likewise, h = silu(g) * u, h requantized per
+ * row (section 12, as for the int4 format), y = (acc_d * s_d) * sh.  Same
+ * outputs and probes as moe_expert_swiglu_i4; xq and hq (if given) must be
+ * 16-byte aligned.  Workspace: moe_workspace_bytes(cfg, S, 4). */
+int moe_expert_swiglu_i8(const moe_config *cfg, const int8_t *xq, const float *sx, int S,
+                         const moe_experts_i8 *w, int expert, float *y, int32_t *acc_gu,
+                         int8_t *hq, float *sh, int32_t *acc_d, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /* The block, one token at a time (each token reads its own K experts):
  * route, quantize, run the K routed experts and the shared expert, and

@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("MOE_I4_LIB") or os.path.join(HERE, "libmoe_i4.so")
 MOE_F32, MOE_BF16 = 0, 1
 F_ACCUMULATE = 1
 F_PRENORM = 2
-WS_FORWARD, WS_BATCH, WS_SWIGLU, WS_ROUTER = 0, 1, 2, 3
+WS_FORWARD, WS_BATCH, WS_SWIGLU, WS_ROUTER, WS_SWIGLU8 = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -75,6 +75,8 @@ def lib():
         L.moe_quant_act_i8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.moe_router_topk.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_swiglu_i4.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_quantize_rows_i8.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_expert_swiglu_i8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp, vp]
@@ -99,7 +101,8 @@ def lib():
         L.moe_tier_lfru_score.restype = ctypes.c_uint64
         L.moe_stream_read_sink_words.argtypes = []
         for name in ("moe_workspace_init", "moe_pack_int4", "moe_quant_act_i8", "moe_router_topk",
-                     "moe_expert_swiglu_i4", "moe_layer_forward", "moe_layer_forward_batch",
+                     "moe_expert_swiglu_i4", "moe_quantize_rows_i8", "moe_expert_swiglu_i8",
+                     "moe_layer_forward", "moe_layer_forward_batch",
                      "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
                      "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
                      "moe_slab_layout_of", "moe_tier_map",
@@ -175,6 +178,47 @@ class DeviceExperts:
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in
                    (self.gate_q4, self.gate_s, self.up_q4, self.up_s, self.down_q4, self.down_s))
+
+
+class Q8Mat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("q_stride", ctypes.c_int64),
+                ("scale_stride", ctypes.c_int64)]
+
+
+class ExpertsI8(ctypes.Structure):
+    _fields_ = [("gate", Q8Mat), ("up", Q8Mat), ("down", Q8Mat)]
+
+
+@dataclass
+class DeviceExpertsI8:
+    """Stacked experts in the int8 format on the device: gate/up codes
+    [n][I][D], scales [n][I]; down codes [n][D][I], scales [n][D]."""
+    gate_q: torch.Tensor
+    gate_s: torch.Tensor
+    up_q: torch.Tensor
+    up_s: torch.Tensor
+    down_q: torch.Tensor
+    down_s: torch.Tensor
+
+    @staticmethod
+    def empty(n: int, D: int, I: int, device="cuda") -> "DeviceExpertsI8":
+        i8, f32 = torch.int8, torch.float32
+        return DeviceExpertsI8(torch.empty(n, I, D, dtype=i8, device=device),
+                               torch.empty(n, I, dtype=f32, device=device),
+                               torch.empty(n, I, D, dtype=i8, device=device),
+                               torch.empty(n, I, dtype=f32, device=device),
+                               torch.empty(n, D, I, dtype=i8, device=device),
+                               torch.empty(n, D, dtype=f32, device=device))
+
+    def cstruct(self) -> ExpertsI8:
+        def q(a, b):
+            return Q8Mat(a.data_ptr(), b.data_ptr(), 0, 0)
+        return ExpertsI8(q(self.gate_q, self.gate_s), q(self.up_q, self.up_s),
+                         q(self.down_q, self.down_s))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.gate_q, self.gate_s, self.up_q, self.up_s, self.down_q, self.down_s))
 
 
 @dataclass
@@ -274,6 +318,39 @@ def moe_expert_swiglu_i4(cfg: Config, xq: torch.Tensor, sx: torch.Tensor, expert
                                       expert, _ptr(y), _ptr(acc_gu), _ptr(hq), _ptr(sh), _ptr(acc_d),
                                       ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
            "moe_expert_swiglu_i4")
+    return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
+
+
+def moe_quantize_rows_i8(w: torch.Tensor, q: torch.Tensor | None = None,
+                         scale: torch.Tensor | None = None, stream=None):
+    """Section 05 quantizer on the device: w [O][C] float32 -> (q [O][C] int8, scale [O])."""
+    _dev(w, torch.float32, "w")
+    O, C = w.shape
+    q = torch.empty(O, C, dtype=torch.int8, device=w.device) if q is None else q
+    scale = torch.empty(O, dtype=torch.float32, device=w.device) if scale is None else scale
+    _check(lib().moe_quantize_rows_i8(_ptr(w), O, C, _ptr(q), _ptr(scale),
+                                      ctypes.c_void_p(_stream(stream))), "moe_quantize_rows_i8")
+    return q, scale
+
+
+def moe_expert_swiglu_i8(cfg: Config, xq: torch.Tensor, sx: torch.Tensor, experts: DeviceExpertsI8,
+                         expert: int, ws: Workspace, probes: bool = False, stream=None, y=None):
+    _dev(xq, torch.int8, "xq")
+    _dev(sx, torch.float32, "sx")
+    S = xq.shape[0]
+    dev = xq.device
+    y = torch.empty(S, cfg.D, dtype=torch.float32, device=dev) if y is None else y
+    acc_gu = hq = sh = acc_d = None
+    if probes:
+        acc_gu = torch.empty(S, 2, cfg.I, dtype=torch.int32, device=dev)
+        hq = torch.empty(S, cfg.I, dtype=torch.int8, device=dev)
+        sh = torch.empty(S, dtype=torch.float32, device=dev)
+        acc_d = torch.empty(S, cfg.D, dtype=torch.int32, device=dev)
+    es = experts.cstruct()
+    _check(lib().moe_expert_swiglu_i8(ctypes.byref(cfg), _ptr(xq), _ptr(sx), S, ctypes.byref(es),
+                                      expert, _ptr(y), _ptr(acc_gu), _ptr(hq), _ptr(sh), _ptr(acc_d),
+                                      ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
+           "moe_expert_swiglu_i8")
     return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
 
 

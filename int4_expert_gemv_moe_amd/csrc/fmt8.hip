@@ -1,0 +1,217 @@
+// fmt8.hip -- the int8 weight format of the reader.mx article "惊呆了！25GB
+// 内存上运行 GLM 5.2 744B 模型": the section 05 per-row quantizer (one int8
+// code per weight, one float scale per row) and the section 12 integer path
+// for that format (int8 weights times int8 activation codes, the int32 sum
+// scaled by the row scale and then by the activation scale), as a SwiGLU
+// expert.
+//
+// The expert runs in two launches: gate/up + SwiGLU (one wave per output
+// row, the row's gate and up codes held in registers while the wave walks the
+// tokens), then the per-row requantization of h and down (one wave per four
+// output rows, same scheme).  Every
+// weight byte is read once per call; the token codes are re-read per wave
+// from the cache.  Rows are split into 16-byte pieces, lane l taking piece l
+// of every 1024-column chunk, so each load instruction of a wave covers 1 KiB
+// of one row.
+#include "moe_kernels.h"
+#include "quant.h"
+#include "rowops.h"
+
+namespace moe {
+
+// One wave per row: s = max(amax/127, 1e-8), q = clamp(rint(w/s), -128, 127),
+// w divided by s as in the article's quantizer.
+__global__ __launch_bounds__(256) void quant_rows_i8_kernel(Q8QuantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (o >= a.O) return;
+  const float *wr = a.w + (int64_t)o * a.C;
+  float m = 0.f;
+  for (int j = lane; j < a.C; j += 64) m = fmax_nan_skip(m, fabsf(wr[j]));
+  m = wave_max_f32(m);
+  float s = m / 127.f;
+  if (s < 1e-8f) s = 1e-8f;
+  int8_t *qr = a.q + (int64_t)o * a.C;
+  for (int j = lane; j < a.C; j += 64)
+    qr[j] = (int8_t)(int)fminf(fmaxf(rintf(wr[j] / s), -128.f), 127.f);
+  if (lane == 0) a.scale[o] = s;
+}
+
+// 16 int8 weights against 16 int8 activation codes.
+__device__ __forceinline__ int dot16_i8(const uint4 &w, const uint4 &x, int acc) {
+  acc = dot4((int)w.x, (int)x.x, acc);
+  acc = dot4((int)w.y, (int)x.y, acc);
+  acc = dot4((int)w.z, (int)x.z, acc);
+  acc = dot4((int)w.w, (int)x.w, acc);
+  return acc;
+}
+
+// Gate/up: wave w of block b owns row o = 4b + w of both matrices.
+// NCH = ceil(D / 1024) chunks; MASKED when D is not a multiple of 1024.
+template <int NCH, bool MASKED>
+__global__ __launch_bounds__(256) void gu8_kernel(Swiglu8Args a) {
+  const int lane = threadIdx.x & 63;
+  const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (o >= a.I) return;
+  const int8_t *gr = a.G + (int64_t)o * a.D;
+  const int8_t *ur = a.U + (int64_t)o * a.D;
+  uint4 g[NCH], u[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    const int col = 1024 * c + 16 * lane;
+    const bool ok = !MASKED || col < a.D;
+    g[c] = ldnt16(gr + col, ok, gr);
+    u[c] = ldnt16(ur + col, ok, ur);
+  }
+  const float gs = a.gs[o], us = a.us[o];
+  for (int s = 0; s < a.S; s++) {
+    const int8_t *xs = a.xq + (int64_t)s * a.D;
+    int ag = 0, au = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+      const int col = 1024 * c + 16 * lane;
+      const uint4 xv = ld16(xs + col, !MASKED || col < a.D, xs);
+      ag = dot16_i8(g[c], xv, ag);
+      au = dot16_i8(u[c], xv, au);
+    }
+    ag = wave_sum_i32(ag);
+    au = wave_sum_i32(au);
+    if (lane == 0) {
+      const float sxs = a.sx[s];
+      const float gv = ((float)ag * gs) * sxs;
+      const float uv = ((float)au * us) * sxs;
+      a.h[(int64_t)s * a.I + o] = silu(gv) * uv;
+      if (a.acc_gu) {
+        a.acc_gu[(int64_t)s * 2 * a.I + o] = ag;
+        a.acc_gu[((int64_t)s * 2 + 1) * a.I + o] = au;
+      }
+    }
+  }
+}
+
+// Down: wave w of block b owns rows d0 .. d0+R-1, d0 = (4b + w) R.  Every
+// block requantizes the rows of h it needs into shared memory (the section 12
+// quantization of the down projection's input, the same bits as the
+// activation quantizer), kDn8CodeBytes of codes at a time: the weight loads
+// are issued first, so their latency overlaps the requantization.  Block 0
+// also writes the codes and scales out when the caller asks for them.
+constexpr int kDn8CodeBytes = 32768;
+
+template <int NCH, bool MASKED, int R>
+__global__ __launch_bounds__(256) void dn8_kernel(Swiglu8Args a) {
+  __shared__ __align__(16) int8_t codes[kDn8CodeBytes];
+  __shared__ float shs[kDn8CodeBytes / 32];  // I >= 32
+  const int lane = threadIdx.x & 63;
+  const int d0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  // no early exit: every wave takes part in the block's barriers
+  uint4 w[R][NCH];
+  float dsc[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const int d = min(d0 + r, a.D - 1);
+    const int8_t *row = a.Dn + (int64_t)d * a.I;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+      const int col = 1024 * c + 16 * lane;
+      w[r][c] = ldnt16(row + col, !MASKED || col < a.I, row);
+    }
+    dsc[r] = a.ds[d];
+  }
+  const int TS = kDn8CodeBytes / a.I;
+  for (int s0 = 0; s0 < a.S; s0 += TS) {
+    const int ns = min(TS, a.S - s0);
+    __syncthreads();  // the previous chunk's codes are consumed
+    for (int j = 0; j < ns; j++)
+      quant_row_block(a.h + (int64_t)(s0 + j) * a.I, nullptr, a.I, nullptr, codes + j * a.I,
+                      &shs[j], nullptr);
+    __syncthreads();  // the scales are written by thread 0 after the last barrier
+    if (blockIdx.x == 0) {
+      if (a.hq_out)
+        for (int i = threadIdx.x; i < ns * a.I / 16; i += 256)
+          reinterpret_cast<uint4 *>(a.hq_out + (int64_t)s0 * a.I)[i] =
+              reinterpret_cast<const uint4 *>(codes)[i];
+      if (a.sh_out && (int)threadIdx.x < ns) a.sh_out[s0 + threadIdx.x] = shs[threadIdx.x];
+    }
+    for (int j = 0; j < ns; j++) {
+      const int8_t *hs = codes + j * a.I;
+      uint4 hv[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; c++) {
+        const int col = 1024 * c + 16 * lane;
+        hv[c] = (!MASKED || col < a.I) ? *reinterpret_cast<const uint4 *>(hs + col)
+                                       : make_uint4(0u, 0u, 0u, 0u);
+      }
+      const float sh = shs[j];
+      const int64_t s = s0 + j;
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+        int acc = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; c++) acc = dot16_i8(w[r][c], hv[c], acc);
+        acc = wave_sum_i32(acc);
+        if (lane == r && d0 + r < a.D) {
+          a.y[s * a.D + d0 + r] = ((float)acc * dsc[r]) * sh;
+          if (a.acc_d) a.acc_d[s * a.D + d0 + r] = acc;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_quant_rows_i8(const Q8QuantArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(quant_rows_i8_kernel, dim3((a.O + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int NCH>
+static void launch_gu8(const Swiglu8Args &a, hipStream_t st) {
+  const dim3 grid((a.I + 3) / 4);
+  if (a.D % 1024)
+    hipLaunchKernelGGL((gu8_kernel<NCH, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gu8_kernel<NCH, false>), grid, dim3(256), 0, st, a);
+}
+
+// D and I are at most 8192 (checked by the caller): at most 8 chunks.
+hipError_t launch_swiglu8_gateup(const Swiglu8Args &a, hipStream_t st) {
+  switch ((a.D + 1023) / 1024) {
+    case 1: launch_gu8<1>(a, st); break;
+    case 2: launch_gu8<2>(a, st); break;
+    case 3: launch_gu8<3>(a, st); break;
+    case 4: launch_gu8<4>(a, st); break;
+    case 5: launch_gu8<5>(a, st); break;
+    case 6: launch_gu8<6>(a, st); break;
+    case 7: launch_gu8<7>(a, st); break;
+    case 8: launch_gu8<8>(a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int NCH, int R>
+static void launch_dn8(const Swiglu8Args &a, hipStream_t st) {
+  const dim3 grid((a.D + 4 * R - 1) / (4 * R));
+  if (a.I % 1024)
+    hipLaunchKernelGGL((dn8_kernel<NCH, true, R>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((dn8_kernel<NCH, false, R>), grid, dim3(256), 0, st, a);
+}
+
+// Rows per wave swept at the GLM shape (I = 2048, one token): 1, 2, 4, 8 rows
+// gave 12.7, 11.5, 11.7, 11.9 us per expert call.
+hipError_t launch_swiglu8_down(const Swiglu8Args &a, hipStream_t st) {
+  switch ((a.I + 1023) / 1024) {
+    case 1: launch_dn8<1, 4>(a, st); break;
+    case 2: launch_dn8<2, 2>(a, st); break;
+    case 3: launch_dn8<3, 2>(a, st); break;
+    case 4: launch_dn8<4, 2>(a, st); break;
+    case 5: launch_dn8<5, 2>(a, st); break;
+    case 6: launch_dn8<6, 2>(a, st); break;
+    case 7: launch_dn8<7, 1>(a, st); break;
+    case 8: launch_dn8<8, 1>(a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -48,7 +48,7 @@ int check_cfg(const moe_config *c) {
   return MOE_OK;
 }
 
-enum Which { W_FWD = 0, W_BATCH = 1, W_SWIGLU = 2, W_ROUTER = 3 };
+enum Which { W_FWD = 0, W_BATCH = 1, W_SWIGLU = 2, W_ROUTER = 3, W_SWIGLU8 = 4 };
 
 // Workgroup counts of the per-token path (rows of a phase are split evenly
 // over its workgroups).  MOE_DECODE_BLOCKS="a,b,c,d" overrides them for
@@ -96,6 +96,11 @@ size_t carve(const moe_config &c, int S, int which, char *base, Work *w) {
     return p;
   };
   Work t{};
+  if (which == W_SWIGLU8) {
+    t.h = (float *)take(s * c.I * 4);
+    if (w) *w = t;
+    return off;
+  }
   if (which != W_SWIGLU) {
     t.logits = (float *)take(s * c.E * 4);
     t.idx = (int32_t *)take(s * c.K * 4);
@@ -156,6 +161,27 @@ int check_experts(const moe_experts &e) {
   int rc;
   if ((rc = check_qmat(e.gate)) || (rc = check_qmat(e.up)) || (rc = check_qmat(e.down))) return rc;
   return MOE_OK;
+}
+
+int check_q8mat(const moe_q8mat &m) {
+  if (!m.q || !m.scale) return MOE_EINVAL;
+  if (!aligned16(m.q) || ((uintptr_t)m.scale & 3u)) return MOE_EALIGN;
+  if (m.q_stride < 0 || m.scale_stride < 0 || (m.q_stride & 15)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+int check_experts_i8(const moe_experts_i8 &e) {
+  int rc;
+  if ((rc = check_q8mat(e.gate)) || (rc = check_q8mat(e.up)) || (rc = check_q8mat(e.down))) return rc;
+  return MOE_OK;
+}
+
+// Expert e's codes and scales in a stacked int8 matrix of O x C.
+void q8_rows(const moe_q8mat &m, int O, int C, int e, const int8_t **q, const float **s) {
+  const int64_t qs = m.q_stride ? m.q_stride : (int64_t)O * C;
+  const int64_t ss = m.scale_stride ? m.scale_stride : (int64_t)O;
+  *q = m.q + (int64_t)e * qs;
+  *s = m.scale + (int64_t)e * ss;
 }
 
 int check_layer(const moe_config &c, const moe_layer *L, bool router = true) {
@@ -277,7 +303,7 @@ const char *moe_status_str(int status) {
 }
 
 size_t moe_workspace_bytes(const moe_config *cfg, int S, int which) {
-  if (check_cfg(cfg) != MOE_OK || S < 1 || which < 0 || which > 3) return 0;
+  if (check_cfg(cfg) != MOE_OK || S < 1 || which < 0 || which > 4) return 0;
   return carve(*cfg, S, which, nullptr, nullptr);
 }
 
@@ -300,6 +326,53 @@ int moe_pack_int4(const float *w, int O, int C, uint8_t *q4, float *scale, hipSt
   MOE_TRY(check_device());
   PackArgs a{w, O, C, q4, scale};
   return hip_rc(launch_pack(a, stream));
+}
+
+int moe_quantize_rows_i8(const float *w, int O, int C, int8_t *q, float *scale,
+                         hipStream_t stream) {
+  if (!w || !q || !scale) return MOE_EINVAL;
+  if (O < 1 || C < 1) return MOE_ESHAPE;
+  if (((uintptr_t)w & 3u) || ((uintptr_t)scale & 3u)) return MOE_EALIGN;
+  MOE_TRY(check_device());
+  Q8QuantArgs a{w, O, C, q, scale};
+  return hip_rc(launch_quant_rows_i8(a, stream));
+}
+
+int moe_expert_swiglu_i8(const moe_config *cfg, const int8_t *xq, const float *sx, int S,
+                         const moe_experts_i8 *wts, int expert, float *y, int32_t *acc_gu,
+                         int8_t *hq, float *sh, int32_t *acc_d, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (S < 1 || !xq || !sx || !wts || !y || !ws) return MOE_EINVAL;
+  if (expert < 0 || expert >= cfg->E) return MOE_EINVAL;
+  MOE_TRY(check_experts_i8(*wts));
+  if (!aligned16(xq) || ((uintptr_t)sx & 3u) || ((uintptr_t)y & 3u) || ((uintptr_t)ws & 255u))
+    return MOE_EALIGN;
+  if ((hq && !aligned16(hq)) || ((uintptr_t)sh & 3u) || ((uintptr_t)acc_gu & 3u) ||
+      ((uintptr_t)acc_d & 3u))
+    return MOE_EALIGN;
+  if (ws_bytes < carve(*cfg, S, W_SWIGLU8, nullptr, nullptr)) return MOE_EWORKSPACE;
+  MOE_TRY(check_device());
+  Work w;
+  carve(*cfg, S, W_SWIGLU8, (char *)ws, &w);
+  Swiglu8Args a{};
+  a.xq = xq;
+  a.sx = sx;
+  a.S = S;
+  a.D = cfg->D;
+  a.I = cfg->I;
+  q8_rows(wts->gate, cfg->I, cfg->D, expert, &a.G, &a.gs);
+  q8_rows(wts->up, cfg->I, cfg->D, expert, &a.U, &a.us);
+  q8_rows(wts->down, cfg->D, cfg->I, expert, &a.Dn, &a.ds);
+  a.h = w.h;
+  a.acc_gu = acc_gu;
+  a.hq_out = hq;
+  a.sh_out = sh;
+  a.y = y;
+  a.acc_d = acc_d;
+  MOE_TRY_HIP(launch_swiglu8_gateup(a, stream));
+  MOE_TRY_HIP(launch_swiglu8_down(a, stream));
+  return MOE_OK;
 }
 
 int moe_quant_act_i8(const void *x, moe_dtype dtype, int S, int D, int8_t *xq, float *sx,

@@ -179,6 +179,34 @@ struct RmsArgs {
 
 // Host launchers, each defined next to its kernels.  They return the launch
 // status (hipGetLastError after the launch).
+// The int8 weight format (fmt8.hip).
+struct Q8QuantArgs {
+  const float *w;  // [O][C]
+  int O, C;
+  int8_t *q;       // [O][C]
+  float *scale;    // [O]
+};
+
+struct Swiglu8Args {
+  const int8_t *xq;        // [S][D] natural-order activation codes
+  const float *sx;         // [S]
+  int S, D, I;
+  const int8_t *G, *U;     // [I][D] this expert's gate and up codes
+  const int8_t *Dn;        // [D][I] down codes
+  const float *gs, *us;    // [I]
+  const float *ds;         // [D]
+  float *h;                // [S][I] SwiGLU output
+  int32_t *acc_gu;         // optional [S][2][I]
+  int8_t *hq_out;          // optional [S][I] requantized h (natural order)
+  float *sh_out;           // optional [S]
+  float *y;                // [S][D]
+  int32_t *acc_d;          // optional [S][D]
+};
+
+hipError_t launch_quant_rows_i8(const Q8QuantArgs &a, hipStream_t st);
+hipError_t launch_swiglu8_gateup(const Swiglu8Args &a, hipStream_t st);
+hipError_t launch_swiglu8_down(const Swiglu8Args &a, hipStream_t st);
+
 hipError_t launch_quant(const QuantArgs &a, int S, hipStream_t st);
 hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st);

@@ -44,3 +44,22 @@ def build_device_layer(seed: int, shape: synth.Shape, layer: int, router_b: np.n
         fill(shared, 0, synth.SHARED)
     del tmp
     return moe.DeviceLayer(cfg, wr, rb, routed, shared)
+
+
+def build_device_experts_i8(seed: int, shape: synth.Shape, layer: int, n: int,
+                            device: str = "cuda") -> moe.DeviceExpertsI8:
+    """n experts of the shape in the int8 weight format, drawn from the same
+    streams as experts 0..n-1 of the layer and quantized by the library's
+    section 05 quantizer (moe_quantize_rows_i8)."""
+    D, I = shape.D, shape.I
+    st = torch.cuda.current_stream().cuda_stream
+    out = moe.DeviceExpertsI8.empty(n, D, I, device)
+    tmp = torch.empty(I * D, dtype=torch.float32, device=device)
+    for e in range(n):
+        sg, su, sd = synth.expert_streams(layer, e)
+        for strm, q, sc, O, C in ((sg, out.gate_q, out.gate_s, I, D), (su, out.up_q, out.up_s, I, D),
+                                  (sd, out.down_q, out.down_s, D, I)):
+            synth.dev_fill_normal(tmp.data_ptr(), seed, strm, O * C, synth.WEIGHT_SIGMA, st)
+            moe.moe_quantize_rows_i8(tmp[: O * C].view(O, C), q[e], sc[e])
+    del tmp
+    return out

@@ -148,3 +148,32 @@ def test_prenorm_flag_host_checks():
         assert call(moe.F_PRENORM, lay=moe.LayerC(base, base, ex, ex, base + 4, 1e-5)) == -3
         # out inside x but not equal to it stays refused
         assert call(moe.F_ACCUMULATE | moe.F_PRENORM, out=ctypes.c_void_p(base + 16)) == -1
+
+
+def test_int8_format_host_checks():
+    """The int8 weight format's calls validate on the host: null pointers,
+    shapes, expert index, alignment of the codes and the workspace size."""
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    buf = ctypes.create_string_buffer(512)
+    a16 = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 256
+    assert L.moe_quantize_rows_i8(None, 4, 8, a16, a16, None) == -1
+    assert L.moe_quantize_rows_i8(a16, 0, 8, a16, a16, None) == -2
+    assert L.moe_quantize_rows_i8(a16 + 2, 4, 8, a16, a16, None) == -3
+    cfg = moe.config(256, 128, 8, 2)
+    # workspace: h [S][I] f32 on a 256-byte boundary
+    up = lambda n: (n + 255) // 256 * 256
+    assert L.moe_workspace_bytes(ctypes.byref(cfg), 3, moe.WS_SWIGLU8) == up(3 * 128 * 4)
+    m = moe.Q8Mat(a16, a16, 0, 0)
+    ex = moe.ExpertsI8(m, m, m)
+    ws_need = L.moe_workspace_bytes(ctypes.byref(cfg), 1, moe.WS_SWIGLU8)
+    call = lambda xq, e, expert, ws_bytes: L.moe_expert_swiglu_i8(
+        ctypes.byref(cfg), xq, a16, 1, e, expert, a16, None, None, None, None, a16, ws_bytes, None)
+    assert call(a16, None, 0, ws_need) == -1                     # no experts
+    assert call(a16, ctypes.byref(ex), 8, ws_need) == -1         # expert index out of range
+    assert call(a16 + 8, ctypes.byref(ex), 0, ws_need) == -3     # codes not 16-byte aligned
+    bad = moe.ExpertsI8(moe.Q8Mat(a16 + 4, a16, 0, 0), m, m)
+    assert call(a16, ctypes.byref(bad), 0, ws_need) == -3        # weight codes misaligned
+    odd = moe.ExpertsI8(m, moe.Q8Mat(a16, a16, 24, 0), m)
+    assert call(a16, ctypes.byref(odd), 0, ws_need) == -3        # stride not a multiple of 16
+    assert call(a16, ctypes.byref(ex), 0, ws_need - 16) == -4    # workspace too small

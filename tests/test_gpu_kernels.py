@@ -101,8 +101,8 @@ def test_router_topk(shape, S, bias):
 @pytest.mark.parametrize("S", [37, 301, 2048])
 def test_router_batch_invariance(S):
     # a token's routing does not depend on the batch it is in (37 tokens: the
-    # 8-token kernel; 301: the 8x8 register tiles with a ragged
-    # last tile; 2048: the prefill batch)
+    # 4x4 register tiles with a ragged last tile; 301: the 8x8 register tiles
+    # with a ragged last tile; 2048: the prefill batch)
     shape = GLM
     cfg = moe.config(shape.D, shape.I, shape.E, shape.K)
     wr = torch.from_numpy(synth.router_w(2, shape)).cuda()
