@@ -59,6 +59,9 @@ def lib():
         L.moe_ref_dot_i8_i8.argtypes = [vp, vp, i32]
         L.moe_ref_dot_i8_i8.restype = ctypes.c_int32
         L.moe_ref_expert_swiglu_i8.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        L.moe_ref_pack_int2.argtypes = [vp, i32, i32, vp, vp]
+        L.moe_ref_unpack_int2.argtypes = [vp, i32, i32, vp]
+        L.moe_ref_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_ref_layer_forward.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint]
         L.moe_ref_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, vp, vp]
         L.moe_ref_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp]
@@ -243,6 +246,62 @@ def expert_swiglu_i8(cfg: Config, xq: np.ndarray, sx: np.ndarray, e: HostExpertI
     _check(lib().moe_ref_expert_swiglu_i8(ctypes.byref(cfg), _p(xq), _p(sx), S, ctypes.byref(es),
                                           _p(y), _p(acc_gu), _p(hq), _p(sh), _p(acc_d)),
            "expert_swiglu_i8")
+    return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
+
+
+def pack_int2(w: np.ndarray):
+    """Packed int2 rows: (q2 [O][(C+3)/4] uint8, scale [O] float32)."""
+    w = _c(w, np.float32)
+    O, C = w.shape
+    q2 = np.empty((O, (C + 3) // 4), np.uint8)
+    s = np.empty(O, np.float32)
+    _check(lib().moe_ref_pack_int2(_p(w), O, C, _p(q2), _p(s)), "pack_int2")
+    return q2, s
+
+
+def unpack_int2(q2: np.ndarray, C: int) -> np.ndarray:
+    q2 = _c(q2, np.uint8)
+    O = q2.shape[0]
+    q = np.empty((O, C), np.int8)
+    _check(lib().moe_ref_unpack_int2(_p(q2), O, C, _p(q)), "unpack_int2")
+    return q
+
+
+@dataclass
+class HostExpertI2:
+    """Packed int2 expert on the host: gate/up [I][D/4], down [D][I/4]."""
+    gate_q2: np.ndarray
+    gate_s: np.ndarray
+    up_q2: np.ndarray
+    up_s: np.ndarray
+    down_q2: np.ndarray
+    down_s: np.ndarray
+
+    def cstruct(self) -> Expert:
+        return Expert(QMat(_p(self.gate_q2), _p(self.gate_s)), QMat(_p(self.up_q2), _p(self.up_s)),
+                      QMat(_p(self.down_q2), _p(self.down_s)))
+
+    @staticmethod
+    def from_f32(g, u, d) -> "HostExpertI2":
+        gq, gs = pack_int2(g)
+        uq, us = pack_int2(u)
+        dq, ds = pack_int2(d)
+        return HostExpertI2(gq, gs, uq, us, dq, ds)
+
+
+def expert_swiglu_i2(cfg: Config, xq: np.ndarray, sx: np.ndarray, e: HostExpertI2):
+    xq = _c(xq, np.int8)
+    sx = _c(sx, np.float32)
+    S = xq.shape[0]
+    y = np.empty((S, cfg.D), np.float32)
+    acc_gu = np.empty((S, 2, cfg.I), np.int32)
+    hq = np.empty((S, cfg.I), np.int8)
+    sh = np.empty(S, np.float32)
+    acc_d = np.empty((S, cfg.D), np.int32)
+    es = e.cstruct()
+    _check(lib().moe_ref_expert_swiglu_i2(ctypes.byref(cfg), _p(xq), _p(sx), S, ctypes.byref(es),
+                                          _p(y), _p(acc_gu), _p(hq), _p(sh), _p(acc_d)),
+           "expert_swiglu_i2")
     return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
 
 

@@ -311,6 +311,65 @@ int moe_ref_expert_swiglu_i8(const moe_ref_config *cfg, const int8_t *xq, const 
   return 0;
 }
 
+/* ---- packed int2 (reading: the int4 container's rule at 2 bits) --------- */
+
+int moe_ref_pack_int2(const float *w, int O, int C, uint8_t *q2, float *scale) {
+  if (!w || !q2 || !scale || O < 1 || C < 1) return -1;
+  int8_t *q = (int8_t *)malloc((size_t)O * C);
+  if (!q) return -2;
+  int rc = moe_ref_quantize_rows(w, O, C, 2, q, scale);
+  const int rb = (C + 3) / 4;
+  for (int o = 0; rc == 0 && o < O; o++)
+    for (int j = 0; j < rb; j++) {
+      unsigned b = 0;
+      for (int k = 0; k < 4; k++) {
+        const int c = 4 * j + k;
+        const int v = c < C ? q[(int64_t)o * C + c] : 0;
+        b |= (unsigned)(v + 2) << (2 * k);
+      }
+      q2[(int64_t)o * rb + j] = (uint8_t)b;
+    }
+  free(q);
+  return rc;
+}
+
+int moe_ref_unpack_int2(const uint8_t *q2, int O, int C, int8_t *q) {
+  if (!q2 || !q || O < 1 || C < 1) return -1;
+  const int rb = (C + 3) / 4;
+  for (int o = 0; o < O; o++)
+    for (int c = 0; c < C; c++) {
+      const uint8_t b = q2[(int64_t)o * rb + c / 4];
+      q[(int64_t)o * C + c] = (int8_t)(((b >> (2 * (c % 4))) & 3) - 2);
+    }
+  return 0;
+}
+
+static int widen_int2(const moe_ref_qmat *m, int O, int C, int8_t **out) {
+  *out = (int8_t *)malloc((size_t)O * C);
+  if (!*out) return -2;
+  return moe_ref_unpack_int2(m->q4, O, C, *out);
+}
+
+int moe_ref_expert_swiglu_i2(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
+                             const moe_ref_expert_i2 *e, float *y, int32_t *acc_gu, int8_t *hq,
+                             float *sh, int32_t *acc_d) {
+  if (bad_cfg(cfg) || !xq || !sx || !e || !y || S < 1) return -1;
+  if (!qmat_ok(&e->gate) || !qmat_ok(&e->up) || !qmat_ok(&e->down)) return -1;
+  const int D = cfg->D, I = cfg->I;
+  int8_t *g = NULL, *u = NULL, *d = NULL;
+  int rc = widen_int2(&e->gate, I, D, &g);
+  if (rc == 0) rc = widen_int2(&e->up, I, D, &u);
+  if (rc == 0) rc = widen_int2(&e->down, D, I, &d);
+  if (rc == 0) {
+    moe_ref_expert_i8 e8 = {{g, e->gate.scale}, {u, e->up.scale}, {d, e->down.scale}};
+    rc = moe_ref_expert_swiglu_i8(cfg, xq, sx, S, &e8, y, acc_gu, hq, sh, acc_d);
+  }
+  free(g);
+  free(u);
+  free(d);
+  return rc;
+}
+
 /* ---- the block ------------------------------------------------------------ */
 
 static int layer_ok(const moe_ref_config *cfg, const moe_ref_layer *L) {

@@ -11,7 +11,9 @@
  *   - section 04 (RMSNorm, SiLU, layer order),
  *   - section 05 (per-row absmax quantization to int8, the expert cache's
  *     int8 weight format),
- *   - section 06 (per-row int4 quantization and nibble packing),
+ *   - section 06 (per-row int4 quantization and nibble packing; the packed
+ *     int2 layout below is a reading of the same rule at 2 bits, parity with
+ *     the article unpinned),
  *   - section 11 (sigmoid router with correction bias, top-K, unique-expert
  *     union, SwiGLU expert, weighted scatter),
  *   - section 12 (per-row int8 activation quantization; integer dot products
@@ -131,6 +133,28 @@ typedef struct {
  * outputs and optional probes. */
 int moe_ref_expert_swiglu_i8(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
                              const moe_ref_expert_i8 *e, float *y, int32_t *acc_gu, int8_t *hq,
+                             float *sh, int32_t *acc_d);
+
+/* Packed int2 weights (the article's 2-bit format; its section 12 keeps an
+ * int2 path beside int8 and int4, and its summary lists packed int2 with
+ * per-row scales).  The article gives no int2 byte layout.  Reading, the
+ * int4 container's rule at 2 bits: codes from moe_ref_quantize_rows with
+ * bits = 2 (values in [-2, 1]), four per byte, each stored as q + 2, column
+ * 4j + k in bits 2k..2k+1 of byte j.  A row of C columns takes (C+3)/4
+ * bytes; missing columns of the last byte hold 2 (value 0). */
+int moe_ref_pack_int2(const float *w, int O, int C, uint8_t *q2, float *scale);
+int moe_ref_unpack_int2(const uint8_t *q2, int O, int C, int8_t *q);
+
+typedef struct {
+  moe_ref_qmat gate; /* q4 field holds the packed int2 rows: O = I, C = D */
+  moe_ref_qmat up;
+  moe_ref_qmat down; /* O = D, C = I */
+} moe_ref_expert_i2;
+
+/* moe_ref_expert_swiglu_i8 with packed int2 weight rows (each code unpacked,
+ * then the same integer path).  Same outputs and optional probes. */
+int moe_ref_expert_swiglu_i2(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
+                             const moe_ref_expert_i2 *e, float *y, int32_t *acc_gu, int8_t *hq,
                              float *sh, int32_t *acc_d);
 
 /* The block for S tokens, one token at a time: route, quantize the token,
