@@ -344,19 +344,20 @@ def bench_topp(layers, x, steps: int = 512, ps=(0.7, 0.9, 1.0)):
     return res
 
 
-EXPERT_I8_BYTES = 3 * I * D + (2 * I + D) * 4   # 37,789,696: int8 codes + row scales
+EXPERT_I8_BYTES = 3 * I * D + (2 * I + D) * 4       # 37,789,696: int8 codes + row scales
+EXPERT_I2_BYTES = 3 * I * D // 4 + (2 * I + D) * 4  # 9,478,144: packed int2 + row scales
 
 
-def bench_fmt8(layer, steps: int = 512, n8: int = 8, n4: int = 16):
-    """One GLM-shape SwiGLU expert on one token, int8 weight format against
-    the int4 one: each call reads one expert (cycling over 8 int8 or 16 int4
-    experts, about 302 MB either way, so the weights come from HBM rather
-    than the MALL); plain stream launches between events."""
+def bench_fmt8(layer, steps: int = 512, n8: int = 8, n4: int = 16, n2: int = 32):
+    """One GLM-shape SwiGLU expert on one token in the int8, int4 and packed
+    int2 weight formats: each call reads one expert (cycling over 8 int8, 16
+    int4 or 32 int2 experts, about 302 MB each, so the weights come from HBM
+    rather than the MALL); plain stream launches between events."""
     import torch
 
     import int4_expert_gemv_moe_amd as moe
     import synth
-    from synth.device_layers import build_device_experts_i8
+    from synth.device_layers import build_device_experts_i2, build_device_experts_i8
 
     lib = moe.lib()
     cfg = layer.cfg
@@ -367,16 +368,18 @@ def bench_fmt8(layer, steps: int = 512, n8: int = 8, n4: int = 16):
     y = torch.empty(1, D, dtype=torch.float32, device="cuda")
     ws8 = moe.Workspace(cfg, 1, moe.WS_SWIGLU8)
     ws4 = moe.Workspace(cfg, 1, moe.WS_SWIGLU)
-    s8, s4 = e8.cstruct(), layer.routed.cstruct()
+    e2 = build_device_experts_i2(0, synth.GLM, 0, n2)
+    s8, s4, s2 = e8.cstruct(), layer.routed.cstruct(), e2.cstruct()
     cref = ctypes.byref(cfg)
     args = (ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(sx.data_ptr()), 1)
     yp = ctypes.c_void_p(y.data_ptr())
     calls = {
         "int8": (lib.moe_expert_swiglu_i8, ctypes.byref(s8), n8, ws8, EXPERT_I8_BYTES),
         "int4": (lib.moe_expert_swiglu_i4, ctypes.byref(s4), n4, ws4, EXPERT_BYTES),
+        "int2": (lib.moe_expert_swiglu_i2, ctypes.byref(s2), n2, ws8, EXPERT_I2_BYTES),
     }
     res = {"workload": "one GLM-shape SwiGLU expert (6144 -> 2048 -> 6144), 1 token per call, "
-                       "int8 weight format against int4, weights cycled over ~302 MB",
+                       "int8 / int4 / packed int2 weight formats, weights cycled over ~302 MB",
            "steps": steps}
     for name, (fn, eref, n, ws, nbytes) in calls.items():
         def run(k):
@@ -681,7 +684,7 @@ def main():
         except Exception as exc:  # reported, the headline line is still printed
             secondary["topp_decode"] = {"error": f"{type(exc).__name__}: {exc}"}
         for key, fn in (("verify_64_zipf", bench_verify), ("prefill_2048", bench_prefill),
-                        ("tiered_decode", bench_tiered), ("expert_int8_format", bench_fmt8)):
+                        ("tiered_decode", bench_tiered), ("expert_weight_formats", bench_fmt8)):
             try:
                 secondary[key] = fn(layers[0])
             except Exception as exc:  # reported, the headline line is still printed

@@ -149,7 +149,7 @@ const char *moe_status_str(int status);
 
 /* Workspace bytes needed by a call with S tokens.  which: 0 = moe_layer_forward,
  * 1 = moe_layer_forward_batch, 2 = moe_expert_swiglu_i4, 3 = moe_router_topk,
- * 4 = moe_expert_swiglu_i8.
+ * 4 = moe_expert_swiglu_i8 and moe_expert_swiglu_i2.
  * Returns 0 for invalid arguments. */
 size_t moe_workspace_bytes(const moe_config *cfg, int S, int which);
 
@@ -205,6 +205,27 @@ int moe_expert_swiglu_i8(const moe_config *cfg, const int8_t *xq, const float *s
                          const moe_experts_i8 *w, int expert, float *y, int32_t *acc_gu,
                          int8_t *hq, float *sh, int32_t *acc_d, void *ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/* Packed int2 weights (section 12 keeps a 2-bit integer path beside int8
+ * and int4; the summaries list packed int2 with per-row scales).  The
+ * article gives no int2 byte layout; this library carries the section 06
+ * int4 rule to 2 bits: per row s = max(amax, 1e-8) (amax/qmax, qmax = 1),
+ * q = clamp(rint(w/s), -2, 1), four codes per byte, each stored as q + 2,
+ * column 4j + k in bits 2k..2k+1 of byte j; a row of C columns takes
+ * (C+3)/4 bytes, missing columns of its last byte hold 2 (value 0).
+ * moe_pack_int2 converts w[O][C] (float32) to q2[O][(C+3)/4] and scale[O];
+ * any C >= 1; w and scale 4-byte aligned. */
+int moe_pack_int2(const float *w, int O, int C, uint8_t *q2, float *scale, hipStream_t stream);
+
+/* moe_expert_swiglu_i8 for an expert in the packed int2 format: *w (host
+ * struct) holds packed int2 rows in the q4 fields (gate/up [I][D/4], down
+ * [D][I/4]; a stride of 0 means densely stacked, O*C/4 bytes per expert).
+ * Needs I % 64 == 0 (MOE_ESHAPE otherwise).  Same arithmetic after the codes
+ * are unpacked, same outputs and probes.  Workspace:
+ * moe_workspace_bytes(cfg, S, 4). */
+int moe_expert_swiglu_i2(const moe_config *cfg, const int8_t *xq, const float *sx, int S,
+                         const moe_experts *w, int expert, float *y, int32_t *acc_gu, int8_t *hq,
+                         float *sh, int32_t *acc_d, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The block, one token at a time (each token reads its own K experts):
  * route, quantize, run the K routed experts and the shared expert, and

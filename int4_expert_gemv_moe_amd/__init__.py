@@ -77,6 +77,8 @@ def lib():
         L.moe_expert_swiglu_i4.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_quantize_rows_i8.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_expert_swiglu_i8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_pack_int2.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp, vp]
@@ -102,6 +104,7 @@ def lib():
         L.moe_stream_read_sink_words.argtypes = []
         for name in ("moe_workspace_init", "moe_pack_int4", "moe_quant_act_i8", "moe_router_topk",
                      "moe_expert_swiglu_i4", "moe_quantize_rows_i8", "moe_expert_swiglu_i8",
+                     "moe_pack_int2", "moe_expert_swiglu_i2",
                      "moe_layer_forward", "moe_layer_forward_batch",
                      "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
                      "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
@@ -351,6 +354,67 @@ def moe_expert_swiglu_i8(cfg: Config, xq: torch.Tensor, sx: torch.Tensor, expert
                                       expert, _ptr(y), _ptr(acc_gu), _ptr(hq), _ptr(sh), _ptr(acc_d),
                                       ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
            "moe_expert_swiglu_i8")
+    return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
+
+
+@dataclass
+class DeviceExpertsI2:
+    """Stacked packed-int2 experts on the device: gate/up [n][I][D/4], scales
+    [n][I]; down [n][D][I/4], scales [n][D]."""
+    gate_q2: torch.Tensor
+    gate_s: torch.Tensor
+    up_q2: torch.Tensor
+    up_s: torch.Tensor
+    down_q2: torch.Tensor
+    down_s: torch.Tensor
+
+    @staticmethod
+    def empty(n: int, D: int, I: int, device="cuda") -> "DeviceExpertsI2":
+        u8, f32 = torch.uint8, torch.float32
+        return DeviceExpertsI2(torch.empty(n, I, D // 4, dtype=u8, device=device),
+                               torch.empty(n, I, dtype=f32, device=device),
+                               torch.empty(n, I, D // 4, dtype=u8, device=device),
+                               torch.empty(n, I, dtype=f32, device=device),
+                               torch.empty(n, D, I // 4, dtype=u8, device=device),
+                               torch.empty(n, D, dtype=f32, device=device))
+
+    def cstruct(self) -> Experts:
+        def q(a, b):
+            return QMat(a.data_ptr(), b.data_ptr(), 0, 0)
+        return Experts(q(self.gate_q2, self.gate_s), q(self.up_q2, self.up_s),
+                       q(self.down_q2, self.down_s))
+
+
+def moe_pack_int2(w: torch.Tensor, q2: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                  stream=None):
+    """Packed int2 on the device: w [O][C] float32 -> (q2 [O][(C+3)/4], scale [O])."""
+    _dev(w, torch.float32, "w")
+    O, C = w.shape
+    q2 = torch.empty(O, (C + 3) // 4, dtype=torch.uint8, device=w.device) if q2 is None else q2
+    scale = torch.empty(O, dtype=torch.float32, device=w.device) if scale is None else scale
+    _check(lib().moe_pack_int2(_ptr(w), O, C, _ptr(q2), _ptr(scale), ctypes.c_void_p(_stream(stream))),
+           "moe_pack_int2")
+    return q2, scale
+
+
+def moe_expert_swiglu_i2(cfg: Config, xq: torch.Tensor, sx: torch.Tensor, experts: DeviceExpertsI2,
+                         expert: int, ws: Workspace, probes: bool = False, stream=None):
+    _dev(xq, torch.int8, "xq")
+    _dev(sx, torch.float32, "sx")
+    S = xq.shape[0]
+    dev = xq.device
+    y = torch.empty(S, cfg.D, dtype=torch.float32, device=dev)
+    acc_gu = hq = sh = acc_d = None
+    if probes:
+        acc_gu = torch.empty(S, 2, cfg.I, dtype=torch.int32, device=dev)
+        hq = torch.empty(S, cfg.I, dtype=torch.int8, device=dev)
+        sh = torch.empty(S, dtype=torch.float32, device=dev)
+        acc_d = torch.empty(S, cfg.D, dtype=torch.int32, device=dev)
+    es = experts.cstruct()
+    _check(lib().moe_expert_swiglu_i2(ctypes.byref(cfg), _ptr(xq), _ptr(sx), S, ctypes.byref(es),
+                                      expert, _ptr(y), _ptr(acc_gu), _ptr(hq), _ptr(sh), _ptr(acc_d),
+                                      ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
+           "moe_expert_swiglu_i2")
     return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
 
 

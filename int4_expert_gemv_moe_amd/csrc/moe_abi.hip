@@ -375,6 +375,59 @@ int moe_expert_swiglu_i8(const moe_config *cfg, const int8_t *xq, const float *s
   return MOE_OK;
 }
 
+int moe_pack_int2(const float *w, int O, int C, uint8_t *q2, float *scale, hipStream_t stream) {
+  if (!w || !q2 || !scale) return MOE_EINVAL;
+  if (O < 1 || C < 1) return MOE_ESHAPE;
+  if (((uintptr_t)w & 3u) || ((uintptr_t)scale & 3u)) return MOE_EALIGN;
+  MOE_TRY(check_device());
+  Pack2Args a{w, O, C, q2, scale};
+  return hip_rc(launch_pack_int2(a, stream));
+}
+
+int moe_expert_swiglu_i2(const moe_config *cfg, const int8_t *xq, const float *sx, int S,
+                         const moe_experts *wts, int expert, float *y, int32_t *acc_gu,
+                         int8_t *hq, float *sh, int32_t *acc_d, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->I % 64) return MOE_ESHAPE;
+  if (S < 1 || !xq || !sx || !wts || !y || !ws) return MOE_EINVAL;
+  if (expert < 0 || expert >= cfg->E) return MOE_EINVAL;
+  MOE_TRY(check_experts(*wts));
+  if (!aligned16(xq) || ((uintptr_t)sx & 3u) || ((uintptr_t)y & 3u) || ((uintptr_t)ws & 255u))
+    return MOE_EALIGN;
+  if ((hq && !aligned16(hq)) || ((uintptr_t)sh & 3u) || ((uintptr_t)acc_gu & 3u) ||
+      ((uintptr_t)acc_d & 3u))
+    return MOE_EALIGN;
+  if (ws_bytes < carve(*cfg, S, W_SWIGLU8, nullptr, nullptr)) return MOE_EWORKSPACE;
+  MOE_TRY(check_device());
+  Work w;
+  carve(*cfg, S, W_SWIGLU8, (char *)ws, &w);
+  auto rows = [&](const moe_qmat &m, int O, int C, const uint8_t **q, const float **sc) {
+    const int64_t qs = m.q4_stride ? m.q4_stride : (int64_t)O * (C / 4);
+    const int64_t ss = m.scale_stride ? m.scale_stride : (int64_t)O;
+    *q = m.q4 + (int64_t)expert * qs;
+    *sc = m.scale + (int64_t)expert * ss;
+  };
+  Swiglu2Args a{};
+  a.xq = xq;
+  a.sx = sx;
+  a.S = S;
+  a.D = cfg->D;
+  a.I = cfg->I;
+  rows(wts->gate, cfg->I, cfg->D, &a.G, &a.gs);
+  rows(wts->up, cfg->I, cfg->D, &a.U, &a.us);
+  rows(wts->down, cfg->D, cfg->I, &a.Dn, &a.ds);
+  a.h = w.h;
+  a.acc_gu = acc_gu;
+  a.hq_out = hq;
+  a.sh_out = sh;
+  a.y = y;
+  a.acc_d = acc_d;
+  MOE_TRY_HIP(launch_swiglu2_gateup(a, stream));
+  MOE_TRY_HIP(launch_swiglu2_down(a, stream));
+  return MOE_OK;
+}
+
 int moe_quant_act_i8(const void *x, moe_dtype dtype, int S, int D, int8_t *xq, float *sx,
                      hipStream_t stream) {
   if (!x || !xq || !sx) return MOE_EINVAL;

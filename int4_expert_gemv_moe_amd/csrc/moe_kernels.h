@@ -203,6 +203,35 @@ struct Swiglu8Args {
   int32_t *acc_d;          // optional [S][D]
 };
 
+// Packed int2 weights (fmt2.hip): four codes per byte, code + 2, column
+// 4j + k in bits 2k..2k+1 of byte j.
+struct Pack2Args {
+  const float *w;  // [O][C]
+  int O, C;
+  uint8_t *q2;     // [O][(C+3)/4]
+  float *scale;    // [O]
+};
+
+struct Swiglu2Args {
+  const int8_t *xq;        // [S][D] natural-order activation codes
+  const float *sx;         // [S]
+  int S, D, I;
+  const uint8_t *G, *U;    // [I][D/4] this expert's packed gate and up rows
+  const uint8_t *Dn;       // [D][I/4] packed down rows
+  const float *gs, *us;    // [I]
+  const float *ds;         // [D]
+  float *h;                // [S][I]
+  int32_t *acc_gu;         // optional [S][2][I]
+  int8_t *hq_out;          // optional [S][I]
+  float *sh_out;           // optional [S]
+  float *y;                // [S][D]
+  int32_t *acc_d;          // optional [S][D]
+};
+
+hipError_t launch_pack_int2(const Pack2Args &a, hipStream_t st);
+hipError_t launch_swiglu2_gateup(const Swiglu2Args &a, hipStream_t st);
+hipError_t launch_swiglu2_down(const Swiglu2Args &a, hipStream_t st);
+
 hipError_t launch_quant_rows_i8(const Q8QuantArgs &a, hipStream_t st);
 hipError_t launch_swiglu8_gateup(const Swiglu8Args &a, hipStream_t st);
 hipError_t launch_swiglu8_down(const Swiglu8Args &a, hipStream_t st);

@@ -63,3 +63,22 @@ def build_device_experts_i8(seed: int, shape: synth.Shape, layer: int, n: int,
             moe.moe_quantize_rows_i8(tmp[: O * C].view(O, C), q[e], sc[e])
     del tmp
     return out
+
+
+def build_device_experts_i2(seed: int, shape: synth.Shape, layer: int, n: int,
+                            device: str = "cuda") -> moe.DeviceExpertsI2:
+    """n experts of the shape in the packed int2 format (moe_pack_int2), drawn
+    from the same streams as experts 0..n-1 of the layer."""
+    D, I = shape.D, shape.I
+    st = torch.cuda.current_stream().cuda_stream
+    out = moe.DeviceExpertsI2.empty(n, D, I, device)
+    tmp = torch.empty(I * D, dtype=torch.float32, device=device)
+    for e in range(n):
+        sg, su, sd = synth.expert_streams(layer, e)
+        for strm, q, sc, O, C in ((sg, out.gate_q2, out.gate_s, I, D),
+                                  (su, out.up_q2, out.up_s, I, D),
+                                  (sd, out.down_q2, out.down_s, D, I)):
+            synth.dev_fill_normal(tmp.data_ptr(), seed, strm, O * C, synth.WEIGHT_SIGMA, st)
+            moe.moe_pack_int2(tmp[: O * C].view(O, C), q[e], sc[e])
+    del tmp
+    return out

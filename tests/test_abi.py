@@ -177,3 +177,24 @@ def test_int8_format_host_checks():
     odd = moe.ExpertsI8(m, moe.Q8Mat(a16, a16, 24, 0), m)
     assert call(a16, ctypes.byref(odd), 0, ws_need) == -3        # stride not a multiple of 16
     assert call(a16, ctypes.byref(ex), 0, ws_need - 16) == -4    # workspace too small
+
+
+def test_int2_format_host_checks():
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    buf = ctypes.create_string_buffer(512)
+    a16 = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 256
+    assert L.moe_pack_int2(None, 4, 8, a16, a16, None) == -1
+    assert L.moe_pack_int2(a16, 4, 0, a16, a16, None) == -2
+    assert L.moe_pack_int2(a16 + 1, 4, 8, a16, a16, None) == -3
+    m = moe.QMat(a16, a16, 0, 0)
+    ex = moe.Experts(m, m, m)
+    cfg = moe.config(256, 128, 8, 2)
+    need = L.moe_workspace_bytes(ctypes.byref(cfg), 1, moe.WS_SWIGLU8)
+    call = lambda c, xq, expert, ws_bytes: L.moe_expert_swiglu_i2(
+        ctypes.byref(c), xq, a16, 1, ctypes.byref(ex), expert, a16, None, None, None, None, a16,
+        ws_bytes, None)
+    assert call(moe.config(256, 96, 8, 2), a16, 0, need) == -2   # I % 64
+    assert call(cfg, a16, -1, need) == -1                        # expert index
+    assert call(cfg, a16 + 4, 0, need) == -3                     # activation codes misaligned
+    assert call(cfg, a16, 0, need - 16) == -4                    # workspace too small
