@@ -60,6 +60,8 @@ def lib():
         L.moe_ref_dot_i8_i8.restype = ctypes.c_int32
         L.moe_ref_expert_swiglu_i8.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_ref_pack_int2.argtypes = [vp, i32, i32, vp, vp]
+        L.moe_ref_quant_act_b32.argtypes = [vp, i32, i32, vp, vp]
+        L.moe_ref_expert_swiglu_i4_b32.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp]
         L.moe_ref_unpack_int2.argtypes = [vp, i32, i32, vp]
         L.moe_ref_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_ref_layer_forward.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint]
@@ -303,6 +305,30 @@ def expert_swiglu_i2(cfg: Config, xq: np.ndarray, sx: np.ndarray, e: HostExpertI
                                           _p(y), _p(acc_gu), _p(hq), _p(sh), _p(acc_d)),
            "expert_swiglu_i2")
     return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
+
+
+def quant_act_b32(x: np.ndarray):
+    """Block-32 activation quantization: (xq [S][D] int8, sxb [S][D/32] float32)."""
+    x = _c(x, np.float32)
+    S, D = x.shape
+    xq = np.empty((S, D), np.int8)
+    sxb = np.empty((S, D // 32), np.float32)
+    _check(lib().moe_ref_quant_act_b32(_p(x), S, D, _p(xq), _p(sxb)), "quant_act_b32")
+    return xq, sxb
+
+
+def expert_swiglu_b32(cfg: Config, xq: np.ndarray, sxb: np.ndarray, e: HostExpert):
+    xq = _c(xq, np.int8)
+    sxb = _c(sxb, np.float32)
+    S = xq.shape[0]
+    y = np.empty((S, cfg.D), np.float32)
+    hq = np.empty((S, cfg.I), np.int8)
+    shb = np.empty((S, cfg.I // 32), np.float32)
+    es = e.cstruct()
+    _check(lib().moe_ref_expert_swiglu_i4_b32(ctypes.byref(cfg), _p(xq), _p(sxb), S,
+                                              ctypes.byref(es), _p(y), _p(hq), _p(shb)),
+           "expert_swiglu_i4_b32")
+    return dict(y=y, hq=hq, shb=shb)
 
 
 class HostLayer:

@@ -370,6 +370,62 @@ int moe_ref_expert_swiglu_i2(const moe_ref_config *cfg, const int8_t *xq, const 
   return rc;
 }
 
+/* ---- block-32 activation scales (reading of the "Q8_0 style" remark) ---- */
+
+int moe_ref_quant_act_b32(const float *x, int S, int D, int8_t *xq, float *sxb) {
+  if (!x || !xq || !sxb || S < 1 || D < 32 || D % 32) return -1;
+  const int nb = D / 32;
+  for (int s = 0; s < S; s++)
+    for (int b = 0; b < nb; b++) {
+      const int64_t off = (int64_t)s * D + 32 * b;
+      sxb[(int64_t)s * nb + b] = moe_ref_quant_row_i8(x + off, 32, xq + off);
+    }
+  return 0;
+}
+
+/* s_w * sum_b acc_b * s_b for one packed int4 row against block-quantized q. */
+static float dot_b32(const uint8_t *q4row, const int8_t *q, const float *sb, int C, float sw) {
+  double t = 0.0;
+  for (int b = 0; b < C / 32; b++) {
+    int32_t acc = 0;
+    for (int c = 32 * b; c < 32 * b + 32; c++) acc += nibble_value(q4row, c) * (int32_t)q[c];
+    t += (double)acc * (double)sb[b];
+  }
+  return (float)(t * (double)sw);
+}
+
+int moe_ref_expert_swiglu_i4_b32(const moe_ref_config *cfg, const int8_t *xq, const float *sxb,
+                                 int S, const moe_ref_expert *e, float *y, int8_t *hq,
+                                 float *shb) {
+  if (bad_cfg(cfg) || !xq || !sxb || !e || !y || S < 1) return -1;
+  if (!qmat_ok(&e->gate) || !qmat_ok(&e->up) || !qmat_ok(&e->down)) return -1;
+  const int D = cfg->D, I = cfg->I;
+  if (D % 32 || I % 32) return -1;
+  const int rbD = D / 2, rbI = I / 2;
+  float *h = (float *)malloc((size_t)I * sizeof(float));
+  int8_t *hqr = (int8_t *)malloc((size_t)I);
+  float *hs = (float *)malloc((size_t)(I / 32) * sizeof(float));
+  if (!h || !hqr || !hs) { free(h); free(hqr); free(hs); return -2; }
+  for (int s = 0; s < S; s++) {
+    const int8_t *xs = xq + (int64_t)s * D;
+    const float *sb = sxb + (int64_t)s * (D / 32);
+    for (int o = 0; o < I; o++) {
+      const float g = dot_b32(e->gate.q4 + (int64_t)o * rbD, xs, sb, D, e->gate.scale[o]);
+      const float u = dot_b32(e->up.q4 + (int64_t)o * rbD, xs, sb, D, e->up.scale[o]);
+      h[o] = silu_ref(g) * u;
+    }
+    moe_ref_quant_act_b32(h, 1, I, hqr, hs);
+    if (hq) memcpy(hq + (int64_t)s * I, hqr, (size_t)I);
+    if (shb) memcpy(shb + (int64_t)s * (I / 32), hs, (size_t)(I / 32) * sizeof(float));
+    for (int d = 0; d < D; d++)
+      y[(int64_t)s * D + d] = dot_b32(e->down.q4 + (int64_t)d * rbI, hqr, hs, I, e->down.scale[d]);
+  }
+  free(h);
+  free(hqr);
+  free(hs);
+  return 0;
+}
+
 /* ---- the block ------------------------------------------------------------ */
 
 static int layer_ok(const moe_ref_config *cfg, const moe_ref_layer *L) {

@@ -16,6 +16,8 @@
  *     the article unpinned),
  *   - section 11 (sigmoid router with correction bias, top-K, unique-expert
  *     union, SwiGLU expert, weighted scatter),
+ *   - the summaries' "Q8_0 style" activation remark (block-32 scales below,
+ *     a reading; parity with the article unpinned),
  *   - section 12 (per-row int8 activation quantization; integer dot products
  *     scaled by the weight and activation scales; activations are quantized in
  *     front of every integer matmul).
@@ -156,6 +158,23 @@ typedef struct {
 int moe_ref_expert_swiglu_i2(const moe_ref_config *cfg, const int8_t *xq, const float *sx, int S,
                              const moe_ref_expert_i2 *e, float *y, int32_t *acc_gu, int8_t *hq,
                              float *sh, int32_t *acc_d);
+
+/* Block-32 activation scales (the summaries call the activation format
+ * "Q8_0 style", a format with one scale per 32 values; the section 12 listing
+ * itself scales whole rows).  Reading: each run of 32 values of a row is
+ * quantized like a section 12 row, s = max(amax/127, 1e-12),
+ * q = lrint(x * (1/s)).  D % 32 == 0.  Outputs xq[S][D], sxb[S][D/32]. */
+int moe_ref_quant_act_b32(const float *x, int S, int D, int8_t *xq, float *sxb);
+
+/* One int4 SwiGLU expert on block-32 quantized rows: for each output row,
+ * acc_b = sum over block b of q_w * q_x (exact int32), the matmul value is
+ * s_w * sum_b acc_b * s_b (in double, rounded once to float); h = silu(g) * u
+ * in float; h is requantized in blocks of 32 the same way (hq[S][I],
+ * shb[S][I/32], both optional outputs) and the down projection is formed the
+ * same way.  y[S][D] is the unweighted expert output. */
+int moe_ref_expert_swiglu_i4_b32(const moe_ref_config *cfg, const int8_t *xq, const float *sxb,
+                                 int S, const moe_ref_expert *e, float *y, int8_t *hq,
+                                 float *shb);
 
 /* The block for S tokens, one token at a time: route, quantize the token,
  * run its K experts and the shared expert, and combine
