@@ -370,22 +370,33 @@ def bench_fmt8(layer, steps: int = 512, n8: int = 8, n4: int = 16, n2: int = 32)
     ws4 = moe.Workspace(cfg, 1, moe.WS_SWIGLU)
     e2 = build_device_experts_i2(0, synth.GLM, 0, n2)
     s8, s4, s2 = e8.cstruct(), layer.routed.cstruct(), e2.cstruct()
+    xqb, sxb = moe.moe_quant_act_b32(torch.from_numpy(synth.activations(7, 1, D)).cuda())
     cref = ctypes.byref(cfg)
     args = (ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(sx.data_ptr()), 1)
+    args_b = (ctypes.c_void_p(xqb.data_ptr()), ctypes.c_void_p(sxb.data_ptr()), 1)
     yp = ctypes.c_void_p(y.data_ptr())
+    r8, r4, r2 = ctypes.byref(s8), ctypes.byref(s4), ctypes.byref(s2)
+    nul4 = (None, None, None, None)
+
+    def call(fn, a, eref, tail, ws):
+        return lambda e: fn(cref, *a, eref, e, yp, *tail, ws.ptr, ws.nbytes, st)
+
     calls = {
-        "int8": (lib.moe_expert_swiglu_i8, ctypes.byref(s8), n8, ws8, EXPERT_I8_BYTES),
-        "int4": (lib.moe_expert_swiglu_i4, ctypes.byref(s4), n4, ws4, EXPERT_BYTES),
-        "int2": (lib.moe_expert_swiglu_i2, ctypes.byref(s2), n2, ws8, EXPERT_I2_BYTES),
+        "int8": (call(lib.moe_expert_swiglu_i8, args, r8, nul4, ws8), n8, EXPERT_I8_BYTES),
+        "int4": (call(lib.moe_expert_swiglu_i4, args, r4, nul4, ws4), n4, EXPERT_BYTES),
+        "int2": (call(lib.moe_expert_swiglu_i2, args, r2, nul4, ws8), n2, EXPERT_I2_BYTES),
+        "int4_block32_act": (call(lib.moe_expert_swiglu_i4_b32, args_b, r4, (None, None), ws8), n4,
+                             EXPERT_BYTES),
     }
     res = {"workload": "one GLM-shape SwiGLU expert (6144 -> 2048 -> 6144), 1 token per call, "
-                       "int8 / int4 / packed int2 weight formats, weights cycled over ~302 MB",
+                       "int8 / int4 / packed int2 weights and int4 with block-32 activation "
+                       "scales, weights cycled over ~302 MB",
            "steps": steps}
-    for name, (fn, eref, n, ws, nbytes) in calls.items():
+    for name, (fn, n, nbytes) in calls.items():
         def run(k):
             rc = 0
             for i in range(k):
-                rc |= fn(cref, *args, eref, i % n, yp, None, None, None, None, ws.ptr, ws.nbytes, st)
+                rc |= fn(i % n)
             if rc:
                 raise moe.MoeError(f"{name} expert call failed ({rc})")
 

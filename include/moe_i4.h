@@ -149,7 +149,7 @@ const char *moe_status_str(int status);
 
 /* Workspace bytes needed by a call with S tokens.  which: 0 = moe_layer_forward,
  * 1 = moe_layer_forward_batch, 2 = moe_expert_swiglu_i4, 3 = moe_router_topk,
- * 4 = moe_expert_swiglu_i8 and moe_expert_swiglu_i2.
+ * 4 = moe_expert_swiglu_i8, moe_expert_swiglu_i2 and moe_expert_swiglu_i4_b32.
  * Returns 0 for invalid arguments. */
 size_t moe_workspace_bytes(const moe_config *cfg, int S, int which);
 
@@ -226,6 +226,25 @@ int moe_pack_int2(const float *w, int O, int C, uint8_t *q2, float *scale, hipSt
 int moe_expert_swiglu_i2(const moe_config *cfg, const int8_t *xq, const float *sx, int S,
                          const moe_experts *w, int expert, float *y, int32_t *acc_gu, int8_t *hq,
                          float *sh, int32_t *acc_d, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Block-32 activation scales (the summaries call the activation format
+ * "Q8_0 style", one scale per 32 values; the section 12 listing scales whole
+ * rows).  moe_quant_act_b32 quantizes every run of 32 values of x[S][D]
+ * (float32) like a section 12 row: s = max(amax/127, 1e-12),
+ * q = rint(x * (1/s)).  Outputs xq[S][D] (natural order) and sxb[S][D/32].
+ * D % 32 == 0; x and xq 16-byte aligned. */
+int moe_quant_act_b32(const float *x, int S, int D, int8_t *xq, float *sxb, hipStream_t stream);
+
+/* One int4 SwiGLU expert (packed as in moe_expert_swiglu_i4) on block-32
+ * quantized rows xq[S][D], sxb[S][D/32]: each gate/up/down output is
+ * s_w * sum_b acc_b * s_b over the blocks b of its row, acc_b the exact int32
+ * sum of block b, the block terms added in float; h = silu(g) * u is
+ * requantized in blocks of 32 the same way before the down projection.
+ * Outputs y[S][D] (unweighted); optional hq[S][I] (natural order, 16-byte
+ * aligned) and shb[S][I/32].  Workspace: moe_workspace_bytes(cfg, S, 4). */
+int moe_expert_swiglu_i4_b32(const moe_config *cfg, const int8_t *xq, const float *sxb, int S,
+                             const moe_experts *w, int expert, float *y, int8_t *hq, float *shb,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The block, one token at a time (each token reads its own K experts):
  * route, quantize, run the K routed experts and the shared expert, and

@@ -78,6 +78,8 @@ def lib():
         L.moe_quantize_rows_i8.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_expert_swiglu_i8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_pack_int2.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_quant_act_b32.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_expert_swiglu_i4_b32.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
@@ -104,7 +106,8 @@ def lib():
         L.moe_stream_read_sink_words.argtypes = []
         for name in ("moe_workspace_init", "moe_pack_int4", "moe_quant_act_i8", "moe_router_topk",
                      "moe_expert_swiglu_i4", "moe_quantize_rows_i8", "moe_expert_swiglu_i8",
-                     "moe_pack_int2", "moe_expert_swiglu_i2",
+                     "moe_pack_int2", "moe_expert_swiglu_i2", "moe_quant_act_b32",
+                     "moe_expert_swiglu_i4_b32",
                      "moe_layer_forward", "moe_layer_forward_batch",
                      "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
                      "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
@@ -416,6 +419,37 @@ def moe_expert_swiglu_i2(cfg: Config, xq: torch.Tensor, sx: torch.Tensor, expert
                                       ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
            "moe_expert_swiglu_i2")
     return dict(y=y, acc_gu=acc_gu, hq=hq, sh=sh, acc_d=acc_d)
+
+
+def moe_quant_act_b32(x: torch.Tensor, stream=None):
+    """Block-32 activation quantization of x [S][D] float32: (xq [S][D], sxb [S][D/32])."""
+    _dev(x, torch.float32, "x")
+    S, D = x.shape
+    xq = torch.empty(S, D, dtype=torch.int8, device=x.device)
+    sxb = torch.empty(S, D // 32, dtype=torch.float32, device=x.device)
+    _check(lib().moe_quant_act_b32(_ptr(x), S, D, _ptr(xq), _ptr(sxb),
+                                   ctypes.c_void_p(_stream(stream))), "moe_quant_act_b32")
+    return xq, sxb
+
+
+def moe_expert_swiglu_i4_b32(cfg: Config, xq: torch.Tensor, sxb: torch.Tensor,
+                             experts: DeviceExperts, expert: int, ws: Workspace, probes: bool = False,
+                             stream=None):
+    _dev(xq, torch.int8, "xq")
+    _dev(sxb, torch.float32, "sxb")
+    S = xq.shape[0]
+    dev = xq.device
+    y = torch.empty(S, cfg.D, dtype=torch.float32, device=dev)
+    hq = shb = None
+    if probes:
+        hq = torch.empty(S, cfg.I, dtype=torch.int8, device=dev)
+        shb = torch.empty(S, cfg.I // 32, dtype=torch.float32, device=dev)
+    es = experts.cstruct()
+    _check(lib().moe_expert_swiglu_i4_b32(ctypes.byref(cfg), _ptr(xq), _ptr(sxb), S,
+                                          ctypes.byref(es), expert, _ptr(y), _ptr(hq), _ptr(shb),
+                                          ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
+           "moe_expert_swiglu_i4_b32")
+    return dict(y=y, hq=hq, shb=shb)
 
 
 def _probe(topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None, keff=None):

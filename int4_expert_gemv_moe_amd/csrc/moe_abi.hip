@@ -428,6 +428,51 @@ int moe_expert_swiglu_i2(const moe_config *cfg, const int8_t *xq, const float *s
   return MOE_OK;
 }
 
+int moe_quant_act_b32(const float *x, int S, int D, int8_t *xq, float *sxb, hipStream_t stream) {
+  if (!x || !xq || !sxb) return MOE_EINVAL;
+  if (S < 1 || D < 32 || (D & 31)) return MOE_ESHAPE;
+  if (!aligned16(x) || !aligned16(xq) || ((uintptr_t)sxb & 3u)) return MOE_EALIGN;
+  MOE_TRY(check_device());
+  QuantB32Args a{x, S, D, xq, sxb};
+  return hip_rc(launch_quant_b32(a, stream));
+}
+
+int moe_expert_swiglu_i4_b32(const moe_config *cfg, const int8_t *xq, const float *sxb, int S,
+                             const moe_experts *wts, int expert, float *y, int8_t *hq, float *shb,
+                             void *ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (S < 1 || !xq || !sxb || !wts || !y || !ws) return MOE_EINVAL;
+  if (expert < 0 || expert >= cfg->E) return MOE_EINVAL;
+  MOE_TRY(check_experts(*wts));
+  if (!aligned16(xq) || ((uintptr_t)sxb & 3u) || ((uintptr_t)y & 3u) || ((uintptr_t)ws & 255u))
+    return MOE_EALIGN;
+  if ((hq && !aligned16(hq)) || ((uintptr_t)shb & 3u)) return MOE_EALIGN;
+  if (ws_bytes < carve(*cfg, S, W_SWIGLU8, nullptr, nullptr)) return MOE_EWORKSPACE;
+  MOE_TRY(check_device());
+  Work w;
+  carve(*cfg, S, W_SWIGLU8, (char *)ws, &w);
+  const ExpertSet es = to_set(*wts, *cfg);
+  SwigluB32Args a{};
+  a.xq = xq;
+  a.sxb = sxb;
+  a.S = S;
+  a.D = cfg->D;
+  a.I = cfg->I;
+  a.G = es.gate.q4 + (int64_t)expert * es.gate.q4_stride;
+  a.U = es.up.q4 + (int64_t)expert * es.up.q4_stride;
+  a.Dn = es.down.q4 + (int64_t)expert * es.down.q4_stride;
+  a.gs = es.gate.scale + (int64_t)expert * es.gate.s_stride;
+  a.us = es.up.scale + (int64_t)expert * es.up.s_stride;
+  a.ds = es.down.scale + (int64_t)expert * es.down.s_stride;
+  a.h = w.h;
+  a.hq_out = hq;
+  a.shb_out = shb;
+  a.y = y;
+  MOE_TRY_HIP(launch_swiglu_b32_gateup(a, stream));
+  MOE_TRY_HIP(launch_swiglu_b32_down(a, stream));
+  return MOE_OK;
+}
+
 int moe_quant_act_i8(const void *x, moe_dtype dtype, int S, int D, int8_t *xq, float *sx,
                      hipStream_t stream) {
   if (!x || !xq || !sx) return MOE_EINVAL;

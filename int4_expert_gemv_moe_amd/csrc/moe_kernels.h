@@ -228,6 +228,32 @@ struct Swiglu2Args {
   int32_t *acc_d;          // optional [S][D]
 };
 
+// Block-32 activation scales (b32.hip).
+struct QuantB32Args {
+  const float *x;  // [S][D]
+  int S, D;
+  int8_t *xq;      // [S][D] natural order
+  float *sxb;      // [S][D/32]
+};
+
+struct SwigluB32Args {
+  const int8_t *xq;        // [S][D] natural-order codes
+  const float *sxb;        // [S][D/32]
+  int S, D, I;
+  const uint8_t *G, *U;    // [I][D/2] this expert's packed int4 gate and up rows
+  const uint8_t *Dn;       // [D][I/2]
+  const float *gs, *us;    // [I]
+  const float *ds;         // [D]
+  float *h;                // [S][I]
+  int8_t *hq_out;          // optional [S][I] natural order
+  float *shb_out;          // optional [S][I/32]
+  float *y;                // [S][D]
+};
+
+hipError_t launch_quant_b32(const QuantB32Args &a, hipStream_t st);
+hipError_t launch_swiglu_b32_gateup(const SwigluB32Args &a, hipStream_t st);
+hipError_t launch_swiglu_b32_down(const SwigluB32Args &a, hipStream_t st);
+
 hipError_t launch_pack_int2(const Pack2Args &a, hipStream_t st);
 hipError_t launch_swiglu2_gateup(const Swiglu2Args &a, hipStream_t st);
 hipError_t launch_swiglu2_down(const Swiglu2Args &a, hipStream_t st);

@@ -198,3 +198,23 @@ def test_int2_format_host_checks():
     assert call(cfg, a16, -1, need) == -1                        # expert index
     assert call(cfg, a16 + 4, 0, need) == -3                     # activation codes misaligned
     assert call(cfg, a16, 0, need - 16) == -4                    # workspace too small
+
+
+def test_block32_host_checks():
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    buf = ctypes.create_string_buffer(512)
+    a16 = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 256
+    assert L.moe_quant_act_b32(None, 1, 64, a16, a16, None) == -1
+    assert L.moe_quant_act_b32(a16, 1, 48, a16, a16, None) == -2      # D % 32
+    assert L.moe_quant_act_b32(a16 + 4, 1, 64, a16, a16, None) == -3  # x misaligned
+    m = moe.QMat(a16, a16, 0, 0)
+    ex = moe.Experts(m, m, m)
+    cfg = moe.config(256, 128, 8, 2)
+    need = L.moe_workspace_bytes(ctypes.byref(cfg), 1, moe.WS_SWIGLU8)
+    call = lambda xq, expert, ws_bytes, hq=None: L.moe_expert_swiglu_i4_b32(
+        ctypes.byref(cfg), xq, a16, 1, ctypes.byref(ex), expert, a16, hq, None, a16, ws_bytes, None)
+    assert call(a16, 8, need) == -1                  # expert index
+    assert call(a16 + 8, 0, need) == -3              # codes misaligned
+    assert call(a16, 0, need, hq=a16 + 8) == -3      # hidden-code probe misaligned
+    assert call(a16, 0, need - 16) == -4             # workspace too small
