@@ -61,6 +61,7 @@ def lib():
         L.moe_ref_expert_swiglu_i8.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_ref_pack_int2.argtypes = [vp, i32, i32, vp, vp]
         L.moe_ref_quant_act_b32.argtypes = [vp, i32, i32, vp, vp]
+        L.moe_ref_mla_decode.argtypes = [vp, vp, i32, vp, vp, vp, i32, vp]
         L.moe_ref_expert_swiglu_i4_b32.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp]
         L.moe_ref_unpack_int2.argtypes = [vp, i32, i32, vp]
         L.moe_ref_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
@@ -329,6 +330,22 @@ def expert_swiglu_b32(cfg: Config, xq: np.ndarray, sxb: np.ndarray, e: HostExper
                                               ctypes.byref(es), _p(y), _p(hq), _p(shb)),
            "expert_swiglu_i4_b32")
     return dict(y=y, hq=hq, shb=shb)
+
+
+class MlaConfig(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("kvl", ctypes.c_int32), ("nope", ctypes.c_int32),
+                ("rope", ctypes.c_int32), ("vdim", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+def mla_decode(cfg: MlaConfig, q: np.ndarray, kv_b: np.ndarray, L: np.ndarray, R: np.ndarray):
+    """Section 09 absorbed MLA decode: q [S][H][nope+rope], kv_b [H*(nope+vdim)][kvl],
+    L [T][kvl], R [T][rope] -> ctx [S][H][vdim]."""
+    q, kv_b, L, R = (_c(a, np.float32) for a in (q, kv_b, L, R))
+    S, T = q.shape[0], L.shape[0]
+    ctx = np.empty((S, cfg.H, cfg.vdim), np.float32)
+    _check(lib().moe_ref_mla_decode(ctypes.byref(cfg), _p(q), S, _p(kv_b), _p(L), _p(R), T, _p(ctx)),
+           "mla_decode")
+    return ctx
 
 
 class HostLayer:

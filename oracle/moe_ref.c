@@ -426,6 +426,57 @@ int moe_ref_expert_swiglu_i4_b32(const moe_ref_config *cfg, const int8_t *xq, co
   return 0;
 }
 
+/* ---- section 09: MLA decode attention with weight absorption -------------- */
+
+int moe_ref_mla_decode(const moe_ref_mla_config *c, const float *q, int S, const float *kv_b,
+                       const float *L, const float *R, int T, float *ctx) {
+  if (!c || !q || !kv_b || !L || !R || !ctx || S < 1 || T < S) return -1;
+  if (c->H < 1 || c->kvl < 1 || c->nope < 1 || c->rope < 0 || c->vdim < 1) return -1;
+  const int H = c->H, kvl = c->kvl, nope = c->nope, rope = c->rope, vd = c->vdim;
+  const int qh = nope + rope, rows = nope + vd;
+  double *qabs = (double *)malloc((size_t)kvl * sizeof(double));
+  double *clat = (double *)malloc((size_t)kvl * sizeof(double));
+  double *sc = (double *)malloc((size_t)T * sizeof(double));
+  if (!qabs || !clat || !sc) { free(qabs); free(clat); free(sc); return -2; }
+  for (int s = 0; s < S; s++) {
+    const int n = T - S + 1 + s;
+    for (int h = 0; h < H; h++) {
+      const float *qp = q + ((int64_t)s * H + h) * qh;
+      const float *wk = kv_b + (int64_t)h * rows * kvl;
+      const float *wv = wk + (int64_t)nope * kvl;
+      for (int i = 0; i < kvl; i++) qabs[i] = 0.0;
+      for (int d = 0; d < nope; d++)
+        for (int i = 0; i < kvl; i++) qabs[i] += (double)qp[d] * (double)wk[(int64_t)d * kvl + i];
+      double mx = -INFINITY;
+      for (int t = 0; t < n; t++) {
+        double a = 0.0;
+        for (int i = 0; i < kvl; i++) a += qabs[i] * (double)L[(int64_t)t * kvl + i];
+        for (int d = 0; d < rope; d++) a += (double)qp[nope + d] * (double)R[(int64_t)t * rope + d];
+        sc[t] = a * (double)c->scale;
+        if (sc[t] > mx) mx = sc[t];
+      }
+      double sum = 0.0;
+      for (int t = 0; t < n; t++) {
+        sc[t] = exp(sc[t] - mx);
+        sum += sc[t];
+      }
+      for (int i = 0; i < kvl; i++) clat[i] = 0.0;
+      for (int t = 0; t < n; t++)
+        for (int i = 0; i < kvl; i++) clat[i] += (sc[t] / sum) * (double)L[(int64_t)t * kvl + i];
+      float *out = ctx + ((int64_t)s * H + h) * vd;
+      for (int v = 0; v < vd; v++) {
+        double a = 0.0;
+        for (int i = 0; i < kvl; i++) a += (double)wv[(int64_t)v * kvl + i] * clat[i];
+        out[v] = (float)a;
+      }
+    }
+  }
+  free(qabs);
+  free(clat);
+  free(sc);
+  return 0;
+}
+
 /* ---- the block ------------------------------------------------------------ */
 
 static int layer_ok(const moe_ref_config *cfg, const moe_ref_layer *L) {

@@ -14,6 +14,8 @@
  *   - section 06 (per-row int4 quantization and nibble packing; the packed
  *     int2 layout below is a reading of the same rule at 2 bits, parity with
  *     the article unpinned),
+ *   - section 09 (MLA decode attention with weight absorption, the step
+ *     after the MoE block),
  *   - section 11 (sigmoid router with correction bias, top-K, unique-expert
  *     union, SwiGLU expert, weighted scatter),
  *   - the summaries' "Q8_0 style" activation remark (block-32 scales below,
@@ -175,6 +177,27 @@ int moe_ref_quant_act_b32(const float *x, int S, int D, int8_t *xq, float *sxb);
 int moe_ref_expert_swiglu_i4_b32(const moe_ref_config *cfg, const int8_t *xq, const float *sxb,
                                  int S, const moe_ref_expert *e, float *y, int8_t *hq,
                                  float *shb);
+
+/* Section 09 MLA decode attention with weight absorption.  The cache keeps
+ * per token a latent row L[t][kvl] and a rotary key R[t][rope] shared by all
+ * heads.  kv_b holds, per head h, nope rows (key up-projection) and then
+ * vdim rows (value up-projection) of kvl columns: rows h*(nope+vdim) + d.
+ * For query s, head h (q[s][h] = nope values, then rope values):
+ *   qabs[i]  = sum_d q_nope[d] * kv_b[h, d][i]          (key absorbed into q)
+ *   score[t] = (sum_i qabs[i] L[t][i] + sum_d q_rope[d] R[t][d]) * scale
+ *   p        = softmax(score) over the visible rows
+ *   clat[i]  = sum_t p[t] L[t][i]
+ *   ctx[s][h][v] = sum_i kv_b[h, nope + v][i] * clat[i]  (value absorbed after)
+ * Visible rows (reading: the S queries are the last S cache rows, in order,
+ * each seeing itself and everything before it): t < T - S + 1 + s.
+ * All arithmetic in double, each output rounded once to float. */
+typedef struct {
+  int32_t H, kvl, nope, rope, vdim;
+  float scale;
+} moe_ref_mla_config;
+
+int moe_ref_mla_decode(const moe_ref_mla_config *c, const float *q, int S, const float *kv_b,
+                       const float *L, const float *R, int T, float *ctx);
 
 /* The block for S tokens, one token at a time: route, quantize the token,
  * run its K experts and the shared expert, and combine
