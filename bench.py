@@ -414,6 +414,59 @@ def bench_fmt8(layer, steps: int = 512, n8: int = 8, n4: int = 16, n2: int = 32)
     return res
 
 
+def bench_mla(contexts=(1024, 4096, 16384), steps: int = 200):
+    """Section 09 absorbed MLA decode at the GLM shape (64 heads, latent 512,
+    nope 192, rope 64, value 256; float32), one query per call over a cache of
+    T rows.  Algorithmic bytes: kv_b once (64 * 448 * 512 floats) + the cache
+    rows (T * 576 floats) + q and ctx."""
+    import numpy as np
+    import torch
+
+    import int4_expert_gemv_moe_amd as moe
+
+    H, kvl, nope, rope, vdim = 64, 512, 192, 64, 256
+    cfg = moe.MlaConfig(H, kvl, nope, rope, vdim, float(1.0 / np.sqrt(nope + rope)))
+    lib = moe.lib()
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    kv_b = torch.randn(H * (nope + vdim), kvl, device="cuda", generator=g) / kvl ** 0.5
+    q = torch.randn(1, H, nope + rope, device="cuda", generator=g)
+    ctx = torch.empty(1, H, vdim, device="cuda")
+    res = {"workload": "GLM-shape MLA decode with weight absorption (64 heads, latent 512 + "
+                       "rope 64, value 256, float32), 1 query per call", "steps": steps}
+    for T in contexts:
+        L = torch.randn(T, kvl, device="cuda", generator=g)
+        R = torch.randn(T, rope, device="cuda", generator=g)
+        ws = moe.MlaWorkspace(cfg, 1, T)
+        args = (ctypes.byref(cfg), ctypes.c_void_p(q.data_ptr()), 1, ctypes.c_void_p(kv_b.data_ptr()),
+                ctypes.c_void_p(L.data_ptr()), ctypes.c_void_p(R.data_ptr()), T,
+                ctypes.c_void_p(ctx.data_ptr()), ws.ptr, ws.nbytes, st)
+
+        def run(k):
+            rc = 0
+            for _ in range(k):
+                rc |= lib.moe_mla_decode(*args)
+            if rc:
+                raise moe.MoeError(f"moe_mla_decode failed ({rc})")
+
+        run(20)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        nbytes = (H * (nope + vdim) * kvl + T * (kvl + rope) + H * (nope + rope + vdim)) * 4
+        res[f"T{T}"] = {"us_per_call": round(us, 3), "bytes": int(nbytes),
+                        "GBps": round(nbytes / us / 1e3, 1),
+                        "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+        log(f"mla T={T}: {us:.2f} us/call ({nbytes / us / 1e3:.0f} GB/s)")
+        del L, R, ws
+    return res
+
+
 def bench_stack(steps: int = 64):
     """48 GLM-shape layers resident in HBM (per-layer Zipf-skewed routing,
     RMSNorm + residual, one MOE_F_PRENORM call per layer): decode steps of
@@ -509,7 +562,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the verify, prefill and 48-layer stack measurements")
-    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered", "topp", "fmt8"],
+    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered", "topp", "fmt8", "mla"],
                     help="run only that secondary measurement and print its record (for profiling)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay pass (value then comes from the stream pass); "
@@ -547,6 +600,8 @@ def main():
     if args.only:
         if args.only == "stack":
             rec = bench_stack()
+        elif args.only == "mla":
+            rec = bench_mla()
         elif args.only == "topp":
             reps = [build_device_layer(r, synth.GLM, r, synth.router_b_uniform(r, synth.GLM, r))
                     for r in range(args.replicas)]
@@ -708,6 +763,10 @@ def main():
             secondary["stack48_decode"] = bench_stack()
         except Exception as exc:
             secondary["stack48_decode"] = {"error": f"{type(exc).__name__}: {exc}"}
+        try:
+            secondary["mla_decode"] = bench_mla()
+        except Exception as exc:
+            secondary["mla_decode"] = {"error": f"{type(exc).__name__}: {exc}"}
 
     layer_gbps = LAYER_TOKEN_BYTES / (us_per_token * 1e-6) / 1e9
     rec = {

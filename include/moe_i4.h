@@ -246,6 +246,40 @@ int moe_expert_swiglu_i4_b32(const moe_config *cfg, const int8_t *xq, const floa
                              const moe_experts *w, int expert, float *y, int8_t *hq, float *shb,
                              void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Section 09 MLA decode attention with weight absorption (the step after the
+ * MoE block in a decoder layer).  The cache keeps per token one latent row
+ * L[t][kvl] and one rotary key R[t][rope] shared by all heads.  kv_b holds,
+ * per head h, nope rows of the key up-projection and then vdim rows of the
+ * value up-projection, kvl columns each: kv_b[h][nope + vdim][kvl].  For
+ * query s and head h, with q[s][h] = (q_nope[nope], q_rope[rope]):
+ * qabs = W_UK[h]^T q_nope, score[t] = (qabs . L[t] + q_rope . R[t]) * scale,
+ * p = softmax(score) over the visible rows, ctx[s][h] = W_UV[h] (sum_t p[t]
+ * L[t]).  The S queries are the last S cache rows, in order: query s sees
+ * rows t < T - S + 1 + s.  All float32; kv_b 16-byte aligned, every other
+ * pointer 4-byte aligned.
+ * Limits: kvl a multiple of 64 up to 1024, rope <= 64, S <= T <= 16384
+ * (MOE_ESHAPE otherwise). */
+typedef struct {
+  int32_t H;     /* heads (64 for the GLM shape) */
+  int32_t kvl;   /* latent width (512) */
+  int32_t nope;  /* non-rotary query/key dims per head (192) */
+  int32_t rope;  /* rotary dims (64) */
+  int32_t vdim;  /* value dims per head (256) */
+  float scale;   /* score scale, e.g. 1/sqrt(nope + rope) */
+} moe_mla_config;
+
+/* Workspace bytes of moe_mla_decode for S queries over T cache rows
+ * (0 for invalid arguments). */
+size_t moe_mla_workspace_bytes(const moe_mla_config *cfg, int S, int T);
+
+/* q[S][H][nope + rope], kv_b as above, L[T][kvl], R[T][rope] (may be NULL
+ * when rope == 0) -> ctx[S][H][vdim].  Launches: query absorption; per
+ * 128-row cache chunk, scores, chunk softmax statistics and the weighted
+ * latent sum; the merge of the chunks and the value up-projection. */
+int moe_mla_decode(const moe_mla_config *cfg, const float *q, int S, const float *kv_b,
+                   const float *L, const float *R, int T, float *ctx, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
+
 /* The block, one token at a time (each token reads its own K experts):
  * route, quantize, run the K routed experts and the shared expert, and
  * combine out[s] = sum_k w_k * y_k (k in selection order, from 0) + y_shared.

@@ -79,6 +79,9 @@ def lib():
         L.moe_expert_swiglu_i8.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_pack_int2.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_quant_act_b32.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_mla_workspace_bytes.argtypes = [vp, i32, i32]
+        L.moe_mla_workspace_bytes.restype = sz
+        L.moe_mla_decode.argtypes = [vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp]
         L.moe_expert_swiglu_i4_b32.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
@@ -107,7 +110,7 @@ def lib():
         for name in ("moe_workspace_init", "moe_pack_int4", "moe_quant_act_i8", "moe_router_topk",
                      "moe_expert_swiglu_i4", "moe_quantize_rows_i8", "moe_expert_swiglu_i8",
                      "moe_pack_int2", "moe_expert_swiglu_i2", "moe_quant_act_b32",
-                     "moe_expert_swiglu_i4_b32",
+                     "moe_expert_swiglu_i4_b32", "moe_mla_decode",
                      "moe_layer_forward", "moe_layer_forward_batch",
                      "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
                      "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
@@ -450,6 +453,42 @@ def moe_expert_swiglu_i4_b32(cfg: Config, xq: torch.Tensor, sxb: torch.Tensor,
                                           ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
            "moe_expert_swiglu_i4_b32")
     return dict(y=y, hq=hq, shb=shb)
+
+
+class MlaConfig(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("kvl", ctypes.c_int32), ("nope", ctypes.c_int32),
+                ("rope", ctypes.c_int32), ("vdim", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class MlaWorkspace:
+    """Device scratch of moe_mla_decode for up to S queries over T cache rows."""
+
+    def __init__(self, cfg: MlaConfig, S: int, T: int, device="cuda"):
+        n = lib().moe_mla_workspace_bytes(ctypes.byref(cfg), S, T)
+        if n == 0:
+            raise MoeError("moe_mla_workspace_bytes rejected the configuration")
+        self.nbytes = int(n)
+        self.buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.buf.data_ptr()) % 256
+        self.view = self.buf[off: off + self.nbytes]
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.view.data_ptr())
+
+
+def moe_mla_decode(cfg: MlaConfig, q: torch.Tensor, kv_b: torch.Tensor, L: torch.Tensor,
+                   R: torch.Tensor, ws: MlaWorkspace, out=None, stream=None):
+    """Section 09 absorbed MLA decode: q [S][H][nope+rope], kv_b [H*(nope+vdim)][kvl],
+    L [T][kvl], R [T][rope] (float32) -> ctx [S][H][vdim]."""
+    for t, n in ((q, "q"), (kv_b, "kv_b"), (L, "L"), (R, "R")):
+        _dev(t, torch.float32, n)
+    S, T = q.shape[0], L.shape[0]
+    ctx = torch.empty(S, cfg.H, cfg.vdim, dtype=torch.float32, device=q.device) if out is None else out
+    _check(lib().moe_mla_decode(ctypes.byref(cfg), _ptr(q), S, _ptr(kv_b), _ptr(L), _ptr(R), T,
+                                _ptr(ctx), ws.ptr, ws.nbytes, ctypes.c_void_p(_stream(stream))),
+           "moe_mla_decode")
+    return ctx
 
 
 def _probe(topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None, keff=None):

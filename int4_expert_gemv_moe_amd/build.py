@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_i4.so")
 SOURCES = ["router.hip", "decode.hip", "grouped.hip", "grouped_mfma.hip", "misc.hip", "moe_abi.hip",
-           "tier.hip", "fmt8.hip", "fmt2.hip", "b32.hip"]
+           "tier.hip", "fmt8.hip", "fmt2.hip", "b32.hip", "mla.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -1,0 +1,241 @@
+// mla.hip -- MLA decode attention with weight absorption (section 09 of the
+// reader.mx article "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型"): the cache
+// keeps one latent row and one rotary key per token; the key up-projection
+// is absorbed into the query and the value up-projection is applied to the
+// attention-weighted latent.
+//
+// Three launches, split over the cache like flash decoding:
+//   1. absorb: qabs[s][h] = W_UK[h]^T q_nope[s][h] (eight workgroups per
+//      query and head, each an eighth of the key rows; 16-byte loads);
+//   2. chunks: workgroup (s, four heads, k) scores cache rows [ck,
+//      ck + c) (c = 64 or 128) of the query's window for its heads (each row loaded once
+//      for all four), then per head the local max m_k, exp sum l_k and
+//      latent sum sum_t e^(score_t - m_k) L[t];
+//   3. combine: per (s, h) the chunks merge with weights e^(m_k - m), the
+//      latent is normalized, and the value up-projection gives ctx (eight
+//      workgroups per query and head, each an eighth of the value rows).
+// All float32; the oracle computes in double.
+#include "moe_kernels.h"
+
+namespace moe {
+
+// Workgroup (s, h, part) sums the key rows d of its share of [0, nope).
+// Thread t takes latent columns 4 (t % (kvl/4)) .. +3 (16-byte loads) of rows
+// d0 + t / (kvl/4), stepping by floor(1024 / kvl) rows;
+// the row phases are added through shared memory in a fixed order.  The
+// chunk kernel adds the parts' vectors in a fixed order.
+__global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
+  __shared__ float4 red[256];
+  const int sh = blockIdx.x / kMlaAbsorbParts, part = blockIdx.x % kMlaAbsorbParts;
+  const int h = sh % a.H;
+  const int d0 = a.nope * part / kMlaAbsorbParts, d1 = a.nope * (part + 1) / kMlaAbsorbParts;
+  const float *qp = a.q + (int64_t)sh * (a.nope + a.rope);
+  const float *wk = a.kv_b + (int64_t)h * (a.nope + a.vdim) * a.kvl;
+  const int tpr = a.kvl >> 2;           // threads per row (16 .. 256)
+  const int nph = 256 / tpr;            // row phases (1 .. 16); threads past nph * tpr idle
+  const int c4 = threadIdx.x % tpr, ph = threadIdx.x / tpr;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int d = d0 + ph; ph < nph && d < d1; d += nph) {
+    const float qd = qp[d];
+    const float4 w = reinterpret_cast<const float4 *>(wk + (int64_t)d * a.kvl)[c4];
+    acc.x = fmaf(qd, w.x, acc.x);
+    acc.y = fmaf(qd, w.y, acc.y);
+    acc.z = fmaf(qd, w.z, acc.z);
+    acc.w = fmaf(qd, w.w, acc.w);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (ph == 0) {
+    float4 t = red[c4];
+    for (int p = 1; p < nph; p++) {
+      const float4 u = red[p * tpr + c4];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    reinterpret_cast<float4 *>(a.qabs + ((int64_t)sh * kMlaAbsorbParts + part) * a.kvl)[c4] = t;
+  }
+}
+
+// kvl % 64 == 0 and kvl <= 1024: lane l holds latent columns l + 64j.
+constexpr int kMlaMaxJ = 16;
+
+// Workgroup (s, hg, k): heads kMlaHeads hg .. +kMlaHeads-1 of query s over
+// cache rows [ck, ck + c) of its window (c = 64 or 128 rows).  Each cache row is loaded once
+// for all of them: a wave scores one row against their absorbed queries
+// (lanes over latent columns, rotary part on the first lanes), wave w then
+// takes the softmax statistics of heads w, w + 4, ..., and the threads (over
+// latent columns) form the weighted latent sums from one load of each value.
+__global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
+  __shared__ float sc[kMlaHeads][kMlaMaxChunk];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ngroups = (a.H + kMlaHeads - 1) / kMlaHeads;
+  const int k = blockIdx.x % a.nsplit;
+  const int sg = blockIdx.x / a.nsplit;  // s * ngroups + hg
+  const int s = sg / ngroups, h0 = (sg % ngroups) * kMlaHeads;
+  const int n = a.T - a.S + 1 + s;  // visible cache rows of query s
+  const int t0 = k * a.chunk;
+  const int nt = max(0, min(a.chunk, n - t0));
+  const int nj = a.kvl >> 6;
+  if (nt == 0) {  // the chunk lies past this query's window
+    for (int hb = 0; hb < kMlaHeads && h0 + hb < a.H; hb++) {
+      const int64_t part = ((int64_t)s * a.H + h0 + hb) * a.nsplit + k;
+      for (int i = tid; i < a.kvl; i += 256) a.pclat[part * a.kvl + i] = 0.f;
+      if (tid == 0) {
+        a.pm[part] = -INFINITY;
+        a.pl[part] = 0.f;
+      }
+    }
+    return;
+  }
+  float qa[kMlaHeads][kMlaMaxJ], qr[kMlaHeads];
+#pragma unroll
+  for (int hb = 0; hb < kMlaHeads; hb++) {
+    const int64_t sh = (int64_t)s * a.H + min(h0 + hb, a.H - 1);
+    const float *qab = a.qabs + sh * kMlaAbsorbParts * a.kvl;
+#pragma unroll
+    for (int j = 0; j < kMlaMaxJ; j++) {
+      const int i = lane + 64 * j;
+      float v = 0.f;
+      if (j < nj)
+#pragma unroll
+        for (int p = 0; p < kMlaAbsorbParts; p++) v += qab[p * a.kvl + i];
+      qa[hb][j] = v;
+    }
+    qr[hb] = lane < a.rope ? a.q[sh * (a.nope + a.rope) + a.nope + lane] : 0.f;
+  }
+  for (int tt = wave; tt < nt; tt += 4) {
+    const int t = t0 + tt;
+    const float *lr = a.L + (int64_t)t * a.kvl;
+    float lv[kMlaMaxJ];
+#pragma unroll
+    for (int j = 0; j < kMlaMaxJ; j++) lv[j] = j < nj ? lr[lane + 64 * j] : 0.f;
+    const float rv = lane < a.rope ? a.R[(int64_t)t * a.rope + lane] : 0.f;
+#pragma unroll
+    for (int hb = 0; hb < kMlaHeads; hb++) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMlaMaxJ; j++)
+        if (j < nj) acc = fmaf(qa[hb][j], lv[j], acc);
+      if (lane < a.rope) acc = fmaf(qr[hb], rv, acc);
+      acc = wave_sum_f32(acc);
+      if (lane == 0) sc[hb][tt] = acc * a.scale;
+    }
+  }
+  __syncthreads();
+  for (int hb = wave; hb < kMlaHeads; hb += 4) {  // wave w: heads w, w + 4, ...
+    float m = -INFINITY;
+    for (int tt = lane; tt < nt; tt += 64) m = fmaxf(m, sc[hb][tt]);
+    m = wave_max_f32(m);
+    float l = 0.f;
+    for (int tt = lane; tt < nt; tt += 64) {
+      const float e = expf(sc[hb][tt] - m);
+      sc[hb][tt] = e;
+      l += e;
+    }
+    l = wave_sum_f32(l);
+    if (lane == 0 && h0 + hb < a.H) {
+      const int64_t part = ((int64_t)s * a.H + h0 + hb) * a.nsplit + k;
+      a.pm[part] = m;
+      a.pl[part] = l;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < a.kvl; i += 256) {
+    const float *lc = a.L + (int64_t)t0 * a.kvl + i;
+    float acc[kMlaHeads];
+#pragma unroll
+    for (int hb = 0; hb < kMlaHeads; hb++) acc[hb] = 0.f;
+#pragma unroll 4
+    for (int tt = 0; tt < nt; tt++) {
+      const float v = lc[(int64_t)tt * a.kvl];
+#pragma unroll
+      for (int hb = 0; hb < kMlaHeads; hb++) acc[hb] = fmaf(sc[hb][tt], v, acc[hb]);
+    }
+#pragma unroll
+    for (int hb = 0; hb < kMlaHeads; hb++)
+      if (h0 + hb < a.H)
+        a.pclat[(((int64_t)s * a.H + h0 + hb) * a.nsplit + k) * a.kvl + i] = acc[hb];
+  }
+}
+
+// Workgroup (s, h, vb) merges the chunks of (s, h) and produces value rows
+// [vdim vb / 8, vdim (vb + 1) / 8), four rows per wave at a time.
+__global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
+  __shared__ float wk[kMlaMaxSplit];
+  __shared__ float clat[64 * kMlaMaxJ];
+  __shared__ float inv_l;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sh = blockIdx.x / kMlaValueParts, vb = blockIdx.x % kMlaValueParts;
+  const int h = sh % a.H;
+  const int nj = a.kvl >> 6;
+  const float *wv = a.kv_b + ((int64_t)h * (a.nope + a.vdim) + a.nope) * a.kvl;
+  const int v0 = a.vdim * vb / kMlaValueParts, v1 = a.vdim * (vb + 1) / kMlaValueParts;
+  // the wave's first four value rows do not depend on the merge: load them first
+  float wr[4][kMlaMaxJ];
+  {
+    const int vg = v0 + 4 * wave;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float *row = wv + (int64_t)max(min(vg + r, v1 - 1), 0) * a.kvl;
+#pragma unroll
+      for (int j = 0; j < kMlaMaxJ; j++) wr[r][j] = j < nj ? row[lane + 64 * j] : 0.f;
+    }
+  }
+  const float *pm = a.pm + (int64_t)sh * a.nsplit;
+  const float *pl = a.pl + (int64_t)sh * a.nsplit;
+  if (tid == 0) {
+    float m = -INFINITY;
+    for (int k = 0; k < a.nsplit; k++) m = fmaxf(m, pm[k]);
+    float l = 0.f;
+    for (int k = 0; k < a.nsplit; k++) {
+      const float w = pl[k] > 0.f ? expf(pm[k] - m) : 0.f;
+      wk[k] = w;
+      l = fmaf(w, pl[k], l);
+    }
+    inv_l = 1.f / l;
+  }
+  __syncthreads();
+  const float *pc = a.pclat + (int64_t)sh * a.nsplit * a.kvl;
+  for (int i = tid; i < a.kvl; i += 256) {
+    float acc = 0.f;
+    for (int k = 0; k < a.nsplit; k++) acc = fmaf(wk[k], pc[(int64_t)k * a.kvl + i], acc);
+    clat[i] = acc * inv_l;
+  }
+  __syncthreads();
+  float cl[kMlaMaxJ];
+#pragma unroll
+  for (int j = 0; j < kMlaMaxJ; j++) cl[j] = j < nj ? clat[lane + 64 * j] : 0.f;
+  for (int vg = v0 + 4 * wave; vg < v1; vg += 16) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if (vg != v0 + 4 * wave) {  // later groups: load now
+        const float *row = wv + (int64_t)min(vg + r, v1 - 1) * a.kvl;
+#pragma unroll
+        for (int j = 0; j < kMlaMaxJ; j++) wr[r][j] = j < nj ? row[lane + 64 * j] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kMlaMaxJ; j++)
+        if (j < nj) acc[r] = fmaf(wr[r][j], cl[j], acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float v = wave_sum_f32(acc[r]);
+      if (lane == 0 && vg + r < v1) a.ctx[(int64_t)sh * a.vdim + vg + r] = v;
+    }
+  }
+}
+
+hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st) {
+  const int sh = a.S * a.H;
+  hipLaunchKernelGGL(mla_absorb_kernel, dim3(sh * kMlaAbsorbParts), dim3(256), 0, st, a);
+  const int ngroups = (a.H + kMlaHeads - 1) / kMlaHeads;
+  hipLaunchKernelGGL(mla_chunk_kernel, dim3(a.S * ngroups * a.nsplit), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(sh * kMlaValueParts), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

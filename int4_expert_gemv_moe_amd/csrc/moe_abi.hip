@@ -428,6 +428,74 @@ int moe_expert_swiglu_i2(const moe_config *cfg, const int8_t *xq, const float *s
   return MOE_OK;
 }
 
+namespace {
+int mla_check(const moe_mla_config *c, int S, int T) {
+  if (!c) return MOE_EINVAL;
+  if (c->H < 1 || c->kvl < 64 || c->kvl % 64 || c->kvl > 1024) return MOE_ESHAPE;
+  if (c->nope < 1 || c->rope < 0 || c->rope > 64 || c->vdim < 1) return MOE_ESHAPE;
+  if (S < 1 || T < S || T > kMlaMaxChunk * kMlaMaxSplit) return MOE_ESHAPE;
+  if (!(c->scale == c->scale)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+size_t mla_carve(const moe_mla_config &c, int S, int T, char *base, MlaArgs *a) {
+  const int chunk = mla_chunk_rows(T);
+  const size_t sh = (size_t)S * c.H, ns = (size_t)((T + chunk - 1) / chunk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> float * {
+    float *p = base ? (float *)(base + off) : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  float *qabs = take(sh * kMlaAbsorbParts * c.kvl * 4);
+  float *pclat = take(sh * ns * c.kvl * 4);
+  float *pm = take(sh * ns * 4);
+  float *pl = take(sh * ns * 4);
+  if (a) {
+    a->qabs = qabs;
+    a->pclat = pclat;
+    a->pm = pm;
+    a->pl = pl;
+    a->nsplit = (int)ns;
+    a->chunk = chunk;
+  }
+  return off;
+}
+}  // namespace
+
+size_t moe_mla_workspace_bytes(const moe_mla_config *cfg, int S, int T) {
+  if (mla_check(cfg, S, T) != MOE_OK) return 0;
+  return mla_carve(*cfg, S, T, nullptr, nullptr);
+}
+
+int moe_mla_decode(const moe_mla_config *cfg, const float *q, int S, const float *kv_b,
+                   const float *L, const float *R, int T, float *ctx, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  MOE_TRY(mla_check(cfg, S, T));
+  if (!q || !kv_b || !L || (cfg->rope > 0 && !R) || !ctx || !ws) return MOE_EINVAL;
+  if (((uintptr_t)q & 3u) || !aligned16(kv_b) || ((uintptr_t)L & 3u) ||
+      ((uintptr_t)R & 3u) || ((uintptr_t)ctx & 3u) || ((uintptr_t)ws & 255u))
+    return MOE_EALIGN;
+  if (ws_bytes < mla_carve(*cfg, S, T, nullptr, nullptr)) return MOE_EWORKSPACE;
+  MOE_TRY(check_device());
+  MlaArgs a{};
+  mla_carve(*cfg, S, T, (char *)ws, &a);
+  a.S = S;
+  a.T = T;
+  a.H = cfg->H;
+  a.kvl = cfg->kvl;
+  a.nope = cfg->nope;
+  a.rope = cfg->rope;
+  a.vdim = cfg->vdim;
+  a.scale = cfg->scale;
+  a.q = q;
+  a.kv_b = kv_b;
+  a.L = L;
+  a.R = R;
+  a.ctx = ctx;
+  return hip_rc(launch_mla_decode(a, stream));
+}
+
 int moe_quant_act_b32(const float *x, int S, int D, int8_t *xq, float *sxb, hipStream_t stream) {
   if (!x || !xq || !sxb) return MOE_EINVAL;
   if (S < 1 || D < 32 || (D & 31)) return MOE_ESHAPE;

@@ -254,6 +254,31 @@ hipError_t launch_quant_b32(const QuantB32Args &a, hipStream_t st);
 hipError_t launch_swiglu_b32_gateup(const SwigluB32Args &a, hipStream_t st);
 hipError_t launch_swiglu_b32_down(const SwigluB32Args &a, hipStream_t st);
 
+// MLA decode attention with weight absorption (mla.hip).
+// Cache rows per attention workgroup: 64 up to 4096 rows, 128 beyond (swept:
+// 64 rows is faster at 1024 rows, 128 at 16384, where merging 256 chunks per
+// (query, head) costs more than the longer chunks).
+constexpr int kMlaMaxChunk = 128;
+constexpr int kMlaMaxSplit = 128;  // chunks per query: T <= 16384
+__host__ __device__ inline int mla_chunk_rows(int T) { return T <= 4096 ? 64 : 128; }
+constexpr int kMlaAbsorbParts = 8; // workgroups per (query, head) in the absorption
+constexpr int kMlaValueParts = 8;  // workgroups per (query, head) in the value projection
+constexpr int kMlaHeads = 4;       // heads per attention workgroup (8 measured slower: fewer workgroups, 171 VGPRs)
+struct MlaArgs {
+  int S, T, H, kvl, nope, rope, vdim, nsplit, chunk;
+  float scale;
+  const float *q;      // [S][H][nope + rope]
+  const float *kv_b;   // [H][nope + vdim][kvl]
+  const float *L;      // [T][kvl]
+  const float *R;      // [T][rope]
+  float *qabs;         // [S][H][kMlaAbsorbParts][kvl] partial absorbed queries
+  float *pclat;        // [S][H][nsplit][kvl] per-chunk latent sums
+  float *pm, *pl;      // [S][H][nsplit] per-chunk max and exp sum
+  float *ctx;          // [S][H][vdim]
+};
+
+hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st);
+
 hipError_t launch_pack_int2(const Pack2Args &a, hipStream_t st);
 hipError_t launch_swiglu2_gateup(const Swiglu2Args &a, hipStream_t st);
 hipError_t launch_swiglu2_down(const Swiglu2Args &a, hipStream_t st);

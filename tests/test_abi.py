@@ -218,3 +218,22 @@ def test_block32_host_checks():
     assert call(a16 + 8, 0, need) == -3              # codes misaligned
     assert call(a16, 0, need, hq=a16 + 8) == -3      # hidden-code probe misaligned
     assert call(a16, 0, need - 16) == -4             # workspace too small
+
+
+def test_mla_host_checks():
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    buf = ctypes.create_string_buffer(512)
+    a = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 256
+    good = moe.MlaConfig(64, 512, 192, 64, 256, 0.0625)
+    assert L.moe_mla_workspace_bytes(ctypes.byref(good), 1, 4096) > 64 * 32 * 512 * 4
+    for bad, S, T in ((moe.MlaConfig(64, 500, 192, 64, 256, 0.0625), 1, 8),   # kvl % 64
+                      (moe.MlaConfig(64, 2048, 192, 64, 256, 0.0625), 1, 8),  # kvl > 1024
+                      (moe.MlaConfig(64, 512, 192, 65, 256, 0.0625), 1, 8),   # rope > 64
+                      (good, 4, 3), (good, 1, 16385)):                         # T < S, T too long
+        assert L.moe_mla_workspace_bytes(ctypes.byref(bad), S, T) == 0
+        assert L.moe_mla_decode(ctypes.byref(bad), a, S, a, a, a, T, a, a, 1 << 20, None) == -2
+    need = L.moe_mla_workspace_bytes(ctypes.byref(good), 1, 64)
+    assert L.moe_mla_decode(ctypes.byref(good), None, 1, a, a, a, 64, a, a, need, None) == -1
+    assert L.moe_mla_decode(ctypes.byref(good), a + 2, 1, a, a, a, 64, a, a, need, None) == -3
+    assert L.moe_mla_decode(ctypes.byref(good), a, 1, a, a, a, 64, a, a, need - 16, None) == -4
