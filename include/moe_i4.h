@@ -15,7 +15,10 @@
  *     used to run a batch of tokens with each selected expert read once;
  *   - section 12: per-row int8 activation quantization (scale amax/127,
  *     floored at 1e-12, round half to even) in front of every integer matmul,
- *     integer dot products rescaled by the weight and activation scales.
+ *     integer dot products rescaled by the weight and activation scales;
+ *   - beside the int4 block: the section 05 int8 weight format, a packed int2
+ *     format, block-32 activation scales (one SwiGLU expert each) and the
+ *     section 09 MLA decode attention with weight absorption.
  *
  * Conventions
  *   - Every pointer is a DEVICE pointer unless its comment says "host".
