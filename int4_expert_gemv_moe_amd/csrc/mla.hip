@@ -7,10 +7,10 @@
 // Three launches, split over the cache like flash decoding:
 //   1. absorb: qabs[s][h] = W_UK[h]^T q_nope[s][h] (eight workgroups per
 //      query and head, each an eighth of the key rows; 16-byte loads);
-//   2. chunks: workgroup (s, four heads, k) scores cache rows [ck,
-//      ck + c) (c = 64 or 128) of the query's window for its heads (each row loaded once
-//      for all four), then per head the local max m_k, exp sum l_k and
-//      latent sum sum_t e^(score_t - m_k) L[t];
+//   2. chunks: workgroup (s, four heads, k) reads cache rows [ck, ck + c)
+//      (c = 64 or 128) of the query's window once and forms, per head, the
+//      chunk's max m_k, exp sum l_k and latent sum sum_t e^(score_t - m_k) L[t]
+//      in one pass (online softmax);
 //   3. combine: per (s, h) the chunks merge with weights e^(m_k - m), the
 //      latent is normalized, and the value up-projection gives ctx (eight
 //      workgroups per query and head, each an eighth of the value rows).
@@ -63,13 +63,18 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
 constexpr int kMlaMaxJ = 16;
 
 // Workgroup (s, hg, k): heads kMlaHeads hg .. +kMlaHeads-1 of query s over
-// cache rows [ck, ck + c) of its window (c = 64 or 128 rows).  Each cache row is loaded once
-// for all of them: a wave scores one row against their absorbed queries
-// (lanes over latent columns, rotary part on the first lanes), wave w then
-// takes the softmax statistics of heads w, w + 4, ..., and the threads (over
-// latent columns) form the weighted latent sums from one load of each value.
+// cache rows [ck, ck + c) of its window (c = 64 or 128 rows).  Each cache row
+// is loaded once, by one wave, for all the heads: the wave scores it against
+// their absorbed queries (lanes over latent columns, rotary part on the first
+// lanes, a DPP sum per head) and folds it into per-head running softmax
+// statistics and latent sums (online softmax: when the running max grows the
+// sums are rescaled).  The four waves' partial results merge through shared
+// memory in a fixed order.
+// MAXJ >= kvl / 64 bounds the latent columns per lane (register arrays).
+template <int MAXJ>
 __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
-  __shared__ float sc[kMlaHeads][kMlaMaxChunk];
+  __shared__ float wacc[4][kMlaHeads][64 * MAXJ];
+  __shared__ float wm[4][kMlaHeads], wl[4][kMlaHeads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ngroups = (a.H + kMlaHeads - 1) / kMlaHeads;
   const int k = blockIdx.x % a.nsplit;
@@ -90,13 +95,13 @@ __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
     }
     return;
   }
-  float qa[kMlaHeads][kMlaMaxJ], qr[kMlaHeads];
+  float qa[kMlaHeads][MAXJ], qr[kMlaHeads];
 #pragma unroll
   for (int hb = 0; hb < kMlaHeads; hb++) {
     const int64_t sh = (int64_t)s * a.H + min(h0 + hb, a.H - 1);
     const float *qab = a.qabs + sh * kMlaAbsorbParts * a.kvl;
 #pragma unroll
-    for (int j = 0; j < kMlaMaxJ; j++) {
+    for (int j = 0; j < MAXJ; j++) {
       const int i = lane + 64 * j;
       float v = 0.f;
       if (j < nj)
@@ -106,58 +111,71 @@ __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
     }
     qr[hb] = lane < a.rope ? a.q[sh * (a.nope + a.rope) + a.nope + lane] : 0.f;
   }
+  float m[kMlaHeads], l[kMlaHeads], acc[kMlaHeads][MAXJ];
+#pragma unroll
+  for (int hb = 0; hb < kMlaHeads; hb++) {
+    m[hb] = -INFINITY;
+    l[hb] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; j++) acc[hb][j] = 0.f;
+  }
   for (int tt = wave; tt < nt; tt += 4) {
     const int t = t0 + tt;
     const float *lr = a.L + (int64_t)t * a.kvl;
-    float lv[kMlaMaxJ];
+    float lv[MAXJ];
 #pragma unroll
-    for (int j = 0; j < kMlaMaxJ; j++) lv[j] = j < nj ? lr[lane + 64 * j] : 0.f;
+    for (int j = 0; j < MAXJ; j++) lv[j] = j < nj ? lr[lane + 64 * j] : 0.f;
     const float rv = lane < a.rope ? a.R[(int64_t)t * a.rope + lane] : 0.f;
 #pragma unroll
     for (int hb = 0; hb < kMlaHeads; hb++) {
-      float acc = 0.f;
+      float d = 0.f;
 #pragma unroll
-      for (int j = 0; j < kMlaMaxJ; j++)
-        if (j < nj) acc = fmaf(qa[hb][j], lv[j], acc);
-      if (lane < a.rope) acc = fmaf(qr[hb], rv, acc);
-      acc = wave_sum_f32(acc);
-      if (lane == 0) sc[hb][tt] = acc * a.scale;
+      for (int j = 0; j < MAXJ; j++)
+        if (j < nj) d = fmaf(qa[hb][j], lv[j], d);
+      if (lane < a.rope) d = fmaf(qr[hb], rv, d);
+      const float sc = wave_sum_f32(d) * a.scale;
+      const float mn = fmaxf(m[hb], sc);
+      const float c = expf(m[hb] - mn);  // 0 for the first row (m = -inf)
+      const float e = expf(sc - mn);
+      l[hb] = fmaf(l[hb], c, e);
+#pragma unroll
+      for (int j = 0; j < MAXJ; j++)
+        if (j < nj) acc[hb][j] = fmaf(e, lv[j], acc[hb][j] * c);
+      m[hb] = mn;
+    }
+  }
+#pragma unroll
+  for (int hb = 0; hb < kMlaHeads; hb++) {
+#pragma unroll
+    for (int j = 0; j < MAXJ; j++)
+      if (j < nj) wacc[wave][hb][lane + 64 * j] = acc[hb][j];
+    if (lane == 0) {
+      wm[wave][hb] = m[hb];
+      wl[wave][hb] = l[hb];
     }
   }
   __syncthreads();
-  for (int hb = wave; hb < kMlaHeads; hb += 4) {  // wave w: heads w, w + 4, ...
-    float m = -INFINITY;
-    for (int tt = lane; tt < nt; tt += 64) m = fmaxf(m, sc[hb][tt]);
-    m = wave_max_f32(m);
-    float l = 0.f;
-    for (int tt = lane; tt < nt; tt += 64) {
-      const float e = expf(sc[hb][tt] - m);
-      sc[hb][tt] = e;
-      l += e;
-    }
-    l = wave_sum_f32(l);
-    if (lane == 0 && h0 + hb < a.H) {
-      const int64_t part = ((int64_t)s * a.H + h0 + hb) * a.nsplit + k;
-      a.pm[part] = m;
-      a.pl[part] = l;
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < a.kvl; i += 256) {
-    const float *lc = a.L + (int64_t)t0 * a.kvl + i;
-    float acc[kMlaHeads];
+  for (int hb = 0; hb < kMlaHeads && h0 + hb < a.H; hb++) {
+    float mm = -INFINITY;
 #pragma unroll
-    for (int hb = 0; hb < kMlaHeads; hb++) acc[hb] = 0.f;
-#pragma unroll 4
-    for (int tt = 0; tt < nt; tt++) {
-      const float v = lc[(int64_t)tt * a.kvl];
+    for (int w = 0; w < 4; w++) mm = fmaxf(mm, wm[w][hb]);
+    float cw[4], ll = 0.f;
 #pragma unroll
-      for (int hb = 0; hb < kMlaHeads; hb++) acc[hb] = fmaf(sc[hb][tt], v, acc[hb]);
+    for (int w = 0; w < 4; w++) {
+      cw[w] = wl[w][hb] > 0.f ? expf(wm[w][hb] - mm) : 0.f;
+      ll = fmaf(cw[w], wl[w][hb], ll);
     }
+    const int64_t part = ((int64_t)s * a.H + h0 + hb) * a.nsplit + k;
+    for (int i = tid; i < a.kvl; i += 256) {
+      float v = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < kMlaHeads; hb++)
-      if (h0 + hb < a.H)
-        a.pclat[(((int64_t)s * a.H + h0 + hb) * a.nsplit + k) * a.kvl + i] = acc[hb];
+      for (int w = 0; w < 4; w++) v = fmaf(cw[w], wacc[w][hb][i], v);
+      a.pclat[part * a.kvl + i] = v;
+    }
+    if (tid == 0) {
+      a.pm[part] = mm;
+      a.pl[part] = ll;
+    }
   }
 }
 
@@ -233,7 +251,12 @@ hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st) {
   const int sh = a.S * a.H;
   hipLaunchKernelGGL(mla_absorb_kernel, dim3(sh * kMlaAbsorbParts), dim3(256), 0, st, a);
   const int ngroups = (a.H + kMlaHeads - 1) / kMlaHeads;
-  hipLaunchKernelGGL(mla_chunk_kernel, dim3(a.S * ngroups * a.nsplit), dim3(256), 0, st, a);
+  const dim3 grid(a.S * ngroups * a.nsplit);
+  const int nj = a.kvl >> 6;
+  if (nj <= 2) hipLaunchKernelGGL((mla_chunk_kernel<2>), grid, dim3(256), 0, st, a);
+  else if (nj <= 4) hipLaunchKernelGGL((mla_chunk_kernel<4>), grid, dim3(256), 0, st, a);
+  else if (nj <= 8) hipLaunchKernelGGL((mla_chunk_kernel<8>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((mla_chunk_kernel<kMlaMaxJ>), grid, dim3(256), 0, st, a);
   hipLaunchKernelGGL(mla_combine_kernel, dim3(sh * kMlaValueParts), dim3(256), 0, st, a);
   return hipGetLastError();
 }
