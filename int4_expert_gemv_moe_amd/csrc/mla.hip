@@ -4,16 +4,18 @@
 // is absorbed into the query and the value up-projection is applied to the
 // attention-weighted latent.
 //
-// Three launches, split over the cache like flash decoding:
+// Four launches, split over the cache like flash decoding:
 //   1. absorb: qabs[s][h] = W_UK[h]^T q_nope[s][h] (eight workgroups per
 //      query and head, each an eighth of the key rows; 16-byte loads);
 //   2. chunks: workgroup (s, four heads, k) reads cache rows [ck, ck + c)
 //      (c = 64 or 128) of the query's window once and forms, per head, the
 //      chunk's max m_k, exp sum l_k and latent sum sum_t e^(score_t - m_k) L[t]
 //      in one pass (online softmax);
-//   3. combine: per (s, h) the chunks merge with weights e^(m_k - m), the
-//      latent is normalized, and the value up-projection gives ctx (eight
-//      workgroups per query and head, each an eighth of the value rows).
+//   3. merge: per (s, h) the chunks merge with weights e^(m_k - m) and the
+//      latent is normalized (four workgroups per query and head, each a
+//      quarter of the latent columns);
+//   4. value: the value up-projection gives ctx (eight workgroups per query
+//      and head, each an eighth of the value rows).
 // All float32; the oracle computes in double.
 #include "moe_kernels.h"
 
@@ -179,29 +181,14 @@ __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
   }
 }
 
-// Workgroup (s, h, vb) merges the chunks of (s, h) and produces value rows
-// [vdim vb / 8, vdim (vb + 1) / 8), four rows per wave at a time.
-__global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
+// Workgroup (s, h, cp) merges the chunks of (s, h) for latent columns
+// [kvl cp / 4, kvl (cp + 1) / 4): weights e^(m_k - m), normalized by the
+// merged exp sum.
+__global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   __shared__ float wk[kMlaMaxSplit];
-  __shared__ float clat[64 * kMlaMaxJ];
   __shared__ float inv_l;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sh = blockIdx.x / kMlaValueParts, vb = blockIdx.x % kMlaValueParts;
-  const int h = sh % a.H;
-  const int nj = a.kvl >> 6;
-  const float *wv = a.kv_b + ((int64_t)h * (a.nope + a.vdim) + a.nope) * a.kvl;
-  const int v0 = a.vdim * vb / kMlaValueParts, v1 = a.vdim * (vb + 1) / kMlaValueParts;
-  // the wave's first four value rows do not depend on the merge: load them first
-  float wr[4][kMlaMaxJ];
-  {
-    const int vg = v0 + 4 * wave;
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const float *row = wv + (int64_t)max(min(vg + r, v1 - 1), 0) * a.kvl;
-#pragma unroll
-      for (int j = 0; j < kMlaMaxJ; j++) wr[r][j] = j < nj ? row[lane + 64 * j] : 0.f;
-    }
-  }
+  const int tid = threadIdx.x;
+  const int sh = blockIdx.x / kMlaMergeParts, cp = blockIdx.x % kMlaMergeParts;
   const float *pm = a.pm + (int64_t)sh * a.nsplit;
   const float *pl = a.pl + (int64_t)sh * a.nsplit;
   if (tid == 0) {
@@ -216,14 +203,38 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
     inv_l = 1.f / l;
   }
   __syncthreads();
+  const int c0 = a.kvl * cp / kMlaMergeParts, c1 = a.kvl * (cp + 1) / kMlaMergeParts;
   const float *pc = a.pclat + (int64_t)sh * a.nsplit * a.kvl;
-  for (int i = tid; i < a.kvl; i += 256) {
+  for (int i = c0 + tid; i < c1; i += 256) {
     float acc = 0.f;
+#pragma unroll 8
     for (int k = 0; k < a.nsplit; k++) acc = fmaf(wk[k], pc[(int64_t)k * a.kvl + i], acc);
-    clat[i] = acc * inv_l;
+    a.clat[(int64_t)sh * a.kvl + i] = acc * inv_l;
   }
-  __syncthreads();
+}
+
+// Workgroup (s, h, vb): value rows [vdim vb / 8, vdim (vb + 1) / 8) of ctx,
+// four rows per wave in flight (the first four requested before the merged
+// latent is read).
+__global__ __launch_bounds__(256) void mla_value_kernel(MlaArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sh = blockIdx.x / kMlaValueParts, vb = blockIdx.x % kMlaValueParts;
+  const int h = sh % a.H;
+  const int nj = a.kvl >> 6;
+  const float *wv = a.kv_b + ((int64_t)h * (a.nope + a.vdim) + a.nope) * a.kvl;
+  const int v0 = a.vdim * vb / kMlaValueParts, v1 = a.vdim * (vb + 1) / kMlaValueParts;
+  float wr[4][kMlaMaxJ];
+  {
+    const int vg = v0 + 4 * wave;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float *row = wv + (int64_t)max(min(vg + r, v1 - 1), 0) * a.kvl;
+#pragma unroll
+      for (int j = 0; j < kMlaMaxJ; j++) wr[r][j] = j < nj ? row[lane + 64 * j] : 0.f;
+    }
+  }
   float cl[kMlaMaxJ];
+  const float *clat = a.clat + (int64_t)sh * a.kvl;
 #pragma unroll
   for (int j = 0; j < kMlaMaxJ; j++) cl[j] = j < nj ? clat[lane + 64 * j] : 0.f;
   for (int vg = v0 + 4 * wave; vg < v1; vg += 16) {
@@ -257,7 +268,8 @@ hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st) {
   else if (nj <= 4) hipLaunchKernelGGL((mla_chunk_kernel<4>), grid, dim3(256), 0, st, a);
   else if (nj <= 8) hipLaunchKernelGGL((mla_chunk_kernel<8>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((mla_chunk_kernel<kMlaMaxJ>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(sh * kMlaValueParts), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(mla_merge_kernel, dim3(sh * kMlaMergeParts), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(mla_value_kernel, dim3(sh * kMlaValueParts), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -451,7 +451,9 @@ size_t mla_carve(const moe_mla_config &c, int S, int T, char *base, MlaArgs *a) 
   float *pclat = take(sh * ns * c.kvl * 4);
   float *pm = take(sh * ns * 4);
   float *pl = take(sh * ns * 4);
+  float *clat = take(sh * c.kvl * 4);
   if (a) {
+    a->clat = clat;
     a->qabs = qabs;
     a->pclat = pclat;
     a->pm = pm;

@@ -263,6 +263,7 @@ constexpr int kMlaMaxSplit = 128;  // chunks per query: T <= 16384
 __host__ __device__ inline int mla_chunk_rows(int T) { return T <= 4096 ? 64 : 128; }
 constexpr int kMlaAbsorbParts = 8; // workgroups per (query, head) in the absorption
 constexpr int kMlaValueParts = 8;  // workgroups per (query, head) in the value projection
+constexpr int kMlaMergeParts = 4;  // workgroups per (query, head) in the chunk merge
 constexpr int kMlaHeads = 4;       // heads per attention workgroup (8 measured slower: fewer workgroups, 171 VGPRs)
 struct MlaArgs {
   int S, T, H, kvl, nope, rope, vdim, nsplit, chunk;
@@ -274,6 +275,7 @@ struct MlaArgs {
   float *qabs;         // [S][H][kMlaAbsorbParts][kvl] partial absorbed queries
   float *pclat;        // [S][H][nsplit][kvl] per-chunk latent sums
   float *pm, *pl;      // [S][H][nsplit] per-chunk max and exp sum
+  float *clat;         // [S][H][kvl] merged, normalized latent
   float *ctx;          // [S][H][vdim]
 };
 
