@@ -43,6 +43,7 @@ def _device_i2(he: oracle.HostExpertI2, n: int, e_id: int, shape) -> moe.DeviceE
     (synth.Shape(D=1280, I=192, E=3, K=1), 3),    # partial chunks in both projections
     (synth.Shape(D=8192, I=1024, E=1, K=1), 2),   # two chunks per gate/up row
     (synth.Shape(D=256, I=8192, E=1, K=1), 2),    # two chunks per down row
+    (synth.Shape(D=256, I=8192, E=1, K=1), 6),    # two passes of 4 tokens' hidden codes
     (GLM, 1), (GLM, 3)])
 def test_expert_swiglu_i2_parity(shape, S):
     say(f"swiglu_i2 D={shape.D} I={shape.I} S={S}")

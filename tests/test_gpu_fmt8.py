@@ -56,6 +56,7 @@ def _run(shape, S, he, e_id, seed=9):
     (synth.Shape(D=1280, I=96, E=3, K=1), 3),     # ragged chunks in both projections
     (synth.Shape(D=8192, I=1024, E=1, K=1), 2),   # widest rows of gate/up
     (synth.Shape(D=256, I=8192, E=1, K=1), 2),    # widest rows of down
+    (synth.Shape(D=256, I=8192, E=1, K=1), 6),    # two passes of 4 tokens' hidden codes
     (GLM, 1), (GLM, 3)])
 def test_expert_swiglu_i8_parity(shape, S):
     say(f"swiglu_i8 D={shape.D} I={shape.I} S={S}")
