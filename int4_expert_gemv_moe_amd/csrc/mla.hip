@@ -97,20 +97,25 @@ __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
     }
     return;
   }
+  // the heads' absorbed queries: the workgroup adds the absorption parts
+  // once into shared memory (fixed order), then every wave reads them
+  __shared__ float qsum[kMlaHeads][64 * MAXJ];
+  for (int idx = tid; idx < kMlaHeads * a.kvl; idx += 256) {
+    const int hb = idx / a.kvl, i = idx - hb * a.kvl;
+    const int64_t sh = (int64_t)s * a.H + min(h0 + hb, a.H - 1);
+    const float *qab = a.qabs + sh * kMlaAbsorbParts * a.kvl + i;
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < kMlaAbsorbParts; p++) v += qab[p * a.kvl];
+    qsum[hb][i] = v;
+  }
+  __syncthreads();
   float qa[kMlaHeads][MAXJ], qr[kMlaHeads];
 #pragma unroll
   for (int hb = 0; hb < kMlaHeads; hb++) {
     const int64_t sh = (int64_t)s * a.H + min(h0 + hb, a.H - 1);
-    const float *qab = a.qabs + sh * kMlaAbsorbParts * a.kvl;
 #pragma unroll
-    for (int j = 0; j < MAXJ; j++) {
-      const int i = lane + 64 * j;
-      float v = 0.f;
-      if (j < nj)
-#pragma unroll
-        for (int p = 0; p < kMlaAbsorbParts; p++) v += qab[p * a.kvl + i];
-      qa[hb][j] = v;
-    }
+    for (int j = 0; j < MAXJ; j++) qa[hb][j] = j < nj ? qsum[hb][lane + 64 * j] : 0.f;
     qr[hb] = lane < a.rope ? a.q[sh * (a.nope + a.rope) + a.nope + lane] : 0.f;
   }
   float m[kMlaHeads], l[kMlaHeads], acc[kMlaHeads][MAXJ];
