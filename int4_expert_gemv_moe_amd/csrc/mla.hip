@@ -12,8 +12,8 @@
 //      chunk's max m_k, exp sum l_k and latent sum sum_t e^(score_t - m_k) L[t]
 //      in one pass (online softmax);
 //   3. merge: per (s, h) the chunks merge with weights e^(m_k - m) and the
-//      latent is normalized (four workgroups per query and head, each a
-//      quarter of the latent columns);
+//      latent is normalized (eight workgroups per query and head, each an
+//      eighth of the latent columns);
 //   4. value: the value up-projection gives ctx (eight workgroups per query
 //      and head, each an eighth of the value rows).
 // All float32; the oracle computes in double.
@@ -187,34 +187,46 @@ __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
 }
 
 // Workgroup (s, h, cp) merges the chunks of (s, h) for latent columns
-// [kvl cp / 4, kvl (cp + 1) / 4): weights e^(m_k - m), normalized by the
-// merged exp sum.
+// [kvl cp / P, kvl (cp + 1) / P) (P = kMlaMergeParts): weights e^(m_k - m),
+// normalized by the merged exp sum.  Wave 0 forms the weights; the threads
+// split the chunks into 256 / ncols slices per column (so each issues a few
+// loads, not nsplit), and the slices are added in a fixed order.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   __shared__ float wk[kMlaMaxSplit];
+  __shared__ float part[256];
   __shared__ float inv_l;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int sh = blockIdx.x / kMlaMergeParts, cp = blockIdx.x % kMlaMergeParts;
   const float *pm = a.pm + (int64_t)sh * a.nsplit;
   const float *pl = a.pl + (int64_t)sh * a.nsplit;
-  if (tid == 0) {
+  if (tid < 64) {
     float m = -INFINITY;
-    for (int k = 0; k < a.nsplit; k++) m = fmaxf(m, pm[k]);
+    for (int k = lane; k < a.nsplit; k += 64) m = fmaxf(m, pm[k]);
+    m = wave_max_f32(m);
     float l = 0.f;
-    for (int k = 0; k < a.nsplit; k++) {
+    for (int k = lane; k < a.nsplit; k += 64) {
       const float w = pl[k] > 0.f ? expf(pm[k] - m) : 0.f;
       wk[k] = w;
       l = fmaf(w, pl[k], l);
     }
-    inv_l = 1.f / l;
+    l = wave_sum_f32(l);
+    if (lane == 0) inv_l = 1.f / l;
   }
   __syncthreads();
   const int c0 = a.kvl * cp / kMlaMergeParts, c1 = a.kvl * (cp + 1) / kMlaMergeParts;
-  const float *pc = a.pclat + (int64_t)sh * a.nsplit * a.kvl;
-  for (int i = c0 + tid; i < c1; i += 256) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < a.nsplit; k++) acc = fmaf(wk[k], pc[(int64_t)k * a.kvl + i], acc);
-    a.clat[(int64_t)sh * a.kvl + i] = acc * inv_l;
+  const int ncols = c1 - c0;              // kvl / P: 8 .. 256 (kvl % 64 == 0)
+  const int nsl = 256 / ncols;            // chunk slices per column
+  const int c = tid % ncols, sl = tid / ncols;
+  const float *pc = a.pclat + (int64_t)sh * a.nsplit * a.kvl + c0 + c;
+  float acc = 0.f;
+  if (sl < nsl)
+    for (int k = sl; k < a.nsplit; k += nsl) acc = fmaf(wk[k], pc[(int64_t)k * a.kvl], acc);
+  part[tid] = acc;
+  __syncthreads();
+  if (tid < ncols) {
+    float v = part[tid];
+    for (int q = 1; q < nsl; q++) v += part[q * ncols + tid];
+    a.clat[(int64_t)sh * a.kvl + c0 + tid] = v * inv_l;
   }
 }
 

@@ -263,7 +263,7 @@ constexpr int kMlaMaxSplit = 128;  // chunks per query: T <= 16384
 __host__ __device__ inline int mla_chunk_rows(int T) { return T <= 4096 ? 64 : 128; }
 constexpr int kMlaAbsorbParts = 8; // workgroups per (query, head) in the absorption
 constexpr int kMlaValueParts = 8;  // workgroups per (query, head) in the value projection
-constexpr int kMlaMergeParts = 4;  // workgroups per (query, head) in the chunk merge
+constexpr int kMlaMergeParts = 8;  // workgroups per (query, head) in the chunk merge
 constexpr int kMlaHeads = 4;       // heads per attention workgroup (8 measured slower: fewer workgroups, 171 VGPRs)
 struct MlaArgs {
   int S, T, H, kvl, nope, rope, vdim, nsplit, chunk;
