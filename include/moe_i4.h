@@ -277,7 +277,7 @@ size_t moe_mla_workspace_bytes(const moe_mla_config *cfg, int S, int T);
 
 /* q[S][H][nope + rope], kv_b as above, L[T][kvl], R[T][rope] (may be NULL
  * when rope == 0) -> ctx[S][H][vdim].  Launches: query absorption; per
- * cache chunk (64 or 128 rows) and four heads, the chunk softmax statistics
+ * cache chunk (32, 64 or 128 rows) and four heads, the chunk softmax statistics
  * and weighted latent sums; the merge of the chunks; the value
  * up-projection. */
 int moe_mla_decode(const moe_mla_config *cfg, const float *q, int S, const float *kv_b,

@@ -255,12 +255,13 @@ hipError_t launch_swiglu_b32_gateup(const SwigluB32Args &a, hipStream_t st);
 hipError_t launch_swiglu_b32_down(const SwigluB32Args &a, hipStream_t st);
 
 // MLA decode attention with weight absorption (mla.hip).
-// Cache rows per attention workgroup: 64 up to 4096 rows, 128 beyond (swept:
-// 64 rows is faster at 1024 rows, 128 at 16384, where merging 256 chunks per
-// (query, head) costs more than the longer chunks).
+// Cache rows per attention workgroup, swept at the GLM shape: 32 up to 2048
+// rows (40.6 against 45.5 us at 1024 rows with 64), 64 up to 4096 (73.8
+// against 83.6 with 32), 128 beyond (the merge of 256 chunks per (query,
+// head) costs more than the longer chunks).
 constexpr int kMlaMaxChunk = 128;
 constexpr int kMlaMaxSplit = 128;  // chunks per query: T <= 16384
-__host__ __device__ inline int mla_chunk_rows(int T) { return T <= 4096 ? 64 : 128; }
+__host__ __device__ inline int mla_chunk_rows(int T) { return T <= 2048 ? 32 : T <= 4096 ? 64 : 128; }
 constexpr int kMlaAbsorbParts = 8; // workgroups per (query, head) in the absorption
 constexpr int kMlaValueParts = 8;  // workgroups per (query, head) in the value projection
 constexpr int kMlaMergeParts = 8;  // workgroups per (query, head) in the chunk merge
