@@ -37,6 +37,7 @@ def test_quant_act_b32_bit_exact(S, D):
 
 @pytest.mark.parametrize("shape,S", [
     (TINY, 4),
+    (synth.Shape(D=256, I=32, E=1, K=1), 1),      # smallest shape: one hidden block
     (synth.Shape(D=1280, I=96, E=3, K=1), 3),     # partial chunks, three hidden blocks
     (synth.Shape(D=8192, I=1024, E=1, K=1), 2),   # four chunks per gate/up row
     (synth.Shape(D=256, I=8192, E=1, K=1), 2),    # four chunks per down row

@@ -40,6 +40,7 @@ def _device_i2(he: oracle.HostExpertI2, n: int, e_id: int, shape) -> moe.DeviceE
 
 @pytest.mark.parametrize("shape,S", [
     (TINY, 4),
+    (synth.Shape(D=256, I=64, E=1, K=1), 1),      # smallest shape
     (synth.Shape(D=1280, I=192, E=3, K=1), 3),    # partial chunks in both projections
     (synth.Shape(D=8192, I=1024, E=1, K=1), 2),   # two chunks per gate/up row
     (synth.Shape(D=256, I=8192, E=1, K=1), 2),    # two chunks per down row

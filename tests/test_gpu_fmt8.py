@@ -53,6 +53,7 @@ def _run(shape, S, he, e_id, seed=9):
 
 @pytest.mark.parametrize("shape,S", [
     (TINY, 4),
+    (synth.Shape(D=256, I=32, E=1, K=1), 1),      # smallest shape
     (synth.Shape(D=1280, I=96, E=3, K=1), 3),     # ragged chunks in both projections
     (synth.Shape(D=8192, I=1024, E=1, K=1), 2),   # widest rows of gate/up
     (synth.Shape(D=256, I=8192, E=1, K=1), 2),    # widest rows of down

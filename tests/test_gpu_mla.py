@@ -24,6 +24,7 @@ def _inputs(H, kvl, nope, rope, vdim, S, T, seed):
 
 @pytest.mark.parametrize("dims,S,T", [
     ((4, 64, 24, 8, 32), 1, 1),
+    ((4, 64, 24, 8, 32), 4, 4),             # T = S: query s sees s + 1 rows
     ((4, 64, 24, 8, 32), 3, 50),
     ((4, 128, 24, 8, 40), 2, 300),          # three chunks, the last one partial
     ((3, 64, 16, 0, 24), 2, 129),           # no rotary part, heads not a multiple of 8
