@@ -62,6 +62,7 @@ def lib():
         L.moe_ref_pack_int2.argtypes = [vp, i32, i32, vp, vp]
         L.moe_ref_quant_act_b32.argtypes = [vp, i32, i32, vp, vp]
         L.moe_ref_mla_decode.argtypes = [vp, vp, i32, vp, vp, vp, i32, vp]
+        L.moe_ref_layer_forward_shared_i8.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint]
         L.moe_ref_expert_swiglu_i4_b32.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp]
         L.moe_ref_unpack_int2.argtypes = [vp, i32, i32, vp]
         L.moe_ref_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
@@ -377,6 +378,20 @@ def layer_forward(layer: HostLayer, x: np.ndarray, out: np.ndarray | None = None
     L, keep = layer.cstruct()
     _check(lib().moe_ref_layer_forward(ctypes.byref(layer.cfg), ctypes.byref(L), _p(x), S, _p(out),
                                        flags), "layer_forward")
+    return out
+
+
+def layer_forward_shared_i8(layer: HostLayer, shared8: HostExpertI8, x: np.ndarray,
+                            out: np.ndarray | None = None, flags: int = 0):
+    """The per-token block with the shared expert in the int8 format."""
+    x = _c(x, np.float32)
+    S = x.shape[0]
+    out = np.zeros((S, layer.cfg.D), np.float32) if out is None else out
+    L, keep = layer.cstruct()
+    e8 = shared8.cstruct()
+    _check(lib().moe_ref_layer_forward_shared_i8(ctypes.byref(layer.cfg), ctypes.byref(L),
+                                                 ctypes.byref(e8), _p(x), S, _p(out), flags),
+           "layer_forward_shared_i8")
     return out
 
 

@@ -501,9 +501,12 @@ static void combine_row(const moe_ref_config *cfg, const float *w, int keff, con
   }
 }
 
-int moe_ref_layer_forward(const moe_ref_config *cfg, const moe_ref_layer *layer, const float *x,
-                          int S, float *out, unsigned flags) {
-  if (!layer_ok(cfg, layer) || !x || !out || S < 1) return -1;
+/* shared8 (optional): the shared expert in the int8 format, used in place of
+ * layer->shared. */
+static int layer_forward_impl(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                              const moe_ref_expert_i8 *shared8, const float *x, int S, float *out,
+                              unsigned flags) {
+  if (!x || !out || S < 1) return -1;
   const int D = cfg->D, K = cfg->K, slots = cfg->K + cfg->n_shared;
   int32_t idx[64];
   float w[64];
@@ -521,13 +524,32 @@ int moe_ref_layer_forward(const moe_ref_config *cfg, const moe_ref_layer *layer,
       rc = moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, &layer->experts[idx[k]],
                                     stage + (int64_t)k * D, NULL, NULL, NULL, NULL);
     if (rc == 0 && cfg->n_shared == 1)
-      rc = moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, layer->shared, stage + (int64_t)K * D, NULL,
-                                    NULL, NULL, NULL);
+      rc = shared8 ? moe_ref_expert_swiglu_i8(cfg, xq, &sxs, 1, shared8, stage + (int64_t)K * D,
+                                              NULL, NULL, NULL, NULL)
+                   : moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, layer->shared,
+                                              stage + (int64_t)K * D, NULL, NULL, NULL, NULL);
     if (rc == 0) combine_row(cfg, w, keff, stage, out + (int64_t)s * D, flags);
   }
   free(xq);
   free(stage);
   return rc;
+}
+
+int moe_ref_layer_forward(const moe_ref_config *cfg, const moe_ref_layer *layer, const float *x,
+                          int S, float *out, unsigned flags) {
+  if (!layer_ok(cfg, layer)) return -1;
+  return layer_forward_impl(cfg, layer, NULL, x, S, out, flags);
+}
+
+int moe_ref_layer_forward_shared_i8(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                    const moe_ref_expert_i8 *shared8, const float *x, int S,
+                                    float *out, unsigned flags) {
+  if (!cfg || cfg->n_shared != 1 || !shared8) return -1;
+  if (!q8mat_ok(&shared8->gate) || !q8mat_ok(&shared8->up) || !q8mat_ok(&shared8->down)) return -1;
+  moe_ref_config c0 = *cfg;
+  c0.n_shared = 0;  /* the routed experts and the router are checked as usual */
+  if (!layer_ok(&c0, layer)) return -1;
+  return layer_forward_impl(cfg, layer, shared8, x, S, out, flags);
 }
 
 int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *layer,

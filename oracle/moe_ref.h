@@ -206,6 +206,14 @@ int moe_ref_mla_decode(const moe_ref_mla_config *c, const float *q, int S, const
 int moe_ref_layer_forward(const moe_ref_config *cfg, const moe_ref_layer *layer, const float *x,
                           int S, float *out, unsigned flags);
 
+/* moe_ref_layer_forward with the shared expert in the int8 format (the
+ * article keeps the shared experts at higher precision than the routed ones:
+ * they belong to its quantization-sensitive dense class).  cfg->n_shared must
+ * be 1; layer->shared is not read. */
+int moe_ref_layer_forward_shared_i8(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                    const moe_ref_expert_i8 *shared8, const float *x, int S,
+                                    float *out, unsigned flags);
+
 /* Same block through the section 11 unique-expert union: the experts selected
  * by any token are visited once each in order of first appearance, each one
  * applied to all its rows; per-(token, slot) results are staged and combined

@@ -154,3 +154,42 @@ def test_int8_expert_is_closer_to_float_than_int4():
     yf = (gg / (1.0 + np.exp(-gg)) * uu) @ Dn.T
     rms = lambda a: np.sqrt((a ** 2).mean())
     assert rms(y8 - yf) < 0.5 * rms(y4 - yf)
+
+
+def test_layer_with_int8_shared_on_int4_codes_equals_int4_layer():
+    # the shared expert's int4 codes widened to int8 (same scales): the
+    # layer with the int8 shared expert gives the int4 layer bit for bit,
+    # plain and accumulating
+    from oracle.layers import LazyLayer
+    shape = TINY
+    b = synth.router_b_uniform(2, shape, 0)
+    layer = LazyLayer(2, shape, 0, b)
+    e4 = layer.shared
+    shared8 = _int4_as_int8(e4, shape)
+    x = synth.activations(2, 5, shape.D)
+    layer.ensure(range(shape.E))
+    ref = oracle.layer_forward(layer, x)
+    got = oracle.layer_forward_shared_i8(layer, shared8, x)
+    assert np.array_equal(ref, got)
+    base = synth.activations(3, 5, shape.D)
+    ref_acc = oracle.layer_forward(layer, x, out=base.copy(), flags=1)
+    got_acc = oracle.layer_forward_shared_i8(layer, shared8, x, out=base.copy(), flags=1)
+    assert np.array_equal(ref_acc, got_acc)
+
+
+def test_layer_with_int8_shared_differs_from_int4_by_the_shared_term():
+    # a genuinely int8 shared expert changes only the shared term: the
+    # difference to the int4 layer is the difference of the two shared
+    # experts' outputs on the token's codes (up to float rounding)
+    from oracle.layers import LazyLayer
+    shape = TINY
+    layer = LazyLayer(4, shape, 0, synth.router_b_uniform(4, shape, 0))
+    g, u, d = synth.host_expert_f32(4, shape, 0, synth.SHARED)
+    shared8 = oracle.HostExpertI8.from_f32(g, u, d)
+    x = synth.activations(4, 3, shape.D)
+    layer.ensure(range(shape.E))
+    diff = oracle.layer_forward_shared_i8(layer, shared8, x) - oracle.layer_forward(layer, x)
+    xq, sx = oracle.quant_act_i8(x)
+    cfg = config_of(shape)
+    want = oracle.expert_swiglu_i8(cfg, xq, sx, shared8)["y"] - oracle.expert_swiglu(cfg, xq, sx, layer.shared)["y"]
+    assert np.abs(diff - want).max() <= 1e-5 * max(1.0, np.abs(want).max())
