@@ -414,6 +414,60 @@ def bench_fmt8(layer, steps: int = 512, n8: int = 8, n4: int = 16, n2: int = 32)
     return res
 
 
+def bench_shared_i8(layers, x, steps: int = 512):
+    """Per-token decode with the shared expert in the int8 format
+    (moe_layer_forward_shared_i8): the headline decode's cold layer replicas
+    and tokens, each replica with its own int8 shared expert; plain stream
+    launches between events.  Weight bytes per token: the router, 8 int4
+    routed experts and one int8 shared expert."""
+    import torch
+
+    import int4_expert_gemv_moe_amd as moe
+    import synth
+    from synth.device_layers import build_device_experts_i8
+
+    T, R = x.shape[0], len(layers)
+    lib = moe.lib()
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    sh8 = build_device_experts_i8(1, synth.GLM, 0, R)
+    views = [moe.DeviceExpertsI8(sh8.gate_q[r:r + 1], sh8.gate_s[r:r + 1], sh8.up_q[r:r + 1],
+                                 sh8.up_s[r:r + 1], sh8.down_q[r:r + 1], sh8.down_s[r:r + 1])
+             for r in range(R)]
+    s8 = [v.cstruct() for v in views]
+    ls = [l.cstruct() for l in layers]
+    cfg = layers[0].cfg
+    ws = moe.Workspace(cfg, 1, moe.WS_SHARED8)
+    out = torch.empty(1, D, dtype=torch.float32, device="cuda")
+    xp = [ctypes.c_void_p(x[t].data_ptr()) for t in range(T)]
+    op = ctypes.c_void_p(out.data_ptr())
+    cref = ctypes.byref(cfg)
+
+    def run(n):
+        rc = 0
+        for i in range(n):
+            r = i % R
+            rc |= lib.moe_layer_forward_shared_i8(cref, ctypes.byref(ls[r]), ctypes.byref(s8[r]),
+                                                  xp[i % T], 1, op, 0, ws.ptr, ws.nbytes, st)
+        if rc:
+            raise moe.MoeError(f"moe_layer_forward_shared_i8 failed ({rc})")
+
+    run(64)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run(steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = K * EXPERT_BYTES + EXPERT_I8_BYTES + ROUTER_BYTES + 2 * D * 4
+    log(f"decode with int8 shared expert: {us:.2f} us/token")
+    return {"workload": "GLM-shape MoE layer decode, 1 token/step, shared expert in the int8 "
+                        "format (moe_layer_forward_shared_i8), 8 cold layer replicas",
+            "steps": steps, "us_per_token": round(us, 3), "bytes_per_token": int(nbytes),
+            "GBps": round(nbytes / us / 1e3, 1),
+            "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+
+
 def bench_mla(contexts=(1024, 4096, 16384), steps: int = 200):
     """Section 09 absorbed MLA decode at the GLM shape (64 heads, latent 512,
     nope 192, rope 64, value 256; float32), one query per call over a cache of
@@ -562,7 +616,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the verify, prefill and 48-layer stack measurements")
-    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered", "topp", "fmt8", "mla"],
+    ap.add_argument("--only", choices=["verify", "prefill", "stack", "tiered", "topp", "fmt8", "mla",
+                                       "shared8"],
                     help="run only that secondary measurement and print its record (for profiling)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay pass (value then comes from the stream pass); "
@@ -602,10 +657,11 @@ def main():
             rec = bench_stack()
         elif args.only == "mla":
             rec = bench_mla()
-        elif args.only == "topp":
+        elif args.only in ("topp", "shared8"):
             reps = [build_device_layer(r, synth.GLM, r, synth.router_b_uniform(r, synth.GLM, r))
                     for r in range(args.replicas)]
-            rec = bench_topp(reps, torch.from_numpy(synth.activations(7, args.tokens, D)).cuda())
+            fn = bench_topp if args.only == "topp" else bench_shared_i8
+            rec = fn(reps, torch.from_numpy(synth.activations(7, args.tokens, D)).cuda())
         else:
             layer = build_device_layer(0, synth.GLM, 0, synth.router_b_uniform(0, synth.GLM, 0))
             rec = {"verify": bench_verify, "prefill": bench_prefill,
@@ -749,6 +805,10 @@ def main():
             secondary["topp_decode"] = bench_topp(layers, x)
         except Exception as exc:  # reported, the headline line is still printed
             secondary["topp_decode"] = {"error": f"{type(exc).__name__}: {exc}"}
+        try:
+            secondary["shared_int8_decode"] = bench_shared_i8(layers, x)
+        except Exception as exc:
+            secondary["shared_int8_decode"] = {"error": f"{type(exc).__name__}: {exc}"}
         for key, fn in (("verify_64_zipf", bench_verify), ("prefill_2048", bench_prefill),
                         ("tiered_decode", bench_tiered), ("expert_weight_formats", bench_fmt8)):
             try:

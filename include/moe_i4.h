@@ -152,7 +152,8 @@ const char *moe_status_str(int status);
 
 /* Workspace bytes needed by a call with S tokens.  which: 0 = moe_layer_forward,
  * 1 = moe_layer_forward_batch, 2 = moe_expert_swiglu_i4, 3 = moe_router_topk,
- * 4 = moe_expert_swiglu_i8, moe_expert_swiglu_i2 and moe_expert_swiglu_i4_b32.
+ * 4 = moe_expert_swiglu_i8, moe_expert_swiglu_i2 and moe_expert_swiglu_i4_b32,
+ * 5 = moe_layer_forward_shared_i8 (0 unless n_shared == 1).
  * Returns 0 for invalid arguments. */
 size_t moe_workspace_bytes(const moe_config *cfg, int S, int which);
 
@@ -283,6 +284,20 @@ size_t moe_mla_workspace_bytes(const moe_mla_config *cfg, int S, int T);
 int moe_mla_decode(const moe_mla_config *cfg, const float *q, int S, const float *kv_b,
                    const float *L, const float *R, int T, float *ctx, void *ws, size_t ws_bytes,
                    hipStream_t stream);
+
+/* moe_layer_forward with the shared expert in the int8 format (the article
+ * keeps shared experts in its quantization-sensitive dense class, at higher
+ * precision than the routed int4 experts): out[s] = sum_k w_k y_k + y_shared
+ * with y_shared from the int8 expert *shared8 (host struct, expert 0 of its
+ * stacks); layer->shared is not read.  cfg->n_shared must be 1 (MOE_ESHAPE);
+ * flags: MOE_F_ACCUMULATE only (MOE_EINVAL otherwise); x 16-byte aligned.
+ * Launches: the per-token path without a shared expert, the tokens'
+ * quantization, the int8 expert's gate/up and down (the down adds into out),
+ * so out = (out +) routed sum, then + y_shared.  Workspace:
+ * moe_workspace_bytes(cfg, S, 5). */
+int moe_layer_forward_shared_i8(const moe_config *cfg, const moe_layer *layer,
+                                const moe_experts_i8 *shared8, const float *x, int S, float *out,
+                                unsigned flags, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The block, one token at a time (each token reads its own K experts):
  * route, quantize, run the K routed experts and the shared expert, and

@@ -150,7 +150,9 @@ __global__ __launch_bounds__(256) void dn8_kernel(Swiglu8Args a) {
         for (int c = 0; c < NCH; c++) acc = dot16_i8(w[r][c], hv[c], acc);
         acc = wave_sum_i32(acc);
         if (lane == r && d0 + r < a.D) {
-          a.y[s * a.D + d0 + r] = ((float)acc * dsc[r]) * sh;
+          const float v = ((float)acc * dsc[r]) * sh;
+          float *yp = a.y + s * a.D + d0 + r;
+          *yp = a.accumulate ? *yp + v : v;
           if (a.acc_d) a.acc_d[s * a.D + d0 + r] = acc;
         }
       }

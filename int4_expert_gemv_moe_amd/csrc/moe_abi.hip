@@ -48,7 +48,18 @@ int check_cfg(const moe_config *c) {
   return MOE_OK;
 }
 
-enum Which { W_FWD = 0, W_BATCH = 1, W_SWIGLU = 2, W_ROUTER = 3, W_SWIGLU8 = 4 };
+enum Which { W_FWD = 0, W_BATCH = 1, W_SWIGLU = 2, W_ROUTER = 3, W_SWIGLU8 = 4, W_SHARED8 = 5 };
+
+// Workspace of moe_layer_forward_shared_i8: the per-token path's (without a
+// shared expert), then the token codes and scales and the int8 expert's h.
+size_t carve(const moe_config &c, int S, int which, char *base, struct Work *w);
+size_t shared8_bytes(const moe_config &c, int S, size_t *fwd) {
+  moe_config c0 = c;
+  c0.n_shared = 0;
+  const size_t f = carve(c0, S, W_FWD, nullptr, nullptr);
+  if (fwd) *fwd = f;
+  return f + align_up((size_t)S * c.D) + align_up((size_t)S * 4) + align_up((size_t)S * c.I * 4);
+}
 
 // Workgroup counts of the per-token path (rows of a phase are split evenly
 // over its workgroups).  MOE_DECODE_BLOCKS="a,b,c,d" overrides them for
@@ -303,7 +314,8 @@ const char *moe_status_str(int status) {
 }
 
 size_t moe_workspace_bytes(const moe_config *cfg, int S, int which) {
-  if (check_cfg(cfg) != MOE_OK || S < 1 || which < 0 || which > 4) return 0;
+  if (check_cfg(cfg) != MOE_OK || S < 1 || which < 0 || which > 5) return 0;
+  if (which == W_SHARED8) return cfg->n_shared == 1 ? shared8_bytes(*cfg, S, nullptr) : 0;
   return carve(*cfg, S, which, nullptr, nullptr);
 }
 
@@ -947,5 +959,55 @@ int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s
 }
 
 int moe_stream_read_sink_words(void) { return stream_read_sink_words(); }
+
+}  // extern "C"
+
+extern "C" {
+
+int moe_layer_forward_shared_i8(const moe_config *cfg, const moe_layer *layer,
+                                const moe_experts_i8 *shared8, const float *x, int S, float *out,
+                                unsigned flags, void *ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->n_shared != 1) return MOE_ESHAPE;
+  if (!shared8 || !x || !out || !ws || S < 1) return MOE_EINVAL;
+  if (flags & ~MOE_F_ACCUMULATE) return MOE_EINVAL;
+  MOE_TRY(check_experts_i8(*shared8));
+  if (!aligned16(x)) return MOE_EALIGN;
+  size_t fwd = 0;
+  if (ws_bytes < shared8_bytes(*cfg, S, &fwd)) return MOE_EWORKSPACE;
+  moe_config c0 = *cfg;
+  c0.n_shared = 0;
+  // the router and the routed experts through the per-token path (it checks
+  // the rest of the arguments and the device)
+  MOE_TRY(layer_forward_impl(&c0, layer, x, S, nullptr, nullptr, out, flags, nullptr, ws, fwd,
+                             stream));
+  char *base = static_cast<char *>(ws) + fwd;
+  int8_t *xq = reinterpret_cast<int8_t *>(base);
+  float *sx = reinterpret_cast<float *>(base + align_up((size_t)S * cfg->D));
+  float *h = reinterpret_cast<float *>(base + align_up((size_t)S * cfg->D) + align_up((size_t)S * 4));
+  // the tokens' codes (section 12 quantization, the same bits as the routed path's)
+  QuantArgs qa{};
+  qa.xf = x;
+  qa.D = cfg->D;
+  qa.xq_nat = xq;
+  qa.sx = sx;
+  MOE_TRY_HIP(launch_quant(qa, S, stream));
+  // the shared expert, added to the routed sum
+  Swiglu8Args a{};
+  a.xq = xq;
+  a.sx = sx;
+  a.S = S;
+  a.D = cfg->D;
+  a.I = cfg->I;
+  q8_rows(shared8->gate, cfg->I, cfg->D, 0, &a.G, &a.gs);
+  q8_rows(shared8->up, cfg->I, cfg->D, 0, &a.U, &a.us);
+  q8_rows(shared8->down, cfg->D, cfg->I, 0, &a.Dn, &a.ds);
+  a.h = h;
+  a.y = out;
+  a.accumulate = 1;
+  MOE_TRY_HIP(launch_swiglu8_gateup(a, stream));
+  MOE_TRY_HIP(launch_swiglu8_down(a, stream));
+  return MOE_OK;
+}
 
 }  // extern "C"

@@ -201,6 +201,7 @@ struct Swiglu8Args {
   float *sh_out;           // optional [S]
   float *y;                // [S][D]
   int32_t *acc_d;          // optional [S][D]
+  int accumulate;          // y += result instead of y = result
 };
 
 // Packed int2 weights (fmt2.hip): four codes per byte, code + 2, column
