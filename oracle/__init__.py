@@ -68,6 +68,11 @@ def lib():
         L.moe_ref_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_ref_layer_forward.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint]
         L.moe_ref_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, vp, vp]
+        L.moe_ref_layer_forward_routed.argtypes = [vp, vp, vp, i32, vp, vp, vp, ctypes.c_uint]
+        L.moe_ref_layer_forward_batch_routed.argtypes = [vp, vp, vp, i32, vp, vp, vp, ctypes.c_uint,
+                                                         vp, vp]
+        L.moe_ref_layer_forward_batch_shared_i8.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint,
+                                                            vp, vp]
         L.moe_ref_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp]
         L.moe_ref_expert_keff.argtypes = [vp, i32, f32]
         L.moe_ref_expert_get.argtypes = [vp, vp, i32, vp, vp, vp, vp, ctypes.c_int32, vp]
@@ -410,6 +415,57 @@ def layer_forward_batch(layer: HostLayer, x: np.ndarray, out: np.ndarray | None 
                                              flags, _p(idx), _p(w), _p(uniq), ctypes.byref(nu)),
            "layer_forward_batch")
     return out, idx, w, uniq[: nu.value].copy()
+
+
+def layer_forward_routed(layer: HostLayer, x: np.ndarray, idx: np.ndarray, w: np.ndarray,
+                         out: np.ndarray | None = None, flags: int = 0):
+    """The per-token block on the given routing idx [S][K] (in [0, E)), w [S][K]."""
+    x = _c(x, np.float32)
+    S = x.shape[0]
+    cfg = layer.cfg
+    idx = _c(idx, np.int32).reshape(S, cfg.K)
+    w = _c(w, np.float32).reshape(S, cfg.K)
+    out = np.zeros((S, cfg.D), np.float32) if out is None else out
+    L, keep = layer.cstruct()
+    _check(lib().moe_ref_layer_forward_routed(ctypes.byref(cfg), ctypes.byref(L), _p(x), S, _p(idx),
+                                              _p(w), _p(out), flags), "layer_forward_routed")
+    return out
+
+
+def layer_forward_batch_routed(layer: HostLayer, x: np.ndarray, idx: np.ndarray, w: np.ndarray,
+                               out: np.ndarray | None = None, flags: int = 0):
+    """The unique-expert union on the given routing: (out, union in first-appearance order)."""
+    x = _c(x, np.float32)
+    S = x.shape[0]
+    cfg = layer.cfg
+    idx = _c(idx, np.int32).reshape(S, cfg.K)
+    w = _c(w, np.float32).reshape(S, cfg.K)
+    out = np.zeros((S, cfg.D), np.float32) if out is None else out
+    uniq = np.empty(cfg.E, np.int32)
+    nu = ctypes.c_int32(0)
+    L, keep = layer.cstruct()
+    _check(lib().moe_ref_layer_forward_batch_routed(ctypes.byref(cfg), ctypes.byref(L), _p(x), S,
+                                                    _p(idx), _p(w), _p(out), flags, _p(uniq),
+                                                    ctypes.byref(nu)), "layer_forward_batch_routed")
+    return out, uniq[: nu.value].copy()
+
+
+def layer_forward_batch_shared_i8(layer: HostLayer, shared8: HostExpertI8, x: np.ndarray,
+                                  out: np.ndarray | None = None, flags: int = 0):
+    """The unique-expert union with the shared expert in the int8 format."""
+    x = _c(x, np.float32)
+    S = x.shape[0]
+    cfg = layer.cfg
+    out = np.zeros((S, cfg.D), np.float32) if out is None else out
+    uniq = np.empty(cfg.E, np.int32)
+    nu = ctypes.c_int32(0)
+    L, keep = layer.cstruct()
+    e8 = shared8.cstruct()
+    _check(lib().moe_ref_layer_forward_batch_shared_i8(ctypes.byref(cfg), ctypes.byref(L),
+                                                       ctypes.byref(e8), _p(x), S, _p(out), flags,
+                                                       _p(uniq), ctypes.byref(nu)),
+           "layer_forward_batch_shared_i8")
+    return out, uniq[: nu.value].copy()
 
 
 def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-5) -> np.ndarray:

@@ -36,33 +36,41 @@ int moe_ref_expert_keff(const float *w, int K, float p) {
 
 /* ---- section 06: int4 weight container ------------------------------------ */
 
+/* Codes of one row: the row's scale is its largest magnitude over qmax,
+ * floored at floor_s; sections 05 and 06 divide each weight by that scale,
+ * section 12 multiplies each activation by its reciprocal.  Every code is
+ * rounded half to even and clamped into [lo, hi]. */
+static float row_absmax(const float *v, int n) {
+  float m = 0.f;
+  for (int i = 0; i < n; i++)
+    if (fabsf(v[i]) > m) m = fabsf(v[i]); /* a NaN never compares greater */
+  return m;
+}
+
+static float row_scale(float amax, int qmax, float floor_s) {
+  const float s = amax / (float)qmax;
+  return s < floor_s ? floor_s : s;
+}
+
+static int clamp_code(long v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : (int)v); }
+
 int moe_ref_pack_int4(const float *w, int O, int C, uint8_t *q4, float *scale) {
   if (!w || !q4 || !scale || O < 1 || C < 1) return -1;
-  const int qmax = 7, rb = (C + 1) / 2;
+  /* the section 06 container is the section 05 quantizer at 4 bits, then two
+   * codes per byte as code + 8 (even column low) */
+  int8_t *codes = (int8_t *)malloc((size_t)O * C);
+  if (!codes) return -2;
+  moe_ref_quantize_rows(w, O, C, 4, codes, scale);
+  const int rb = (C + 1) / 2;
   for (int o = 0; o < O; o++) {
-    const float *wr = w + (int64_t)o * C;
-    float amax = 0.f;
-    for (int i = 0; i < C; i++) {
-      float a = fabsf(wr[i]);
-      if (a > amax) amax = a;
-    }
-    float s = amax / (float)qmax;
-    if (s < 1e-8f) s = 1e-8f;
-    scale[o] = s;
-    uint8_t *qr = q4 + (int64_t)o * rb;
-    for (int i = 0; i < C; i += 2) {
-      int v0 = (int)lrintf(wr[i] / s);
-      if (v0 > qmax) v0 = qmax;
-      if (v0 < -8) v0 = -8;
-      int v1 = 0;
-      if (i + 1 < C) {
-        v1 = (int)lrintf(wr[i + 1] / s);
-        if (v1 > qmax) v1 = qmax;
-        if (v1 < -8) v1 = -8;
-      }
-      qr[i >> 1] = (uint8_t)((v0 + 8) | ((v1 + 8) << 4));
+    const int8_t *cr = codes + (int64_t)o * C;
+    for (int j = 0; j < rb; j++) {
+      const int lo = cr[2 * j] + 8;
+      const int hi = (2 * j + 1 < C ? cr[2 * j + 1] : 0) + 8;
+      q4[(int64_t)o * rb + j] = (uint8_t)(lo | (hi << 4));
     }
   }
+  free(codes);
   return 0;
 }
 
@@ -83,21 +91,10 @@ int moe_ref_unpack_int4(const uint8_t *q4, int O, int C, int8_t *q) {
 /* ---- section 12: activation quantization and integer dots ---------------- */
 
 float moe_ref_quant_row_i8(const float *x, int n, int8_t *q) {
-  float amax = 0.f;
-  for (int i = 0; i < n; i++) {
-    float a = fabsf(x[i]);
-    if (a > amax) amax = a;
-  }
-  float s = amax / 127.f;
-  if (s < 1e-12f) s = 1e-12f;
-  float inv = 1.f / s;
-  for (int i = 0; i < n; i++) {
-    long v = lrintf(x[i] * inv);
-    /* |x * inv| <= 127 up to rounding, so this clamp never changes a value. */
-    if (v > 127) v = 127;
-    if (v < -127) v = -127;
-    q[i] = (int8_t)v;
-  }
+  const float s = row_scale(row_absmax(x, n), 127, 1e-12f);
+  const float inv = 1.f / s;
+  /* |x * inv| <= 127 up to rounding, so the clamp never changes a code */
+  for (int i = 0; i < n; i++) q[i] = (int8_t)clamp_code(lrintf(x[i] * inv), -127, 127);
   return s;
 }
 
@@ -137,34 +134,45 @@ int32_t moe_ref_dot_i4_i8(const uint8_t *q4row, const int8_t *x, int C) {
 
 static float sigmoid_ref(float v) { return 1.f / (1.f + expf(-v)); }
 
-/* Top-K by repeated argmax over the experts not yet taken.  An expert is a
- * candidate when choice > -1e30 (the article's initial best value; a NaN is
- * never greater, so NaN choices are never picked).  If fewer than K experts are
- * candidates, the remaining slots take the lowest-numbered experts not yet
- * taken (the article leaves this case undefined). */
-static void topk_row(const float *choice, const float *sig, int E, int K, float scale,
-                     int32_t *idx, float *w) {
-  for (int kk = 0; kk < K; kk++) {
-    int best = -1;
-    float bv = -1e30f;
-    for (int e = 0; e < E; e++) {
-      int taken = 0;
-      for (int j = 0; j < kk; j++)
-        if (idx[j] == e) { taken = 1; break; }
-      if (!taken && choice[e] > bv) { bv = choice[e]; best = e; }
-    }
-    if (best < 0) {
-      for (int e = 0; e < E && best < 0; e++) {
-        int taken = 0;
-        for (int j = 0; j < kk; j++)
-          if (idx[j] == e) { taken = 1; break; }
-        if (!taken) best = e;
-      }
-    }
-    idx[kk] = best;
-    w[kk] = sig[best];
+/* Top-K selection.  Each pass of the section 11 rule takes the largest
+ * choice among the experts not yet taken, scanning the experts in ascending
+ * order with a strict comparison, so the K passes return the experts ranked
+ * by (choice descending, index ascending).  The listing's running best starts
+ * at -1e30 and a NaN never compares greater, so only choices > -1e30 are
+ * candidates; if fewer than K experts are candidates, the remaining passes
+ * find none and (a reading: the article leaves this case undefined) take the
+ * lowest-numbered experts not yet taken.  The ranking below sorts by exactly
+ * that order: candidates first, by choice then index, then the others by
+ * index. */
+typedef struct {
+  float choice;
+  int expert;
+  int candidate;
+} ranked;
+
+static int rank_order(const void *pa, const void *pb) {
+  const ranked *a = (const ranked *)pa, *b = (const ranked *)pb;
+  if (a->candidate != b->candidate) return b->candidate - a->candidate;
+  if (a->candidate && a->choice != b->choice) return a->choice > b->choice ? -1 : 1;
+  return a->expert - b->expert;
+}
+
+static int select_top_k(const float *choice, const float *sig, int E, int K, float scale,
+                        int32_t *idx, float *w) {
+  ranked *r = (ranked *)malloc((size_t)E * sizeof(ranked));
+  if (!r) return -2;
+  for (int e = 0; e < E; e++) {
+    r[e].choice = choice[e];
+    r[e].expert = e;
+    r[e].candidate = choice[e] > -1e30f;
   }
-  for (int kk = 0; kk < K; kk++) w[kk] *= scale;
+  qsort(r, (size_t)E, sizeof(ranked), rank_order);
+  for (int k = 0; k < K; k++) {
+    idx[k] = r[k].expert;
+    w[k] = sig[idx[k]] * scale; /* the unbiased sigmoid times the routed scale */
+  }
+  free(r);
+  return 0;
 }
 
 int moe_ref_router_topk(const moe_ref_config *cfg, const float *x, int S, const float *router_w,
@@ -174,8 +182,8 @@ int moe_ref_router_topk(const moe_ref_config *cfg, const float *x, int S, const 
   const int D = cfg->D, E = cfg->E, K = cfg->K;
   float *sig = (float *)malloc((size_t)E * sizeof(float));
   float *ch = (float *)malloc((size_t)E * sizeof(float));
-  if (!sig || !ch) { free(sig); free(ch); return -2; }
-  for (int s = 0; s < S; s++) {
+  int rc = (sig && ch) ? 0 : -2;
+  for (int s = 0; s < S && rc == 0; s++) {
     const float *xs = x + (int64_t)s * D;
     for (int e = 0; e < E; e++) {
       const float *we = router_w + (int64_t)e * D;
@@ -187,11 +195,11 @@ int moe_ref_router_topk(const moe_ref_config *cfg, const float *x, int S, const 
       ch[e] = sig[e] + router_b[e];
       if (choice) choice[(int64_t)s * E + e] = ch[e];
     }
-    topk_row(ch, sig, E, K, cfg->routed_scale, idx + (int64_t)s * K, w + (int64_t)s * K);
+    rc = select_top_k(ch, sig, E, K, cfg->routed_scale, idx + (int64_t)s * K, w + (int64_t)s * K);
   }
   free(sig);
   free(ch);
-  return 0;
+  return rc;
 }
 
 /* ---- sections 11 and 12: one SwiGLU expert ---------------------------------- */
@@ -247,21 +255,10 @@ int moe_ref_quantize_rows(const float *w, int O, int C, int bits, int8_t *q, flo
   const int qmax = (1 << (bits - 1)) - 1;
   for (int o = 0; o < O; o++) {
     const float *wr = w + (int64_t)o * C;
-    float amax = 0.f;
-    for (int i = 0; i < C; i++) {
-      float a = fabsf(wr[i]);
-      if (a > amax) amax = a;
-    }
-    float s = amax / (float)qmax;
-    if (s < 1e-8f) s = 1e-8f;
+    const float s = row_scale(row_absmax(wr, C), qmax, 1e-8f);
     scale[o] = s;
-    int8_t *qr = q + (int64_t)o * C;
-    for (int i = 0; i < C; i++) {
-      long v = lrintf(wr[i] / s);
-      if (v > qmax) v = qmax;
-      if (v < -qmax - 1) v = -qmax - 1;
-      qr[i] = (int8_t)v;
-    }
+    for (int i = 0; i < C; i++)
+      q[(int64_t)o * C + i] = (int8_t)clamp_code(lrintf(wr[i] / s), -qmax - 1, qmax);
   }
   return 0;
 }
@@ -479,56 +476,92 @@ int moe_ref_mla_decode(const moe_ref_mla_config *c, const float *q, int S, const
 
 /* ---- the block ------------------------------------------------------------ */
 
-static int layer_ok(const moe_ref_config *cfg, const moe_ref_layer *L) {
-  if (bad_cfg(cfg) || !L || !L->router_w || !L->router_b || !L->experts) return 0;
+static int layer_ok(const moe_ref_config *cfg, const moe_ref_layer *L, int need_router) {
+  if (bad_cfg(cfg) || !L || !L->experts) return 0;
+  if (need_router && (!L->router_w || !L->router_b)) return 0;
   if (cfg->n_shared == 1 && !L->shared) return 0;
   return 1;
 }
 
+static int routing_ok(const moe_ref_config *cfg, const int32_t *idx, const float *w, int S) {
+  if (!idx || !w) return 0;
+  for (int64_t p = 0; p < (int64_t)S * cfg->K; p++)
+    if (idx[p] < 0 || idx[p] >= cfg->E) return 0;
+  return 1;
+}
+
+/* Section 11's combine for one token: the first keff routed results weighted
+ * by their combine weights, added in slot order starting from 0, then the
+ * shared expert's result with weight 1 (a reading: the article's listing
+ * shows the routed sum only).  stage holds K (+1 shared) rows of D floats. */
 static void combine_row(const moe_ref_config *cfg, const float *w, int keff, const float *stage,
                         float *out, unsigned flags) {
-  /* stage holds K (+1 shared) rows of D floats for one token; the first keff
-   * routed rows take part */
   const int D = cfg->D, K = cfg->K;
   for (int d = 0; d < D; d++) {
     float acc = 0.f;
     for (int k = 0; k < keff; k++) acc += w[k] * stage[(int64_t)k * D + d];
     if (cfg->n_shared == 1) acc += stage[(int64_t)K * D + d];
-    if (flags & MOE_REF_ACCUMULATE)
-      out[d] = out[d] + acc;
-    else
-      out[d] = acc;
+    out[d] = (flags & MOE_REF_ACCUMULATE) ? out[d] + acc : acc;
   }
 }
 
-/* shared8 (optional): the shared expert in the int8 format, used in place of
- * layer->shared. */
-static int layer_forward_impl(const moe_ref_config *cfg, const moe_ref_layer *layer,
-                              const moe_ref_expert_i8 *shared8, const float *x, int S, float *out,
-                              unsigned flags) {
+/* The shared expert on S quantized rows, in the int4 format or (shared8 set)
+ * the int8 one. */
+static int shared_rows(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                       const moe_ref_expert_i8 *shared8, const int8_t *xq, const float *sx, int S,
+                       float *y) {
+  return shared8 ? moe_ref_expert_swiglu_i8(cfg, xq, sx, S, shared8, y, NULL, NULL, NULL, NULL)
+                 : moe_ref_expert_swiglu_i4(cfg, xq, sx, S, layer->shared, y, NULL, NULL, NULL,
+                                            NULL);
+}
+
+/* The experts of the block for one token whose routing is known: quantize
+ * the token, run the first keff selected experts and the shared expert on
+ * it, combine.  stage: (K + 1) * D floats of scratch. */
+static int token_block(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                       const moe_ref_expert_i8 *shared8, const float *xs, const int32_t *idx,
+                       const float *w, int keff, float *stage, int8_t *xq, float *out,
+                       unsigned flags) {
+  const int D = cfg->D, K = cfg->K;
+  float sxs = moe_ref_quant_row_i8(xs, D, xq);
+  int rc = 0;
+  for (int k = 0; k < keff && rc == 0; k++)
+    rc = moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, &layer->experts[idx[k]],
+                                  stage + (int64_t)k * D, NULL, NULL, NULL, NULL);
+  if (rc == 0 && cfg->n_shared == 1)
+    rc = shared_rows(cfg, layer, shared8, xq, &sxs, 1, stage + (int64_t)K * D);
+  if (rc == 0) combine_row(cfg, w, keff, stage, out, flags);
+  return rc;
+}
+
+/* Per-token path.  With given_idx/given_w the routing is the caller's and all
+ * K experts run; otherwise each token is routed first (section 11: routing,
+ * then the experts) and keeps keff experts. */
+static int per_token(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                     const moe_ref_expert_i8 *shared8, const float *x, int S,
+                     const int32_t *given_idx, const float *given_w, float *out, unsigned flags) {
   if (!x || !out || S < 1) return -1;
-  const int D = cfg->D, K = cfg->K, slots = cfg->K + cfg->n_shared;
+  const int D = cfg->D, K = cfg->K;
   int32_t idx[64];
   float w[64];
   int8_t *xq = (int8_t *)malloc((size_t)D);
-  float *stage = (float *)malloc((size_t)slots * D * sizeof(float));
-  if (!xq || !stage) { free(xq); free(stage); return -2; }
-  int rc = 0;
+  float *stage = (float *)malloc((size_t)(K + 1) * D * sizeof(float));
+  int rc = (xq && stage) ? 0 : -2;
   for (int s = 0; s < S && rc == 0; s++) {
     const float *xs = x + (int64_t)s * D;
-    rc = moe_ref_router_topk(cfg, xs, 1, layer->router_w, layer->router_b, idx, w, NULL, NULL);
-    if (rc) break;
-    float sxs = moe_ref_quant_row_i8(xs, D, xq);
-    const int keff = moe_ref_expert_keff(w, K, cfg->expert_topp);
-    for (int k = 0; k < keff && rc == 0; k++)
-      rc = moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, &layer->experts[idx[k]],
-                                    stage + (int64_t)k * D, NULL, NULL, NULL, NULL);
-    if (rc == 0 && cfg->n_shared == 1)
-      rc = shared8 ? moe_ref_expert_swiglu_i8(cfg, xq, &sxs, 1, shared8, stage + (int64_t)K * D,
-                                              NULL, NULL, NULL, NULL)
-                   : moe_ref_expert_swiglu_i4(cfg, xq, &sxs, 1, layer->shared,
-                                              stage + (int64_t)K * D, NULL, NULL, NULL, NULL);
-    if (rc == 0) combine_row(cfg, w, keff, stage, out + (int64_t)s * D, flags);
+    const int32_t *ti = idx;
+    const float *tw = w;
+    int keff = K;
+    if (given_idx) {
+      ti = given_idx + (int64_t)s * K;
+      tw = given_w + (int64_t)s * K;
+    } else {
+      rc = moe_ref_router_topk(cfg, xs, 1, layer->router_w, layer->router_b, idx, w, NULL, NULL);
+      keff = moe_ref_expert_keff(w, K, cfg->expert_topp);
+    }
+    if (rc == 0)
+      rc = token_block(cfg, layer, shared8, xs, ti, tw, keff, stage, xq, out + (int64_t)s * D,
+                       flags);
   }
   free(xq);
   free(stage);
@@ -537,88 +570,163 @@ static int layer_forward_impl(const moe_ref_config *cfg, const moe_ref_layer *la
 
 int moe_ref_layer_forward(const moe_ref_config *cfg, const moe_ref_layer *layer, const float *x,
                           int S, float *out, unsigned flags) {
-  if (!layer_ok(cfg, layer)) return -1;
-  return layer_forward_impl(cfg, layer, NULL, x, S, out, flags);
+  if (!layer_ok(cfg, layer, 1)) return -1;
+  return per_token(cfg, layer, NULL, x, S, NULL, NULL, out, flags);
+}
+
+int moe_ref_layer_forward_routed(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                 const float *x, int S, const int32_t *idx, const float *w,
+                                 float *out, unsigned flags) {
+  if (!layer_ok(cfg, layer, 0) || S < 1 || !routing_ok(cfg, idx, w, S)) return -1;
+  return per_token(cfg, layer, NULL, x, S, idx, w, out, flags);
+}
+
+static int shared8_ok(const moe_ref_config *cfg, const moe_ref_expert_i8 *e) {
+  return cfg && cfg->n_shared == 1 && e && q8mat_ok(&e->gate) && q8mat_ok(&e->up) &&
+         q8mat_ok(&e->down);
 }
 
 int moe_ref_layer_forward_shared_i8(const moe_ref_config *cfg, const moe_ref_layer *layer,
                                     const moe_ref_expert_i8 *shared8, const float *x, int S,
                                     float *out, unsigned flags) {
-  if (!cfg || cfg->n_shared != 1 || !shared8) return -1;
-  if (!q8mat_ok(&shared8->gate) || !q8mat_ok(&shared8->up) || !q8mat_ok(&shared8->down)) return -1;
+  if (!shared8_ok(cfg, shared8)) return -1;
   moe_ref_config c0 = *cfg;
-  c0.n_shared = 0;  /* the routed experts and the router are checked as usual */
-  if (!layer_ok(&c0, layer)) return -1;
-  return layer_forward_impl(cfg, layer, shared8, x, S, out, flags);
+  c0.n_shared = 0; /* layer->shared is not read */
+  if (!layer_ok(&c0, layer, 1)) return -1;
+  return per_token(cfg, layer, shared8, x, S, NULL, NULL, out, flags);
+}
+
+/* Section 11 unique-expert union for S tokens whose routing is known (the
+ * first keff[s] of the K selected experts of token s take part).  Each
+ * expert selected by any kept pair is visited once, in order of its first
+ * appearance scanning the pairs token by token and slot by slot; its rows are
+ * gathered, run through the expert together, and scattered to a staging
+ * area indexed by (token, slot).  The shared expert runs once on all S
+ * rows.  Each row's arithmetic is that of the per-token path, and the staged
+ * rows are combined per token in the same order, so the result equals the
+ * per-token path bit for bit. */
+static int union_block(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                       const moe_ref_expert_i8 *shared8, const float *x, int S, const int32_t *idx,
+                       const float *w, const int32_t *keff, float *out, unsigned flags,
+                       int32_t *uniq_out, int32_t *n_uniq_out) {
+  const int D = cfg->D, E = cfg->E, K = cfg->K, P = cfg->K + 1;
+  int8_t *xq = (int8_t *)malloc((size_t)S * D);
+  float *sx = (float *)malloc((size_t)S * sizeof(float));
+  float *stage = (float *)malloc((size_t)S * P * D * sizeof(float));
+  int64_t *first = (int64_t *)malloc((size_t)E * sizeof(int64_t));
+  int32_t *order = (int32_t *)malloc((size_t)E * sizeof(int32_t));
+  int32_t *rows = (int32_t *)malloc((size_t)S * K * sizeof(int32_t));
+  int8_t *xg = NULL;
+  float *sg = NULL, *yg = NULL;
+  int rc = -2, nu = 0;
+  if (!xq || !sx || !stage || !first || !order || !rows) goto done;
+  rc = moe_ref_quant_act_i8(x, S, D, xq, sx);
+  if (rc) goto done;
+  /* first[e]: the first kept pair p = s*K + k that selects e (-1: none) */
+  for (int e = 0; e < E; e++) first[e] = -1;
+  for (int64_t p = (int64_t)S * K - 1; p >= 0; p--)
+    if (p % K < keff[p / K]) first[idx[p]] = p;
+  /* the selected experts ordered by first appearance (counting the pairs in
+   * order, each expert at its first pair) */
+  for (int64_t p = 0; p < (int64_t)S * K; p++)
+    if (p % K < keff[p / K] && first[idx[p]] == p) order[nu++] = idx[p];
+  for (int u = 0; u < nu && rc == 0; u++) {
+    const int e = order[u];
+    int nr = 0; /* the expert's kept (token, slot) pairs */
+    for (int64_t p = first[e]; p < (int64_t)S * K; p++)
+      if (idx[p] == e && p % K < keff[p / K]) rows[nr++] = (int32_t)p;
+    xg = (int8_t *)malloc((size_t)nr * D);
+    sg = (float *)malloc((size_t)nr * sizeof(float));
+    yg = (float *)malloc((size_t)nr * D * sizeof(float));
+    rc = (xg && sg && yg) ? 0 : -2;
+    for (int r = 0; r < nr && rc == 0; r++) { /* gather */
+      memcpy(xg + (int64_t)r * D, xq + (int64_t)(rows[r] / K) * D, (size_t)D);
+      sg[r] = sx[rows[r] / K];
+    }
+    if (rc == 0)
+      rc = moe_ref_expert_swiglu_i4(cfg, xg, sg, nr, &layer->experts[e], yg, NULL, NULL, NULL, NULL);
+    for (int r = 0; r < nr && rc == 0; r++) { /* scatter to (token, slot) */
+      const int64_t s = rows[r] / K, k = rows[r] % K;
+      memcpy(stage + (s * P + k) * D, yg + (int64_t)r * D, (size_t)D * sizeof(float));
+    }
+    free(xg); free(sg); free(yg);
+    xg = NULL; sg = NULL; yg = NULL;
+  }
+  if (rc == 0 && cfg->n_shared == 1) {
+    /* staged in place: row s of the shared expert's output is (s, K) */
+    float *ys = (float *)malloc((size_t)S * D * sizeof(float));
+    rc = ys ? shared_rows(cfg, layer, shared8, xq, sx, S, ys) : -2;
+    for (int s = 0; s < S && rc == 0; s++)
+      memcpy(stage + ((int64_t)s * P + K) * D, ys + (int64_t)s * D, (size_t)D * sizeof(float));
+    free(ys);
+  }
+  if (rc == 0)
+    for (int s = 0; s < S; s++)
+      combine_row(cfg, w + (int64_t)s * K, keff[s], stage + (int64_t)s * P * D,
+                  out + (int64_t)s * D, flags);
+  if (rc == 0) {
+    if (uniq_out) memcpy(uniq_out, order, (size_t)nu * sizeof(int32_t));
+    if (n_uniq_out) *n_uniq_out = nu;
+  }
+done:
+  free(xq); free(sx); free(stage); free(first); free(order); free(rows);
+  return rc;
+}
+
+/* The union path with the router: route all S tokens (section 11 routes
+ * before it forms the union), keff per token, then union_block. */
+static int routed_union(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                        const moe_ref_expert_i8 *shared8, const float *x, int S, float *out,
+                        unsigned flags, int32_t *idx_out, float *w_out, int32_t *uniq_out,
+                        int32_t *n_uniq_out) {
+  if (!x || !out || S < 1) return -1;
+  const int K = cfg->K;
+  int32_t *idx = (int32_t *)malloc((size_t)S * K * sizeof(int32_t));
+  float *w = (float *)malloc((size_t)S * K * sizeof(float));
+  int32_t *keff = (int32_t *)malloc((size_t)S * sizeof(int32_t));
+  int rc = (idx && w && keff) ? 0 : -2;
+  if (rc == 0) rc = moe_ref_router_topk(cfg, x, S, layer->router_w, layer->router_b, idx, w, NULL, NULL);
+  for (int s = 0; s < S && rc == 0; s++)
+    keff[s] = moe_ref_expert_keff(w + (int64_t)s * K, K, cfg->expert_topp);
+  if (rc == 0) rc = union_block(cfg, layer, shared8, x, S, idx, w, keff, out, flags, uniq_out, n_uniq_out);
+  if (rc == 0) {
+    if (idx_out) memcpy(idx_out, idx, (size_t)S * K * sizeof(int32_t));
+    if (w_out) memcpy(w_out, w, (size_t)S * K * sizeof(float));
+  }
+  free(idx);
+  free(w);
+  free(keff);
+  return rc;
 }
 
 int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *layer,
                                 const float *x, int S, float *out, unsigned flags, int32_t *idx_out,
                                 float *w_out, int32_t *uniq_out, int32_t *n_uniq_out) {
-  if (!layer_ok(cfg, layer) || !x || !out || S < 1) return -1;
-  const int D = cfg->D, E = cfg->E, K = cfg->K, slots = cfg->K + cfg->n_shared;
-  int32_t *idx = (int32_t *)malloc((size_t)S * K * sizeof(int32_t));
-  float *w = (float *)malloc((size_t)S * K * sizeof(float));
-  int8_t *xq = (int8_t *)malloc((size_t)S * D);
-  float *sx = (float *)malloc((size_t)S * sizeof(float));
-  float *stage = (float *)malloc((size_t)S * slots * D * sizeof(float));
-  int32_t *uniq = (int32_t *)malloc((size_t)E * sizeof(int32_t));
-  unsigned char *seen = (unsigned char *)calloc((size_t)E, 1);
-  int32_t *rows = (int32_t *)malloc((size_t)S * sizeof(int32_t));
-  int32_t *slot = (int32_t *)malloc((size_t)S * sizeof(int32_t));
-  int8_t *xg = (int8_t *)malloc((size_t)S * D);
-  float *sg = (float *)malloc((size_t)S * sizeof(float));
-  float *yg = (float *)malloc((size_t)S * D * sizeof(float));
+  if (!layer_ok(cfg, layer, 1)) return -1;
+  return routed_union(cfg, layer, NULL, x, S, out, flags, idx_out, w_out, uniq_out, n_uniq_out);
+}
+
+int moe_ref_layer_forward_batch_shared_i8(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                          const moe_ref_expert_i8 *shared8, const float *x, int S,
+                                          float *out, unsigned flags, int32_t *uniq_out,
+                                          int32_t *n_uniq_out) {
+  if (!shared8_ok(cfg, shared8)) return -1;
+  moe_ref_config c0 = *cfg;
+  c0.n_shared = 0;
+  if (!layer_ok(&c0, layer, 1)) return -1;
+  return routed_union(cfg, layer, shared8, x, S, out, flags, NULL, NULL, uniq_out, n_uniq_out);
+}
+
+int moe_ref_layer_forward_batch_routed(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                       const float *x, int S, const int32_t *idx, const float *w,
+                                       float *out, unsigned flags, int32_t *uniq_out,
+                                       int32_t *n_uniq_out) {
+  if (!layer_ok(cfg, layer, 0) || !x || !out || S < 1 || !routing_ok(cfg, idx, w, S)) return -1;
   int32_t *keff = (int32_t *)malloc((size_t)S * sizeof(int32_t));
-  int rc = -2;
-  if (!idx || !w || !xq || !sx || !stage || !uniq || !seen || !rows || !slot || !xg || !sg || !yg ||
-      !keff)
-    goto done;
-  rc = moe_ref_router_topk(cfg, x, S, layer->router_w, layer->router_b, idx, w, NULL, NULL);
-  if (rc) goto done;
-  moe_ref_quant_act_i8(x, S, D, xq, sx);
-  /* keff[s] experts per token; the union of the kept experts, in order of
-   * first appearance */
-  for (int s = 0; s < S; s++) keff[s] = moe_ref_expert_keff(w + (int64_t)s * K, K, cfg->expert_topp);
-  int nu = 0;
-  for (int s = 0; s < S; s++)
-    for (int k = 0; k < keff[s]; k++) {
-      int e = idx[(int64_t)s * K + k];
-      if (!seen[e]) { seen[e] = 1; uniq[nu++] = e; }
-    }
-  for (int u = 0; u < nu && rc == 0; u++) {
-    int e = uniq[u], nr = 0;
-    for (int s = 0; s < S; s++)
-      for (int k = 0; k < keff[s]; k++)
-        if (idx[(int64_t)s * K + k] == e) { rows[nr] = s; slot[nr] = k; nr++; }
-    for (int r = 0; r < nr; r++) {
-      memcpy(xg + (int64_t)r * D, xq + (int64_t)rows[r] * D, (size_t)D);
-      sg[r] = sx[rows[r]];
-    }
-    rc = moe_ref_expert_swiglu_i4(cfg, xg, sg, nr, &layer->experts[e], yg, NULL, NULL, NULL, NULL);
-    for (int r = 0; r < nr && rc == 0; r++)
-      memcpy(stage + ((int64_t)rows[r] * slots + slot[r]) * D, yg + (int64_t)r * D,
-             (size_t)D * sizeof(float));
-  }
-  if (rc == 0 && cfg->n_shared == 1) {
-    /* the shared expert is read once and applied to every row */
-    rc = moe_ref_expert_swiglu_i4(cfg, xq, sx, S, layer->shared, yg, NULL, NULL, NULL, NULL);
-    for (int s = 0; s < S && rc == 0; s++)
-      memcpy(stage + ((int64_t)s * slots + K) * D, yg + (int64_t)s * D, (size_t)D * sizeof(float));
-  }
-  if (rc == 0)
-    for (int s = 0; s < S; s++)
-      combine_row(cfg, w + (int64_t)s * K, keff[s], stage + (int64_t)s * slots * D,
-                  out + (int64_t)s * D, flags);
-  if (rc == 0) {
-    if (idx_out) memcpy(idx_out, idx, (size_t)S * K * sizeof(int32_t));
-    if (w_out) memcpy(w_out, w, (size_t)S * K * sizeof(float));
-    if (uniq_out) memcpy(uniq_out, uniq, (size_t)nu * sizeof(int32_t));
-    if (n_uniq_out) *n_uniq_out = nu;
-  }
-done:
-  free(idx); free(w); free(xq); free(sx); free(stage); free(uniq); free(seen);
-  free(rows); free(slot); free(xg); free(sg); free(yg); free(keff);
+  if (!keff) return -2;
+  for (int s = 0; s < S; s++) keff[s] = cfg->K;
+  const int rc = union_block(cfg, layer, NULL, x, S, idx, w, keff, out, flags, uniq_out, n_uniq_out);
+  free(keff);
   return rc;
 }
 
@@ -639,37 +747,43 @@ int moe_ref_rmsnorm(const float *x, const float *gamma, int S, int D, float eps,
 
 /* ---- section 05 expert cache and section 13 tier policy ---------------- */
 
+/* The slot holding eid among the n_used filled ones, or -1. */
+static int cache_lookup(const int32_t *slot_eid, int n_used, int32_t eid) {
+  for (int z = 0; z < n_used; z++)
+    if (slot_eid[z] == eid) return z;
+  return -1;
+}
+
+/* Where a missing expert goes: the next unfilled slot while there is one,
+ * else the least recently used slot (the smallest use value, the lowest slot
+ * among equals). */
+static int cache_victim(const uint64_t *slot_used, int n_used, int cap) {
+  if (n_used < cap) return n_used;
+  int v = 0;
+  for (int z = 1; z < n_used; z++)
+    if (slot_used[z] < slot_used[v]) v = z;
+  return v;
+}
+
 int moe_ref_expert_get(int32_t *slot_eid, uint64_t *slot_used, int cap, int *n_used,
                        uint64_t *clock, uint64_t *hits, uint64_t *misses, int32_t eid,
                        int *loaded) {
-  int i, victim;
   if (!slot_eid || !slot_used || !n_used || !clock || !hits || !misses || !loaded) return -1;
   if (cap < 1 || *n_used < 0 || *n_used > cap) return -1;
-  /* lookup: a hit refreshes the slot's use */
-  for (i = 0; i < *n_used; i++) {
-    if (slot_eid[i] == eid) {
-      *hits += 1;
-      *clock += 1;
-      slot_used[i] = *clock;
-      *loaded = 0;
-      return i;
-    }
-  }
-  *misses += 1;
-  if (*n_used < cap) {
-    victim = *n_used;
-    *n_used += 1;
+  int z = cache_lookup(slot_eid, *n_used, eid);
+  *loaded = z < 0;
+  if (z >= 0) {
+    *hits += 1;
   } else {
-    /* least recently used slot */
-    victim = 0;
-    for (i = 1; i < *n_used; i++)
-      if (slot_used[i] < slot_used[victim]) victim = i;
+    *misses += 1;
+    z = cache_victim(slot_used, *n_used, cap);
+    if (z == *n_used) *n_used += 1;
+    slot_eid[z] = eid;
   }
-  slot_eid[victim] = eid;
+  /* every use, hit or load, stamps the slot with the next clock value */
   *clock += 1;
-  slot_used[victim] = *clock;
-  *loaded = 1;
-  return victim;
+  slot_used[z] = *clock;
+  return z;
 }
 
 int moe_ref_tier_pick_swap(const uint32_t *heat, int nexpert, const int32_t *pinned, int npin,

@@ -223,6 +223,34 @@ int moe_ref_layer_forward_batch(const moe_ref_config *cfg, const moe_ref_layer *
                                 const float *x, int S, float *out, unsigned flags, int32_t *idx,
                                 float *w, int32_t *uniq, int32_t *n_uniq);
 
+/* The per-token block with the routing given instead of the router's
+ * (section 11 routes first and runs the experts after; section 13 fetches the
+ * selected experts in between): idx[S][K] in [0, E) and w[S][K]; all K
+ * experts of every token run (expert_topp does not apply); router_w and
+ * router_b are not read.  Fed the routing moe_ref_router_topk selects, it
+ * returns moe_ref_layer_forward's bits. */
+int moe_ref_layer_forward_routed(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                 const float *x, int S, const int32_t *idx, const float *w,
+                                 float *out, unsigned flags);
+
+/* The unique-expert union with the routing given, as
+ * moe_ref_layer_forward_routed is to moe_ref_layer_forward.  A token may name
+ * an expert more than once; each (token, slot) pair is then a row of its own.
+ * Optional outputs uniq[E] (first-appearance order) and n_uniq. */
+int moe_ref_layer_forward_batch_routed(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                       const float *x, int S, const int32_t *idx, const float *w,
+                                       float *out, unsigned flags, int32_t *uniq,
+                                       int32_t *n_uniq);
+
+/* The unique-expert union with the shared expert in the int8 format: the
+ * union of moe_ref_layer_forward_batch for the routed experts, the int8
+ * shared expert read once for all S rows, the per-token combine; equal bit
+ * for bit to moe_ref_layer_forward_shared_i8.  cfg->n_shared must be 1. */
+int moe_ref_layer_forward_batch_shared_i8(const moe_ref_config *cfg, const moe_ref_layer *layer,
+                                          const moe_ref_expert_i8 *shared8, const float *x, int S,
+                                          float *out, unsigned flags, int32_t *uniq,
+                                          int32_t *n_uniq);
+
 /* Section 04 RMSNorm: ms = mean of squares in double, r = 1/sqrtf(ms + eps),
  * y = x * r * gamma. */
 int moe_ref_rmsnorm(const float *x, const float *gamma, int S, int D, float eps, float *y);

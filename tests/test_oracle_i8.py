@@ -193,3 +193,31 @@ def test_layer_with_int8_shared_differs_from_int4_by_the_shared_term():
     cfg = config_of(shape)
     want = oracle.expert_swiglu_i8(cfg, xq, sx, shared8)["y"] - oracle.expert_swiglu(cfg, xq, sx, layer.shared)["y"]
     assert np.abs(diff - want).max() <= 1e-5 * max(1.0, np.abs(want).max())
+
+
+@pytest.mark.parametrize("shape,S,topp", [(TINY, 5, 0.0), (synth.Shape(D=512, I=256, E=64, K=8), 9, 0.0),
+                                          (synth.Shape(D=512, I=256, E=64, K=8), 9, 0.6)])
+def test_union_with_int8_shared_equals_per_token_and_int4_codes(shape, S, topp):
+    """The union path with the int8 shared expert: equal bit for bit to the
+    per-token path with it (plain and accumulating, top-p on or off), and on
+    the shared expert's int4 codes widened to int8, to the int4 union."""
+    from oracle.layers import LazyLayer
+    layer = LazyLayer(6, shape, 0, synth.router_b_uniform(6, shape, 0))
+    layer.cfg.expert_topp = topp
+    g, u, d = synth.host_expert_f32(6, shape, 0, synth.SHARED)
+    shared8 = oracle.HostExpertI8.from_f32(g, u, d)
+    x = synth.activations(6, S, shape.D)
+    layer.ensure_for(x)
+    a = oracle.layer_forward_shared_i8(layer, shared8, x)
+    b, uniq = oracle.layer_forward_batch_shared_i8(layer, shared8, x)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    _, _, _, u0 = oracle.layer_forward_batch(layer, x)
+    assert uniq.tolist() == u0.tolist()
+    base = synth.activations(7, S, shape.D)
+    a2 = oracle.layer_forward_shared_i8(layer, shared8, x, out=base.copy(), flags=1)
+    b2, _ = oracle.layer_forward_batch_shared_i8(layer, shared8, x, out=base.copy(), flags=1)
+    assert np.array_equal(a2.view(np.uint32), b2.view(np.uint32))
+    w4 = _int4_as_int8(layer.shared, shape)
+    c, _ = oracle.layer_forward_batch_shared_i8(layer, w4, x)
+    ref, _, _, _ = oracle.layer_forward_batch(layer, x)
+    assert np.array_equal(c.view(np.uint32), ref.view(np.uint32))

@@ -138,3 +138,96 @@ def test_zipf_recipe_is_skewed():
     hot = int(np.argmax(p))
     assert counts[hot] >= 40  # the rank-1 expert is in most selections
     assert 100 <= (counts > 0).sum() <= 200  # union size of the batch
+
+
+# ---- the block on given routing ------------------------------------------
+
+@pytest.mark.parametrize("shape,S,seed", [(TINY, 4, 9), (MID, 11, 10),
+                                          (synth.Shape(D=256, I=128, E=8, K=2, n_shared=0), 5, 11)])
+def test_routed_on_the_routers_choice_equals_the_block_bit_exact(shape, S, seed):
+    """Fed the routing that the router selects, the given-routing calls return
+    the routed block's bits (per token and through the union)."""
+    L = LazyLayer(seed, shape, 0, bias_for("uniform", seed, shape))
+    x = synth.activations(seed, S, shape.D)
+    idx = L.ensure_for(x)
+    a = oracle.layer_forward(L, x)
+    idx2, w2, _, _ = oracle.router_topk(L.cfg, x, L.router_w, L.router_b)
+    assert np.array_equal(idx, idx2)
+    r = oracle.layer_forward_routed(L, x, idx2, w2)
+    b, uniq = oracle.layer_forward_batch_routed(L, x, idx2, w2)
+    assert np.array_equal(a.view(np.uint32), r.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    _, _, _, u0 = oracle.layer_forward_batch(L, x)
+    assert uniq.tolist() == u0.tolist()
+
+
+def test_routed_closed_form_on_arbitrary_routing():
+    """Any routing, duplicates within a token included: out[s] =
+    sum_k w[s][k] * y_{idx[s][k]}(x_s) + y_shared(x_s), the sum in k order
+    (float32, starting from 0), each y from the single-expert oracle call;
+    the union on the same routing returns the same bits."""
+    shape = synth.Shape(D=256, I=128, E=8, K=3)
+    L = LazyLayer(12, shape, 0, np.zeros(shape.E, np.float32))
+    L.ensure(range(shape.E))
+    S = 6
+    x = synth.activations(12, S, shape.D)
+    rng = np.random.default_rng(12)
+    idx = rng.integers(0, shape.E, size=(S, shape.K)).astype(np.int32)
+    idx[0] = [5, 5, 5]     # one expert three times in one token
+    idx[1] = [2, 7, 2]
+    w = rng.uniform(-1.5, 2.5, size=(S, shape.K)).astype(np.float32)
+    got = oracle.layer_forward_routed(L, x, idx, w)
+    xq, sx = oracle.quant_act_i8(x)
+    cfg = config_of(shape)
+    want = np.zeros((S, shape.D), np.float32)
+    for s in range(S):
+        acc = np.zeros(shape.D, np.float32)
+        for k in range(shape.K):
+            y = oracle.expert_swiglu(cfg, xq[s:s + 1], sx[s:s + 1], L.experts[int(idx[s, k])])["y"][0]
+            acc = acc + w[s, k] * y
+        ysh = oracle.expert_swiglu(cfg, xq[s:s + 1], sx[s:s + 1], L.shared)["y"][0]
+        want[s] = acc + ysh
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    b, uniq = oracle.layer_forward_batch_routed(L, x, idx, w)
+    assert np.array_equal(b.view(np.uint32), got.view(np.uint32))
+    first = []
+    for e in idx.ravel().tolist():
+        if e not in first:
+            first.append(e)
+    assert uniq.tolist() == first
+
+
+def test_routed_within_1e3_of_float64_reference_on_given_routing():
+    """The float64 reference fed the same (non-router) routing."""
+    from ref64 import expert64
+    shape = MID
+    L = LazyLayer(13, shape, 0, np.zeros(shape.E, np.float32))
+    S = 5
+    x = synth.activations(13, S, shape.D)
+    rng = np.random.default_rng(13)
+    idx = np.stack([rng.permutation(shape.E)[:shape.K] for _ in range(S)]).astype(np.int32)
+    w = rng.uniform(0.1, 2.5, size=(S, shape.K)).astype(np.float32)
+    L.ensure(idx)
+    got = oracle.layer_forward_routed(L, x, idx, w)
+    xq, sx = oracle.quant_act_i8(x)
+    want = np.zeros((S, shape.D))
+    for s in range(S):
+        xd = xq[s:s + 1].astype(np.float64) * float(sx[s])
+        for k in range(shape.K):
+            want[s] += float(w[s, k]) * expert64(xd, L.experts[int(idx[s, k])], shape.D, shape.I)[0]
+        want[s] += expert64(xd, L.shared, shape.D, shape.I)[0]
+    assert max_rel_err(got, want).max() <= 1e-3
+
+
+def test_routed_rejects_out_of_range_experts():
+    shape = synth.Shape(D=256, I=128, E=8, K=2)
+    L = LazyLayer(14, shape, 0, np.zeros(8, np.float32))
+    L.ensure(range(8))
+    x = synth.activations(14, 2, shape.D)
+    w = np.ones((2, 2), np.float32)
+    for bad in (8, -1):
+        idx = np.array([[0, 1], [bad, 2]], np.int32)
+        with pytest.raises(ValueError):
+            oracle.layer_forward_routed(L, x, idx, w)
+        with pytest.raises(ValueError):
+            oracle.layer_forward_batch_routed(L, x, idx, w)
