@@ -6,12 +6,12 @@
 // results are the same integers, and the same floats, as the GEMV kernels of
 // grouped.hip.
 //
-// Work unit: a tile of up to 128 (token, slot) pairs of one expert group (the
-// tile list is built by group_kernel; a routed expert of a 2048-token prefill
-// gets about 64 pairs, so its weights are read once) times 64 (gate/up) or
-// 128 (down) output rows.  A workgroup has 4 waves; wave w owns 16 gate rows
-// and the 16 up rows with the same indices (gate/up), or 32 down rows, for
-// all pairs of the tile.
+// Work unit: a tile of up to 64 (batches of at most 64 tokens) or 80 (larger
+// batches) (token, slot) pairs of one expert group (the tile list is built by
+// group_kernel; a routed expert of a 2048-token prefill gets about 64 pairs,
+// so its weights are read once) times a chunk of output rows.  A workgroup
+// has 4 or 8 waves; each wave owns 8 NS gate rows and the 8 NS up rows with
+// the same indices (gate/up), or 16 NS down rows, for all pairs of the tile.
 //
 // v_mfma_i32_16x16x64_i8 (layout checked on the device): lane l supplies row
 // l % 16 of A (a pair) and column l % 16 of B (an output row), each 16 int8
@@ -35,7 +35,7 @@ namespace moe {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));  // 16 staged bytes
 
-constexpr int kMT = kGroupedMfmaTile;  // pairs per tile (128)
+constexpr int kMT = kGroupedMfmaTile;  // bound on the pairs of a tile (128)
 constexpr int kKS = 256;        // columns per pipeline step
 constexpr int kAStride = 272;   // LDS bytes per pair row (256 + 16: no bank conflicts)
 
@@ -368,10 +368,17 @@ __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a
 
 bool grouped_mfma_fits(int C) { return C % kKS == 0; }
 
-// Pairs per tile: batches above 64 tokens use tiles of 80 pairs (the 8-wave
-// kernel holds at most 5 subtiles); smaller batches never have more than 64
-// pairs per group, so their tiles are whole groups.
-int grouped_mfma_tile_rows(int S) { return S > 64 ? 80 : kMT; }
+// Subtiles (16 pairs each) of the two launch shapes: batches of up to 64
+// tokens run 4-wave workgroups holding at most 4 subtiles, larger batches
+// 8-wave workgroups holding at most 5.
+constexpr int kSmallMsv = 4, kLargeMsv = 5;
+
+// Pairs per tile: as many as the launch's workgroups hold.  A group larger
+// than that (a routed expert with more pairs, or the shared expert) is cut
+// into several tiles.  With the router's selection no group of a batch of S
+// <= 64 tokens exceeds 64 pairs, but given routing may repeat an expert
+// within a token or clamp several ids onto one expert.
+int grouped_mfma_tile_rows(int S) { return 16 * (S > 64 ? kLargeMsv : kSmallMsv); }
 
 int grouped_mfma_max_tiles(int S, int P, int E) {
   const int tr = grouped_mfma_tile_rows(S);
@@ -393,14 +400,14 @@ hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles
                                hipStream_t st) {
   if (S <= 64) {
     if (mode == 0)
-      launch_mode<0, 4, 2, 4>(a, max_tiles, st);
+      launch_mode<0, 4, 2, kSmallMsv>(a, max_tiles, st);
     else
-      launch_mode<1, 4, 2, 4>(a, max_tiles, st);
+      launch_mode<1, 4, 2, kSmallMsv>(a, max_tiles, st);
   } else {
     if (mode == 0)
-      launch_mode<0, 8, 4, 5>(a, max_tiles, st);
+      launch_mode<0, 8, 4, kLargeMsv>(a, max_tiles, st);
     else
-      launch_mode<1, 8, 4, 5>(a, max_tiles, st);
+      launch_mode<1, 8, 4, kLargeMsv>(a, max_tiles, st);
   }
   return hipGetLastError();
 }

@@ -13,6 +13,13 @@
 
 using namespace moe;
 
+namespace moe {
+// host bookkeeping of the residency tiers (tier.hip)
+void tier_sizes(const moe_tier *t, int *n_experts, int *n_slot_total);
+void tier_unmap_loads(moe_tier *t, int layer, const int32_t *eids, const int32_t *slots,
+                      const int32_t *loads, int n);
+}  // namespace moe
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -904,6 +911,17 @@ int moe_tier_forward(moe_tier *t, int layer_index, const moe_config *cfg, const 
     return MOE_EALIGN;
   if (ws_router_bytes < carve(c, S, W_ROUTER, nullptr, nullptr)) return MOE_EWORKSPACE;
   if (ws_bytes < carve(c, S, union_path ? W_BATCH : W_FWD, nullptr, nullptr)) return MOE_EWORKSPACE;
+  // the slabs must hold this shape's layout, and every slot number must be a
+  // valid expert index of the slot stack (the block clamps indices into
+  // [0, E)); the router's experts must be experts of the tier
+  moe_slab_layout lay;
+  MOE_TRY(moe_slab_layout_of(cfg, &lay));
+  if (slab_bytes == 0 || (slab_bytes & 15u)) return MOE_EALIGN;
+  if (slab_bytes < (size_t)lay.bytes) return MOE_ESHAPE;
+  int t_experts = 0, t_slots = 0;
+  tier_sizes(t, &t_experts, &t_slots);
+  if (t_slots > c.E || t_experts < c.E) return MOE_ESHAPE;
+  if (layer_index < 0) return MOE_EINVAL;
   MOE_TRY(check_device());
   // 1. selection on the device (all K experts; top-p does not apply here)
   Work wr;
@@ -928,8 +946,12 @@ int moe_tier_forward(moe_tier *t, int layer_index, const moe_config *cfg, const 
   if (nm < 0) return nm;
   if (misses) *misses = nm;
   // 3. the missing slabs, then the routing as slot numbers, both in stream order
-  MOE_TRY(moe_tier_fetch(host_slabs, hbm_slots, slab_bytes, eids.data(), slots.data(),
-                         loads.data(), (int)eids.size(), stream));
+  const int frc = moe_tier_fetch(host_slabs, hbm_slots, slab_bytes, eids.data(), slots.data(),
+                                 loads.data(), (int)eids.size(), stream);
+  if (frc != MOE_OK) {
+    tier_unmap_loads(t, layer_index, eids.data(), slots.data(), loads.data(), (int)eids.size());
+    return frc;
+  }
   for (size_t i = 0; i < n; i++) host_idx[i] = slots[pos[i]];
   MOE_TRY_HIP(hipMemcpyAsync(wr.idx, host_idx, n * 4, hipMemcpyHostToDevice, stream));
   // 4. the block on the slot stack

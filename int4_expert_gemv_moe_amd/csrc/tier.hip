@@ -23,17 +23,35 @@
 struct moe_tier {
   int n_layers, n_experts, n_slots;  // n_slots: the LRU slots of a layer
   int n_pinned = 0;                  // heat-managed slots of a layer, numbered first
-  // per layer: LRU slots in use, and per LRU slot the expert it holds and the
-  // clock value of its last use
-  std::vector<int> used_n;
-  std::vector<int32_t> eid;
-  std::vector<uint64_t> used;
+  // per layer and LRU slot: the expert it holds (-1: empty) and the clock
+  // value of its last use
+  std::vector<int32_t> slot_eid;
+  std::vector<uint64_t> slot_used;
+  // per layer and expert: the LRU slot holding it (-1: none), so a lookup
+  // does not scan the slots
+  std::vector<int32_t> where;
   // per layer: the expert of each pinned slot (-1: empty) and every expert's
   // heat (lookups so far)
   std::vector<int32_t> pinned;
   std::vector<uint32_t> heat;
   uint64_t clock = 0, hits = 0, misses = 0;
 };
+
+namespace {
+
+// The LRU slot a missing expert takes: the lowest empty slot while there is
+// one (slots fill in order 0, 1, ...), else the least recently used slot,
+// the lowest among equals.
+int lru_victim(const int32_t *eid, const uint64_t *used, int n) {
+  int v = -1;
+  for (int z = 0; z < n; z++) {
+    if (eid[z] < 0) return z;
+    if (v < 0 || used[z] < used[v]) v = z;
+  }
+  return v;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -61,9 +79,9 @@ moe_tier *moe_tier_create(int n_layers, int n_experts, int n_slots) {
   t->n_experts = n_experts;
   t->n_slots = n_slots;
   try {
-    t->used_n.assign(n_layers, 0);
-    t->eid.assign((size_t)n_layers * n_slots, -1);
-    t->used.assign((size_t)n_layers * n_slots, 0);
+    t->slot_eid.assign((size_t)n_layers * n_slots, -1);
+    t->slot_used.assign((size_t)n_layers * n_slots, 0);
+    t->where.assign((size_t)n_layers * n_experts, -1);
   } catch (...) {
     delete t;
     return nullptr;
@@ -98,9 +116,9 @@ int moe_tier_map(moe_tier *t, int layer, const int32_t *eids, int n, int32_t *sl
   if (n > t->n_slots) return MOE_ESHAPE;
   for (int i = 0; i < n; i++)
     if (eids[i] < 0 || eids[i] >= t->n_experts) return MOE_EINVAL;
-  int32_t *le = t->eid.data() + (size_t)layer * t->n_slots;
-  uint64_t *lu = t->used.data() + (size_t)layer * t->n_slots;
-  int &ln = t->used_n[layer];
+  int32_t *eid = t->slot_eid.data() + (size_t)layer * t->n_slots;
+  uint64_t *used = t->slot_used.data() + (size_t)layer * t->n_slots;
+  int32_t *where = t->where.data() + (size_t)layer * t->n_experts;
   const int np = t->n_pinned;
   const int32_t *pin = np ? t->pinned.data() + (size_t)layer * np : nullptr;
   uint32_t *heat = np ? t->heat.data() + (size_t)layer * t->n_experts : nullptr;
@@ -111,38 +129,26 @@ int moe_tier_map(moe_tier *t, int layer, const int32_t *eids, int n, int32_t *sl
     // a pinned expert is a hit in its pinned slot (slots 0 .. n_pinned-1)
     int z = 0;
     while (z < np && pin[z] != e) z++;
+    loads[i] = 0;
     if (z < np) {
       t->hits++;
       slots[i] = z;
-      loads[i] = 0;
       continue;
     }
-    int s = -1;
-    for (int z = 0; z < ln; z++)
-      if (le[z] == e) {
-        s = z;
-        break;
-      }
-    if (s >= 0) {
+    z = where[e];
+    if (z >= 0) {
       t->hits++;
-      lu[s] = ++t->clock;
-      slots[i] = np + s;
-      loads[i] = 0;
-      continue;
-    }
-    t->misses++;
-    misses++;
-    if (ln < t->n_slots) {
-      s = ln++;
     } else {
-      s = 0;  // least recently used; ties to the lowest slot
-      for (int z = 1; z < ln; z++)
-        if (lu[z] < lu[s]) s = z;
+      t->misses++;
+      misses++;
+      z = lru_victim(eid, used, t->n_slots);
+      if (eid[z] >= 0) where[eid[z]] = -1;  // evicted
+      eid[z] = e;
+      where[e] = z;
+      loads[i] = 1;
     }
-    le[s] = e;
-    lu[s] = ++t->clock;
-    slots[i] = np + s;
-    loads[i] = 1;
+    used[z] = ++t->clock;
+    slots[i] = np + z;
   }
   return misses;
 }
@@ -245,3 +251,30 @@ uint64_t moe_tier_lfru_score(uint32_t heat, uint32_t last, uint32_t clock) {
 }
 
 }  // extern "C"
+
+namespace moe {
+
+void tier_sizes(const moe_tier *t, int *n_experts, int *n_slot_total) {
+  *n_experts = t->n_experts;
+  *n_slot_total = t->n_pinned + t->n_slots;
+}
+
+// Undo the loads of one moe_tier_map call whose copies were not enqueued: the
+// LRU slots it filled become empty again (they are taken first by the next
+// miss), so no later lookup finds an expert whose slab never arrived.
+void tier_unmap_loads(moe_tier *t, int layer, const int32_t *eids, const int32_t *slots,
+                      const int32_t *loads, int n) {
+  int32_t *eid = t->slot_eid.data() + (size_t)layer * t->n_slots;
+  uint64_t *used = t->slot_used.data() + (size_t)layer * t->n_slots;
+  int32_t *where = t->where.data() + (size_t)layer * t->n_experts;
+  for (int i = 0; i < n; i++) {
+    if (!loads[i]) continue;
+    const int z = slots[i] - t->n_pinned;
+    if (z < 0 || z >= t->n_slots || eid[z] != eids[i]) continue;
+    where[eids[i]] = -1;
+    eid[z] = -1;
+    used[z] = 0;
+  }
+}
+
+}  // namespace moe

@@ -34,10 +34,21 @@ class LazyLayer(HostLayer):
         super().__init__(cfg, wr, router_b, {}, shared)
         self.seed, self.shape, self.layer = seed, shape, layer
 
-    def ensure(self, ids) -> None:
-        for e in sorted(set(int(i) for i in np.asarray(ids).ravel())):
-            if e not in self.experts:
+    def ensure(self, ids, workers: int = 1) -> None:
+        """Materialize the listed experts; with workers > 1 they are generated
+        and packed by that many threads (the generator and the packer are C
+        calls that run outside the interpreter lock)."""
+        todo = [e for e in sorted(set(int(i) for i in np.asarray(ids).ravel()))
+                if e not in self.experts]
+        if workers <= 1 or len(todo) < 2:
+            for e in todo:
                 self.experts[e] = host_expert(self.seed, self.shape, self.layer, e)
+            return
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            made = ex.map(lambda e: (e, host_expert(self.seed, self.shape, self.layer, e)), todo)
+            for e, h in made:
+                self.experts[e] = h
 
     def ensure_for(self, x: np.ndarray) -> np.ndarray:
         """Route x with the oracle router and materialize the selected experts."""

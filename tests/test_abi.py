@@ -114,6 +114,29 @@ def test_given_routing_and_tier_host_checks():
                               a16, 0, 0, a16, None, a16, 0, a16, 0, None) == -1
     assert L.moe_tier_forward(t, 0, ctypes.byref(cfg), ctypes.byref(layer), a16, a16, 32, a16, 1,
                               a16, 2, 0, a16, None, a16, 0, a16, 0, None) == -1
+    # before any slot is mapped: the slab size must be a multiple of 16 that
+    # holds the shape's layout, and every slot must be an index of the slot
+    # stack (at most E slots)
+    big = 1 << 40
+    lay = moe.SlabLayout()
+    assert L.moe_slab_layout_of(ctypes.byref(cfg), ctypes.byref(lay)) == 0
+    hb = ctypes.create_string_buffer(1024)
+    a256 = ctypes.addressof(hb) + (-ctypes.addressof(hb)) % 256
+    rl = moe.LayerC(a256, a256, moe.Experts(), moe.Experts(), None, 0.0)
+
+    def tier_call(tt, slab):
+        return L.moe_tier_forward(tt, 0, ctypes.byref(cfg), ctypes.byref(rl), a256, a256, slab, a256,
+                                  1, a256, 0, 0, a256, None, a256, big, a256, big, None)
+    assert tier_call(t, lay.bytes + 8) == -3
+    assert tier_call(t, lay.bytes - 16) == -2
+    t_wide = L.moe_tier_create(1, cfg.E, cfg.E + 1)
+    assert tier_call(t_wide, lay.bytes) == -2
+    t_pin = L.moe_tier_create_pinned(1, cfg.E, cfg.E - 1, 2)
+    assert tier_call(t_pin, lay.bytes) == -2
+    t_few = L.moe_tier_create(1, cfg.E - 1, 2)   # fewer experts than the layer
+    assert tier_call(t_few, lay.bytes) == -2
+    for tt in (t_wide, t_pin, t_few):
+        L.moe_tier_destroy(tt)
     L.moe_tier_destroy(t)
     # tier objects: invalid sizes give no object
     assert not L.moe_tier_create(0, 8, 4) and not L.moe_tier_create(1, 8, 0)

@@ -7,8 +7,8 @@ import torch
 import int4_expert_gemv_moe_amd as moe
 import oracle
 import synth
-from gpu_util import (assert_close_rows, bias_for, check_routing, device_layer, oracle_layer, say,
-                      to_np)
+from gpu_util import (assert_close_rows, bias_for, device_layer, oracle_block_ref, oracle_layer,
+                      say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,13 +28,16 @@ def _run(layer, x_np, path, flags=0, out=None):
     return to_np(o), to_np(idx), to_np(w)
 
 
-def _oracle_tokens(L, x_np, rows):
-    """Oracle outputs and choice values for the given token rows."""
-    xs = x_np[rows]
-    L.ensure_for(xs)
-    out = oracle.layer_forward(L, xs)
-    _, _, _, choice = oracle.router_topk(L.cfg, xs, L.router_w, L.router_b)
-    return out, choice
+def _sample_rows(S, n=16):
+    """At most n token rows spread evenly over [0, S), first and last included."""
+    return np.unique(np.linspace(0, S - 1, min(n, S)).round().astype(np.int64))
+
+
+def _check_oracle(L, x_np, out, idx, w, rows, what):
+    """The GPU block's rows against the oracle (near-tie tokens on the GPU's
+    routing, see oracle_block_ref)."""
+    ref, _ = oracle_block_ref(L, x_np[rows], idx[rows], w[rows])
+    return assert_close_rows(out[rows], ref, what=what)
 
 
 @pytest.mark.parametrize("path", ["fwd", "batch"])
@@ -43,10 +46,8 @@ def test_tiny_block(path):
     dl = device_layer(0, TINY, 0, b)
     ol = oracle_layer(0, TINY, 0, b)
     x = synth.activations(0, 4, TINY.D)
-    out, idx, _ = _run(dl, x, path)
-    ref, choice = _oracle_tokens(ol, x, np.arange(4))
-    uniq = check_routing(idx, choice, TINY.K)
-    assert_close_rows(out, ref, uniq, what=f"tiny {path}")
+    out, idx, w = _run(dl, x, path)
+    _check_oracle(ol, x, out, idx, w, np.arange(4), f"tiny {path}")
 
 
 @pytest.mark.parametrize("shape,S,bias", [(TINY, 4, "uniform"), (TINY, 1, "uniform"),
@@ -67,19 +68,88 @@ def test_tiny_block(path):
                                           # expert (E = K = 1)
                                           (synth.Shape(D=256, I=32, E=1, K=1), 2, "uniform"),
                                           # widest rows: 4 KB packed gate/up rows
-                                          (synth.Shape(D=8192, I=4096, E=8, K=2), 2, "uniform")])
+                                          (synth.Shape(D=8192, I=4096, E=8, K=2), 2, "uniform"),
+                                          # more than 64 tokens: the 8-wave MFMA kernels
+                                          # with 80-pair tiles
+                                          (MID, 65, "uniform"), (MID, 100, "zero"),
+                                          (MID, 255, "uniform"),
+                                          # every group exactly one full 80-pair tile
+                                          (synth.Shape(D=512, I=256, E=8, K=8), 80, "uniform"),
+                                          # groups of about 127 pairs (a full and a ragged
+                                          # tile) and a shared group of four tiles
+                                          (synth.Shape(D=512, I=256, E=8, K=4), 255, "uniform"),
+                                          # no shared expert, more than 64 tokens
+                                          (synth.Shape(D=256, I=128, E=16, K=4, n_shared=0), 130,
+                                           "uniform")])
 def test_batch_union_equals_per_token_bit_exact(shape, S, bias):
     b = bias_for(bias, 1, shape)
     dl = device_layer(1, shape, 0, b)
     x = synth.activations(1, S, shape.D)
-    a, ia, _ = _run(dl, x, "fwd")
-    c, ic, _ = _run(dl, x, "batch")
+    a, ia, wa = _run(dl, x, "fwd")
+    c, ic, wc = _run(dl, x, "batch")
     assert np.array_equal(ia, ic)
+    assert np.array_equal(wa.view(np.uint32), wc.view(np.uint32))
     assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
     ol = oracle_layer(1, shape, 0, b)
-    ref, choice = _oracle_tokens(ol, x, np.arange(S))
-    uniq = check_routing(ia, choice, shape.K)
-    assert_close_rows(a, ref, uniq, what=f"D={shape.D} E={shape.E} K={shape.K} S={S}")
+    _check_oracle(ol, x, a, ia, wa, _sample_rows(S), f"D={shape.D} E={shape.E} K={shape.K} S={S}")
+
+
+@pytest.mark.parametrize("S,recipe", [(65, "zipf"), (200, "uniform")])
+def test_glm_union_mid_batches(S, recipe):
+    """GLM shape, batches between the verify (64) and the prefill (2048)
+    sizes through the 8-wave MFMA kernels: union == per-token bit for bit,
+    sampled tokens against the oracle."""
+    say(f"glm union S={S} {recipe}")
+    wr = synth.router_w(2, GLM)
+    b = np.zeros(GLM.E, np.float32)
+    if recipe == "zipf":
+        x, _, _ = synth.zipf_activations(2, GLM, S, wr)
+    else:
+        x = synth.activations(22, S, GLM.D)
+    dl = device_layer(2, GLM, 0, b, router_w=wr)
+    out_b, idx_b, w_b = _run(dl, x, "batch")
+    out_f, idx_f, w_f = _run(dl, x, "fwd")
+    assert np.array_equal(idx_b, idx_f)
+    assert np.array_equal(out_b.view(np.uint32), out_f.view(np.uint32))
+    counts = np.bincount(idx_b.ravel(), minlength=GLM.E)
+    say(f"  union size {int((counts > 0).sum())}, largest group {int(counts.max())} pairs")
+    ol = oracle_layer(2, GLM, 0, b, router_w=wr)
+    _check_oracle(ol, x, out_b, idx_b, w_b, _sample_rows(S), f"glm union S={S}")
+
+
+@pytest.mark.parametrize("shape,S", [(MID, 33), (MID, 64), (MID, 100), (TINY, 48)])
+def test_batch_routed_repeated_and_clamped_experts(shape, S):
+    """Given routing may repeat an expert within a token and name experts
+    outside [0, E), which the library clamps into the stack: one expert then
+    holds more pairs than a batch of S tokens would give it, up to several
+    tiles.  The union equals the per-token routed call bit for bit, and the
+    oracle on the clamped routing."""
+    say(f"batch routed repeats D={shape.D} E={shape.E} K={shape.K} S={S}")
+    b = bias_for("uniform", 3, shape)
+    dl = device_layer(3, shape, 0, b)
+    K, E = shape.K, shape.E
+    rng = np.random.default_rng(S)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(S)]).astype(np.int32)
+    idx[:, 0] = 3                      # expert 3 in every token ...
+    idx[::2, K - 1] = 3                # ... and twice in every other token
+    idx[1::3, 1 % K] = E + 7           # clamps to E - 1
+    idx[2::5, K // 2] = -4             # clamps to 0
+    w = rng.uniform(0.05, 2.5, size=(S, K)).astype(np.float32)
+    x = synth.activations(23, S, shape.D)
+    xt = torch.from_numpy(x).cuda()
+    it, wt = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()
+    o_f = moe.moe_layer_forward_routed(dl, xt, it, wt, moe.Workspace(dl.cfg, S, moe.WS_FORWARD))
+    o_b = moe.moe_layer_forward_routed(dl, xt, it, wt, moe.Workspace(dl.cfg, S, moe.WS_BATCH),
+                                       fn_name="moe_layer_forward_batch_routed")
+    torch.cuda.synchronize()
+    a, c = to_np(o_f), to_np(o_b)
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+    ol = oracle_layer(3, shape, 0, b)
+    clamped = np.clip(idx, 0, E - 1)
+    ol.ensure(clamped)
+    rows = _sample_rows(S, 12)
+    ref = oracle.layer_forward_routed(ol, x[rows], clamped[rows], w[rows])
+    assert_close_rows(a[rows], ref, what=f"batch routed S={S}")
 
 
 def test_accumulate_flag_and_residual():
@@ -126,52 +196,57 @@ def test_glm_decode_tokens():
     dl = device_layer(0, GLM, 0, b)
     ol = oracle_layer(0, GLM, 0, b)
     x = synth.activations(11, 4, GLM.D)
-    outs, idxs = [], []
+    outs, idxs, ws = [], [], []
     for s in range(4):
         say(f"glm decode token {s}")
-        o, i, _ = _run(dl, x[s:s + 1], "fwd")
+        o, i, w = _run(dl, x[s:s + 1], "fwd")
         outs.append(o[0])
         idxs.append(i[0])
-    ref, choice = _oracle_tokens(ol, x, np.arange(4))
-    uniq = check_routing(np.stack(idxs), choice, GLM.K)
-    assert_close_rows(np.stack(outs), ref, uniq, what="glm decode")
+        ws.append(w[0])
+    _check_oracle(ol, x, np.stack(outs), np.stack(idxs), np.stack(ws), np.arange(4), "glm decode")
 
 
 def test_glm_batched_verify_zipf():
     """GLM shape, 64 tokens with Zipf(1.1)-skewed routing through the union
-    path; sampled tokens against the oracle; batch == per-token on the GPU."""
+    path; 16 sampled tokens against the oracle; batch == per-token on the GPU."""
     wr = synth.router_w(0, GLM)
     b = np.zeros(GLM.E, np.float32)
     x, _, _ = synth.zipf_activations(0, GLM, 64, wr)
     dl = device_layer(0, GLM, 0, b, router_w=wr)
-    out_b, idx_b, _ = _run(dl, x, "batch")
+    out_b, idx_b, w_b = _run(dl, x, "batch")
     out_f, idx_f, _ = _run(dl, x, "fwd")
     assert np.array_equal(idx_b, idx_f)
     assert np.array_equal(out_b.view(np.uint32), out_f.view(np.uint32))
     counts = np.bincount(idx_b.ravel(), minlength=GLM.E)
     say(f"  union size {int((counts > 0).sum())}, hottest expert {int(counts.max())} tokens")
-    rows = np.array([0, 21, 42, 63])
     ol = oracle_layer(0, GLM, 0, b, router_w=wr)
-    ref, choice = _oracle_tokens(ol, x, rows)
-    uniq = check_routing(idx_b[rows], choice, GLM.K)
-    assert_close_rows(out_b[rows], ref, uniq, what="glm zipf verify")
+    _check_oracle(ol, x, out_b, idx_b, w_b, _sample_rows(64), "glm zipf verify")
 
 
 @pytest.mark.slow
 def test_glm_prefill_2048_bf16():
     """GLM shape, 2048 tokens whose activations are bf16 values, uniform
-    routing (b = 0): sampled tokens against the oracle."""
+    routing (b = 0), through the union path: two calls give the same bits,
+    the union equals the per-token path bit for bit on every token, and 64
+    tokens spread over the batch match the oracle."""
     b = np.zeros(GLM.E, np.float32)
     x = synth.bf16_to_f32(synth.bf16_bits(synth.activations(12, 2048, GLM.D)))
     dl = device_layer(1, GLM, 0, b)
-    out_b, idx_b, _ = _run(dl, x, "batch")
+    say("prefill: union path twice")
+    out_b, idx_b, w_b = _run(dl, x, "batch")
+    out_b2, idx_b2, _ = _run(dl, x, "batch")
+    assert np.array_equal(idx_b, idx_b2)
+    assert np.array_equal(out_b.view(np.uint32), out_b2.view(np.uint32))
+    say("prefill: per-token path")
+    out_f, idx_f, w_f = _run(dl, x, "fwd")
+    assert np.array_equal(idx_b, idx_f)
+    assert np.array_equal(w_b.view(np.uint32), w_f.view(np.uint32))
+    assert np.array_equal(out_b.view(np.uint32), out_f.view(np.uint32))
     counts = np.bincount(idx_b.ravel(), minlength=GLM.E)
     say(f"  tokens per expert: min {counts.min()} max {counts.max()}")
-    rows = np.array([0, 1000, 2047])
     ol = oracle_layer(1, GLM, 0, b)
-    ref, choice = _oracle_tokens(ol, x, rows)
-    uniq = check_routing(idx_b[rows], choice, GLM.K)
-    assert_close_rows(out_b[rows], ref, uniq, what="glm prefill")
+    say("prefill: 64 tokens through the oracle")
+    _check_oracle(ol, x, out_b, idx_b, w_b, _sample_rows(2048, 64), "glm prefill")
 
 
 def test_error_codes():

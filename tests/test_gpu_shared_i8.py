@@ -8,7 +8,8 @@ import torch
 import int4_expert_gemv_moe_amd as moe
 import oracle
 import synth
-from gpu_util import assert_close_rows, bias_for, check_routing, device_layer, oracle_layer, say, to_np
+from gpu_util import (assert_close_rows, bias_for, device_layer, oracle_block_ref, oracle_layer, say,
+                      to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,24 +25,38 @@ def _shared8(seed, shape):
     return h8, dev
 
 
-@pytest.mark.parametrize("shape,S,acc", [(TINY, 4, False), (TINY, 3, True), (GLM, 2, False),
-                                         (GLM, 1, True)])
-def test_layer_with_int8_shared_expert(shape, S, acc):
-    say(f"shared_i8 D={shape.D} S={S} acc={acc}")
+MID = synth.Shape(D=512, I=256, E=64, K=8)
+
+
+@pytest.mark.parametrize("shape,S,acc,topp", [(TINY, 4, False, 0.0), (TINY, 3, True, 0.0),
+                                              (GLM, 2, False, 0.0), (GLM, 1, True, 0.0),
+                                              (MID, 24, False, 0.0), (MID, 9, True, 0.6),
+                                              (GLM, 5, False, 0.7)])
+def test_layer_with_int8_shared_expert(shape, S, acc, topp):
+    say(f"shared_i8 D={shape.D} S={S} acc={acc} topp={topp}")
     b = bias_for("uniform", 0, shape)
     dl = device_layer(0, shape, 0, b)
     ol = oracle_layer(0, shape, 0, b)
+    if topp:
+        c = dl.cfg
+        dl = moe.DeviceLayer(moe.config(c.D, c.I, c.E, c.K, c.n_shared, c.routed_scale, topp),
+                             dl.router_w, dl.router_b, dl.routed, dl.shared)
+        ol.cfg.expert_topp = topp
     h8, d8 = _shared8(7, shape)
     x = synth.activations(13, S, shape.D)
     base = synth.activations(14, S, shape.D)
+    xt = torch.from_numpy(x).cuda()
     ws = moe.Workspace(dl.cfg, S, moe.WS_SHARED8)
     out = torch.from_numpy(base.copy()).cuda() if acc else None
-    o = moe.moe_layer_forward_shared_i8(dl, d8, torch.from_numpy(x).cuda(), ws, out=out,
+    o = moe.moe_layer_forward_shared_i8(dl, d8, xt, ws, out=out,
                                         flags=moe.F_ACCUMULATE if acc else 0)
+    # the GPU's routing: the per-token path selects exactly what the router
+    # and top-K kernels select for the same tokens
+    idx, w, _ = moe.moe_router_topk(dl.cfg, xt, dl.router_w, dl.router_b,
+                                    moe.Workspace(dl.cfg, S, moe.WS_ROUTER))
     torch.cuda.synchronize()
-    ol.ensure_for(x)
-    ref = oracle.layer_forward_shared_i8(ol, h8, x, out=base.copy() if acc else None,
-                                         flags=1 if acc else 0)
-    idx, _, _, choice = oracle.router_topk(ol.cfg, x, ol.router_w, ol.router_b)
-    uniq = check_routing(idx, choice, shape.K)
-    assert_close_rows(to_np(o), ref, uniq, what=f"shared int8 S={S}")
+    idx, w = to_np(idx), to_np(w)
+    keff = np.array([oracle.expert_keff(w[s], topp) for s in range(S)]) if topp else None
+    ref, _ = oracle_block_ref(ol, x, idx, w, keff_gpu=keff, base=base if acc else None,
+                              shared8=h8)
+    assert_close_rows(to_np(o), ref, what=f"shared int8 S={S}")

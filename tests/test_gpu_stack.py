@@ -15,7 +15,7 @@ import torch
 import int4_expert_gemv_moe_amd as moe
 import oracle
 import synth
-from gpu_util import assert_close_rows, check_routing, device_layer, oracle_layer, say, to_np
+from gpu_util import assert_close_rows, device_layer, oracle_block_ref, oracle_layer, say, to_np
 from int4_expert_gemv_moe_amd.stack import Stack
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,8 @@ def _check_layers(stack, taps, x_final, check, union):
         x_next = taps[l + 1] if l + 1 < nl else x_final
         xn = moe.moe_rmsnorm(x_in, stack.gamma, EPS)
         idx = torch.empty(S, GLM.K, dtype=torch.int32, device="cuda")
-        out = fn(stack.layers[l], xn, ws, topk_idx=idx)
+        w = torch.empty(S, GLM.K, dtype=torch.float32, device="cuda")
+        out = fn(stack.layers[l], xn, ws, topk_idx=idx, topk_w=w)
         torch.cuda.synchronize()
         x_in_h, xn_h, out_h = to_np(x_in), to_np(xn), to_np(out)
         # the stack's update is exactly x + block(rmsnorm(x)) in float32
@@ -64,11 +65,8 @@ def _check_layers(stack, taps, x_final, check, union):
         xn_ref = oracle.rmsnorm(x_in_h, gamma, EPS)
         np.testing.assert_allclose(xn_h, xn_ref, rtol=2e-6, atol=1e-6)
         L = oracle_layer(SEED, GLM, l, synth.zipf_bias(SEED, GLM.E, l, BETA))
-        L.ensure_for(xn_h)
-        ref = oracle.layer_forward(L, xn_h)
-        _, _, _, choice = oracle.router_topk(L.cfg, xn_h, L.router_w, L.router_b)
-        uniq = check_routing(to_np(idx), choice, GLM.K)
-        assert_close_rows(out_h, ref, uniq, what=f"stack layer {l} ({'union' if union else 'per-token'})")
+        ref, _ = oracle_block_ref(L, xn_h, to_np(idx), to_np(w))
+        assert_close_rows(out_h, ref, what=f"stack layer {l} ({'union' if union else 'per-token'})")
         del L
 
 

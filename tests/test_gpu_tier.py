@@ -9,7 +9,8 @@ import torch
 import int4_expert_gemv_moe_amd as moe
 import oracle
 import synth
-from gpu_util import bias_for, device_layer, say, to_np
+from gpu_util import (assert_close_rows, bias_for, device_layer, oracle_block_ref, oracle_layer,
+                      say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +31,14 @@ def _bits(t):
     return to_np(t).view(np.uint32)
 
 
+def _vs_oracle(L, x, out, idx, w, rows, what):
+    """Rows of a GPU result against the oracle's block on the same tokens
+    (tokens near a routing tie on the GPU's routing)."""
+    xh = to_np(x)[rows]
+    ref, _ = oracle_block_ref(L, xh, to_np(idx)[rows], to_np(w)[rows])
+    assert_close_rows(to_np(out)[rows], ref, what=what)
+
+
 @pytest.mark.parametrize("shape,S", [(TINY, 4), (MID, 5), (GLM, 1), (GLM, 3)])
 def test_routed_call_equals_per_token_path(shape, S):
     say(f"routed call D={shape.D} E={shape.E} S={S}")
@@ -39,6 +48,11 @@ def test_routed_call_equals_per_token_path(shape, S):
     out = moe.moe_layer_forward_routed(dl, x, idx, w, moe.Workspace(dl.cfg, S, moe.WS_FORWARD))
     torch.cuda.synchronize()
     assert np.array_equal(_bits(out), _bits(ref))
+    # the oracle's given-routing block on the same routing
+    L = oracle_layer(5, shape, 0, bias_for("uniform", 5, shape))
+    L.ensure(to_np(idx))
+    want = oracle.layer_forward_routed(L, to_np(x), to_np(idx), to_np(w))
+    assert_close_rows(to_np(out), want, what=f"routed call S={S}")
 
 
 def test_routed_call_clamps_indices():
@@ -59,7 +73,9 @@ def test_routed_call_clamps_indices():
                                                    (GLM, 24, 1, 12)])
 def test_tiered_layer_matches_resident_layer(shape, n_slots, S, calls):
     say(f"tiered D={shape.D} E={shape.E} slots={n_slots} S={S}")
-    dl = device_layer(7, shape, 0, bias_for("zipf", 7, shape, 0, 0.05))
+    b = bias_for("zipf", 7, shape, 0, 0.05)
+    dl = device_layer(7, shape, 0, b)
+    L = oracle_layer(7, shape, 0, b)
     tl = moe.TieredLayer.from_device_layer(dl, n_slots)
     cache = oracle.ExpertCache(1, n_slots)
     wsr = moe.Workspace(dl.cfg, S, moe.WS_ROUTER)
@@ -68,10 +84,12 @@ def test_tiered_layer_matches_resident_layer(shape, n_slots, S, calls):
     hits = 0
     for c in range(calls):
         x = x_all[c * S:(c + 1) * S]
-        ref, idx, _ = _resident(dl, x)
+        ref, idx, w = _resident(dl, x)
         out, misses = tl.forward(x, wsr, ws)
         torch.cuda.synchronize()
         assert np.array_equal(_bits(out), _bits(ref)), f"call {c}"
+        if c < 3 or shape is not GLM:
+            _vs_oracle(L, x, out, idx, w, np.arange(S), f"tiered call {c}")
         flat = to_np(idx).ravel().tolist()
         eids = [e for i, e in enumerate(flat) if e not in flat[:i]]  # first appearance
         expect = [cache.get(0, e)[1] for e in eids]
@@ -113,7 +131,9 @@ def test_batch_routed_call_clamps_indices():
 @pytest.mark.parametrize("shape,n_slots,S,calls", [(MID, 48, 6, 12), (GLM, 192, 64, 3)])
 def test_tiered_union_matches_resident_union(shape, n_slots, S, calls):
     say(f"tiered union D={shape.D} E={shape.E} slots={n_slots} S={S}")
-    dl = device_layer(13, shape, 0, bias_for("zipf", 13, shape, 0, 0.05))
+    b = bias_for("zipf", 13, shape, 0, 0.05)
+    dl = device_layer(13, shape, 0, b)
+    L = oracle_layer(13, shape, 0, b)
     tl = moe.TieredLayer.from_device_layer(dl, n_slots)
     cache = oracle.ExpertCache(1, n_slots)
     wsr = moe.Workspace(dl.cfg, S, moe.WS_ROUTER)
@@ -123,10 +143,14 @@ def test_tiered_union_matches_resident_union(shape, n_slots, S, calls):
     for c in range(calls):
         x = x_all[c * S:(c + 1) * S]
         idx = torch.empty(S, shape.K, dtype=torch.int32, device="cuda")
-        ref = moe.moe_layer_forward_batch(dl, x, wsb, topk_idx=idx)
+        w = torch.empty(S, shape.K, dtype=torch.float32, device="cuda")
+        ref = moe.moe_layer_forward_batch(dl, x, wsb, topk_idx=idx, topk_w=w)
         out, misses = tl.forward(x, wsr, ws, union=True)
         torch.cuda.synchronize()
         assert np.array_equal(_bits(out), _bits(ref)), f"call {c}"
+        if c == 0:
+            rows = np.unique(np.linspace(0, S - 1, min(S, 8)).round().astype(np.int64))
+            _vs_oracle(L, x, out, idx, w, rows, f"tiered union call {c}")
         flat = to_np(idx).ravel().tolist()
         eids = [e for i, e in enumerate(flat) if e not in flat[:i]]
         assert misses == sum(cache.get(0, e)[1] for e in eids), f"call {c}"
@@ -140,15 +164,19 @@ def test_tiered_layer_with_pinned_slots_matches_resident(shape, n_slots, n_pinne
     slots: the slab copies of a rebalance are ordered after the call that
     decided them, and every call still returns the resident layer's bits."""
     say(f"pinned tier D={shape.D} E={shape.E} lru={n_slots} pinned={n_pinned}")
-    dl = device_layer(14, shape, 0, bias_for("zipf", 14, shape, 0, 0.05))
+    b = bias_for("zipf", 14, shape, 0, 0.05)
+    dl = device_layer(14, shape, 0, b)
+    L = oracle_layer(14, shape, 0, b)
     tl = moe.TieredLayer.from_device_layer(dl, n_slots, n_pinned=n_pinned)
     wsr = moe.Workspace(dl.cfg, 1, moe.WS_ROUTER)
     ws = moe.Workspace(dl.cfg, 1, moe.WS_FORWARD)
     x_all = torch.from_numpy(synth.activations(37, calls, shape.D)).cuda()
     for c in range(calls):
         x = x_all[c:c + 1]
-        ref, _, _ = _resident(dl, x)
+        ref, idx, w = _resident(dl, x)
         out, _ = tl.forward(x, wsr, ws)
         torch.cuda.synchronize()
         assert np.array_equal(_bits(out), _bits(ref)), f"call {c}"
+        if c % 8 == 7:  # after rebalances have moved experts into pinned slots
+            _vs_oracle(L, x, out, idx, w, np.arange(1), f"pinned tier call {c}")
     say(f"  hits/misses {tl.tier.stats()}")

@@ -9,7 +9,7 @@ import torch
 import int4_expert_gemv_moe_amd as moe
 import oracle
 import synth
-from gpu_util import (assert_close_rows, bias_for, check_routing, device_layer, oracle_layer, say,
+from gpu_util import (assert_close_rows, bias_for, device_layer, oracle_block_ref, oracle_layer, say,
                       to_np)
 
 pytestmark = pytest.mark.gpu
@@ -55,15 +55,9 @@ def test_topp_against_oracle(shape, S, p):
         assert [oracle.expert_keff(w[s], p) for s in range(S)] == keff.tolist()
         ol = oracle_layer(8, shape, 0, b)
         ol.cfg.expert_topp = p
-        ol.ensure_for(x)
-        ref = oracle.layer_forward(ol, x)
-        _, ow, _, choice = oracle.router_topk(ol.cfg, x, ol.router_w, ol.router_b)
-        uniq = check_routing(idx, choice, shape.K)
-        same_keff = np.array([oracle.expert_keff(ow[s], p) == keff[s] for s in range(S)])
-        rows = uniq & same_keff
-        assert rows.sum() >= S - 1
-        assert_close_rows(out[rows], ref[rows], np.ones(int(rows.sum()), bool),
-                          what=f"top-p {p} {path}")
+        ref, uniq = oracle_block_ref(ol, x, idx, w, keff_gpu=keff)
+        assert uniq.sum() >= S - 1
+        assert_close_rows(out, ref, what=f"top-p {p} {path}")
         say(f"  {path}: keff {keff.tolist()}")
 
 
