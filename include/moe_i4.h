@@ -28,10 +28,10 @@
  *     moe_status.  Arguments are validated on the host before anything is
  *     enqueued; an invalid call enqueues nothing.  No call allocates, frees or
  *     keeps device memory: scratch space comes from the caller's workspace.
- *   - Calls that take a workspace need it zero-filled once by
- *     moe_workspace_init; every call leaves its counters at zero again.  Calls
- *     that share one workspace must not overlap (use one workspace per
- *     concurrent stream).
+ *   - A workspace holds only values written and read within one call: its
+ *     contents before a call do not matter (no zero fill is needed) and are
+ *     undefined after it.  Calls that share one workspace must not overlap
+ *     (use one workspace per concurrent stream).
  *   - Shape limits: D a multiple of 256 (the router's lane order), I a
  *     multiple of 32, D/2 and I/2 at most 4096 bytes per packed row,
  *     1 <= K <= E <= 1024, K <= 64, n_shared 0 or 1, S >= 1 (MOE_ESHAPE
@@ -157,7 +157,8 @@ const char *moe_status_str(int status);
  * Returns 0 for invalid arguments. */
 size_t moe_workspace_bytes(const moe_config *cfg, int S, int which);
 
-/* Zero-fill a workspace (once, before its first use). */
+/* Zero-fill a workspace.  Not needed by any call (a workspace's contents
+ * before a call do not matter); kept for callers that want defined memory. */
 int moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Section 06 converter: quantize w[O][C] (float32) to the int4 container,

@@ -5,7 +5,6 @@
 #include <vector>
 #include <atomic>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 
 #include "moe_kernels.h"
@@ -69,27 +68,21 @@ size_t shared8_bytes(const moe_config &c, int S, size_t *fwd) {
 }
 
 // Workgroup counts of the per-token path (rows of a phase are split evenly
-// over its workgroups).  MOE_DECODE_BLOCKS="a,b,c,d" overrides them for
-// tuning: shared gate/up (phase A), routed gate/up per slot and shared down
-// (phase B), routed down (phase C).
+// over its workgroups): shared gate/up (phase A), routed gate/up over the
+// concatenated slots and shared down (phase B), routed down (phase C).  The
+// counts were swept on the device at the GLM shape.
 struct DecodeShape {
   int gu_fx, gu_rt, dn_fx, dn;
 };
 
 DecodeShape decode_shape(const moe_config &c) {
-  static const DecodeShape env = [] {
-    DecodeShape d{0, 0, 0, 0};
-    if (const char *v = std::getenv("MOE_DECODE_BLOCKS"))
-      std::sscanf(v, "%d,%d,%d,%d", &d.gu_fx, &d.gu_rt, &d.dn_fx, &d.dn);
-    return d;
-  }();
   DecodeShape d;
-  d.gu_fx = env.gu_fx > 0 ? env.gu_fx : 128;
-  d.gu_rt = env.gu_rt > 0 ? env.gu_rt : 256;
-  d.dn_fx = env.dn_fx > 0 ? env.dn_fx : 192;
+  d.gu_fx = 128;
+  d.gu_rt = 256;
+  d.dn_fx = 192;
   // phase C: one pass of rows per workgroup
   const int cr = decode_c_rows_per_pass(c.I);
-  d.dn = env.dn > 0 ? env.dn : (c.D + cr - 1) / cr;
+  d.dn = (c.D + cr - 1) / cr;
   // at least 8 rows per workgroup, at most the rows whose scales fit in LDS
   // (512 for gate/up, 256 for down)
   auto clampn = [](int n, int rows, int maxrows) {
@@ -738,6 +731,7 @@ int moe_layer_forward_routed(const moe_config *cfg, const moe_layer *layer, cons
 }
 
 }  // extern "C"
+
 
 namespace {
 

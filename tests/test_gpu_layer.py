@@ -289,3 +289,23 @@ def test_per_token_selection_repeated_calls(S):
     torch.cuda.synchronize()
     assert torch.equal(idx.view(-1, cfg.K), ridx)
     assert torch.equal(w.view(-1, cfg.K).view(torch.int32), rw.view(torch.int32))
+
+
+@pytest.mark.parametrize("path,shape,S", [("fwd", MID, 5), ("batch", MID, 70), ("fwd", GLM, 1),
+                                          ("batch", GLM, 4)])
+def test_workspace_contents_do_not_matter(path, shape, S):
+    """No kernel reads workspace memory it has not written in the same call:
+    a workspace filled with 0xFF bytes (NaN floats, -1 integers) gives the
+    bits of a zero-filled one."""
+    b = bias_for("uniform", 5, shape)
+    dl = device_layer(5, shape, 0, b)
+    x = torch.from_numpy(synth.activations(24, S, shape.D)).cuda()
+    which = moe.WS_FORWARD if path == "fwd" else moe.WS_BATCH
+    fn = moe.moe_layer_forward if path == "fwd" else moe.moe_layer_forward_batch
+    clean = moe.Workspace(dl.cfg, S, which)
+    dirty = moe.Workspace(dl.cfg, S, which)
+    dirty.view.fill_(0xFF)
+    a = fn(dl, x, clean)
+    c = fn(dl, x, dirty)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(a).view(np.uint32), to_np(c).view(np.uint32))
