@@ -27,7 +27,8 @@
  *   - All calls are asynchronous on the given HIP stream and return a
  *     moe_status.  Arguments are validated on the host before anything is
  *     enqueued; an invalid call enqueues nothing.  No call allocates, frees or
- *     keeps device memory: scratch space comes from the caller's workspace.
+ *     keeps device memory: scratch space comes from the caller's workspace
+ *     (moe_layer_forward_noalloc: from a library-held array, see there).
  *   - A workspace holds only values written and read within one call: its
  *     contents before a call do not matter (no zero fill is needed) and are
  *     undefined after it.  Calls that share one workspace must not overlap
@@ -312,6 +313,21 @@ int moe_layer_forward_shared_i8(const moe_config *cfg, const moe_layer *layer,
 int moe_layer_forward(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                       float *out, unsigned flags, const moe_probe *probe, void *ws,
                       size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a library-held device
+ * array of MOE_NOALLOC_WS_BYTES per GPU, allocated with the library's code
+ * object and kept until the process ends; the call itself allocates nothing.
+ * Calls whose moe_workspace_bytes(cfg, S, 0) exceeds MOE_NOALLOC_WS_BYTES
+ * return MOE_EWORKSPACE (16 MiB holds a GLM-shape call of up to 128 tokens).
+ * Every call on one GPU uses the same array: calls that overlap on one GPU
+ * (different streams, or different host threads) race and must be
+ * serialized by the caller.  Arguments, flags and results are as in
+ * moe_layer_forward with no probe. */
+#define MOE_NOALLOC_WS_BYTES (16u << 20)
+int moe_layer_forward_noalloc(const moe_config *cfg, const moe_layer *layer, const float *x,
+                              int S, float *out, unsigned flags, hipStream_t stream);
 
 /* The same block through the unique-expert union (section 11): tokens are
  * grouped by selected expert and every selected expert's weights are read

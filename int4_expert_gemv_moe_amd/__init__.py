@@ -87,6 +87,7 @@ def lib():
         L.moe_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
         L.moe_layer_forward_batch.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
+        L.moe_layer_forward_noalloc.argtypes = [vp, vp, vp, i32, vp, u32, vp]
         L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, f32, vp, vp]
         L.moe_stream_read.argtypes = [vp, sz, vp, vp]
         L.moe_layer_forward_routed.argtypes = [vp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
@@ -112,7 +113,7 @@ def lib():
                      "moe_expert_swiglu_i4", "moe_quantize_rows_i8", "moe_expert_swiglu_i8",
                      "moe_pack_int2", "moe_expert_swiglu_i2", "moe_quant_act_b32",
                      "moe_expert_swiglu_i4_b32", "moe_mla_decode", "moe_layer_forward_shared_i8",
-                     "moe_layer_forward", "moe_layer_forward_batch",
+                     "moe_layer_forward", "moe_layer_forward_batch", "moe_layer_forward_noalloc",
                      "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
                      "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
                      "moe_slab_layout_of", "moe_tier_map",
@@ -554,6 +555,27 @@ def moe_layer_forward_batch(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, 
     """Unique-expert union path: each selected expert is read once per call."""
     return _layer_call("moe_layer_forward_batch", layer, x, out, flags, ws, topk_idx, topk_w,
                        ev_gateup, ev_down, stream, norm_gamma, norm_eps, keff)
+
+
+NOALLOC_WS_BYTES = 16 << 20
+
+
+def moe_layer_forward_noalloc(layer: DeviceLayer, x: torch.Tensor, out=None, flags: int = 0,
+                              stream=None, norm_gamma=None, norm_eps: float = 1e-5):
+    """moe_layer_forward on the library's own device scratch (no workspace)."""
+    _dev(x, torch.float32, "x")
+    S = x.shape[0]
+    if out is None:
+        out = torch.empty(S, layer.cfg.D, dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    if norm_gamma is not None:
+        _dev(norm_gamma, torch.float32, "norm_gamma")
+        flags |= F_PRENORM
+    L = layer.cstruct(norm_gamma, norm_eps)
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(layer.cfg), ctypes.byref(L), _ptr(x), S,
+                                           _ptr(out), flags, ctypes.c_void_p(_stream(stream))),
+           "moe_layer_forward_noalloc")
+    return out
 
 
 def moe_stream_read(buf: torch.Tensor, stream=None) -> torch.Tensor:

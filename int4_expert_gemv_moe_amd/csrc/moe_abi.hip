@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <vector>
 #include <atomic>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 
@@ -732,6 +733,53 @@ int moe_layer_forward_routed(const moe_config *cfg, const moe_layer *layer, cons
 
 }  // extern "C"
 
+// ---- moe_layer_forward_noalloc: the per-token path on a library-held scratch ----
+//
+// One file-scope device array per GPU serves as the workspace.  In host code
+// `noalloc_scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device with hipGetSymbolAddress (with that
+// device current) and only that address is ever passed to a kernel.  No
+// kernel of the per-token path needs the workspace to start at zero, so the
+// array is never cleared.
+static __device__ __align__(256) unsigned char noalloc_scratch[MOE_NOALLOC_WS_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_noalloc_ptr[kMaxDevices];
+std::mutex g_noalloc_mu;
+
+int noalloc_ptr(void **p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EDEVICE;
+  void *v = g_noalloc_ptr[dev].load(std::memory_order_acquire);
+  if (!v) {
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    v = g_noalloc_ptr[dev].load(std::memory_order_relaxed);
+    if (!v) {
+      if (hipGetSymbolAddress(&v, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || !v) return MOE_EHIP;
+      g_noalloc_ptr[dev].store(v, std::memory_order_release);
+    }
+  }
+  *p = v;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_layer_forward_noalloc(const moe_config *cfg, const moe_layer *layer,
+                                         const float *x, int S, float *out, unsigned flags,
+                                         hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (S < 1) return MOE_EINVAL;
+  if (carve(*cfg, S, W_FWD, nullptr, nullptr) > (size_t)MOE_NOALLOC_WS_BYTES) return MOE_EWORKSPACE;
+  MOE_TRY(check_device());
+  void *ws = nullptr;
+  MOE_TRY(noalloc_ptr(&ws));
+  return layer_forward_impl(cfg, layer, x, S, nullptr, nullptr, out, flags, nullptr, ws,
+                            (size_t)MOE_NOALLOC_WS_BYTES, stream);
+}
 
 namespace {
 

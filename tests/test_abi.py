@@ -282,3 +282,14 @@ def test_shared_i8_layer_host_checks():
     assert call(cfg, ctypes.byref(e8), a, 2, need) == -1      # PRENORM is not supported
     assert call(cfg, ctypes.byref(e8), a + 4, 0, need) == -3  # x misaligned
     assert call(cfg, ctypes.byref(e8), a, 0, need - 16) == -4
+
+
+def test_noalloc_entry_point_refuses_oversize_calls_on_the_host():
+    """moe_layer_forward_noalloc compares the call's workspace need with its
+    fixed scratch before touching the device."""
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    cfg = moe.config(6144, 2048, 256, 8)
+    assert L.moe_layer_forward_noalloc(ctypes.byref(cfg), None, None, 129, None, 0, None) == -4
+    assert L.moe_layer_forward_noalloc(ctypes.byref(cfg), None, None, 0, None, 0, None) == -1
+    assert L.moe_workspace_bytes(ctypes.byref(cfg), 128, 0) <= moe.NOALLOC_WS_BYTES
