@@ -61,6 +61,8 @@ typedef enum {
   MOE_EDEVICE = -6     /* current device is not a gfx950 */
 } moe_status;
 
+/* Element types of activation inputs (passed as int: any other value is
+ * refused with MOE_EINVAL). */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Flags of the layer calls. */
@@ -177,7 +179,7 @@ int moe_quantize_rows_i8(const float *w, int O, int C, int8_t *q, float *scale,
 
 /* Section 12: per-row int8 quantization of x[S][D] (float32, or bf16 widened
  * exactly).  Outputs xq[S][D] and sx[S].  D must be a multiple of 8. */
-int moe_quant_act_i8(const void *x, moe_dtype dtype, int S, int D, int8_t *xq, float *sx,
+int moe_quant_act_i8(const void *x, int dtype, int S, int D, int8_t *xq, float *sx,
                      hipStream_t stream);
 
 /* Section 11 router for S tokens x[S][D]: logits = x . router_w^T in float32,

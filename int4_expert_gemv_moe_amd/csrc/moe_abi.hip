@@ -556,7 +556,7 @@ int moe_expert_swiglu_i4_b32(const moe_config *cfg, const int8_t *xq, const floa
   return MOE_OK;
 }
 
-int moe_quant_act_i8(const void *x, moe_dtype dtype, int S, int D, int8_t *xq, float *sx,
+int moe_quant_act_i8(const void *x, int dtype, int S, int D, int8_t *xq, float *sx,
                      hipStream_t stream) {
   if (!x || !xq || !sx) return MOE_EINVAL;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EINVAL;

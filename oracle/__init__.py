@@ -40,7 +40,8 @@ class Layer(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        path = os.path.join(HERE, "libmoe_ref.so")
+        # MOE_REF_LIB may name another build of the same source (e.g. a sanitizer build)
+        path = os.environ.get("MOE_REF_LIB") or os.path.join(HERE, "libmoe_ref.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: run oracle/build.py (or __graft_entry__.build())")
         L = ctypes.CDLL(path)

@@ -40,7 +40,8 @@ _dev = None
 def _load_host():
     global _host
     if _host is None:
-        path = os.path.join(HERE, "libsynth_host.so")
+        # SYNTH_HOST_LIB may name another build of the same source (e.g. a sanitizer build)
+        path = os.environ.get("SYNTH_HOST_LIB") or os.path.join(HERE, "libsynth_host.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: run synth/build.py (or __graft_entry__.build())")
         lib = ctypes.CDLL(path)
