@@ -627,11 +627,39 @@ def bench_shared_i8(layers, x, steps: int = 512):
     us = e0.elapsed_time(e1) * 1e3 / steps
     nbytes = K * EXPERT_BYTES + EXPERT_I8_BYTES + ROUTER_BYTES + 2 * D * 4
     log(f"decode with int8 shared expert: {us:.2f} us/token")
-    return {"workload": "GLM-shape MoE layer decode, 1 token/step, shared expert in the int8 "
-                        "format (moe_layer_forward_shared_i8), 8 cold layer replicas",
-            "steps": steps, "us_per_token": round(us, 3), "bytes_per_token": int(nbytes),
-            "GBps": round(nbytes / us / 1e3, 1),
-            "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    res = {"workload": "GLM-shape MoE layer decode, 1 token/step, shared expert in the int8 "
+                       "format (moe_layer_forward_shared_i8: inside the per-token launches), "
+                       "8 cold layer replicas",
+           "steps": steps, "us_per_token": round(us, 3), "bytes_per_token": int(nbytes),
+           "GBps": round(nbytes / us / 1e3, 1),
+           "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    # the 64-token Zipf verify through the union path with the int8 shared expert
+    import numpy as np
+    S = 64
+    wr = synth.router_w(0, synth.GLM)
+    x_np, _, _ = synth.zipf_activations(0, synth.GLM, S, wr)
+    zl = moe.DeviceLayer(cfg, torch.from_numpy(wr).cuda(),
+                         torch.zeros(E, dtype=torch.float32, device="cuda"), layers[0].routed,
+                         layers[0].shared)
+    xv = torch.from_numpy(x_np).cuda()
+    wsb = moe.Workspace(cfg, S, moe.WS_BATCH)
+    outb = torch.empty(S, D, dtype=torch.float32, device="cuda")
+    call = lambda: moe.moe_layer_forward_shared_i8(zl, views[0], xv, wsb, out=outb,
+                                                   fn_name="moe_layer_forward_batch_shared_i8")
+    call()
+    idx, _, _ = moe.moe_router_topk(cfg, xv, zl.router_w, zl.router_b,
+                                    moe.Workspace(cfg, S, moe.WS_ROUTER))
+    torch.cuda.synchronize()
+    used = int(np.unique(idx.cpu().numpy()).size)
+    cold = timed_cold(call, 20)
+    vb = used * EXPERT_BYTES + EXPERT_I8_BYTES + ROUTER_BYTES + 2 * S * D * 4
+    vus = float(np.median(cold))
+    res["verify64_union"] = {"us": round(vus, 1), "us_spread": spread(cold),
+                             "union_routed_experts": used, "hbm_bytes": vb,
+                             "GBps": round(vb / vus / 1e3, 1),
+                             "frac_of_hbm_peak": round(vb / vus / 1e3 / HBM_PEAK_GBPS, 4)}
+    log(f"verify 64 with int8 shared expert: {vus:.1f} us cold")
+    return res
 
 
 def bench_mla(contexts=(1024, 4096, 16384), steps: int = 200):

@@ -295,9 +295,11 @@ int moe_mla_decode(const moe_mla_config *cfg, const float *q, int S, const float
  * with y_shared from the int8 expert *shared8 (host struct, expert 0 of its
  * stacks); layer->shared is not read.  cfg->n_shared must be 1 (MOE_ESHAPE);
  * flags: MOE_F_ACCUMULATE only (MOE_EINVAL otherwise); x 16-byte aligned.
- * Launches: the per-token path without a shared expert, the tokens'
- * quantization, the int8 expert's gate/up and down (the down adds into out),
- * so out = (out +) routed sum, then + y_shared.  Workspace:
+ * With D % 2048 == 0, D <= 8192, I % 1024 == 0 and I <= 4096 (the GLM shape)
+ * the int8 expert runs inside the per-token path's launches, its gate/up
+ * beside the router and its down beside the routed gate/up, exactly as the
+ * int4 shared expert does.  Other shapes run the launches of
+ * moe_layer_forward_batch_shared_i8 (which return the same bits).  Workspace:
  * moe_workspace_bytes(cfg, S, 5). */
 int moe_layer_forward_shared_i8(const moe_config *cfg, const moe_layer *layer,
                                 const moe_experts_i8 *shared8, const float *x, int S, float *out,
@@ -340,6 +342,21 @@ int moe_layer_forward_noalloc(const moe_config *cfg, const moe_layer *layer, con
 int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                             float *out, unsigned flags, const moe_probe *probe, void *ws,
                             size_t ws_bytes, hipStream_t stream);
+
+/* The unique-expert union (moe_layer_forward_batch) with the shared expert in
+ * the int8 format, as moe_layer_forward_shared_i8 is to moe_layer_forward:
+ * the routed experts are grouped and read once as in the union path, the
+ * int8 expert *shared8 (host struct, expert 0 of its stacks) is read once
+ * for all S tokens (its gate/up and down each one launch whose waves own
+ * weight rows and walk the tokens), its results are staged as the shared
+ * slot, and the per-token combine adds it last.  Returns the bits of
+ * moe_layer_forward_shared_i8 for the same inputs.  cfg->n_shared must be 1
+ * (MOE_ESHAPE); flags: MOE_F_ACCUMULATE only; layer->shared is not read.
+ * Workspace: moe_workspace_bytes(cfg, S, 1). */
+int moe_layer_forward_batch_shared_i8(const moe_config *cfg, const moe_layer *layer,
+                                      const moe_experts_i8 *shared8, const float *x, int S,
+                                      float *out, unsigned flags, void *ws, size_t ws_bytes,
+                                      hipStream_t stream);
 
 /* The per-token block with the routing given by the caller instead of the
  * router (section 11 computes the routing first and the experts after it;

@@ -83,6 +83,7 @@ def lib():
         L.moe_mla_workspace_bytes.restype = sz
         L.moe_mla_decode.argtypes = [vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp]
         L.moe_layer_forward_shared_i8.argtypes = [vp, vp, vp, vp, i32, vp, u32, vp, sz, vp]
+        L.moe_layer_forward_batch_shared_i8.argtypes = [vp, vp, vp, vp, i32, vp, u32, vp, sz, vp]
         L.moe_expert_swiglu_i4_b32.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_expert_swiglu_i2.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_layer_forward.argtypes = [vp, vp, vp, i32, vp, u32, vp, vp, sz, vp]
@@ -113,6 +114,7 @@ def lib():
                      "moe_expert_swiglu_i4", "moe_quantize_rows_i8", "moe_expert_swiglu_i8",
                      "moe_pack_int2", "moe_expert_swiglu_i2", "moe_quant_act_b32",
                      "moe_expert_swiglu_i4_b32", "moe_mla_decode", "moe_layer_forward_shared_i8",
+                     "moe_layer_forward_batch_shared_i8",
                      "moe_layer_forward", "moe_layer_forward_batch", "moe_layer_forward_noalloc",
                      "moe_rmsnorm", "moe_stream_read", "moe_stream_read_sink_words",
                      "moe_layer_forward_routed", "moe_layer_forward_batch_routed",
@@ -458,17 +460,19 @@ def moe_expert_swiglu_i4_b32(cfg: Config, xq: torch.Tensor, sxb: torch.Tensor,
 
 
 def moe_layer_forward_shared_i8(layer: DeviceLayer, shared8: DeviceExpertsI8, x: torch.Tensor,
-                                ws: Workspace, out=None, flags: int = 0, stream=None):
-    """The per-token block with the shared expert in the int8 format (workspace WS_SHARED8)."""
+                                ws: Workspace, out=None, flags: int = 0, stream=None,
+                                fn_name: str = "moe_layer_forward_shared_i8"):
+    """The per-token block with the shared expert in the int8 format (workspace
+    WS_SHARED8); fn_name="moe_layer_forward_batch_shared_i8": the union path
+    instead (workspace WS_BATCH)."""
     _dev(x, torch.float32, "x")
     S = x.shape[0]
     out = torch.empty(S, layer.cfg.D, dtype=torch.float32, device=x.device) if out is None else out
     lc = layer.cstruct()
     e8 = shared8.cstruct()
-    _check(lib().moe_layer_forward_shared_i8(ctypes.byref(layer.cfg), ctypes.byref(lc),
-                                             ctypes.byref(e8), _ptr(x), S, _ptr(out), flags, ws.ptr,
-                                             ws.nbytes, ctypes.c_void_p(_stream(stream))),
-           "moe_layer_forward_shared_i8")
+    _check(getattr(lib(), fn_name)(ctypes.byref(layer.cfg), ctypes.byref(lc), ctypes.byref(e8),
+                                   _ptr(x), S, _ptr(out), flags, ws.ptr, ws.nbytes,
+                                   ctypes.c_void_p(_stream(stream))), fn_name)
     return out
 
 

@@ -72,7 +72,7 @@ struct GuLds {
 // Walks this wave's items with a two-stage pipeline (the caller issued the
 // first stage into sa), then writes the block's
 // hidden values (and accumulators when acc_gu is set) to global memory.
-template <int NCH, bool MASKED, int ROWS, class Res>
+template <int NCH, bool MASKED, int ROWS, class Res, bool W8 = false>
 __device__ __forceinline__ void gu_items(Res res, int I, int rowbytes, int lo, int hi,
                                          const uint4 (&xv)[NCH][2], int corr, float sxs,
                                          GuLds &L, int *acco, int32_t *acc_gu,
@@ -85,9 +85,9 @@ __device__ __forceinline__ void gu_items(Res res, int I, int rowbytes, int lo, i
   for (int i = 0; i < nsteps; i += 2) {
     const int ra = first + i * stride, rb = ra + stride;
     gu_load<NCH, MASKED, ROWS>(res, I, rowbytes, rb, hi, dummy, sb);
-    gu_step<NCH, ROWS>(sa, xv, corr, sxs, ra, lo, hi, L.h, acco);
+    gu_step<NCH, ROWS, W8>(sa, xv, corr, sxs, ra, lo, hi, L.h, acco);
     gu_load<NCH, MASKED, ROWS>(res, I, rowbytes, rb + stride, hi, dummy, sa);
-    if (i + 1 < nsteps) gu_step<NCH, ROWS>(sb, xv, corr, sxs, rb, lo, hi, L.h, acco);
+    if (i + 1 < nsteps) gu_step<NCH, ROWS, W8>(sb, xv, corr, sxs, rb, lo, hi, L.h, acco);
   }
   __syncthreads();
   for (int t = threadIdx.x; t < hi - lo; t += 64 * kWaves) {
@@ -104,17 +104,26 @@ __device__ __forceinline__ void gu_items(Res res, int I, int rowbytes, int lo, i
 
 // Fixed expert (the shared one, or the single expert of a one-expert call) for
 // token s, rows of block gb.  LOCALQ: quantize the float token row in the
-// wave; otherwise read its codes.
-template <int NCH, bool MASKED, int ROWS, bool LOCALQ>
+// block; otherwise read its codes.  W8: the fixed expert is in the int8
+// format (a.f8g, a.f8u; NCH = 1 KB chunks of a D-byte row; LOCALQ only).
+template <int NCH, bool MASKED, int ROWS, bool LOCALQ, bool W8 = false>
 __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
+  static_assert(!W8 || LOCALQ, "the int8 fixed expert quantizes its token in the block");
+  // chunks of 2048 columns held per thread by the row quantization
+  constexpr int NX = W8 ? (NCH + 1) / 2 : NCH;
   __shared__ GuLds L;
   __shared__ int acco[2 * MOE_GU_MAX_ROWS];
   const int wave = threadIdx.x >> 6;
-  const int rowbytes = a.D >> 1;
+  const int rowbytes = W8 ? a.D : a.D >> 1;
   const int pair = s * a.P + a.fx_slot;
   GuMats m;
-  m.G = pick(a.fx.gate, a.fx.gate, false, a.fx_index);
-  m.U = pick(a.fx.up, a.fx.up, false, a.fx_index);
+  if constexpr (W8) {
+    m.G = a.f8g;
+    m.U = a.f8u;
+  } else {
+    m.G = pick(a.fx.gate, a.fx.gate, false, a.fx_index);
+    m.U = pick(a.fx.up, a.fx.up, false, a.fx_index);
+  }
   m.h = a.h + (int64_t)pair * a.I;
   auto res = [m](int) { return m; };
   int lo, hi;
@@ -131,7 +140,7 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
     // then reads its lanes' codes); the first weight stage is already in
     // flight while it does
     __shared__ __align__(16) int8_t xcodes[2048 * 4];
-    float4 xr[NCH][2];
+    float4 xr[NX][2];
     if (a.gamma) {
       // the token row and gain, then the first weight stage, are in flight
       // together; the normalization waits only for the former
@@ -139,20 +148,22 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
       norm_row_load(a.x + (int64_t)s * a.D, a.gamma, a.D, nr);
       gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
       prenorm_finish_lds(nr, a.D, a.eps, xn);
-      quant_row_load<NCH>(xn, a.D, xr);
+      quant_row_load<NX>(xn, a.D, xr);
     } else {
-      quant_row_load<NCH>(a.x + (int64_t)s * a.D, a.D, xr);
+      quant_row_load<NX>(a.x + (int64_t)s * a.D, a.D, xr);
       gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
     }
-    sumx = quant_row_block_lds<NCH>(xr, a.D, xcodes, &sxs);
+    sumx = quant_row_block_lds<NX>(xr, a.D, xcodes, &sxs);
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
-      const int col = 2048 * c + 32 * lane;
+      // int4 rows: lane l of chunk c covers columns 2048c + 32l .. +32;
+      // int8 rows: 1024c + 16l .. +16
+      const int col = W8 ? 1024 * c + 16 * lane : 2048 * c + 32 * lane;
       const bool ok = !MASKED || col < a.D;
       const int cc = ok ? col : 0;
       const uint4 v0 = *reinterpret_cast<const uint4 *>(xcodes + cc);
-      const uint4 v1 = *reinterpret_cast<const uint4 *>(xcodes + cc + 16);
+      const uint4 v1 = W8 ? v0 : *reinterpret_cast<const uint4 *>(xcodes + cc + 16);
       xv[c][0] = ok ? v0 : make_uint4(0u, 0u, 0u, 0u);
       xv[c][1] = ok ? v1 : make_uint4(0u, 0u, 0u, 0u);
     }
@@ -162,8 +173,10 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
     sumx = a.sumx[s];
     gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
   }
-  gu_items<NCH, MASKED, ROWS>(res, a.I, rowbytes, lo, hi, xv, 8 * sumx, sxs, L,
-                              acc_gu ? acco : nullptr, acc_gu, dummy, sa);
+  // int8 codes are signed: no offset to remove
+  gu_items<NCH, MASKED, ROWS, decltype(res), W8>(res, a.I, rowbytes, lo, hi, xv,
+                                                 W8 ? 0 : 8 * sumx, sxs, L,
+                                                 acc_gu ? acco : nullptr, acc_gu, dummy, sa);
 }
 
 // Routed experts of token s: the block runs the token's K selection rounds
@@ -373,11 +386,12 @@ struct DnLds {
   int accd[MOE_DN_MAX_ROWS];
 };
 
-template <int NCH, bool MASKED, int ROWS, int PMAX>
+// W8: the rows are int8 codes (lane l of chunk c: columns 1024c + 16l .. +16).
+template <int NCH, bool MASKED, int ROWS, int PMAX, bool W8 = false>
 __device__ __forceinline__ void dn_step(const DownTask &t, const DnStage<NCH, ROWS, PMAX> &st,
                                         const int8_t *codes, DnLds &L, int I, int row) {
   const int lane = threadIdx.x & 63;
-  const int rowbytes = I >> 1;
+  const int rowbytes = W8 ? I : I >> 1;
   const int i0 = row - t.d0;
   const int n = t.d1 - t.d0;
   float comb[ROWS];
@@ -390,21 +404,24 @@ __device__ __forceinline__ void dn_step(const DownTask &t, const DnStage<NCH, RO
     for (int c = 0; c < NCH; c++) {
       const int off = c * 1024 + lane * 16;
       const int offc = (!MASKED || off < rowbytes) ? off : 0;
-      hv[c][0] = *reinterpret_cast<const uint4 *>(codes + p * I + 2 * offc);
-      hv[c][1] = *reinterpret_cast<const uint4 *>(codes + p * I + 2 * offc + 16);
+      const int col = W8 ? offc : 2 * offc;  // first column of the lane's bytes
+      hv[c][0] = *reinterpret_cast<const uint4 *>(codes + p * I + col);
+      hv[c][1] = W8 ? hv[c][0] : *reinterpret_cast<const uint4 *>(codes + p * I + col + 16);
       if (MASKED && off >= rowbytes) {
         hv[c][0] = make_uint4(0u, 0u, 0u, 0u);
         hv[c][1] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    const int corr = 8 * L.sums[p];
+    const int corr = W8 ? 0 : 8 * L.sums[p];  // int8 codes are signed
     const float shs = L.sh[p];
     const bool use = p < t.np;
 #pragma unroll
     for (int r = 0; r < ROWS; r++) {
       int acc = 0;
 #pragma unroll
-      for (int c = 0; c < NCH; c++) acc = dot32_i4(st.w[p][r][c], hv[c][0], hv[c][1], acc);
+      for (int c = 0; c < NCH; c++)
+        acc = W8 ? dot16_i8p(st.w[p][r][c], hv[c][0], acc)
+                 : dot32_i4(st.w[p][r][c], hv[c][0], hv[c][1], acc);
       acc = wave_sum_i32(acc) - corr;
       const float y = ((float)acc * L.dsc[p][min(i0 + r, n - 1)]) * shs;
       const float nc = t.weighted[p] ? comb[r] + t.wgt[p] * y : comb[r] + y;
@@ -419,12 +436,14 @@ __device__ __forceinline__ void dn_step(const DownTask &t, const DnStage<NCH, RO
   if (lane < ROWS && i0 + lane < n) L.out[i0 + lane] = mine;
 }
 
-template <int NCH, bool MASKED, int ROWS, int PMAX>
+template <int NCH, bool MASKED, int ROWS, int PMAX, bool W8 = false>
 __device__ void down_block(const DownTask &t, int I) {
+  // chunks of 2048 columns per thread in the requantization
+  constexpr int NR = W8 ? (NCH + 1) / 2 : NCH;
   extern __shared__ __align__(16) int8_t codes[];
   __shared__ DnLds L;
   const int wave = threadIdx.x >> 6;
-  const int rowbytes = I >> 1;
+  const int rowbytes = W8 ? I : I >> 1;
   const int stride = kWaves * ROWS;
   const int first = t.d0 + wave * ROWS;
   const int nsteps = (first < t.d1) ? (t.d1 - first + stride - 1) / stride : 0;
@@ -433,13 +452,13 @@ __device__ void down_block(const DownTask &t, int I) {
   dn_scales<PMAX>(t, L.dsc, L.init, L.extra);
   // the first step's weights do not depend on the hidden rows: issue them early
   dn_load<NCH, MASKED, ROWS, PMAX>(t, rowbytes, first, dummy, sa);
-  requant_to_lds<PMAX, NCH>(t, I, codes, L.sh, L.sums);  // ends with a barrier
+  requant_to_lds<PMAX, NR>(t, I, codes, L.sh, L.sums);  // ends with a barrier
   for (int i = 0; i < nsteps; i += 2) {
     const int ra = first + i * stride, rb = ra + stride;
     dn_load<NCH, MASKED, ROWS, PMAX>(t, rowbytes, rb, dummy, sb);
-    dn_step<NCH, MASKED, ROWS, PMAX>(t, sa, codes, L, I, ra);
+    dn_step<NCH, MASKED, ROWS, PMAX, W8>(t, sa, codes, L, I, ra);
     dn_load<NCH, MASKED, ROWS, PMAX>(t, rowbytes, rb + stride, dummy, sa);
-    if (i + 1 < nsteps) dn_step<NCH, MASKED, ROWS, PMAX>(t, sb, codes, L, I, rb);
+    if (i + 1 < nsteps) dn_step<NCH, MASKED, ROWS, PMAX, W8>(t, sb, codes, L, I, rb);
   }
   __syncthreads();
   const int n = t.d1 - t.d0;
@@ -452,15 +471,16 @@ __device__ void down_block(const DownTask &t, int I) {
   }
 }
 
-// Down projection of the fixed expert for token s, rows of block db.
-template <int NCH, bool MASKED, int ROWS>
+// Down projection of the fixed expert for token s, rows of block db (W8: the
+// int8 fixed expert a.f8d; NCH = 1 KB chunks of an I-byte row).
+template <int NCH, bool MASKED, int ROWS, bool W8 = false>
 __device__ void down_fixed(const DecodeArgs &a, int s, int db) {
   DownTask t;
   const int pair = s * a.P + a.fx_slot;
   t.np = 1;
 #pragma unroll
   for (int j = 0; j < MOE_DOWN_MAXP; j++) {
-    t.M[j] = pick(a.fx.down, a.fx.down, false, a.fx_index);
+    t.M[j] = W8 ? a.f8d : pick(a.fx.down, a.fx.down, false, a.fx_index);
     t.wgt[j] = 1.f;
     t.weighted[j] = false;
     t.h[j] = a.h + (int64_t)pair * a.I;
@@ -474,7 +494,7 @@ __device__ void down_fixed(const DecodeArgs &a, int s, int db) {
   t.hq_nat = a.hq_nat ? a.hq_nat + (int64_t)s * a.I : nullptr;
   t.sh_out = a.sh_out ? a.sh_out + s : nullptr;
   t.first_block = (db == 0);
-  down_block<NCH, MASKED, ROWS, 1>(t, a.I);
+  down_block<NCH, MASKED, ROWS, 1, W8>(t, a.I);
 }
 
 #ifndef MOE_DNFX_ROWS
@@ -489,7 +509,9 @@ __device__ void down_fixed(const DecodeArgs &a, int s, int db) {
 
 // With a.gamma set every workgroup of phase A first forms the token's RMSNorm
 // row in dynamic shared memory (D floats) and works on that.
-template <int NCHD, bool MD, bool LOCALQ>
+// W8: the fixed expert is in the int8 format (NCHD = 1 KB chunks of its
+// D-byte rows).
+template <int NCHD, bool MD, bool LOCALQ, bool W8 = false>
 __global__ __launch_bounds__(256) void decode_a_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) float xn_dyn[];
   const int s = blockIdx.y, b = blockIdx.x;
@@ -510,17 +532,18 @@ __global__ __launch_bounds__(256) void decode_a_kernel(DecodeArgs a) {
                     const_cast<float *>(a.sx) + s, const_cast<int32_t *>(a.sumx) + s);
     return;
   }
-  gateup_fixed<NCHD, MD, MOE_GU_ROWS, LOCALQ>(a, s, b - a.n_router - a.n_quant, xn_dyn);
+  gateup_fixed<NCHD, MD, MOE_GU_ROWS, LOCALQ, W8>(a, s, b - a.n_router - a.n_quant, xn_dyn);
 }
 
-template <int NCHD, bool MD, int NCHI, bool MI>
+// W8: the fixed expert's down rows are int8 (NCHI = 1 KB chunks of I bytes).
+template <int NCHD, bool MD, int NCHI, bool MI, bool W8 = false>
 __global__ __launch_bounds__(256) void decode_b_kernel(DecodeArgs a) {
   const int s = blockIdx.y, b = blockIdx.x;
   if (b < a.n_gu_rt) {
     gateup_routed<NCHD, MD, MOE_GU_ROWS>(a, s, b);
     return;
   }
-  down_fixed<NCHI, MI, MOE_DNFX_ROWS>(a, s, b - a.n_gu_rt);
+  down_fixed<NCHI, MI, MOE_DNFX_ROWS, W8>(a, s, b - a.n_gu_rt);
 }
 
 // ---- phase C: routed down + combine ---------------------------------------------
@@ -674,6 +697,18 @@ hipError_t launch_decode_a(const DecodeArgs &a, bool local_quant, hipStream_t st
   const dim3 grid(a.n_router + a.n_quant + a.n_gu_fx, a.S);
   const int rb = a.D / 2;
   const size_t lds = a.gamma ? (size_t)a.D * 4 : 0;  // the normalized row
+  if (a.fx8) {
+    // int8 fixed expert: D-byte rows, D % 2048 == 0 and D <= 8192 (checked
+    // by the caller), so 2, 4, 6 or 8 whole 1 KB chunks
+    switch (a.D / 1024) {
+      case 2: hipLaunchKernelGGL((decode_a_kernel<2, false, true, true>), grid, dim3(256), lds, st, a); break;
+      case 4: hipLaunchKernelGGL((decode_a_kernel<4, false, true, true>), grid, dim3(256), lds, st, a); break;
+      case 6: hipLaunchKernelGGL((decode_a_kernel<6, false, true, true>), grid, dim3(256), lds, st, a); break;
+      case 8: hipLaunchKernelGGL((decode_a_kernel<8, false, true, true>), grid, dim3(256), lds, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
 #define MOE_FA(N, M)                                                                     \
   do {                                                                                   \
     if (local_quant)                                                                     \
@@ -686,10 +721,34 @@ hipError_t launch_decode_a(const DecodeArgs &a, bool local_quant, hipStream_t st
   return hipGetLastError();
 }
 
+template <int ND>
+static hipError_t launch_decode_b8(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st,
+                                   hipEvent_t e0, hipEvent_t e1) {
+  // int8 fixed expert: I-byte down rows, I % 1024 == 0 and I <= 4096
+  switch (a.I / 1024) {
+    case 1: launch_timed((decode_b_kernel<ND, false, 1, false, true>), grid, dim3(256), lds, st, e0, e1, a); break;
+    case 2: launch_timed((decode_b_kernel<ND, false, 2, false, true>), grid, dim3(256), lds, st, e0, e1, a); break;
+    case 3: launch_timed((decode_b_kernel<ND, false, 3, false, true>), grid, dim3(256), lds, st, e0, e1, a); break;
+    case 4: launch_timed((decode_b_kernel<ND, false, 4, false, true>), grid, dim3(256), lds, st, e0, e1, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_b(const DecodeArgs &a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(a.n_gu_rt + a.n_dn_fx, a.S);
   const size_t lds = (size_t)a.I;  // one hidden row of codes
   const int rbd = a.D / 2, rbi = a.I / 2;
+  if (a.fx8) {
+    // routed int4 rows of D/2 bytes, D % 2048 == 0 and D <= 8192: 1 to 4 whole chunks
+    switch (a.D / 2048) {
+      case 1: return launch_decode_b8<1>(a, grid, lds, st, e0, e1);
+      case 2: return launch_decode_b8<2>(a, grid, lds, st, e0, e1);
+      case 3: return launch_decode_b8<3>(a, grid, lds, st, e0, e1);
+      case 4: return launch_decode_b8<4>(a, grid, lds, st, e0, e1);
+      default: return hipErrorInvalidValue;
+    }
+  }
 #define MOE_FBI(NI, MI, ND, MD) \
   launch_timed((decode_b_kernel<ND, MD, NI, MI>), grid, dim3(256), lds, st, e0, e1, a)
 #define MOE_FBD(ND, MD)                                          \

@@ -48,7 +48,9 @@ __device__ __forceinline__ int dot16_i8(const uint4 &w, const uint4 &x, int acc)
 
 // Gate/up: wave w of block b owns row o = 4b + w of both matrices.
 // NCH = ceil(D / 1024) chunks; MASKED when D is not a multiple of 1024.
-template <int NCH, bool MASKED>
+// XPERM: the token codes are in the permuted layout (the weight bytes are
+// reordered to meet them, dot16_i8p).
+template <int NCH, bool MASKED, bool XPERM = false>
 __global__ __launch_bounds__(256) void gu8_kernel(Swiglu8Args a) {
   const int lane = threadIdx.x & 63;
   const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -71,8 +73,8 @@ __global__ __launch_bounds__(256) void gu8_kernel(Swiglu8Args a) {
     for (int c = 0; c < NCH; c++) {
       const int col = 1024 * c + 16 * lane;
       const uint4 xv = ld16(xs + col, !MASKED || col < a.D, xs);
-      ag = dot16_i8(g[c], xv, ag);
-      au = dot16_i8(u[c], xv, au);
+      ag = XPERM ? dot16_i8p(g[c], xv, ag) : dot16_i8(g[c], xv, ag);
+      au = XPERM ? dot16_i8p(u[c], xv, au) : dot16_i8(u[c], xv, au);
     }
     ag = wave_sum_i32(ag);
     au = wave_sum_i32(au);
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void gu8_kernel(Swiglu8Args a) {
       const float sxs = a.sx[s];
       const float gv = ((float)ag * gs) * sxs;
       const float uv = ((float)au * us) * sxs;
-      a.h[(int64_t)s * a.I + o] = silu(gv) * uv;
+      a.h[(int64_t)s * (a.h_stride ? a.h_stride : a.I) + o] = silu(gv) * uv;
       if (a.acc_gu) {
         a.acc_gu[(int64_t)s * 2 * a.I + o] = ag;
         a.acc_gu[((int64_t)s * 2 + 1) * a.I + o] = au;
@@ -121,8 +123,9 @@ __global__ __launch_bounds__(256) void dn8_kernel(Swiglu8Args a) {
   for (int s0 = 0; s0 < a.S; s0 += TS) {
     const int ns = min(TS, a.S - s0);
     __syncthreads();  // the previous chunk's codes are consumed
+    const int64_t hs = a.h_stride ? a.h_stride : a.I;
     for (int j = 0; j < ns; j++)
-      quant_row_block(a.h + (int64_t)(s0 + j) * a.I, nullptr, a.I, nullptr, codes + j * a.I,
+      quant_row_block(a.h + (int64_t)(s0 + j) * hs, nullptr, a.I, nullptr, codes + j * a.I,
                       &shs[j], nullptr);
     __syncthreads();  // the scales are written by thread 0 after the last barrier
     if (blockIdx.x == 0) {
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(256) void dn8_kernel(Swiglu8Args a) {
         acc = wave_sum_i32(acc);
         if (lane == r && d0 + r < a.D) {
           const float v = ((float)acc * dsc[r]) * sh;
-          float *yp = a.y + s * a.D + d0 + r;
+          float *yp = a.y + s * (a.y_stride ? a.y_stride : a.D) + d0 + r;
           *yp = a.accumulate ? *yp + v : v;
           if (a.acc_d) a.acc_d[s * a.D + d0 + r] = acc;
         }
@@ -168,10 +171,16 @@ hipError_t launch_quant_rows_i8(const Q8QuantArgs &a, hipStream_t st) {
 template <int NCH>
 static void launch_gu8(const Swiglu8Args &a, hipStream_t st) {
   const dim3 grid((a.I + 3) / 4);
-  if (a.D % 1024)
+  if (a.x_perm) {
+    if (a.D % 1024)
+      hipLaunchKernelGGL((gu8_kernel<NCH, true, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((gu8_kernel<NCH, false, true>), grid, dim3(256), 0, st, a);
+  } else if (a.D % 1024) {
     hipLaunchKernelGGL((gu8_kernel<NCH, true>), grid, dim3(256), 0, st, a);
-  else
+  } else {
     hipLaunchKernelGGL((gu8_kernel<NCH, false>), grid, dim3(256), 0, st, a);
+  }
 }
 
 // D and I are at most 8192 (checked by the caller): at most 8 chunks.

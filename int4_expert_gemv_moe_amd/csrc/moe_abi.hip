@@ -57,15 +57,19 @@ int check_cfg(const moe_config *c) {
 
 enum Which { W_FWD = 0, W_BATCH = 1, W_SWIGLU = 2, W_ROUTER = 3, W_SWIGLU8 = 4, W_SHARED8 = 5 };
 
-// Workspace of moe_layer_forward_shared_i8: the per-token path's (without a
-// shared expert), then the token codes and scales and the int8 expert's h.
+// Shapes whose int8 shared expert runs inside the per-token path's launches
+// (whole 1 KB chunks of its rows, within the kernels' instantiations):
+// D % 2048 == 0 and D <= 8192, I % 1024 == 0 and I <= 4096.  Other shapes
+// run it in launches of its own after the routed experts.
+bool shared8_fused_ok(const moe_config &c) {
+  return c.D % 2048 == 0 && c.D <= 8192 && c.I % 1024 == 0 && c.I <= 4096;
+}
+
+// Workspace of moe_layer_forward_shared_i8: the per-token path's with the
+// shared slot (fused shapes), else the union path's.
 size_t carve(const moe_config &c, int S, int which, char *base, struct Work *w);
-size_t shared8_bytes(const moe_config &c, int S, size_t *fwd) {
-  moe_config c0 = c;
-  c0.n_shared = 0;
-  const size_t f = carve(c0, S, W_FWD, nullptr, nullptr);
-  if (fwd) *fwd = f;
-  return f + align_up((size_t)S * c.D) + align_up((size_t)S * 4) + align_up((size_t)S * c.I * 4);
+size_t shared8_bytes(const moe_config &c, int S) {
+  return carve(c, S, shared8_fused_ok(c) ? W_FWD : W_BATCH, nullptr, nullptr);
 }
 
 // Workgroup counts of the per-token path (rows of a phase are split evenly
@@ -74,6 +78,7 @@ size_t shared8_bytes(const moe_config &c, int S, size_t *fwd) {
 // counts were swept on the device at the GLM shape.
 struct DecodeShape {
   int gu_fx, gu_rt, dn_fx, dn;
+  int gu_fx8, dn_fx8;  // the same for an int8 fixed expert (rows twice as long)
 };
 
 DecodeShape decode_shape(const moe_config &c) {
@@ -81,6 +86,8 @@ DecodeShape decode_shape(const moe_config &c) {
   d.gu_fx = 128;
   d.gu_rt = 256;
   d.dn_fx = 192;
+  d.gu_fx8 = 256;
+  d.dn_fx8 = 256;
   // phase C: one pass of rows per workgroup
   const int cr = decode_c_rows_per_pass(c.I);
   d.dn = (c.D + cr - 1) / cr;
@@ -94,6 +101,8 @@ DecodeShape decode_shape(const moe_config &c) {
   d.gu_rt = clampn(d.gu_rt, c.I * c.K, 512);
   d.dn_fx = clampn(d.dn_fx, c.D, 256);
   d.dn = clampn(d.dn, c.D, 256);
+  d.gu_fx8 = clampn(d.gu_fx8, c.I, 512);
+  d.dn_fx8 = clampn(d.dn_fx8, c.D, 256);
   return d;
 }
 
@@ -196,7 +205,10 @@ void q8_rows(const moe_q8mat &m, int O, int C, int e, const int8_t **q, const fl
   *s = m.scale + (int64_t)e * ss;
 }
 
-int check_layer(const moe_config &c, const moe_layer *L, bool router = true) {
+// shared_i4: the shared expert is layer->shared (otherwise the caller passes
+// it in another format and checks it itself).
+int check_layer(const moe_config &c, const moe_layer *L, bool router = true,
+                bool shared_i4 = true) {
   if (!L) return MOE_EINVAL;
   if (router) {
     if (!L->router_w || !L->router_b) return MOE_EINVAL;
@@ -204,7 +216,7 @@ int check_layer(const moe_config &c, const moe_layer *L, bool router = true) {
   }
   int rc = check_experts(L->routed);
   if (rc) return rc;
-  if (c.n_shared) return check_experts(L->shared);
+  if (c.n_shared && shared_i4) return check_experts(L->shared);
   return MOE_OK;
 }
 
@@ -274,11 +286,11 @@ int record(const moe_probe *probe, int which, int side, hipStream_t st) {
 
 int layer_common_checks(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                         float *out, unsigned flags, void *ws, size_t ws_bytes, int which,
-                        bool router = true) {
+                        bool router = true, bool shared_i4 = true) {
   MOE_TRY(check_cfg(cfg));
   if (S < 1 || !x || !out || !ws) return MOE_EINVAL;
   if (flags & ~(MOE_F_ACCUMULATE | MOE_F_PRENORM)) return MOE_EINVAL;
-  MOE_TRY(check_layer(*cfg, layer, router));
+  MOE_TRY(check_layer(*cfg, layer, router, shared_i4));
   if (!aligned16(x) || ((uintptr_t)out & 3u) || ((uintptr_t)ws & 255u)) return MOE_EALIGN;
   const bool prenorm = (flags & MOE_F_PRENORM) != 0;
   if (prenorm) {
@@ -316,7 +328,7 @@ const char *moe_status_str(int status) {
 
 size_t moe_workspace_bytes(const moe_config *cfg, int S, int which) {
   if (check_cfg(cfg) != MOE_OK || S < 1 || which < 0 || which > 5) return 0;
-  if (which == W_SHARED8) return cfg->n_shared == 1 ? shared8_bytes(*cfg, S, nullptr) : 0;
+  if (which == W_SHARED8) return cfg->n_shared == 1 ? shared8_bytes(*cfg, S) : 0;
   return carve(*cfg, S, which, nullptr, nullptr);
 }
 
@@ -642,15 +654,19 @@ int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *s
 namespace {
 
 // The per-token path; with given_idx / given_w the caller's routing replaces
-// the router and the selection (phase A then has no router workgroups).
+// the router and the selection (phase A then has no router workgroups).  With
+// shared8 the shared expert is that int8 expert (checked by the caller, and
+// the shape by shared8_fused_ok), run inside phases A and B like the int4 one.
 int layer_forward_impl(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                        const int32_t *given_idx, const float *given_w, float *out,
                        unsigned flags, const moe_probe *probe, void *ws, size_t ws_bytes,
-                       hipStream_t stream) {
+                       hipStream_t stream, const moe_experts_i8 *shared8 = nullptr) {
   const bool given = given_idx != nullptr;
   if (given && !given_w) return MOE_EINVAL;
   if (given && (((uintptr_t)given_idx & 3u) || ((uintptr_t)given_w & 3u))) return MOE_EALIGN;
-  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_FWD, !given));
+  if (shared8 && cfg->n_shared != 1) return MOE_ESHAPE;
+  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_FWD, !given,
+                              shared8 == nullptr));
   const moe_config &c = *cfg;
   Work w;
   carve(c, S, W_FWD, (char *)ws, &w);
@@ -667,9 +683,20 @@ int layer_forward_impl(const moe_config *cfg, const moe_layer *layer, const floa
   d.W = layer->router_w;
   d.bias = layer->router_b;
   d.rt = to_set(layer->routed, c);
-  d.fx = c.n_shared ? to_set(layer->shared, c) : d.rt;
+  d.fx = (c.n_shared && !shared8) ? to_set(layer->shared, c) : d.rt;
   d.fx_index = 0;
   d.fx_slot = c.K;
+  if (shared8) {
+    const int8_t *q;
+    const float *sc;
+    d.fx8 = 1;
+    q8_rows(shared8->gate, c.I, c.D, 0, &q, &sc);
+    d.f8g = RowPtr{reinterpret_cast<const uint8_t *>(q), sc};
+    q8_rows(shared8->up, c.I, c.D, 0, &q, &sc);
+    d.f8u = RowPtr{reinterpret_cast<const uint8_t *>(q), sc};
+    q8_rows(shared8->down, c.D, c.I, 0, &q, &sc);
+    d.f8d = RowPtr{reinterpret_cast<const uint8_t *>(q), sc};
+  }
   d.xq = w.xq;
   d.sx = w.sx;
   d.sumx = w.sumx;
@@ -684,9 +711,9 @@ int layer_forward_impl(const moe_config *cfg, const moe_layer *layer, const floa
   d.tmp = w.tmp;
   d.n_router = given ? 0 : (c.E + kARouterWaves - 1) / kARouterWaves;
   d.n_quant = 1;
-  d.n_gu_fx = c.n_shared ? ds.gu_fx : 0;
+  d.n_gu_fx = c.n_shared ? (shared8 ? ds.gu_fx8 : ds.gu_fx) : 0;
   d.n_gu_rt = ds.gu_rt;
-  d.n_dn_fx = c.n_shared ? ds.dn_fx : 0;
+  d.n_dn_fx = c.n_shared ? (shared8 ? ds.dn_fx8 : ds.dn_fx) : 0;
   d.n_dn = ds.dn;
   d.out = out;
   d.flags = flags & MOE_F_ACCUMULATE;
@@ -783,16 +810,44 @@ extern "C" int moe_layer_forward_noalloc(const moe_config *cfg, const moe_layer 
 
 namespace {
 
+// The int8 shared expert of the union path on all S tokens, its gate/up
+// (mode 0: codes xq in the permuted layout, h into slot K of every token's
+// hidden rows) or its down (mode 1: y into slot K of the staging rows).
+int shared8_rows(const moe_config &c, const moe_experts_i8 &e, const Work &w, int S, int mode,
+                 hipStream_t st) {
+  const int P = c.K + 1;
+  Swiglu8Args a{};
+  a.xq = w.xq;
+  a.sx = w.sx;
+  a.S = S;
+  a.D = c.D;
+  a.I = c.I;
+  q8_rows(e.gate, c.I, c.D, 0, &a.G, &a.gs);
+  q8_rows(e.up, c.I, c.D, 0, &a.U, &a.us);
+  q8_rows(e.down, c.D, c.I, 0, &a.Dn, &a.ds);
+  a.x_perm = 1;
+  a.h = w.h + (size_t)c.K * c.I;
+  a.h_stride = (int64_t)P * c.I;
+  a.y = w.stage + (size_t)c.K * c.D;
+  a.y_stride = (int64_t)P * c.D;
+  return hip_rc(mode == 0 ? launch_swiglu8_gateup(a, st) : launch_swiglu8_down(a, st));
+}
+
 // The union path; with given_idx / given_w the caller's routing replaces the
-// router and the selection (the tokens are only quantized).
+// router and the selection (the tokens are only quantized).  With shared8 the
+// shared expert is that int8 expert (checked by the caller): the routed
+// experts are grouped without a shared group, and the int8 expert runs on all
+// tokens into the shared slot of the hidden and staging rows.
 int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, const float *x, int S,
                              const int32_t *given_idx, const float *given_w, float *out,
                              unsigned flags, const moe_probe *probe, void *ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             hipStream_t stream, const moe_experts_i8 *shared8 = nullptr) {
   const bool given = given_idx != nullptr;
   if (given && !given_w) return MOE_EINVAL;
   if (given && (((uintptr_t)given_idx & 3u) || ((uintptr_t)given_w & 3u))) return MOE_EALIGN;
-  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_BATCH, !given));
+  if (shared8 && cfg->n_shared != 1) return MOE_ESHAPE;
+  MOE_TRY(layer_common_checks(cfg, layer, x, S, out, flags, ws, ws_bytes, W_BATCH, !given,
+                              shared8 == nullptr));
   const moe_config &c = *cfg;
   const int P = c.K + c.n_shared;
   Work w;
@@ -831,8 +886,9 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
   const bool offs_ok = (int64_t)S * P * std::max(c.D, c.I) < INT32_MAX;
   const bool mfma_gu = grouped_mfma_fits(c.D) && offs_ok, mfma_dn = grouped_mfma_fits(c.I) && offs_ok;
   const int max_tiles = grouped_mfma_max_tiles(S, P, c.E);
-  GroupArgs ga{idx,      S,     c.E,     c.K,      P, c.n_shared, w.gcount, w.goff, w.pairs,
-               (mfma_gu || mfma_dn) ? w.tiles : nullptr, w.ntiles, grouped_mfma_tile_rows(S)};
+  GroupArgs ga{idx,      S,     c.E,     c.K,      P, shared8 ? 0 : c.n_shared, w.gcount, w.goff,
+               w.pairs, (mfma_gu || mfma_dn) ? w.tiles : nullptr, w.ntiles,
+               grouped_mfma_tile_rows(S)};
   ga.with_topk = topk_in_group ? 1 : 0;
   ga.topp = c.expert_topp;
   ga.keff = keff;
@@ -844,7 +900,7 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
   MOE_TRY_HIP(launch_group(ga, stream));
   if (!given) MOE_TRY(copy_probe(c, S, probe, w, stream));
   const ExpertSet rt = to_set(layer->routed, c);
-  const ExpertSet sh = c.n_shared ? to_set(layer->shared, c) : rt;
+  const ExpertSet sh = (c.n_shared && !shared8) ? to_set(layer->shared, c) : rt;
   GroupedMfmaArgs m{};
   m.rt = rt;
   m.sh = sh;
@@ -882,6 +938,7 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
   } else {
     MOE_TRY_HIP(launch_grouped_gateup(g, stream));
   }
+  if (shared8) MOE_TRY(shared8_rows(c, *shared8, w, S, 0, stream));
   MOE_TRY(record(probe, 0, 1, stream));
   RequantArgs rq{w.h, c.I, w.hq, w.sh, w.sumh};
   MOE_TRY_HIP(launch_requant(rq, S * P, stream));
@@ -912,6 +969,7 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
   } else {
     MOE_TRY_HIP(launch_grouped_down(d, stream));
   }
+  if (shared8) MOE_TRY(shared8_rows(c, *shared8, w, S, 1, stream));
   MOE_TRY(record(probe, 1, 1, stream));
   CombineArgs cb{w.stage, wts, S, c.D, c.K, P, c.n_shared, out, flags, topp_on ? keff : nullptr};
   MOE_TRY_HIP(launch_combine(cb, stream));
@@ -927,6 +985,19 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
                             size_t ws_bytes, hipStream_t stream) {
   return layer_forward_batch_impl(cfg, layer, x, S, nullptr, nullptr, out, flags, probe, ws,
                                   ws_bytes, stream);
+}
+
+int moe_layer_forward_batch_shared_i8(const moe_config *cfg, const moe_layer *layer,
+                                      const moe_experts_i8 *shared8, const float *x, int S,
+                                      float *out, unsigned flags, void *ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->n_shared != 1) return MOE_ESHAPE;
+  if (!shared8) return MOE_EINVAL;
+  if (flags & ~MOE_F_ACCUMULATE) return MOE_EINVAL;
+  MOE_TRY(check_experts_i8(*shared8));
+  return layer_forward_batch_impl(cfg, layer, x, S, nullptr, nullptr, out, flags, nullptr, ws,
+                                  ws_bytes, stream, shared8);
 }
 
 int moe_layer_forward_batch_routed(const moe_config *cfg, const moe_layer *layer, const float *x,
@@ -1033,45 +1104,16 @@ int moe_layer_forward_shared_i8(const moe_config *cfg, const moe_layer *layer,
                                 unsigned flags, void *ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));
   if (cfg->n_shared != 1) return MOE_ESHAPE;
-  if (!shared8 || !x || !out || !ws || S < 1) return MOE_EINVAL;
+  if (!shared8) return MOE_EINVAL;
   if (flags & ~MOE_F_ACCUMULATE) return MOE_EINVAL;
   MOE_TRY(check_experts_i8(*shared8));
-  if (!aligned16(x)) return MOE_EALIGN;
-  size_t fwd = 0;
-  if (ws_bytes < shared8_bytes(*cfg, S, &fwd)) return MOE_EWORKSPACE;
-  moe_config c0 = *cfg;
-  c0.n_shared = 0;
-  // the router and the routed experts through the per-token path (it checks
-  // the rest of the arguments and the device)
-  MOE_TRY(layer_forward_impl(&c0, layer, x, S, nullptr, nullptr, out, flags, nullptr, ws, fwd,
-                             stream));
-  char *base = static_cast<char *>(ws) + fwd;
-  int8_t *xq = reinterpret_cast<int8_t *>(base);
-  float *sx = reinterpret_cast<float *>(base + align_up((size_t)S * cfg->D));
-  float *h = reinterpret_cast<float *>(base + align_up((size_t)S * cfg->D) + align_up((size_t)S * 4));
-  // the tokens' codes (section 12 quantization, the same bits as the routed path's)
-  QuantArgs qa{};
-  qa.xf = x;
-  qa.D = cfg->D;
-  qa.xq_nat = xq;
-  qa.sx = sx;
-  MOE_TRY_HIP(launch_quant(qa, S, stream));
-  // the shared expert, added to the routed sum
-  Swiglu8Args a{};
-  a.xq = xq;
-  a.sx = sx;
-  a.S = S;
-  a.D = cfg->D;
-  a.I = cfg->I;
-  q8_rows(shared8->gate, cfg->I, cfg->D, 0, &a.G, &a.gs);
-  q8_rows(shared8->up, cfg->I, cfg->D, 0, &a.U, &a.us);
-  q8_rows(shared8->down, cfg->D, cfg->I, 0, &a.Dn, &a.ds);
-  a.h = h;
-  a.y = out;
-  a.accumulate = 1;
-  MOE_TRY_HIP(launch_swiglu8_gateup(a, stream));
-  MOE_TRY_HIP(launch_swiglu8_down(a, stream));
-  return MOE_OK;
+  // shapes outside the fused kernels' instantiations take the union path's
+  // launches, which return the per-token path's bits
+  if (shared8_fused_ok(*cfg))
+    return layer_forward_impl(cfg, layer, x, S, nullptr, nullptr, out, flags, nullptr, ws,
+                              ws_bytes, stream, shared8);
+  return layer_forward_batch_impl(cfg, layer, x, S, nullptr, nullptr, out, flags, nullptr, ws,
+                                  ws_bytes, stream, shared8);
 }
 
 }  // extern "C"

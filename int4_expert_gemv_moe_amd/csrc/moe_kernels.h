@@ -87,6 +87,8 @@ struct DecodeArgs {
   const float *gamma;       // optional [D]: phase A works on RMSNorm(x) with gamma, eps
   float eps;
   int given;                // routing given by the caller: idx and w are inputs
+  int fx8;                  // the fixed expert is in the int8 format: rows f8g, f8u, f8d
+  RowPtr f8g, f8u, f8d;     // its int8 gate/up [I][D] and down [D][I] codes and row scales
   float topp;               // adaptive expert top-p (0: all K)
   int32_t *keff;            // [S] experts kept per token (phase B writes, C reads); null: K
 };
@@ -202,6 +204,9 @@ struct Swiglu8Args {
   float *y;                // [S][D]
   int32_t *acc_d;          // optional [S][D]
   int accumulate;          // y += result instead of y = result
+  int x_perm;              // xq holds permuted-layout codes (the union path's) instead
+  int64_t h_stride;        // floats between the tokens' h rows (0: I)
+  int64_t y_stride;        // floats between the tokens' y rows (0: D)
 };
 
 // Packed int2 weights (fmt2.hip): four codes per byte, code + 2, column

@@ -25,6 +25,18 @@ __device__ __forceinline__ uint4 ld16(const void *p, bool ok, const void *safe) 
   return ok ? t : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// 16 int8 weights in natural column order against 16 activation codes in the
+// permuted layout (see moe_common.h): each 8-column group of weights
+// w0..w7 is reordered with byte permutes into the words [w0 w2 w4 w6] and
+// [w1 w3 w5 w7] that meet the two code words of the group.
+__device__ __forceinline__ int dot16_i8p(const uint4 &w, const uint4 &x, int acc) {
+  acc = dot4((int)__builtin_amdgcn_perm(w.y, w.x, 0x06040200u), (int)x.x, acc);
+  acc = dot4((int)__builtin_amdgcn_perm(w.y, w.x, 0x07050301u), (int)x.y, acc);
+  acc = dot4((int)__builtin_amdgcn_perm(w.w, w.z, 0x06040200u), (int)x.z, acc);
+  acc = dot4((int)__builtin_amdgcn_perm(w.w, w.z, 0x07050301u), (int)x.w, acc);
+  return acc;
+}
+
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
          ((uint32_t)(d & 0xFF) << 24);
@@ -200,7 +212,9 @@ __device__ __forceinline__ void gu_load(Res res, int I, int rowbytes, int item, 
   st.us = m.U.s[row];
 }
 
-template <int NCH, int ROWS>
+// W8: the rows are int8 codes (16 columns per lane and 1 KB chunk, codes
+// xv[c][0]; corr is 0); otherwise packed int4 (32 columns, xv[c][0..1]).
+template <int NCH, int ROWS, bool W8 = false>
 __device__ __forceinline__ void gu_step(const GuStage<NCH, ROWS> &st, const uint4 (&xv)[NCH][2],
                                         int corr, float sxs, int item, int lo, int hi,
                                         float *hout, int *acco) {
@@ -212,8 +226,13 @@ __device__ __forceinline__ void gu_step(const GuStage<NCH, ROWS> &st, const uint
     au[r] = 0;
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
-      ag[r] = dot32_i4(st.g[r][c], xv[c][0], xv[c][1], ag[r]);
-      au[r] = dot32_i4(st.u[r][c], xv[c][0], xv[c][1], au[r]);
+      if constexpr (W8) {
+        ag[r] = dot16_i8p(st.g[r][c], xv[c][0], ag[r]);
+        au[r] = dot16_i8p(st.u[r][c], xv[c][0], au[r]);
+      } else {
+        ag[r] = dot32_i4(st.g[r][c], xv[c][0], xv[c][1], ag[r]);
+        au[r] = dot32_i4(st.u[r][c], xv[c][0], xv[c][1], au[r]);
+      }
     }
     ag[r] = wave_sum_i32(ag[r]);
     au[r] = wave_sum_i32(au[r]);

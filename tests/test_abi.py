@@ -265,18 +265,20 @@ def test_mla_host_checks():
 def test_shared_i8_layer_host_checks():
     import int4_expert_gemv_moe_amd as moe
     L = moe.lib()
-    buf = ctypes.create_string_buffer(512)
+    buf = ctypes.create_string_buffer(8192)
     a = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 256
+    out = a + 4096  # apart from x (2 x 256 floats)
     cfg = moe.config(256, 128, 8, 2)
     m = moe.Q8Mat(a, a, 0, 0)
     e8 = moe.ExpertsI8(m, m, m)
-    layer = moe.LayerC()
+    q = moe.QMat(a, a, 0, 0)
+    layer = moe.LayerC(a, a, moe.Experts(q, q, q), moe.Experts(), None, 0.0)  # shared not read
     need = L.moe_workspace_bytes(ctypes.byref(cfg), 2, moe.WS_SHARED8)
     assert need > L.moe_workspace_bytes(ctypes.byref(moe.config(256, 128, 8, 2, n_shared=0)), 2, 0)
     assert L.moe_workspace_bytes(ctypes.byref(moe.config(256, 128, 8, 2, n_shared=0)), 2,
                                  moe.WS_SHARED8) == 0
     call = lambda c, e, x, flags, ws_bytes: L.moe_layer_forward_shared_i8(
-        ctypes.byref(c), ctypes.byref(layer), e, x, 2, a, flags, a, ws_bytes, None)
+        ctypes.byref(c), ctypes.byref(layer), e, x, 2, out, flags, a, ws_bytes, None)
     assert call(moe.config(256, 128, 8, 2, n_shared=0), ctypes.byref(e8), a, 0, need) == -2
     assert call(cfg, None, a, 0, need) == -1                  # no int8 shared expert
     assert call(cfg, ctypes.byref(e8), a, 2, need) == -1      # PRENORM is not supported
