@@ -276,8 +276,9 @@ def spread(us):
 
 def bench_prefill(layer, iters: int = 5):
     """Prefill of 2048 tokens through one GLM-shape layer on the unique-expert
-    union path (int8 MFMA grouped GEMMs): activations N(0,1) rounded to bf16,
-    router bias 0 (uniform routing)."""
+    union path (int8 MFMA grouped GEMMs): activations N(0,1) rounded to bf16
+    and handed over as bf16 rows (the same bits as their float32 widening,
+    which is timed beside them), router bias 0 (uniform routing)."""
     import numpy as np
     import torch
 
@@ -289,15 +290,21 @@ def bench_prefill(layer, iters: int = 5):
     zl = moe.DeviceLayer(layer.cfg, layer.router_w,
                          torch.zeros(E, dtype=torch.float32, device="cuda"), layer.routed,
                          layer.shared)
-    x = torch.from_numpy(synth.bf16_to_f32(synth.bf16_bits(synth.activations(5, S, D)))).cuda()
+    bits = synth.bf16_bits(synth.activations(5, S, D))
+    x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    x32 = torch.from_numpy(synth.bf16_to_f32(bits)).cuda()
     ws = moe.Workspace(zl.cfg, S, moe.WS_BATCH)
     out = moe.moe_layer_forward_batch(zl, x, ws)
     idx = torch.empty(S, K, dtype=torch.int32, device="cuda")
     moe.moe_layer_forward_batch(zl, x, ws, out=out, topk_idx=idx)
+    out32 = moe.moe_layer_forward_batch(zl, x32, ws)
     torch.cuda.synchronize()
+    if not torch.equal(out.view(torch.int32), out32.view(torch.int32)):
+        raise RuntimeError("bf16 rows and their float32 widening gave different bits")
     used = int(np.unique(idx.cpu().numpy()).size) + 1  # + the shared expert
     cold = timed_cold(lambda: moe.moe_layer_forward_batch(zl, x, ws, out=out), 2 * iters)
     us = float(np.median(cold))
+    cold32 = timed_cold(lambda: moe.moe_layer_forward_batch(zl, x32, ws, out=out32), 2 * iters)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
@@ -306,14 +313,15 @@ def bench_prefill(layer, iters: int = 5):
     torch.cuda.synchronize()
     warm_us = e0.elapsed_time(e1) * 1e3 / iters
     ops = 2 * S * P * 3 * I * D  # int8 multiply-adds of the expert matmuls, x2
-    nbytes = used * EXPERT_BYTES + ROUTER_BYTES + S * D * 4 + S * D * 4  # x read as float32
+    nbytes = used * EXPERT_BYTES + ROUTER_BYTES + S * D * 2 + S * D * 4  # bf16 x, float32 out
     ideal_us = max(nbytes / (HBM_PEAK_GBPS * 1e3), ops / (INT8_PEAK_TOPS * 1e6))
     log(f"prefill 2048: {us:.1f} us cold ({warm_us:.1f} warm), {ops / us / 1e6:.1f} TOPS "
-        f"({used} experts read)")
-    return {"workload": "GLM-shape layer, 2048-token prefill (bf16 activation values, uniform "
+        f"({used} experts read); float32 rows {float(np.median(cold32)):.1f} us")
+    return {"workload": "GLM-shape layer, 2048-token prefill (bf16 activation rows, uniform "
                         "routing), unique-expert union with int8 MFMA grouped GEMMs",
             "timing": "cold: a 1 GiB buffer written before each iteration (median reported)",
             "us": round(us, 1), "us_spread": spread(cold), "warm_us": round(warm_us, 1),
+            "us_float32_rows": round(float(np.median(cold32)), 1),
             "tokens_per_s": round(S / us * 1e6, 1),
             "int8_TOPS": round(ops / us / 1e6, 1), "expert_int8_ops": ops,
             "experts_read": used, "hbm_bytes": nbytes,

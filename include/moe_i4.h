@@ -73,6 +73,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * x <- x + block(rmsnorm(x)) in place.  Needs D % 4 == 0, D <= 8192 and
  * 16-byte aligned x and gamma (MOE_EALIGN otherwise). */
 #define MOE_F_PRENORM 2u
+/* x holds bf16 values (uint16 bit patterns, [S][D], 16-byte aligned) instead
+ * of float32.  Section 08 reads bf16 tensors by widening them to float32; the
+ * widening is exact (a bf16 value is the top 16 bits of its float32), and the
+ * router and the section 12 quantization do it as they load, so the call
+ * returns the bits it returns for the widened float32 rows while x costs half
+ * the bytes.  Union-path calls only (moe_layer_forward_batch,
+ * moe_layer_forward_batch_routed), not with MOE_F_PRENORM; MOE_EINVAL
+ * otherwise. */
+#define MOE_F_X_BF16 4u
 
 typedef struct {
   int32_t D;          /* hidden size (6144 for the GLM shape) */

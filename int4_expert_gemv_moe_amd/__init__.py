@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("MOE_I4_LIB") or os.path.join(HERE, "libmoe_i4.so")
 MOE_F32, MOE_BF16 = 0, 1
 F_ACCUMULATE = 1
 F_PRENORM = 2
+F_X_BF16 = 4
 WS_FORWARD, WS_BATCH, WS_SWIGLU, WS_ROUTER, WS_SWIGLU8, WS_SHARED8 = 0, 1, 2, 3, 4, 5
 
 _lib = None
@@ -524,9 +525,19 @@ def _probe(topk_idx=None, topk_w=None, ev_gateup=None, ev_down=None, keff=None):
     return p
 
 
+def _x_flags(x, flags, union: bool):
+    """Checks x (float32, or bf16 on the union calls) and returns flags with
+    F_X_BF16 set for bf16 rows."""
+    if union and x.dtype == torch.bfloat16:
+        _dev(x, torch.bfloat16, "x")
+        return flags | F_X_BF16
+    _dev(x, torch.float32, "x")
+    return flags
+
+
 def _layer_call(fn_name, layer: DeviceLayer, x, out, flags, ws, topk_idx, topk_w, ev_gateup,
                 ev_down, stream, norm_gamma=None, norm_eps=1e-5, keff=None):
-    _dev(x, torch.float32, "x")
+    flags = _x_flags(x, flags, fn_name == "moe_layer_forward_batch")
     S = x.shape[0]
     if out is None:
         out = torch.empty(S, layer.cfg.D, dtype=torch.float32, device=x.device)
@@ -556,7 +567,8 @@ def moe_layer_forward_batch(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, 
                             flags: int = 0, topk_idx=None, topk_w=None, ev_gateup=None,
                             ev_down=None, stream=None, norm_gamma=None, norm_eps: float = 1e-5,
                             keff=None):
-    """Unique-expert union path: each selected expert is read once per call."""
+    """Unique-expert union path: each selected expert is read once per call.
+    x may be bf16 (flag F_X_BF16): the result is that of x.float()."""
     return _layer_call("moe_layer_forward_batch", layer, x, out, flags, ws, topk_idx, topk_w,
                        ev_gateup, ev_down, stream, norm_gamma, norm_eps, keff)
 
@@ -609,8 +621,8 @@ def moe_layer_forward_routed(layer, x: torch.Tensor, topk_idx: torch.Tensor, top
     """Per-token path with the routing given: topk_idx [S][K] int32 indices
     into layer's routed stack, topk_w [S][K] float32 weights (device).
     fn_name="moe_layer_forward_batch_routed": the union path instead (its
-    workspace is WS_BATCH)."""
-    _dev(x, torch.float32, "x")
+    workspace is WS_BATCH; x may then be bf16)."""
+    flags = _x_flags(x, flags, fn_name == "moe_layer_forward_batch_routed")
     _dev(topk_idx, torch.int32, "topk_idx")
     _dev(topk_w, torch.float32, "topk_w")
     S = x.shape[0]

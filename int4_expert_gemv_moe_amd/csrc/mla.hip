@@ -7,44 +7,58 @@
 // Four launches, split over the cache like flash decoding:
 //   1. absorb: qabs[s][h] = W_UK[h]^T q_nope[s][h] (eight workgroups per
 //      query and head, each an eighth of the key rows; 16-byte loads);
-//   2. chunks: workgroup (s, four heads, k) reads cache rows [ck, ck + c)
-//      (c = 64 or 128) of the query's window once and forms, per head, the
-//      chunk's max m_k, exp sum l_k and latent sum sum_t e^(score_t - m_k) L[t]
-//      in one pass (online softmax);
+//   2. splits: workgroup (s, 32 heads, k) walks cache rows [k R, (k + 1) R)
+//      of the query's window 32 rows at a time and forms, per head, the
+//      split's max m_k, exp sum l_k and latent sum sum_t e^(score_t - m_k) L[t]
+//      (online softmax), both products on fp32 matrix cores
+//      (mla_attn_mfma_kernel, latent + rotary width up to 576); wider latents
+//      use mla_chunk_kernel (four heads per workgroup, v_fma);
 //   3. merge: per (s, h) the chunks merge with weights e^(m_k - m) and the
 //      latent is normalized (eight workgroups per query and head, each an
 //      eighth of the latent columns);
 //   4. value: the value up-projection gives ctx (eight workgroups per query
 //      and head, each an eighth of the value rows).
 // All float32; the oracle computes in double.
+#include <algorithm>
+
 #include "moe_kernels.h"
 
 namespace moe {
 
-// Workgroup (s, h, part) sums the key rows d of its share of [0, nope).
-// Thread t takes latent columns 4 (t % (kvl/4)) .. +3 (16-byte loads) of rows
-// d0 + t / (kvl/4), stepping by floor(1024 / kvl) rows;
-// the row phases are added through shared memory in a fixed order.  The
-// chunk kernel adds the parts' vectors in a fixed order.
+// Workgroup (s, h, part) forms latent columns [c0, c1) = kvl part / P ..
+// (P = kMlaAbsorbParts) of qabs[s][h] over all key rows d < nope.  Thread t
+// takes columns c0 + 4 (t % tpr) .. +3 (16-byte loads, tpr = (c1 - c0) / 4
+// threads per row) of rows d = t / tpr, t / tpr + nph, ... (nph = 256 / tpr
+// row phases), all its loads issued before the sums; the row phases are
+// added through shared memory in a fixed order.
 __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   __shared__ float4 red[256];
   const int sh = blockIdx.x / kMlaAbsorbParts, part = blockIdx.x % kMlaAbsorbParts;
   const int h = sh % a.H;
-  const int d0 = a.nope * part / kMlaAbsorbParts, d1 = a.nope * (part + 1) / kMlaAbsorbParts;
+  const int c0 = a.kvl * part / kMlaAbsorbParts, c1 = a.kvl * (part + 1) / kMlaAbsorbParts;
   const float *qp = a.q + (int64_t)sh * (a.nope + a.rope);
-  const float *wk = a.kv_b + (int64_t)h * (a.nope + a.vdim) * a.kvl;
-  const int tpr = a.kvl >> 2;           // threads per row (16 .. 256)
-  const int nph = 256 / tpr;            // row phases (1 .. 16); threads past nph * tpr idle
+  const float *wk = a.kv_b + (int64_t)h * (a.nope + a.vdim) * a.kvl + c0;
+  const int tpr = (c1 - c0) >> 2;       // threads per row (2 .. 32)
+  const int nph = 256 / tpr;            // row phases (8 .. 128)
   const int c4 = threadIdx.x % tpr, ph = threadIdx.x / tpr;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int d = d0 + ph; ph < nph && d < d1; d += nph) {
-    const float qd = qp[d];
-    const float4 w = reinterpret_cast<const float4 *>(wk + (int64_t)d * a.kvl)[c4];
-    acc.x = fmaf(qd, w.x, acc.x);
-    acc.y = fmaf(qd, w.y, acc.y);
-    acc.z = fmaf(qd, w.z, acc.z);
-    acc.w = fmaf(qd, w.w, acc.w);
+  constexpr int U = 8;  // rows per batch of loads in flight
+  for (int d0 = ph; d0 < a.nope; d0 += U * nph) {
+    float4 w[U];
+    float qd[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int d = min(d0 + u * nph, a.nope - 1);
+      w[u] = reinterpret_cast<const float4 *>(wk + (int64_t)d * a.kvl)[c4];
+      qd[u] = d0 + u * nph < a.nope ? qp[d] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      acc.x = fmaf(qd[u], w[u].x, acc.x);
+      acc.y = fmaf(qd[u], w[u].y, acc.y);
+      acc.z = fmaf(qd[u], w[u].z, acc.z);
+      acc.w = fmaf(qd[u], w[u].w, acc.w);
+    }
   }
   red[threadIdx.x] = acc;
   __syncthreads();
@@ -57,7 +71,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
       t.z += u.z;
       t.w += u.w;
     }
-    reinterpret_cast<float4 *>(a.qabs + ((int64_t)sh * kMlaAbsorbParts + part) * a.kvl)[c4] = t;
+    reinterpret_cast<float4 *>(a.qabs + (int64_t)sh * a.kvl + c0)[c4] = t;
   }
 }
 
@@ -97,17 +111,12 @@ __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
     }
     return;
   }
-  // the heads' absorbed queries: the workgroup adds the absorption parts
-  // once into shared memory (fixed order), then every wave reads them
+  // the heads' absorbed queries into shared memory, then every wave reads them
   __shared__ float qsum[kMlaHeads][64 * MAXJ];
   for (int idx = tid; idx < kMlaHeads * a.kvl; idx += 256) {
     const int hb = idx / a.kvl, i = idx - hb * a.kvl;
     const int64_t sh = (int64_t)s * a.H + min(h0 + hb, a.H - 1);
-    const float *qab = a.qabs + sh * kMlaAbsorbParts * a.kvl + i;
-    float v = 0.f;
-#pragma unroll
-    for (int p = 0; p < kMlaAbsorbParts; p++) v += qab[p * a.kvl];
-    qsum[hb][i] = v;
+    qsum[hb][i] = a.qabs[sh * a.kvl + i];
   }
   __syncthreads();
   float qa[kMlaHeads][MAXJ], qr[kMlaHeads];
@@ -183,6 +192,255 @@ __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
       a.pm[part] = mm;
       a.pl[part] = ll;
     }
+  }
+}
+
+// ---- attention on fp32 matrix cores ----------------------------------------------
+//
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][k] and B[k][l % 16] for
+// its k-group l / 16 and receives C[4 (l / 16) + i][l % 16], i = 0..3.  The
+// contraction index is permuted consistently for A and B: MFMA number s
+// (0..3) of a 16-column block q takes column 16 q + 4 (l / 16) + s, so one
+// 16-byte shared-memory read gives a lane its operands of four MFMAs.
+//
+// Per 32-row step of a workgroup (32 heads, four waves):
+//   scores  S[row][head] = L_row . qabs_head + R_row . qrope_head: wave w
+//           takes rows 16 (w % 2) .., heads 16 (w / 2) .. (one 16x16 tile,
+//           Kp / 4 MFMAs);
+//   softmax per head over the step's rows, folded into the running max and
+//           exp sum (the running latent sums are rescaled by e^(m_old - m_new));
+//   latent  clat[head][col] += sum_row p[head][row] L[row][col]: wave w takes
+//           columns w kvl / 4 .., both 16-head tiles (kvl / 64 column tiles).
+// The step's cache rows (latent and rotary columns, row stride kMlaMS floats,
+// 4 banks apart so the 16 lanes of a read hit distinct banks) are read from
+// global memory once per workgroup; the next step's rows are loaded into
+// registers while the step computes.
+constexpr int kMlaMH = 32;               // heads per workgroup
+constexpr int kMlaMR = 32;               // cache rows per step
+constexpr int kMlaMK = 576;              // latent + rotary (rounded up to 16) columns at most
+constexpr int kMlaMS = kMlaMK + 4;       // shared row stride (floats)
+constexpr int kMlaPS = kMlaMR + 4;       // softmax-weight row stride (floats)
+constexpr int kMlaLoads = kMlaMR * kMlaMK / 4 / 256;  // 16-byte row loads per thread per step
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+bool mla_mfma_fits(int kvl, int rope, const float *L, const float *R) {
+  // the cache rows are read in 16-byte pieces
+  const bool al = ((uintptr_t)L & 15u) == 0 && (rope == 0 || ((uintptr_t)R & 15u) == 0);
+  return al && rope % 4 == 0 && kvl + (rope + 15) / 16 * 16 <= kMlaMK;
+}
+
+int mla_mfma_splits(int S, int T, int H) {
+  const int groups = (H + kMlaMH - 1) / kMlaMH;
+  const int target = std::max(1, 256 / std::max(1, S * groups));
+  return std::max(1, std::min(std::min(kMlaMaxSplit, (T + kMlaMR - 1) / kMlaMR), target));
+}
+
+__global__ __launch_bounds__(256) void mla_attn_mfma_kernel(MlaArgs a) {
+  __shared__ __align__(16) float qs[kMlaMH * kMlaMS];  // [head][column]
+  __shared__ __align__(16) float ls[kMlaMR * kMlaMS];  // [row][column]
+  __shared__ __align__(16) float ps[kMlaMH * kMlaPS];  // [head][row]
+  __shared__ float cmax[2][kMlaMH], csum[2][kMlaMH];
+  __shared__ float mrun[kMlaMH], lrun[kMlaMH], mnew[kMlaMH], alpha[kMlaMH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int groups = (a.H + kMlaMH - 1) / kMlaMH;
+  const int k = blockIdx.x % a.nsplit;
+  const int sg = blockIdx.x / a.nsplit;
+  const int s = sg / groups, h0 = (sg % groups) * kMlaMH;
+  const int kp = a.kvl + (a.rope + 15) / 16 * 16;  // contraction columns
+  const int c4n = kp / 4, kv4 = a.kvl / 4, ro4 = a.rope / 4;
+  const int n = a.T - a.S + 1 + s;                  // visible rows of query s
+  const int per = (a.T + a.nsplit - 1) / a.nsplit;
+  const int rows = (per + kMlaMR - 1) / kMlaMR * kMlaMR;
+  const int r0 = k * rows, r1 = min(n, r0 + rows);
+  const int steps = r1 > r0 ? (r1 - r0 + kMlaMR - 1) / kMlaMR : 0;
+
+  // the absorbed queries, the same pieces as a step's rows (head for row),
+  // every load unconditional (a piece outside the queries reads qabs[0] and
+  // is replaced by zeros); then the rotary queries (4-byte aligned, scalar
+  // loads) and zeros in the padding columns
+  {
+    const float *qbase = a.qabs;
+    float4 qv[kMlaLoads];
+#pragma unroll
+    for (int i = 0; i < kMlaLoads; i++) {
+      const int f = tid + 256 * i;
+      const int hb = f / c4n, c4 = f - hb * c4n, h = h0 + hb;
+      const bool ok = hb < kMlaMH && h < a.H && c4 < kv4;
+      const float *src = ok ? a.qabs + ((int64_t)s * a.H + h) * a.kvl + 4 * c4 : qbase;
+      const float4 v = *reinterpret_cast<const float4 *>(src);
+      qv[i] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < kMlaLoads; i++) {
+      const int f = tid + 256 * i;
+      const int hb = f / c4n, c4 = f - hb * c4n;
+      if (hb < kMlaMH) *reinterpret_cast<float4 *>(qs + hb * kMlaMS + 4 * c4) = qv[i];
+    }
+    __syncthreads();
+    const int pad = kp - a.kvl;  // rotary columns and their padding
+    for (int i = tid; i < kMlaMH * pad; i += 256) {
+      const int hb = i / pad, d = i - hb * pad, h = h0 + hb;
+      float v = 0.f;
+      if (h < a.H && d < a.rope) v = a.q[((int64_t)s * a.H + h) * (a.nope + a.rope) + a.nope + d];
+      qs[hb * kMlaMS + a.kvl + d] = v;
+    }
+  }
+  if (tid < kMlaMH) {
+    mrun[tid] = -INFINITY;
+    lrun[tid] = 0.f;
+  }
+  // the rows of a step into registers: load i of thread t is 16-byte piece
+  // f = t + 256 i of the step, row f / c4n, column piece f % c4n
+  float4 pre[kMlaLoads];
+  // every load unconditional: pieces past the step's rows or the row's
+  // columns read L[0] and are replaced by zeros
+  auto load_rows = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < kMlaLoads; i++) {
+      const int f = tid + 256 * i;
+      const int r = f / c4n, c4 = f - r * c4n;
+      const int t = t0 + r;
+      const bool ok = r < kMlaMR && t < r1 && c4 < kv4 + ro4;
+      const float *src = c4 < kv4 ? a.L + (int64_t)t * a.kvl + 4 * c4
+                                  : a.R + (int64_t)t * a.rope + 4 * (c4 - kv4);
+      const float4 v = *reinterpret_cast<const float4 *>(ok ? src : a.L);
+      pre[i] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  v4f acc[2][8];  // running latent sums: head tile, column tile
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int ct = 0; ct < 8; ct++) acc[mt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int nct = a.kvl / 64;            // column tiles per wave (kvl / 4 columns)
+  const int cw0 = wave * (a.kvl / 4);
+  const int rt = wave & 1, ht = wave >> 1;
+  if (steps > 0) load_rows(r0);
+  for (int st = 0; st < steps; st++) {
+    const int t0 = r0 + st * kMlaMR;
+#pragma unroll
+    for (int i = 0; i < kMlaLoads; i++) {
+      const int f = tid + 256 * i;
+      const int r = f / c4n, c4 = f - r * c4n;
+      if (r < kMlaMR) *reinterpret_cast<float4 *>(ls + r * kMlaMS + 4 * c4) = pre[i];
+    }
+    __syncthreads();  // the rows (and, on the first step, the queries) are in place
+    if (st + 1 < steps) load_rows(t0 + kMlaMR);
+    // scores of rows 16 rt + .., heads 16 ht + ..
+    // four independent accumulators (one per MFMA of a column block), added
+    // at the end in a fixed order
+    v4f sc;
+    {
+      const float *arow = ls + (16 * rt + ln) * kMlaMS + 4 * lg;
+      const float *brow = qs + (16 * ht + ln) * kMlaMS + 4 * lg;
+      v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+#pragma unroll 4
+      for (int q = 0; q < kp / 16; q++) {
+        const float4 av = *reinterpret_cast<const float4 *>(arow + 16 * q);
+        const float4 bv = *reinterpret_cast<const float4 *>(brow + 16 * q);
+        s0 = mfma_f32(av.x, bv.x, s0);
+        s1 = mfma_f32(av.y, bv.y, s1);
+        s2 = mfma_f32(av.z, bv.z, s2);
+        s3 = mfma_f32(av.w, bv.w, s3);
+      }
+      sc = (s0 + s1) + (s2 + s3);
+    }
+    // lane holds rows 16 rt + 4 lg + i of head 16 ht + ln
+    const int hh = 16 * ht + ln;
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int t = t0 + 16 * rt + 4 * lg + i;
+      sv[i] = t < r1 ? sc[i] * a.scale : -INFINITY;
+      mx = fmaxf(mx, sv[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (lg == 0) cmax[rt][hh] = mx;
+    __syncthreads();
+    if (tid < kMlaMH) {
+      const float mo = mrun[tid];
+      const float mn = fmaxf(mo, fmaxf(cmax[0][tid], cmax[1][tid]));
+      alpha[tid] = mo == -INFINITY ? 0.f : expf(mo - mn);
+      mnew[tid] = mn;
+      mrun[tid] = mn;
+    }
+    __syncthreads();
+    {
+      const float mn = mnew[hh];
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float pv = sv[i] == -INFINITY ? 0.f : expf(sv[i] - mn);
+        ps[hh * kMlaPS + 16 * rt + 4 * lg + i] = pv;
+        sum += pv;
+      }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      if (lg == 0) csum[rt][hh] = sum;
+    }
+    __syncthreads();  // the weights and row sums are in place
+    if (tid < kMlaMH) lrun[tid] = fmaf(lrun[tid], alpha[tid], csum[0][tid] + csum[1][tid]);
+    // latent sums of columns cw0 + 16 ct + ln, heads 16 mt + 4 lg + i
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) al[i] = alpha[16 * mt + 4 * lg + i];
+#pragma unroll
+      for (int ct = 0; ct < 8; ct++)
+        if (ct < nct)
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[mt][ct][i] *= al[i];
+    }
+#pragma unroll
+    for (int q = 0; q < kMlaMR / 16; q++) {
+      float4 pa[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++)
+        pa[mt] = *reinterpret_cast<const float4 *>(ps + (16 * mt + ln) * kMlaPS + 16 * q + 4 * lg);
+      const float *lrow = ls + (16 * q + 4 * lg) * kMlaMS + cw0 + ln;
+#pragma unroll
+      for (int ct = 0; ct < 8; ct++) {
+        if (ct < nct) {
+          const float b0 = lrow[16 * ct], b1 = lrow[kMlaMS + 16 * ct];
+          const float b2 = lrow[2 * kMlaMS + 16 * ct], b3 = lrow[3 * kMlaMS + 16 * ct];
+#pragma unroll
+          for (int mt = 0; mt < 2; mt++) {
+            acc[mt][ct] = mfma_f32(pa[mt].x, b0, acc[mt][ct]);
+            acc[mt][ct] = mfma_f32(pa[mt].y, b1, acc[mt][ct]);
+            acc[mt][ct] = mfma_f32(pa[mt].z, b2, acc[mt][ct]);
+            acc[mt][ct] = mfma_f32(pa[mt].w, b3, acc[mt][ct]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with the step's rows and weights
+  }
+  // the split's partial results
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int h = h0 + 16 * mt + 4 * lg + i;
+      if (h < a.H) {
+        float *dst = a.pclat + (((int64_t)s * a.H + h) * a.nsplit + k) * a.kvl + cw0 + ln;
+#pragma unroll
+        for (int ct = 0; ct < 8; ct++)
+          if (ct < nct) dst[16 * ct] = acc[mt][ct][i];
+      }
+    }
+  if (tid < kMlaMH && h0 + tid < a.H) {
+    const int64_t part = ((int64_t)s * a.H + h0 + tid) * a.nsplit + k;
+    a.pm[part] = mrun[tid];
+    a.pl[part] = lrun[tid];
   }
 }
 
@@ -278,6 +536,13 @@ __global__ __launch_bounds__(256) void mla_value_kernel(MlaArgs a) {
 hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st) {
   const int sh = a.S * a.H;
   hipLaunchKernelGGL(mla_absorb_kernel, dim3(sh * kMlaAbsorbParts), dim3(256), 0, st, a);
+  if (mla_mfma_fits(a.kvl, a.rope, a.L, a.R)) {
+    const int groups = (a.H + kMlaMH - 1) / kMlaMH;
+    hipLaunchKernelGGL(mla_attn_mfma_kernel, dim3(a.S * groups * a.nsplit), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(mla_merge_kernel, dim3(sh * kMlaMergeParts), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(mla_value_kernel, dim3(sh * kMlaValueParts), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   const int ngroups = (a.H + kMlaHeads - 1) / kMlaHeads;
   const dim3 grid(a.S * ngroups * a.nsplit);
   const int nj = a.kvl >> 6;

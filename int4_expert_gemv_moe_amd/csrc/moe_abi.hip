@@ -240,11 +240,12 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 // its own when with_topk, otherwise inside the per-token gate/up kernel.
 int run_router(const moe_config &c, const float *x, int S, const float *W, const float *b,
                const Work &w, bool with_quant, bool with_topk, float *logits_out, hipStream_t st,
-               const float *gamma = nullptr, float eps = 0.f) {
+               const float *gamma = nullptr, float eps = 0.f, const uint16_t *xb = nullptr) {
   RouterArgs r{};
   r.gamma = gamma;
   r.eps = eps;
-  r.x = x;
+  r.x = xb ? nullptr : x;
+  r.xb = xb;
   r.W = W;
   r.S = S;
   r.D = c.D;
@@ -289,7 +290,9 @@ int layer_common_checks(const moe_config *cfg, const moe_layer *layer, const flo
                         bool router = true, bool shared_i4 = true) {
   MOE_TRY(check_cfg(cfg));
   if (S < 1 || !x || !out || !ws) return MOE_EINVAL;
-  if (flags & ~(MOE_F_ACCUMULATE | MOE_F_PRENORM)) return MOE_EINVAL;
+  if (flags & ~(MOE_F_ACCUMULATE | MOE_F_PRENORM | MOE_F_X_BF16)) return MOE_EINVAL;
+  // bf16 tokens: union-path calls only, without the in-call RMSNorm
+  if ((flags & MOE_F_X_BF16) && (which != W_BATCH || (flags & MOE_F_PRENORM))) return MOE_EINVAL;
   MOE_TRY(check_layer(*cfg, layer, router, shared_i4));
   if (!aligned16(x) || ((uintptr_t)out & 3u) || ((uintptr_t)ws & 255u)) return MOE_EALIGN;
   const bool prenorm = (flags & MOE_F_PRENORM) != 0;
@@ -300,7 +303,7 @@ int layer_common_checks(const moe_config *cfg, const moe_layer *layer, const flo
   }
   // out may be x itself only for the in-place residual update of PRENORM:
   // every read of x then precedes the first write of out
-  const size_t xb = (size_t)S * cfg->D * 4;
+  const size_t xb = (size_t)S * cfg->D * ((flags & MOE_F_X_BF16) ? 2 : 4);
   const bool same = (const void *)out == (const void *)x;
   if ((const char *)out < (const char *)x + xb && (const char *)x < (const char *)out + xb &&
       !(prenorm && same))
@@ -463,16 +466,23 @@ int mla_check(const moe_mla_config *c, int S, int T) {
   return MOE_OK;
 }
 
-size_t mla_carve(const moe_mla_config &c, int S, int T, char *base, MlaArgs *a) {
+// L and R: the call's cache arrays (their alignment chooses the attention
+// kernel); moe_mla_workspace_bytes sizes for the larger of the two layouts.
+size_t mla_carve(const moe_mla_config &c, int S, int T, char *base, MlaArgs *a,
+                 const float *L = nullptr, const float *R = nullptr, bool size_max = false) {
   const int chunk = mla_chunk_rows(T);
-  const size_t sh = (size_t)S * c.H, ns = (size_t)((T + chunk - 1) / chunk);
+  const size_t ns_v = (size_t)((T + chunk - 1) / chunk);
+  const size_t ns_m = (size_t)mla_mfma_splits(S, T, c.H);
+  const bool mf = mla_mfma_fits(c.kvl, c.rope, L, R);
+  const size_t sh = (size_t)S * c.H;
+  const size_t ns = size_max ? std::max(ns_v, ns_m) : (mf ? ns_m : ns_v);
   size_t off = 0;
   auto take = [&](size_t bytes) -> float * {
     float *p = base ? (float *)(base + off) : nullptr;
     off += align_up(bytes);
     return p;
   };
-  float *qabs = take(sh * kMlaAbsorbParts * c.kvl * 4);
+  float *qabs = take(sh * c.kvl * 4);
   float *pclat = take(sh * ns * c.kvl * 4);
   float *pm = take(sh * ns * 4);
   float *pl = take(sh * ns * 4);
@@ -492,7 +502,7 @@ size_t mla_carve(const moe_mla_config &c, int S, int T, char *base, MlaArgs *a) 
 
 size_t moe_mla_workspace_bytes(const moe_mla_config *cfg, int S, int T) {
   if (mla_check(cfg, S, T) != MOE_OK) return 0;
-  return mla_carve(*cfg, S, T, nullptr, nullptr);
+  return mla_carve(*cfg, S, T, nullptr, nullptr, nullptr, nullptr, true);
 }
 
 int moe_mla_decode(const moe_mla_config *cfg, const float *q, int S, const float *kv_b,
@@ -503,10 +513,10 @@ int moe_mla_decode(const moe_mla_config *cfg, const float *q, int S, const float
   if (((uintptr_t)q & 3u) || !aligned16(kv_b) || ((uintptr_t)L & 3u) ||
       ((uintptr_t)R & 3u) || ((uintptr_t)ctx & 3u) || ((uintptr_t)ws & 255u))
     return MOE_EALIGN;
-  if (ws_bytes < mla_carve(*cfg, S, T, nullptr, nullptr)) return MOE_EWORKSPACE;
+  if (ws_bytes < mla_carve(*cfg, S, T, nullptr, nullptr, L, R)) return MOE_EWORKSPACE;
   MOE_TRY(check_device());
   MlaArgs a{};
-  mla_carve(*cfg, S, T, (char *)ws, &a);
+  mla_carve(*cfg, S, T, (char *)ws, &a, L, R);
   a.S = S;
   a.T = T;
   a.H = cfg->H;
@@ -869,12 +879,15 @@ int layer_forward_batch_impl(const moe_config *cfg, const moe_layer *layer, cons
   }
   // small batches select inside the grouping kernel (one launch fewer)
   const bool topk_in_group = !given && S <= kGroupTopkMaxTokens && c.E <= 256;
+  // bf16 tokens (MOE_F_X_BF16): x holds bf16 bit patterns
+  const uint16_t *xbf = (flags & MOE_F_X_BF16) ? reinterpret_cast<const uint16_t *>(x) : nullptr;
+  flags &= ~MOE_F_X_BF16;
   if (given) {
-    QuantArgs q{x, nullptr, c.D, w.xq, nullptr, w.sx, w.sumx};
+    QuantArgs q{xbf ? nullptr : x, xbf, c.D, w.xq, nullptr, w.sx, w.sumx};
     MOE_TRY_HIP(launch_quant(q, S, stream));
   } else {
     MOE_TRY(run_router(c, x, S, layer->router_w, layer->router_b, w, true, !topk_in_group, nullptr,
-                       stream, gamma, layer->norm_eps));
+                       stream, gamma, layer->norm_eps, xbf));
   }
   int32_t *idx = given ? const_cast<int32_t *>(given_idx) : w.idx;
   const float *wts = given ? given_w : w.w;

@@ -16,7 +16,8 @@ struct QuantArgs {
 };
 
 struct RouterArgs {
-  const float *x;      // [S][D]
+  const float *x;      // [S][D] float32 tokens, or
+  const uint16_t *xb;  // [S][D] bf16 tokens (bit patterns; then x is unused)
   const float *W;      // [E][D]
   int S, D, E;
   float *logits;       // [S][E] scratch (always written)
@@ -279,7 +280,7 @@ struct MlaArgs {
   const float *kv_b;   // [H][nope + vdim][kvl]
   const float *L;      // [T][kvl]
   const float *R;      // [T][rope]
-  float *qabs;         // [S][H][kMlaAbsorbParts][kvl] partial absorbed queries
+  float *qabs;         // [S][H][kvl] absorbed queries
   float *pclat;        // [S][H][nsplit][kvl] per-chunk latent sums
   float *pm, *pl;      // [S][H][nsplit] per-chunk max and exp sum
   float *clat;         // [S][H][kvl] merged, normalized latent
@@ -287,6 +288,11 @@ struct MlaArgs {
 };
 
 hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st);
+// The matrix-core attention applies when kvl + rope (rounded up to 16) <= 576,
+// rope % 4 == 0 and the cache arrays are 16-byte aligned; it splits each
+// query's cache into mla_mfma_splits parts.
+bool mla_mfma_fits(int kvl, int rope, const float *L, const float *R);
+int mla_mfma_splits(int S, int T, int H);
 
 hipError_t launch_pack_int2(const Pack2Args &a, hipStream_t st);
 hipError_t launch_swiglu2_gateup(const Swiglu2Args &a, hipStream_t st);

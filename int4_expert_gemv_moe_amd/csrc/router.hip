@@ -20,6 +20,20 @@
 
 namespace moe {
 
+// Four consecutive activations of row `row` (element offset 4 i): float32
+// rows, or bf16 rows (XB) widened exactly (a bf16 value is the top half of
+// its float32), so both give the router the same float operands.
+template <bool XB>
+__device__ __forceinline__ float4 ldx4(const RouterArgs &a, const float *row, int64_t rowi, int i) {
+  if constexpr (XB) {
+    const uint2 w = reinterpret_cast<const uint2 *>(a.xb + rowi * a.D)[i];
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+  } else {
+    return reinterpret_cast<const float4 *>(row)[i];
+  }
+}
+
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
   const int s = blockIdx.x;
   quant_row_block(a.xf ? a.xf + (int64_t)s * a.D : nullptr,
@@ -73,7 +87,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 // quantize token (index - n_router) and clear its amax slots.
 // With a.gamma (TS == 1 launches) every workgroup first forms its token's
 // RMSNorm row in dynamic shared memory and works on that.
-template <int TS, int JB>
+// XB: the tokens are bf16 rows a.xb (no RMSNorm with them).
+template <int TS, int JB, bool XB = false>
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   extern __shared__ __align__(16) float xn_dyn[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -82,7 +97,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   const bool quant = (int)blockIdx.x >= n_router;
   const int e = (blockIdx.x % ne4) * 4 + wave;
   const int s0 = quant ? blockIdx.x - n_router : (blockIdx.x / ne4) * TS;
-  const bool normed = TS == 1 && a.gamma;
+  const bool normed = !XB && TS == 1 && a.gamma;
   if (normed) {
     NormRow nr;
     norm_row_load(a.x + (int64_t)s0 * a.D, a.gamma, a.D, nr);
@@ -93,8 +108,8 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   if (quant) {
     const int s = s0;
     if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
-    quant_row_block(xrow(s), nullptr, a.D, a.xq_perm + (int64_t)s * a.D, nullptr, a.sx + s,
-                    a.sumx + s);
+    quant_row_block(XB ? nullptr : xrow(s), XB ? a.xb + (int64_t)s * a.D : nullptr, a.D,
+                    a.xq_perm + (int64_t)s * a.D, nullptr, a.sx + s, a.sumx + s);
     return;
   }
   if (e >= a.E) return;
@@ -113,12 +128,12 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 #pragma unroll
     for (int t = 0; t < TS; t++) {
       if (s0 + t < a.S) {
-        const float4 *xr = reinterpret_cast<const float4 *>(xrow(s0 + t));
+        const float *xr = XB ? nullptr : xrow(s0 + t);
         float4 xv[JB];
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) {
           xv[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (j0 + jj < nj) xv[jj] = xr[lane + 64 * (j0 + jj)];
+          if (j0 + jj < nj) xv[jj] = ldx4<XB>(a, xr, s0 + t, lane + 64 * (j0 + jj));
         }
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) {
@@ -148,7 +163,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 // is still lane p's ascending FMA chain over k = 4p + 256j + q followed by
 // wave_sum_f32, i.e. the same bits as router_kernel.  The operands of step
 // j + 1 are loaded while step j is multiplied.
-template <int TT, int EE, int TG>
+template <int TT, int EE, int TG, bool XB = false>
 __global__ __launch_bounds__(256 * TG) void router_tile_kernel(RouterArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int neb = (a.E + 4 * EE - 1) / (4 * EE);
@@ -156,8 +171,8 @@ __global__ __launch_bounds__(256 * TG) void router_tile_kernel(RouterArgs a) {
   if ((int)blockIdx.x >= n_router) {
     const int s = blockIdx.x - n_router;
     if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
-    quant_row_block(a.x + (int64_t)s * a.D, nullptr, a.D, a.xq_perm + (int64_t)s * a.D, nullptr,
-                    a.sx + s, a.sumx + s);
+    quant_row_block(XB ? nullptr : a.x + (int64_t)s * a.D, XB ? a.xb + (int64_t)s * a.D : nullptr,
+                    a.D, a.xq_perm + (int64_t)s * a.D, nullptr, a.sx + s, a.sumx + s);
     return;
   }
   // TG groups of 4 waves: group g takes tokens s0 + TT g .. +TT, wave w % 4
@@ -166,10 +181,11 @@ __global__ __launch_bounds__(256 * TG) void router_tile_kernel(RouterArgs a) {
   const int e0 = (blockIdx.x % neb) * 4 * EE + (wave & 3) * EE;
   const int s0 = (blockIdx.x / neb) * TG * TT + (wave >> 2) * TT;
   if (e0 >= a.E || s0 >= a.S) return;
-  const float4 *xr[TT], *wr[EE];
+  const float4 *wr[EE];
+  int64_t xs[TT];  // token rows (clamped)
 #pragma unroll
-  for (int t = 0; t < TT; t++)
-    xr[t] = reinterpret_cast<const float4 *>(a.x + (int64_t)min(s0 + t, a.S - 1) * a.D) + lane;
+  for (int t = 0; t < TT; t++) xs[t] = min(s0 + t, a.S - 1);
+  const float *xbase = XB ? nullptr : a.x;
 #pragma unroll
   for (int e = 0; e < EE; e++)
     wr[e] = reinterpret_cast<const float4 *>(a.W + (int64_t)min(e0 + e, a.E - 1) * a.D) + lane;
@@ -181,14 +197,15 @@ __global__ __launch_bounds__(256 * TG) void router_tile_kernel(RouterArgs a) {
   const int nj = a.D >> 8;
   float4 xv[TT], wv[EE];
 #pragma unroll
-  for (int t = 0; t < TT; t++) xv[t] = xr[t][0];
+  for (int t = 0; t < TT; t++) xv[t] = ldx4<XB>(a, XB ? nullptr : xbase + xs[t] * a.D, xs[t], lane);
 #pragma unroll
   for (int e = 0; e < EE; e++) wv[e] = wr[e][0];
   for (int j = 0; j < nj; j++) {
     const int jn = min(j + 1, nj - 1) * 64;
     float4 xn[TT], wn[EE];
 #pragma unroll
-    for (int t = 0; t < TT; t++) xn[t] = xr[t][jn];
+    for (int t = 0; t < TT; t++)
+      xn[t] = ldx4<XB>(a, XB ? nullptr : xbase + xs[t] * a.D, xs[t], lane + jn);
 #pragma unroll
     for (int e = 0; e < EE; e++) wn[e] = wr[e][jn];
 #pragma unroll
@@ -234,21 +251,31 @@ hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
   // a few tokens: one token per wave, the whole weight row in one batch of
   // loads (rows are re-read per token from L2); up to 255: 4 x 4 register
   // tiles; more: 8 x 8 register tiles
+  const bool xb = a.xb != nullptr;  // bf16 tokens (no RMSNorm with them)
   if (a.S <= 8) {
     const size_t lds = a.gamma ? (size_t)a.D * 4 : 0;  // the normalized row
-    hipLaunchKernelGGL((router_kernel<1, 24>), dim3(ne4 * a.S + nq), dim3(256), lds, st, a);
+    if (xb)
+      hipLaunchKernelGGL((router_kernel<1, 24, true>), dim3(ne4 * a.S + nq), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((router_kernel<1, 24>), dim3(ne4 * a.S + nq), dim3(256), lds, st, a);
   } else if (a.S < kRouterTileMinTokens) {
     // 4 x 4 register tiles, 4 tokens x 16 experts per workgroup (swept against
     // one expert x 8 tokens per wave: 19-20 against 21-24 us up to 64 tokens,
     // 26-37 against 38-63 us from 128 to 255, router and selection together)
-    hipLaunchKernelGGL((router_tile_kernel<4, 4, 1>), dim3(((a.E + 15) / 16) * ((a.S + 3) / 4) + nq),
-                       dim3(256), 0, st, a);
+    const dim3 grid(((a.E + 15) / 16) * ((a.S + 3) / 4) + nq);
+    if (xb)
+      hipLaunchKernelGGL((router_tile_kernel<4, 4, 1, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((router_tile_kernel<4, 4, 1>), grid, dim3(256), 0, st, a);
   } else {
     // 4-wave workgroups of 8 tokens x 32 experts (swept against 8-wave
     // workgroups of 16 x 32 and other tiles: 188 against 209 us at 2048 tokens)
     const int neb = (a.E + 31) / 32;
-    hipLaunchKernelGGL((router_tile_kernel<8, 8, 1>), dim3(neb * ((a.S + 7) / 8) + nq), dim3(256),
-                       0, st, a);
+    const dim3 grid(neb * ((a.S + 7) / 8) + nq);
+    if (xb)
+      hipLaunchKernelGGL((router_tile_kernel<8, 8, 1, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((router_tile_kernel<8, 8, 1>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -161,7 +161,7 @@ def test_prenorm_flag_host_checks():
     for fn in (L.moe_layer_forward, L.moe_layer_forward_batch):
         def call(flags, out=x, lay=layer):
             return fn(ctypes.byref(cfg), ctypes.byref(lay), x, 1, out, flags, None, ws, 256, None)
-        assert call(4) == -1                                   # unknown flag bit
+        assert call(8) == -1                                   # unknown flag bit
         assert call(moe.F_ACCUMULATE) == -1                    # out overlaps x without the flag
         assert call(moe.F_ACCUMULATE | moe.F_PRENORM) == -4    # in place: only the workspace is short
         no_gamma = moe.LayerC(base, base, ex, ex, None, 1e-5)
@@ -171,6 +171,40 @@ def test_prenorm_flag_host_checks():
         assert call(moe.F_PRENORM, lay=moe.LayerC(base, base, ex, ex, base + 4, 1e-5)) == -3
         # out inside x but not equal to it stays refused
         assert call(moe.F_ACCUMULATE | moe.F_PRENORM, out=ctypes.c_void_p(base + 16)) == -1
+
+
+def test_bf16_token_flag_host_checks():
+    """MOE_F_X_BF16: accepted by the union calls only and not with
+    MOE_F_PRENORM; x then spans S * D * 2 bytes (the calls stop at the
+    workspace check here, before any device work)."""
+    import numpy as np
+    import int4_expert_gemv_moe_amd as moe
+    L = moe.lib()
+    cfg = moe.config(256, 128, 8, 2)
+    host = np.zeros(1 << 16, np.uint8)
+    base = host.ctypes.data + (-host.ctypes.data) % 256
+    q = moe.QMat(base, base, 0, 0)
+    ex = moe.Experts(q, q, q)
+    layer = moe.LayerC(base, base, ex, ex, base, 1e-5)
+    x = ctypes.c_void_p(base)
+    ws = ctypes.c_void_p(base)
+    out = ctypes.c_void_p(base + 2 * 256)  # just past one bf16 row of 256
+    bf = moe.F_X_BF16
+
+    def fwd(fn, flags, o=out):
+        return fn(ctypes.byref(cfg), ctypes.byref(layer), x, 1, o, flags, None, ws, 256, None)
+
+    def routed(fn, flags, o=out):
+        return fn(ctypes.byref(cfg), ctypes.byref(layer), x, 1, x, x, o, flags, ws, 256, None)
+
+    assert fwd(L.moe_layer_forward, bf) == -1                     # per-token path: refused
+    assert routed(L.moe_layer_forward_routed, bf) == -1
+    assert fwd(L.moe_layer_forward_batch, bf) == -4               # union: only the workspace is short
+    assert routed(L.moe_layer_forward_batch_routed, bf) == -4
+    assert fwd(L.moe_layer_forward_batch, bf | moe.F_PRENORM) == -1
+    # out one float32 row further would overlap a float32 x, not a bf16 one
+    assert fwd(L.moe_layer_forward_batch, 0) == -1
+    assert fwd(L.moe_layer_forward_batch, bf, ctypes.c_void_p(base + 256)) == -1
 
 
 def test_int8_format_host_checks():

@@ -237,6 +237,10 @@ def test_glm_prefill_2048_bf16():
     out_b2, idx_b2, _ = _run(dl, x, "batch")
     assert np.array_equal(idx_b, idx_b2)
     assert np.array_equal(out_b.view(np.uint32), out_b2.view(np.uint32))
+    say("prefill: union path on the bf16 rows themselves")
+    out_h, idx_h = _run_bf16(dl, x)
+    assert np.array_equal(idx_b, idx_h)
+    assert np.array_equal(out_b.view(np.uint32), out_h.view(np.uint32))
     say("prefill: per-token path")
     out_f, idx_f, w_f = _run(dl, x, "fwd")
     assert np.array_equal(idx_b, idx_f)
@@ -247,6 +251,49 @@ def test_glm_prefill_2048_bf16():
     ol = oracle_layer(1, GLM, 0, b)
     say("prefill: 64 tokens through the oracle")
     _check_oracle(ol, x, out_b, idx_b, w_b, _sample_rows(2048, 64), "glm prefill")
+
+
+def _run_bf16(layer, x_np, idx=None, w=None):
+    """The union path on bf16 rows (x_np must hold bf16 values); with idx/w
+    the given-routing union instead."""
+    S = x_np.shape[0]
+    bits = synth.bf16_bits(x_np)
+    assert np.array_equal(synth.bf16_to_f32(bits).view(np.uint32), x_np.view(np.uint32))
+    xh = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = moe.Workspace(layer.cfg, S, moe.WS_BATCH)
+    if idx is not None:
+        o = moe.moe_layer_forward_batch_routed(layer, xh, idx, w, ws)
+        torch.cuda.synchronize()
+        return to_np(o), None
+    ti = torch.empty(S, layer.cfg.K, dtype=torch.int32, device="cuda")
+    o = moe.moe_layer_forward_batch(layer, xh, ws, topk_idx=ti)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(ti)
+
+
+# the router's three launch shapes: up to 8 tokens, up to 255, and more
+@pytest.mark.parametrize("shape,S", [(MID, 5), (MID, 100), (MID, 300), (TINY, 1)])
+def test_bf16_tokens_equal_their_float32_widening(shape, S):
+    """bf16 token rows through the union path (router and quantization widen
+    them as they load) return the bits of the float32 rows they widen to,
+    with the router's selection and with given routing; the per-token path
+    refuses the flag."""
+    b = bias_for("uniform", 7, shape)
+    dl = device_layer(7, shape, 0, b)
+    x = synth.bf16_to_f32(synth.bf16_bits(synth.activations(30 + S, S, shape.D)))
+    say(f"bf16 tokens {shape} S={S}")
+    out_f, idx_f, w_f = _run(dl, x, "batch")
+    out_h, idx_h = _run_bf16(dl, x)
+    assert np.array_equal(idx_f, idx_h)
+    assert np.array_equal(out_f.view(np.uint32), out_h.view(np.uint32))
+    ti = torch.from_numpy(idx_f).cuda()
+    tw = torch.from_numpy(w_f).cuda()
+    out_r, _ = _run_bf16(dl, x, ti, tw)
+    assert np.array_equal(out_f.view(np.uint32), out_r.view(np.uint32))
+    xf = torch.from_numpy(x).cuda()
+    with pytest.raises(moe.MoeError):
+        moe.moe_layer_forward(dl, xf, moe.Workspace(dl.cfg, S, moe.WS_FORWARD),
+                              flags=moe.F_X_BF16)
 
 
 def test_error_codes():
