@@ -167,6 +167,29 @@ __device__ void gateup_fixed(const DecodeArgs &a, int s, int gb, float *xn) {
       xv[c][0] = ok ? v0 : make_uint4(0u, 0u, 0u, 0u);
       xv[c][1] = ok ? v1 : make_uint4(0u, 0u, 0u, 0u);
     }
+  } else if (a.xq_natural) {
+    // natural-order codes: each wave holds the whole row, so it reorders
+    // every 8 codes into the permuted layout and sums the row itself
+    load_x_codes<NCH, MASKED>(a.xq + (int64_t)s * a.D, a.D, xv);
+    sxs = a.sx[s];
+    gu_load<NCH, MASKED, ROWS>(res, a.I, rowbytes, first, hi, dummy, sa);
+    int part = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        uint4 &v = xv[c][h];
+        const uint32_t e0 = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u);
+        const uint32_t o0 = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
+        const uint32_t e1 = __builtin_amdgcn_perm(v.w, v.z, 0x06040200u);
+        const uint32_t o1 = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
+        v = make_uint4(e0, o0, e1, o1);
+        part = dot4((int)e0, 0x01010101, part);
+        part = dot4((int)o0, 0x01010101, part);
+        part = dot4((int)e1, 0x01010101, part);
+        part = dot4((int)o1, 0x01010101, part);
+      }
+    sumx = wave_sum_i32(part);
   } else {
     load_x_codes<NCH, MASKED>(a.xq + (int64_t)s * a.D, a.D, xv);
     sxs = a.sx[s];

@@ -79,7 +79,15 @@ size_t shared8_bytes(const moe_config &c, int S) {
 struct DecodeShape {
   int gu_fx, gu_rt, dn_fx, dn;
   int gu_fx8, dn_fx8;  // the same for an int8 fixed expert (rows twice as long)
+  int gu_one, dn_one;  // a one-expert call (the expert has the chip to itself)
 };
+
+#ifndef MOE_ONE_GU
+#define MOE_ONE_GU 256
+#endif
+#ifndef MOE_ONE_DN
+#define MOE_ONE_DN 256
+#endif
 
 DecodeShape decode_shape(const moe_config &c) {
   DecodeShape d;
@@ -88,6 +96,8 @@ DecodeShape decode_shape(const moe_config &c) {
   d.dn_fx = 192;
   d.gu_fx8 = 256;
   d.dn_fx8 = 256;
+  d.gu_one = MOE_ONE_GU;
+  d.dn_one = MOE_ONE_DN;
   // phase C: one pass of rows per workgroup
   const int cr = decode_c_rows_per_pass(c.I);
   d.dn = (c.D + cr - 1) / cr;
@@ -103,6 +113,8 @@ DecodeShape decode_shape(const moe_config &c) {
   d.dn = clampn(d.dn, c.D, 256);
   d.gu_fx8 = clampn(d.gu_fx8, c.I, 512);
   d.dn_fx8 = clampn(d.dn_fx8, c.D, 256);
+  d.gu_one = clampn(d.gu_one, c.I, 512);
+  d.dn_one = clampn(d.dn_one, c.D, 256);
   return d;
 }
 
@@ -625,8 +637,14 @@ int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *s
   MOE_TRY(check_device());
   Work w;
   carve(*cfg, S, W_SWIGLU, (char *)ws, &w);
-  PrepArgs pa{xq, cfg->D, w.xq, w.sumx, nullptr, 1};
-  MOE_TRY_HIP(launch_prep_xq(pa, S, stream));
+  // 16-byte aligned code rows are read as they are by the gate/up blocks
+  // (each reorders and sums its row); others are first copied in the
+  // permuted layout with their sums
+  const bool natural = aligned16(xq) && cfg->D % 16 == 0;
+  if (!natural) {
+    PrepArgs pa{xq, cfg->D, w.xq, w.sumx, nullptr, 1};
+    MOE_TRY_HIP(launch_prep_xq(pa, S, stream));
+  }
   const DecodeShape ds = decode_shape(*cfg);
   DecodeArgs d{};
   d.S = S;
@@ -640,16 +658,17 @@ int moe_expert_swiglu_i4(const moe_config *cfg, const int8_t *xq, const float *s
   d.fx = d.rt;
   d.fx_index = expert;
   d.fx_slot = 0;
-  d.xq = w.xq;
+  d.xq = natural ? xq : w.xq;
+  d.xq_natural = natural ? 1 : 0;
   d.sx = sx;
   d.sumx = w.sumx;
   d.h = w.h;
   d.ysh = y;
   d.n_router = 0;
   d.n_quant = 0;
-  d.n_gu_fx = ds.gu_fx;
+  d.n_gu_fx = ds.gu_one;
   d.n_gu_rt = 0;
-  d.n_dn_fx = ds.dn_fx;
+  d.n_dn_fx = ds.dn_one;
   d.acc_gu = acc_gu;
   d.acc_d = acc_d;
   d.hq_nat = hq;

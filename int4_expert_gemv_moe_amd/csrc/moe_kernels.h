@@ -65,6 +65,9 @@ struct DecodeArgs {
   const int8_t *xq;         // [S][D] permuted codes (phase B; also phase A single-expert calls)
   const float *sx;          // [S]
   const int32_t *sumx;      // [S]
+  // phase A single-expert calls: xq holds natural-order codes (16-byte
+  // aligned rows); the gate/up blocks permute them and form their sum
+  int xq_natural;
   float *logits;            // [S][E]
   int32_t *idx;             // [S][K]
   float *w;                 // [S][K]

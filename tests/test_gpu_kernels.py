@@ -115,9 +115,12 @@ def test_router_batch_invariance(S):
         assert torch.equal(lg1[0], lg_all[s])
 
 
-@pytest.mark.parametrize("shape,S", [(TINY, 4), (GLM, 1), (GLM, 3)])
-def test_expert_swiglu_parity(shape, S):
-    say(f"swiglu D={shape.D} I={shape.I} S={S}")
+# off: byte offset of the code rows; 16-byte aligned rows are read as they
+# are, others go through the layout copy first (same results)
+@pytest.mark.parametrize("shape,S,off", [(TINY, 4, 0), (TINY, 4, 8), (GLM, 1, 0), (GLM, 1, 8),
+                                         (GLM, 3, 0)])
+def test_expert_swiglu_parity(shape, S, off):
+    say(f"swiglu D={shape.D} I={shape.I} S={S} offset {off}")
     cfg = moe.config(shape.D, shape.I, shape.E, shape.K)
     e_id = 3
     he = host_expert(4, shape, 0, e_id)
@@ -127,8 +130,10 @@ def test_expert_swiglu_parity(shape, S):
     x = synth.activations(9, S, shape.D)
     xq, sx = oracle.quant_act_i8(x)
     ws = moe.Workspace(cfg, S, moe.WS_SWIGLU)
-    r = moe.moe_expert_swiglu_i4(cfg, torch.from_numpy(xq).cuda(), torch.from_numpy(sx).cuda(), dev,
-                                 e_id, ws, probes=True)
+    buf = torch.zeros(xq.size + 16, dtype=torch.int8, device="cuda")
+    xq_d = buf[off:off + xq.size].view(S, shape.D)
+    xq_d.copy_(torch.from_numpy(xq))
+    r = moe.moe_expert_swiglu_i4(cfg, xq_d, torch.from_numpy(sx).cuda(), dev, e_id, ws, probes=True)
     ref = oracle.expert_swiglu(config_of(shape), xq, sx, he)
     assert np.array_equal(to_np(r["acc_gu"]), ref["acc_gu"])
     hq = to_np(r["hq"])
