@@ -9,9 +9,12 @@
 // Work unit: a tile of up to 64 (batches of at most 64 tokens) or 80 (larger
 // batches) (token, slot) pairs of one expert group (the tile list is built by
 // group_kernel; a routed expert of a 2048-token prefill gets about 64 pairs,
-// so its weights are read once) times a chunk of output rows.  A workgroup
-// has 4 or 8 waves; each wave owns 8 NS gate rows and the 8 NS up rows with
-// the same indices (gate/up), or 16 NS down rows, for all pairs of the tile.
+// so its weights are read once) times a chunk of output rows.  Each wave
+// owns 8 NS gate rows and the 8 NS up rows with the same indices (gate/up),
+// or 16 NS down rows, for all pairs of the tile.  Two kernels: up to 64
+// tokens grouped_mfma_kernel (operands staged through registers, NS = 2),
+// larger batches grouped_mfma_dma_kernel (operands copied into shared
+// memory by DMA, NS = 4); both 4-wave workgroups.
 //
 // v_mfma_i32_16x16x64_i8 (layout checked on the device): lane l supplies row
 // l % 16 of A (a pair) and column l % 16 of B (an output row), each 16 int8
@@ -366,12 +369,303 @@ __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a
   }
 }
 
+// ---- large batches: operands staged by shared-memory DMA ----------------------
+//
+// The same tiles, waves and MFMA layout as grouped_mfma_kernel<MODE, 8, 4, ..>
+// (8 waves of 64 weight rows, tiles of up to 80 pairs), but the operands
+// travel from global memory straight into shared memory
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the instruction's
+// shared base + 16 lane), so no registers hold loads in flight and two steps
+// of 128 columns are requested ahead through three-stage rings: weights in a
+// ring per wave (only that wave reads them), activations in one ring per
+// workgroup.  A step waits for its own loads (the next step's stay in
+// flight), passes the workgroup barrier, requests the step after next into
+// the buffer every wave finished with, and multiplies.
+//
+// Layouts (16-byte pieces XOR-swizzled by row, so the MFMA-layout reads of
+// 16 lanes hit 16 distinct bank groups):
+//   weights: a wave's stage is 64 rows x 64 bytes; piece q of row R holds
+//            logical piece q ^ ((R >> 2) & 3);
+//   activations: 16 MSV rows x 128 bytes; piece q of row R holds logical
+//            piece q ^ ((R >> 1) & 7).
+// Lane group j of an MFMA covers columns 32 j + 16 c .. +16 of the step
+// (c = the step's two MFMAs): one 16-byte weight piece feeds both, the
+// activation pieces are logical 2 j + c.
+constexpr int kSmallMsv = 4, kLargeMsv = 5;
+// Larger batches: the shared-memory DMA kernel in 4-wave workgroups, two
+// per CU (measured against one 8-wave workgroup per CU and against the
+// register-staged grouped_mfma_kernel<.., 8, 4, 5>: the same gate/up time,
+// down 486 against 545 and 567 us at 2048 tokens), with whole tiles per XCD.
+constexpr int kPrefillDmaWaves = 4;
+constexpr bool kDmaXcdTiles = true;
+
+
+constexpr int kDKS = 128;                    // columns per step
+constexpr int kDNS = 4;                      // 16-row weight subtiles per wave
+constexpr int kDBWave = 16 * kDNS * kDKS / 2;  // weight bytes of a wave's stage (4 KB)
+constexpr int kDARow = kDKS;                 // activation bytes of a pair row per step
+
+typedef __attribute__((address_space(3))) void lds_t;
+
+// 16 bytes per lane from global memory into shared memory at base + 16 lane.
+__device__ __forceinline__ void dma16(const void *g, int8_t *base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_t *)base, 16, 0, 0);
+}
+
+// Activation pieces per wave and step: the 2 MSVMAX instructions of a stage
+// spread over the NW waves, every wave issuing the same count (an
+// instruction number past the last repeats an earlier one, same data into
+// the same place), so one wait count fits every wave.
+template <int NW, int MSVMAX>
+constexpr int dma_a_per_wave() { return (2 * MSVMAX + NW - 1) / NW; }
+
+// Wait until at most N of this wave's vector-memory operations are in
+// flight.  s_waitcnt fields: vmcnt bits 3:0, expcnt 6:4 and lgkmcnt 11:8
+// (expcnt at its maximum; lgkmcnt at its maximum, or 0 with LDS0: every
+// shared-memory read of the wave has returned).
+template <int N, bool LDS0 = false>
+__device__ __forceinline__ void wait_vm_at_most() {
+  static_assert(N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((LDS0 ? 0x0070 : 0x0F70) | N);
+}
+
+// The workgroup barrier of a step: this wave's pieces of the step are in
+// (the next step's may stay in flight) and its shared-memory reads of the
+// previous step have returned; then every wave's are.  The compiler may
+// move no memory access across it (the empty asm) and the scheduler no
+// instruction (sched_barrier); no fence, which would wait for the requests
+// in flight as well.
+template <int PIECES>
+__device__ __forceinline__ void dma_step_barrier() {
+  asm volatile("" ::: "memory");
+  wait_vm_at_most<PIECES, true>();
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// The three stages are separate shared arrays (A0..A2, B0..B2), so the
+// compiler can tell a step's reads from the requests in flight into the
+// other stages and does not wait for those.
+template <int MODE, int NW, int MSVMAX, int MSV, int ABUF>
+__device__ __forceinline__ void dma_tile(const GroupedMfmaArgs &a, const MfmaTile &t,
+                                         int8_t *A0, int8_t *A1, int8_t *A2, int8_t *B0,
+                                         int8_t *B1, int8_t *B2, const int *pr_l,
+                                         const int *sum_l, const float *scl_l) {
+  constexpr int NS = kDNS;
+  constexpr int NA = 2 * MSV;  // activation DMA instructions of a stage (8 rows x 128 bytes each)
+  constexpr int AW = dma_a_per_wave<NW, MSVMAX>();
+  constexpr int PIECES = NS + AW;  // requests per wave and step
+  const int C = a.C, O = a.O;
+  const int lane = t.lane, j = t.j, rows = t.rows, wave = t.wave;
+  const int ln = lane & 15;
+  const int rowbytes = C >> 1;
+  // weights: instruction i of a step is subtile i: row lane / 4 of it,
+  // shared piece lane % 4 = logical piece (lane % 4) ^ (lane / 16)
+  const uint8_t *bsrc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; i++) {
+    const int o = t.ob[i] - ln + (lane >> 2);  // first row of subtile i + lane / 4
+    const int p = (lane & 3) ^ (lane >> 4);
+    bsrc[i] = t.bbase[i] + (int64_t)min(o, O - 1) * rowbytes + 16 * p;
+  }
+  // activations: instruction n = wave + NW u: pair row 8 n + lane / 8, shared
+  // piece lane % 8 = logical piece (lane % 8) ^ ((row >> 1) & 7)
+  int asrc[AW], adst[AW];
+#pragma unroll
+  for (int u = 0; u < AW; u++) {
+    const int n = (wave + NW * u) % NA;
+    const int r = 8 * n + (lane >> 3);
+    const int apr = pr_l[min(r, rows - 1)];
+    const int p = (lane & 7) ^ ((r >> 1) & 7);
+    asrc[u] = (MODE == 0 ? apr / a.P : apr) * C + 16 * p;
+    adst[u] = 1024 * n;
+  }
+  const int nsteps = C / kDKS;
+  auto stage_a = [&](auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    return B == 0 ? A0 : (B == 1 ? A1 : A2);
+  };
+  auto stage_b = [&](auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    return (B == 0 ? B0 : (B == 1 ? B1 : B2)) + wave * kDBWave;
+  };
+  auto issue = [&](int st, auto bc) __attribute__((always_inline)) {
+    const int k0 = min(st, nsteps - 1) * kDKS;
+    int8_t *bd = stage_b(bc);
+#pragma unroll
+    for (int i = 0; i < NS; i++) dma16(bsrc[i] + k0 / 2, bd + 1024 * i);
+    int8_t *ad = stage_a(bc);
+#pragma unroll
+    for (int u = 0; u < AW; u++) dma16(a.act + asrc[u] + k0, ad + adst[u]);
+  };
+  v4i acc[MSV][NS];
+#pragma unroll
+  for (int ms = 0; ms < MSV; ms++)
+#pragma unroll
+    for (int s = 0; s < NS; s++) acc[ms][s] = v4i{0, 0, 0, 0};
+  float sc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; s++) sc[s] = t.Bm[s].s[min(t.ob[s], O - 1)];
+  // shared offsets of the lane's MFMA-layout reads within a stage
+  const int boff = ln * 64 + 16 * (j ^ ((ln >> 2) & 3));  // + subtile * 1024
+  int aoff[2];
+#pragma unroll
+  for (int c = 0; c < 2; c++) aoff[c] = ln * kDARow + 16 * ((2 * j + c) ^ ((ln >> 1) & 7));
+
+  issue(0, std::integral_constant<int, 0>{});
+  issue(1, std::integral_constant<int, 1>{});
+  auto step = [&](int st, auto bc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bc)::value;
+    // after the barrier every wave's pieces of the step are in, and every
+    // wave is done with the stage of step st - 1, which the request below
+    // refills
+    dma_step_barrier<PIECES>();
+    issue(st + 2, std::integral_constant<int, (BUF + 2) % 3>{});
+    const int8_t *bw = stage_b(bc) + boff;
+    const int8_t *aw = stage_a(bc);
+    uint4 bm[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++) bm[s] = *reinterpret_cast<const uint4 *>(bw + 1024 * s);
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      v4i aa[MSV];
+#pragma unroll
+      for (int ms = 0; ms < MSV; ms++) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(aw + ms * 16 * kDARow + aoff[c]);
+        aa[ms] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+      }
+      v4i bb[NS];
+#pragma unroll
+      for (int s = 0; s < NS; s++) bb[s] = c ? unpack16(bm[s].z, bm[s].w) : unpack16(bm[s].x, bm[s].y);
+#pragma unroll
+      for (int ms = 0; ms < MSV; ms++)
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+          acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[s], acc[ms][s], 0, 0, 0);
+    }
+  };
+  int st = 0;
+  for (; st + 2 < nsteps; st += 3) {
+    step(st, std::integral_constant<int, 0>{});
+    step(st + 1, std::integral_constant<int, 1>{});
+    step(st + 2, std::integral_constant<int, 2>{});
+  }
+  if (st < nsteps) step(st, std::integral_constant<int, 0>{});
+  if (st + 1 < nsteps) step(st + 1, std::integral_constant<int, 1>{});
+  // the last requests (repeats of the last step) land in stages no step
+  // reads; none may still be in flight when the workgroup ends
+  wait_vm_at_most<0>();
+
+  // epilogue as in mfma_tile
+#pragma unroll
+  for (int ms = 0; ms < MSV; ms++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 16 * ms + 4 * j + i;
+      if (r < rows) {
+        const int pr = pr_l[r];
+        const int corr = 8 * sum_l[r];
+        const float as = scl_l[r];
+        if (MODE == 0) {
+#pragma unroll
+          for (int s = 0; s < NS / 2; s++) {
+            const int o = t.ob[s];
+            if (o < O) {
+              const float gv = ((float)(acc[ms][s][i] - corr) * sc[s]) * as;
+              const float uv = ((float)(acc[ms][s + NS / 2][i] - corr) * sc[s + NS / 2]) * as;
+              a.out[(int64_t)pr * O + o] = silu(gv) * uv;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < NS; s++) {
+            const int o = t.ob[s];
+            if (o < O) a.out[(int64_t)pr * O + o] = ((float)(acc[ms][s][i] - corr) * sc[s]) * as;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Two waves per SIMD: two 4-wave workgroups (80 KB of shared memory each)
+// or one 8-wave workgroup per CU, at most 256 registers per wave.
+template <int MODE, int NW, int MSVMAX>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void grouped_mfma_dma_kernel(GroupedMfmaArgs a) {
+  constexpr int NS = kDNS;
+  constexpr int ABUF = 16 * MSVMAX * kDARow;
+  __shared__ __align__(1024) int8_t B0[NW * kDBWave], B1[NW * kDBWave], B2[NW * kDBWave];
+  __shared__ __align__(1024) int8_t A0[ABUF], A1[ABUF], A2[ABUF];
+  __shared__ int pr_l[16 * MSVMAX];
+  __shared__ int sum_l[16 * MSVMAX];
+  __shared__ float scl_l[16 * MSVMAX];
+  // kDmaXcdTiles: a one-dimensional grid in which workgroup i reaches XCD
+  // i % 8 (round-robin dispatch) and every XCD takes whole tiles, all row
+  // chunks of one tile back to back, so a tile's activation rows are fetched
+  // into one XCD's L2 once; otherwise blockIdx = (row chunk, tile)
+  int tile, chunk;
+  if (kDmaXcdTiles) {
+    const int nx = (a.O + mfma_block_rows<MODE, NW, NS>() - 1) / mfma_block_rows<MODE, NW, NS>();
+    const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
+    tile = (k / nx) * 8 + xcd;
+    chunk = k % nx;
+  } else {
+    tile = blockIdx.y;
+    chunk = blockIdx.x;
+  }
+  if (tile >= *a.ntiles) return;
+  const int2 tg = a.tiles[tile];
+  const int g = tg.x, m0 = tg.y;
+  MfmaTile t;
+  t.rows = min(16 * MSVMAX, a.gcount[g] - m0);
+  t.lane = threadIdx.x & 63;
+  t.wave = threadIdx.x >> 6;
+  t.j = t.lane >> 4;
+  const bool shared = (g == a.E);
+  const int e = shared ? 0 : g;
+  const int o_blk = chunk * mfma_block_rows<MODE, NW, NS>();
+  const RowPtr G = MODE == 0 ? pick(a.rt.gate, a.sh.gate, shared, e) : pick(a.rt.down, a.sh.down, shared, e);
+  const RowPtr U = MODE == 0 ? pick(a.rt.up, a.sh.up, shared, e) : G;
+  auto sub_row = [&](int s, int r) {
+    return MODE == 0 ? o_blk + 8 * NS * t.wave + 16 * (s % (NS / 2)) + r
+                     : o_blk + 16 * NS * t.wave + 16 * s + r;
+  };
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    t.Bm[s] = (MODE == 0 && s >= NS / 2) ? U : G;
+    t.ob[s] = sub_row(s, t.lane & 15);
+    t.bbase[s] = t.Bm[s].q;
+  }
+  const int *plist = a.pairs + a.goff[g] + m0;
+  for (int i = threadIdx.x; i < 16 * MSVMAX; i += NW * 64) {
+    const int pr = plist[min(i, t.rows - 1)];
+    const int ar = MODE == 0 ? pr / a.P : pr;
+    pr_l[i] = pr;
+    sum_l[i] = a.asum[ar];
+    scl_l[i] = a.ascale[ar];
+  }
+  __syncthreads();
+#define MOE_DMA_TILE(M) \
+  dma_tile<MODE, NW, MSVMAX, M, ABUF>(a, t, A0, A1, A2, B0, B1, B2, pr_l, sum_l, scl_l)
+  switch ((t.rows + 15) >> 4) {
+    case 1: MOE_DMA_TILE(1); break;
+    case 2: MOE_DMA_TILE(cmin(2, MSVMAX)); break;
+    case 3: MOE_DMA_TILE(cmin(3, MSVMAX)); break;
+    case 4: MOE_DMA_TILE(cmin(4, MSVMAX)); break;
+    default: MOE_DMA_TILE(MSVMAX); break;
+  }
+#undef MOE_DMA_TILE
+}
+
 bool grouped_mfma_fits(int C) { return C % kKS == 0; }
 
 // Subtiles (16 pairs each) of the two launch shapes: batches of up to 64
 // tokens run 4-wave workgroups holding at most 4 subtiles, larger batches
 // 8-wave workgroups holding at most 5.
-constexpr int kSmallMsv = 4, kLargeMsv = 5;
+
 
 // Pairs per tile: as many as the launch's workgroups hold.  A group larger
 // than that (a routed expert with more pairs, or the shared expert) is cut
@@ -394,8 +688,8 @@ static void launch_mode(const GroupedMfmaArgs &a, int max_tiles, hipStream_t st)
 
 // Batches of up to 64 tokens (at most 4 subtiles per tile): 4-wave
 // workgroups of 32 B rows per wave, so that a few experts still spread over
-// many workgroups; larger batches: 8-wave workgroups of 64 B rows per wave,
-// which halves the shared-memory reads of activations per weight byte.
+// many workgroups (the DMA kernel took the 64-token verify from 532 to 632
+// us); larger batches: grouped_mfma_dma_kernel, 64 B rows per wave.
 hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, int S,
                                hipStream_t st) {
   if (S <= 64) {
@@ -404,10 +698,14 @@ hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles
     else
       launch_mode<1, 4, 2, kSmallMsv>(a, max_tiles, st);
   } else {
+    constexpr int NW = kPrefillDmaWaves;
+    const int rpb = mode == 0 ? mfma_block_rows<0, NW, kDNS>() : mfma_block_rows<1, NW, kDNS>();
+    const int nx = (a.O + rpb - 1) / rpb;
+    const dim3 grid = kDmaXcdTiles ? dim3(nx * ((max_tiles + 7) / 8) * 8) : dim3(nx, max_tiles);
     if (mode == 0)
-      launch_mode<0, 8, 4, kLargeMsv>(a, max_tiles, st);
+      hipLaunchKernelGGL((grouped_mfma_dma_kernel<0, NW, kLargeMsv>), grid, dim3(NW * 64), 0, st, a);
     else
-      launch_mode<1, 8, 4, kLargeMsv>(a, max_tiles, st);
+      hipLaunchKernelGGL((grouped_mfma_dma_kernel<1, NW, kLargeMsv>), grid, dim3(NW * 64), 0, st, a);
   }
   return hipGetLastError();
 }
