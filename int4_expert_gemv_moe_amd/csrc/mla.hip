@@ -446,12 +446,13 @@ __global__ __launch_bounds__(256) void mla_attn_mfma_kernel(MlaArgs a) {
 
 // Workgroup (s, h, cp) merges the chunks of (s, h) for latent columns
 // [kvl cp / P, kvl (cp + 1) / P) (P = kMlaMergeParts): weights e^(m_k - m),
-// normalized by the merged exp sum.  Wave 0 forms the weights; the threads
-// split the chunks into 256 / ncols slices per column (so each issues a few
-// loads, not nsplit), and the slices are added in a fixed order.
+// normalized by the merged exp sum.  Wave 0 forms the weights; thread t
+// takes four columns (16-byte loads) and every nsl-th chunk from slice t /
+// (columns / 4), its loads issued together (8 at a time), and the slices are
+// added in a fixed order.
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   __shared__ float wk[kMlaMaxSplit];
-  __shared__ float part[256];
+  __shared__ float4 part[256];
   __shared__ float inv_l;
   const int tid = threadIdx.x, lane = tid & 63;
   const int sh = blockIdx.x / kMlaMergeParts, cp = blockIdx.x % kMlaMergeParts;
@@ -472,19 +473,46 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   }
   __syncthreads();
   const int c0 = a.kvl * cp / kMlaMergeParts, c1 = a.kvl * (cp + 1) / kMlaMergeParts;
-  const int ncols = c1 - c0;              // kvl / P: 8 .. 256 (kvl % 64 == 0)
-  const int nsl = 256 / ncols;            // chunk slices per column
-  const int c = tid % ncols, sl = tid / ncols;
-  const float *pc = a.pclat + (int64_t)sh * a.nsplit * a.kvl + c0 + c;
-  float acc = 0.f;
-  if (sl < nsl)
-    for (int k = sl; k < a.nsplit; k += nsl) acc = fmaf(wk[k], pc[(int64_t)k * a.kvl], acc);
+  const int nq = (c1 - c0) / 4;           // column quads: 2 .. 64 (kvl % 64 == 0)
+  const int nsl = 256 / nq;               // chunk slices
+  const int q = tid % nq, sl = tid / nq;
+  const float *pc = a.pclat + (int64_t)sh * a.nsplit * a.kvl + c0 + 4 * q;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (sl < nsl) {
+    constexpr int U = 8;
+    for (int k0 = sl; k0 < a.nsplit; k0 += U * nsl) {
+      float4 v[U];
+      float w[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int k = k0 + u * nsl;
+        const bool ok = k < a.nsplit;
+        v[u] = *reinterpret_cast<const float4 *>(pc + (int64_t)(ok ? k : k0) * a.kvl);
+        w[u] = ok ? wk[k] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        acc.x = fmaf(w[u], v[u].x, acc.x);
+        acc.y = fmaf(w[u], v[u].y, acc.y);
+        acc.z = fmaf(w[u], v[u].z, acc.z);
+        acc.w = fmaf(w[u], v[u].w, acc.w);
+      }
+    }
+  }
   part[tid] = acc;
   __syncthreads();
-  if (tid < ncols) {
-    float v = part[tid];
-    for (int q = 1; q < nsl; q++) v += part[q * ncols + tid];
-    a.clat[(int64_t)sh * a.kvl + c0 + tid] = v * inv_l;
+  if (tid < nq) {
+    float4 v = part[tid];
+    for (int k = 1; k < nsl; k++) {
+      const float4 u = part[k * nq + tid];
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    const float il = inv_l;
+    reinterpret_cast<float4 *>(a.clat + (int64_t)sh * a.kvl + c0)[tid] =
+        make_float4(v.x * il, v.y * il, v.z * il, v.w * il);
   }
 }
 
