@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(MlaArgs a) {
   const int nph = 256 / tpr;            // row phases (8 .. 128)
   const int c4 = threadIdx.x % tpr, ph = threadIdx.x / tpr;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int U = 8;  // rows per batch of loads in flight
+  constexpr int U = 12;  // rows per batch of loads in flight (a GLM head: 192 / 16 phases)
   for (int d0 = ph; d0 < a.nope; d0 += U * nph) {
     float4 w[U];
     float qd[U];
@@ -561,6 +561,58 @@ __global__ __launch_bounds__(256) void mla_value_kernel(MlaArgs a) {
   }
 }
 
+// kvl % 256 == 0: lane l holds latent columns 4l + 256c .. +4 (c < NJ4) of a
+// row as 16-byte loads, and a wave requests all of its up to 8 value rows of
+// the part at once before any product.
+template <int NJ4>
+__global__ __launch_bounds__(256) void mla_value4_kernel(MlaArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sh = blockIdx.x / kMlaValueParts, vb = blockIdx.x % kMlaValueParts;
+  const int h = sh % a.H;
+  const float *wv = a.kv_b + ((int64_t)h * (a.nope + a.vdim) + a.nope) * a.kvl;
+  const int v0 = a.vdim * vb / kMlaValueParts, v1 = a.vdim * (vb + 1) / kMlaValueParts;
+  const float4 *cl4 = reinterpret_cast<const float4 *>(a.clat + (int64_t)sh * a.kvl);
+  float4 cl[NJ4];
+#pragma unroll
+  for (int c = 0; c < NJ4; c++) cl[c] = cl4[lane + 64 * c];
+  constexpr int RW = 8;  // rows per wave in flight
+  for (int vg = v0 + RW * wave; vg < v1; vg += 4 * RW) {
+    float4 w[RW][NJ4];
+#pragma unroll
+    for (int r = 0; r < RW; r++) {
+      const float4 *row = reinterpret_cast<const float4 *>(wv + (int64_t)min(vg + r, v1 - 1) * a.kvl);
+#pragma unroll
+      for (int c = 0; c < NJ4; c++) w[r][c] = row[lane + 64 * c];
+    }
+#pragma unroll
+    for (int r = 0; r < RW; r++) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < NJ4; c++) {
+        acc = fmaf(w[r][c].x, cl[c].x, acc);
+        acc = fmaf(w[r][c].y, cl[c].y, acc);
+        acc = fmaf(w[r][c].z, cl[c].z, acc);
+        acc = fmaf(w[r][c].w, cl[c].w, acc);
+      }
+      const float v = wave_sum_f32(acc);
+      if (lane == 0 && vg + r < v1) a.ctx[(int64_t)sh * a.vdim + vg + r] = v;
+    }
+  }
+}
+
+// The value projection: 16-byte loads when the latent width allows them
+// (kv_b rows then start 16-byte aligned: kv_b itself is checked on the host).
+static void launch_mla_value(const MlaArgs &a, hipStream_t st) {
+  const dim3 grid(a.S * a.H * kMlaValueParts);
+  switch (a.kvl % 256 == 0 ? a.kvl / 256 : 0) {
+    case 1: hipLaunchKernelGGL((mla_value4_kernel<1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((mla_value4_kernel<2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((mla_value4_kernel<3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((mla_value4_kernel<4>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(mla_value_kernel, grid, dim3(256), 0, st, a); break;
+  }
+}
+
 hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st) {
   const int sh = a.S * a.H;
   hipLaunchKernelGGL(mla_absorb_kernel, dim3(sh * kMlaAbsorbParts), dim3(256), 0, st, a);
@@ -568,7 +620,7 @@ hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st) {
     const int groups = (a.H + kMlaMH - 1) / kMlaMH;
     hipLaunchKernelGGL(mla_attn_mfma_kernel, dim3(a.S * groups * a.nsplit), dim3(256), 0, st, a);
     hipLaunchKernelGGL(mla_merge_kernel, dim3(sh * kMlaMergeParts), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(mla_value_kernel, dim3(sh * kMlaValueParts), dim3(256), 0, st, a);
+    launch_mla_value(a, st);
     return hipGetLastError();
   }
   const int ngroups = (a.H + kMlaHeads - 1) / kMlaHeads;
@@ -579,7 +631,7 @@ hipError_t launch_mla_decode(const MlaArgs &a, hipStream_t st) {
   else if (nj <= 8) hipLaunchKernelGGL((mla_chunk_kernel<8>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((mla_chunk_kernel<kMlaMaxJ>), grid, dim3(256), 0, st, a);
   hipLaunchKernelGGL(mla_merge_kernel, dim3(sh * kMlaMergeParts), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(mla_value_kernel, dim3(sh * kMlaValueParts), dim3(256), 0, st, a);
+  launch_mla_value(a, st);
   return hipGetLastError();
 }
 
