@@ -42,4 +42,16 @@ __device__ __forceinline__ void dma_step_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// A workgroup barrier after this wave's shared-memory accesses have
+// completed, leaving its global-to-shared requests in flight (vmcnt at its
+// maximum: bits 3:0 and 15:14 all set).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace moe

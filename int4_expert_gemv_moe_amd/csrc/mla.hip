@@ -7,8 +7,8 @@
 // Four launches, split over the cache like flash decoding:
 //   1. absorb: qabs[s][h] = W_UK[h]^T q_nope[s][h] (eight workgroups per
 //      query and head, each an eighth of the key rows; 16-byte loads);
-//   2. splits: workgroup (s, 32 heads, k) walks cache rows [k R, (k + 1) R)
-//      of the query's window 32 rows at a time and forms, per head, the
+//   2. splits: workgroup (s, 16 heads, k) walks cache rows [k R, (k + 1) R)
+//      of the query's window 16 rows at a time and forms, per head, the
 //      split's max m_k, exp sum l_k and latent sum sum_t e^(score_t - m_k) L[t]
 //      (online softmax), both products on fp32 matrix cores
 //      (mla_attn_mfma_kernel, latent + rotary width up to 576); wider latents
@@ -22,6 +22,7 @@
 #include <algorithm>
 
 #include "moe_kernels.h"
+#include "dma.h"
 
 namespace moe {
 
@@ -197,30 +198,40 @@ __global__ __launch_bounds__(256) void mla_chunk_kernel(MlaArgs a) {
 
 // ---- attention on fp32 matrix cores ----------------------------------------------
 //
-// v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][k] and B[k][l % 16] for
-// its k-group l / 16 and receives C[4 (l / 16) + i][l % 16], i = 0..3.  The
-// contraction index is permuted consistently for A and B: MFMA number s
-// (0..3) of a 16-column block q takes column 16 q + 4 (l / 16) + s, so one
-// 16-byte shared-memory read gives a lane its operands of four MFMAs.
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
+// and receives C[4 (l / 16) + i][l % 16], i = 0..3.  The contraction index is
+// permuted consistently for A and B: MFMA number s (0..3) of a 16-column block q
+// takes column 16 q + 4 (l / 16) + s, so one 16-byte read gives a lane its
+// operands of four MFMAs.
 //
-// Per 32-row step of a workgroup (32 heads, four waves):
-//   scores  S[row][head] = L_row . qabs_head + R_row . qrope_head: wave w
-//           takes rows 16 (w % 2) .., heads 16 (w / 2) .. (one 16x16 tile,
-//           Kp / 4 MFMAs);
-//   softmax per head over the step's rows, folded into the running max and
-//           exp sum (the running latent sums are rescaled by e^(m_old - m_new));
+// A workgroup (four waves) takes 16 heads of one query and one split of its
+// window, 16 cache rows per step; two workgroups share a CU (77 KB of shared
+// memory, about 110 registers per lane).  Per step:
+//   rows    the step's 16 cache rows (latent and rotary columns) arrive in a
+//           shared-memory stage by DMA (global_load_lds_dwordx4; two stages,
+//           the next step's rows requested while this one computes);
+//   scores  S[row][head] = L_row . qabs_head + R_row . qrope_head, one 16 x 16
+//           tile: wave w takes a quarter of the columns, its queries held in
+//           registers for the whole split; the four partial tiles meet in
+//           shared memory and every wave adds them in the same order;
+//   softmax every wave forms the same running max, exp sum and weights
+//           (online softmax; the latent sums are rescaled by e^(m_old - m_new)),
+//           the weights staying in the registers that the next products read;
 //   latent  clat[head][col] += sum_row p[head][row] L[row][col]: wave w takes
-//           columns w kvl / 4 .., both 16-head tiles (kvl / 64 column tiles).
-// The step's cache rows (latent and rotary columns, row stride kMlaMS floats,
-// 4 banks apart so the 16 lanes of a read hit distinct banks) are read from
-// global memory once per workgroup; the next step's rows are loaded into
-// registers while the step computes.
-constexpr int kMlaMH = 32;               // heads per workgroup
-constexpr int kMlaMR = 32;               // cache rows per step
+//           columns w kvl / 4 .. (kvl / 64 tiles of 16).
+// Stage layout: row r of a stage is 145 pieces of 16 bytes (latent, rotary,
+// padding to 576 columns, one spare piece), so the 16 lanes of a score read,
+// one row each, hit 16 distinct bank groups and the 64 lanes of a latent-sum
+// read 64 distinct banks.
+constexpr int kMlaMH = 16;               // heads per workgroup
+constexpr int kMlaMR = 16;               // cache rows per step
 constexpr int kMlaMK = 576;              // latent + rotary (rounded up to 16) columns at most
-constexpr int kMlaMS = kMlaMK + 4;       // shared row stride (floats)
-constexpr int kMlaPS = kMlaMR + 4;       // softmax-weight row stride (floats)
-constexpr int kMlaLoads = kMlaMR * kMlaMK / 4 / 256;  // 16-byte row loads per thread per step
+constexpr int kMlaRowP = kMlaMK / 4 + 1; // 16-byte pieces per shared row (144 + 1 of padding)
+constexpr int kMlaRowB = 16 * kMlaRowP;  // 2320 bytes
+constexpr int kMlaDmaN = (kMlaMR * kMlaRowP + 63) / 64;  // DMA requests of a stage (37)
+constexpr int kMlaStage = 1024 * kMlaDmaN;               // 37 KB
+constexpr int kMlaDma = (kMlaDmaN + 3) / 4;  // at most per wave and step (10)
+constexpr int kMlaQB = kMlaMK / 16 / 4;  // 16-column blocks of a wave's score quarter (9)
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -234,213 +245,181 @@ bool mla_mfma_fits(int kvl, int rope, const float *L, const float *R) {
   return al && rope % 4 == 0 && kvl + (rope + 15) / 16 * 16 <= kMlaMK;
 }
 
+// Splits per query: 16-row steps, up to 128 splits, about 512 workgroups.
 int mla_mfma_splits(int S, int T, int H) {
   const int groups = (H + kMlaMH - 1) / kMlaMH;
-  const int target = std::max(1, 256 / std::max(1, S * groups));
+  const int target = std::max(1, 512 / std::max(1, S * groups));
   return std::max(1, std::min(std::min(kMlaMaxSplit, (T + kMlaMR - 1) / kMlaMR), target));
 }
 
-__global__ __launch_bounds__(256) void mla_attn_mfma_kernel(MlaArgs a) {
-  __shared__ __align__(16) float qs[kMlaMH * kMlaMS];  // [head][column]
-  __shared__ __align__(16) float ls[kMlaMR * kMlaMS];  // [row][column]
-  __shared__ __align__(16) float ps[kMlaMH * kMlaPS];  // [head][row]
-  __shared__ float cmax[2][kMlaMH], csum[2][kMlaMH];
-  __shared__ float mrun[kMlaMH], lrun[kMlaMH], mnew[kMlaMH], alpha[kMlaMH];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void mla_attn_mfma_kernel(MlaArgs a) {
+  __shared__ __align__(1024) int8_t st0[kMlaStage], st1[kMlaStage];
+  __shared__ __align__(16) float4 part[4][64];  // the waves' partial score tiles
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int groups = (a.H + kMlaMH - 1) / kMlaMH;
   const int k = blockIdx.x % a.nsplit;
   const int sg = blockIdx.x / a.nsplit;
   const int s = sg / groups, h0 = (sg % groups) * kMlaMH;
-  const int kp = a.kvl + (a.rope + 15) / 16 * 16;  // contraction columns
-  const int c4n = kp / 4, kv4 = a.kvl / 4, ro4 = a.rope / 4;
-  const int n = a.T - a.S + 1 + s;                  // visible rows of query s
+  const int kv4 = a.kvl / 4, ro4 = a.rope / 4;
+  const int n = a.T - a.S + 1 + s;                 // visible rows of query s
   const int per = (a.T + a.nsplit - 1) / a.nsplit;
   const int rows = (per + kMlaMR - 1) / kMlaMR * kMlaMR;
   const int r0 = k * rows, r1 = min(n, r0 + rows);
   const int steps = r1 > r0 ? (r1 - r0 + kMlaMR - 1) / kMlaMR : 0;
 
-  // the absorbed queries, the same pieces as a step's rows (head for row),
-  // every load unconditional (a piece outside the queries reads qabs[0] and
-  // is replaced by zeros); then the rotary queries (4-byte aligned, scalar
-  // loads) and zeros in the padding columns
-  {
-    const float *qbase = a.qabs;
-    float4 qv[kMlaLoads];
+  // the wave's quarter of the queries: blocks q = kQB wave .. (columns 16 q +
+  // 4 lg + 0..3 of head h0 + ln), zero past the head count and the columns
+  const int h = h0 + ln;
+  const int64_t shq = (int64_t)s * a.H + min(h, a.H - 1);
+  float4 qv[kMlaQB];
 #pragma unroll
-    for (int i = 0; i < kMlaLoads; i++) {
-      const int f = tid + 256 * i;
-      const int hb = f / c4n, c4 = f - hb * c4n, h = h0 + hb;
-      const bool ok = hb < kMlaMH && h < a.H && c4 < kv4;
-      const float *src = ok ? a.qabs + ((int64_t)s * a.H + h) * a.kvl + 4 * c4 : qbase;
-      const float4 v = *reinterpret_cast<const float4 *>(src);
-      qv[i] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int b = 0; b < kMlaQB; b++) {
+    const int c = 16 * (kMlaQB * wave + b) + 4 * lg;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (h < a.H) {
+      if (c < a.kvl) {
+        v = *reinterpret_cast<const float4 *>(a.qabs + shq * a.kvl + c);
+      } else if (c < a.kvl + a.rope) {
+        const float *qr = a.q + shq * (a.nope + a.rope) + a.nope + (c - a.kvl);
+        v = make_float4(qr[0], qr[1], qr[2], qr[3]);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < kMlaLoads; i++) {
-      const int f = tid + 256 * i;
-      const int hb = f / c4n, c4 = f - hb * c4n;
-      if (hb < kMlaMH) *reinterpret_cast<float4 *>(qs + hb * kMlaMS + 4 * c4) = qv[i];
-    }
-    __syncthreads();
-    const int pad = kp - a.kvl;  // rotary columns and their padding
-    for (int i = tid; i < kMlaMH * pad; i += 256) {
-      const int hb = i / pad, d = i - hb * pad, h = h0 + hb;
-      float v = 0.f;
-      if (h < a.H && d < a.rope) v = a.q[((int64_t)s * a.H + h) * (a.nope + a.rope) + a.nope + d];
-      qs[hb * kMlaMS + a.kvl + d] = v;
-    }
+    qv[b] = v;
   }
-  if (tid < kMlaMH) {
-    mrun[tid] = -INFINITY;
-    lrun[tid] = 0.f;
-  }
-  // the rows of a step into registers: load i of thread t is 16-byte piece
-  // f = t + 256 i of the step, row f / c4n, column piece f % c4n
-  float4 pre[kMlaLoads];
-  // every load unconditional: pieces past the step's rows or the row's
-  // columns read L[0] and are replaced by zeros
-  auto load_rows = [&](int t0) {
+
+  // DMA request n = 4 u + wave of a stage (n < kMlaDmaN): slot g = 64 n +
+  // lane, row g / 145, piece g % 145 (pieces past the row's columns, the
+  // spare piece and the slots past the last row copy the row's first latent
+  // piece: a finite value that no product uses)
+  int roff[kMlaDma];   // byte offset of the piece within its row
+  int rrow[kMlaDma];   // row of the step
+  bool rrot[kMlaDma];  // rotary piece (R) rather than latent (L)
 #pragma unroll
-    for (int i = 0; i < kMlaLoads; i++) {
-      const int f = tid + 256 * i;
-      const int r = f / c4n, c4 = f - r * c4n;
-      const int t = t0 + r;
-      const bool ok = r < kMlaMR && t < r1 && c4 < kv4 + ro4;
-      const float *src = c4 < kv4 ? a.L + (int64_t)t * a.kvl + 4 * c4
-                                  : a.R + (int64_t)t * a.rope + 4 * (c4 - kv4);
-      const float4 v = *reinterpret_cast<const float4 *>(ok ? src : a.L);
-      pre[i] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int u = 0; u < kMlaDma; u++) {
+    const int g = 64 * (4 * u + wave) + lane;
+    const int r = g / kMlaRowP, lp = g % kMlaRowP;
+    rrow[u] = min(r, kMlaMR - 1);
+    rrot[u] = r < kMlaMR && lp >= kv4 && lp < kv4 + ro4;
+    roff[u] = r < kMlaMR && lp < kv4 ? 16 * lp : (rrot[u] ? 16 * (lp - kv4) : 0);
+  }
+  auto issue = [&](int st, int8_t *dst) __attribute__((always_inline)) {
+    // rows past the split's window repeat its last row (their weights are 0)
+    const int tb = r0 + st * kMlaMR;
+#pragma unroll
+    for (int u = 0; u < kMlaDma; u++) {
+      if (4 * u + wave < kMlaDmaN) {  // uniform across the wave
+        const int64_t t = max(min(tb + rrow[u], r1 - 1), 0);
+        const float *row = rrot[u] ? a.R + t * a.rope : a.L + t * a.kvl;
+        dma16(reinterpret_cast<const int8_t *>(row) + roff[u], dst + 1024 * (4 * u + wave));
+      }
     }
   };
-  v4f acc[2][8];  // running latent sums: head tile, column tile
+
+  v4f acc[8];  // latent sums: heads 4 lg + i, columns cw0 + 16 ct + ln
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-    for (int ct = 0; ct < 8; ct++) acc[mt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int nct = a.kvl / 64;            // column tiles per wave (kvl / 4 columns)
+  for (int ct = 0; ct < 8; ct++) acc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;  // of head h0 + ln (every lane group alike)
+  const int nct = a.kvl / 64;
   const int cw0 = wave * (a.kvl / 4);
-  const int rt = wave & 1, ht = wave >> 1;
-  if (steps > 0) load_rows(r0);
-  for (int st = 0; st < steps; st++) {
+  if (steps > 0) issue(0, st0);
+  auto step = [&](int st, int8_t *cur, int8_t *nxt) __attribute__((always_inline)) {
+    // this step's rows are in (the wave's only requests in flight) and every
+    // wave is done with the previous step, whose stage now takes the next rows
+    dma_step_barrier<0>();
+    if (st + 1 < steps) issue(st + 1, nxt);
     const int t0 = r0 + st * kMlaMR;
+    // scores of rows ln (A) against heads ln (B) over the wave's quarter
+    v4f c0 = v4f{0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;
+    const int8_t *arow = cur + ln * kMlaRowB;
+    // blocks past the contraction columns read padding pieces against zero queries
 #pragma unroll
-    for (int i = 0; i < kMlaLoads; i++) {
-      const int f = tid + 256 * i;
-      const int r = f / c4n, c4 = f - r * c4n;
-      if (r < kMlaMR) *reinterpret_cast<float4 *>(ls + r * kMlaMS + 4 * c4) = pre[i];
+    for (int b = 0; b < kMlaQB; b++) {
+      const int q = kMlaQB * wave + b;
+      const float4 av = *reinterpret_cast<const float4 *>(arow + 16 * (4 * q + lg));
+      c0 = mfma_f32(av.x, qv[b].x, c0);
+      c1 = mfma_f32(av.y, qv[b].y, c1);
+      c2 = mfma_f32(av.z, qv[b].z, c2);
+      c3 = mfma_f32(av.w, qv[b].w, c3);
     }
-    __syncthreads();  // the rows (and, on the first step, the queries) are in place
-    if (st + 1 < steps) load_rows(t0 + kMlaMR);
-    // scores of rows 16 rt + .., heads 16 ht + ..
-    // four independent accumulators (one per MFMA of a column block), added
-    // at the end in a fixed order
-    v4f sc;
-    {
-      const float *arow = ls + (16 * rt + ln) * kMlaMS + 4 * lg;
-      const float *brow = qs + (16 * ht + ln) * kMlaMS + 4 * lg;
-      v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
-#pragma unroll 4
-      for (int q = 0; q < kp / 16; q++) {
-        const float4 av = *reinterpret_cast<const float4 *>(arow + 16 * q);
-        const float4 bv = *reinterpret_cast<const float4 *>(brow + 16 * q);
-        s0 = mfma_f32(av.x, bv.x, s0);
-        s1 = mfma_f32(av.y, bv.y, s1);
-        s2 = mfma_f32(av.z, bv.z, s2);
-        s3 = mfma_f32(av.w, bv.w, s3);
-      }
-      sc = (s0 + s1) + (s2 + s3);
-    }
-    // lane holds rows 16 rt + 4 lg + i of head 16 ht + ln
-    const int hh = 16 * ht + ln;
+    const v4f pw = (c0 + c1) + (c2 + c3);
+    part[wave][lane] = make_float4(pw[0], pw[1], pw[2], pw[3]);
+    lds_barrier();  // every wave's partial tile is in place (the next rows stay in flight)
+    const float4 p0 = part[0][lane], p1 = part[1][lane], p2 = part[2][lane], p3 = part[3][lane];
+    // lane: rows 4 lg + i of head h0 + ln
     float sv[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int t = t0 + 16 * rt + 4 * lg + i;
-      sv[i] = t < r1 ? sc[i] * a.scale : -INFINITY;
+      const float pa = i == 0 ? p0.x : (i == 1 ? p0.y : (i == 2 ? p0.z : p0.w));
+      const float pb = i == 0 ? p1.x : (i == 1 ? p1.y : (i == 2 ? p1.z : p1.w));
+      const float pc = i == 0 ? p2.x : (i == 1 ? p2.y : (i == 2 ? p2.z : p2.w));
+      const float pd = i == 0 ? p3.x : (i == 1 ? p3.y : (i == 2 ? p3.z : p3.w));
+      const float sc = (pa + pb) + (pc + pd);
+      const int t = t0 + 4 * lg + i;
+      sv[i] = t < r1 ? sc * a.scale : -INFINITY;
       mx = fmaxf(mx, sv[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (lg == 0) cmax[rt][hh] = mx;
-    __syncthreads();
-    if (tid < kMlaMH) {
-      const float mo = mrun[tid];
-      const float mn = fmaxf(mo, fmaxf(cmax[0][tid], cmax[1][tid]));
-      alpha[tid] = mo == -INFINITY ? 0.f : expf(mo - mn);
-      mnew[tid] = mn;
-      mrun[tid] = mn;
-    }
-    __syncthreads();
-    {
-      const float mn = mnew[hh];
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float pv = sv[i] == -INFINITY ? 0.f : expf(sv[i] - mn);
-        ps[hh * kMlaPS + 16 * rt + 4 * lg + i] = pv;
-        sum += pv;
-      }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      if (lg == 0) csum[rt][hh] = sum;
-    }
-    __syncthreads();  // the weights and row sums are in place
-    if (tid < kMlaMH) lrun[tid] = fmaf(lrun[tid], alpha[tid], csum[0][tid] + csum[1][tid]);
-    // latent sums of columns cw0 + 16 ct + ln, heads 16 mt + 4 lg + i
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) al[i] = alpha[16 * mt + 4 * lg + i];
-#pragma unroll
-      for (int ct = 0; ct < 8; ct++)
-        if (ct < nct)
-#pragma unroll
-          for (int i = 0; i < 4; i++) acc[mt][ct][i] *= al[i];
-    }
-#pragma unroll
-    for (int q = 0; q < kMlaMR / 16; q++) {
-      float4 pa[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-        pa[mt] = *reinterpret_cast<const float4 *>(ps + (16 * mt + ln) * kMlaPS + 16 * q + 4 * lg);
-      const float *lrow = ls + (16 * q + 4 * lg) * kMlaMS + cw0 + ln;
-#pragma unroll
-      for (int ct = 0; ct < 8; ct++) {
-        if (ct < nct) {
-          const float b0 = lrow[16 * ct], b1 = lrow[kMlaMS + 16 * ct];
-          const float b2 = lrow[2 * kMlaMS + 16 * ct], b3 = lrow[3 * kMlaMS + 16 * ct];
-#pragma unroll
-          for (int mt = 0; mt < 2; mt++) {
-            acc[mt][ct] = mfma_f32(pa[mt].x, b0, acc[mt][ct]);
-            acc[mt][ct] = mfma_f32(pa[mt].y, b1, acc[mt][ct]);
-            acc[mt][ct] = mfma_f32(pa[mt].z, b2, acc[mt][ct]);
-            acc[mt][ct] = mfma_f32(pa[mt].w, b3, acc[mt][ct]);
-          }
-        }
-      }
-    }
-    __syncthreads();  // every wave is done with the step's rows and weights
-  }
-  // the split's partial results
-#pragma unroll
-  for (int mt = 0; mt < 2; mt++)
+    const float mn = fmaxf(mrun, mx);
+    const float al = mrun == -INFINITY ? 0.f : expf(mrun - mn);
+    float pv[4], sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int h = h0 + 16 * mt + 4 * lg + i;
-      if (h < a.H) {
-        float *dst = a.pclat + (((int64_t)s * a.H + h) * a.nsplit + k) * a.kvl + cw0 + ln;
-#pragma unroll
-        for (int ct = 0; ct < 8; ct++)
-          if (ct < nct) dst[16 * ct] = acc[mt][ct][i];
-      }
+      pv[i] = sv[i] == -INFINITY ? 0.f : expf(sv[i] - mn);
+      sum += pv[i];
     }
-  if (tid < kMlaMH && h0 + tid < a.H) {
-    const int64_t part = ((int64_t)s * a.H + h0 + tid) * a.nsplit + k;
-    a.pm[part] = mrun[tid];
-    a.pl[part] = lrun[tid];
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    lrun = fmaf(lrun, al, sum);
+    mrun = mn;
+    // the latent sums hold heads 4 lg + i: their rescale factors from lanes 4 lg + i
+    float ali[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) ali[i] = __shfl(al, 4 * lg + i, 64);
+#pragma unroll
+    for (int ct = 0; ct < 8; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[ct][i] *= ali[i];
+    // the weights p[head ln][rows 4 lg + i] are this lane's A operands; all 8
+    // column tiles run (with a latent narrower than 512 the tiles past kvl / 64
+    // read other finite columns and are not written)
+#pragma unroll
+    for (int ct = 0; ct < 8; ct++) {
+      const int c = cw0 + 16 * ct + ln;
+      float b[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        b[i] = *reinterpret_cast<const float *>(cur + (4 * lg + i) * kMlaRowB + 4 * c);
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[ct] = mfma_f32(pv[i], b[i], acc[ct]);
+    }
+  };
+  int st = 0;
+  for (; st + 1 < steps; st += 2) {
+    step(st, st0, st1);
+    step(st + 1, st1, st0);
+  }
+  if (st < steps) step(st, st0, st1);
+  wait_vm_at_most<0>();  // no request may still be in flight when the workgroup ends
+
+  // the split's partial results: lane holds heads h0 + 4 lg + i, columns cw0 + 16 ct + ln
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int hh = h0 + 4 * lg + i;
+    if (hh < a.H) {
+      float *dst = a.pclat + (((int64_t)s * a.H + hh) * a.nsplit + k) * a.kvl + cw0 + ln;
+#pragma unroll
+      for (int ct = 0; ct < 8; ct++)
+        if (ct < nct) dst[16 * ct] = acc[ct][i];
+    }
+  }
+  if (wave == 0 && lg == 0 && h < a.H) {
+    const int64_t pidx = ((int64_t)s * a.H + h) * a.nsplit + k;
+    a.pm[pidx] = mrun;
+    a.pl[pidx] = lrun;
   }
 }
 
