@@ -513,6 +513,20 @@ __device__ __forceinline__ void dma_tile(const GroupedMfmaArgs &a, const MfmaTil
         for (int s = 0; s < NS; s++)
           acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[s], acc[ms][s], 0, 0, 0);
     }
+    // instruction order of the step: the weight reads and the first
+    // activation reads, then each of the step's DMA requests between three
+    // MFMAs and one shared read, then the remaining MFMAs (measured against
+    // the compiler's own order: 857 against 883 us for gate/up, 474 against
+    // 492 us for down at 2048 tokens)
+    __builtin_amdgcn_sched_group_barrier(0x100, NS + 2, 0);  // shared-memory reads
+#pragma unroll
+    for (int g = 0; g < PIECES; g++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);     // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // global (DMA) request
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    constexpr int REST = 2 * MSV * NS - 3 * PIECES;  // small tiles have fewer MFMAs than the groups
+    if constexpr (REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);
   };
   int st = 0;
   for (; st + 2 < nsteps; st += 3) {
