@@ -31,6 +31,7 @@ def _inputs(H, kvl, nope, rope, vdim, S, T, seed):
     ((2, 192, 16, 8, 8), 2, 260),           # latent width not a power of two
     ((2, 1024, 16, 64, 8), 2, 16384),       # widest latent, most cache rows
     ((12, 256, 32, 16, 24), 2, 5000),       # 128-row chunks, heads not a multiple of 4
+    ((8, 448, 32, 36, 64), 2, 777),         # rotary width not a multiple of 16, 7 column tiles
     ((64, 512, 192, 64, 256), 1, 9000),     # GLM shape, long cache
     ((64, 512, 192, 64, 256), 1, 1000),     # GLM shape, decode
     ((64, 512, 192, 64, 256), 4, 2048),     # GLM shape, 4 queries
