@@ -370,6 +370,16 @@ __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a
   }
 }
 
+// Subtiles (16 pairs each) of the two launch shapes: batches of up to 64
+// tokens hold at most 4 per tile, larger batches at most 5.
+constexpr int kSmallMsv = 4, kLargeMsv = 5;
+// Larger batches: the shared-memory DMA kernel in 4-wave workgroups, two
+// per CU (measured against one 8-wave workgroup per CU and against the
+// register-staged grouped_mfma_kernel<.., 8, 4, 5>: the same gate/up time,
+// down 486 against 545 and 567 us at 2048 tokens), with whole tiles per XCD.
+constexpr int kPrefillDmaWaves = 4;
+constexpr bool kDmaXcdTiles = true;
+
 // ---- large batches: operands staged by shared-memory DMA ----------------------
 //
 // The same tiles, waves and MFMA layout as grouped_mfma_kernel<MODE, 8, 4, ..>
@@ -392,14 +402,6 @@ __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a
 // Lane group j of an MFMA covers columns 32 j + 16 c .. +16 of the step
 // (c = the step's two MFMAs): one 16-byte weight piece feeds both, the
 // activation pieces are logical 2 j + c.
-constexpr int kSmallMsv = 4, kLargeMsv = 5;
-// Larger batches: the shared-memory DMA kernel in 4-wave workgroups, two
-// per CU (measured against one 8-wave workgroup per CU and against the
-// register-staged grouped_mfma_kernel<.., 8, 4, 5>: the same gate/up time,
-// down 486 against 545 and 567 us at 2048 tokens), with whole tiles per XCD.
-constexpr int kPrefillDmaWaves = 4;
-constexpr bool kDmaXcdTiles = true;
-
 
 constexpr int kDKS = 128;                    // columns per step
 constexpr int kDNS = 4;                      // 16-row weight subtiles per wave
@@ -643,11 +645,6 @@ void grouped_mfma_dma_kernel(GroupedMfmaArgs a) {
 }
 
 bool grouped_mfma_fits(int C) { return C % kKS == 0; }
-
-// Subtiles (16 pairs each) of the two launch shapes: batches of up to 64
-// tokens run 4-wave workgroups holding at most 4 subtiles, larger batches
-// 8-wave workgroups holding at most 5.
-
 
 // Pairs per tile: as many as the launch's workgroups hold.  A group larger
 // than that (a routed expert with more pairs, or the shared expert) is cut
