@@ -14,6 +14,7 @@
 // which costs about a microsecond per workgroup, so every cross-workgroup
 // dependency goes through a kernel boundary instead.
 #include "moe_kernels.h"
+#include "dma.h"
 #include "topk.h"
 #include "quant.h"
 #include "norm.h"
@@ -236,6 +237,139 @@ __global__ __launch_bounds__(256 * TG) void router_tile_kernel(RouterArgs a) {
     }
 }
 
+// Mid-size batches: a workgroup of 4 waves over 8 tokens x 8 experts, each
+// wave a 4 x 4 register tile of logits (wave w: tokens 4 (w / 2) .., experts
+// 4 (w % 2) ..), with the step's 8 token rows and 8 weight rows copied into
+// shared memory once per workgroup
+// (global_load_lds_dwordx4, a three-stage ring, two steps of 256 columns
+// requested ahead) instead of once per wave.  Every logit is lane p's
+// ascending FMA chain over k = 4p + 256j + q followed by wave_sum_f32: the
+// same bits as router_kernel.
+constexpr int kRmT = 8, kRmE = 8;  // tokens and experts of a workgroup
+
+template <bool XB>
+struct RouterMid {
+  static constexpr int XR = XB ? 512 : 1024;             // shared bytes of a token row per step
+  static constexpr int XI = kRmT * XR / 1024;            // token-row requests per step
+  static constexpr int PIECES = (XI + kRmE) / 4;         // per wave and step (4, or 3 with bf16)
+  static constexpr int STAGE = kRmT * XR + kRmE * 1024;  // shared bytes of a stage
+};
+
+template <bool XB>
+__global__ __launch_bounds__(256) void router_mid_kernel(RouterArgs a) {
+  using R = RouterMid<XB>;
+  static_assert((R::XI + kRmE) % 4 == 0, "requests per wave");
+  __shared__ __align__(1024) int8_t S0[R::STAGE], S1[R::STAGE], S2[R::STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int neb = (a.E + kRmE - 1) / kRmE;
+  const int n_router = neb * ((a.S + kRmT - 1) / kRmT);
+  if ((int)blockIdx.x >= n_router) {
+    const int s = blockIdx.x - n_router;
+    if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
+    quant_row_block(XB ? nullptr : a.x + (int64_t)s * a.D, XB ? a.xb + (int64_t)s * a.D : nullptr,
+                    a.D, a.xq_perm + (int64_t)s * a.D, nullptr, a.sx + s, a.sumx + s);
+    return;
+  }
+  const int eb = (blockIdx.x % neb) * kRmE, sb = (blockIdx.x / neb) * kRmT;
+  // request n = PIECES wave + u of a step: n < XI token rows (XR bytes each,
+  // 1024 / XR rows per request), otherwise weight row n - XI; lane l copies
+  // bytes 16 (l % (XR / 16)) of its row
+  const int8_t *src[R::PIECES];
+  int step_bytes[R::PIECES], dst[R::PIECES];
+#pragma unroll
+  for (int u = 0; u < R::PIECES; u++) {
+    const int n = R::PIECES * wave + u;
+    if (n < R::XI) {
+      const int r = (1024 / R::XR) * n + lane / (R::XR / 16);
+      const int srow = min(sb + r, a.S - 1);
+      const int8_t *base = XB ? reinterpret_cast<const int8_t *>(a.xb) + (int64_t)srow * a.D * 2
+                              : reinterpret_cast<const int8_t *>(a.x) + (int64_t)srow * a.D * 4;
+      src[u] = base + 16 * (lane % (R::XR / 16));
+      step_bytes[u] = R::XR;
+      dst[u] = 1024 * n;
+    } else {
+      const int r = n - R::XI;
+      const int erow = min(eb + r, a.E - 1);
+      src[u] = reinterpret_cast<const int8_t *>(a.W) + (int64_t)erow * a.D * 4 + 16 * lane;
+      step_bytes[u] = 1024;
+      dst[u] = kRmT * R::XR + 1024 * r;
+    }
+  }
+  const int nj = a.D >> 8;
+  auto stage = [&](auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    return B == 0 ? S0 : (B == 1 ? S1 : S2);
+  };
+  auto issue = [&](int j, auto bc) __attribute__((always_inline)) {
+    const int jj = min(j, nj - 1);
+    int8_t *st = stage(bc);
+#pragma unroll
+    for (int u = 0; u < R::PIECES; u++) dma16(src[u] + (int64_t)jj * step_bytes[u], st + dst[u]);
+  };
+  const int tg = wave >> 1, eg = wave & 1;
+  float acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; t++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) acc[t][e] = 0.f;
+  issue(0, std::integral_constant<int, 0>{});
+  issue(1, std::integral_constant<int, 1>{});
+  auto step = [&](int j, auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    dma_step_barrier<R::PIECES>();
+    issue(j + 2, std::integral_constant<int, (B + 2) % 3>{});
+    const int8_t *st = stage(bc);
+    float4 xv[4], wv[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const int8_t *row = st + (4 * tg + t) * R::XR;
+      if constexpr (XB) {
+        const uint2 w = reinterpret_cast<const uint2 *>(row)[lane];
+        xv[t] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+      } else {
+        xv[t] = reinterpret_cast<const float4 *>(row)[lane];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      wv[e] = reinterpret_cast<const float4 *>(st + kRmT * R::XR + (4 * eg + e) * 1024)[lane];
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        float c = acc[t][e];
+        c = fmaf(xv[t].x, wv[e].x, c);
+        c = fmaf(xv[t].y, wv[e].y, c);
+        c = fmaf(xv[t].z, wv[e].z, c);
+        c = fmaf(xv[t].w, wv[e].w, c);
+        acc[t][e] = c;
+      }
+  };
+  int j = 0;
+  for (; j + 2 < nj; j += 3) {
+    step(j, std::integral_constant<int, 0>{});
+    step(j + 1, std::integral_constant<int, 1>{});
+    step(j + 2, std::integral_constant<int, 2>{});
+  }
+  if (j < nj) step(j, std::integral_constant<int, 0>{});
+  if (j + 1 < nj) step(j + 1, std::integral_constant<int, 1>{});
+  // the last requests (repeats of the last step) land in stages no step
+  // reads; none may still be in flight when the workgroup ends
+  wait_vm_at_most<0>();
+  const int s0 = sb + 4 * tg, e0 = eb + 4 * eg;
+#pragma unroll
+  for (int t = 0; t < 4; t++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float v = wave_sum_f32(acc[t][e]);
+      if (lane == 0 && s0 + t < a.S && e0 + e < a.E) {
+        a.logits[(int64_t)(s0 + t) * a.E + e0 + e] = v;
+        if (a.logits_out) a.logits_out[(int64_t)(s0 + t) * a.E + e0 + e] = v;
+      }
+    }
+}
+
 }  // namespace moe
 
 namespace moe {
@@ -249,8 +383,8 @@ hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
   const int ne4 = (a.E + 3) / 4;
   const int nq = with_quant ? a.S : 0;
   // a few tokens: one token per wave, the whole weight row in one batch of
-  // loads (rows are re-read per token from L2); up to 255: 4 x 4 register
-  // tiles; more: 8 x 8 register tiles
+  // loads (rows are re-read per token from L2); up to 255: 8 x 8 tiles staged
+  // in shared memory; more: 8 x 8 register tiles per wave
   const bool xb = a.xb != nullptr;  // bf16 tokens (no RMSNorm with them)
   if (a.S <= 8) {
     const size_t lds = a.gamma ? (size_t)a.D * 4 : 0;  // the normalized row
@@ -259,14 +393,14 @@ hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
     else
       hipLaunchKernelGGL((router_kernel<1, 24>), dim3(ne4 * a.S + nq), dim3(256), lds, st, a);
   } else if (a.S < kRouterTileMinTokens) {
-    // 4 x 4 register tiles, 4 tokens x 16 experts per workgroup (swept against
-    // one expert x 8 tokens per wave: 19-20 against 21-24 us up to 64 tokens,
-    // 26-37 against 38-63 us from 128 to 255, router and selection together)
-    const dim3 grid(((a.E + 15) / 16) * ((a.S + 3) / 4) + nq);
+    // 8 tokens x 8 experts per workgroup through shared memory (against the
+    // 4 x 4 register tiles of router_tile_kernel, 4 tokens x 16 experts per
+    // workgroup: 14.0 against 20.5 us at 64 tokens)
+    const dim3 grid(((a.E + kRmE - 1) / kRmE) * ((a.S + kRmT - 1) / kRmT) + nq);
     if (xb)
-      hipLaunchKernelGGL((router_tile_kernel<4, 4, 1, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((router_mid_kernel<true>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((router_tile_kernel<4, 4, 1>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((router_mid_kernel<false>), grid, dim3(256), 0, st, a);
   } else {
     // 4-wave workgroups of 8 tokens x 32 experts (swept against 8-wave
     // workgroups of 16 x 32 and other tiles: 188 against 209 us at 2048 tokens)
