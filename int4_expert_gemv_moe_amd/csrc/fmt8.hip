@@ -163,6 +163,157 @@ __global__ __launch_bounds__(256) void dn8_kernel(Swiglu8Args a) {
   }
 }
 
+// The int8 shared expert of the union path on int8 matrix cores
+// (v_mfma_i32_16x16x64_i8; lane l supplies A[l % 16][16 (l / 16) ..] and
+// B[16 (l / 16) ..][l % 16] and receives C[4 (l / 16) + i][l % 16]).  A
+// workgroup takes 16 weight rows (MODE 0: the gate rows of 8 hidden units in
+// columns 0..7 of the tile and their up rows in columns 8..15; MODE 1: 16
+// down rows) and up to 64 tokens (16-token subtiles).  Its waves split the
+// contraction, wave w of W taking 64-column steps w, w + W, ..., and add
+// their int32 tiles in shared memory: integer sums, so the split changes no
+// bit.
+// The token codes are in the permuted layout (per 8 columns the even columns,
+// then the odd ones); each 8-column group of weight bytes is permuted alike
+// before the product.  Operands come straight from global memory, 16 bytes
+// per lane (a weight load covers 16 rows x 64 bytes, a token load 16 tokens x
+// 64 bytes), several steps of loads in flight.  Row blocks vary fastest over the
+// grid, so each XCD's L2 keeps the weight rows of its blocks across token
+// chunks.  The epilogues are those of gu8_kernel and dn8_kernel.
+typedef int v4i8x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i8x4 perm_i8x16(const uint4 &w) {
+  return v4i8x4{(int)__builtin_amdgcn_perm(w.y, w.x, 0x06040200u),
+                (int)__builtin_amdgcn_perm(w.y, w.x, 0x07050301u),
+                (int)__builtin_amdgcn_perm(w.w, w.z, 0x06040200u),
+                (int)__builtin_amdgcn_perm(w.w, w.z, 0x07050301u)};
+}
+
+constexpr int kS8Tokens = 64;  // tokens of a workgroup (at most four 16-token subtiles)
+constexpr int kS8U = 2;        // steps of a wave with loads in flight together
+
+// MS: 16-token subtiles of a workgroup (1..4; fewer when S is small); NW:
+// waves of a workgroup, the contraction split; R: 16-row weight tiles of a
+// workgroup (each token load feeds all R).
+template <int MODE, int MS, int NW, int R>
+__global__ __launch_bounds__(64 * NW) void shared8_mfma_kernel(Shared8MfmaArgs a) {
+  constexpr int kS8Waves = NW, kS8R = R;
+  __shared__ v4i8x4 part[kS8Waves][MS * kS8R][64];  // [wave][tile][lane]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  constexpr int RB = (MODE == 0 ? 8 : 16) * kS8R;  // output rows of a workgroup
+  const int nrb = (a.O + RB - 1) / RB;
+  const int rb = blockIdx.x % nrb, s0 = (blockIdx.x / nrb) * (16 * MS);
+  // the lane's weight row (B column n) of row tile r
+  const int8_t *wrow[kS8R];
+  int orow[kS8R];
+#pragma unroll
+  for (int r = 0; r < kS8R; r++) {
+    orow[r] = MODE == 0 ? rb * RB + 8 * r + (n & 7) : rb * RB + 16 * r + n;
+    wrow[r] = (MODE == 0 && n >= 8 ? a.W1 : a.W0) + (int64_t)min(orow[r], a.O - 1) * a.C;
+  }
+  const int8_t *xrow[MS];  // A row n of subtile ms: token s0 + 16 ms + n (past S: the last token)
+#pragma unroll
+  for (int ms = 0; ms < MS; ms++)
+    xrow[ms] = a.act + (int64_t)min(s0 + 16 * ms + n, a.S - 1) * a.act_stride;
+  v4i8x4 acc[MS][kS8R];
+#pragma unroll
+  for (int ms = 0; ms < MS; ms++)
+#pragma unroll
+    for (int r = 0; r < kS8R; r++) acc[ms][r] = v4i8x4{0, 0, 0, 0};
+  const int nsteps = (a.C + 63) / 64;
+  for (int st0 = wave; st0 < nsteps; st0 += kS8Waves * kS8U) {
+    uint4 wv[kS8U][kS8R], xv[kS8U][MS];
+#pragma unroll
+    for (int u = 0; u < kS8U; u++) {
+      // columns 64 st + 16 g .. +16 (C % 32 == 0: a piece is whole or past the end)
+      const int col = 64 * (st0 + kS8Waves * u) + 16 * g;
+      const bool ok = col < a.C;
+#pragma unroll
+      for (int r = 0; r < kS8R; r++) wv[u][r] = ldnt16(wrow[r] + col, ok, wrow[r]);
+#pragma unroll
+      for (int ms = 0; ms < MS; ms++) xv[u][ms] = ld16(xrow[ms] + col, ok, xrow[ms]);
+    }
+#pragma unroll
+    for (int u = 0; u < kS8U; u++) {
+#pragma unroll
+      for (int r = 0; r < kS8R; r++) {
+        const v4i8x4 b = perm_i8x16(wv[u][r]);
+#pragma unroll
+        for (int ms = 0; ms < MS; ms++) {
+          const v4i8x4 x = v4i8x4{(int)xv[u][ms].x, (int)xv[u][ms].y, (int)xv[u][ms].z,
+                                  (int)xv[u][ms].w};
+          acc[ms][r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, b, acc[ms][r], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int ms = 0; ms < MS; ms++)
+#pragma unroll
+    for (int r = 0; r < kS8R; r++) part[wave][ms * kS8R + r][lane] = acc[ms][r];
+  __syncthreads();
+  // wave w finishes tile w (token subtile w / R, row tile w % R): lane holds
+  // tokens s0 + 16 (w / R) + 4 g + i of column n
+  for (int tile = wave; tile < MS * kS8R; tile += kS8Waves) {
+    v4i8x4 tot = part[0][tile][lane];
+#pragma unroll
+    for (int w = 1; w < kS8Waves; w++) tot += part[w][tile][lane];
+    const int ms = tile / kS8R, r = tile % kS8R;
+    const int o = MODE == 0 ? rb * RB + 8 * r + (n & 7) : rb * RB + 16 * r + n;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int t = s0 + 16 * ms + 4 * g + i;
+      if (MODE == 0) {
+        const int au = __shfl_xor(tot[i], 8, 64);  // the up sum of the lane's hidden unit
+        if (n < 8 && t < a.S && o < a.O) {
+          const float sxs = a.ascale[(int64_t)t * a.ascale_stride];
+          const float gv = ((float)tot[i] * a.ws0[o]) * sxs;
+          const float uv = ((float)au * a.ws1[o]) * sxs;
+          a.out[(int64_t)t * a.out_stride + o] = silu(gv) * uv;
+        }
+      } else if (t < a.S && o < a.O) {
+        const float v = ((float)tot[i] * a.ws0[o]) * a.ascale[(int64_t)t * a.ascale_stride];
+        a.out[(int64_t)t * a.out_stride + o] = v;
+      }
+    }
+  }
+}
+
+template <int MODE, int MS, int NW, int R>
+static void launch_s8(const Shared8MfmaArgs &a, hipStream_t st) {
+  constexpr int RB = (MODE == 0 ? 8 : 16) * R;
+  const int nrb = (a.O + RB - 1) / RB;
+  const dim3 grid(nrb * ((a.S + 16 * MS - 1) / (16 * MS))), block(64 * NW);
+  hipLaunchKernelGGL((shared8_mfma_kernel<MODE, MS, NW, R>), grid, block, 0, st, a);
+}
+
+// Swept at the GLM shape (int8 gate/up, down): up to 64 tokens 16 waves and
+// 2 row tiles (64 tokens: 27.8, 11.6 us; 8 waves and 1 or 4 row tiles:
+// 23.8, 15.9 and 38.3, 16.6 us); more tokens 8 waves and 4 row tiles (2048
+// tokens: 254, 154 us; 2 row tiles 334-352, 178-198 us; 1 row tile 543, 272
+// us), every token load feeding more weight rows.
+template <int MODE>
+static void launch_s8_mode(const Shared8MfmaArgs &a, hipStream_t st) {
+  if (a.S > 64) {
+    launch_s8<MODE, 4, 8, 4>(a, st);
+    return;
+  }
+  switch ((a.S + 15) / 16) {
+    case 1: launch_s8<MODE, 1, 16, 2>(a, st); break;
+    case 2: launch_s8<MODE, 2, 16, 2>(a, st); break;
+    case 3: launch_s8<MODE, 3, 16, 2>(a, st); break;
+    default: launch_s8<MODE, 4, 16, 2>(a, st); break;
+  }
+}
+
+hipError_t launch_shared8_mfma(const Shared8MfmaArgs &a, int mode, hipStream_t st) {
+  if (mode == 0)
+    launch_s8_mode<0>(a, st);
+  else
+    launch_s8_mode<1>(a, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_rows_i8(const Q8QuantArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(quant_rows_i8_kernel, dim3((a.O + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();

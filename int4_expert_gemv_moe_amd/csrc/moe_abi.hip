@@ -839,27 +839,38 @@ extern "C" int moe_layer_forward_noalloc(const moe_config *cfg, const moe_layer 
 
 namespace {
 
-// The int8 shared expert of the union path on all S tokens, its gate/up
-// (mode 0: codes xq in the permuted layout, h into slot K of every token's
-// hidden rows) or its down (mode 1: y into slot K of the staging rows).
+// The int8 shared expert of the union path on all S tokens (int8 matrix
+// cores): its gate/up (mode 0: codes xq in the permuted layout, h into slot K
+// of every token's hidden rows) or its down (mode 1: the requantized slot K
+// of the hidden rows, y into slot K of the staging rows).
 int shared8_rows(const moe_config &c, const moe_experts_i8 &e, const Work &w, int S, int mode,
                  hipStream_t st) {
   const int P = c.K + 1;
-  Swiglu8Args a{};
-  a.xq = w.xq;
-  a.sx = w.sx;
+  Shared8MfmaArgs a{};
   a.S = S;
-  a.D = c.D;
-  a.I = c.I;
-  q8_rows(e.gate, c.I, c.D, 0, &a.G, &a.gs);
-  q8_rows(e.up, c.I, c.D, 0, &a.U, &a.us);
-  q8_rows(e.down, c.D, c.I, 0, &a.Dn, &a.ds);
-  a.x_perm = 1;
-  a.h = w.h + (size_t)c.K * c.I;
-  a.h_stride = (int64_t)P * c.I;
-  a.y = w.stage + (size_t)c.K * c.D;
-  a.y_stride = (int64_t)P * c.D;
-  return hip_rc(mode == 0 ? launch_swiglu8_gateup(a, st) : launch_swiglu8_down(a, st));
+  if (mode == 0) {
+    a.act = w.xq;
+    a.act_stride = c.D;
+    a.ascale = w.sx;
+    a.ascale_stride = 1;
+    q8_rows(e.gate, c.I, c.D, 0, &a.W0, &a.ws0);
+    q8_rows(e.up, c.I, c.D, 0, &a.W1, &a.ws1);
+    a.O = c.I;
+    a.C = c.D;
+    a.out = w.h + (size_t)c.K * c.I;
+    a.out_stride = (int64_t)P * c.I;
+  } else {
+    a.act = w.hq + (size_t)c.K * c.I;
+    a.act_stride = (int64_t)P * c.I;
+    a.ascale = w.sh + c.K;
+    a.ascale_stride = P;
+    q8_rows(e.down, c.D, c.I, 0, &a.W0, &a.ws0);
+    a.O = c.D;
+    a.C = c.I;
+    a.out = w.stage + (size_t)c.K * c.D;
+    a.out_stride = (int64_t)P * c.D;
+  }
+  return hip_rc(launch_shared8_mfma(a, mode, st));
 }
 
 // The union path; with given_idx / given_w the caller's routing replaces the

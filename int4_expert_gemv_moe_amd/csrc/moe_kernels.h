@@ -213,6 +213,20 @@ struct Swiglu8Args {
   int64_t y_stride;        // floats between the tokens' y rows (0: D)
 };
 
+// The int8 shared expert of the union path on int8 matrix cores (fmt8.hip):
+// MODE 0 gate/up + SwiGLU into h, MODE 1 down into y, on all S tokens.
+struct Shared8MfmaArgs {
+  const int8_t *act;       // token codes, permuted layout; token t's row at act + t * act_stride
+  int64_t act_stride;      // bytes between token rows
+  const float *ascale;     // token t's scale at ascale[t * ascale_stride]
+  int64_t ascale_stride;
+  const int8_t *W0, *W1;   // MODE 0: gate and up codes [O][C]; MODE 1: down codes [O][C] (W0)
+  const float *ws0, *ws1;  // their row scales [O]
+  int S, O, C;             // tokens, output rows (MODE 0: hidden units), columns
+  float *out;              // token t's output row at out + t * out_stride (h or y)
+  int64_t out_stride;      // floats between output rows
+};
+
 // Packed int2 weights (fmt2.hip): four codes per byte, code + 2, column
 // 4j + k in bits 2k..2k+1 of byte j.
 struct Pack2Args {
@@ -304,6 +318,7 @@ hipError_t launch_swiglu2_down(const Swiglu2Args &a, hipStream_t st);
 hipError_t launch_quant_rows_i8(const Q8QuantArgs &a, hipStream_t st);
 hipError_t launch_swiglu8_gateup(const Swiglu8Args &a, hipStream_t st);
 hipError_t launch_swiglu8_down(const Swiglu8Args &a, hipStream_t st);
+hipError_t launch_shared8_mfma(const Shared8MfmaArgs &a, int mode, hipStream_t st);
 
 hipError_t launch_quant(const QuantArgs &a, int S, hipStream_t st);
 hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st);

@@ -67,8 +67,13 @@ def test_layer_with_int8_shared_expert(shape, S, acc, topp):
     assert_close_rows(to_np(o), ref, what=f"shared int8 S={S}")
 
 
+# the union's int8 shared expert runs on the int8 matrix cores in chunks of 64
+# tokens (100 and 150: two and three chunks, the last ragged); I = 96 leaves a
+# half 64-column step in the down contraction
 @pytest.mark.parametrize("shape,S,acc", [(TINY, 4, False), (MID, 24, True), (MID, 100, False),
-                                         (FUSED, 7, False), (GLM, 4, True), (GLM, 64, False)])
+                                         (FUSED, 7, False), (GLM, 4, True), (GLM, 64, False),
+                                         (GLM, 100, False), (MID, 150, True),
+                                         (synth.Shape(D=512, I=96, E=16, K=4), 70, False)])
 def test_union_with_int8_shared_expert(shape, S, acc):
     """The union path with the int8 shared expert returns the per-token
     path's bits (whether the per-token path runs the int8 expert inside its
