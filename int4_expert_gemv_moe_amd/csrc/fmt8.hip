@@ -14,6 +14,7 @@
 // of every 1024-column chunk, so each load instruction of a wave covers 1 KiB
 // of one row.
 #include "moe_kernels.h"
+#include "dma.h"
 #include "quant.h"
 #include "rowops.h"
 
@@ -279,6 +280,128 @@ __global__ __launch_bounds__(64 * NW) void shared8_mfma_kernel(Shared8MfmaArgs a
   }
 }
 
+// Larger batches: a workgroup (four waves) takes 128 tokens x 128 weight rows
+// (MODE 0: 64 hidden units, each wave two 16-row tiles of the gate rows of 8
+// units beside their up rows; MODE 1: 128 down rows) over the whole
+// contraction, in steps of 128 columns.  A step's token rows (16 KB) and the
+// waves' weight rows (4 KB each) travel from global memory into shared memory
+// by DMA (global_load_lds_dwordx4, two stages: the next step is requested
+// while this one computes), so each token row is fetched once per 128 weight
+// rows and each weight row once per 128 tokens.  The 128-byte rows of a stage
+// have their 16-byte pieces XOR-swizzled by row (piece q of row R holds
+// logical piece q ^ ((R >> 1) & 7)).  MFMA chunk c of a step covers columns
+// 64 c .. +64, lane group g logical piece 4 c + g.  Pieces past C read the
+// row's first piece and meet zeroed weights.  Row blocks vary fastest over the
+// grid, so each XCD keeps the weight rows of its blocks in L2 across the token
+// chunks.  The epilogues are those of shared8_mfma_kernel.
+constexpr int kS8TT = 128;             // tokens of a workgroup
+constexpr int kS8TR = 32;              // weight rows of a wave (two 16-row tiles)
+constexpr int kS8TK = 128;             // columns of a step
+constexpr int kS8TA = kS8TT * kS8TK;   // token bytes of a stage (16 KB)
+constexpr int kS8TW = kS8TR * kS8TK;   // weight bytes of a wave's stage (4 KB)
+
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void shared8_tile_kernel(Shared8MfmaArgs a) {
+  __shared__ __align__(1024) int8_t A0[kS8TA], A1[kS8TA], B0[4 * kS8TW], B1[4 * kS8TW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  constexpr int RB = MODE == 0 ? 64 : 128;  // output rows (MODE 0: hidden units) of a workgroup
+  const int nrb = (a.O + RB - 1) / RB;
+  const int rb = blockIdx.x % nrb, s0 = (blockIdx.x / nrb) * kS8TT;
+  // output row of the wave's local weight row R (0..31): tile R / 16, row R % 16
+  auto out_row = [&](int R) {
+    return MODE == 0 ? rb * 64 + wave * 16 + 8 * (R >> 4) + (R & 7) : rb * 128 + wave * 32 + R;
+  };
+  // DMA request k of a stage: token rows 8 (wave + 4 k) + lane / 8 and local
+  // weight rows 8 k + lane / 8; the lane fetches logical piece
+  // (lane % 8) ^ ((row >> 1) & 7) of its row into slot lane
+  const int8_t *asrc[4], *wsrc[4];
+  int apc[4], wpc[4];  // column of the fetched piece within a step
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int ra = 8 * (wave + 4 * k) + (lane >> 3);
+    asrc[k] = a.act + (int64_t)min(s0 + ra, a.S - 1) * a.act_stride;
+    apc[k] = 16 * ((lane & 7) ^ ((ra >> 1) & 7));
+    const int rw = 8 * k + (lane >> 3);
+    wsrc[k] = (MODE == 0 && (rw & 8) ? a.W1 : a.W0) + (int64_t)min(out_row(rw), a.O - 1) * a.C;
+    wpc[k] = 16 * ((lane & 7) ^ ((rw >> 1) & 7));
+  }
+  const int nsteps = (a.C + kS8TK - 1) / kS8TK;
+  auto issue = [&](int st, int8_t *As, int8_t *Bs) __attribute__((always_inline)) {
+    const int k0 = st * kS8TK;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int ca = k0 + apc[k], cw = k0 + wpc[k];
+      dma16(asrc[k] + (ca < a.C ? ca : 0), As + 1024 * (wave + 4 * k));
+      dma16(wsrc[k] + (cw < a.C ? cw : 0), Bs + wave * kS8TW + 1024 * k);
+    }
+  };
+  v4i8x4 acc[8][2];
+#pragma unroll
+  for (int ms = 0; ms < 8; ms++)
+#pragma unroll
+    for (int r = 0; r < 2; r++) acc[ms][r] = v4i8x4{0, 0, 0, 0};
+  issue(0, A0, B0);
+  auto step = [&](int st, int8_t *As, int8_t *Bs, int8_t *An, int8_t *Bn)
+                  __attribute__((always_inline)) {
+    // this step's pieces are in and every wave is done with the other stage
+    dma_step_barrier<0>();
+    if (st + 1 < nsteps) issue(st + 1, An, Bn);
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const int q = 4 * c + g;  // logical piece of the lane
+      const bool ok = st * kS8TK + 16 * q < a.C;
+      v4i8x4 b[2];
+#pragma unroll
+      for (int r = 0; r < 2; r++) {
+        const int R = 16 * r + n;
+        const uint4 v = *reinterpret_cast<const uint4 *>(Bs + wave * kS8TW + R * kS8TK +
+                                                         16 * (q ^ ((R >> 1) & 7)));
+        b[r] = ok ? perm_i8x16(v) : v4i8x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int ms = 0; ms < 8; ms++) {
+        const int R = 16 * ms + n;
+        const uint4 v = *reinterpret_cast<const uint4 *>(As + R * kS8TK + 16 * (q ^ ((R >> 1) & 7)));
+        const v4i8x4 x = v4i8x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+#pragma unroll
+        for (int r = 0; r < 2; r++)
+          acc[ms][r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, b[r], acc[ms][r], 0, 0, 0);
+      }
+    }
+  };
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(st, A0, B0, A1, B1);
+    step(st + 1, A1, B1, A0, B0);
+  }
+  if (st < nsteps) step(st, A0, B0, A1, B1);
+  wait_vm_at_most<0>();  // nothing in flight when the workgroup ends
+  // lane: tokens s0 + 16 ms + 4 g + i of column n of tile (ms, r)
+#pragma unroll
+  for (int ms = 0; ms < 8; ms++)
+#pragma unroll
+    for (int r = 0; r < 2; r++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int t = s0 + 16 * ms + 4 * g + i;
+        const int o = out_row(16 * r + n);
+        if (MODE == 0) {
+          const int au = __shfl_xor(acc[ms][r][i], 8, 64);  // the up sum of the lane's unit
+          if (n < 8 && t < a.S && o < a.O) {
+            const float sxs = a.ascale[(int64_t)t * a.ascale_stride];
+            const float gv = ((float)acc[ms][r][i] * a.ws0[o]) * sxs;
+            const float uv = ((float)au * a.ws1[o]) * sxs;
+            a.out[(int64_t)t * a.out_stride + o] = silu(gv) * uv;
+          }
+        } else if (t < a.S && o < a.O) {
+          const float v = ((float)acc[ms][r][i] * a.ws0[o]) * a.ascale[(int64_t)t * a.ascale_stride];
+          a.out[(int64_t)t * a.out_stride + o] = v;
+        }
+      }
+}
+
 template <int MODE, int MS, int NW, int R>
 static void launch_s8(const Shared8MfmaArgs &a, hipStream_t st) {
   constexpr int RB = (MODE == 0 ? 8 : 16) * R;
@@ -289,11 +412,23 @@ static void launch_s8(const Shared8MfmaArgs &a, hipStream_t st) {
 
 // Swept at the GLM shape (int8 gate/up, down): up to 64 tokens 16 waves and
 // 2 row tiles (64 tokens: 27.8, 11.6 us; 8 waves and 1 or 4 row tiles:
-// 23.8, 15.9 and 38.3, 16.6 us); more tokens 8 waves and 4 row tiles (2048
-// tokens: 254, 154 us; 2 row tiles 334-352, 178-198 us; 1 row tile 543, 272
-// us), every token load feeding more weight rows.
+// 23.8, 15.9 and 38.3, 16.6 us); 65 to 511 tokens 8 waves and 4 row tiles
+// (at 2048 tokens: 254, 154 us; 2 row tiles 334-352, 178-198 us; 1 row tile
+// 543, 272 us), every token load feeding more weight rows.
+// Batches from this size take shared8_tile_kernel (GLM shape, int8 gate/up +
+// down: 256 tokens 104 against 59 us with shared8_mfma_kernel<., 4, 8, 4>,
+// 384 112 against 111, 512 105 against 105, 768 108 against 157, 1024 112
+// against 206, 2048 163 against 410).
+constexpr int kS8TileMinTokens = 512;
+
 template <int MODE>
 static void launch_s8_mode(const Shared8MfmaArgs &a, hipStream_t st) {
+  if (a.S >= kS8TileMinTokens) {
+    const int nrb = (a.O + (MODE == 0 ? 63 : 127)) / (MODE == 0 ? 64 : 128);
+    const dim3 grid(nrb * ((a.S + kS8TT - 1) / kS8TT));
+    hipLaunchKernelGGL(shared8_tile_kernel<MODE>, grid, dim3(256), 0, st, a);
+    return;
+  }
   if (a.S > 64) {
     launch_s8<MODE, 4, 8, 4>(a, st);
     return;

@@ -67,13 +67,18 @@ def test_layer_with_int8_shared_expert(shape, S, acc, topp):
     assert_close_rows(to_np(o), ref, what=f"shared int8 S={S}")
 
 
-# the union's int8 shared expert runs on the int8 matrix cores in chunks of 64
-# tokens (100 and 150: two and three chunks, the last ragged); I = 96 leaves a
-# half 64-column step in the down contraction
+# the union's int8 shared expert runs on the int8 matrix cores: up to 511
+# tokens in chunks of 64 (100 and 150: two and three chunks, the last ragged),
+# from 512 tokens in 128-token tiles through shared memory (520 and 530: a
+# ragged last tile); I = 96 leaves a partial contraction step in the down
+# projection
+I96 = synth.Shape(D=512, I=96, E=16, K=4)
+
+
 @pytest.mark.parametrize("shape,S,acc", [(TINY, 4, False), (MID, 24, True), (MID, 100, False),
                                          (FUSED, 7, False), (GLM, 4, True), (GLM, 64, False),
-                                         (GLM, 100, False), (MID, 150, True),
-                                         (synth.Shape(D=512, I=96, E=16, K=4), 70, False)])
+                                         (GLM, 100, False), (MID, 150, True), (I96, 70, False),
+                                         (GLM, 520, False), (I96, 530, True)])
 def test_union_with_int8_shared_expert(shape, S, acc):
     """The union path with the int8 shared expert returns the per-token
     path's bits (whether the per-token path runs the int8 expert inside its
