@@ -5,14 +5,16 @@
 // scaled by the row scale and then by the activation scale), as a SwiGLU
 // expert.
 //
-// The expert runs in two launches: gate/up + SwiGLU (one wave per output
-// row, the row's gate and up codes held in registers while the wave walks the
-// tokens), then the per-row requantization of h and down (one wave per four
-// output rows, same scheme).  Every
-// weight byte is read once per call; the token codes are re-read per wave
-// from the cache.  Rows are split into 16-byte pieces, lane l taking piece l
-// of every 1024-column chunk, so each load instruction of a wave covers 1 KiB
-// of one row.
+// The one-expert call runs in two launches: gate/up + SwiGLU (one wave per
+// output row, the row's gate and up codes held in registers while the wave
+// walks the tokens), then the per-row requantization of h and down (one wave
+// per one to four output rows, same scheme).  Every weight byte is read once
+// per call; the token codes are re-read per wave from the cache.  Rows are
+// split into 16-byte pieces, lane l taking piece l of every 1024-column
+// chunk, so each load instruction of a wave covers 1 KiB of one row.  That
+// suits a token or a few; the union path's int8 shared expert, which sees
+// every token of a batch, runs on the int8 matrix cores instead
+// (shared8_mfma_kernel, shared8_tile_kernel below).
 #include "moe_kernels.h"
 #include "dma.h"
 #include "quant.h"
