@@ -356,9 +356,9 @@ int moe_layer_forward_batch(const moe_config *cfg, const moe_layer *layer, const
  * the int8 format, as moe_layer_forward_shared_i8 is to moe_layer_forward:
  * the routed experts are grouped and read once as in the union path, the
  * int8 expert *shared8 (host struct, expert 0 of its stacks) is read once
- * for all S tokens (its gate/up and down each one launch whose waves own
- * weight rows and walk the tokens), its results are staged as the shared
- * slot, and the per-token combine adds it last.  Returns the bits of
+ * for all S tokens (its gate/up and down each one launch on the int8 matrix
+ * cores, the same int32 sums as the per-token path), its results are staged
+ * as the shared slot, and the per-token combine adds it last.  Returns the bits of
  * moe_layer_forward_shared_i8 for the same inputs.  cfg->n_shared must be 1
  * (MOE_ESHAPE); flags: MOE_F_ACCUMULATE only; layer->shared is not read.
  * Workspace: moe_workspace_bytes(cfg, S, 1). */
