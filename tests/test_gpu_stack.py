@@ -70,6 +70,26 @@ def _check_layers(stack, taps, x_final, check, union):
         del L
 
 
+def _check_all_layers_gpu(stack, taps, x_final):
+    """Every layer, on the GPU alone: the stack's update equals x + block(RMSNorm(x))
+    from separate calls, and the per-token and union paths give the same bits."""
+    S = taps[0].shape[0]
+    nl = len(stack.layers)
+    ws_f = moe.Workspace(stack.cfg, S, moe.WS_FORWARD)
+    ws_b = moe.Workspace(stack.cfg, S, moe.WS_BATCH)
+    for l in range(nl):
+        x_in = taps[l]
+        x_next = taps[l + 1] if l + 1 < nl else x_final
+        xn = moe.moe_rmsnorm(x_in, stack.gamma, EPS)
+        out_f = moe.moe_layer_forward(stack.layers[l], xn, ws_f)
+        out_b = moe.moe_layer_forward_batch(stack.layers[l], xn, ws_b)
+        torch.cuda.synchronize()
+        of, ob = to_np(out_f), to_np(out_b)
+        assert np.array_equal(of.view(np.uint32), ob.view(np.uint32)), f"layer {l}: union != per-token"
+        assert np.array_equal(to_np(x_next).view(np.uint32), (to_np(x_in) + of).view(np.uint32)), \
+            f"layer {l}: residual update differs"
+
+
 @pytest.mark.parametrize("S,union", [(1, False), (4, True)])
 def test_stack_3_layers(S, union):
     _free()
@@ -87,7 +107,8 @@ def test_stack_3_layers(S, union):
 def test_stack_48_layers_resident():
     """The whole 48-layer stack resident in HBM (about 233 GB of int4
     experts); a decode step of one token and one of four tokens (union path)
-    through all layers, checked at sampled layers."""
+    through all layers: every layer checked on the GPU (update = x + block,
+    union == per-token bit for bit), layers 0, 23 and 47 against the oracle."""
     _free()
     say("building 48 GLM-shape layers")
     stack = _build(48)
@@ -99,6 +120,7 @@ def test_stack_48_layers_resident():
         stack.forward(x, ws, union=union, taps=taps)
         torch.cuda.synchronize()
         assert np.isfinite(to_np(x)).all()
+        _check_all_layers_gpu(stack, taps, x)
         _check_layers(stack, taps, x, (0, 23, 47), union)
     del stack
     _free()
