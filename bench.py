@@ -593,7 +593,9 @@ def bench_shared_i8(layers, x, steps: int = 512):
     (moe_layer_forward_shared_i8): the headline decode's cold layer replicas
     and tokens, each replica with its own int8 shared expert; plain stream
     launches between events.  Weight bytes per token: the router, 8 int4
-    routed experts and one int8 shared expert."""
+    routed experts and one int8 shared expert.  Then the union path with the
+    int8 shared expert (moe_layer_forward_batch_shared_i8), timed cold: the
+    64-token Zipf verify and the 2048-token prefill (uniform routing)."""
     import torch
 
     import int4_expert_gemv_moe_amd as moe
@@ -667,6 +669,28 @@ def bench_shared_i8(layers, x, steps: int = 512):
                              "GBps": round(vb / vus / 1e3, 1),
                              "frac_of_hbm_peak": round(vb / vus / 1e3 / HBM_PEAK_GBPS, 4)}
     log(f"verify 64 with int8 shared expert: {vus:.1f} us cold")
+    # the 2048-token prefill (uniform routing, float32 rows) with the int8 shared expert
+    S = 2048
+    xp_np = synth.bf16_to_f32(synth.bf16_bits(synth.activations(5, S, D)))
+    zu = moe.DeviceLayer(cfg, layers[0].router_w, torch.zeros(E, dtype=torch.float32, device="cuda"),
+                         layers[0].routed, layers[0].shared)
+    xpf = torch.from_numpy(xp_np).cuda()
+    wsp = moe.Workspace(cfg, S, moe.WS_BATCH)
+    outp = torch.empty(S, D, dtype=torch.float32, device="cuda")
+    callp = lambda: moe.moe_layer_forward_shared_i8(zu, views[0], xpf, wsp, out=outp,
+                                                    fn_name="moe_layer_forward_batch_shared_i8")
+    callp()
+    idxp, _, _ = moe.moe_router_topk(cfg, xpf, zu.router_w, zu.router_b,
+                                     moe.Workspace(cfg, S, moe.WS_ROUTER))
+    torch.cuda.synchronize()
+    usedp = int(np.unique(idxp.cpu().numpy()).size)
+    coldp = timed_cold(callp, 10)
+    pus = float(np.median(coldp))
+    pb = usedp * EXPERT_BYTES + EXPERT_I8_BYTES + ROUTER_BYTES + 2 * S * D * 4
+    res["prefill2048_union"] = {"us": round(pus, 1), "us_spread": spread(coldp),
+                                "union_routed_experts": usedp, "hbm_bytes": pb,
+                                "GBps": round(pb / pus / 1e3, 1)}
+    log(f"prefill 2048 with int8 shared expert: {pus:.1f} us cold")
     return res
 
 
