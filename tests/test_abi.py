@@ -318,6 +318,16 @@ def test_shared_i8_layer_host_checks():
     assert call(cfg, ctypes.byref(e8), a, 2, need) == -1      # PRENORM is not supported
     assert call(cfg, ctypes.byref(e8), a + 4, 0, need) == -3  # x misaligned
     assert call(cfg, ctypes.byref(e8), a, 0, need - 16) == -4
+    # the union variant: the same checks against the union workspace
+    need_b = L.moe_workspace_bytes(ctypes.byref(cfg), 2, moe.WS_BATCH)
+    callb = lambda c, e, x, flags, ws_bytes: L.moe_layer_forward_batch_shared_i8(
+        ctypes.byref(c), ctypes.byref(layer), e, x, 2, out, flags, a, ws_bytes, None)
+    assert callb(moe.config(256, 128, 8, 2, n_shared=0), ctypes.byref(e8), a, 0, need_b) == -2
+    assert callb(cfg, None, a, 0, need_b) == -1                      # no int8 shared expert
+    assert callb(cfg, ctypes.byref(e8), a, moe.F_PRENORM, need_b) == -1  # only MOE_F_ACCUMULATE
+    assert callb(cfg, ctypes.byref(e8), a, moe.F_X_BF16, need_b) == -1
+    assert callb(cfg, ctypes.byref(e8), a + 4, 0, need_b) == -3      # x misaligned
+    assert callb(cfg, ctypes.byref(e8), a, 0, need_b - 16) == -4
 
 
 def test_noalloc_entry_point_refuses_oversize_calls_on_the_host():
