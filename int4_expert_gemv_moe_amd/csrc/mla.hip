@@ -245,11 +245,19 @@ bool mla_mfma_fits(int kvl, int rope, const float *L, const float *R) {
   return al && rope % 4 == 0 && kvl + (rope + 15) / 16 * 16 <= kMlaMK;
 }
 
-// Splits per query: 16-row steps, up to 128 splits, about 512 workgroups.
+// Splits per query (16-row steps): at most kMlaMaxSplit and about 512
+// workgroups (hi), and between that and about 256 workgroups (lo) as few as
+// leave every split four steps.  Swept at the GLM shape (64 heads, one
+// query): 1024 rows 64 splits 25.1 us (16 or 32 splits 30.1, 26.1); 4096
+// rows 64 splits 31.8-32.1 us (128: 34.1); 16384 rows 128 splits 54.3 us
+// (64: 58.1).
 int mla_mfma_splits(int S, int T, int H) {
   const int groups = (H + kMlaMH - 1) / kMlaMH;
-  const int target = std::max(1, 512 / std::max(1, S * groups));
-  return std::max(1, std::min(std::min(kMlaMaxSplit, (T + kMlaMR - 1) / kMlaMR), target));
+  const int sg = std::max(1, S * groups);
+  const int one_step = (T + kMlaMR - 1) / kMlaMR, four_steps = (T + 4 * kMlaMR - 1) / (4 * kMlaMR);
+  const int hi = std::max(1, std::min(std::min(kMlaMaxSplit, one_step), 512 / sg));
+  const int lo = std::max(1, std::min(hi, 256 / sg));
+  return std::max(lo, std::min(hi, four_steps));
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
