@@ -158,111 +158,82 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
   }
 }
 
-// Many tokens: a register tile per wave, TT tokens x EE experts, so each
-// loaded x vector serves EE experts and each weight vector TT tokens.  Block
-// = TG x 4 waves over TG * TT tokens and 4 * EE consecutive experts.  Every logit
-// is still lane p's ascending FMA chain over k = 4p + 256j + q followed by
-// wave_sum_f32, i.e. the same bits as router_kernel.  The operands of step
-// j + 1 are loaded while step j is multiplied.
-template <int TT, int EE, int TG, bool XB = false>
-__global__ __launch_bounds__(256 * TG) void router_tile_kernel(RouterArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int neb = (a.E + 4 * EE - 1) / (4 * EE);
-  const int n_router = neb * ((a.S + TG * TT - 1) / (TG * TT));
-  if ((int)blockIdx.x >= n_router) {
-    const int s = blockIdx.x - n_router;
-    if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
-    quant_row_block(XB ? nullptr : a.x + (int64_t)s * a.D, XB ? a.xb + (int64_t)s * a.D : nullptr,
-                    a.D, a.xq_perm + (int64_t)s * a.D, nullptr, a.sx + s, a.sumx + s);
-    return;
+// Lane partner l ^ MASK of every lane, for a value in each lane.
+template <int MASK>
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (MASK == 1) {
+    return dpp_f<MOE_DPP_QUAD_X1>(v);
+  } else if constexpr (MASK == 2) {
+    return dpp_f<MOE_DPP_QUAD_X2>(v);
+  } else if constexpr (MASK == 4 || MASK == 8) {
+    // lanes with the bit clear read lane + MASK (row shift left), the others
+    // lane - MASK (row shift right); the bank masks pick the 4-lane groups
+    constexpr int clear = MASK == 4 ? 0x5 : 0x3, set = MASK == 4 ? 0xA : 0xC;
+    const int x = __float_as_int(v);
+    int r = __builtin_amdgcn_update_dpp(0, x, 0x100 + MASK, 0xF, clear, false);
+    r = __builtin_amdgcn_update_dpp(r, x, 0x110 + MASK, 0xF, set, false);
+    return __int_as_float(r);
+  } else {
+    return __shfl_xor(v, MASK);
   }
-  // TG groups of 4 waves: group g takes tokens s0 + TT g .. +TT, wave w % 4
-  // of a group takes experts e0 + EE (w % 4) .. +EE; the groups share each
-  // weight vector through the cache
-  const int e0 = (blockIdx.x % neb) * 4 * EE + (wave & 3) * EE;
-  const int s0 = (blockIdx.x / neb) * TG * TT + (wave >> 2) * TT;
-  if (e0 >= a.E || s0 >= a.S) return;
-  const float4 *wr[EE];
-  int64_t xs[TT];  // token rows (clamped)
-#pragma unroll
-  for (int t = 0; t < TT; t++) xs[t] = min(s0 + t, a.S - 1);
-  const float *xbase = XB ? nullptr : a.x;
-#pragma unroll
-  for (int e = 0; e < EE; e++)
-    wr[e] = reinterpret_cast<const float4 *>(a.W + (int64_t)min(e0 + e, a.E - 1) * a.D) + lane;
-  float acc[TT][EE];
-#pragma unroll
-  for (int t = 0; t < TT; t++)
-#pragma unroll
-    for (int e = 0; e < EE; e++) acc[t][e] = 0.f;
-  const int nj = a.D >> 8;
-  float4 xv[TT], wv[EE];
-#pragma unroll
-  for (int t = 0; t < TT; t++) xv[t] = ldx4<XB>(a, XB ? nullptr : xbase + xs[t] * a.D, xs[t], lane);
-#pragma unroll
-  for (int e = 0; e < EE; e++) wv[e] = wr[e][0];
-  for (int j = 0; j < nj; j++) {
-    const int jn = min(j + 1, nj - 1) * 64;
-    float4 xn[TT], wn[EE];
-#pragma unroll
-    for (int t = 0; t < TT; t++)
-      xn[t] = ldx4<XB>(a, XB ? nullptr : xbase + xs[t] * a.D, xs[t], lane + jn);
-#pragma unroll
-    for (int e = 0; e < EE; e++) wn[e] = wr[e][jn];
-#pragma unroll
-    for (int t = 0; t < TT; t++)
-#pragma unroll
-      for (int e = 0; e < EE; e++) {
-        float c = acc[t][e];
-        c = fmaf(xv[t].x, wv[e].x, c);
-        c = fmaf(xv[t].y, wv[e].y, c);
-        c = fmaf(xv[t].z, wv[e].z, c);
-        c = fmaf(xv[t].w, wv[e].w, c);
-        acc[t][e] = c;
-      }
-#pragma unroll
-    for (int t = 0; t < TT; t++) xv[t] = xn[t];
-#pragma unroll
-    for (int e = 0; e < EE; e++) wv[e] = wn[e];
-  }
-#pragma unroll
-  for (int t = 0; t < TT; t++)
-#pragma unroll
-    for (int e = 0; e < EE; e++) {
-      const float v = wave_sum_f32(acc[t][e]);
-      if (lane == 0 && s0 + t < a.S && e0 + e < a.E) {
-        a.logits[(int64_t)(s0 + t) * a.E + e0 + e] = v;
-        if (a.logits_out) a.logits_out[(int64_t)(s0 + t) * a.E + e0 + e] = v;
-      }
-    }
 }
 
-// Mid-size batches: a workgroup of 4 waves over 8 tokens x 8 experts, each
-// wave a 4 x 4 register tile of logits (wave w: tokens 4 (w / 2) .., experts
-// 4 (w % 2) ..), with the step's 8 token rows and 8 weight rows copied into
-// shared memory once per workgroup
-// (global_load_lds_dwordx4, a three-stage ring, two steps of 256 columns
-// requested ahead) instead of once per wave.  Every logit is lane p's
-// ascending FMA chain over k = 4p + 256j + q followed by wave_sum_f32: the
-// same bits as router_kernel.
-constexpr int kRmT = 8, kRmE = 8;  // tokens and experts of a workgroup
+// Wave sums of N values per lane at once.  Step L adds lane l and lane
+// l ^ 2^L, as wave_sum_f32 does (its half-row and row mirrors pair the same
+// groups of 4 and 8 lanes, whose lanes hold equal bits by then), so every
+// sum has wave_sum_f32's bits.  While a lane holds more than one value, step
+// L keeps half of them: lanes with bit L set keep the upper half and send
+// the lower half to their partner, the others the reverse.  On return v[0]
+// of lane l is the sum of value m, m the low log2(N) bits of l reversed.
+template <int L, int N>
+__device__ __forceinline__ void wave_sum_many(float (&v)[N], int lane) {
+  constexpr int MASK = 1 << L, n = N >> L;
+  if constexpr (n > 1) {
+    const bool up = (lane & MASK) != 0;
+#pragma unroll
+    for (int k = 0; k < n / 2; k++) {
+      const float send = up ? v[k] : v[k + n / 2];
+      const float keep = up ? v[k + n / 2] : v[k];
+      v[k] = keep + xor_lane<MASK>(send);
+    }
+  } else {
+    v[0] = v[0] + xor_lane<MASK>(v[0]);
+  }
+  if constexpr (L < 5) wave_sum_many<L + 1, N>(v, lane);
+}
 
-template <bool XB>
-struct RouterMid {
-  static constexpr int XR = XB ? 512 : 1024;             // shared bytes of a token row per step
-  static constexpr int XI = kRmT * XR / 1024;            // token-row requests per step
-  static constexpr int PIECES = (XI + kRmE) / 4;         // per wave and step (4, or 3 with bf16)
-  static constexpr int STAGE = kRmT * XR + kRmE * 1024;  // shared bytes of a stage
+// Batches through shared memory: a workgroup of 4 waves over 2TT tokens x
+// 2TT experts, each wave a TT x TT register tile of logits (wave w: tokens
+// TT (w / 2) .., experts TT (w % 2) ..), with the step's token rows and
+// weight rows copied into shared memory once per workgroup
+// (global_load_lds_dwordx4 into a ring of stages, steps of 256 columns
+// requested ahead) instead of once per wave.  Every logit is lane p's
+// ascending FMA chain over k = 4p + 256j + q followed by the additions of
+// wave_sum_f32 (all TT x TT at once through wave_sum_many): the same bits as
+// router_kernel.
+template <bool XB, int TT>
+struct RouterShared {
+  static constexpr int T = 2 * TT, E = 2 * TT;      // tokens and experts of a workgroup
+  static constexpr int XR = XB ? 512 : 1024;        // shared bytes of a token row per step
+  static constexpr int XI = T * XR / 1024;          // token-row requests per step
+  static constexpr int PIECES = (XI + E) / 4;       // per wave and step
+  static constexpr int STAGE = T * XR + E * 1024;   // shared bytes of a stage
+  static_assert((XI + E) % 4 == 0, "requests per wave");
 };
 
-template <bool XB>
-__global__ __launch_bounds__(256) void router_mid_kernel(RouterArgs a) {
-  using R = RouterMid<XB>;
-  static_assert((R::XI + kRmE) % 4 == 0, "requests per wave");
-  __shared__ __align__(1024) int8_t S0[R::STAGE], S1[R::STAGE], S2[R::STAGE];
+// NS stages in the ring (NS - 1 steps requested ahead); WPE caps the
+// registers so that WPE waves fit on a SIMD.
+template <bool XB, int TT, int NS, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
+void router_shared_kernel(RouterArgs a) {
+  using R = RouterShared<XB, TT>;
+  static_assert(NS >= 2 && NS <= 6 && R::PIECES * (NS - 2) < 16, "ring stages");
+  constexpr int SZ = R::STAGE;
+  __shared__ __align__(1024) int8_t S0[SZ], S1[SZ], S2[NS > 2 ? SZ : 16], S3[NS > 3 ? SZ : 16],
+      S4[NS > 4 ? SZ : 16], S5[NS > 5 ? SZ : 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int neb = (a.E + kRmE - 1) / kRmE;
-  const int n_router = neb * ((a.S + kRmT - 1) / kRmT);
+  const int neb = (a.E + R::E - 1) / R::E;
+  const int n_router = neb * ((a.S + R::T - 1) / R::T);
   if ((int)blockIdx.x >= n_router) {
     const int s = blockIdx.x - n_router;
     if (a.amax && threadIdx.x < a.P) a.amax[(int64_t)s * a.P + threadIdx.x] = 0u;
@@ -270,7 +241,7 @@ __global__ __launch_bounds__(256) void router_mid_kernel(RouterArgs a) {
                     a.D, a.xq_perm + (int64_t)s * a.D, nullptr, a.sx + s, a.sumx + s);
     return;
   }
-  const int eb = (blockIdx.x % neb) * kRmE, sb = (blockIdx.x / neb) * kRmT;
+  const int eb = (blockIdx.x % neb) * R::E, sb = (blockIdx.x / neb) * R::T;
   // request n = PIECES wave + u of a step: n < XI token rows (XR bytes each,
   // 1024 / XR rows per request), otherwise weight row n - XI; lane l copies
   // bytes 16 (l % (XR / 16)) of its row
@@ -292,13 +263,13 @@ __global__ __launch_bounds__(256) void router_mid_kernel(RouterArgs a) {
       const int erow = min(eb + r, a.E - 1);
       src[u] = reinterpret_cast<const int8_t *>(a.W) + (int64_t)erow * a.D * 4 + 16 * lane;
       step_bytes[u] = 1024;
-      dst[u] = kRmT * R::XR + 1024 * r;
+      dst[u] = R::T * R::XR + 1024 * r;
     }
   }
   const int nj = a.D >> 8;
   auto stage = [&](auto bc) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
-    return B == 0 ? S0 : (B == 1 ? S1 : S2);
+    return B == 0 ? S0 : B == 1 ? S1 : B == 2 ? S2 : B == 3 ? S3 : B == 4 ? S4 : S5;
   };
   auto issue = [&](int j, auto bc) __attribute__((always_inline)) {
     const int jj = min(j, nj - 1);
@@ -307,22 +278,28 @@ __global__ __launch_bounds__(256) void router_mid_kernel(RouterArgs a) {
     for (int u = 0; u < R::PIECES; u++) dma16(src[u] + (int64_t)jj * step_bytes[u], st + dst[u]);
   };
   const int tg = wave >> 1, eg = wave & 1;
-  float acc[4][4];
+  float acc[TT][TT];
 #pragma unroll
-  for (int t = 0; t < 4; t++)
+  for (int t = 0; t < TT; t++)
 #pragma unroll
-    for (int e = 0; e < 4; e++) acc[t][e] = 0.f;
+    for (int e = 0; e < TT; e++) acc[t][e] = 0.f;
+  // steps 0 .. NS - 2 requested ahead; step j waits for its own pieces (the
+  // NS - 2 later steps stay in flight), then requests step j + NS - 1 into
+  // the stage step j - 1 read
   issue(0, std::integral_constant<int, 0>{});
-  issue(1, std::integral_constant<int, 1>{});
+  if constexpr (NS > 2) issue(1, std::integral_constant<int, 1>{});
+  if constexpr (NS > 3) issue(2, std::integral_constant<int, 2>{});
+  if constexpr (NS > 4) issue(3, std::integral_constant<int, 3>{});
+  if constexpr (NS > 5) issue(4, std::integral_constant<int, 4>{});
   auto step = [&](int j, auto bc) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
-    dma_step_barrier<R::PIECES>();
-    issue(j + 2, std::integral_constant<int, (B + 2) % 3>{});
+    dma_step_barrier<R::PIECES * (NS - 2)>();
+    issue(j + NS - 1, std::integral_constant<int, (B + NS - 1) % NS>{});
     const int8_t *st = stage(bc);
-    float4 xv[4], wv[4];
+    float4 xv[TT], wv[TT];
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      const int8_t *row = st + (4 * tg + t) * R::XR;
+    for (int t = 0; t < TT; t++) {
+      const int8_t *row = st + (TT * tg + t) * R::XR;
       if constexpr (XB) {
         const uint2 w = reinterpret_cast<const uint2 *>(row)[lane];
         xv[t] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
@@ -332,12 +309,12 @@ __global__ __launch_bounds__(256) void router_mid_kernel(RouterArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; e++)
-      wv[e] = reinterpret_cast<const float4 *>(st + kRmT * R::XR + (4 * eg + e) * 1024)[lane];
+    for (int e = 0; e < TT; e++)
+      wv[e] = reinterpret_cast<const float4 *>(st + R::T * R::XR + (TT * eg + e) * 1024)[lane];
 #pragma unroll
-    for (int t = 0; t < 4; t++)
+    for (int t = 0; t < TT; t++)
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
+      for (int e = 0; e < TT; e++) {
         float c = acc[t][e];
         c = fmaf(xv[t].x, wv[e].x, c);
         c = fmaf(xv[t].y, wv[e].y, c);
@@ -346,28 +323,37 @@ __global__ __launch_bounds__(256) void router_mid_kernel(RouterArgs a) {
         acc[t][e] = c;
       }
   };
+  // NS steps per turn of the ring, then the rest (fewer than NS)
+  auto steps = [&](int j, int n) __attribute__((always_inline)) {
+    if (n > 0) step(j, std::integral_constant<int, 0>{});
+    if (n > 1) step(j + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS > 2) if (n > 2) step(j + 2, std::integral_constant<int, 2 % NS>{});
+    if constexpr (NS > 3) if (n > 3) step(j + 3, std::integral_constant<int, 3 % NS>{});
+    if constexpr (NS > 4) if (n > 4) step(j + 4, std::integral_constant<int, 4 % NS>{});
+    if constexpr (NS > 5) if (n > 5) step(j + 5, std::integral_constant<int, 5 % NS>{});
+  };
   int j = 0;
-  for (; j + 2 < nj; j += 3) {
-    step(j, std::integral_constant<int, 0>{});
-    step(j + 1, std::integral_constant<int, 1>{});
-    step(j + 2, std::integral_constant<int, 2>{});
-  }
-  if (j < nj) step(j, std::integral_constant<int, 0>{});
-  if (j + 1 < nj) step(j + 1, std::integral_constant<int, 1>{});
+  for (; j + NS <= nj; j += NS) steps(j, NS);
+  steps(j, nj - j);
   // the last requests (repeats of the last step) land in stages no step
   // reads; none may still be in flight when the workgroup ends
   wait_vm_at_most<0>();
-  const int s0 = sb + 4 * tg, e0 = eb + 4 * eg;
+  const int s0 = sb + TT * tg, e0 = eb + TT * eg;
+  // all TT x TT wave sums at once; lane l then holds logit m (token m / TT,
+  // expert m % TT of the wave's tile)
+  constexpr int N = TT * TT, LOGN = TT == 8 ? 6 : 4;
+  float v[N];
 #pragma unroll
-  for (int t = 0; t < 4; t++)
+  for (int t = 0; t < TT; t++)
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const float v = wave_sum_f32(acc[t][e]);
-      if (lane == 0 && s0 + t < a.S && e0 + e < a.E) {
-        a.logits[(int64_t)(s0 + t) * a.E + e0 + e] = v;
-        if (a.logits_out) a.logits_out[(int64_t)(s0 + t) * a.E + e0 + e] = v;
-      }
-    }
+    for (int e = 0; e < TT; e++) v[t * TT + e] = acc[t][e];
+  wave_sum_many<0, N>(v, lane);
+  const int m = (int)(__builtin_bitreverse32((uint32_t)lane) >> (32 - LOGN));
+  const int s = s0 + m / TT, e = e0 + m % TT;
+  if (lane < N && s < a.S && e < a.E) {
+    a.logits[(int64_t)s * a.E + e] = v[0];
+    if (a.logits_out) a.logits_out[(int64_t)s * a.E + e] = v[0];
+  }
 }
 
 }  // namespace moe
@@ -384,7 +370,7 @@ hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
   const int nq = with_quant ? a.S : 0;
   // a few tokens: one token per wave, the whole weight row in one batch of
   // loads (rows are re-read per token from L2); up to 255: 8 x 8 tiles staged
-  // in shared memory; more: 8 x 8 register tiles per wave
+  // in shared memory; more: 16 x 16 tiles staged in shared memory
   const bool xb = a.xb != nullptr;  // bf16 tokens (no RMSNorm with them)
   if (a.S <= 8) {
     const size_t lds = a.gamma ? (size_t)a.D * 4 : 0;  // the normalized row
@@ -393,23 +379,24 @@ hipError_t launch_router(const RouterArgs &a, bool with_quant, hipStream_t st) {
     else
       hipLaunchKernelGGL((router_kernel<1, 24>), dim3(ne4 * a.S + nq), dim3(256), lds, st, a);
   } else if (a.S < kRouterTileMinTokens) {
-    // 8 tokens x 8 experts per workgroup through shared memory (against the
-    // 4 x 4 register tiles of router_tile_kernel, 4 tokens x 16 experts per
-    // workgroup: 14.0 against 20.5 us at 64 tokens)
-    const dim3 grid(((a.E + kRmE - 1) / kRmE) * ((a.S + kRmT - 1) / kRmT) + nq);
+    // 8 tokens x 8 experts per workgroup, 4 x 4 logits per wave, three stages
+    const dim3 grid(((a.E + 7) / 8) * ((a.S + 7) / 8) + nq);
     if (xb)
-      hipLaunchKernelGGL((router_mid_kernel<true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((router_shared_kernel<true, 4, 3, 1>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((router_mid_kernel<false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((router_shared_kernel<false, 4, 3, 1>), grid, dim3(256), 0, st, a);
   } else {
-    // 4-wave workgroups of 8 tokens x 32 experts (swept against 8-wave
-    // workgroups of 16 x 32 and other tiles: 188 against 209 us at 2048 tokens)
-    const int neb = (a.E + 31) / 32;
-    const dim3 grid(neb * ((a.S + 7) / 8) + nq);
+    // 16 tokens x 16 experts per workgroup, 8 x 8 logits per wave, two
+    // stages (48 KB with bf16 rows) and at most 168 registers, so three
+    // workgroups share a CU (two with float32 rows, 64 KB).  2048 bf16
+    // tokens: 136 us, against 147 with one wave sum at a time, 175 with
+    // three stages and 189 with 8 x 8 register tiles loaded by every wave
+    // for itself
+    const dim3 grid(((a.E + 15) / 16) * ((a.S + 15) / 16) + nq);
     if (xb)
-      hipLaunchKernelGGL((router_tile_kernel<8, 8, 1, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((router_shared_kernel<true, 8, 2, 3>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((router_tile_kernel<8, 8, 1>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((router_shared_kernel<false, 8, 2, 3>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -78,11 +78,14 @@ def test_quant_bf16_and_degenerate_rows():
 
 # the router's launch shapes: up to 8 tokens, 9 to 255 (8 x 8 tiles through
 # shared memory; 37 experts and 29 tokens leave both tile edges ragged), and
-# 256 and more (8 x 8 register tiles)
+# 256 and more (16 x 16 tiles through shared memory; 37 experts and 301
+# tokens leave both edges ragged, and 512 columns are fewer steps than the
+# ring has stages)
 @pytest.mark.parametrize("shape,S,bias", [(TINY, 4, "uniform"), (GLM, 1, "uniform"),
                                           (GLM, 64, "uniform"), (GLM, 200, "zero"),
                                           (synth.Shape(D=512, I=64, E=37, K=4), 29, "uniform"),
-                                          (GLM, 300, "uniform")])
+                                          (GLM, 300, "uniform"),
+                                          (synth.Shape(D=512, I=64, E=37, K=4), 301, "uniform")])
 def test_router_topk(shape, S, bias):
     say(f"router D={shape.D} E={shape.E} S={S}")
     cfg_o = config_of(shape)
@@ -105,8 +108,8 @@ def test_router_topk(shape, S, bias):
 @pytest.mark.parametrize("S", [37, 301, 2048])
 def test_router_batch_invariance(S):
     # a token's routing does not depend on the batch it is in (37 tokens: the
-    # 8 x 8 tiles through shared memory with a ragged last tile; 301: the 8 x 8
-    # register tiles with a ragged last tile; 2048: the prefill batch)
+    # 8 x 8 tiles through shared memory with a ragged last tile; 301: the
+    # 16 x 16 tiles with a ragged last tile; 2048: the prefill batch)
     shape = GLM
     cfg = moe.config(shape.D, shape.I, shape.E, shape.K)
     wr = torch.from_numpy(synth.router_w(2, shape)).cuda()
