@@ -73,97 +73,111 @@ __global__ __launch_bounds__(256) void requant_kernel(RequantArgs a) {
                     a.sumh + r);
 }
 
+// Exclusive prefix sums over up to 2048 slots in a workgroup of 1024 threads:
+// thread t holds the values of slots 2t and 2t + 1 and receives their
+// offsets; every wave scans its 128 slots at once (shuffles), then adds the
+// totals of the waves before it.  Returns the total to every thread.
+__device__ __forceinline__ int scan_2048(int v0, int v1, int *wtot, int &e0, int &e1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int two = v0 + v1;
+  int incl = two;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; w++) {
+    const int x = wtot[w];
+    before += w < wave ? x : 0;
+    total += x;
+  }
+  e0 = before + incl - two;
+  e1 = e0 + v0;
+  __syncthreads();  // wtot may be reused
+  return total;
+}
+
 // One block of 1024 threads: (optionally the top-K of every token, then) a
 // counting sort of the S*K routed pairs by expert, plus the shared expert as
 // group E holding every token.  The order of pairs
 // inside a group is whatever the shared-memory atomics produce; it does not
-// affect any result, because each pair is computed on its own.
+// affect any result, because each pair is computed on its own.  Each thread
+// requests the expert ids of up to 8 pairs before it counts or places them,
+// so the global loads overlap.
 __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
-  __shared__ int cnt[1025];
-  __shared__ int fill[1025];
-  __shared__ int off[1026];
+  constexpr int U = 8;  // pairs per thread and round
+  __shared__ int cnt[2048];
+  __shared__ int fill[2048];
+  __shared__ int off[2048];
+  __shared__ int wtot[16];
   const int G = a.E + 1;  // group E is the shared expert (empty without one)
+  const int t = threadIdx.x;
   if (a.with_topk) {
     // the tokens' selections (E <= 256), one wave per token; the writes are
     // visible to the whole workgroup after the barrier below
-    for (int s = threadIdx.x >> 6; s < a.S; s += blockDim.x >> 6)
+    for (int s = t >> 6; s < a.S; s += blockDim.x >> 6)
       topk_rounds_m<4>(a.logits + (int64_t)s * a.E, a.bias, a.E, a.K, a.scale,
                        a.idx + (int64_t)s * a.K, a.wts + (int64_t)s * a.K, nullptr, a.topp,
                        a.keff ? a.keff + s : nullptr);
   }
-  for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    cnt[g] = 0;
-    fill[g] = 0;
-  }
+  cnt[2 * t] = cnt[2 * t + 1] = 0;
+  fill[2 * t] = fill[2 * t + 1] = 0;
   __syncthreads();
   const int np = a.S * a.K;
-  // pairs past a token's keff (adaptive top-p) are not grouped
-  auto kept = [&](int p) { return !a.use_keff || (p % a.K) < a.keff[p / a.K]; };
-  // expert ids (the caller's, when the routing is given) kept inside [0, E)
-  auto expert = [&](int p) { return min(max((int)a.idx[p], 0), a.E - 1); };
-  for (int p = threadIdx.x; p < np; p += blockDim.x)
-    if (kept(p)) atomicAdd(&cnt[expert(p)], 1);
-  if (threadIdx.x == 0) cnt[a.E] = a.n_shared ? a.S : 0;
-  __syncthreads();
-  // exclusive scan over G <= 1025 counts: each wave scans a 64-wide slice in
-  // turn after the slices before it are done
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int carry = 0;
-    for (int base = 0; base < G; base += 64) {
-      const int g = base + lane;
-      int v = (g < G) ? cnt[g] : 0;
-      int incl = v;
+  // the expert of pair p (kept inside [0, E)), or -1 for a pair past its
+  // token's keff (adaptive top-p) or past the end
+  auto expert = [&](int p) {
+    if (p >= np || (a.use_keff && (p % a.K) >= a.keff[p / a.K])) return -1;
+    return min(max((int)a.idx[p], 0), a.E - 1);
+  };
+  for (int p0 = t; p0 < np; p0 += U * 1024) {
+    int ex[U];
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        int t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-      }
-      if (g < G) off[g] = carry + incl - v;
-      carry += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) off[G] = carry;
+    for (int u = 0; u < U; u++) ex[u] = expert(p0 + 1024 * u);
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (ex[u] >= 0) atomicAdd(&cnt[ex[u]], 1);
   }
+  if (t == 0) cnt[a.E] = a.n_shared ? a.S : 0;
   __syncthreads();
-  for (int p = threadIdx.x; p < np; p += blockDim.x) {
-    if (!kept(p)) continue;
-    const int e = expert(p);
-    const int pos = off[e] + atomicAdd(&fill[e], 1);
-    a.pairs[pos] = (p / a.K) * a.P + (p % a.K);
+  int e0, e1;
+  const int np_kept = scan_2048(cnt[2 * t], cnt[2 * t + 1], wtot, e0, e1);
+  off[2 * t] = e0;
+  off[2 * t + 1] = e1;
+  __syncthreads();
+  for (int p0 = t; p0 < np; p0 += U * 1024) {
+    int ex[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) ex[u] = expert(p0 + 1024 * u);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (ex[u] < 0) continue;
+      const int p = p0 + 1024 * u;
+      const int pos = off[ex[u]] + atomicAdd(&fill[ex[u]], 1);
+      a.pairs[pos] = (p / a.K) * a.P + (p % a.K);
+    }
   }
   if (a.n_shared)
-    for (int s = threadIdx.x; s < a.S; s += blockDim.x) a.pairs[off[a.E] + s] = s * a.P + a.K;
-  for (int g = threadIdx.x; g <= G; g += blockDim.x) {
+    for (int s = t; s < a.S; s += blockDim.x) a.pairs[off[a.E] + s] = s * a.P + a.K;
+  for (int g = t; g <= G; g += blockDim.x) {
     if (g < G) a.gcount[g] = cnt[g];
-    a.goff[g] = off[g];
+    a.goff[g] = g < G ? off[g] : np_kept;
   }
   if (!a.tiles) return;
   // tiles of up to tile_rows pairs, groups in order: the same scan over the
   // tile counts of the groups
-  __syncthreads();
-  int *toff = fill;  // reuse: the fill counters are no longer needed
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int carry = 0;
-    for (int base = 0; base < G; base += 64) {
-      const int g = base + lane;
-      int v = (g < G) ? (cnt[g] + a.tile_rows - 1) / a.tile_rows : 0;
-      int incl = v;
+  auto ntile = [&](int g) { return g < G ? (cnt[g] + a.tile_rows - 1) / a.tile_rows : 0; };
+  const int total = scan_2048(ntile(2 * t), ntile(2 * t + 1), wtot, e0, e1);
+  if (t == 0) *a.ntiles = total;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        int t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-      }
-      if (g < G) toff[g] = carry + incl - v;
-      carry += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) *a.ntiles = carry;
-  }
-  __syncthreads();
-  for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    const int nt = (cnt[g] + a.tile_rows - 1) / a.tile_rows;
-    for (int t = 0; t < nt; t++) a.tiles[toff[g] + t] = make_int2(g, t * a.tile_rows);
+  for (int h = 0; h < 2; h++) {
+    const int g = 2 * t + h;
+    const int nt = ntile(g);
+    for (int i = 0; i < nt; i++) a.tiles[(h ? e1 : e0) + i] = make_int2(g, i * a.tile_rows);
   }
 }
 
