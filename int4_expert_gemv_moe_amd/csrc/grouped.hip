@@ -107,13 +107,17 @@ __device__ __forceinline__ int scan_2048(int v0, int v1, int *wtot, int &e0, int
 // inside a group is whatever the shared-memory atomics produce; it does not
 // affect any result, because each pair is computed on its own.  Each thread
 // requests the expert ids of up to 8 pairs before it counts or places them,
-// so the global loads overlap.
+// so the global loads overlap; a long list is assembled in shared memory
+// when it fits, so that it reaches global memory in coalesced stores.
+constexpr int kGroupStage = 24576;  // pairs the shared-memory list holds (96 KB)
+
 __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
   constexpr int U = 8;  // pairs per thread and round
   __shared__ int cnt[2048];
   __shared__ int fill[2048];
   __shared__ int off[2048];
   __shared__ int wtot[16];
+  __shared__ int pstage[kGroupStage];
   const int G = a.E + 1;  // group E is the shared expert (empty without one)
   const int t = threadIdx.x;
   if (a.with_topk) {
@@ -149,6 +153,14 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
   off[2 * t] = e0;
   off[2 * t + 1] = e1;
   __syncthreads();
+  // a long pair list is built in shared memory when it fits and then
+  // written out in order (2048 tokens: about 2 us less); short ones, and
+  // lists too long for it, are placed in global memory pair by pair
+  const bool staged = np_kept >= 4096 && np_kept <= kGroupStage;
+  auto place = [&](int pos, int v) {
+    if (staged) pstage[pos] = v;
+    else a.pairs[pos] = v;
+  };
   for (int p0 = t; p0 < np; p0 += U * 1024) {
     int ex[U];
 #pragma unroll
@@ -157,12 +169,15 @@ __global__ __launch_bounds__(1024) void group_kernel(GroupArgs a) {
     for (int u = 0; u < U; u++) {
       if (ex[u] < 0) continue;
       const int p = p0 + 1024 * u;
-      const int pos = off[ex[u]] + atomicAdd(&fill[ex[u]], 1);
-      a.pairs[pos] = (p / a.K) * a.P + (p % a.K);
+      place(off[ex[u]] + atomicAdd(&fill[ex[u]], 1), (p / a.K) * a.P + (p % a.K));
     }
   }
   if (a.n_shared)
-    for (int s = t; s < a.S; s += blockDim.x) a.pairs[off[a.E] + s] = s * a.P + a.K;
+    for (int s = t; s < a.S; s += blockDim.x) place(off[a.E] + s, s * a.P + a.K);
+  if (staged) {
+    __syncthreads();
+    for (int i = t; i < np_kept; i += blockDim.x) a.pairs[i] = pstage[i];
+  }
   for (int g = t; g <= G; g += blockDim.x) {
     if (g < G) a.gcount[g] = cnt[g];
     a.goff[g] = g < G ? off[g] : np_kept;

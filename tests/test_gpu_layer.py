@@ -80,7 +80,12 @@ def test_tiny_block(path):
                                           (synth.Shape(D=512, I=256, E=8, K=4), 255, "uniform"),
                                           # no shared expert, more than 64 tokens
                                           (synth.Shape(D=256, I=128, E=16, K=4, n_shared=0), 130,
-                                           "uniform")])
+                                           "uniform"),
+                                          # 4,500 pairs with the shared expert's: the
+                                          # grouping kernel assembles the list in shared
+                                          # memory; 25,200: more than that holds (24,576),
+                                          # so it places them one by one
+                                          (MID, 500, "uniform"), (MID, 2800, "uniform")])
 def test_batch_union_equals_per_token_bit_exact(shape, S, bias):
     b = bias_for(bias, 1, shape)
     dl = device_layer(1, shape, 0, b)
