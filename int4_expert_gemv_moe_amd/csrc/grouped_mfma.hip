@@ -11,10 +11,11 @@
 // group_kernel; a routed expert of a 2048-token prefill gets about 64 pairs,
 // so its weights are read once) times a chunk of output rows.  Each wave
 // owns 8 NS gate rows and the 8 NS up rows with the same indices (gate/up),
-// or 16 NS down rows, for all pairs of the tile.  Two kernels: up to 64
-// tokens grouped_mfma_kernel (operands staged through registers, NS = 2),
-// larger batches grouped_mfma_dma_kernel (operands copied into shared
-// memory by DMA, NS = 4); both 4-wave workgroups.
+// or 16 NS down rows, for all pairs of the tile.  Up to 64
+// tokens grouped_mfma_kernel (operands staged through registers, NS = 2,
+// 4-wave workgroups); larger batches operands copied into shared memory by
+// DMA, NS = 4: gate/up grouped_mfma_dma2_kernel (8-wave workgroups, weights
+// requested two steps at a time), down grouped_mfma_dma_kernel (4-wave).
 //
 // v_mfma_i32_16x16x64_i8 (layout checked on the device): lane l supplies row
 // l % 16 of A (a pair) and column l % 16 of B (an output row), each 16 int8
@@ -373,10 +374,10 @@ __global__ __launch_bounds__(NW * 64) void grouped_mfma_kernel(GroupedMfmaArgs a
 // Subtiles (16 pairs each) of the two launch shapes: batches of up to 64
 // tokens hold at most 4 per tile, larger batches at most 5.
 constexpr int kSmallMsv = 4, kLargeMsv = 5;
-// Larger batches: the shared-memory DMA kernel in 4-wave workgroups, two
-// per CU (measured against one 8-wave workgroup per CU and against the
-// register-staged grouped_mfma_kernel<.., 8, 4, 5>: the same gate/up time,
-// down 486 against 545 and 567 us at 2048 tokens), with whole tiles per XCD.
+// Larger batches, down: the shared-memory DMA kernel in 4-wave workgroups,
+// two per CU (measured against one 8-wave workgroup per CU and against the
+// register-staged grouped_mfma_kernel<.., 8, 4, 5>: down 486 against 545 and
+// 567 us at 2048 tokens), with whole tiles per XCD.
 constexpr int kPrefillDmaWaves = 4;
 constexpr bool kDmaXcdTiles = true;
 
@@ -644,6 +645,239 @@ void grouped_mfma_dma_kernel(GroupedMfmaArgs a) {
 #undef MOE_DMA_TILE
 }
 
+// ---- gate/up of large batches: 8-wave workgroups, 128-byte weight requests ----
+//
+// As grouped_mfma_dma_kernel<0, ..>, but one 8-wave workgroup per CU (8 x 64
+// weight rows, so the activation ring serves 512 rows) and the weights
+// requested two steps at a time: an instruction copies 8 rows x 128 bytes,
+// a whole cache line of each row, where the single-step kernel copies 16
+// rows x 64 bytes.  Weight ring: two double stages per wave (8 KB each);
+// activations: the three-stage ring of single steps.  Step t requests the
+// activations of step t + 2 and, when t is even, the weights of steps t + 2
+// and t + 3.
+// Layout of a wave's weight double stage: 64 rows x 128 bytes, row R (the
+// wave's row; subtile R / 16) at 128 R; piece q of row R holds logical piece
+// q ^ ((R >> 1) & 7), logical pieces 0-3 being the first step's 64 bytes.
+constexpr int kD2Waves = 8;
+constexpr int kD2BWave = 16 * kDNS * 128;  // weight bytes of a wave's double stage (8 KB)
+
+template <int NW, int MSVMAX, int MSV, int ABUF>
+__device__ __forceinline__ void dma2_tile(const GroupedMfmaArgs &a, const MfmaTile &t,
+                                          int8_t *A0, int8_t *A1, int8_t *A2, int8_t *W0,
+                                          int8_t *W1, const int *pr_l, const int *sum_l,
+                                          const float *scl_l) {
+  constexpr int NS = kDNS;
+  constexpr int NA = 2 * MSV;  // activation DMA instructions of a stage (8 rows x 128 bytes each)
+  constexpr int AW = dma_a_per_wave<NW, MSVMAX>();
+  constexpr int NWI = 2 * NS;  // weight DMA instructions of a double stage (8 rows each)
+  static_assert(AW + NWI < 16, "vmcnt field");
+  const int C = a.C, O = a.O;
+  const int lane = t.lane, j = t.j, rows = t.rows, wave = t.wave;
+  const int ln = lane & 15;
+  const int rowbytes = C >> 1;
+  // weights: instruction i covers the wave's rows 8 i .. 8 i + 7; lane: row
+  // 8 i + lane / 8, shared piece lane % 8
+  const uint8_t *bsrc[NWI];
+#pragma unroll
+  for (int i = 0; i < NWI; i++) {
+    const int R = 8 * i + (lane >> 3);
+    const int s = R >> 4;
+    const int o = t.ob[s] - ln + (R & 15);  // t.ob[s] is the output row of row ln of subtile s
+    const int p = (lane & 7) ^ ((R >> 1) & 7);
+    bsrc[i] = t.bbase[s] + (int64_t)min(o, O - 1) * rowbytes + 16 * p;
+  }
+  // activations: as in dma_tile
+  int asrc[AW], adst[AW];
+#pragma unroll
+  for (int u = 0; u < AW; u++) {
+    const int n = (wave + NW * u) % NA;
+    const int r = 8 * n + (lane >> 3);
+    const int apr = pr_l[min(r, rows - 1)];
+    const int p = (lane & 7) ^ ((r >> 1) & 7);
+    asrc[u] = (apr / a.P) * C + 16 * p;
+    adst[u] = 1024 * n;
+  }
+  const int nsteps = C / kDKS, ndouble = nsteps / 2;
+  auto stage_a = [&](auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    return B == 0 ? A0 : (B == 1 ? A1 : A2);
+  };
+  auto stage_w = [&](auto bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    return (B == 0 ? W0 : W1) + wave * kD2BWave;
+  };
+  auto issue_a = [&](int st, auto bc) __attribute__((always_inline)) {
+    const int k0 = min(st, nsteps - 1) * kDKS;
+    int8_t *ad = stage_a(bc);
+#pragma unroll
+    for (int u = 0; u < AW; u++) dma16(a.act + asrc[u] + k0, ad + adst[u]);
+  };
+  auto issue_w = [&](int d, auto bc) __attribute__((always_inline)) {
+    const int k = min(d, ndouble - 1) * 128;
+    int8_t *wd = stage_w(bc);
+#pragma unroll
+    for (int i = 0; i < NWI; i++) dma16(bsrc[i] + k, wd + 1024 * i);
+  };
+  v4i acc[MSV][NS];
+#pragma unroll
+  for (int ms = 0; ms < MSV; ms++)
+#pragma unroll
+    for (int s = 0; s < NS; s++) acc[ms][s] = v4i{0, 0, 0, 0};
+  float sc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; s++) sc[s] = t.Bm[s].s[min(t.ob[s], O - 1)];
+  const int bswz = (ln >> 1) & 7;
+  int aoff[2];
+#pragma unroll
+  for (int c = 0; c < 2; c++) aoff[c] = ln * kDARow + 16 * ((2 * j + c) ^ ((ln >> 1) & 7));
+
+  // as if steps -2 and -1 had run: activations of steps 0 and 1, weights of 0 and 1
+  issue_a(0, std::integral_constant<int, 0>{});
+  issue_w(0, std::integral_constant<int, 0>{});
+  issue_a(1, std::integral_constant<int, 1>{});
+  // K = st % 12 fixes the activation stage (st % 3), the weight double
+  // stage ((st / 2) % 2) and the half (st % 2)
+  auto step = [&](int st, auto kc) __attribute__((always_inline)) {
+    constexpr int K = decltype(kc)::value;
+    constexpr int AB = K % 3, WB = (K / 2) % 2, H = K % 2;
+    // in flight may stay what step st - 1 requested: activations, and on
+    // odd st the weights requested by the even step before
+    dma_step_barrier<H == 0 ? AW : AW + NWI>();
+    if constexpr (H == 0) issue_w(st / 2 + 1, std::integral_constant<int, (WB + 1) % 2>{});
+    issue_a(st + 2, std::integral_constant<int, (AB + 2) % 3>{});
+    const int8_t *bw = stage_w(std::integral_constant<int, WB>{}) + 128 * ln + 16 * ((4 * H + j) ^ bswz);
+    const int8_t *aw = stage_a(std::integral_constant<int, AB>{});
+    uint4 bm[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++) bm[s] = *reinterpret_cast<const uint4 *>(bw + 2048 * s);
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      v4i aa[MSV];
+#pragma unroll
+      for (int ms = 0; ms < MSV; ms++) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(aw + ms * 16 * kDARow + aoff[c]);
+        aa[ms] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+      }
+      v4i bb[NS];
+#pragma unroll
+      for (int s = 0; s < NS; s++) bb[s] = c ? unpack16(bm[s].z, bm[s].w) : unpack16(bm[s].x, bm[s].y);
+#pragma unroll
+      for (int ms = 0; ms < MSV; ms++)
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+          acc[ms][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[ms], bb[s], acc[ms][s], 0, 0, 0);
+    }
+    constexpr int PIECES = H == 0 ? AW + NWI : AW;
+    // the step's order as in dma_tile (the compiler's own: 847 against 835 us)
+    __builtin_amdgcn_sched_group_barrier(0x100, NS + 2, 0);  // shared-memory reads
+#pragma unroll
+    for (int g = 0; g < PIECES; g++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);     // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // global (DMA) request
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    constexpr int REST = 2 * MSV * NS - 3 * PIECES;
+    if constexpr (REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);
+  };
+  auto steps = [&](int st, int n) __attribute__((always_inline)) {
+    if (n > 0) step(st, std::integral_constant<int, 0>{});
+    if (n > 1) step(st + 1, std::integral_constant<int, 1>{});
+    if (n > 2) step(st + 2, std::integral_constant<int, 2>{});
+    if (n > 3) step(st + 3, std::integral_constant<int, 3>{});
+    if (n > 4) step(st + 4, std::integral_constant<int, 4>{});
+    if (n > 5) step(st + 5, std::integral_constant<int, 5>{});
+    if (n > 6) step(st + 6, std::integral_constant<int, 6>{});
+    if (n > 7) step(st + 7, std::integral_constant<int, 7>{});
+    if (n > 8) step(st + 8, std::integral_constant<int, 8>{});
+    if (n > 9) step(st + 9, std::integral_constant<int, 9>{});
+    if (n > 10) step(st + 10, std::integral_constant<int, 10>{});
+    if (n > 11) step(st + 11, std::integral_constant<int, 11>{});
+  };
+  int st = 0;
+  for (; st + 12 <= nsteps; st += 12) steps(st, 12);
+  steps(st, nsteps - st);
+  // the last requests (repeats of the last steps) land in stages no step
+  // reads; none may still be in flight when the workgroup ends
+  wait_vm_at_most<0>();
+
+#pragma unroll
+  for (int ms = 0; ms < MSV; ms++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 16 * ms + 4 * j + i;
+      if (r < rows) {
+        const int pr = pr_l[r];
+        const int corr = 8 * sum_l[r];
+        const float as = scl_l[r];
+#pragma unroll
+        for (int s = 0; s < NS / 2; s++) {
+          const int o = t.ob[s];
+          if (o < O) {
+            const float gv = ((float)(acc[ms][s][i] - corr) * sc[s]) * as;
+            const float uv = ((float)(acc[ms][s + NS / 2][i] - corr) * sc[s + NS / 2]) * as;
+            a.out[(int64_t)pr * O + o] = silu(gv) * uv;
+          }
+        }
+      }
+    }
+  }
+}
+
+// One 8-wave workgroup per CU (159 KB of shared memory), two waves per SIMD.
+template <int MSVMAX>
+__global__ __launch_bounds__(kD2Waves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void grouped_mfma_dma2_kernel(GroupedMfmaArgs a) {
+  constexpr int NW = kD2Waves, NS = kDNS;
+  constexpr int ABUF = 16 * MSVMAX * kDARow;
+  __shared__ __align__(1024) int8_t W0[NW * kD2BWave], W1[NW * kD2BWave];
+  __shared__ __align__(1024) int8_t A0[ABUF], A1[ABUF], A2[ABUF];
+  __shared__ int pr_l[16 * MSVMAX];
+  __shared__ int sum_l[16 * MSVMAX];
+  __shared__ float scl_l[16 * MSVMAX];
+  // whole tiles per XCD, all row chunks of a tile back to back (as in
+  // grouped_mfma_dma_kernel)
+  const int nx = (a.O + mfma_block_rows<0, NW, NS>() - 1) / mfma_block_rows<0, NW, NS>();
+  const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int tile = (k / nx) * 8 + xcd, chunk = k % nx;
+  if (tile >= *a.ntiles) return;
+  const int2 tg = a.tiles[tile];
+  const int g = tg.x, m0 = tg.y;
+  MfmaTile t;
+  t.rows = min(16 * MSVMAX, a.gcount[g] - m0);
+  t.lane = threadIdx.x & 63;
+  t.wave = threadIdx.x >> 6;
+  t.j = t.lane >> 4;
+  const bool shared = (g == a.E);
+  const int e = shared ? 0 : g;
+  const int o_blk = chunk * mfma_block_rows<0, NW, NS>();
+  const RowPtr G = pick(a.rt.gate, a.sh.gate, shared, e);
+  const RowPtr U = pick(a.rt.up, a.sh.up, shared, e);
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    t.Bm[s] = s >= NS / 2 ? U : G;
+    t.ob[s] = o_blk + 8 * NS * t.wave + 16 * (s % (NS / 2)) + (t.lane & 15);
+    t.bbase[s] = t.Bm[s].q;
+  }
+  const int *plist = a.pairs + a.goff[g] + m0;
+  for (int i = threadIdx.x; i < 16 * MSVMAX; i += NW * 64) {
+    const int pr = plist[min(i, t.rows - 1)];
+    const int ar = pr / a.P;
+    pr_l[i] = pr;
+    sum_l[i] = a.asum[ar];
+    scl_l[i] = a.ascale[ar];
+  }
+  __syncthreads();
+#define MOE_DMA2_TILE(M) dma2_tile<NW, MSVMAX, M, ABUF>(a, t, A0, A1, A2, W0, W1, pr_l, sum_l, scl_l)
+  switch ((t.rows + 15) >> 4) {
+    case 1: MOE_DMA2_TILE(1); break;
+    case 2: MOE_DMA2_TILE(cmin(2, MSVMAX)); break;
+    case 3: MOE_DMA2_TILE(cmin(3, MSVMAX)); break;
+    case 4: MOE_DMA2_TILE(cmin(4, MSVMAX)); break;
+    default: MOE_DMA2_TILE(MSVMAX); break;
+  }
+#undef MOE_DMA2_TILE
+}
+
 bool grouped_mfma_fits(int C) { return C % kKS == 0; }
 
 // Pairs per tile: as many as the launch's workgroups hold.  A group larger
@@ -668,7 +902,11 @@ static void launch_mode(const GroupedMfmaArgs &a, int max_tiles, hipStream_t st)
 // Batches of up to 64 tokens (at most 4 subtiles per tile): 4-wave
 // workgroups of 32 B rows per wave, so that a few experts still spread over
 // many workgroups (the DMA kernel took the 64-token verify from 532 to 632
-// us); larger batches: grouped_mfma_dma_kernel, 64 B rows per wave.
+// us); larger batches: 64 B rows per wave, gate/up in grouped_mfma_dma2_kernel
+// (against grouped_mfma_dma_kernel: 2048 tokens 829-839 against 857-862 us,
+// the union call 1 to 4 % faster from 96 to 2048 tokens), down in
+// grouped_mfma_dma_kernel (the double-step form was slower there, 1555-1561
+// against 1540-1550 us per 2048-token call).
 hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles, int S,
                                hipStream_t st) {
   if (S <= 64) {
@@ -676,15 +914,18 @@ hipError_t launch_grouped_mfma(const GroupedMfmaArgs &a, int mode, int max_tiles
       launch_mode<0, 4, 2, kSmallMsv>(a, max_tiles, st);
     else
       launch_mode<1, 4, 2, kSmallMsv>(a, max_tiles, st);
+  } else if (mode == 0) {
+    // gate/up: 8-wave workgroups, the weights requested two steps at a time
+    constexpr int RPB = mfma_block_rows<0, kD2Waves, kDNS>();
+    const int nx = (a.O + RPB - 1) / RPB;
+    hipLaunchKernelGGL((grouped_mfma_dma2_kernel<kLargeMsv>), dim3(nx * ((max_tiles + 7) / 8) * 8),
+                       dim3(kD2Waves * 64), 0, st, a);
   } else {
     constexpr int NW = kPrefillDmaWaves;
-    const int rpb = mode == 0 ? mfma_block_rows<0, NW, kDNS>() : mfma_block_rows<1, NW, kDNS>();
-    const int nx = (a.O + rpb - 1) / rpb;
+    constexpr int RPB = mfma_block_rows<1, NW, kDNS>();
+    const int nx = (a.O + RPB - 1) / RPB;
     const dim3 grid = kDmaXcdTiles ? dim3(nx * ((max_tiles + 7) / 8) * 8) : dim3(nx, max_tiles);
-    if (mode == 0)
-      hipLaunchKernelGGL((grouped_mfma_dma_kernel<0, NW, kLargeMsv>), grid, dim3(NW * 64), 0, st, a);
-    else
-      hipLaunchKernelGGL((grouped_mfma_dma_kernel<1, NW, kLargeMsv>), grid, dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((grouped_mfma_dma_kernel<1, NW, kLargeMsv>), grid, dim3(NW * 64), 0, st, a);
   }
   return hipGetLastError();
 }
