@@ -113,12 +113,12 @@ def _cpu_job(job):
     kind, lo, hi = job
     w = _CPU_WORK[kind]
     t0 = time.perf_counter()
-    if kind == "c2":  # per-token decode, one call per token
+    if kind == "decode":  # per-token decode, one call per token
         for s in range(lo, hi):
             oracle.layer_forward(w["layer"], w["x"][s:s + 1])
-    elif kind in ("c3", "c4"):  # the unique-expert union over the token range
+    elif kind in ("verify", "prefill"):  # the unique-expert union over the token range
         oracle.layer_forward_batch(w["layer"], w["x"][lo:hi])
-    else:  # c5: the token range through the stack's layers
+    else:  # stack: the token range through the stack's layers
         x = w["x"][lo:hi].copy()
         for L in w["layers"]:
             x = stack_layer(L, x, w["gamma"])
@@ -136,8 +136,8 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baselines(c2_tokens: int = 32, c4_subset: int = 64, c4_fanout: int = 512,
-                  c5_layers: int = 4, seed: int = 0):
+def cpu_baselines(decode_tokens: int = 32, prefill_subset: int = 64, prefill_fanout: int = 512,
+                  stack_layers: int = 4, seed: int = 0):
     """The oracle on bounded samples of every configuration, on 1 core and
     fanned out over N cores (N independent single-threaded processes over
     disjoint tokens).  Must run before the first GPU call."""
@@ -153,27 +153,27 @@ def cpu_baselines(c2_tokens: int = 32, c4_subset: int = 64, c4_fanout: int = 512
         n_cpu = len(os.sched_getaffinity(0))
     except AttributeError:
         n_cpu = os.cpu_count() or 1
-    N = max(1, min(16, n_cpu))  # a GPU machine gives one process a 16-CPU share
+    N = max(1, min(16, n_cpu))  # a process may use a 16-CPU share of the host
     t_prep = time.perf_counter()
     glm = synth.GLM
     gen = lambda L, ids: L.ensure(ids, workers=N)
-    # C2: decode tokens through one layer (the headline's replica 0 recipe)
+    # decode tokens through one layer (the headline's replica 0 recipe)
     L2 = LazyLayer(seed, glm, 0, bias_for("uniform", seed, glm))
-    x2 = synth.activations(7, c2_tokens, D)
+    x2 = synth.activations(7, decode_tokens, D)
     gen(L2, L2.ensure_for(x2))
-    # C3: the 64-token Zipf(1.1) verify
+    # the 64-token Zipf(1.1) verify
     wr = synth.router_w(0, glm)
     L3 = LazyLayer(0, glm, 0, np.zeros(E, np.float32), router_w=wr)
     x3, _, _ = synth.zipf_activations(0, glm, 64, wr)
     gen(L3, L3.ensure_for(x3))
-    # C4: the 2048-token bf16 prefill (uniform routing: every expert is used)
+    # the 2048-token bf16 prefill (uniform routing: every expert is used)
     L4 = LazyLayer(0, glm, 0, np.zeros(E, np.float32))
-    x4 = synth.bf16_to_f32(synth.bf16_bits(synth.activations(5, 2048, D)))[:c4_fanout]
+    x4 = synth.bf16_to_f32(synth.bf16_bits(synth.activations(5, 2048, D)))[:prefill_fanout]
     gen(L4, range(E))
-    # C5: the stack's first c5_layers layers, batch 1 and batch 4
+    # the stack's first stack_layers layers, batch 1 and batch 4
     with open(os.path.join(ROOT, "tests", "golden", "stack_beta.json")) as f:
         beta = json.load(f)["beta"]
-    L5 = [LazyLayer(0, glm, l, synth.zipf_bias(0, E, l, beta)) for l in range(c5_layers)]
+    L5 = [LazyLayer(0, glm, l, synth.zipf_bias(0, E, l, beta)) for l in range(stack_layers)]
     x5 = synth.activations(0, 4, D, item=74)
     gamma = np.ones(D, np.float32)
     # the experts each layer's tokens select (routing follows the residual
@@ -184,8 +184,9 @@ def cpu_baselines(c2_tokens: int = 32, c4_subset: int = 64, c4_fanout: int = 512
         idx, _, _, _ = router_topk(L.cfg, xn, L.router_w, L.router_b)
         gen(L, idx)
         xs = xs + layer_forward(L, xn)
-    _CPU_WORK.update(c2={"layer": L2, "x": x2}, c3={"layer": L3, "x": x3},
-                     c4={"layer": L4, "x": x4}, c5={"layers": L5, "x": x5, "gamma": gamma})
+    _CPU_WORK.update(decode={"layer": L2, "x": x2}, verify={"layer": L3, "x": x3},
+                     prefill={"layer": L4, "x": x4},
+                     stack={"layers": L5, "x": x5, "gamma": gamma})
     prep_s = time.perf_counter() - t_prep
     log(f"cpu baseline inputs ready in {prep_s:.1f}s ({N} workers)")
 
@@ -201,43 +202,44 @@ def cpu_baselines(c2_tokens: int = 32, c4_subset: int = 64, c4_fanout: int = 512
     res = {}
     with ctx.Pool(processes=N) as pool:
         one = lambda job: pool.apply(_cpu_job, (job,))  # 1 core: one worker, one job
-        # C2
-        t1 = one(("c2", 0, c2_tokens))
-        tn, nproc = fanout("c2", c2_tokens)
-        res["c2_decode"] = {"sample": f"{c2_tokens} GLM decode tokens, per-token path",
-                            "us_per_token_1core": round(t1 / c2_tokens * 1e6, 1),
-                            "us_per_token_ncore": round(tn / c2_tokens * 1e6, 1),
-                            "tokens_per_s_ncore": round(c2_tokens / tn, 2), "procs": nproc}
-        # C3 (the whole workload)
-        t1 = one(("c3", 0, 64))
-        tn, nproc = fanout("c3", 64)
-        res["c3_verify64"] = {"sample": "the whole 64-token Zipf verify, union path",
+        # per-token decode
+        t1 = one(("decode", 0, decode_tokens))
+        tn, nproc = fanout("decode", decode_tokens)
+        res["decode"] = {"sample": f"{decode_tokens} GLM decode tokens, per-token path",
+                            "us_per_token_1core": round(t1 / decode_tokens * 1e6, 1),
+                            "us_per_token_ncore": round(tn / decode_tokens * 1e6, 1),
+                            "tokens_per_s_ncore": round(decode_tokens / tn, 2), "procs": nproc}
+        # the 64-token verify (the whole workload)
+        t1 = one(("verify", 0, 64))
+        tn, nproc = fanout("verify", 64)
+        res["verify64"] = {"sample": "the whole 64-token Zipf verify, union path",
                               "us_per_step_1core": round(t1 * 1e6, 1),
                               "us_per_step_ncore": round(tn * 1e6, 1), "procs": nproc}
-        # C4: 1 core on c4_subset tokens, N cores on c4_fanout, both extrapolated
-        t1 = one(("c4", 0, c4_subset))
-        tn, nproc = fanout("c4", c4_fanout)
-        res["c4_prefill2048"] = {
-            "sample": f"1 core: {c4_subset} of the 2048 prefill tokens; N cores: {c4_fanout} "
+        # the prefill: 1 core on prefill_subset tokens, N cores on prefill_fanout,
+        # both extrapolated
+        t1 = one(("prefill", 0, prefill_subset))
+        tn, nproc = fanout("prefill", prefill_fanout)
+        res["prefill2048"] = {
+            "sample": f"1 core: {prefill_subset} of the 2048 prefill tokens; N cores: {prefill_fanout} "
                       f"tokens; union path; per-step times extrapolated linearly to 2048 tokens",
-            "us_per_step_1core_extrapolated": round(t1 * 2048 / c4_subset * 1e6, 1),
-            "us_per_step_ncore_extrapolated": round(tn * 2048 / c4_fanout * 1e6, 1),
+            "us_per_step_1core_extrapolated": round(t1 * 2048 / prefill_subset * 1e6, 1),
+            "us_per_step_ncore_extrapolated": round(tn * 2048 / prefill_fanout * 1e6, 1),
             "measured_s_1core": round(t1, 2), "measured_s_ncore": round(tn, 2), "procs": nproc}
-        # C5: batch 1 and batch 4 through c5_layers layers, extrapolated to 48
-        t1b1 = one(("c5", 0, 1))
-        t1b4 = one(("c5", 0, 4))
-        tnb4, nproc = fanout("c5", 4, per_proc=1)
-        sc = 48 / c5_layers
-        res["c5_stack48"] = {
-            "sample": f"first {c5_layers} of the 48 stack layers (RMSNorm + block + residual), "
+        # the stack: batch 1 and batch 4 through stack_layers layers, extrapolated to 48
+        t1b1 = one(("stack", 0, 1))
+        t1b4 = one(("stack", 0, 4))
+        tnb4, nproc = fanout("stack", 4, per_proc=1)
+        sc = 48 / stack_layers
+        res["stack48"] = {
+            "sample": f"first {stack_layers} of the 48 stack layers (RMSNorm + block + residual), "
                       f"times extrapolated linearly to 48 layers",
             "batch1_us_per_token_1core": round(t1b1 * sc * 1e6, 1),
             "batch4_us_per_step_1core": round(t1b4 * sc * 1e6, 1),
             "batch4_us_per_step_ncore": round(tnb4 * sc * 1e6, 1), "procs_batch4": nproc}
     _CPU_WORK.clear()
-    head = res["c2_decode"]
+    head = res["decode"]
     return {"value": head["us_per_token_1core"], "unit": "us/token", "cores": 1, "kind": "oracle",
-            "sample": f"{c2_tokens} GLM-shape decode tokens through one layer, oracle per-token "
+            "sample": f"{decode_tokens} GLM-shape decode tokens through one layer, oracle per-token "
                       f"path, single-threaded C (per-config and {N}-process figures in 'configs')",
             "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "cpus_available": n_cpu,
             "workers": N, "prep_s": round(prep_s, 1), "configs": res,
@@ -872,7 +874,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and not args.only and not args.copy_calibration:
         log("timing the CPU oracle ...")
-        cpu = cpu_baselines(c2_tokens=args.cpu_tokens)
+        cpu = cpu_baselines(decode_tokens=args.cpu_tokens)
         log(f"oracle: {cpu['value']} us/token on 1 core; {json.dumps(cpu['configs'])}")
 
     import numpy as np

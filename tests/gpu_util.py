@@ -96,7 +96,8 @@ def _routed_one(L, xs, idx, w, base_row, shared8):
 
 
 def _workers():
-    # the GPU machine gives a process a 16-CPU share whatever os.cpu_count() says
+    # at most 16 worker processes: a process may use a 16-CPU share of the host,
+    # whatever os.cpu_count() says
     return max(1, min(16, os.cpu_count() or 1))
 
 
