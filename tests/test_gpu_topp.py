@@ -61,8 +61,10 @@ def test_topp_against_oracle(shape, S, p):
         say(f"  {path}: keff {keff.tolist()}")
 
 
+# (MID, 800, 0.7): more than 64 tokens, and a pair list long enough that the
+# grouping kernel assembles it in shared memory, with dropped pairs
 @pytest.mark.parametrize("shape,S,p", [(MID, 5, 0.6), (MID, 37, 0.8), (GLM, 4, 0.7),
-                                       (K16, 7, 0.4), (E512, 5, 0.6)])
+                                       (K16, 7, 0.4), (E512, 5, 0.6), (MID, 800, 0.7)])
 def test_topp_union_equals_per_token_bit_exact(shape, S, p):
     dl = _with_topp(device_layer(9, shape, 0, bias_for("uniform", 9, shape)), p)
     x = synth.activations(41, S, shape.D)
