@@ -85,7 +85,11 @@ def test_tiny_block(path):
                                           # grouping kernel assembles the list in shared
                                           # memory; 25,200: more than that holds (24,576),
                                           # so it places them one by one
-                                          (MID, 500, "uniform"), (MID, 2800, "uniform")])
+                                          (MID, 500, "uniform"), (MID, 2800, "uniform"),
+                                          # more than 64 tokens with 10 and 26 steps of 128
+                                          # columns: the gate/up loop's partial turn of 12
+                                          (synth.Shape(D=1280, I=256, E=16, K=4), 100, "uniform"),
+                                          (synth.Shape(D=3328, I=256, E=8, K=2), 80, "uniform")])
 def test_batch_union_equals_per_token_bit_exact(shape, S, bias):
     b = bias_for(bias, 1, shape)
     dl = device_layer(1, shape, 0, b)
